@@ -1,0 +1,428 @@
+"""HyperAttention forward pass, step by step, on the CPU in fp64.
+
+Test infrastructure only (see the package docstring).
+
+The method ([S] "Approach"; [A] "Abstract") approximates softmax attention
+D^-1 A V, with A = exp(Q K^T) and D the diagonal of row sums of A:
+
+  1. sortLSH: hash the rows of Q and K, sort each by bucket in
+     Hamming (Gray-code) order and keep the equal-size diagonal blocks of
+     the sorted matrix -- the entries found to be large;
+  2. the normaliser D is the exact masked row sum over the row's block plus
+     an estimate of the rest from uniformly sampled key columns;
+  3. the product with V uses the same split: exact inside the block, the
+     sampled columns outside it (reading below);
+  4. causal masking by recursion ([S] summary line and "Limitations": a
+     recursive causal-masking extension whose partitioning and merging cost
+     shrinks the causal speed-up): both diagonal halves recurse causally,
+     the off-diagonal quadrant (later queries, earlier keys) is unmasked
+     and handled by steps 1-3, and the halves fall back to exact causal
+     attention once they are short.
+
+Readings taken where the pages are silent or garbled (each is repeated at
+the function that uses it):
+
+  * the product with V re-uses the uniform column samples of the
+    normaliser; [S] "Approach" names row-norm sampling for the product,
+    which is a different estimator and not built here;
+  * A = exp(Q K^T) with no softmax scale (callers pre-scale Q and K);
+  * no clipping or threshold constants (none are printed);
+  * samples are iid uniform *with replacement* over the sorted key
+    positions of the (sub)problem, shared by all its rows, and excluded for
+    a row when they fall inside that row's block; each kept sample carries
+    weight ns/m, so the out-of-block estimate is unbiased;
+  * causal leaves: a span of length <= min_seq_len is computed exactly;
+    a longer span must split into two even halves;
+  * the non-causal call is one problem (node 1) and ignores min_seq_len.
+"""
+
+from dataclasses import dataclass
+
+import numpy as np
+
+from .gauss import projections
+from .philox import philox_words
+
+
+@dataclass
+class HAConfig:
+    block: int
+    samples: int
+    proj_bits: int
+    causal: bool = False
+    min_seq_len: int = 0
+    seed: int = 0
+
+
+# ----------------------------------------------------------------------------
+# Step 1: sortLSH -- hash, Gray-code rank, stable sort  ([S] "Approach",
+# "Builds on": Hamming sorted LSH)
+# ----------------------------------------------------------------------------
+
+def _padded_dim(d):
+    """Smallest 8 * 2^k >= d."""
+    g = 1
+    while 8 * g < d:
+        g *= 2
+    return 8 * g
+
+
+def _halving_sum_last(v):
+    """Sum over the last axis by repeated halving: v <- v[:h] + v[h:]."""
+    while v.shape[-1] > 1:
+        h = v.shape[-1] // 2
+        v = v[..., :h] + v[..., h:]
+    return v[..., 0]
+
+
+def projection_sums(x32, R):
+    """t[i, p] = <x_i, R_p> in fp32 with a fixed summation order.
+
+    Reading: the pages give no arithmetic for the hash.  Here every product
+    x_k * R[p][k] is rounded to fp32, the row is cut into consecutive groups
+    of 8 products, each group is summed by halving (pairs 4 apart, then 2,
+    then 1), and the group sums are summed by halving.  d is padded with
+    zeros to 8 * 2^k.  No fused multiply-add anywhere."""
+    x32 = np.asarray(x32, dtype=np.float32)
+    R = np.asarray(R, dtype=np.float32)
+    rows, d = x32.shape
+    r = R.shape[0]
+    dp = _padded_dim(d)
+    xp = np.zeros((rows, dp), dtype=np.float32)
+    xp[:, :d] = x32
+    rp = np.zeros((r, dp), dtype=np.float32)
+    rp[:, :d] = R
+    t = np.empty((rows, r), dtype=np.float32)
+    for p in range(r):
+        prod = xp * rp[p]                                  # fp32 products
+        groups = _halving_sum_last(prod.reshape(rows, dp // 8, 8))
+        t[:, p] = _halving_sum_last(groups)
+    return t
+
+
+def hash_codes(x32, R):
+    """Sign-bit code: bit p is 1 iff <x, R_p> > 0 (so +0, -0 and NaN give 0);
+    projection 0 is the least significant bit."""
+    t = projection_sums(x32, R)
+    bits = (t > 0).astype(np.uint32)
+    code = np.zeros(t.shape[0], dtype=np.uint32)
+    for p in range(t.shape[1]):
+        code |= bits[:, p] << np.uint32(p)
+    return code
+
+
+def gray_inverse(code, r):
+    """Position of ``code`` in the reflected-binary Gray sequence g(k) = k ^ (k>>1):
+    the prefix xor code ^ code>>1 ^ code>>2 ^ ... ^ code>>(r-1).
+
+    Reading of "Hamming sorted": buckets are ordered by this position, so
+    consecutive buckets differ in exactly one hash bit."""
+    x = np.asarray(code, dtype=np.uint32).copy()
+    shift = 1
+    while shift < r:
+        x ^= x >> np.uint32(shift)
+        shift *= 2
+    return x
+
+
+def ranks(x32, R):
+    """Bucket rank of each row: Gray position of its sign code."""
+    return gray_inverse(hash_codes(x32, R), R.shape[0])
+
+
+def sort_perm(rank):
+    """Sorted position -> original index, ordered by (rank, index): the
+    sort is stable, ties keep their original order."""
+    return np.argsort(np.asarray(rank), kind="stable")
+
+
+# ----------------------------------------------------------------------------
+# Steps 2-3: exact block part + sampled part ([S] "Approach": exact masked
+# row sums + uniform column sampling)
+# ----------------------------------------------------------------------------
+
+def sample_positions(seed, batch_idx, head, node, ns, m):
+    """m sorted-key positions in [0, ns), iid uniform with replacement.
+
+    Reading: word i of the Philox stream with counters
+    (i // 4, node, head, 2*batch_idx + 1) under the seed (word i % 4 of that
+    counter) becomes floor(word * ns / 2^32).  The last counter word is odd
+    here and 0 for the projections, so the two streams never meet."""
+    if m == 0:
+        return np.zeros(0, dtype=np.int64)
+    w = philox_words(seed, m, c1=node, c2=head, c3=2 * batch_idx + 1)
+    return ((w * np.uint64(ns)) >> np.uint64(32)).astype(np.int64)
+
+
+def _softmax_stats(S, V):
+    """lse and softmax(S) V row by row, fp64 with max shift; rows whose
+    scores are all -inf give lse = -inf and o = 0."""
+    mx = np.max(S, axis=-1, keepdims=True)
+    finite = np.isfinite(mx)
+    mx_safe = np.where(finite, mx, 0.0)
+    E = np.where(np.isfinite(S), np.exp(S - mx_safe), 0.0)
+    ssum = E.sum(axis=-1)
+    with np.errstate(divide="ignore", invalid="ignore"):
+        o = np.matmul(E, V) / ssum[..., None]
+        lse = mx_safe[..., 0] + np.log(ssum)
+    o = np.where((ssum > 0)[..., None], o, 0.0)
+    lse = np.where(ssum > 0, lse, -np.inf)
+    return lse, o
+
+
+def block_part(Qs, Ks, Vs, b_eff, positions=None):
+    """Exact attention of sorted query p over the sorted keys of its own
+    diagonal block t = p // b_eff, i.e. keys [t b_eff, (t+1) b_eff).
+    Returns (lse_blk, o_blk) for ``positions`` (all if None):
+    exp(lse_blk) = sum_{j in blk} e^{S_pj},  o_blk = that softmax times V."""
+    ns, d = Qs.shape
+    if positions is None:
+        nb = ns // b_eff
+        S = np.matmul(Qs.reshape(nb, b_eff, d), Ks.reshape(nb, b_eff, d).transpose(0, 2, 1))
+        lse, o = _softmax_stats(S, Vs.reshape(nb, b_eff, d))
+        return lse.reshape(ns), o.reshape(ns, d)
+    positions = np.asarray(positions, dtype=np.int64)
+    lse = np.empty(len(positions))
+    o = np.empty((len(positions), d))
+    for c in range(0, len(positions), 256):
+        p = positions[c:c + 256]
+        keys = (p // b_eff)[:, None] * b_eff + np.arange(b_eff)[None, :]
+        S = np.einsum("rd,rkd->rk", Qs[p], Ks[keys])
+        l, oo = _softmax_stats(S[:, None, :], Vs[keys])
+        lse[c:c + 256] = l[:, 0]
+        o[c:c + 256] = oo[:, 0, :]
+    return lse, o
+
+
+def sample_part(Qs, Ks, Vs, idx, b_eff, positions=None):
+    """Sampled estimate of the mass outside the row's block:
+    D_smp = (ns/m) sum_{i: idx_i // b_eff != p // b_eff} e^{S_{p, idx_i}}
+    and the matching weighted sum of value rows; duplicates count each time.
+    Returns (lse_smp, o_smp) with exp(lse_smp) = D_smp; an empty sum gives
+    lse = -inf, o = 0."""
+    ns, d = Qs.shape
+    if positions is None:
+        positions = np.arange(ns)
+    positions = np.asarray(positions, dtype=np.int64)
+    m = len(idx)
+    if m == 0:
+        return np.full(len(positions), -np.inf), np.zeros((len(positions), d))
+    idx = np.asarray(idx, dtype=np.int64)
+    Ksm = Ks[idx]
+    Vsm = Vs[idx]
+    col_blk = idx // b_eff
+    lse = np.empty(len(positions))
+    o = np.empty((len(positions), d))
+    for c in range(0, len(positions), 4096):
+        p = positions[c:c + 4096]
+        S = Qs[p] @ Ksm.T
+        keep = (p // b_eff)[:, None] != col_blk[None, :]
+        S = np.where(keep, S, -np.inf)
+        l, oo = _softmax_stats(S, Vsm)
+        lse[c:c + 4096] = l + np.log(ns / m)
+        o[c:c + 4096] = oo
+    return lse, o
+
+
+def lse_merge(l1, o1, l2, o2):
+    """Merge two parts given as (lse, normalised output):
+    lse = ln(e^l1 + e^l2), o = o1 e^{l1 - lse} + o2 e^{l2 - lse}."""
+    l = np.logaddexp(l1, l2)
+    with np.errstate(invalid="ignore"):
+        w1 = np.where(np.isfinite(l1), np.exp(l1 - l), 0.0)
+        w2 = np.where(np.isfinite(l2), np.exp(l2 - l), 0.0)
+    return l, o1 * w1[..., None] + o2 * w2[..., None]
+
+
+def noncausal_problem(q, k, v, rank_q, rank_k, seed, batch_idx, head, node,
+                      block, samples, rows=None, parts=None):
+    """One non-causal (sub)problem of ns queries and ns keys.
+
+    q, k, v: fp64 [ns, d] rows in original order; rank_q, rank_k: bucket
+    ranks of those rows.  Returns (o, lse) for ``rows`` (local indices,
+    all if None) in original row order.  If ``parts`` is a dict it receives
+    the intermediates (perms, samples, per-part lse/o in sorted order)."""
+    ns, d = q.shape
+    if k.shape[0] != ns:
+        raise ValueError("square problems only")
+    if ns == 0:
+        return np.zeros((0, d)), np.zeros(0)
+    b_eff = min(block, ns)
+    if b_eff < 1 or ns % b_eff:
+        raise ValueError(f"segment length {ns} is not a multiple of block {b_eff}")
+    pq = sort_perm(rank_q)
+    pk = sort_perm(rank_k)
+    Qs, Ks, Vs = q[pq], k[pk], v[pk]
+    idx = sample_positions(seed, batch_idx, head, node, ns, samples)
+    if rows is None:
+        positions = None
+    else:
+        inv = np.empty(ns, dtype=np.int64)
+        inv[pq] = np.arange(ns)
+        positions = inv[np.asarray(rows, dtype=np.int64)]
+    lb, ob = block_part(Qs, Ks, Vs, b_eff, positions)
+    ls, osm = sample_part(Qs, Ks, Vs, idx, b_eff, positions)
+    lse, o = lse_merge(lb, ob, ls, osm)
+    if parts is not None:
+        parts.update(perm_q=pq, perm_k=pk, idx=idx, lse_blk=lb, o_blk=ob,
+                     lse_smp=ls, o_smp=osm, b_eff=b_eff)
+    if rows is None:
+        out = np.empty_like(o)
+        out[pq] = o                                # unsort
+        lse_out = np.empty_like(lse)
+        lse_out[pq] = lse
+        return out, lse_out
+    return o, lse
+
+
+# ----------------------------------------------------------------------------
+# Step 4: causal recursion ([S] summary and "Limitations")
+# ----------------------------------------------------------------------------
+
+def _exact_causal_rows(q, k, v, rows):
+    """Exact causal softmax attention: local row i attends keys 0..i."""
+    rows = np.asarray(rows, dtype=np.int64)
+    S = q[rows] @ k.T
+    S = np.where(np.arange(k.shape[0])[None, :] <= rows[:, None], S, -np.inf)
+    lse, o = _softmax_stats(S, v)
+    return o, lse
+
+
+def causal_levels(n, min_seq_len):
+    """Number of recursion levels: halvings until a span is <= min_seq_len."""
+    L, ns = 0, n
+    while ns > min_seq_len:
+        if ns % 2:
+            raise ValueError(f"causal split of odd length {ns}")
+        ns //= 2
+        L += 1
+    return L
+
+
+def causal_problem(q, k, v, rank_q, rank_k, seed, batch_idx, head, cfg, rows=None):
+    """Causal HyperAttention of one head.  causal(lo, hi, node): a span of
+    length <= min_seq_len is exact causal attention; otherwise, with
+    mid = (lo + hi) / 2, causal(lo, mid, 2 node) and causal(mid, hi,
+    2 node + 1) recurse, and rows [mid, hi) are merged (deepest level
+    first) with the non-causal problem of queries [mid, hi) over keys
+    [lo, mid), with this node's samples.  Ranks come from the one hash of
+    the whole sequence (one projection matrix for all nodes)."""
+    n, d = q.shape
+    s = cfg.min_seq_len
+    all_rows = np.arange(n) if rows is None else np.sort(np.asarray(rows, dtype=np.int64))
+    o_out = np.zeros((len(all_rows), d))
+    l_out = np.zeros(len(all_rows))
+    pos_of = {int(r): i for i, r in enumerate(all_rows)}
+
+    def rec(lo, hi, node, want):
+        ns = hi - lo
+        if len(want) == 0:
+            return
+        if ns <= s:
+            o, l = _exact_causal_rows(q[lo:hi], k[lo:hi], v[lo:hi], want - lo)
+            for j, r in enumerate(want):
+                o_out[pos_of[int(r)]] = o[j]
+                l_out[pos_of[int(r)]] = l[j]
+            return
+        if ns % 2:
+            raise ValueError(f"causal split of odd length {ns}")
+        mid = lo + ns // 2
+        rec(lo, mid, 2 * node, want[want < mid])
+        upper = want[want >= mid]
+        rec(mid, hi, 2 * node + 1, upper)
+        if len(upper) == 0:
+            return
+        oq, lq = noncausal_problem(q[mid:hi], k[lo:mid], v[lo:mid], rank_q[mid:hi],
+                                   rank_k[lo:mid], seed, batch_idx, head, node,
+                                   cfg.block, cfg.samples, rows=upper - mid)
+        sel = np.array([pos_of[int(r)] for r in upper])
+        l_new, o_new = lse_merge(l_out[sel], o_out[sel], lq, oq)
+        l_out[sel] = l_new
+        o_out[sel] = o_new
+
+    rec(0, n, 1, all_rows)
+    return o_out, l_out
+
+
+# ----------------------------------------------------------------------------
+# Whole forward and exact attention
+# ----------------------------------------------------------------------------
+
+def _check(q, k, v, cfg):
+    B, H, n, d = q.shape
+    if k.shape[0] != B or k.shape[2] != n or k.shape[3] != d or v.shape != k.shape:
+        raise ValueError("shape mismatch")
+    Hkv = k.shape[1]
+    if Hkv < 1 or H % Hkv:
+        raise ValueError("heads must be a multiple of kv_heads")
+    if not 1 <= cfg.proj_bits <= 16:
+        raise ValueError("proj_bits must be in [1, 16]")
+    if cfg.block < 1 or cfg.samples < 0:
+        raise ValueError("block >= 1 and samples >= 0 required")
+    if cfg.causal:
+        causal_levels(n, cfg.min_seq_len)
+    return B, H, Hkv, n, d
+
+
+def forward_rows(q, k, v, cfg, heads=None, rows=None):
+    """HyperAttention forward for the listed (batch, head) pairs and
+    original row indices (all if None).
+
+    q: [B, H, n, d], k, v: [B, Hkv, n, d] float32 arrays holding the input
+    values exactly (bf16 inputs widened); query head h uses KV head
+    h // (H / Hkv).  Returns (out, lse) in fp64 with shapes
+    [len(heads), len(rows), d] and [len(heads), len(rows)]."""
+    B, H, Hkv, n, d = _check(q, k, v, cfg)
+    G = H // Hkv
+    if heads is None:
+        heads = [(b, h) for b in range(B) for h in range(H)]
+    if rows is not None:
+        rows = np.sort(np.asarray(rows, dtype=np.int64))
+    nr = n if rows is None else len(rows)
+    R = projections(cfg.seed, d, cfg.proj_bits)
+    out = np.zeros((len(heads), nr, d))
+    lse = np.zeros((len(heads), nr))
+    rank_cache = {}
+    for i, (b, h) in enumerate(heads):
+        g = h // G
+        if (b, g) not in rank_cache:
+            rank_cache[(b, g)] = ranks(k[b, g], R)
+        rk = rank_cache[(b, g)]
+        rq = ranks(q[b, h], R)
+        qh = q[b, h].astype(np.float64)
+        kh = k[b, g].astype(np.float64)
+        vh = v[b, g].astype(np.float64)
+        if cfg.causal:
+            o, l = causal_problem(qh, kh, vh, rq, rk, cfg.seed, b, h, cfg, rows=rows)
+        else:
+            o, l = noncausal_problem(qh, kh, vh, rq, rk, cfg.seed, b, h, 1,
+                                     cfg.block, cfg.samples, rows=rows)
+        out[i] = o
+        lse[i] = l
+    return out, lse
+
+
+def forward(q, k, v, cfg):
+    """Full forward: (out [B, H, n, d], lse [B, H, n]) in fp64."""
+    B, H = q.shape[:2]
+    out, lse = forward_rows(q, k, v, cfg)
+    return out.reshape(B, H, q.shape[2], q.shape[3]), lse.reshape(B, H, q.shape[2])
+
+
+def exact_attention(q, k, v, causal=False):
+    """softmax(Q K^T) V per head (no scale), fp64, GQA by h // (H / Hkv).
+    Returns (out, lse)."""
+    B, H, n, d = q.shape
+    G = H // k.shape[1]
+    out = np.zeros((B, H, n, d))
+    lse = np.zeros((B, H, n))
+    for b in range(B):
+        for h in range(H):
+            qh = q[b, h].astype(np.float64)
+            kh = k[b, h // G].astype(np.float64)
+            vh = v[b, h // G].astype(np.float64)
+            S = qh @ kh.T
+            if causal:
+                S = np.where(np.tri(n, dtype=bool), S, -np.inf)
+            lse[b, h], out[b, h] = _softmax_stats(S, vh)
+    return out, lse
