@@ -1,0 +1,663 @@
+// Host driver and C ABI of the HyperAttention forward.
+//
+// ("HyperAttention: Long-context Attention in Near-Linear Time",
+// research-map summary: sections Approach and Limitations, and the summary
+// line on the recursive causal-masking extension.)
+//
+// Non-causal forward, all on the caller's stream:
+//   projections -> hash Q, hash K -> sort Q, sort K (one segment per head)
+//   -> sample positions (node 1) -> fused block + sample attention with
+//   the merge and the unsort in its epilogue.
+// Causal forward: projections and hashes once; the exact causal leaves of
+// length n / 2^L write the first leaf's rows to the output and the others
+// to an fp32 accumulator; then for level l = L .. 1 (deepest first) the
+// 2^(l-1) off-diagonal quadrants of that level (queries = odd halves,
+// keys = even halves, each n / 2^l long) are sorted, sampled and attended
+// in one batched launch each, merged into the accumulator; the rows of
+// the leftmost quadrant of a level are final and go to the output.  No
+// host synchronisation inside.
+#include <hip/hip_runtime.h>
+
+#include <cmath>
+#include <cstdarg>
+#include <cstdio>
+#include <cstdlib>
+#include <cstring>
+#include <mutex>
+#include <string>
+#include <vector>
+
+#include "ha_kernels.h"
+#include "ha_rng.h"
+
+namespace ha {
+
+static thread_local std::string g_last_error;
+
+void set_error(const char* fmt, ...) {
+  char buf[512];
+  va_list ap;
+  va_start(ap, fmt);
+  std::vsnprintf(buf, sizeof(buf), fmt, ap);
+  va_end(ap);
+  g_last_error = buf;
+}
+
+int hip_status(hipError_t e, const char* what) {
+  set_error("%s failed: %s", what, hipGetErrorString(e));
+  return HA_EHIP;
+}
+
+static bool sync_mode() {
+  static int mode = [] {
+    const char* s = std::getenv("HYPERATTN_SYNC");
+    return (s && s[0] == '1') ? 1 : 0;
+  }();
+  return mode != 0;
+}
+
+int after_launch(const char* stage, hipStream_t stream) {
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess) {
+    set_error("launch of %s failed: %s", stage, hipGetErrorString(e));
+    return HA_EHIP;
+  }
+  if (sync_mode()) {
+    e = hipStreamSynchronize(stream);
+    if (e != hipSuccess) {
+      set_error("%s failed while running: %s", stage, hipGetErrorString(e));
+      return HA_EHIP;
+    }
+  }
+  return HA_OK;
+}
+
+// ---- timing hooks -----------------------------------------------------------
+
+struct TimingRec {
+  int kind;
+  hipEvent_t start, stop;
+};
+
+static std::mutex g_tmu;
+static bool g_timing = false;
+static std::vector<TimingRec> g_recs;
+static std::vector<hipEvent_t> g_event_pool;
+static std::vector<size_t> g_open;   // indices of records awaiting timing_end
+
+static hipEvent_t pool_event() {
+  if (!g_event_pool.empty()) {
+    hipEvent_t e = g_event_pool.back();
+    g_event_pool.pop_back();
+    return e;
+  }
+  hipEvent_t e = nullptr;
+  if (hipEventCreate(&e) != hipSuccess) return nullptr;
+  return e;
+}
+
+void timing_begin(int kind, hipStream_t s) {
+  std::lock_guard<std::mutex> lk(g_tmu);
+  if (!g_timing) return;
+  TimingRec r{kind, pool_event(), pool_event()};
+  if (!r.start || !r.stop) return;
+  (void)hipEventRecord(r.start, s);
+  g_recs.push_back(r);
+  g_open.push_back(g_recs.size() - 1);
+}
+
+void timing_end(int kind, hipStream_t s) {
+  std::lock_guard<std::mutex> lk(g_tmu);
+  if (!g_timing || g_open.empty()) return;
+  size_t i = g_open.back();
+  g_open.pop_back();
+  if (g_recs[i].kind != kind) return;
+  (void)hipEventRecord(g_recs[i].stop, s);
+}
+
+// ---- validation and planning ------------------------------------------------
+
+struct Shape {
+  int batch, n, d, heads, kv_heads, block, samples, r, causal, s, dtype, flags;
+  int levels = 0;    // causal levels
+  int leaf = 0;      // causal leaf length
+};
+
+static int validate(Shape& sh) {
+  if (sh.dtype != HA_BF16 && sh.dtype != HA_F32) {
+    set_error("dtype %d is neither HA_BF16 nor HA_F32", sh.dtype);
+    return HA_EINVAL;
+  }
+  if (sh.batch < 0 || sh.n < 0 || sh.heads < 0 || sh.kv_heads < 0) {
+    set_error("negative size");
+    return HA_EINVAL;
+  }
+  if (sh.kv_heads == 0 || sh.heads % sh.kv_heads != 0) {
+    if (!(sh.heads == 0 && sh.kv_heads == 0)) {
+      set_error("heads (%d) must be a positive multiple of kv_heads (%d)", sh.heads, sh.kv_heads);
+      return HA_EINVAL;
+    }
+  }
+  if (sh.block < 1 || sh.samples < 0) {
+    set_error("block must be >= 1 and samples >= 0 (block %d, samples %d)", sh.block, sh.samples);
+    return HA_EINVAL;
+  }
+  if (sh.r < 1 || sh.r > 16) {
+    set_error("proj_bits %d outside [1, 16]", sh.r);
+    return HA_EINVAL;
+  }
+  if (sh.causal && sh.s < 1) {
+    set_error("causal needs min_seq_len >= 1 (got %d)", sh.s);
+    return HA_EINVAL;
+  }
+  if (sh.d != 64 && sh.d != 128) {
+    set_error("head dim %d not built (64 or 128)", sh.d);
+    return HA_EUNSUPPORTED;
+  }
+  if (sh.flags & ~(HA_FLAG_MATERIALIZE | HA_FLAG_UNFUSED)) {
+    set_error("unknown flags 0x%x", sh.flags);
+    return HA_EINVAL;
+  }
+  if (sh.causal && sh.flags) {
+    set_error("flags apply to the non-causal forward only");
+    return HA_EUNSUPPORTED;
+  }
+  if (sh.samples > kMaxSamples) {
+    set_error("samples %d > %d", sh.samples, kMaxSamples);
+    return HA_EUNSUPPORTED;
+  }
+  if (sh.n == 0) return HA_OK;
+  if (!sh.causal) {
+    const int b = sh.block < sh.n ? sh.block : sh.n;
+    if (sh.n % b) {
+      set_error("n = %d is not a multiple of block %d", sh.n, b);
+      return HA_ESHAPE;
+    }
+    return HA_OK;
+  }
+  int ns = sh.n, L = 0;
+  while (ns > sh.s) {
+    if (ns % 2) {
+      set_error("causal split of odd length %d", ns);
+      return HA_ESHAPE;
+    }
+    ns /= 2;
+    ++L;
+    const int b = sh.block < ns ? sh.block : ns;
+    if (ns % b) {
+      set_error("causal quadrant length %d is not a multiple of block %d", ns, b);
+      return HA_ESHAPE;
+    }
+  }
+  sh.levels = L;
+  sh.leaf = ns;
+  return HA_OK;
+}
+
+struct Plan {
+  float* R;
+  uint16_t* rank_q;
+  uint16_t* rank_k;
+  int32_t* perm_q;
+  int32_t* perm_k;
+  int32_t* sidx;
+  void* sort_ws;
+  size_t sort_ws_bytes;
+  float* acc_o;
+  float* acc_lse;
+  void* qs;
+  void* ks;
+  void* vs;
+  float* part_o[2];
+  float* part_lse[2];
+  size_t total;
+};
+
+static Plan make_plan(const Shape& sh, void* ws, size_t cap) {
+  Plan pl{};
+  Carve cv(ws, cap);
+  const int64_t BH = static_cast<int64_t>(sh.batch) * sh.heads;
+  const int64_t BK = static_cast<int64_t>(sh.batch) * sh.kv_heads;
+  const size_t esz = sh.dtype == HA_BF16 ? 2 : 4;
+  pl.R = cv.take<float>(static_cast<size_t>(sh.r) * sh.d);
+  pl.rank_q = cv.take<uint16_t>(BH * sh.n);
+  pl.rank_k = cv.take<uint16_t>(BK * sh.n);
+  if (!sh.causal) {
+    pl.perm_q = cv.take<int32_t>(BH * sh.n);
+    pl.perm_k = cv.take<int32_t>(BK * sh.n);
+    pl.sidx = cv.take<int32_t>(BH * (sh.samples > 0 ? sh.samples : 1));
+    size_t a = sort_ws_bytes(BH, sh.n, 1, sh.r), b = sort_ws_bytes(BK, sh.n, 1, sh.r);
+    pl.sort_ws_bytes = a > b ? a : b;
+    pl.sort_ws = cv.take<char>(pl.sort_ws_bytes);
+    if (sh.flags & HA_FLAG_MATERIALIZE) {
+      pl.qs = cv.take<char>(BH * sh.n * sh.d * esz);
+      pl.ks = cv.take<char>(BK * sh.n * sh.d * esz);
+      pl.vs = cv.take<char>(BK * sh.n * sh.d * esz);
+    }
+    if (sh.flags & HA_FLAG_UNFUSED) {
+      for (int i = 0; i < 2; ++i) {
+        pl.part_o[i] = cv.take<float>(BH * sh.n * sh.d);
+        pl.part_lse[i] = cv.take<float>(BH * sh.n);
+      }
+    }
+  } else {
+    if (sh.levels > 0) {
+      pl.acc_o = cv.take<float>(BH * sh.n * sh.d);
+      pl.acc_lse = cv.take<float>(BH * sh.n);
+      pl.perm_q = cv.take<int32_t>(BH * (sh.n / 2));
+      pl.perm_k = cv.take<int32_t>(BK * (sh.n / 2));
+      const int64_t maxp = int64_t(1) << (sh.levels - 1);
+      pl.sidx = cv.take<int32_t>(BH * maxp * (sh.samples > 0 ? sh.samples : 1));
+      size_t mx = 0;
+      for (int l = 1; l <= sh.levels; ++l) {
+        const int seg = sh.n >> l;
+        const int pieces = 1 << (l - 1);
+        size_t a = sort_ws_bytes(BH, seg, pieces, sh.r), b = sort_ws_bytes(BK, seg, pieces, sh.r);
+        if (a > mx) mx = a;
+        if (b > mx) mx = b;
+      }
+      pl.sort_ws_bytes = mx;
+      pl.sort_ws = cv.take<char>(mx);
+    }
+  }
+  pl.total = align_up(cv.used, 256) + 256;
+  return pl;
+}
+
+static int forward_impl(const void* q, const void* k, const void* v, Shape sh, uint64_t seed,
+                        void* out, float* lse, void* ws, size_t ws_bytes, hipStream_t s) {
+  HA_TRY(validate(sh));
+  if (sh.n == 0 || sh.batch == 0 || sh.heads == 0) return HA_OK;
+  if (!q || !k || !v || !out) {
+    set_error("null q, k, v or out");
+    return HA_EINVAL;
+  }
+  const Plan need = make_plan(sh, nullptr, 0);
+  if (!ws || ws_bytes < need.total) {
+    set_error("workspace of %zu bytes < %zu required", ws_bytes, need.total);
+    return HA_EWORKSPACE;
+  }
+  if (reinterpret_cast<uintptr_t>(ws) % 256) {
+    set_error("workspace must be 256-byte aligned");
+    return HA_EINVAL;
+  }
+  const Plan pl = make_plan(sh, ws, ws_bytes);
+  const int64_t BH = static_cast<int64_t>(sh.batch) * sh.heads;
+  const int64_t BK = static_cast<int64_t>(sh.batch) * sh.kv_heads;
+
+  HA_TRY(launch_projections(seed, sh.d, sh.r, pl.R, s));
+  HA_TRY(launch_hash(q, sh.dtype, BH * sh.n, sh.d, sh.r, pl.R, pl.rank_q, s));
+  HA_TRY(launch_hash(k, sh.dtype, BK * sh.n, sh.d, sh.r, pl.R, pl.rank_k, s));
+
+  AttnParams ap;
+  ap.q = q;
+  ap.k = k;
+  ap.v = v;
+  ap.dtype = sh.dtype;
+  ap.d = sh.d;
+  ap.n = sh.n;
+  ap.H = sh.heads;
+  ap.Hkv = sh.kv_heads;
+  ap.BH = static_cast<int>(BH);
+  ap.out = out;
+  ap.lse = lse;
+
+  if (!sh.causal) {
+    HA_TRY(launch_sort(pl.rank_q, BH, sh.n, sh.n, 0, sh.n, 1, sh.r, pl.perm_q, pl.sort_ws,
+                       pl.sort_ws_bytes, s));
+    HA_TRY(launch_sort(pl.rank_k, BK, sh.n, sh.n, 0, sh.n, 1, sh.r, pl.perm_k, pl.sort_ws,
+                       pl.sort_ws_bytes, s));
+    HA_TRY(launch_sample_indices(seed, sh.batch, sh.heads, 1, 1, sh.n, sh.samples, pl.sidx, s));
+    ap.kind = kKindSorted;
+    ap.pieces = 1;
+    ap.seg = sh.n;
+    ap.stride = sh.n;
+    ap.perm_q = pl.perm_q;
+    ap.perm_k = pl.perm_k;
+    ap.b_eff = sh.block < sh.n ? sh.block : sh.n;
+    ap.sidx = pl.sidx;
+    ap.m = sh.samples;
+    ap.log2w = sh.samples > 0 ? static_cast<float>(std::log2(static_cast<double>(sh.n) / sh.samples)) : 0.f;
+    if (sh.flags & HA_FLAG_MATERIALIZE) {
+      HA_TRY(launch_gather(q, sh.dtype, BH, sh.n, sh.d, pl.perm_q, sh.n, pl.qs, s));
+      HA_TRY(launch_gather(k, sh.dtype, BK, sh.n, sh.d, pl.perm_k, sh.n, pl.ks, s));
+      HA_TRY(launch_gather(v, sh.dtype, BK, sh.n, sh.d, pl.perm_k, sh.n, pl.vs, s));
+      ap.qs = pl.qs;
+      ap.ks = pl.ks;
+      ap.vs = pl.vs;
+    }
+    if (sh.flags & HA_FLAG_UNFUSED) {
+      ap.out_mode = kOutPartial;
+      ap.use_block = 1;
+      ap.use_samples = 0;
+      ap.part_o = pl.part_o[0];
+      ap.part_lse = pl.part_lse[0];
+      HA_TRY(launch_attention(ap, HA_K_ATTEND, s));
+      ap.use_block = 0;
+      ap.use_samples = 1;
+      ap.part_o = pl.part_o[1];
+      ap.part_lse = pl.part_lse[1];
+      HA_TRY(launch_attention(ap, HA_K_ATTEND, s));
+      return launch_merge_unsort(pl.part_o[0], pl.part_lse[0], pl.part_o[1], pl.part_lse[1],
+                                 pl.perm_q, BH, sh.n, sh.d, sh.dtype, out, lse, s);
+    }
+    ap.out_mode = kOutFinal;
+    ap.use_block = 1;
+    ap.use_samples = sh.samples > 0;
+    return launch_attention(ap, HA_K_ATTEND, s);
+  }
+
+  // ---- causal ----
+  AttnParams lp = ap;
+  lp.kind = kKindLeaf;
+  lp.pieces = sh.n / sh.leaf;
+  lp.seg = sh.leaf;
+  lp.stride = sh.leaf;
+  lp.b_eff = sh.leaf;
+  lp.use_block = 1;
+  lp.use_samples = 0;
+  lp.out_mode = kOutLeaf;
+  lp.acc_o = pl.acc_o;
+  lp.acc_lse = pl.acc_lse;
+  HA_TRY(launch_attention(lp, HA_K_LEAF, s));
+
+  for (int l = sh.levels; l >= 1; --l) {
+    const int seg = sh.n >> l;
+    const int pieces = 1 << (l - 1);
+    HA_TRY(launch_sort(pl.rank_q, BH, sh.n, seg, seg, 2 * seg, pieces, sh.r, pl.perm_q,
+                       pl.sort_ws, pl.sort_ws_bytes, s));
+    HA_TRY(launch_sort(pl.rank_k, BK, sh.n, seg, 0, 2 * seg, pieces, sh.r, pl.perm_k,
+                       pl.sort_ws, pl.sort_ws_bytes, s));
+    HA_TRY(launch_sample_indices(seed, sh.batch, sh.heads, pieces, pieces, seg, sh.samples,
+                                 pl.sidx, s));
+    AttnParams qp = ap;
+    qp.kind = kKindSorted;
+    qp.pieces = pieces;
+    qp.seg = seg;
+    qp.q_first = seg;
+    qp.k_first = 0;
+    qp.stride = 2 * seg;
+    qp.perm_q = pl.perm_q;
+    qp.perm_k = pl.perm_k;
+    qp.b_eff = sh.block < seg ? sh.block : seg;
+    qp.use_block = 1;
+    qp.use_samples = sh.samples > 0;
+    qp.sidx = pl.sidx;
+    qp.m = sh.samples;
+    qp.log2w = sh.samples > 0 ? static_cast<float>(std::log2(static_cast<double>(seg) / sh.samples)) : 0.f;
+    qp.out_mode = kOutMerge;
+    qp.acc_o = pl.acc_o;
+    qp.acc_lse = pl.acc_lse;
+    HA_TRY(launch_attention(qp, HA_K_QUADRANT, s));
+  }
+  return HA_OK;
+}
+
+}  // namespace ha
+
+using namespace ha;
+
+extern "C" {
+
+const char* hyperattn_last_error(void) { return g_last_error.c_str(); }
+
+const char* hyperattn_version(void) { return "hyperattn-gfx950 0.1"; }
+
+size_t hyperattn_workspace_bytes(int batch, int n, int d, int heads, int kv_heads, int block,
+                                 int samples, int proj_bits, int causal, int min_seq_len,
+                                 int dtype, int flags) {
+  Shape sh{batch, n, d, heads, kv_heads, block, samples, proj_bits, causal, min_seq_len, dtype, flags};
+  if (validate(sh) != HA_OK) return 0;
+  return make_plan(sh, nullptr, 0).total;
+}
+
+int hyperattn_forward_ex(const void* q, const void* k, const void* v, int dtype, int batch, int n,
+                         int d, int heads, int kv_heads, int block, int samples, int proj_bits,
+                         int causal, int min_seq_len, uint64_t seed, int flags, void* out,
+                         float* lse, void* workspace, size_t workspace_bytes, void* stream) {
+  g_last_error.clear();
+  Shape sh{batch, n, d, heads, kv_heads, block, samples, proj_bits, causal, min_seq_len, dtype, flags};
+  return forward_impl(q, k, v, sh, seed, out, lse, workspace, workspace_bytes,
+                      static_cast<hipStream_t>(stream));
+}
+
+int hyperattn_forward(const void* q, const void* k, const void* v, int dtype, int batch, int n,
+                      int d, int heads, int kv_heads, int block, int samples, int proj_bits,
+                      int causal, int min_seq_len, uint64_t seed, void* out, float* lse,
+                      void* workspace, size_t workspace_bytes, void* stream) {
+  return hyperattn_forward_ex(q, k, v, dtype, batch, n, d, heads, kv_heads, block, samples,
+                              proj_bits, causal, min_seq_len, seed, 0, out, lse, workspace,
+                              workspace_bytes, stream);
+}
+
+int hyperattn_projections_host(uint64_t seed, int d, int proj_bits, float* host_out) {
+  g_last_error.clear();
+  if (!host_out || d < 1 || proj_bits < 1 || proj_bits > 16) {
+    set_error("projections: bad arguments");
+    return HA_EINVAL;
+  }
+  const int total = d * proj_bits;
+  for (int pi = 0; pi < (total + 1) / 2; ++pi) {
+    float z0, z1;
+    gauss_pair(seed, static_cast<uint32_t>(pi), &z0, &z1);
+    host_out[2 * pi] = z0;
+    if (2 * pi + 1 < total) host_out[2 * pi + 1] = z1;
+  }
+  return HA_OK;
+}
+
+int hyperattn_projections(uint64_t seed, int d, int proj_bits, float* dev_out, void* stream) {
+  g_last_error.clear();
+  if (!dev_out || d < 1 || proj_bits < 1 || proj_bits > 16) {
+    set_error("projections: bad arguments");
+    return HA_EINVAL;
+  }
+  return launch_projections(seed, d, proj_bits, dev_out, static_cast<hipStream_t>(stream));
+}
+
+int hyperattn_hash(const void* x, int dtype, int64_t rows, int d, int proj_bits,
+                   const float* proj_dev, uint16_t* rank_out, void* stream) {
+  g_last_error.clear();
+  if (rows < 0 || (rows > 0 && (!x || !proj_dev || !rank_out)) ||
+      (dtype != HA_BF16 && dtype != HA_F32) || proj_bits < 1 || proj_bits > 16) {
+    set_error("hash: bad arguments");
+    return HA_EINVAL;
+  }
+  if (d != 64 && d != 128) {
+    set_error("hash: head dim %d not built", d);
+    return HA_EUNSUPPORTED;
+  }
+  return launch_hash(x, dtype, rows, d, proj_bits, proj_dev, rank_out,
+                     static_cast<hipStream_t>(stream));
+}
+
+size_t hyperattn_sort_workspace_bytes(int64_t heads, int len, int pieces, int proj_bits) {
+  if (heads < 0 || len < 0 || pieces < 0 || proj_bits < 1 || proj_bits > 16) return 0;
+  return sort_ws_bytes(heads, len, pieces, proj_bits);
+}
+
+int hyperattn_sort(const uint16_t* rank, int64_t heads, int n, int len, int first, int stride,
+                   int pieces, int proj_bits, int32_t* perm_out, void* workspace,
+                   size_t workspace_bytes, void* stream) {
+  g_last_error.clear();
+  if (heads < 0 || n < 0 || len < 0 || first < 0 || stride < 0 || pieces < 0 || proj_bits < 1 ||
+      proj_bits > 16) {
+    set_error("sort: bad arguments");
+    return HA_EINVAL;
+  }
+  if (heads == 0 || len == 0 || pieces == 0) return HA_OK;
+  if (static_cast<int64_t>(first) + static_cast<int64_t>(pieces - 1) * stride + len > n) {
+    set_error("sort: segments run past n");
+    return HA_EINVAL;
+  }
+  if (!rank || !perm_out) {
+    set_error("sort: null pointer");
+    return HA_EINVAL;
+  }
+  return launch_sort(rank, heads, n, len, first, stride, pieces, proj_bits, perm_out, workspace,
+                     workspace_bytes, static_cast<hipStream_t>(stream));
+}
+
+int hyperattn_sample_indices(uint64_t seed, int batch, int heads, int node_first, int node_count,
+                             int ns, int samples, int32_t* idx_out, void* stream) {
+  g_last_error.clear();
+  if (batch < 0 || heads < 0 || node_first < 0 || node_count < 0 || ns < 1 || samples < 0 ||
+      (samples > 0 && batch > 0 && heads > 0 && node_count > 0 && !idx_out)) {
+    set_error("sample_indices: bad arguments");
+    return HA_EINVAL;
+  }
+  return launch_sample_indices(seed, batch, heads, node_first, node_count, ns, samples, idx_out,
+                               static_cast<hipStream_t>(stream));
+}
+
+int hyperattn_gather(const void* src, int dtype, int64_t heads, int n, int d, const int32_t* perm,
+                     int rows_per_head, void* dst, void* stream) {
+  g_last_error.clear();
+  if (heads < 0 || n < 0 || rows_per_head < 0 || (dtype != HA_BF16 && dtype != HA_F32) ||
+      d < 8 || d % 8 || (heads * rows_per_head > 0 && (!src || !perm || !dst))) {
+    set_error("gather: bad arguments");
+    return HA_EINVAL;
+  }
+  return launch_gather(src, dtype, heads, n, d, perm, rows_per_head, dst,
+                       static_cast<hipStream_t>(stream));
+}
+
+int hyperattn_attend(const void* q, const void* k, const void* v, int dtype, int batch, int n,
+                     int d, int heads, int kv_heads, int block, int samples,
+                     const int32_t* perm_q, const int32_t* perm_k, const int32_t* idx, int parts,
+                     float* o_out, float* lse_out, void* stream) {
+  g_last_error.clear();
+  Shape sh{batch, n, d, heads, kv_heads, block, samples, 7, 0, 0, dtype, 0};
+  HA_TRY(validate(sh));
+  if (parts < 1 || parts > 3) {
+    set_error("attend: parts %d outside 1..3", parts);
+    return HA_EINVAL;
+  }
+  if (n == 0 || batch == 0 || heads == 0) return HA_OK;
+  if (!q || !k || !v || !perm_q || !perm_k || !o_out || !lse_out || ((parts & 2) && samples > 0 && !idx)) {
+    set_error("attend: null pointer");
+    return HA_EINVAL;
+  }
+  AttnParams ap;
+  ap.q = q;
+  ap.k = k;
+  ap.v = v;
+  ap.dtype = dtype;
+  ap.d = d;
+  ap.n = n;
+  ap.H = heads;
+  ap.Hkv = kv_heads;
+  ap.BH = batch * heads;
+  ap.kind = kKindSorted;
+  ap.pieces = 1;
+  ap.seg = n;
+  ap.stride = n;
+  ap.perm_q = perm_q;
+  ap.perm_k = perm_k;
+  ap.b_eff = block < n ? block : n;
+  ap.use_block = (parts & 1) ? 1 : 0;
+  ap.use_samples = (parts & 2) ? 1 : 0;
+  ap.sidx = idx;
+  ap.m = samples;
+  ap.log2w = samples > 0 ? static_cast<float>(std::log2(static_cast<double>(n) / samples)) : 0.f;
+  ap.out_mode = kOutPartial;
+  ap.part_o = o_out;
+  ap.part_lse = lse_out;
+  return launch_attention(ap, HA_K_ATTEND, static_cast<hipStream_t>(stream));
+}
+
+int hyperattn_merge_unsort(const float* o1, const float* lse1, const float* o2, const float* lse2,
+                           const int32_t* perm_q, int64_t heads, int n, int d, int dtype,
+                           void* out, float* lse_out, void* stream) {
+  g_last_error.clear();
+  if (heads < 0 || n < 0 || d < 4 || d % 4 || (dtype != HA_BF16 && dtype != HA_F32) ||
+      (heads * n > 0 && (!o1 || !lse1 || !o2 || !lse2 || !perm_q || !out))) {
+    set_error("merge_unsort: bad arguments");
+    return HA_EINVAL;
+  }
+  return launch_merge_unsort(o1, lse1, o2, lse2, perm_q, heads, n, d, dtype, out, lse_out,
+                             static_cast<hipStream_t>(stream));
+}
+
+int hyperattn_causal_leaves(const void* q, const void* k, const void* v, int dtype, int batch,
+                            int n, int d, int heads, int kv_heads, int leaf_len, float* o_out,
+                            float* lse_out, void* stream) {
+  g_last_error.clear();
+  Shape sh{batch, n, d, heads, kv_heads, 1, 0, 7, 0, 0, dtype, 0};
+  HA_TRY(validate(sh));
+  if (leaf_len < 1) {
+    set_error("causal_leaves: leaf_len %d < 1", leaf_len);
+    return HA_EINVAL;
+  }
+  if (n % leaf_len) {
+    set_error("causal_leaves: n %d not a multiple of leaf_len %d", n, leaf_len);
+    return HA_ESHAPE;
+  }
+  if (n == 0 || batch == 0 || heads == 0) return HA_OK;
+  if (!q || !k || !v || !o_out || !lse_out) {
+    set_error("causal_leaves: null pointer");
+    return HA_EINVAL;
+  }
+  AttnParams lp;
+  lp.q = q;
+  lp.k = k;
+  lp.v = v;
+  lp.dtype = dtype;
+  lp.d = d;
+  lp.n = n;
+  lp.H = heads;
+  lp.Hkv = kv_heads;
+  lp.BH = batch * heads;
+  lp.kind = kKindLeaf;
+  lp.pieces = n / leaf_len;
+  lp.seg = leaf_len;
+  lp.stride = leaf_len;
+  lp.b_eff = leaf_len;
+  lp.use_block = 1;
+  lp.use_samples = 0;
+  lp.out_mode = kOutAcc;
+  lp.acc_o = o_out;
+  lp.acc_lse = lse_out;
+  HA_TRY(launch_attention(lp, HA_K_LEAF, static_cast<hipStream_t>(stream)));
+  return HA_OK;
+}
+
+int hyperattn_timing_enable(int enable) {
+  std::lock_guard<std::mutex> lk(g_tmu);
+  for (auto& r : g_recs) {
+    g_event_pool.push_back(r.start);
+    g_event_pool.push_back(r.stop);
+  }
+  g_recs.clear();
+  g_open.clear();
+  g_timing = enable != 0;
+  return HA_OK;
+}
+
+int hyperattn_timing_read(double* ms, int64_t* launches) {
+  std::lock_guard<std::mutex> lk(g_tmu);
+  double acc[HA_K_COUNT] = {0};
+  int64_t cnt[HA_K_COUNT] = {0};
+  for (auto& r : g_recs) {
+    if (hipEventSynchronize(r.stop) != hipSuccess) {
+      set_error("timing: event synchronisation failed");
+      return HA_EHIP;
+    }
+    float t = 0.f;
+    if (hipEventElapsedTime(&t, r.start, r.stop) == hipSuccess) {
+      acc[r.kind] += t;
+      cnt[r.kind] += 1;
+    }
+    g_event_pool.push_back(r.start);
+    g_event_pool.push_back(r.stop);
+  }
+  g_recs.clear();
+  g_open.clear();
+  for (int i = 0; i < HA_K_COUNT; ++i) {
+    if (ms) ms[i] = acc[i];
+    if (launches) launches[i] = cnt[i];
+  }
+  return HA_OK;
+}
+
+}  // extern "C"

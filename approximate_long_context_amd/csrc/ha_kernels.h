@@ -1,0 +1,83 @@
+// Internal launch interface between the host driver and the HIP kernels.
+#pragma once
+
+#include "ha_common.h"
+
+namespace ha {
+
+// ---- timing hooks (ha_api.cpp) -------------------------------------------
+void timing_begin(int kind, hipStream_t s);
+void timing_end(int kind, hipStream_t s);
+
+// ---- projections + hash (ha_hash.hip) ------------------------------------
+int launch_projections(uint64_t seed, int d, int r, float* R, hipStream_t s);
+int launch_hash(const void* x, int dtype, int64_t rows, int d, int r, const float* R,
+                uint16_t* rank, hipStream_t s);
+
+// ---- segmented stable counting sort (ha_sort.hip) ------------------------
+size_t sort_ws_bytes(int64_t heads, int len, int pieces, int r);
+int launch_sort(const uint16_t* rank, int64_t heads, int n, int len, int first, int stride,
+                int pieces, int r, int32_t* perm, void* ws, size_t ws_bytes, hipStream_t s);
+
+// ---- samples, gather, merge (ha_attn.hip) --------------------------------
+int launch_sample_indices(uint64_t seed, int batch, int heads, int node_first, int node_count,
+                          int ns, int m, int32_t* out, hipStream_t s);
+int launch_gather(const void* src, int dtype, int64_t heads, int n, int d, const int32_t* perm,
+                  int rows_per_head, void* dst, hipStream_t s);
+int launch_merge_unsort(const float* o1, const float* l1, const float* o2, const float* l2,
+                        const int32_t* perm, int64_t heads, int n, int d, int dtype, void* out,
+                        float* lse, hipStream_t s);
+
+// ---- attention kernel (ha_attn.hip) --------------------------------------
+enum AttnKind { kKindSorted = 0, kKindLeaf = 1 };
+enum AttnOut {
+  kOutFinal = 0,      // out/lse at the original row (perm_q or identity)
+  kOutPartial = 1,    // fp32 part_o/part_lse at the sorted position
+  kOutLeaf = 2,       // piece 0 -> out/lse, other pieces -> acc (no read)
+  kOutMerge = 3,      // merge with acc at the row; piece 0 -> out/lse, else -> acc
+  kOutAcc = 4         // every piece -> acc at the row (no read)
+};
+
+constexpr int kMaxSamples = 4096;   // sample list staged in LDS
+
+struct AttnParams {
+  const void* q = nullptr;
+  const void* k = nullptr;
+  const void* v = nullptr;
+  int dtype = HA_BF16;
+  int d = 64;
+  int n = 0;             // rows per head in q, k, v
+  int H = 1, Hkv = 1;    // query / kv heads per batch entry
+  int BH = 0;            // batch * H
+  // problems: `pieces` per head, each of `seg` queries and `seg` keys.
+  // Piece i reads query rows q_first + i*stride + [0, seg) and key rows
+  // k_first + i*stride + [0, seg) (through the permutations when given).
+  int pieces = 1;
+  int seg = 0;
+  int q_first = 0, k_first = 0, stride = 0;
+  const int32_t* perm_q = nullptr;   // [BH][pieces][seg]  sorted pos -> row
+  const int32_t* perm_k = nullptr;   // [BHkv][pieces][seg]
+  // materialised sorted copies ([BH or BHkv][pieces*seg][d]); when set,
+  // rows are read at their sorted position and perm_q is used for stores.
+  const void* qs = nullptr;
+  const void* ks = nullptr;
+  const void* vs = nullptr;
+  int kind = kKindSorted;
+  int b_eff = 1;
+  int use_block = 1;
+  int use_samples = 1;
+  const int32_t* sidx = nullptr;     // [BH][pieces][m] sorted key positions
+  int m = 0;
+  float log2w = 0.f;                 // log2(seg / m)
+  int out_mode = kOutFinal;
+  void* out = nullptr;               // [BH][n][d] dtype
+  float* lse = nullptr;              // [BH][n] (may be null for kOutFinal)
+  float* acc_o = nullptr;            // [BH][n][d]
+  float* acc_lse = nullptr;          // [BH][n]
+  float* part_o = nullptr;           // [BH][pieces][seg][d]
+  float* part_lse = nullptr;         // [BH][pieces][seg]
+};
+
+int launch_attention(const AttnParams& p, int timing_kind, hipStream_t s);
+
+}  // namespace ha

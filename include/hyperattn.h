@@ -1,0 +1,279 @@
+/*
+ * hyperattn.h -- C ABI of the MI355X (gfx950) HyperAttention forward pass.
+ *
+ * The method: "HyperAttention: Long-context Attention in Near-Linear Time"
+ * (ICLR 2024).  Sources cited below:
+ *   [S] the atlas.scime.ai research-map summary of that paper, sections
+ *       "Approach", "Limitations", "Experimental setup";
+ *   [A] the OpenReview forum page of that paper, "Abstract".
+ * It approximates softmax attention D^-1 A V, A = exp(Q K^T), D = diag of
+ * the row sums of A ([S] Approach): queries and keys are hashed with
+ * Hamming-sorted LSH and sorted by bucket, attention is exact inside the
+ * equal-size diagonal blocks of the sorted matrix, the mass outside a
+ * row's block is estimated from uniformly sampled key columns, and causal
+ * masking recurses on the two diagonal halves with the off-diagonal
+ * quadrant handled unmasked ([S] summary and Limitations).
+ *
+ * Conventions shared by every entry point
+ * ---------------------------------------
+ *  - Pointers marked "device" are HIP device pointers owned by the caller;
+ *    the library never allocates or frees device memory and keeps no
+ *    device state between calls.  "host" pointers are ordinary memory.
+ *  - `stream` is a hipStream_t (NULL = the default stream).  Device work
+ *    is enqueued on it and the call returns without waiting; errors raised
+ *    while the kernels run surface at the caller's next synchronisation
+ *    (set HYPERATTN_SYNC=1 to wait and check after every stage).
+ *  - Return value: HA_OK (0) or a negative HA_E* code.  Argument errors are
+ *    detected on the host before anything is enqueued, so no output buffer
+ *    is written when one is returned.  hyperattn_last_error() gives a
+ *    thread-local message for the last failure of the calling thread.
+ *  - Tensors are dense, row-major, with the innermost dimension last;
+ *    dtype HA_BF16 (bfloat16) or HA_F32 (float32).
+ *  - A = exp(Q K^T) carries no softmax scale: callers pre-scale Q and K.
+ *  - Results are bitwise deterministic for fixed inputs, sizes and seed.
+ */
+#ifndef HYPERATTN_H
+#define HYPERATTN_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+/* element types */
+enum { HA_BF16 = 0, HA_F32 = 1 };
+
+/* status codes */
+enum {
+  HA_OK = 0,
+  HA_EINVAL = -1,       /* null pointer, negative size, bad enum value       */
+  HA_EUNSUPPORTED = -2, /* valid for the method, not built here (e.g. d=96)  */
+  HA_EWORKSPACE = -3,   /* workspace missing or smaller than required        */
+  HA_ESHAPE = -4,       /* sizes the method cannot split (see forward)       */
+  HA_EHIP = -5          /* a HIP runtime call failed                         */
+};
+
+/* hyperattn_forward_ex flags */
+enum {
+  /* Materialise sorted copies of Q, K, V with hyperattn_gather before the
+   * attention kernel instead of loading rows through the permutations
+   * (non-causal only; same results, more HBM traffic). */
+  HA_FLAG_MATERIALIZE = 1,
+  /* Run the block part, the sampled part and the merge as three kernels
+   * (hyperattn_attend twice, then hyperattn_merge_unsort) instead of one
+   * fused kernel (non-causal only; same results up to fp32 rounding). */
+  HA_FLAG_UNFUSED = 2
+};
+
+/* Thread-local text of the last error returned on this thread ("" if none). */
+const char* hyperattn_last_error(void);
+
+/* Library version string. */
+const char* hyperattn_version(void);
+
+/* ------------------------------------------------------------------------
+ * Whole forward pass
+ * ------------------------------------------------------------------------ */
+
+/*
+ * Bytes of device workspace hyperattn_forward / hyperattn_forward_ex need
+ * for these sizes.  Returns 0 for sizes that forward would reject.
+ */
+size_t hyperattn_workspace_bytes(int batch, int n, int d, int heads, int kv_heads,
+                                 int block, int samples, int proj_bits, int causal,
+                                 int min_seq_len, int dtype, int flags);
+
+/*
+ * HyperAttention forward ([S] Approach; causal recursion [S] summary and
+ * Limitations).
+ *
+ *   q    device, [batch, heads,    n, d] of dtype
+ *   k, v device, [batch, kv_heads, n, d] of dtype; query head h uses KV head
+ *        h / (heads / kv_heads)
+ *   out  device, [batch, heads, n, d] of dtype, written in full
+ *   lse  device, [batch, heads, n] float32, natural log of the row's
+ *        estimated normaliser D; may be NULL
+ *   workspace  device, >= hyperattn_workspace_bytes(...) bytes, 256-byte
+ *        aligned; its contents on entry do not matter
+ *
+ * Method parameters: block b (rows per diagonal block), samples m (uniform
+ * key columns per problem), proj_bits r in [1, 16] (hash bits), causal,
+ * min_seq_len s (causal leaf length bound), seed (64-bit Philox key of
+ * the projections and the samples).
+ *
+ * Readings taken where the pages are silent: one Gaussian projection
+ * matrix per call shared by Q, K, every head and every recursion node;
+ * bucket order = position in the reflected-binary Gray sequence of the
+ * sign code; stable sort (ties by original row); m samples iid uniform
+ * with replacement over the problem's sorted key positions, shared by its
+ * rows, drawn per query head, excluded for rows whose block holds them,
+ * weight ns/m; the product with V re-uses those samples; non-causal calls
+ * ignore min_seq_len; causal spans of length <= s are exact causal
+ * attention and longer spans split into halves.
+ *
+ * Errors: HA_EINVAL for null q/k/v/out/workspace (when needed), batch,
+ * n, heads, kv_heads < 0 or heads % kv_heads != 0, samples < 0, block < 1,
+ * proj_bits outside [1, 16], bad dtype; HA_EUNSUPPORTED for d not in
+ * {64, 128} or flags combined with causal; HA_ESHAPE when n (non-causal)
+ * or a causal quadrant length is not a multiple of min(block, length), or
+ * a causal span longer than s has odd length; HA_EWORKSPACE when
+ * workspace_bytes is too small.  n == 0 or batch == 0 returns HA_OK and
+ * writes nothing.
+ */
+int hyperattn_forward(const void* q, const void* k, const void* v, int dtype,
+                      int batch, int n, int d, int heads, int kv_heads,
+                      int block, int samples, int proj_bits, int causal, int min_seq_len,
+                      uint64_t seed, void* out, float* lse,
+                      void* workspace, size_t workspace_bytes, void* stream);
+
+/* As hyperattn_forward, with HA_FLAG_* flags. */
+int hyperattn_forward_ex(const void* q, const void* k, const void* v, int dtype,
+                         int batch, int n, int d, int heads, int kv_heads,
+                         int block, int samples, int proj_bits, int causal, int min_seq_len,
+                         uint64_t seed, int flags, void* out, float* lse,
+                         void* workspace, size_t workspace_bytes, void* stream);
+
+/* ------------------------------------------------------------------------
+ * Stages of the forward, exported for parity checks and timing.  The
+ * forward calls the same kernels.
+ * ------------------------------------------------------------------------ */
+
+/*
+ * Projection matrix R of the sortLSH hash ([S] Approach, "Hamming-sorted
+ * LSH"; [A] Abstract, LSH finds the large entries): float32 [proj_bits][d],
+ * Gaussian by Box-Muller from Philox4x32-10 words (counter (e/4, 0, 0, 0)
+ * for element e = p*d + col, key = seed).
+ *   _host: host_out is host memory of proj_bits*d floats, computed on the
+ *          host with the same arithmetic as the device kernel.
+ *   plain: dev_out is device memory; enqueued on stream.
+ * Errors: HA_EINVAL for null output, d < 1, proj_bits outside [1, 16].
+ */
+int hyperattn_projections_host(uint64_t seed, int d, int proj_bits, float* host_out);
+int hyperattn_projections(uint64_t seed, int d, int proj_bits, float* dev_out, void* stream);
+
+/*
+ * Bucket rank of each row of x ([S] Approach, Hamming-sorted LSH):
+ * bit p of the code is 1 iff <x_row, R_p> > 0, the dot product taken in
+ * fp32 with every product rounded, the d products cut into groups of 8
+ * consecutive elements, each group summed by halving (pairs 4, 2, 1
+ * apart) and the group sums by halving; rank = position of the code in
+ * the reflected-binary Gray sequence.
+ *   x         device, [rows, d] of dtype (d in {64, 128})
+ *   proj_dev  device, float32 [proj_bits, d] (from hyperattn_projections)
+ *   rank_out  device, uint16 [rows]
+ * Errors: HA_EINVAL (null pointers, rows < 0, bad dtype, proj_bits outside
+ * [1, 16]); HA_EUNSUPPORTED (d not in {64, 128}).
+ */
+int hyperattn_hash(const void* x, int dtype, int64_t rows, int d, int proj_bits,
+                   const float* proj_dev, uint16_t* rank_out, void* stream);
+
+/*
+ * Stable segmented sort of bucket ranks ([S] Approach: rows are sorted by
+ * bucket; ties keep their original order).  The ranks are uint16
+ * [heads, n]; segment i of head hd covers rows
+ * first + i*stride ... first + i*stride + len - 1 of that head, for
+ * i < pieces.  perm_out (device, int32 [heads, pieces, len]) receives, for
+ * each sorted position, the row index (within the head, 0..n-1) of the
+ * element that lands there.  proj_bits <= 8 takes one counting pass,
+ * 9..16 two.  Workspace: hyperattn_sort_workspace_bytes(...) bytes.
+ * Errors: HA_EINVAL (null pointers, negative sizes, segments outside
+ * [0, n)), HA_EWORKSPACE.
+ */
+size_t hyperattn_sort_workspace_bytes(int64_t heads, int len, int pieces, int proj_bits);
+int hyperattn_sort(const uint16_t* rank, int64_t heads, int n, int len, int first,
+                   int stride, int pieces, int proj_bits, int32_t* perm_out,
+                   void* workspace, size_t workspace_bytes, void* stream);
+
+/*
+ * Uniform sample positions ([S] Approach: uniform column sampling):
+ * for batch b < batch, query head h < heads and node
+ * node_first + j (j < node_count), `samples` positions in [0, ns):
+ * word i of Philox counters (i/4, node, h, 2b+1) under seed, mapped to
+ * floor(word * ns / 2^32).  idx_out: device int32
+ * [batch, heads, node_count, samples].
+ * Errors: HA_EINVAL (null output with samples > 0, negative sizes, ns < 1).
+ */
+int hyperattn_sample_indices(uint64_t seed, int batch, int heads, int node_first,
+                             int node_count, int ns, int samples, int32_t* idx_out,
+                             void* stream);
+
+/*
+ * Permutation gather: dst[hd, j, :] = src[hd, perm[hd*rows_per_head + j], :]
+ * for hd < heads, j < rows_per_head; src [heads, n, d], dst
+ * [heads, rows_per_head, d], both device, of dtype.  (Sorted copies of
+ * Q, K, V, [S] Approach.)  Errors: HA_EINVAL.
+ */
+int hyperattn_gather(const void* src, int dtype, int64_t heads, int n, int d,
+                     const int32_t* perm, int rows_per_head, void* dst, void* stream);
+
+/*
+ * One part of a non-causal problem per (batch, head), in sorted order
+ * ([S] Approach: exact masked row sums over the diagonal blocks; the
+ * uniform column samples for the rest).
+ *   parts = 1: block part -- sorted query p attends the sorted keys of its
+ *              block, positions [t b', (t+1) b'), t = p / b', b' = min(block, n);
+ *   parts = 2: sampled part -- the sorted keys at idx (device int32
+ *              [batch, heads, samples]) except those in the row's block,
+ *              each with weight n / samples;
+ *   parts = 3: both in one softmax (the forward's fused kernel).
+ *   perm_q device int32 [batch*heads, n], perm_k [batch*kv_heads, n]:
+ *          sorted position -> original row (from hyperattn_sort).
+ *   o_out  device float32 [batch, heads, n, d], lse_out float32
+ *          [batch, heads, n]: normalised output and natural-log mass of
+ *          that part at each *sorted* position (lse = -inf, o = 0 when no
+ *          key is left).
+ * Errors: as hyperattn_forward for the shared arguments; HA_EINVAL for
+ * parts outside 1..3.
+ */
+int hyperattn_attend(const void* q, const void* k, const void* v, int dtype,
+                     int batch, int n, int d, int heads, int kv_heads,
+                     int block, int samples, const int32_t* perm_q, const int32_t* perm_k,
+                     const int32_t* idx, int parts, float* o_out, float* lse_out,
+                     void* stream);
+
+/*
+ * Log-sum-exp merge of two parts and unsort: for each head and sorted
+ * position p, lse = ln(e^lse1 + e^lse2), o = o1 e^(lse1-lse) + o2 e^(lse2-lse),
+ * written to row perm_q[hd*n + p] of out (dtype, [heads, n, d]) and of
+ * lse_out (float32 [heads, n], may be NULL).  Inputs float32 [heads, n, d]
+ * and [heads, n], all device.  Errors: HA_EINVAL.
+ */
+int hyperattn_merge_unsort(const float* o1, const float* lse1, const float* o2,
+                           const float* lse2, const int32_t* perm_q, int64_t heads,
+                           int n, int d, int dtype, void* out, float* lse_out,
+                           void* stream);
+
+/*
+ * Exact causal attention inside consecutive leaves of leaf_len rows (the
+ * recursion's fallback below min_seq_len): row i of leaf [a, a+leaf_len)
+ * attends keys a..i.  o_out float32 [batch, heads, n, d], lse_out float32
+ * [batch, heads, n], device.  Errors: HA_EINVAL; HA_ESHAPE when n is not a
+ * multiple of leaf_len.
+ */
+int hyperattn_causal_leaves(const void* q, const void* k, const void* v, int dtype,
+                            int batch, int n, int d, int heads, int kv_heads,
+                            int leaf_len, float* o_out, float* lse_out, void* stream);
+
+/* ------------------------------------------------------------------------
+ * Timing hooks (used by the benchmark): when enabled, the forward records
+ * a pair of HIP events around each kernel launch on its stream and sums
+ * the elapsed times per kernel class on the next hyperattn_timing_read.
+ * ------------------------------------------------------------------------ */
+enum {
+  HA_K_PROJ = 0, HA_K_HASH, HA_K_SORT, HA_K_SAMPLES, HA_K_GATHER,
+  HA_K_ATTEND, HA_K_MERGE, HA_K_LEAF, HA_K_QUADRANT, HA_K_COUNT
+};
+/* Enable (1) or disable (0) event timing; clears the accumulators. */
+int hyperattn_timing_enable(int enable);
+/* Synchronises the recorded events, then fills ms[HA_K_COUNT] (total
+ * milliseconds per kernel class) and launches[HA_K_COUNT] (launch counts)
+ * since the last enable, and clears them.  Either pointer may be NULL. */
+int hyperattn_timing_read(double* ms, int64_t* launches);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* HYPERATTN_H */

@@ -1,0 +1,117 @@
+"""C-ABI checks that need no GPU: the library loads, exports every entry
+point declared in include/hyperattn.h, its host projection routine equals
+the oracle bit for bit, and invalid arguments return the documented codes
+before anything is enqueued (null device pointers are passed: a call that
+got past validation would fail differently)."""
+
+import ctypes
+import os
+import re
+
+import numpy as np
+import pytest
+import torch
+
+import approximate_long_context_amd as ha
+import oracle
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+
+
+def _declared_functions():
+    text = open(os.path.join(ROOT, "include", "hyperattn.h")).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b(hyperattn_\w+)\s*\(", text)))
+
+
+def test_exports_every_declared_symbol():
+    names = _declared_functions()
+    assert len(names) >= 15
+    lib = ha.lib()
+    for name in names:
+        assert hasattr(lib, name), name
+    assert ha.version().startswith("hyperattn")
+
+
+@pytest.mark.parametrize("d,r", [(64, 7), (128, 8), (64, 16), (128, 1), (8, 3), (100, 5)])
+def test_host_projections_equal_oracle(d, r):
+    for seed in list(range(25)) + [2**63 + 12345, 2**64 - 1]:
+        got = ha.projections_host(seed, d, r).numpy()
+        assert np.array_equal(got, oracle.projections(seed, d, r)), (seed, d, r)
+
+
+def _fwd(**kw):
+    args = dict(q=None, k=None, v=None, dtype=ha.HA_BF16, batch=1, n=1024, d=64, heads=4, kv_heads=2,
+                block=64, samples=16, proj_bits=7, causal=0, min_seq_len=0, seed=0, flags=0,
+                out=None, lse=None, ws=None, wsb=1 << 30, stream=None)
+    args.update(kw)
+    a = args
+    return ha.lib().hyperattn_forward_ex(a["q"], a["k"], a["v"], a["dtype"], a["batch"], a["n"], a["d"],
+                                         a["heads"], a["kv_heads"], a["block"], a["samples"],
+                                         a["proj_bits"], a["causal"], a["min_seq_len"], a["seed"],
+                                         a["flags"], a["out"], a["lse"], a["ws"], a["wsb"], a["stream"])
+
+
+@pytest.mark.parametrize("kw,code", [
+    (dict(dtype=7), ha.HA_EINVAL),
+    (dict(heads=3, kv_heads=2), ha.HA_EINVAL),
+    (dict(kv_heads=0), ha.HA_EINVAL),
+    (dict(block=0), ha.HA_EINVAL),
+    (dict(samples=-1), ha.HA_EINVAL),
+    (dict(proj_bits=0), ha.HA_EINVAL),
+    (dict(proj_bits=17), ha.HA_EINVAL),
+    (dict(n=-5), ha.HA_EINVAL),
+    (dict(d=96), ha.HA_EUNSUPPORTED),
+    (dict(n=1000, block=64), ha.HA_ESHAPE),
+    (dict(causal=1, min_seq_len=0), ha.HA_EINVAL),
+    (dict(causal=1, n=1000, min_seq_len=100, block=64), ha.HA_ESHAPE),
+    (dict(causal=1, n=96, min_seq_len=4, block=8), ha.HA_ESHAPE),
+    (dict(causal=1, min_seq_len=128, flags=1), ha.HA_EUNSUPPORTED),
+    (dict(flags=8), ha.HA_EINVAL),
+    (dict(samples=5000), ha.HA_EUNSUPPORTED),
+    (dict(), ha.HA_EINVAL),                    # null q/k/v/out
+])
+def test_forward_argument_errors(kw, code):
+    assert _fwd(**kw) == code
+    assert ha.lib().hyperattn_last_error().decode() != ""
+
+
+def test_forward_workspace_error_and_empty():
+    dummy = ctypes.c_void_p(256)   # never dereferenced: validation fails first
+    assert _fwd(q=dummy, k=dummy, v=dummy, out=dummy, ws=dummy, wsb=16) == ha.HA_EWORKSPACE
+    assert _fwd(q=dummy, k=dummy, v=dummy, out=dummy, ws=None, wsb=0) == ha.HA_EWORKSPACE
+    assert _fwd(n=0) == ha.HA_OK
+    assert _fwd(batch=0) == ha.HA_OK
+
+
+def test_workspace_bytes():
+    nb = ha.workspace_bytes(1, 131072, 64, 32, 32, 256, 256, 7)
+    cb = ha.workspace_bytes(1, 131072, 64, 32, 32, 256, 256, 7, True, 4096)
+    assert nb > 32 * 131072 * 12 and cb > 32 * 131072 * 64 * 4
+    assert ha.workspace_bytes(1, 1000, 64, 1, 1, 64, 4, 7) == 0      # rejected shape
+    big = ha.workspace_bytes(1, 4096, 64, 2, 2, 64, 4, 7, flags=ha.HA_FLAG_MATERIALIZE | ha.HA_FLAG_UNFUSED)
+    assert big > ha.workspace_bytes(1, 4096, 64, 2, 2, 64, 4, 7) + 3 * 2 * 4096 * 64 * 2
+
+
+def test_stage_argument_errors():
+    L = ha.lib()
+    assert L.hyperattn_projections_host(0, 64, 0, None) == ha.HA_EINVAL
+    assert L.hyperattn_hash(None, ha.HA_BF16, 10, 64, 7, None, None, None) == ha.HA_EINVAL
+    assert L.hyperattn_hash(ctypes.c_void_p(256), ha.HA_BF16, 10, 96, 7, ctypes.c_void_p(256),
+                            ctypes.c_void_p(256), None) == ha.HA_EUNSUPPORTED
+    assert L.hyperattn_sort(None, 2, 100, 60, 50, 60, 1, 7, None, None, 0, None) == ha.HA_EINVAL
+    assert L.hyperattn_sample_indices(0, 1, 1, 1, 1, 0, 4, None, None) == ha.HA_EINVAL
+    assert L.hyperattn_gather(None, ha.HA_BF16, 1, 10, 64, None, 10, None, None) == ha.HA_EINVAL
+    assert L.hyperattn_causal_leaves(None, None, None, ha.HA_BF16, 1, 100, 64, 1, 1, 30, None, None,
+                                     None) == ha.HA_ESHAPE
+    assert L.hyperattn_merge_unsort(None, None, None, None, None, 1, 10, 64, ha.HA_BF16, None, None,
+                                    None) == ha.HA_EINVAL
+    assert L.hyperattn_attend(None, None, None, ha.HA_BF16, 1, 64, 64, 1, 1, 64, 4, None, None, None, 4,
+                              None, None, None) == ha.HA_EINVAL
+
+
+def test_binding_fails_loudly_without_library(monkeypatch):
+    monkeypatch.setattr(ha, "_lib", None)
+    monkeypatch.setattr(ha, "LIB_PATH", "/nonexistent/libhyperattn.so")
+    with pytest.raises(RuntimeError):
+        ha.lib()
