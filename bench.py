@@ -1,0 +1,246 @@
+"""Benchmark of the HyperAttention forward on one MI355X.
+
+One step = one non-causal forward plus one causal forward (min_seq_len
+4096) of a single attention layer at n = 131072: batch 1, 32 heads, d = 64,
+bf16, block 256, 256 sampled columns, 7 hash bits, planted large entries
+(1% of key rows are noisy copies of query rows).  Inputs are generated on
+the GPU before timing and stay resident.
+
+Prints one JSON line.  ``value`` is the effective throughput of the step:
+algorithmic FLOPs (4 d B H n (b + m) per non-causal pass; for the causal
+pass the same per level over n/2 query rows plus 4 d B H (n/s) s(s+1)/2 for
+the exact leaves) divided by the measured step time.  ``roofline`` is taken
+for the kernel class with the largest share of the step, timed by HIP
+events recorded around each of its launches on the launch stream.
+``cpu_baseline`` times the CPU oracle on one of the 32 heads of the same
+workload (both passes) and scales it to the same unit.
+"""
+
+import argparse
+import hashlib
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+HBM_PEAK_GBS = 8000.0            # MI355X HBM3E, GB/s
+MFMA_BF16_PEAK_TFLOPS = 2500.0   # MI355X dense bf16 MFMA, TFLOP/s
+MFMA_FP32_PEAK_TFLOPS = 157.3
+
+
+def alg_flops(w, causal):
+    """Algorithmic FLOPs of one forward (the work the method must do)."""
+    d, BH, n, m = w.d, w.batch * w.heads, w.n, w.samples
+    if not causal:
+        b = min(w.block, n)
+        return 4.0 * d * BH * n * (b + m), {"attend": 4.0 * d * BH * n * (b + m)}
+    s = w.min_seq_len
+    ns, levels = n, []
+    while ns > s:
+        ns //= 2
+        levels.append(ns)
+    leaf = ns
+    quad = sum(4.0 * d * BH * (n / 2) * (min(w.block, seg) + m) for seg in levels)
+    leaves = 4.0 * d * BH * (n / leaf) * leaf * (leaf + 1) / 2
+    return quad + leaves, {"quadrant": quad, "leaf": leaves}
+
+
+def alg_bytes(w, causal):
+    """Algorithmic HBM bytes per kernel class for one forward."""
+    e = 2 if str(w.dtype).endswith("bfloat16") else 4
+    BH, BK, n, d = w.batch * w.heads, w.batch * w.kv_heads, w.n, w.d
+    out = {"hash": (BH + BK) * n * (d * e + 2)}
+    if not causal:
+        out["sort"] = (BH + BK) * n * (2 + 2 + 4)        # hist read, scatter read, perm write
+    else:
+        L = 0
+        ns = n
+        while ns > w.min_seq_len:
+            ns //= 2
+            L += 1
+        out["sort"] = L * (BH + BK) * (n // 2) * (2 + 2 + 4)
+    return out
+
+
+def cpu_baseline(w_nc, w_c, q, k, v):
+    """Time the oracle on head 0 of both passes; returns the baseline dict."""
+    import numpy as np
+    import oracle
+    from oracle.hyperattn import HAConfig
+    try:
+        from threadpoolctl import threadpool_info
+        threads = max([p.get("num_threads", 1) for p in threadpool_info()] or [1])
+    except Exception:
+        threads = os.cpu_count()
+    qh = q[:, :1].float().cpu().numpy()
+    kh = k[:, :1].float().cpu().numpy()
+    vh = v[:, :1].float().cpu().numpy()
+    flops = 0.0
+    t0 = time.perf_counter()
+    for w in (w_nc, w_c):
+        cfg = HAConfig(block=w.block, samples=w.samples, proj_bits=w.proj_bits, causal=w.causal,
+                       min_seq_len=w.min_seq_len, seed=w.seed)
+        oracle.forward(qh, kh, vh, cfg)
+        f, _ = alg_flops(w.with_(heads=1, kv_heads=1), w.causal)
+        flops += f
+    dt = time.perf_counter() - t0
+    return {"value": flops / dt / 1e12, "unit": "TFLOP/s", "cores": int(threads), "kind": "oracle",
+            "sample": f"head 0 of 32, all {w_nc.n} rows, non-causal + causal passes, fp64 numpy; "
+                      f"{dt:.1f} s on {os.cpu_count()} host CPUs", "seconds": dt}
+
+
+def traffic_record(kernel_class):
+    """HBM bytes per launch measured by rocprofv3 counters, if the summary in
+    profiles/ was taken on the current kernel source."""
+    path = os.path.join(ROOT, "profiles", "traffic_long131k.json")
+    if not os.path.exists(path):
+        return None
+    rec = json.load(open(path))
+    src = os.path.join(ROOT, "approximate_long_context_amd", "csrc", "ha_attn.hip")
+    sha = hashlib.sha256(open(src, "rb").read()).hexdigest()
+    entry = rec.get("kernels", {}).get(kernel_class)
+    if entry is None or entry.get("source_sha256") != sha:
+        return None
+    return entry.get("bytes_per_launch")
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=10)
+    ap.add_argument("--warmup", type=int, default=3)
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--workload", default="long131k")
+    args = ap.parse_args()
+    if args.gpus != 1:
+        print(f"bench.py runs on one GPU only (asked for {args.gpus}); each head is an independent "
+              "problem, so more GPUs would split the heads with no communication.", file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+    import approximate_long_context_amd as ha
+    from approximate_long_context_amd.workloads import WORKLOADS, make_inputs
+
+    dev = torch.device("cuda:0")
+    w_nc = WORKLOADS[args.workload]
+    w_c = WORKLOADS.get(args.workload + "_causal", w_nc.with_(causal=True))
+    q, k, v = make_inputs(w_nc, dev)
+    out = torch.empty_like(q)
+    lse = torch.empty(q.shape[:3], dtype=torch.float32, device=dev)
+    wsb = max(ha.workspace_bytes(w.batch, w.n, w.d, w.heads, w.kv_heads, w.block, w.samples, w.proj_bits,
+                                 w.causal, w.min_seq_len, w.dtype) for w in (w_nc, w_c))
+    ws = torch.empty(wsb, dtype=torch.uint8, device=dev)
+
+    def step():
+        ha.forward(q, k, v, out=out, lse=lse, workspace=ws, **w_nc.method_args())
+        ha.forward(q, k, v, out=out, lse=lse, workspace=ws, **w_c.method_args())
+
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+
+    stream = torch.cuda.current_stream(dev)
+    ev0 = torch.cuda.Event(enable_timing=True)
+    ev1 = torch.cuda.Event(enable_timing=True)
+    ha.timing_enable(True)
+    torch.cuda.synchronize()
+    ev0.record(stream)
+    t0 = time.perf_counter()
+    for _ in range(args.steps):
+        step()
+    ev1.record(stream)
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    per_kernel = ha.timing_read()
+    ha.timing_enable(False)
+    ms_total = ev0.elapsed_time(ev1)
+    ms_step = ms_total / args.steps
+
+    # separate per-pass timing (untimed for `value`, reported for context)
+    pass_ms = {}
+    for name, w in (("noncausal", w_nc), ("causal", w_c)):
+        e0 = torch.cuda.Event(enable_timing=True)
+        e1 = torch.cuda.Event(enable_timing=True)
+        e0.record(stream)
+        for _ in range(args.steps):
+            ha.forward(q, k, v, out=out, lse=lse, workspace=ws, **w.method_args())
+        e1.record(stream)
+        torch.cuda.synchronize()
+        pass_ms[name] = e0.elapsed_time(e1) / args.steps
+
+    f_nc, parts_nc = alg_flops(w_nc, False)
+    f_c, parts_c = alg_flops(w_c, True)
+    flops_step = f_nc + f_c
+    value = flops_step / (ms_step * 1e-3) / 1e12
+
+    # dominant kernel class and its roofline
+    kflops = {"attend": parts_nc["attend"], "leaf": parts_c["leaf"], "quadrant": parts_c["quadrant"]}
+    bytes_nc, bytes_c = alg_bytes(w_nc, False), alg_bytes(w_c, True)
+    kbytes = {"hash": bytes_nc["hash"] + bytes_c["hash"], "sort": bytes_nc["sort"] + bytes_c["sort"]}
+    breakdown = {}
+    for name, (ms, cnt) in per_kernel.items():
+        if cnt:
+            breakdown[name] = {"ms_per_step": ms / args.steps, "launches_per_step": cnt / args.steps,
+                               "avg_launch_ms": ms / cnt}
+    dom = max(breakdown, key=lambda kname: breakdown[kname]["ms_per_step"])
+    ms_dom, cnt_dom = per_kernel[dom]
+    launches = cnt_dom / args.steps
+    if dom in kflops:
+        per_launch = kflops[dom] / launches
+        achieved = per_launch / (ms_dom / cnt_dom * 1e-3) / 1e12
+        roof = {"bound": "mfma", "achieved": achieved, "peak": MFMA_BF16_PEAK_TFLOPS, "unit": "TFLOP/s",
+                "frac": achieved / MFMA_BF16_PEAK_TFLOPS, "kernel": dom,
+                "work_per_launch": per_launch, "avg_launch_ms": ms_dom / cnt_dom}
+    else:
+        per_launch = kbytes[dom] / launches
+        achieved = per_launch / (ms_dom / cnt_dom * 1e-3) / 1e9
+        roof = {"bound": "hbm", "achieved": achieved, "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                "frac": achieved / HBM_PEAK_GBS, "kernel": dom,
+                "work_per_launch": per_launch, "avg_launch_ms": ms_dom / cnt_dom}
+    roof["traffic"] = traffic_record(dom)
+    for name in breakdown:
+        if name in kflops:
+            tot = kflops[name]
+            breakdown[name]["tflops"] = tot / (breakdown[name]["ms_per_step"] * 1e-3) / 1e12
+        if name in kbytes:
+            breakdown[name]["gbs"] = kbytes[name] / (breakdown[name]["ms_per_step"] * 1e-3) / 1e9
+
+    result = {
+        "metric": "HyperAttention fwd ms + effective TFLOP/s at n=131072, 32 heads, causal/non",
+        "value": value,
+        "unit": "TFLOP/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": ms_step,
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16",
+        "data": "synthetic",
+        "config": {"workload": f"{w_nc.name}: one attention layer, batch {w_nc.batch}, {w_nc.heads} heads, "
+                               f"n={w_nc.n}, d={w_nc.d}, bf16, block {w_nc.block}, samples {w_nc.samples}, "
+                               f"r={w_nc.proj_bits}; step = non-causal + causal (min_seq_len "
+                               f"{w_c.min_seq_len}) forward",
+                   "batch": w_nc.batch, "heads": w_nc.heads, "seq_len": w_nc.n, "head_dim": w_nc.d,
+                   "parallelism": "single GPU"},
+        "ms_noncausal": pass_ms["noncausal"],
+        "ms_causal": pass_ms["causal"],
+        "tflops_noncausal": f_nc / (pass_ms["noncausal"] * 1e-3) / 1e12,
+        "tflops_causal": f_c / (pass_ms["causal"] * 1e-3) / 1e12,
+        "wall_s_timed": wall,
+        "roofline": roof,
+        "kernels": breakdown,
+    }
+    if not args.no_cpu_baseline:
+        result["cpu_baseline"] = cpu_baseline(w_nc, w_c, q, k, v)
+    else:
+        result["cpu_baseline"] = None
+    print(json.dumps(result))
+
+
+if __name__ == "__main__":
+    main()
