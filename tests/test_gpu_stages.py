@@ -139,9 +139,11 @@ def test_attend_parts_match_oracle(dtype, n, d, block, m, H, Hkv):
         lse_t, o_t = oh.lse_merge(parts["lse_blk"], parts["o_blk"], ls, parts["o_smp"])
         compare(np32(o3[0, h]), o_t, dtype, "fused parts")
         compare_lse(np32(l3[0, h]), lse_t, dtype, "fused lse")
-        # mass invariant on the GPU: exp(lse) = exp(lse_blk) + exp(lse_smp)
+        # mass invariant on the GPU: exp(lse) = exp(lse_blk) + exp(lse_smp).
+        # bf16: the kernel sums the bf16-rounded P it multiplies V with, so
+        # each of the three lse values carries up to 2^-9 relative error.
         gl = np.logaddexp(np32(l1[0, h]).astype(np.float64), np32(l2[0, h]).astype(np.float64))
-        assert np.max(np.abs(gl - np32(l3[0, h]))) < (1e-5 if dtype == torch.float32 else 1e-4)
+        assert np.max(np.abs(gl - np32(l3[0, h]))) < (1e-5 if dtype == torch.float32 else 3 * 2.0**-9)
         del tol
     # merge + unsort kernel reproduces the fused result
     out, lse = ha.merge_unsort(res[1][0].view(H, n, d), res[1][1].view(H, n), res[2][0].view(H, n, d),
