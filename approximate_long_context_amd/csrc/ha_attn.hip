@@ -224,10 +224,22 @@ __global__ __launch_bounds__(64 * NW, 2) void attn_kernel(AttnParams p) {
   constexpr int JSTEP = G::NT / G::CPR;
   uint4v kreg[G::CPT], vreg[G::CPT];
 
+  // leaf rows are contiguous: per-thread base + a uniform step per tile
+  const T* kleaf = kbase + static_cast<int64_t>(krow0 + j_first) * D + G::EPC * c_in_row;
+  const T* vleaf = vbase + static_cast<int64_t>(krow0 + j_first) * D + G::EPC * c_in_row;
   auto load_tile = [&](int it) {
     const bool isB = it >= nA;
     const int kb = isB ? (it - nA) * kKT : ka0 + it * kKT;
     const int kcnt = isB ? min(kKT, nsamp - kb) : min(kKT, ka1 - kb);
+    if (LEAF && kcnt == kKT) {
+#pragma unroll
+      for (int c = 0; c < G::CPT; ++c) {
+        const int64_t off = static_cast<int64_t>(kb + c * JSTEP) * D;
+        kreg[c] = *reinterpret_cast<const uint4v*>(kleaf + off);
+        vreg[c] = *reinterpret_cast<const uint4v*>(vleaf + off);
+      }
+      return;
+    }
 #pragma unroll
     for (int c = 0; c < G::CPT; ++c) {
       const int j = j_first + c * JSTEP;
@@ -338,11 +350,15 @@ __global__ __launch_bounds__(64 * NW, 2) void attn_kernel(AttnParams p) {
       }
     }
 
-    // ---- online softmax (per query tile) ------------------------------------------
+    // ---- online softmax ------------------------------------------------------------
+    // All weights of a row are taken relative to one running reference
+    // mrun (log2 units, sample weight included), raised when a tile's
+    // maximum exceeds it by more than 2^8.  For the causal leaves the tile
+    // maximum is only computed when no reference exists yet or when a
+    // tile's fresh weights sum above 2^15 on some lane; otherwise the
+    // weights are used as they are (exact either way, and bounded).
     const float bias = isB ? p.log2w : 0.f;
-    float off[NQT];
-#pragma unroll
-    for (int u = 0; u < NQT; ++u) {
+    auto tile_max_raise = [&](int u) {
       float mx0 = fmaxf(s[0][u][0], s[0][u][1]), mx1 = fmaxf(s[1][u][0], s[1][u][1]);
 #pragma unroll
       for (int r = 2; r < 16; ++r) {
@@ -363,12 +379,19 @@ __global__ __launch_bounds__(64 * NW, 2) void attn_kernel(AttnParams p) {
         lsum[u] *= alpha;
         mrun[u] = mnew;
       }
-      off[u] = bias - (mrun[u] == -INFINITY ? 0.f : mrun[u]);
-    }
+    };
 
     // ---- P, row sums and O^T += V^T P^T -----------------------------------------
-    if constexpr (BF) {
+    if constexpr (BF && !LEAF) {
+      // sorted problems (gather-bound, occupancy-sensitive): maximum every
+      // tile, exponentials interleaved with the P V MFMAs chunk by chunk
       const bf16x2 ones = {static_cast<bf16>(1.f), static_cast<bf16>(1.f)};
+      float off[NQT];
+#pragma unroll
+      for (int u = 0; u < NQT; ++u) {
+        tile_max_raise(u);
+        off[u] = bias - (mrun[u] == -INFINITY ? 0.f : mrun[u]);
+      }
 #pragma unroll
       for (int c16 = 0; c16 < 4; ++c16) {
         const int kt = c16 >> 1;
@@ -376,17 +399,17 @@ __global__ __launch_bounds__(64 * NW, 2) void attn_kernel(AttnParams p) {
         bf16x8 pb[NQT];
 #pragma unroll
         for (int u = 0; u < NQT; ++u) {
-          float ls = 0.f;
+          float l = 0.f;
 #pragma unroll
           for (int i = 0; i < 8; i += 2) {
             const float e0 = fast_exp2(fmaf(s[kt][u][8 * hi + i], kLog2e, off[u]));
             const float e1 = fast_exp2(fmaf(s[kt][u][8 * hi + i + 1], kLog2e, off[u]));
             const bf16x2 two = __builtin_convertvector((float __attribute__((ext_vector_type(2)))){e0, e1}, bf16x2);
-            ls = __builtin_amdgcn_fdot2_f32_bf16(two, ones, ls, false);
+            l = __builtin_amdgcn_fdot2_f32_bf16(two, ones, l, false);
             pb[u][i] = two[0];
             pb[u][i + 1] = two[1];
           }
-          lsum[u] += ls;
+          lsum[u] += l;
         }
 #pragma unroll
         for (int t = 0; t < NDT; ++t) {
@@ -400,12 +423,62 @@ __global__ __launch_bounds__(64 * NW, 2) void attn_kernel(AttnParams p) {
             o[u][t] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(va, pb[u], o[u][t], 0, 0, 0);
         }
       }
+    } else if constexpr (BF) {
+      // causal leaves (compute-bound): maximum only when needed
+      const bf16x2 ones = {static_cast<bf16>(1.f), static_cast<bf16>(1.f)};
+      bf16x8 pb[4][NQT];
+      float ls[NQT];
+      auto make_p = [&](int u) {
+        const float off = bias - (mrun[u] == -INFINITY ? 0.f : mrun[u]);
+        float l0 = 0.f, l1 = 0.f;
+#pragma unroll
+        for (int c16 = 0; c16 < 4; ++c16) {
+          const int kt = c16 >> 1;
+          const int hi = c16 & 1;
+#pragma unroll
+          for (int i = 0; i < 8; i += 2) {
+            const float e0 = fast_exp2(fmaf(s[kt][u][8 * hi + i], kLog2e, off));
+            const float e1 = fast_exp2(fmaf(s[kt][u][8 * hi + i + 1], kLog2e, off));
+            const bf16x2 two = __builtin_convertvector((float __attribute__((ext_vector_type(2)))){e0, e1}, bf16x2);
+            if (i & 2) l1 = __builtin_amdgcn_fdot2_f32_bf16(two, ones, l1, false);
+            else l0 = __builtin_amdgcn_fdot2_f32_bf16(two, ones, l0, false);
+            pb[c16][u][i] = two[0];
+            pb[c16][u][i + 1] = two[1];
+          }
+        }
+        ls[u] = l0 + l1;
+      };
+#pragma unroll
+      for (int u = 0; u < NQT; ++u) {
+        if (mrun[u] == -INFINITY) tile_max_raise(u);
+        make_p(u);
+        if (__any(!(ls[u] <= 32768.f))) {        // reference too low (or no reference)
+          tile_max_raise(u);
+          make_p(u);
+        }
+        lsum[u] += ls[u];
+      }
+#pragma unroll
+      for (int c16 = 0; c16 < 4; ++c16)
+#pragma unroll
+        for (int t = 0; t < NDT; ++t) {
+          const T* vp = vs + (16 * c16 + tr_key) * G::VSTR + 32 * t + tr_col;
+          const short4v lo = lds_read_tr16(vp);
+          const short4v hv = lds_read_tr16(vp + 8 * G::VSTR);
+          const short __attribute__((ext_vector_type(8))) va8 = {lo[0], lo[1], lo[2], lo[3], hv[0], hv[1], hv[2], hv[3]};
+          const bf16x8 va = __builtin_bit_cast(bf16x8, va8);
+#pragma unroll
+          for (int u = 0; u < NQT; ++u)
+            o[u][t] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(va, pb[c16][u], o[u][t], 0, 0, 0);
+        }
     } else {
+      tile_max_raise(0);
+      const float off = bias - (mrun[0] == -INFINITY ? 0.f : mrun[0]);
 #pragma unroll
       for (int kt = 0; kt < 2; ++kt)
 #pragma unroll
         for (int jr = 0; jr < 16; ++jr) {
-          const float e = fast_exp2(fmaf(s[kt][0][jr], kLog2e, off[0]));
+          const float e = fast_exp2(fmaf(s[kt][0][jr], kLog2e, off));
           lsum[0] += e;
           const int key = 32 * kt + 8 * (jr >> 2) + 4 * h2 + (jr & 3);
 #pragma unroll
