@@ -49,19 +49,28 @@ def alg_flops(w, causal):
 
 
 def alg_bytes(w, causal):
-    """Algorithmic HBM bytes per kernel class for one forward."""
+    """Algorithmic HBM bytes per kernel class for one forward: every input
+    row the kernel needs read once, every output written once, the causal
+    accumulator read and written once per merge (fp32 values + lse)."""
     e = 2 if str(w.dtype).endswith("bfloat16") else 4
     BH, BK, n, d = w.batch * w.heads, w.batch * w.kv_heads, w.n, w.d
+    row, acc = d * e, d * 4 + 4
     out = {"hash": (BH + BK) * n * (d * e + 2)}
     if not causal:
-        out["sort"] = (BH + BK) * n * (2 + 2 + 4)        # hist read, scatter read, perm write
-    else:
-        L = 0
-        ns = n
-        while ns > w.min_seq_len:
-            ns //= 2
-            L += 1
-        out["sort"] = L * (BH + BK) * (n // 2) * (2 + 2 + 4)
+        out["sort"] = (BH + BK) * n * (2 + 2 + 4)          # hist read, scatter read, perm write
+        out["attend"] = (BH * n * (row + 4 + 4)             # Q row, its perm entry, lse
+                         + BK * n * (2 * row + 4)           # K and V rows, perm entry
+                         + BH * n * row)                    # output row
+        return out
+    L, ns = 0, n
+    while ns > w.min_seq_len:
+        ns //= 2
+        L += 1
+    out["sort"] = L * (BH + BK) * (n // 2) * (2 + 2 + 4)
+    half = n // 2
+    out["quadrant"] = L * (BH * half * (row + 4 + 2 * acc)  # Q row, perm, accumulator read + write
+                           + BK * half * (2 * row + 4))    # K and V rows, perm
+    out["leaf"] = BH * n * row + 2 * BK * n * row + BH * n * acc
     return out
 
 
@@ -93,16 +102,18 @@ def cpu_baseline(w_nc, w_c, q, k, v):
 
 
 def traffic_record(kernel_class):
-    """HBM bytes per launch measured by rocprofv3 counters, if the summary in
-    profiles/ was taken on the current kernel source."""
+    """HBM bytes per launch measured by rocprofv3 counters (profiles/
+    traffic_long131k.json), if they were taken on the current kernel source."""
     path = os.path.join(ROOT, "profiles", "traffic_long131k.json")
     if not os.path.exists(path):
         return None
     rec = json.load(open(path))
-    src = os.path.join(ROOT, "approximate_long_context_amd", "csrc", "ha_attn.hip")
-    sha = hashlib.sha256(open(src, "rb").read()).hexdigest()
     entry = rec.get("kernels", {}).get(kernel_class)
-    if entry is None or entry.get("source_sha256") != sha:
+    if entry is None:
+        return None
+    src = "ha_hash.hip" if kernel_class == "hash" else "ha_sort.hip" if kernel_class == "sort" else "ha_attn.hip"
+    sha = hashlib.sha256(open(os.path.join(ROOT, "approximate_long_context_amd", "csrc", src), "rb").read()).hexdigest()
+    if entry.get("source_sha256") != sha:
         return None
     return entry.get("bytes_per_launch")
 
@@ -188,10 +199,15 @@ def main():
     flops_step = f_nc + f_c
     value = flops_step / (ms_step * 1e-3) / 1e12
 
-    # dominant kernel class and its roofline
+    # dominant kernel class and its roofline (HBM-bound when the kernel's
+    # algorithmic intensity is below the MFMA/HBM ridge)
     kflops = {"attend": parts_nc["attend"], "leaf": parts_c["leaf"], "quadrant": parts_c["quadrant"]}
     bytes_nc, bytes_c = alg_bytes(w_nc, False), alg_bytes(w_c, True)
-    kbytes = {"hash": bytes_nc["hash"] + bytes_c["hash"], "sort": bytes_nc["sort"] + bytes_c["sort"]}
+    kbytes = {}
+    for dct in (bytes_nc, bytes_c):
+        for kname, b in dct.items():
+            kbytes[kname] = kbytes.get(kname, 0) + b
+    ridge = MFMA_BF16_PEAK_TFLOPS * 1e12 / (HBM_PEAK_GBS * 1e9)
     breakdown = {}
     for name, (ms, cnt) in per_kernel.items():
         if cnt:
@@ -201,18 +217,22 @@ def main():
     dom = max(modelled, key=lambda kname: breakdown[kname]["ms_per_step"])
     ms_dom, cnt_dom = per_kernel[dom]
     launches = cnt_dom / args.steps
-    if dom in kflops:
+    avg_s = ms_dom / cnt_dom * 1e-3
+    intensity = kflops[dom] / kbytes[dom] if dom in kflops else 0.0
+    if dom in kflops and intensity >= ridge:
         per_launch = kflops[dom] / launches
-        achieved = per_launch / (ms_dom / cnt_dom * 1e-3) / 1e12
+        achieved = per_launch / avg_s / 1e12
         roof = {"bound": "mfma", "achieved": achieved, "peak": MFMA_BF16_PEAK_TFLOPS, "unit": "TFLOP/s",
-                "frac": achieved / MFMA_BF16_PEAK_TFLOPS, "kernel": dom,
-                "work_per_launch": per_launch, "avg_launch_ms": ms_dom / cnt_dom}
+                "frac": achieved / MFMA_BF16_PEAK_TFLOPS}
     else:
         per_launch = kbytes[dom] / launches
-        achieved = per_launch / (ms_dom / cnt_dom * 1e-3) / 1e9
+        achieved = per_launch / avg_s / 1e9
         roof = {"bound": "hbm", "achieved": achieved, "peak": HBM_PEAK_GBS, "unit": "GB/s",
-                "frac": achieved / HBM_PEAK_GBS, "kernel": dom,
-                "work_per_launch": per_launch, "avg_launch_ms": ms_dom / cnt_dom}
+                "frac": achieved / HBM_PEAK_GBS}
+    roof.update({"kernel": dom, "work_per_launch": per_launch, "avg_launch_ms": ms_dom / cnt_dom,
+                 "intensity_flop_per_byte": intensity, "ridge_flop_per_byte": ridge})
+    if dom in kflops:
+        roof["mfma_tflops"] = kflops[dom] / launches / avg_s / 1e12
     roof["traffic"] = traffic_record(dom)
     for name in breakdown:
         if name in kflops:
