@@ -21,17 +21,18 @@
 // Work split: a workgroup of NW waves owns 32*NW consecutive sorted queries
 // (32 per wave).  Keys stream through LDS in tiles of 64, double buffered:
 // the next tile's rows are loaded into registers while the current one is
-// computed, then written to the other buffer; one barrier per tile.  Per
-// wave and tile, S^T = K Q^T (64 keys x 32 queries) is built with MFMA, so
-// each lane owns one query column (lanes l and l+32 share query l%32 and
-// hold different keys).  The softmax runs on those registers, P^T is
-// packed into the B operand of O^T = V^T P^T, and O^T (d x 32) stays in
-// registers.  bf16 uses v_mfma_f32_32x32x16_bf16 with V stored transposed
-// in LDS (keys permuted inside 16-key chunks so that one 16-byte LDS read
-// is one operand) and row sums taken from the packed bf16 P with
-// v_dot2_f32_bf16; fp32 uses v_mfma_f32_32x32x2_f32.  Accumulation and
-// softmax are fp32.  The running maximum is only raised when a tile
-// exceeds it by more than 2^8, and then the accumulators are rescaled.
+// computed, then written to the other buffer; one barrier per tile.  The
+// key rows of a sorted problem (block keys and the samples that count) are
+// listed in LDS once per workgroup, so a tile load is one global access per
+// row.  Per wave and tile, S^T = K Q^T (64 keys x 32 queries) is built with
+// MFMA, so each lane owns one query column (lanes l and l+32 share query
+// l%32 and hold different keys).  The softmax runs on those registers, P^T
+// is packed into the B operand of O^T = V^T P^T, and O^T (d x 32) stays in
+// registers.  bf16 uses v_mfma_f32_32x32x16_bf16 with V row-major in LDS,
+// read as the A operand with the transposing LDS read (ds_read_b64_tr_b16;
+// keys permuted inside 16-key chunks to match P), and row sums taken from
+// the packed bf16 P with v_dot2_f32_bf16; fp32 uses
+// v_mfma_f32_32x32x2_f32.  Accumulation and softmax are fp32.
 //
 // Per query and key the kernel does 4 d MFMA flops (Q K^T and P V) and
 // reads each of its K/V rows once per workgroup; Q rows are read once.
@@ -73,6 +74,10 @@ struct Geo {
   static_assert(QPW == 32 || (QPW == 64 && BF), "64 queries per wave: bf16 only");
 };
 
+// LDS bytes after the two K/V buffers (sorted problems): brow[bcap],
+// srow[m], spos[m], rrow[m] and one count per 64 samples.
+__host__ __device__ constexpr int list_bytes(int bcap, int m) { return 4 * (bcap + 3 * m + (m + 63) / 64); }
+
 __device__ __forceinline__ int xcd_remap(int bid, int nblocks) {
   // Dispatch places workgroup i on XCD i % 8; give each XCD a contiguous
   // range of logical tiles so tiles that share keys share an L2.
@@ -94,8 +99,15 @@ __device__ __forceinline__ short4v lds_read_tr16(const void* p) {
   return __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_short4v*)(const_cast<void*>(p)));
 }
 
+// Minimum waves per SIMD the register allocation must allow: the sorted
+// problems are gather-bound and need 4 (<= 128 VGPRs) where that fits.
+template <typename T, int D, int KIND, int NW, int QPW>
+constexpr int min_waves() {
+  return (KIND == kKindSorted && sizeof(T) == 2 && D == 64 && NW == 8 && QPW == 32) ? 4 : 2;
+}
+
 template <typename T, int D, int KIND, int OUT, int NW, int QPW>
-__global__ __launch_bounds__(64 * NW, 2) void attn_kernel(AttnParams p) {
+__global__ __launch_bounds__(64 * NW, (min_waves<T, D, KIND, NW, QPW>())) void attn_kernel(AttnParams p) {
   typedef Geo<T, D, NW, QPW> G;
   constexpr bool BF = G::BF;
   constexpr int NQT = G::NQT;
@@ -104,7 +116,6 @@ __global__ __launch_bounds__(64 * NW, 2) void attn_kernel(AttnParams p) {
   constexpr int NDT = D / 32;           // O^T tiles per query tile
   constexpr bool LEAF = KIND == kKindLeaf;
   extern __shared__ __attribute__((aligned(16))) char smem[];
-  int* slist = reinterpret_cast<int*>(smem + 2 * G::BUF);
 
   const int tid = threadIdx.x;
   const int lane = tid & 63;
@@ -155,44 +166,70 @@ __global__ __launch_bounds__(64 * NW, 2) void attn_kernel(AttnParams p) {
   const bool samp = !LEAF && p.use_samples && p.m > 0;
   const bool samp_multi = samp && multi_block;
 
-  // ---- sample list (compacted when all rows share one block) ----------------
+  // row of k/v (or of the sorted copies) holding sorted key position kp
+  auto key_row = [&](int kp) -> int { return mat ? kp : (pk ? pk[kp] : krow0 + kp); };
+
+  // ---- key row lists (sorted problems) -------------------------------------------
+  // Staged in LDS once per workgroup so that loading a tile costs one global
+  // access per row: brow = rows of the block keys [ka0, ka1) (when bcap > 0)
+  // and srow = rows of the samples that count for the workgroup's rows.
+  // When all rows share one block, the samples inside it are dropped from
+  // the list (compacted in sample order); otherwise every sample is kept
+  // and spos (sorted positions) serves the per-row mask.
+  int* brow = reinterpret_cast<int*>(smem + 2 * G::BUF);
+  int* srow = brow + p.bcap;
+  int* spos = srow + p.m;
+  int* rrow = spos + p.m;                 // rows before compaction
+  int* ccount = rrow + p.m;               // kept samples per 64
+  const bool blist = !LEAF && p.bcap > 0;
   int nsamp = 0;
-  if (samp) {
-    const int32_t* si = p.sidx + qpiece * p.m;
-    if (!samp_multi) {
-      if (wave == 0) {
-        const int tq = q0 / p.b_eff;
-        int run = 0;
-        for (int c = 0; c < p.m; c += 64) {
+  if (!LEAF) {
+    if (blist)
+      for (int j = tid; j < ka1 - ka0; j += G::NT) brow[j] = key_row(ka0 + j);
+    if (samp) {
+      const int32_t* si = p.sidx + qpiece * p.m;
+      const int tq = q0 / p.b_eff;
+      int* raw = samp_multi ? srow : rrow;
+      for (int c = 64 * wave; c < p.m; c += G::NT) {
+        const int i = c + lane;
+        const int sp = i < p.m ? si[i] : 0;
+        if (i < p.m) {
+          spos[i] = sp;
+          raw[i] = key_row(sp);
+        }
+        const uint64_t keep = __ballot(i < p.m && (samp_multi || (sp / p.b_eff) != tq));
+        if (lane == 0) ccount[c / 64] = __popcll(keep);
+      }
+      __syncthreads();
+      const int nchunk = (p.m + 63) / 64;
+      for (int k = 0; k < nchunk; ++k) nsamp += ccount[k];
+      if (!samp_multi) {
+        for (int c = 64 * wave; c < p.m; c += G::NT) {
+          int base = 0;
+          for (int k = 0; k < c / 64; ++k) base += ccount[k];
           const int i = c + lane;
-          const int s = i < p.m ? si[i] : 0;
-          const bool keep = i < p.m && (s / p.b_eff) != tq;
+          const bool keep = i < p.m && (spos[i] / p.b_eff) != tq;
           const uint64_t bal = __ballot(keep);
           const uint64_t lower = lane == 0 ? 0ull : (~0ull >> (64 - lane));
-          if (keep) slist[run + __popcll(bal & lower)] = s;
-          run += __popcll(bal);
+          if (keep) srow[base + __popcll(bal & lower)] = rrow[i];
         }
-        if (lane == 0) slist[p.m] = run;
       }
-    } else {
-      for (int i = tid; i < p.m; i += G::NT) slist[i] = si[i];
-      if (tid == 0) slist[p.m] = p.m;
     }
-    __syncthreads();
-    nsamp = slist[p.m];
+    if (blist || samp) __syncthreads();
   }
 
   // ---- query fragments ----------------------------------------------------------
-  int ql[NQT];
+  int ql[NQT], orow[NQT];   // query (sorted / local position) and its original row
   typedef typename std::conditional<BF, bf16x8, float>::type QF;
   QF qf[NQT][NQF];
 #pragma unroll
   for (int u = 0; u < NQT; ++u) {
-    ql[u] = wq0 + 32 * u + col;                // this lane's query (sorted / local position)
+    ql[u] = wq0 + 32 * u + col;
     const int qls = ql[u] < qend ? ql[u] : q0;
+    orow[u] = pq ? pq[qls] : qrow0 + qls;
     const T* qrow;
     if (mat) qrow = static_cast<const T*>(p.qs) + (qpiece * p.seg + qls) * D;
-    else qrow = qbase + static_cast<int64_t>(pq ? pq[qls] : qrow0 + qls) * D;
+    else qrow = qbase + static_cast<int64_t>(orow[u]) * D;
 #pragma unroll
     for (int c = 0; c < NQF; ++c) {
       if constexpr (BF) qf[u][c] = *reinterpret_cast<const bf16x8*>(qrow + 16 * c + 8 * h2);
@@ -245,18 +282,10 @@ __global__ __launch_bounds__(64 * NW, 2) void attn_kernel(AttnParams p) {
       const int j = j_first + c * JSTEP;
       uint4v kw = {0u, 0u, 0u, 0u}, vw = {0u, 0u, 0u, 0u};
       if (j < kcnt) {
-        const int kp = isB ? slist[kb + j] : kb + j;
-        const T *kr, *vr;
-        if (mat) {
-          kr = ksb + static_cast<int64_t>(kp) * D;
-          vr = vsb + static_cast<int64_t>(kp) * D;
-        } else {
-          const int64_t row = pk ? pk[kp] : krow0 + kp;
-          kr = kbase + row * D;
-          vr = vbase + row * D;
-        }
-        kw = *reinterpret_cast<const uint4v*>(kr + G::EPC * c_in_row);
-        vw = *reinterpret_cast<const uint4v*>(vr + G::EPC * c_in_row);
+        const int row = isB ? srow[kb + j] : (blist ? brow[kb - ka0 + j] : key_row(kb + j));
+        const int64_t off = static_cast<int64_t>(row) * D + G::EPC * c_in_row;
+        kw = *reinterpret_cast<const uint4v*>((mat ? ksb : kbase) + off);
+        vw = *reinterpret_cast<const uint4v*>((mat ? vsb : vbase) + off);
       }
       kreg[c] = kw;
       vreg[c] = vw;
@@ -301,192 +330,344 @@ __global__ __launch_bounds__(64 * NW, 2) void attn_kernel(AttnParams p) {
     const T* ks = reinterpret_cast<const T*>(smem + buf * G::BUF);
     const T* vs = reinterpret_cast<const T*>(smem + buf * G::BUF + G::KBYTES);
 
-    // ---- S^T = K Q^T for 64 keys x QPW queries -------------------------------
-    floatx16 s[2][NQT];
+    if constexpr (BF && NQT == 1) {
+      // ---- bf16, one 32-query tile per wave: half-tile pipeline ------------------
+      // Keys [0, 32) and [32, 64) of the tile are two halves.  The S^T MFMAs
+      // of the second half do not depend on the softmax of the first, nor
+      // the P V MFMAs of the first half on the softmax of the second, so
+      // each pair is issued alternately (on gfx950 this hides only part of
+      // the matrix time: the two units largely take turns within a SIMD).
+      // Weights are taken against the running reference mrun
+      // as it stands; a half is redone after raising mrun only when some
+      // lane's weights of that half sum above 2^15 (or no reference exists
+      // yet), which bounds every weight while keeping the result exact.
+      const bf16x2 ones = {static_cast<bf16>(1.f), static_cast<bf16>(1.f)};
+      const float bias = isB ? p.log2w : 0.f;
+      const bool diag = LEAF && (kb + kKT - 1 > wq0);
+      const bool need_mask = kcnt < kKT || (isB ? samp_multi : (multi_block || diag));
+      const int row_blk = ql[0] / p.b_eff;
+
+      auto k_read = [&](int kt, int c) {
+        return *reinterpret_cast<const bf16x8*>(&ks[(32 * kt + col) * G::KSTR + 16 * c + 8 * h2]);
+      };
+      auto v_read = [&](int c16, int t) {
+        const T* vp = vs + (16 * c16 + tr_key) * G::VSTR + 32 * t + tr_col;
+        const short4v lo = lds_read_tr16(vp);
+        const short4v hv = lds_read_tr16(vp + 8 * G::VSTR);
+        const short __attribute__((ext_vector_type(8))) va8 = {lo[0], lo[1], lo[2], lo[3], hv[0], hv[1], hv[2], hv[3]};
+        return __builtin_bit_cast(bf16x8, va8);
+      };
+      auto mask_half = [&](int kt, floatx16& sv) {
 #pragma unroll
-    for (int kt = 0; kt < 2; ++kt) {
-#pragma unroll
-      for (int u = 0; u < NQT; ++u)
-#pragma unroll
-        for (int r = 0; r < 16; ++r) s[kt][u][r] = 0.f;
-#pragma unroll
-      for (int c = 0; c < NQF; ++c) {
-        if constexpr (BF) {
-          const bf16x8 ka = *reinterpret_cast<const bf16x8*>(&ks[(32 * kt + col) * G::KSTR + 16 * c + 8 * h2]);
-#pragma unroll
-          for (int u = 0; u < NQT; ++u)
-            s[kt][u] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ka, qf[u][c], s[kt][u], 0, 0, 0);
+        for (int r = 0; r < 16; ++r) {
+          const int j = 32 * kt + 8 * (r >> 2) + 4 * h2 + (r & 3);
+          bool ok = j < kcnt;
+          if (isB) {
+            if (samp_multi) ok = ok && (spos[kb + min(j, kcnt - 1)] / p.b_eff) != row_blk;
+          } else if (LEAF) {
+            ok = ok && (kb + j <= ql[0]);
+          } else if (multi_block) {
+            ok = ok && ((kb + j) / p.b_eff) == row_blk;
+          }
+          if (!ok) sv[r] = -INFINITY;
+        }
+      };
+      auto offset = [&]() { return bias - (mrun[0] == -INFINITY ? 0.f : mrun[0]); };
+      // weights of S elements i, i+1 into the B operands of the half's two
+      // 16-key chunks (elements 0..7 -> pa, 8..15 -> pb), summed into l
+      auto p_pair = [&](const floatx16& sv, int i, float off, bf16x8& pa, bf16x8& pb, float& l) {
+        const float e0 = fast_exp2(fmaf(sv[i], kLog2e, off));
+        const float e1 = fast_exp2(fmaf(sv[i + 1], kLog2e, off));
+        const bf16x2 two = __builtin_convertvector((float __attribute__((ext_vector_type(2)))){e0, e1}, bf16x2);
+        l = __builtin_amdgcn_fdot2_f32_bf16(two, ones, l, false);
+        if (i < 8) {
+          pa[i] = two[0];
+          pa[i + 1] = two[1];
         } else {
-          const float ka = ks[(32 * kt + col) * G::KSTR + 2 * c + h2];
+          pb[i - 8] = two[0];
+          pb[i - 7] = two[1];
+        }
+      };
+      auto raise_half = [&](const floatx16& sv) {
+        float mx = fmaxf(sv[0], sv[1]);
 #pragma unroll
-          for (int u = 0; u < NQT; ++u)
-            s[kt][u] = __builtin_amdgcn_mfma_f32_32x32x2f32(ka, qf[u][c], s[kt][u], 0, 0, 0);
+        for (int r = 2; r < 16; ++r) mx = fmaxf(mx, sv[r]);
+        mx = fmaxf(mx, __shfl_xor(mx, 32));
+        const float tmax = mx * kLog2e + bias;
+        const bool raise = tmax > mrun[0] + kRescale;
+        if (__any(raise)) {
+          const float mnew = raise ? fmaxf(mrun[0], tmax) : mrun[0];
+          const float alpha = (mnew == mrun[0]) ? 1.f : fast_exp2(mrun[0] - mnew);
+#pragma unroll
+          for (int t = 0; t < NDT; ++t)
+#pragma unroll
+            for (int r = 0; r < 16; ++r) o[0][t][r] *= alpha;
+          lsum[0] *= alpha;
+          mrun[0] = mnew;
+        }
+      };
+      // rare path: some lane's weights of the half outgrew the reference
+      auto settle = [&](const floatx16& sv, bf16x8& pa, bf16x8& pb, float& l) {
+        if (__any(!(l <= 32768.f) || mrun[0] == -INFINITY)) {
+          raise_half(sv);
+          const float off = offset();
+          l = 0.f;
+#pragma unroll
+          for (int i = 0; i < 16; i += 2) p_pair(sv, i, off, pa, pb, l);
+        }
+        lsum[0] += l;
+      };
+
+      // phase 1: S^T of keys [0, 32)
+      floatx16 s0, s1;
+#pragma unroll
+      for (int r = 0; r < 16; ++r) s0[r] = s1[r] = 0.f;
+#pragma unroll
+      for (int c = 0; c < NQF; ++c) s0 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(k_read(0, c), qf[0][c], s0, 0, 0, 0);
+      if (need_mask) mask_half(0, s0);
+
+      // phase 2: S^T of keys [32, 64), each MFMA followed by a share of the
+      // weights of keys [0, 32).  Written out in issue order; the
+      // scheduling fences keep the compiler from regrouping it.
+      bf16x8 pa, pb;
+      float l0 = 0.f;
+      {
+        const float off = offset();
+        constexpr int kPer = 16 / NQF;
+        bf16x8 ka = k_read(1, 0);
+#pragma unroll
+        for (int c = 0; c < NQF; ++c) {
+          bf16x8 kn = ka;
+          if (c + 1 < NQF) kn = k_read(1, c + 1);
+          s1 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ka, qf[0][c], s1, 0, 0, 0);
+          __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+          for (int i = kPer * c; i < kPer * (c + 1); i += 2) p_pair(s0, i, off, pa, pb, l0);
+          __builtin_amdgcn_sched_barrier(0);
+          ka = kn;
         }
       }
-    }
+      settle(s0, pa, pb, l0);
+      if (need_mask) mask_half(1, s1);
 
-    // ---- masks -------------------------------------------------------------------
-    const bool diag = LEAF && (kb + kKT - 1 > wq0);
-    const bool need_mask = kcnt < kKT || (isB ? samp_multi : (multi_block || diag));
-    if (need_mask) {
+      // phase 3: P V of keys [0, 32), each MFMA followed by a share of the
+      // weights of keys [32, 64)
+      bf16x8 pc, pd;
+      float l1 = 0.f;
+      {
+        const float off = offset();
+        constexpr int kSteps = 2 * NDT;
+        constexpr int kPer = 16 / kSteps;
+        bf16x8 va = v_read(0, 0);
 #pragma unroll
-      for (int u = 0; u < NQT; ++u) {
-        const int row_blk = ql[u] / p.b_eff;
+        for (int st = 0; st < kSteps; ++st) {
+          const int c16 = st / NDT, t = st % NDT;
+          bf16x8 vn = va;
+          if (st + 1 < kSteps) vn = v_read((st + 1) / NDT, (st + 1) % NDT);
+          o[0][t] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(va, c16 == 0 ? pa : pb, o[0][t], 0, 0, 0);
+          __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
-        for (int kt = 0; kt < 2; ++kt)
+          for (int i = kPer * st; i < kPer * (st + 1); i += 2) p_pair(s1, i, off, pc, pd, l1);
+          __builtin_amdgcn_sched_barrier(0);
+          va = vn;
+        }
+      }
+      settle(s1, pc, pd, l1);
+
+      // phase 4: P V of keys [32, 64)
 #pragma unroll
-          for (int r = 0; r < 16; ++r) {
-            const int j = 32 * kt + 8 * (r >> 2) + 4 * h2 + (r & 3);
-            bool ok = j < kcnt;
-            if (isB) {
-              if (samp_multi) ok = ok && (slist[kb + min(j, kcnt - 1)] / p.b_eff) != row_blk;
-            } else if (LEAF) {
-              ok = ok && (kb + j <= ql[u]);
-            } else if (multi_block) {
-              ok = ok && ((kb + j) / p.b_eff) == row_blk;
-            }
-            if (!ok) s[kt][u][r] = -INFINITY;
+      for (int st = 0; st < 2 * NDT; ++st) {
+        const int c16 = 2 + st / NDT, t = st % NDT;
+        o[0][t] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(v_read(c16, t), c16 == 2 ? pc : pd, o[0][t], 0, 0, 0);
+      }
+    } else {
+      // ---- S^T = K Q^T for 64 keys x QPW queries -------------------------------
+      floatx16 s[2][NQT];
+  #pragma unroll
+      for (int kt = 0; kt < 2; ++kt) {
+  #pragma unroll
+        for (int u = 0; u < NQT; ++u)
+  #pragma unroll
+          for (int r = 0; r < 16; ++r) s[kt][u][r] = 0.f;
+  #pragma unroll
+        for (int c = 0; c < NQF; ++c) {
+          if constexpr (BF) {
+            const bf16x8 ka = *reinterpret_cast<const bf16x8*>(&ks[(32 * kt + col) * G::KSTR + 16 * c + 8 * h2]);
+  #pragma unroll
+            for (int u = 0; u < NQT; ++u)
+              s[kt][u] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ka, qf[u][c], s[kt][u], 0, 0, 0);
+          } else {
+            const float ka = ks[(32 * kt + col) * G::KSTR + 2 * c + h2];
+  #pragma unroll
+            for (int u = 0; u < NQT; ++u)
+              s[kt][u] = __builtin_amdgcn_mfma_f32_32x32x2f32(ka, qf[u][c], s[kt][u], 0, 0, 0);
           }
+        }
       }
-    }
 
-    // ---- online softmax ------------------------------------------------------------
-    // All weights of a row are taken relative to one running reference
-    // mrun (log2 units, sample weight included), raised when a tile's
-    // maximum exceeds it by more than 2^8.  For the causal leaves the tile
-    // maximum is only computed when no reference exists yet or when a
-    // tile's fresh weights sum above 2^15 on some lane; otherwise the
-    // weights are used as they are (exact either way, and bounded).
-    const float bias = isB ? p.log2w : 0.f;
-    auto tile_max_raise = [&](int u) {
-      float mx0 = fmaxf(s[0][u][0], s[0][u][1]), mx1 = fmaxf(s[1][u][0], s[1][u][1]);
-#pragma unroll
-      for (int r = 2; r < 16; ++r) {
-        mx0 = fmaxf(mx0, s[0][u][r]);
-        mx1 = fmaxf(mx1, s[1][u][r]);
-      }
-      float mx = fmaxf(mx0, mx1);
-      mx = fmaxf(mx, __shfl_xor(mx, 32));
-      const float tmax = mx * kLog2e + bias;
-      const bool raise = tmax > mrun[u] + kRescale;
-      if (__any(raise)) {
-        const float mnew = raise ? fmaxf(mrun[u], tmax) : mrun[u];
-        const float alpha = (mnew == mrun[u]) ? 1.f : fast_exp2(mrun[u] - mnew);
-#pragma unroll
-        for (int t = 0; t < NDT; ++t)
-#pragma unroll
-          for (int r = 0; r < 16; ++r) o[u][t][r] *= alpha;
-        lsum[u] *= alpha;
-        mrun[u] = mnew;
-      }
-    };
-
-    // ---- P, row sums and O^T += V^T P^T -----------------------------------------
-    if constexpr (BF && !LEAF) {
-      // sorted problems (gather-bound, occupancy-sensitive): maximum every
-      // tile, exponentials interleaved with the P V MFMAs chunk by chunk
-      const bf16x2 ones = {static_cast<bf16>(1.f), static_cast<bf16>(1.f)};
-      float off[NQT];
-#pragma unroll
-      for (int u = 0; u < NQT; ++u) {
-        tile_max_raise(u);
-        off[u] = bias - (mrun[u] == -INFINITY ? 0.f : mrun[u]);
-      }
-#pragma unroll
-      for (int c16 = 0; c16 < 4; ++c16) {
-        const int kt = c16 >> 1;
-        const int hi = c16 & 1;
-        bf16x8 pb[NQT];
-#pragma unroll
+      // ---- masks -------------------------------------------------------------------
+      const bool diag = LEAF && (kb + kKT - 1 > wq0);
+      const bool need_mask = kcnt < kKT || (isB ? samp_multi : (multi_block || diag));
+      if (need_mask) {
+  #pragma unroll
         for (int u = 0; u < NQT; ++u) {
-          float l = 0.f;
-#pragma unroll
-          for (int i = 0; i < 8; i += 2) {
-            const float e0 = fast_exp2(fmaf(s[kt][u][8 * hi + i], kLog2e, off[u]));
-            const float e1 = fast_exp2(fmaf(s[kt][u][8 * hi + i + 1], kLog2e, off[u]));
-            const bf16x2 two = __builtin_convertvector((float __attribute__((ext_vector_type(2)))){e0, e1}, bf16x2);
-            l = __builtin_amdgcn_fdot2_f32_bf16(two, ones, l, false);
-            pb[u][i] = two[0];
-            pb[u][i + 1] = two[1];
-          }
-          lsum[u] += l;
-        }
-#pragma unroll
-        for (int t = 0; t < NDT; ++t) {
-          const T* vp = vs + (16 * c16 + tr_key) * G::VSTR + 32 * t + tr_col;
-          const short4v lo = lds_read_tr16(vp);
-          const short4v hv = lds_read_tr16(vp + 8 * G::VSTR);
-          const short __attribute__((ext_vector_type(8))) va8 = {lo[0], lo[1], lo[2], lo[3], hv[0], hv[1], hv[2], hv[3]};
-          const bf16x8 va = __builtin_bit_cast(bf16x8, va8);
-#pragma unroll
-          for (int u = 0; u < NQT; ++u)
-            o[u][t] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(va, pb[u], o[u][t], 0, 0, 0);
+          const int row_blk = ql[u] / p.b_eff;
+  #pragma unroll
+          for (int kt = 0; kt < 2; ++kt)
+  #pragma unroll
+            for (int r = 0; r < 16; ++r) {
+              const int j = 32 * kt + 8 * (r >> 2) + 4 * h2 + (r & 3);
+              bool ok = j < kcnt;
+              if (isB) {
+                if (samp_multi) ok = ok && (spos[kb + min(j, kcnt - 1)] / p.b_eff) != row_blk;
+              } else if (LEAF) {
+                ok = ok && (kb + j <= ql[u]);
+              } else if (multi_block) {
+                ok = ok && ((kb + j) / p.b_eff) == row_blk;
+              }
+              if (!ok) s[kt][u][r] = -INFINITY;
+            }
         }
       }
-    } else if constexpr (BF) {
-      // causal leaves (compute-bound): maximum only when needed
-      const bf16x2 ones = {static_cast<bf16>(1.f), static_cast<bf16>(1.f)};
-      bf16x8 pb[4][NQT];
-      float ls[NQT];
-      auto make_p = [&](int u) {
-        const float off = bias - (mrun[u] == -INFINITY ? 0.f : mrun[u]);
-        float l0 = 0.f, l1 = 0.f;
-#pragma unroll
+
+      // ---- online softmax ------------------------------------------------------------
+      // All weights of a row are taken relative to one running reference
+      // mrun (log2 units, sample weight included), raised when a tile's
+      // maximum exceeds it by more than 2^8.  For the causal leaves the tile
+      // maximum is only computed when no reference exists yet or when a
+      // tile's fresh weights sum above 2^15 on some lane; otherwise the
+      // weights are used as they are (exact either way, and bounded).
+      const float bias = isB ? p.log2w : 0.f;
+      auto tile_max_raise = [&](int u) {
+        float mx0 = fmaxf(s[0][u][0], s[0][u][1]), mx1 = fmaxf(s[1][u][0], s[1][u][1]);
+  #pragma unroll
+        for (int r = 2; r < 16; ++r) {
+          mx0 = fmaxf(mx0, s[0][u][r]);
+          mx1 = fmaxf(mx1, s[1][u][r]);
+        }
+        float mx = fmaxf(mx0, mx1);
+        mx = fmaxf(mx, __shfl_xor(mx, 32));
+        const float tmax = mx * kLog2e + bias;
+        const bool raise = tmax > mrun[u] + kRescale;
+        if (__any(raise)) {
+          const float mnew = raise ? fmaxf(mrun[u], tmax) : mrun[u];
+          const float alpha = (mnew == mrun[u]) ? 1.f : fast_exp2(mrun[u] - mnew);
+  #pragma unroll
+          for (int t = 0; t < NDT; ++t)
+  #pragma unroll
+            for (int r = 0; r < 16; ++r) o[u][t][r] *= alpha;
+          lsum[u] *= alpha;
+          mrun[u] = mnew;
+        }
+      };
+
+      // ---- P, row sums and O^T += V^T P^T -----------------------------------------
+      if constexpr (BF && !LEAF) {
+        // sorted problems (gather-bound, occupancy-sensitive): maximum every
+        // tile, exponentials interleaved with the P V MFMAs chunk by chunk
+        const bf16x2 ones = {static_cast<bf16>(1.f), static_cast<bf16>(1.f)};
+        float off[NQT];
+  #pragma unroll
+        for (int u = 0; u < NQT; ++u) {
+          tile_max_raise(u);
+          off[u] = bias - (mrun[u] == -INFINITY ? 0.f : mrun[u]);
+        }
+  #pragma unroll
         for (int c16 = 0; c16 < 4; ++c16) {
           const int kt = c16 >> 1;
           const int hi = c16 & 1;
-#pragma unroll
-          for (int i = 0; i < 8; i += 2) {
-            const float e0 = fast_exp2(fmaf(s[kt][u][8 * hi + i], kLog2e, off));
-            const float e1 = fast_exp2(fmaf(s[kt][u][8 * hi + i + 1], kLog2e, off));
-            const bf16x2 two = __builtin_convertvector((float __attribute__((ext_vector_type(2)))){e0, e1}, bf16x2);
-            if (i & 2) l1 = __builtin_amdgcn_fdot2_f32_bf16(two, ones, l1, false);
-            else l0 = __builtin_amdgcn_fdot2_f32_bf16(two, ones, l0, false);
-            pb[c16][u][i] = two[0];
-            pb[c16][u][i + 1] = two[1];
+          bf16x8 pb[NQT];
+  #pragma unroll
+          for (int u = 0; u < NQT; ++u) {
+            float l = 0.f;
+  #pragma unroll
+            for (int i = 0; i < 8; i += 2) {
+              const float e0 = fast_exp2(fmaf(s[kt][u][8 * hi + i], kLog2e, off[u]));
+              const float e1 = fast_exp2(fmaf(s[kt][u][8 * hi + i + 1], kLog2e, off[u]));
+              const bf16x2 two = __builtin_convertvector((float __attribute__((ext_vector_type(2)))){e0, e1}, bf16x2);
+              l = __builtin_amdgcn_fdot2_f32_bf16(two, ones, l, false);
+              pb[u][i] = two[0];
+              pb[u][i + 1] = two[1];
+            }
+            lsum[u] += l;
           }
-        }
-        ls[u] = l0 + l1;
-      };
-#pragma unroll
-      for (int u = 0; u < NQT; ++u) {
-        if (mrun[u] == -INFINITY) tile_max_raise(u);
-        make_p(u);
-        if (__any(!(ls[u] <= 32768.f))) {        // reference too low (or no reference)
-          tile_max_raise(u);
-          make_p(u);
-        }
-        lsum[u] += ls[u];
-      }
-#pragma unroll
-      for (int c16 = 0; c16 < 4; ++c16)
-#pragma unroll
-        for (int t = 0; t < NDT; ++t) {
-          const T* vp = vs + (16 * c16 + tr_key) * G::VSTR + 32 * t + tr_col;
-          const short4v lo = lds_read_tr16(vp);
-          const short4v hv = lds_read_tr16(vp + 8 * G::VSTR);
-          const short __attribute__((ext_vector_type(8))) va8 = {lo[0], lo[1], lo[2], lo[3], hv[0], hv[1], hv[2], hv[3]};
-          const bf16x8 va = __builtin_bit_cast(bf16x8, va8);
-#pragma unroll
-          for (int u = 0; u < NQT; ++u)
-            o[u][t] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(va, pb[c16][u], o[u][t], 0, 0, 0);
-        }
-    } else {
-      tile_max_raise(0);
-      const float off = bias - (mrun[0] == -INFINITY ? 0.f : mrun[0]);
-#pragma unroll
-      for (int kt = 0; kt < 2; ++kt)
-#pragma unroll
-        for (int jr = 0; jr < 16; ++jr) {
-          const float e = fast_exp2(fmaf(s[kt][0][jr], kLog2e, off));
-          lsum[0] += e;
-          const int key = 32 * kt + 8 * (jr >> 2) + 4 * h2 + (jr & 3);
-#pragma unroll
+  #pragma unroll
           for (int t = 0; t < NDT; ++t) {
-            const float va = vs[key * G::VSTR + 32 * t + col];
-            o[0][t] = __builtin_amdgcn_mfma_f32_32x32x2f32(va, e, o[0][t], 0, 0, 0);
+            const T* vp = vs + (16 * c16 + tr_key) * G::VSTR + 32 * t + tr_col;
+            const short4v lo = lds_read_tr16(vp);
+            const short4v hv = lds_read_tr16(vp + 8 * G::VSTR);
+            const short __attribute__((ext_vector_type(8))) va8 = {lo[0], lo[1], lo[2], lo[3], hv[0], hv[1], hv[2], hv[3]};
+            const bf16x8 va = __builtin_bit_cast(bf16x8, va8);
+  #pragma unroll
+            for (int u = 0; u < NQT; ++u)
+              o[u][t] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(va, pb[u], o[u][t], 0, 0, 0);
           }
         }
+      } else if constexpr (BF) {
+        // causal leaves (compute-bound): maximum only when needed
+        const bf16x2 ones = {static_cast<bf16>(1.f), static_cast<bf16>(1.f)};
+        bf16x8 pb[4][NQT];
+        float ls[NQT];
+        auto make_p = [&](int u) {
+          const float off = bias - (mrun[u] == -INFINITY ? 0.f : mrun[u]);
+          float l0 = 0.f, l1 = 0.f;
+  #pragma unroll
+          for (int c16 = 0; c16 < 4; ++c16) {
+            const int kt = c16 >> 1;
+            const int hi = c16 & 1;
+  #pragma unroll
+            for (int i = 0; i < 8; i += 2) {
+              const float e0 = fast_exp2(fmaf(s[kt][u][8 * hi + i], kLog2e, off));
+              const float e1 = fast_exp2(fmaf(s[kt][u][8 * hi + i + 1], kLog2e, off));
+              const bf16x2 two = __builtin_convertvector((float __attribute__((ext_vector_type(2)))){e0, e1}, bf16x2);
+              if (i & 2) l1 = __builtin_amdgcn_fdot2_f32_bf16(two, ones, l1, false);
+              else l0 = __builtin_amdgcn_fdot2_f32_bf16(two, ones, l0, false);
+              pb[c16][u][i] = two[0];
+              pb[c16][u][i + 1] = two[1];
+            }
+          }
+          ls[u] = l0 + l1;
+        };
+  #pragma unroll
+        for (int u = 0; u < NQT; ++u) {
+          if (mrun[u] == -INFINITY) tile_max_raise(u);
+          make_p(u);
+          if (__any(!(ls[u] <= 32768.f))) {        // reference too low (or no reference)
+            tile_max_raise(u);
+            make_p(u);
+          }
+          lsum[u] += ls[u];
+        }
+  #pragma unroll
+        for (int c16 = 0; c16 < 4; ++c16)
+  #pragma unroll
+          for (int t = 0; t < NDT; ++t) {
+            const T* vp = vs + (16 * c16 + tr_key) * G::VSTR + 32 * t + tr_col;
+            const short4v lo = lds_read_tr16(vp);
+            const short4v hv = lds_read_tr16(vp + 8 * G::VSTR);
+            const short __attribute__((ext_vector_type(8))) va8 = {lo[0], lo[1], lo[2], lo[3], hv[0], hv[1], hv[2], hv[3]};
+            const bf16x8 va = __builtin_bit_cast(bf16x8, va8);
+  #pragma unroll
+            for (int u = 0; u < NQT; ++u)
+              o[u][t] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(va, pb[c16][u], o[u][t], 0, 0, 0);
+          }
+      } else {
+        tile_max_raise(0);
+        const float off = bias - (mrun[0] == -INFINITY ? 0.f : mrun[0]);
+  #pragma unroll
+        for (int kt = 0; kt < 2; ++kt)
+  #pragma unroll
+          for (int jr = 0; jr < 16; ++jr) {
+            const float e = fast_exp2(fmaf(s[kt][0][jr], kLog2e, off));
+            lsum[0] += e;
+            const int key = 32 * kt + 8 * (jr >> 2) + 4 * h2 + (jr & 3);
+  #pragma unroll
+            for (int t = 0; t < NDT; ++t) {
+              const float va = vs[key * G::VSTR + 32 * t + col];
+              o[0][t] = __builtin_amdgcn_mfma_f32_32x32x2f32(va, e, o[0][t], 0, 0, 0);
+            }
+          }
+      }
     }
   }
 
@@ -501,8 +682,7 @@ __global__ __launch_bounds__(64 * NW, 2) void attn_kernel(AttnParams p) {
     const float lse2 = any ? (mrun[u] + log2f(ltot)) * kLn2 : -INFINITY;
     if (ql[u] >= qend) continue;
 
-    const int64_t orow = pq ? static_cast<int64_t>(pq[ql[u]]) : static_cast<int64_t>(qrow0 + ql[u]);
-    const int64_t ridx = static_cast<int64_t>(bh) * p.n + orow;
+    const int64_t ridx = static_cast<int64_t>(bh) * p.n + (LEAF ? qrow0 + ql[u] : orow[u]);
 
     float w_new = 1.f, w_old = 0.f, lse_out = lse2;
     if constexpr (OUT == kOutMerge) {
@@ -569,7 +749,18 @@ static int launch_attn_t(const AttnParams& p, hipStream_t s) {
     set_error("attention: grid of %lld workgroups too large", static_cast<long long>(blocks));
     return HA_EUNSUPPORTED;
   }
-  const size_t lds = 2 * G::BUF + (KIND == kKindSorted ? (p.m + 1) * sizeof(int) : 0);
+  AttnParams q = p;
+  q.bcap = 0;
+  size_t lds = 2 * G::BUF;
+  if (KIND == kKindSorted) {
+    if (p.use_block) {
+      // a workgroup's queries span at most (TQ - 1) / b_eff + 2 blocks
+      const int64_t span = static_cast<int64_t>((G::TQ - 1) / p.b_eff + 2) * p.b_eff;
+      const int64_t cap = span < p.seg ? span : p.seg;
+      if (cap <= kBlockListCap) q.bcap = static_cast<int>(cap);
+    }
+    lds += list_bytes(q.bcap, p.m);
+  }
   auto fn = attn_kernel<T, D, KIND, OUT, NW, QPW>;
   static bool attr_set = false;   // once per instantiation
   if (!attr_set) {
@@ -577,7 +768,7 @@ static int launch_attn_t(const AttnParams& p, hipStream_t s) {
                                      hipFuncAttributeMaxDynamicSharedMemorySize, 160 * 1024));
     attr_set = true;
   }
-  hipLaunchKernelGGL(fn, dim3(static_cast<unsigned>(blocks)), dim3(G::NT), lds, s, p);
+  hipLaunchKernelGGL(fn, dim3(static_cast<unsigned>(blocks)), dim3(G::NT), lds, s, q);
   return HA_OK;
 }
 

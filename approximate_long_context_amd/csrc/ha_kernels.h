@@ -39,6 +39,7 @@ enum AttnOut {
 };
 
 constexpr int kMaxSamples = 4096;   // sample list staged in LDS
+constexpr int kBlockListCap = 2048; // largest block key list staged in LDS
 
 struct AttnParams {
   const void* q = nullptr;
@@ -64,6 +65,7 @@ struct AttnParams {
   const void* vs = nullptr;
   int kind = kKindSorted;
   int b_eff = 1;
+  int bcap = 0;          // LDS block key list capacity (set by the launcher)
   int use_block = 1;
   int use_samples = 1;
   const int32_t* sidx = nullptr;     // [BH][pieces][m] sorted key positions
