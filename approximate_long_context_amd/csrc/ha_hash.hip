@@ -8,11 +8,9 @@
 //
 // The fp32 dot products follow one fixed order so that ranks are exact
 // and reproducible: the d products are cut into groups of 8 consecutive
-// elements; a lane owns one group (one 16-byte load of bf16), sums it by
-// halving (pairs 4, 2, 1 apart), and the group sums are combined by an
-// xor butterfly across the d/8 lanes of the row, which is the same
-// halving order over the groups (fp32 addition is commutative).  No
-// multiply-add contraction.
+// elements, each group is summed by halving (pairs 4, 2, 1 apart), and the
+// d/8 group sums are combined by halving as well (pairs d/16, ..., 1
+// apart).  No multiply-add contraction.
 //
 // HBM traffic: each input row is read once (d * elem bytes) and 2 bytes
 // of rank are written.
@@ -48,85 +46,99 @@ __device__ __forceinline__ uint32_t gray_inverse(uint32_t x) {
   return x;
 }
 
-template <typename T>
-__device__ __forceinline__ void load8(const T* p, float* x);
-
-template <>
-__device__ __forceinline__ void load8<bf16>(const bf16* p, float* x) {
-  uint4v w = *reinterpret_cast<const uint4v*>(p);
+// Halving sum of v[0 .. N): pairs N/2 apart, then N/4 apart, ... (the fixed
+// order of the group sums).
+template <int N>
+__device__ __forceinline__ float halving_sum(const float* v) {
+#pragma clang fp contract(off)
+  if constexpr (N == 1) {
+    return v[0];
+  } else {
+    float h[N / 2];
 #pragma unroll
-  for (int i = 0; i < 4; ++i) {
-    x[2 * i] = __uint_as_float(w[i] << 16);
-    x[2 * i + 1] = __uint_as_float(w[i] & 0xFFFF0000u);
+    for (int i = 0; i < N / 2; ++i) h[i] = v[i] + v[i + N / 2];
+    return halving_sum<N / 2>(h);
   }
 }
 
-template <>
-__device__ __forceinline__ void load8<float>(const float* p, float* x) {
-  floatx4 a = *reinterpret_cast<const floatx4*>(p);
-  floatx4 b = *reinterpret_cast<const floatx4*>(p + 4);
-#pragma unroll
-  for (int i = 0; i < 4; ++i) {
-    x[i] = a[i];
-    x[4 + i] = b[i];
-  }
-}
-
+// One row per lane.  A workgroup of 4 waves takes 256 consecutive rows per
+// step: the rows are read with coalesced 16-byte loads into LDS (padded
+// rows, conflict-free), then each lane walks its own row group by group.
+// The projection values are uniform across lanes and come from scalar
+// loads.  Per row: d r products and the adds of the two halving levels.
 template <typename T, int D, int R>
 __global__ __launch_bounds__(256) void hash_kernel(const T* __restrict__ x, int64_t rows,
                                                    const float* __restrict__ Rm,
                                                    uint16_t* __restrict__ rank) {
 #pragma clang fp contract(off)
-  constexpr int LPR = D / 8;      // lanes per row
-  constexpr int RPW = 64 / LPR;   // rows per wave
-  const int lane = threadIdx.x & 63;
-  const int grp = lane % LPR;
-  const int sub = lane / LPR;
-  float rr[R][8];
-#pragma unroll
-  for (int p = 0; p < R; ++p)
-#pragma unroll
-    for (int i = 0; i < 8; ++i) rr[p][i] = Rm[p * D + 8 * grp + i];
+  constexpr int G = D / 8;                          // groups of 8 elements
+  constexpr int ROWB = D * static_cast<int>(sizeof(T));
+  constexpr int CH = ROWB / 16;                     // 16-byte chunks per row
+  constexpr int STR = ROWB + 16;                    // LDS row stride (bytes)
+  constexpr int TR = 256;                           // rows per workgroup step
+  __shared__ __attribute__((aligned(16))) char stage[TR * STR];
+  const int tid = threadIdx.x;
+  const char* xb = reinterpret_cast<const char*>(x);
 
-  const int64_t wave = (static_cast<int64_t>(blockIdx.x) * blockDim.x + threadIdx.x) >> 6;
-  const int64_t nwaves = (static_cast<int64_t>(gridDim.x) * blockDim.x) >> 6;
-  for (int64_t rb = wave * RPW; rb < rows; rb += nwaves * RPW) {
-    const int64_t row = rb + sub;
-    const bool valid = row < rows;
-    float xv[8];
-    if (valid) {
-      load8<T>(x + row * D + 8 * grp, xv);
-    } else {
+  for (int64_t r0 = static_cast<int64_t>(blockIdx.x) * TR; r0 < rows; r0 += static_cast<int64_t>(gridDim.x) * TR) {
+    const int nr = rows - r0 < TR ? static_cast<int>(rows - r0) : TR;
+    // coalesced staging: chunk q of the step = row q / CH, chunk q % CH
 #pragma unroll
-      for (int i = 0; i < 8; ++i) xv[i] = 0.f;
+    for (int c = 0; c < CH; ++c) {
+      const int q = c * TR + tid;
+      const int rr = q / CH, cc = q % CH;
+      uint4v w = {0u, 0u, 0u, 0u};
+      if (rr < nr) w = *reinterpret_cast<const uint4v*>(xb + (r0 + rr) * ROWB + 16 * cc);
+      *reinterpret_cast<uint4v*>(stage + rr * STR + 16 * cc) = w;
     }
+    __syncthreads();
+
+    const char* row = stage + tid * STR;
+    float xv[D];                                     // this lane's row in fp32
+#pragma unroll
+    for (int g = 0; g < G; ++g) {
+      if constexpr (sizeof(T) == 2) {
+        const uint4v w = *reinterpret_cast<const uint4v*>(row + 16 * g);
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          xv[8 * g + 2 * i] = __uint_as_float(w[i] << 16);
+          xv[8 * g + 2 * i + 1] = __uint_as_float(w[i] & 0xFFFF0000u);
+        }
+      } else {
+        const floatx4 a = *reinterpret_cast<const floatx4*>(row + 32 * g);
+        const floatx4 b = *reinterpret_cast<const floatx4*>(row + 32 * g + 16);
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          xv[8 * g + i] = a[i];
+          xv[8 * g + 4 + i] = b[i];
+        }
+      }
+    }
+    // one projection at a time (its d values sit in scalar registers)
     uint32_t code = 0;
-#pragma unroll
+#pragma unroll 1
     for (int p = 0; p < R; ++p) {
-      float pr[8];
+      const float* rp = Rm + p * D;
+      float gsum[G];
 #pragma unroll
-      for (int i = 0; i < 8; ++i) pr[i] = xv[i] * rr[p][i];
-      float s4[4];
+      for (int g = 0; g < G; ++g) {
+        float pr[8];
 #pragma unroll
-      for (int i = 0; i < 4; ++i) s4[i] = pr[i] + pr[i + 4];
-      float s2a = s4[0] + s4[2];
-      float s2b = s4[1] + s4[3];
-      float t = s2a + s2b;
-#pragma unroll
-      for (int o = LPR / 2; o >= 1; o >>= 1) t = t + __shfl_xor(t, o);
-      code |= (t > 0.f ? 1u : 0u) << p;
+        for (int i = 0; i < 8; ++i) pr[i] = xv[8 * g + i] * rp[8 * g + i];
+        gsum[g] = halving_sum<8>(pr);
+      }
+      code |= (halving_sum<G>(gsum) > 0.f ? 1u : 0u) << p;
     }
-    if (valid && grp == 0) rank[row] = static_cast<uint16_t>(gray_inverse(code));
+    if (tid < nr) rank[r0 + tid] = static_cast<uint16_t>(gray_inverse(code));
+    __syncthreads();
   }
 }
 
 template <typename T, int D>
 static int launch_hash_d(const T* x, int64_t rows, int r, const float* R, uint16_t* rank,
                          hipStream_t s) {
-  constexpr int RPW = 64 / (D / 8);
-  int64_t waves = (rows + RPW - 1) / RPW;
-  int64_t blocks = (waves + 3) / 4;
-  if (blocks > 65536) blocks = 65536;
+  int64_t blocks = (rows + 255) / 256;
+  if (blocks > 8192) blocks = 8192;
   if (blocks < 1) blocks = 1;
   dim3 g(static_cast<unsigned>(blocks)), b(256);
   switch (r) {
