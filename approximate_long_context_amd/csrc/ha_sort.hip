@@ -8,13 +8,11 @@
 //
 // A pass over a segment cut into tiles of kTile elements:
 //   1. hist:    each tile counts its digits in LDS -> counts[seg][digit][tile]
-//   2. scan:    exclusive scan of counts in (digit, tile) order gives each
-//               tile's first output slot for each digit
-//   3. scatter: each wave ranks its elements among equal digits of the
-//               lower lanes (ballot per digit bit), processing 64-element
-//               chunks in order, and writes the element's row index.
-// A segment of one tile takes a single fused kernel (hist, scan and
-// scatter in LDS).
+//   2. scatter: each tile sums the counts of the segment into its first
+//               output slot per digit, then each wave ranks its elements
+//               among equal digits of the lower lanes (ballot per digit
+//               bit), chunk by chunk in order, and writes the row index.
+// A segment of one tile takes a single fused kernel.
 //
 // HBM traffic per pass: 2 bytes of rank read twice (hist + scatter) or
 // 4 bytes of input permutation + 2 of rank per element, 4 bytes written.
@@ -68,38 +66,10 @@ __global__ __launch_bounds__(kSortThreads) void sort_hist_kernel(SortPass p) {
     p.counts[(seg * 256 + b) * p.tiles + tile] = hist[b];
 }
 
-// Exclusive scan of counts[seg][0..nb)[0..tiles) in place, one block per segment.
-__global__ __launch_bounds__(kSortThreads) void sort_scan_kernel(int32_t* counts, int nb, int tiles) {
-  __shared__ int part[kSortThreads];
-  const int64_t seg = blockIdx.x;
-  int32_t* c = counts + seg * 256 * tiles;   // digits nb..255 are unused
-  const int total = nb * tiles;
-  const int chunk = (total + kSortThreads - 1) / kSortThreads;
-  const int lo = min(total, threadIdx.x * chunk);
-  const int hi = min(total, lo + chunk);
-  int s = 0;
-  for (int i = lo; i < hi; ++i) s += c[i];
-  part[threadIdx.x] = s;
-  __syncthreads();
-  // Hillis-Steele inclusive scan of the per-thread sums
-  for (int off = 1; off < kSortThreads; off <<= 1) {
-    int v = threadIdx.x >= off ? part[threadIdx.x - off] : 0;
-    __syncthreads();
-    part[threadIdx.x] += v;
-    __syncthreads();
-  }
-  int run = part[threadIdx.x] - s;
-  for (int i = lo; i < hi; ++i) {
-    int x = c[i];
-    c[i] = run;
-    run += x;
-  }
-}
-
-// Rank the wave's 64 elements among equal digits: returns the number of
-// lower lanes with the same digit and the number of lanes with it.
-__device__ __forceinline__ void wave_peers(bool valid, uint32_t dg, int bits, int lane,
-                                           int* below, int* count) {
+// Rank the wave's 64 elements among equal digits: the mask of lanes with the
+// same digit, the number of them below this lane, and their count.
+__device__ __forceinline__ uint64_t wave_peers(bool valid, uint32_t dg, int bits, int lane,
+                                               int* below, int* count) {
   uint64_t peers = __ballot(valid);
   for (int b = 0; b < bits; ++b) {
     const bool set = (dg >> b) & 1u;
@@ -109,117 +79,147 @@ __device__ __forceinline__ void wave_peers(bool valid, uint32_t dg, int bits, in
   const uint64_t lower = (lane == 0) ? 0ull : (~0ull >> (64 - lane));
   *below = __popcll(peers & lower);
   *count = __popcll(peers);
+  return peers;
 }
 
-// offsets[w][d]: output slot of the next element with digit d in wave w.
+// One tile [e0, e1) of a segment: each wave holds kWaveSpan consecutive
+// elements (kChunks chunks of 64) in registers.  base[d] is the tile's first
+// output slot for digit d.  Per-wave digit counts give each wave its own
+// slots (stable across waves); inside a wave the chunks take their slots in
+// order through LDS fetch-and-add by the first lane of each digit group
+// (LDS operations of one wave complete in issue order, so the chunks stay
+// ordered while their ranking overlaps).
+constexpr int kChunks = kWaveSpan / 64;
 __device__ __forceinline__ void scatter_tile(const SortPass& p, int64_t seg, int e0, int e1,
-                                             int (*offsets)[256]) {
+                                             const int* base, int (*wh)[256]) {
+  const int nb = 1 << p.bits;
   const int w = threadIdx.x >> 6;
   const int lane = threadIdx.x & 63;
   const int ws = e0 + w * kWaveSpan;
-  for (int c = 0; c < kWaveSpan; c += 64) {
-    if (ws + c >= e1) break;                      // wave-uniform
-    const int e = ws + c + lane;
-    const bool valid = e < e1;
-    int32_t row = 0;
-    uint32_t dg = 0;
-    if (valid) sort_elem(p, seg, e, &row, &dg);
-    int below, cnt;
-    wave_peers(valid, dg, p.bits, lane, &below, &cnt);
-    int base = valid ? offsets[w][dg] : 0;
-    if (valid) p.perm_out[seg * p.len + base + below] = row;
-    __builtin_amdgcn_wave_barrier();
-    if (valid && below == 0) offsets[w][dg] = base + cnt;
-    __builtin_amdgcn_wave_barrier();
+  int32_t row[kChunks];
+  uint32_t dg[kChunks];
+#pragma unroll
+  for (int c = 0; c < kChunks; ++c) {
+    const int e = ws + 64 * c + lane;
+    row[c] = 0;
+    dg[c] = 0;
+    if (e < e1) sort_elem(p, seg, e, &row[c], &dg[c]);
   }
-}
-
-// Per-wave digit histograms of the tile, then per-wave starting slots.
-__device__ __forceinline__ void wave_histograms(const SortPass& p, int64_t seg, int e0, int e1,
-                                                int (*wh)[256]) {
-  const int nb = 1 << p.bits;
   for (int i = threadIdx.x; i < kSortWaves * 256; i += kSortThreads) (&wh[0][0])[i] = 0;
   __syncthreads();
-  const int w = threadIdx.x >> 6;
-  const int lane = threadIdx.x & 63;
-  const int ws = e0 + w * kWaveSpan;
-  for (int c = 0; c < kWaveSpan; c += 64) {
-    const int e = ws + c + lane;
-    if (e < e1) {
-      int32_t row;
-      uint32_t dg;
-      sort_elem(p, seg, e, &row, &dg);
-      atomicAdd(&wh[w][dg], 1);
+#pragma unroll
+  for (int c = 0; c < kChunks; ++c)
+    if (ws + 64 * c + lane < e1) atomicAdd(&wh[w][dg[c]], 1);
+  __syncthreads();
+  for (int b = threadIdx.x; b < nb; b += kSortThreads) {
+    int run = base[b];
+    for (int v = 0; v < kSortWaves; ++v) {
+      const int x = wh[v][b];
+      wh[v][b] = run;
+      run += x;
     }
   }
   __syncthreads();
-  (void)nb;
+#pragma unroll
+  for (int c = 0; c < kChunks; ++c) {
+    if (ws + 64 * c >= e1) break;                 // wave-uniform
+    const bool valid = ws + 64 * c + lane < e1;
+    int below, cnt;
+    const uint64_t peers = wave_peers(valid, dg[c], p.bits, lane, &below, &cnt);
+    int slot = 0;
+    if (valid && below == 0) slot = atomicAdd(&wh[w][dg[c]], cnt);
+    const int leader = valid ? static_cast<int>(__builtin_ctzll(peers)) : lane;
+    slot = __shfl(slot, leader);
+    if (valid) p.perm_out[seg * p.len + slot + below] = row[c];
+  }
 }
 
+// Tile t of a segment: its first slot per digit is the number of elements
+// with a smaller digit in the segment plus those with the same digit in the
+// tiles before it (read from the per-tile counts of the histogram pass).
 __global__ __launch_bounds__(kSortThreads) void sort_scatter_kernel(SortPass p) {
   __shared__ int wh[kSortWaves][256];
+  __shared__ int base[256];
+  __shared__ int tot[256];
   const int tile = blockIdx.x;
   const int64_t seg = blockIdx.y;
   const int nb = 1 << p.bits;
   const int e0 = tile * kTile;
   const int e1 = min(p.len, e0 + kTile);
-  wave_histograms(p, seg, e0, e1, wh);
-  for (int b = threadIdx.x; b < nb; b += kSortThreads) {
-    int run = p.counts[(seg * 256 + b) * p.tiles + tile];
-    for (int w = 0; w < kSortWaves; ++w) {
-      int x = wh[w][b];
-      wh[w][b] = run;
-      run += x;
+  for (int b = threadIdx.x; b < 256; b += kSortThreads) {
+    int before = 0, all = 0;
+    if (b < nb) {
+      const int32_t* c = p.counts + (seg * 256 + b) * p.tiles;
+      for (int t = 0; t < p.tiles; ++t) {
+        const int x = c[t];
+        before += t < tile ? x : 0;
+        all += x;
+      }
+    }
+    base[b] = before;
+    tot[b] = all;
+  }
+  __syncthreads();
+  if (threadIdx.x < 64) {                         // exclusive scan of the 256 digit totals
+    const int lane = threadIdx.x;
+    int v[4];
+    int sum = 0;
+    for (int i = 0; i < 4; ++i) {
+      v[i] = tot[lane * 4 + i];
+      sum += v[i];
+    }
+    int incl = sum;
+    for (int off = 1; off < 64; off <<= 1) {
+      const int y = __shfl_up(incl, off);
+      if (lane >= off) incl += y;
+    }
+    int run = incl - sum;
+    for (int i = 0; i < 4; ++i) {
+      base[lane * 4 + i] += run;
+      run += v[i];
     }
   }
   __syncthreads();
-  scatter_tile(p, seg, e0, e1, wh);
+  scatter_tile(p, seg, e0, e1, base, wh);
 }
 
 // Whole segment in one tile: histogram, scan and scatter in one block.
 __global__ __launch_bounds__(kSortThreads) void sort_single_tile_kernel(SortPass p) {
   __shared__ int wh[kSortWaves][256];
-  __shared__ int tot[256];
+  __shared__ int base[256];
   const int64_t seg = blockIdx.x;
   const int nb = 1 << p.bits;
-  wave_histograms(p, seg, 0, p.len, wh);
-  for (int b = threadIdx.x; b < 256; b += kSortThreads) {
-    int s = 0;
-    if (b < nb)
-      for (int w = 0; w < kSortWaves; ++w) s += wh[w][b];
-    tot[b] = s;
+  for (int b = threadIdx.x; b < 256; b += kSortThreads) base[b] = 0;
+  __syncthreads();
+  for (int e = threadIdx.x; e < p.len; e += kSortThreads) {
+    int32_t row;
+    uint32_t dg;
+    sort_elem(p, seg, e, &row, &dg);
+    atomicAdd(&base[dg], 1);
   }
   __syncthreads();
-  if (threadIdx.x < 64) {                         // exclusive scan of 256 totals by wave 0
+  if (threadIdx.x < 64) {                         // exclusive scan of the 256 digit totals
     const int lane = threadIdx.x;
     int v[4];
-    int s = 0;
+    int sum = 0;
     for (int i = 0; i < 4; ++i) {
-      v[i] = tot[lane * 4 + i];
-      s += v[i];
+      v[i] = base[lane * 4 + i];
+      sum += v[i];
     }
-    int incl = s;
+    int incl = sum;
     for (int off = 1; off < 64; off <<= 1) {
-      int y = __shfl_up(incl, off);
+      const int y = __shfl_up(incl, off);
       if (lane >= off) incl += y;
     }
-    int run = incl - s;
+    int run = incl - sum;
     for (int i = 0; i < 4; ++i) {
-      tot[lane * 4 + i] = run;
+      base[lane * 4 + i] = run;
       run += v[i];
     }
   }
   __syncthreads();
-  for (int b = threadIdx.x; b < nb; b += kSortThreads) {
-    int run = tot[b];
-    for (int w = 0; w < kSortWaves; ++w) {
-      int x = wh[w][b];
-      wh[w][b] = run;
-      run += x;
-    }
-  }
-  __syncthreads();
-  scatter_tile(p, seg, 0, p.len, wh);
+  (void)nb;
+  scatter_tile(p, seg, 0, p.len, base, wh);
 }
 
 size_t sort_ws_bytes(int64_t heads, int len, int pieces, int r) {
@@ -239,9 +239,6 @@ static int run_pass(SortPass p, int64_t segs, hipStream_t s) {
   dim3 g(p.tiles, static_cast<unsigned>(segs));
   hipLaunchKernelGGL(sort_hist_kernel, g, dim3(kSortThreads), 0, s, p);
   HA_TRY(after_launch("sort hist", s));
-  hipLaunchKernelGGL(sort_scan_kernel, dim3(static_cast<unsigned>(segs)), dim3(kSortThreads), 0,
-                     s, p.counts, 1 << p.bits, p.tiles);
-  HA_TRY(after_launch("sort scan", s));
   hipLaunchKernelGGL(sort_scatter_kernel, g, dim3(kSortThreads), 0, s, p);
   return after_launch("sort scatter", s);
 }
