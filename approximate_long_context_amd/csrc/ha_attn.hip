@@ -182,22 +182,100 @@ __global__ __launch_bounds__(64 * NW, (min_waves<T, D, KIND, NW, QPW>())) void a
   int* rrow = spos + p.m;                 // rows before compaction
   int* ccount = rrow + p.m;               // kept samples per 64
   const bool blist = !LEAF && p.bcap > 0;
+  const int nbl = ka1 - ka0;
+  const int nA = ka1 > ka0 ? (nbl + kKT - 1) / kKT : 0;
+
+  // ---- tile staging: global -> registers -> LDS ------------------------------
+  const int c_in_row = tid % G::CPR;            // chunk column, fixed per thread
+  const int j_first = tid / G::CPR;             // first key row of this thread
+  constexpr int JSTEP = G::NT / G::CPR;
+  uint4v kreg[G::CPT], vreg[G::CPT];
+
+  // ---- prologue loads ------------------------------------------------------------
+  // Issued in dependency levels so that their latencies overlap: first the
+  // permutation entries (query rows, the rows of the first block tile, the
+  // first list entries, sample positions), then what they address (query
+  // fragments, the first tile's K/V rows, sample rows), then the LDS lists.
+  // Common case (permuted rows, block list, samples): every load of a level
+  // is unconditional (indices clamped into range) so the levels overlap.
+  const int32_t* si = samp ? p.sidx + qpiece * p.m : nullptr;
+  const bool fast = !LEAF && !mat && pq != nullptr && pk != nullptr && blist && samp && nbl > 0;
+  const bool early0 = !LEAF && nA > 0;          // first tile is a block tile: load it now
+  int ql[NQT], orow[NQT];   // query (sorted / local position) and its original row
+  int t0row[G::CPT];
+  int bl = 0, sp = 0, sr = 0;
+  typedef typename std::conditional<BF, bf16x8, float>::type QF;
+  QF qf[NQT][NQF];
+  auto load_q = [&]() {
+#pragma unroll
+    for (int u = 0; u < NQT; ++u) {
+      const int qls = ql[u] < qend ? ql[u] : q0;
+      const T* qrow;
+      if (mat) qrow = static_cast<const T*>(p.qs) + (qpiece * p.seg + qls) * D;
+      else qrow = qbase + static_cast<int64_t>(orow[u]) * D;
+#pragma unroll
+      for (int c = 0; c < NQF; ++c) {
+        if constexpr (BF) qf[u][c] = *reinterpret_cast<const bf16x8*>(qrow + 16 * c + 8 * h2);
+        else qf[u][c] = qrow[2 * c + h2];
+      }
+    }
+  };
+  auto load_t0 = [&]() {
+#pragma unroll
+    for (int c = 0; c < G::CPT; ++c) {
+      const int64_t off = static_cast<int64_t>(t0row[c]) * D + G::EPC * c_in_row;
+      kreg[c] = *reinterpret_cast<const uint4v*>((mat ? ksb : kbase) + off);
+      vreg[c] = *reinterpret_cast<const uint4v*>((mat ? vsb : vbase) + off);
+    }
+  };
+#pragma unroll
+  for (int u = 0; u < NQT; ++u) ql[u] = wq0 + 32 * u + col;
+  if (fast) {
+    const int kc0 = min(kKT, nbl);
+#pragma unroll
+    for (int u = 0; u < NQT; ++u) orow[u] = pq[ql[u] < qend ? ql[u] : q0];
+#pragma unroll
+    for (int c = 0; c < G::CPT; ++c) t0row[c] = pk[ka0 + min(j_first + c * JSTEP, kc0 - 1)];
+    bl = pk[ka0 + min(tid, nbl - 1)];
+    sp = si[min(tid, p.m - 1)];
+    load_q();
+    load_t0();                                  // rows past kc0 repeat a valid row; masked
+    sr = pk[sp];
+  } else {
+#pragma unroll
+    for (int u = 0; u < NQT; ++u) {
+      const int qls = ql[u] < qend ? ql[u] : q0;
+      orow[u] = pq ? pq[qls] : qrow0 + qls;
+    }
+    if (early0) {
+#pragma unroll
+      for (int c = 0; c < G::CPT; ++c) t0row[c] = key_row(ka0 + min(j_first + c * JSTEP, min(kKT, nbl) - 1));
+    }
+    if (blist && tid < nbl) bl = key_row(ka0 + tid);
+    if (samp && tid < p.m) sp = si[tid];
+    load_q();
+    if (early0) load_t0();
+    if (samp && tid < p.m) sr = key_row(sp);
+  }
+
   int nsamp = 0;
   if (!LEAF) {
-    if (blist)
-      for (int j = tid; j < ka1 - ka0; j += G::NT) brow[j] = key_row(ka0 + j);
+    if (blist) {
+      if (tid < nbl) brow[tid] = bl;
+      for (int j = tid + G::NT; j < nbl; j += G::NT) brow[j] = key_row(ka0 + j);
+    }
     if (samp) {
-      const int32_t* si = p.sidx + qpiece * p.m;
       const int tq = q0 / p.b_eff;
       int* raw = samp_multi ? srow : rrow;
       for (int c = 64 * wave; c < p.m; c += G::NT) {
         const int i = c + lane;
-        const int sp = i < p.m ? si[i] : 0;
+        const bool first = c == 64 * wave;     // i == tid: loaded above
+        const int spi = first ? sp : (i < p.m ? si[i] : 0);
         if (i < p.m) {
-          spos[i] = sp;
-          raw[i] = key_row(sp);
+          spos[i] = spi;
+          raw[i] = first ? sr : key_row(spi);
         }
-        const uint64_t keep = __ballot(i < p.m && (samp_multi || (sp / p.b_eff) != tq));
+        const uint64_t keep = __ballot(i < p.m && (samp_multi || (spi / p.b_eff) != tq));
         if (lane == 0) ccount[c / 64] = __popcll(keep);
       }
       __syncthreads();
@@ -218,25 +296,6 @@ __global__ __launch_bounds__(64 * NW, (min_waves<T, D, KIND, NW, QPW>())) void a
     if (blist || samp) __syncthreads();
   }
 
-  // ---- query fragments ----------------------------------------------------------
-  int ql[NQT], orow[NQT];   // query (sorted / local position) and its original row
-  typedef typename std::conditional<BF, bf16x8, float>::type QF;
-  QF qf[NQT][NQF];
-#pragma unroll
-  for (int u = 0; u < NQT; ++u) {
-    ql[u] = wq0 + 32 * u + col;
-    const int qls = ql[u] < qend ? ql[u] : q0;
-    orow[u] = pq ? pq[qls] : qrow0 + qls;
-    const T* qrow;
-    if (mat) qrow = static_cast<const T*>(p.qs) + (qpiece * p.seg + qls) * D;
-    else qrow = qbase + static_cast<int64_t>(orow[u]) * D;
-#pragma unroll
-    for (int c = 0; c < NQF; ++c) {
-      if constexpr (BF) qf[u][c] = *reinterpret_cast<const bf16x8*>(qrow + 16 * c + 8 * h2);
-      else qf[u][c] = qrow[2 * c + h2];
-    }
-  }
-
   floatx16 o[NQT][NDT];
 #pragma unroll
   for (int u = 0; u < NQT; ++u)
@@ -251,15 +310,8 @@ __global__ __launch_bounds__(64 * NW, (min_waves<T, D, KIND, NW, QPW>())) void a
     lsum[u] = 0.f;
   }
 
-  const int nA = ka1 > ka0 ? (ka1 - ka0 + kKT - 1) / kKT : 0;
   const int nB = (nsamp + kKT - 1) / kKT;
   const int ntiles = nA + nB;
-
-  // ---- tile staging: global -> registers -> LDS ------------------------------
-  const int c_in_row = tid % G::CPR;            // chunk column, fixed per thread
-  const int j_first = tid / G::CPR;             // first key row of this thread
-  constexpr int JSTEP = G::NT / G::CPR;
-  uint4v kreg[G::CPT], vreg[G::CPT];
 
   // leaf rows are contiguous: per-thread base + a uniform step per tile
   const T* kleaf = kbase + static_cast<int64_t>(krow0 + j_first) * D + G::EPC * c_in_row;
@@ -316,7 +368,7 @@ __global__ __launch_bounds__(64 * NW, (min_waves<T, D, KIND, NW, QPW>())) void a
   const int tr_key = 4 * h2 + ((lane & 15) >> 2);
   const int tr_col = 16 * ((lane >> 4) & 1) + 4 * (lane & 3);
 
-  if (ntiles > 0) load_tile(0);
+  if (ntiles > 0 && !early0) load_tile(0);
   for (int it = 0; it < ntiles; ++it) {
     const int buf = it & 1;
     store_tile(buf);
