@@ -89,6 +89,13 @@ __device__ __forceinline__ int xcd_remap(int bid, int nblocks) {
 
 __device__ __forceinline__ float fast_exp2(float x) { return __builtin_amdgcn_exp2f(x); }
 
+// 16-byte load from a workgroup-uniform base plus a per-lane byte offset
+// below 2^32 (one head's rows; the host checks n * d * element < 2^32), so
+// the base stays in scalar registers and the lane carries 32 bits.
+__device__ __forceinline__ uint4v ld16(const void* base, uint32_t off) {
+  return *reinterpret_cast<const uint4v*>(static_cast<const char*>(base) + off);
+}
+
 typedef short short4v __attribute__((ext_vector_type(4)));
 typedef __attribute__((address_space(3))) short4v lds_short4v;
 
@@ -99,11 +106,12 @@ __device__ __forceinline__ short4v lds_read_tr16(const void* p) {
   return __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_short4v*)(const_cast<void*>(p)));
 }
 
-// Minimum waves per SIMD the register allocation must allow: the sorted
-// problems are gather-bound and need 4 (<= 128 VGPRs) where that fits.
+// Minimum waves per SIMD the register allocation must allow: 4 (<= 128
+// VGPRs) for the bf16 d = 64 shapes of 8 waves x 32 queries, where it fits
+// without spilling and measurably pays; 2 otherwise.
 template <typename T, int D, int KIND, int NW, int QPW>
 constexpr int min_waves() {
-  return (KIND == kKindSorted && sizeof(T) == 2 && D == 64 && NW == 8 && QPW == 32) ? 4 : 2;
+  return (sizeof(T) == 2 && D == 64 && NW == 8 && QPW == 32) ? 4 : 2;
 }
 
 template <typename T, int D, int KIND, int OUT, int NW, int QPW>
@@ -210,22 +218,21 @@ __global__ __launch_bounds__(64 * NW, (min_waves<T, D, KIND, NW, QPW>())) void a
 #pragma unroll
     for (int u = 0; u < NQT; ++u) {
       const int qls = ql[u] < qend ? ql[u] : q0;
-      const T* qrow;
-      if (mat) qrow = static_cast<const T*>(p.qs) + (qpiece * p.seg + qls) * D;
-      else qrow = qbase + static_cast<int64_t>(orow[u]) * D;
+      const T* qb = mat ? static_cast<const T*>(p.qs) + qpiece * p.seg * D : qbase;
+      const uint32_t qoff = static_cast<uint32_t>(mat ? qls : orow[u]) * (D * sizeof(T));
 #pragma unroll
       for (int c = 0; c < NQF; ++c) {
-        if constexpr (BF) qf[u][c] = *reinterpret_cast<const bf16x8*>(qrow + 16 * c + 8 * h2);
-        else qf[u][c] = qrow[2 * c + h2];
+        if constexpr (BF) qf[u][c] = __builtin_bit_cast(bf16x8, ld16(qb, qoff + (16 * c + 8 * h2) * 2));
+        else qf[u][c] = *reinterpret_cast<const float*>(reinterpret_cast<const char*>(qb) + qoff + (2 * c + h2) * 4);
       }
     }
   };
   auto load_t0 = [&]() {
 #pragma unroll
     for (int c = 0; c < G::CPT; ++c) {
-      const int64_t off = static_cast<int64_t>(t0row[c]) * D + G::EPC * c_in_row;
-      kreg[c] = *reinterpret_cast<const uint4v*>((mat ? ksb : kbase) + off);
-      vreg[c] = *reinterpret_cast<const uint4v*>((mat ? vsb : vbase) + off);
+      const uint32_t off = static_cast<uint32_t>(t0row[c] * D + G::EPC * c_in_row) * sizeof(T);
+      kreg[c] = ld16(mat ? ksb : kbase, off);
+      vreg[c] = ld16(mat ? vsb : vbase, off);
     }
   };
 #pragma unroll
@@ -314,8 +321,7 @@ __global__ __launch_bounds__(64 * NW, (min_waves<T, D, KIND, NW, QPW>())) void a
   const int ntiles = nA + nB;
 
   // leaf rows are contiguous: per-thread base + a uniform step per tile
-  const T* kleaf = kbase + static_cast<int64_t>(krow0 + j_first) * D + G::EPC * c_in_row;
-  const T* vleaf = vbase + static_cast<int64_t>(krow0 + j_first) * D + G::EPC * c_in_row;
+  const uint32_t leaf_off = static_cast<uint32_t>((krow0 + j_first) * D + G::EPC * c_in_row) * sizeof(T);
   auto load_tile = [&](int it) {
     const bool isB = it >= nA;
     const int kb = isB ? (it - nA) * kKT : ka0 + it * kKT;
@@ -323,9 +329,9 @@ __global__ __launch_bounds__(64 * NW, (min_waves<T, D, KIND, NW, QPW>())) void a
     if (LEAF && kcnt == kKT) {
 #pragma unroll
       for (int c = 0; c < G::CPT; ++c) {
-        const int64_t off = static_cast<int64_t>(kb + c * JSTEP) * D;
-        kreg[c] = *reinterpret_cast<const uint4v*>(kleaf + off);
-        vreg[c] = *reinterpret_cast<const uint4v*>(vleaf + off);
+        const uint32_t off = leaf_off + static_cast<uint32_t>((kb + c * JSTEP) * D) * sizeof(T);
+        kreg[c] = ld16(kbase, off);
+        vreg[c] = ld16(vbase, off);
       }
       return;
     }
@@ -335,9 +341,9 @@ __global__ __launch_bounds__(64 * NW, (min_waves<T, D, KIND, NW, QPW>())) void a
       uint4v kw = {0u, 0u, 0u, 0u}, vw = {0u, 0u, 0u, 0u};
       if (j < kcnt) {
         const int row = isB ? srow[kb + j] : (blist ? brow[kb - ka0 + j] : key_row(kb + j));
-        const int64_t off = static_cast<int64_t>(row) * D + G::EPC * c_in_row;
-        kw = *reinterpret_cast<const uint4v*>((mat ? ksb : kbase) + off);
-        vw = *reinterpret_cast<const uint4v*>((mat ? vsb : vbase) + off);
+        const uint32_t off = static_cast<uint32_t>(row * D + G::EPC * c_in_row) * sizeof(T);
+        kw = ld16(mat ? ksb : kbase, off);
+        vw = ld16(mat ? vsb : vbase, off);
       }
       kreg[c] = kw;
       vreg[c] = vw;
@@ -724,49 +730,83 @@ __global__ __launch_bounds__(64 * NW, (min_waves<T, D, KIND, NW, QPW>())) void a
   }
 
   // ---- epilogue -------------------------------------------------------------------
+  // The result leaves through LDS so that rows are read and written in
+  // 128-byte slices (8 lanes x 16 bytes per row) rather than as 16-byte
+  // pieces of 32 rows per instruction: per wave and 32-dim slice t, the
+  // normalised O^T (32 queries x 32 dims, fp32) is staged in the K/V
+  // buffers, then lane L merges and stores dims 4 (L & 7) .. +3 of staged
+  // query (L >> 3) + 8 k.
   const bool to_final = OUT == kOutFinal || ((OUT == kOutLeaf || OUT == kOutMerge) && piece == 0);
   const bool to_acc = ((OUT == kOutLeaf || OUT == kOutMerge) && piece != 0) || OUT == kOutAcc;
+  constexpr int SST = 36;                         // staged row stride (floats)
+  constexpr int STG = 32 * SST + 64;              // floats per wave: slice, lse, rows
+  static_assert(NW * STG * 4 <= 2 * G::BUF, "epilogue staging fits the K/V buffers");
+  float* stg = reinterpret_cast<float*>(smem) + wave * STG;
+  float* stg_lse = stg + 32 * SST;
+  int* stg_row = reinterpret_cast<int*>(stg_lse + 32);
+  auto wave_sync = [&]() {
+    __builtin_amdgcn_fence(__ATOMIC_SEQ_CST, "wavefront");
+    __builtin_amdgcn_wave_barrier();
+    __builtin_amdgcn_fence(__ATOMIC_SEQ_CST, "wavefront");
+  };
+  __syncthreads();                                // every wave is done with the K/V tiles
 #pragma unroll
   for (int u = 0; u < NQT; ++u) {
     const float ltot = lsum[u] + __shfl_xor(lsum[u], 32);
     const bool any = ltot > 0.f;
     const float inv = any ? 1.f / ltot : 0.f;
     const float lse2 = any ? (mrun[u] + log2f(ltot)) * kLn2 : -INFINITY;
-    if (ql[u] >= qend) continue;
-
-    const int64_t ridx = static_cast<int64_t>(bh) * p.n + (LEAF ? qrow0 + ql[u] : orow[u]);
-
-    float w_new = 1.f, w_old = 0.f, lse_out = lse2;
-    if constexpr (OUT == kOutMerge) {
-      const float l1 = p.acc_lse[ridx];
-      const float mm = fmaxf(l1, lse2);
-      if (mm == -INFINITY) {
-        lse_out = -INFINITY;
-        w_new = 0.f;
-      } else {
-        lse_out = mm + logf(expf(l1 - mm) + expf(lse2 - mm));
-        w_old = expf(l1 - lse_out);
-        w_new = expf(lse2 - lse_out);
-      }
+    if (h2 == 0) {
+      stg_lse[col] = lse2;
+      stg_row[col] = ql[u] >= qend ? -1 : (OUT == kOutPartial ? ql[u] : (LEAF ? qrow0 + ql[u] : orow[u]));
     }
 #pragma unroll
-    for (int t = 0; t < NDT; ++t)
+    for (int t = 0; t < NDT; ++t) {
 #pragma unroll
       for (int g = 0; g < 4; ++g) {
-        const int dc = 32 * t + 8 * g + 4 * h2;   // 4 consecutive columns
-        floatx4 val;
+        floatx4 v;
 #pragma unroll
-        for (int i = 0; i < 4; ++i) val[i] = o[u][t][4 * g + i] * inv;
-        if constexpr (OUT == kOutMerge) {
-          const floatx4 old = *reinterpret_cast<const floatx4*>(p.acc_o + ridx * D + dc);
+        for (int i = 0; i < 4; ++i) v[i] = o[u][t][4 * g + i] * inv;
+        *reinterpret_cast<floatx4*>(stg + col * SST + 8 * g + 4 * h2) = v;
+      }
+      wave_sync();
+      const int c = lane & 7;
+      const int dc = 32 * t + 4 * c;              // 4 consecutive columns
 #pragma unroll
-          for (int i = 0; i < 4; ++i) val[i] = old[i] * w_old + val[i] * w_new;
-        }
+      for (int k = 0; k < 4; ++k) {
+        const int qi = (lane >> 3) + 8 * k;
+        const int rowv = stg_row[qi];
+        if (rowv < 0) continue;
+        const float lq = stg_lse[qi];
+        floatx4 val = *reinterpret_cast<const floatx4*>(stg + qi * SST + 4 * c);
+        // one lane per row writes the lse, on the last slice: a merge reads
+        // the old accumulator lse on every slice
+        const bool head = t == NDT - 1 && c == 0;
         if constexpr (OUT == kOutPartial) {
-          *reinterpret_cast<floatx4*>(p.part_o + (qpiece * p.seg + ql[u]) * D + dc) = val;
+          const int64_t pr = qpiece * p.seg + rowv;
+          *reinterpret_cast<floatx4*>(p.part_o + pr * D + dc) = val;
+          if (head) p.part_lse[pr] = lq;
         } else {
+          const int64_t ridx = static_cast<int64_t>(bh) * p.n + rowv;
+          float w_new = 1.f, w_old = 0.f, lse_out = lq;
+          if constexpr (OUT == kOutMerge) {
+            const float l1 = p.acc_lse[ridx];
+            const float mm = fmaxf(l1, lq);
+            if (mm == -INFINITY) {
+              lse_out = -INFINITY;
+              w_new = 0.f;
+            } else {
+              lse_out = mm + logf(expf(l1 - mm) + expf(lq - mm));
+              w_old = expf(l1 - lse_out);
+              w_new = expf(lq - lse_out);
+            }
+            const floatx4 old = *reinterpret_cast<const floatx4*>(p.acc_o + ridx * D + dc);
+#pragma unroll
+            for (int i = 0; i < 4; ++i) val[i] = old[i] * w_old + val[i] * w_new;
+          }
           if (to_acc) {
             *reinterpret_cast<floatx4*>(p.acc_o + ridx * D + dc) = val;
+            if (head) p.acc_lse[ridx] = lse_out;
           } else if (to_final) {
             if constexpr (BF) {
               bf16x4 ob;
@@ -776,16 +816,11 @@ __global__ __launch_bounds__(64 * NW, (min_waves<T, D, KIND, NW, QPW>())) void a
             } else {
               *reinterpret_cast<floatx4*>(static_cast<float*>(p.out) + ridx * D + dc) = val;
             }
+            if (head && p.lse) p.lse[ridx] = lse_out;
           }
         }
       }
-    if (h2 == 0) {
-      if constexpr (OUT == kOutPartial) {
-        p.part_lse[qpiece * p.seg + ql[u]] = lse2;
-      } else {
-        if (to_acc) p.acc_lse[ridx] = lse_out;
-        else if (to_final && p.lse) p.lse[ridx] = lse_out;
-      }
+      wave_sync();                                // before the next slice is staged
     }
   }
 }
@@ -880,6 +915,11 @@ int launch_attention(const AttnParams& p, int timing_kind, hipStream_t s) {
   if (p.seg == 0 || p.BH == 0 || p.pieces == 0) return HA_OK;
   if (p.m > kMaxSamples) {
     set_error("attention: samples %d > %d", p.m, kMaxSamples);
+    return HA_EUNSUPPORTED;
+  }
+  const int64_t head_bytes = static_cast<int64_t>(p.n) * p.d * (p.dtype == HA_BF16 ? 2 : 4);
+  if (head_bytes >= (int64_t(1) << 32)) {
+    set_error("attention: one head of q/k/v spans %lld bytes (limit 4 GiB)", static_cast<long long>(head_bytes));
     return HA_EUNSUPPORTED;
   }
   timing_begin(timing_kind, s);
