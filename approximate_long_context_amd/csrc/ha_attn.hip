@@ -750,15 +750,61 @@ __global__ __launch_bounds__(64 * NW, (min_waves<T, D, KIND, NW, QPW>())) void a
     __builtin_amdgcn_fence(__ATOMIC_SEQ_CST, "wavefront");
   };
   __syncthreads();                                // every wave is done with the K/V tiles
+  const int c = lane & 7;                         // this lane's 4-column chunk of a slice
 #pragma unroll
   for (int u = 0; u < NQT; ++u) {
     const float ltot = lsum[u] + __shfl_xor(lsum[u], 32);
     const bool any = ltot > 0.f;
     const float inv = any ? 1.f / ltot : 0.f;
     const float lse2 = any ? (mrun[u] + log2f(ltot)) * kLn2 : -INFINITY;
+    // rows of the staged queries (clamped into range; `valid` marks the real ones)
+    const uint64_t valid = __ballot(ql[u] < qend);
     if (h2 == 0) {
+      const int qls = ql[u] < qend ? ql[u] : q0;
       stg_lse[col] = lse2;
-      stg_row[col] = ql[u] >= qend ? -1 : (OUT == kOutPartial ? ql[u] : (LEAF ? qrow0 + ql[u] : orow[u]));
+      stg_row[col] = OUT == kOutPartial ? qls : (LEAF ? qrow0 + qls : orow[u]);
+    }
+    wave_sync();
+    int rowk[4];
+    float lqk[4];
+    bool vk[4];
+#pragma unroll
+    for (int k = 0; k < 4; ++k) {
+      const int qi = (lane >> 3) + 8 * k;
+      rowk[k] = stg_row[qi];
+      lqk[k] = stg_lse[qi];
+      vk[k] = (valid >> qi) & 1ull;
+    }
+    // merge: all accumulator loads of this lane are issued before any is used
+    floatx4 oldv[NDT][4];
+    float w_old[4], w_new[4], lse_out[4];
+#pragma unroll
+    for (int k = 0; k < 4; ++k) {
+      w_old[k] = 0.f;
+      w_new[k] = 1.f;
+      lse_out[k] = lqk[k];
+    }
+    if constexpr (OUT == kOutMerge) {
+      float l1[4];
+#pragma unroll
+      for (int k = 0; k < 4; ++k) {
+        const int64_t ridx = static_cast<int64_t>(bh) * p.n + rowk[k];
+        l1[k] = p.acc_lse[ridx];
+#pragma unroll
+        for (int t = 0; t < NDT; ++t) oldv[t][k] = *reinterpret_cast<const floatx4*>(p.acc_o + ridx * D + 32 * t + 4 * c);
+      }
+#pragma unroll
+      for (int k = 0; k < 4; ++k) {
+        const float mm = fmaxf(l1[k], lqk[k]);
+        if (mm == -INFINITY) {
+          lse_out[k] = -INFINITY;
+          w_new[k] = 0.f;
+        } else {
+          lse_out[k] = mm + logf(expf(l1[k] - mm) + expf(lqk[k] - mm));
+          w_old[k] = expf(l1[k] - lse_out[k]);
+          w_new[k] = expf(lqk[k] - lse_out[k]);
+        }
+      }
     }
 #pragma unroll
     for (int t = 0; t < NDT; ++t) {
@@ -770,43 +816,27 @@ __global__ __launch_bounds__(64 * NW, (min_waves<T, D, KIND, NW, QPW>())) void a
         *reinterpret_cast<floatx4*>(stg + col * SST + 8 * g + 4 * h2) = v;
       }
       wave_sync();
-      const int c = lane & 7;
       const int dc = 32 * t + 4 * c;              // 4 consecutive columns
 #pragma unroll
       for (int k = 0; k < 4; ++k) {
         const int qi = (lane >> 3) + 8 * k;
-        const int rowv = stg_row[qi];
-        if (rowv < 0) continue;
-        const float lq = stg_lse[qi];
         floatx4 val = *reinterpret_cast<const floatx4*>(stg + qi * SST + 4 * c);
-        // one lane per row writes the lse, on the last slice: a merge reads
-        // the old accumulator lse on every slice
+        if (!vk[k]) continue;
+        // one lane per row writes the lse, on the last slice
         const bool head = t == NDT - 1 && c == 0;
         if constexpr (OUT == kOutPartial) {
-          const int64_t pr = qpiece * p.seg + rowv;
+          const int64_t pr = qpiece * p.seg + rowk[k];
           *reinterpret_cast<floatx4*>(p.part_o + pr * D + dc) = val;
-          if (head) p.part_lse[pr] = lq;
+          if (head) p.part_lse[pr] = lqk[k];
         } else {
-          const int64_t ridx = static_cast<int64_t>(bh) * p.n + rowv;
-          float w_new = 1.f, w_old = 0.f, lse_out = lq;
+          const int64_t ridx = static_cast<int64_t>(bh) * p.n + rowk[k];
           if constexpr (OUT == kOutMerge) {
-            const float l1 = p.acc_lse[ridx];
-            const float mm = fmaxf(l1, lq);
-            if (mm == -INFINITY) {
-              lse_out = -INFINITY;
-              w_new = 0.f;
-            } else {
-              lse_out = mm + logf(expf(l1 - mm) + expf(lq - mm));
-              w_old = expf(l1 - lse_out);
-              w_new = expf(lq - lse_out);
-            }
-            const floatx4 old = *reinterpret_cast<const floatx4*>(p.acc_o + ridx * D + dc);
 #pragma unroll
-            for (int i = 0; i < 4; ++i) val[i] = old[i] * w_old + val[i] * w_new;
+            for (int i = 0; i < 4; ++i) val[i] = oldv[t][k][i] * w_old[k] + val[i] * w_new[k];
           }
           if (to_acc) {
             *reinterpret_cast<floatx4*>(p.acc_o + ridx * D + dc) = val;
-            if (head) p.acc_lse[ridx] = lse_out;
+            if (head) p.acc_lse[ridx] = lse_out[k];
           } else if (to_final) {
             if constexpr (BF) {
               bf16x4 ob;
@@ -816,7 +846,7 @@ __global__ __launch_bounds__(64 * NW, (min_waves<T, D, KIND, NW, QPW>())) void a
             } else {
               *reinterpret_cast<floatx4*>(static_cast<float*>(p.out) + ridx * D + dc) = val;
             }
-            if (head && p.lse) p.lse[ridx] = lse_out;
+            if (head && p.lse) p.lse[ridx] = lse_out[k];
           }
         }
       }
