@@ -124,6 +124,8 @@ def main():
     ap.add_argument("--steps", type=int, default=10)
     ap.add_argument("--warmup", type=int, default=3)
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-extras", action="store_true",
+                    help="skip the other configurations and the error against exact attention")
     ap.add_argument("--workload", default="long131k")
     ap.add_argument("--copy-calibration", type=int, default=0, metavar="MIB",
                     help="also run 5 device-to-device copies of MIB MiB (known HBM traffic) "
@@ -268,11 +270,62 @@ def main():
         "roofline": roof,
         "kernels": breakdown,
     }
+    if not args.no_extras:
+        result["approx_rel_error"] = approx_error(ha, torch, w_nc, w_c, q, k, v, out)
+        result["configs"] = other_configs(ha, torch, dev, stream)
     if not args.no_cpu_baseline:
         result["cpu_baseline"] = cpu_baseline(w_nc, w_c, q, k, v)
     else:
         result["cpu_baseline"] = None
     print(json.dumps(result))
+
+
+def approx_error(ha, torch, w_nc, w_c, q, k, v, out):
+    """Secondary number: ||O - O_exact||_F / ||O_exact||_F of the headline
+    configuration, with O_exact from the library's exact mode (block = n
+    non-causal, min_seq_len = n causal; both oracle-checked at small n)."""
+    res = {}
+    ex = torch.empty_like(out)
+    for name, w, exact in (("noncausal", w_nc, w_nc.with_(block=w_nc.n)),
+                           ("causal", w_c, w_c.with_(min_seq_len=w_c.n))):
+        ha.forward(q, k, v, out=out, **w.method_args())
+        ha.forward(q, k, v, out=ex, **exact.method_args())
+        a = out.float()
+        b = ex.float()
+        res[name] = float(torch.linalg.vector_norm(a - b) / torch.linalg.vector_norm(b))
+        del a, b
+    return res
+
+
+def other_configs(ha, torch, dev, stream, reps=5):
+    """ms per forward and effective TFLOP/s of the other bf16 configurations
+    (not part of `value`)."""
+    from approximate_long_context_amd.workloads import WORKLOADS, make_inputs
+    res = {}
+    for name in ("c32k", "glm32k", "stress512k"):
+        w = WORKLOADS[name]
+        q, k, v = make_inputs(w, dev)
+        out = torch.empty_like(q)
+        ws = torch.empty(ha.workspace_bytes(w.batch, w.n, w.d, w.heads, w.kv_heads, w.block, w.samples,
+                                            w.proj_bits, w.causal, w.min_seq_len, w.dtype),
+                         dtype=torch.uint8, device=dev)
+        for _ in range(2):
+            ha.forward(q, k, v, out=out, workspace=ws, **w.method_args())
+        e0 = torch.cuda.Event(enable_timing=True)
+        e1 = torch.cuda.Event(enable_timing=True)
+        torch.cuda.synchronize()
+        e0.record(stream)
+        for _ in range(reps):
+            ha.forward(q, k, v, out=out, workspace=ws, **w.method_args())
+        e1.record(stream)
+        torch.cuda.synchronize()
+        ms = e0.elapsed_time(e1) / reps
+        f, _ = alg_flops(w, w.causal)
+        res[name] = {"ms": ms, "tflops": f / (ms * 1e-3) / 1e12, "causal": w.causal, "n": w.n,
+                     "heads": w.heads, "kv_heads": w.kv_heads, "head_dim": w.d,
+                     "block": w.block, "samples": w.samples}
+        del q, k, v, out, ws
+    return res
 
 
 if __name__ == "__main__":
