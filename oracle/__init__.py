@@ -1,4 +1,4 @@
-"""CPU oracle for the HyperAttention forward pass.
+"""CPU oracle for the HyperAttention forward pass and its backward.
 
 TEST INFRASTRUCTURE ONLY.  Nothing on the product path may import, call or
 link anything in this package: only ``tests/``, ``__graft_entry__.smoke()``
@@ -12,7 +12,7 @@ another precision (the fp32 hash).  Sources cited below:
 
   [S] "HyperAttention: Long-context Attention in Near-Linear Time",
       atlas.scime.ai research-map summary page; sections "Approach",
-      "Limitations", "Experimental setup" ("Builds on").
+      "Limitations", "Key results", "Experimental setup" ("Builds on").
   [A] "HyperAttention: Long-context Attention in Near-Linear Time",
       OpenReview forum page, "Abstract".
   [P] Salmon, Moraes, Dror, Shaw, "Parallel random numbers: as easy as
@@ -59,3 +59,4 @@ __all__ = [
     "lse_merge", "noncausal_problem", "causal_problem", "forward", "forward_rows",
     "exact_attention", "causal_levels",
 ]
+from . import backward  # noqa: E402  (weighted-softmax backward, fp64)

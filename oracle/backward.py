@@ -1,0 +1,151 @@
+"""Backward pass of the HyperAttention forward (dQ, dK, dV) on the CPU in fp64.
+
+Test infrastructure only (see the package docstring).
+
+Reading (the pages print no backward formulas; [S] "Key results" times the
+method forward and backward): hashing, sorting and sampling do
+not depend continuously on the inputs, so for fixed ranks and samples the
+forward of ``oracle.hyperattn`` is, row by row, a softmax over key rows with
+fixed multiplicities W_ij:
+
+    O_i = sum_j W_ij e^{s_ij} v_j / sum_j W_ij e^{s_ij},   s_ij = q_i . k_j,
+
+where, for one non-causal problem, W_ij = [j is in row i's block] + (ns/m)
+times the number of kept samples at j's sorted position (kept: outside row
+i's block); for the causal recursion W is the sum of the exact leaves'
+lower triangles and every level's quadrant weights -- the log-sum-exp merge
+of the parts is exactly the joint weighted softmax.  For an upstream dO its
+gradient is the weighted-softmax backward:
+
+    P = W o exp(S - lse),  dV = P^T dO,  dP = dO V^T,
+    D_i = sum_j P_ij dP_ij = dO_i . O_i,  dS = P o (dP - D),
+    dQ = dS K,  dK = dS^T Q,
+
+with dK and dV of a KV head summed over its query heads (grouped heads).
+The weights are built here from the same ranks, permutations and samples as
+the forward; the tests pin them against the step-by-step forward and the
+gradients against finite differences of it and, for W = 1, against autograd.
+"""
+
+import numpy as np
+
+from .gauss import projections
+from .hyperattn import (_check, causal_levels, ranks, sample_positions, sort_perm)
+
+
+def noncausal_weights(rank_q, rank_k, seed, batch_idx, head, node, block, samples):
+    """W [ns, ns] (rows: queries, columns: keys, both in original local
+    order) of one non-causal problem: 1 inside the row's diagonal block of
+    the sorted matrix, plus ns/m per sample at the key's sorted position
+    when that position lies outside the row's block."""
+    ns = len(rank_q)
+    if len(rank_k) != ns:
+        raise ValueError("square problems only")
+    if ns == 0:
+        return np.zeros((0, 0))
+    b_eff = min(block, ns)
+    if ns % b_eff:
+        raise ValueError(f"segment length {ns} is not a multiple of block {b_eff}")
+    pq = sort_perm(rank_q)
+    pk = sort_perm(rank_k)
+    spos_q = np.empty(ns, dtype=np.int64)
+    spos_q[pq] = np.arange(ns)                      # sorted position of each query row
+    spos_k = np.empty(ns, dtype=np.int64)
+    spos_k[pk] = np.arange(ns)
+    blk_q = spos_q // b_eff
+    blk_k = spos_k // b_eff
+    same = blk_q[:, None] == blk_k[None, :]
+    W = same.astype(np.float64)
+    if samples > 0:
+        idx = sample_positions(seed, batch_idx, head, node, ns, samples)
+        count = np.bincount(idx, minlength=ns)[spos_k]   # samples on each key row
+        W += np.where(same, 0.0, (ns / samples) * count[None, :])
+    return W
+
+
+def causal_weights(rank_q, rank_k, seed, batch_idx, head, cfg):
+    """W [n, n] of the causal recursion: every leaf of length <= min_seq_len
+    contributes its causal lower triangle (weight 1), every split
+    [lo, mid, hi) with node id contributes the non-causal weights of queries
+    [mid, hi) over keys [lo, mid)."""
+    n = len(rank_q)
+    causal_levels(n, cfg.min_seq_len)
+    W = np.zeros((n, n))
+
+    def rec(lo, hi, node):
+        ns = hi - lo
+        if ns <= cfg.min_seq_len:
+            W[lo:hi, lo:hi] += np.tril(np.ones((ns, ns)))
+            return
+        mid = lo + ns // 2
+        rec(lo, mid, 2 * node)
+        rec(mid, hi, 2 * node + 1)
+        W[mid:hi, lo:mid] += noncausal_weights(rank_q[mid:hi], rank_k[lo:mid], seed, batch_idx,
+                                               head, node, cfg.block, cfg.samples)
+
+    rec(0, n, 1)
+    return W
+
+
+def weighted_attention(q, k, v, W):
+    """(O, lse) of the weighted softmax sum_j W_ij e^{q_i.k_j} v_j / (its row
+    sum); rows with no positive weight give O = 0, lse = -inf."""
+    S = q @ k.T
+    with np.errstate(divide="ignore"):
+        logits = np.where(W > 0, S + np.log(np.where(W > 0, W, 1.0)), -np.inf)
+    mx = np.max(logits, axis=1, keepdims=True)
+    mx = np.where(np.isfinite(mx), mx, 0.0)
+    E = np.exp(logits - mx)
+    den = E.sum(axis=1, keepdims=True)
+    with np.errstate(divide="ignore", invalid="ignore"):
+        O = np.where(den > 0, (E @ v) / np.where(den > 0, den, 1.0), 0.0)
+        lse = np.where(den[:, 0] > 0, np.log(np.where(den[:, 0] > 0, den[:, 0], 1.0)) + mx[:, 0], -np.inf)
+    return O, lse
+
+
+def weighted_backward(q, k, v, W, do):
+    """(dq, dk, dv) of sum(do * O) for O = weighted_attention(q, k, v, W)."""
+    O, lse = weighted_attention(q, k, v, W)
+    S = q @ k.T
+    with np.errstate(invalid="ignore", over="ignore"):
+        P = np.where(W > 0, W * np.exp(S - np.where(np.isfinite(lse), lse, 0.0)[:, None]), 0.0)
+    dv = P.T @ do
+    dP = do @ v.T
+    D = np.sum(do * O, axis=1)
+    dS = P * (dP - D[:, None])
+    dq = dS @ k
+    dk = dS.T @ q
+    return dq, dk, dv
+
+
+def head_weights(q32, k32, cfg, b, h, G, R):
+    """W of query head h of batch entry b (KV head h // G)."""
+    rq = ranks(q32[b, h], R)
+    rk = ranks(k32[b, h // G], R)
+    if cfg.causal:
+        return causal_weights(rq, rk, cfg.seed, b, h, cfg)
+    return noncausal_weights(rq, rk, cfg.seed, b, h, 1, cfg.block, cfg.samples)
+
+
+def backward(q, k, v, do, cfg):
+    """Full backward: (dq [B, H, n, d], dk, dv [B, Hkv, n, d]) in fp64 for
+    the forward of ``oracle.hyperattn.forward`` with config ``cfg``.
+
+    q, k, v: float32 arrays holding the input values exactly (bf16 widened);
+    do: the upstream gradient of the output (any float array)."""
+    B, H, Hkv, n, d = _check(q, k, v, cfg)
+    G = H // Hkv
+    R = projections(cfg.seed, d, cfg.proj_bits)
+    dq = np.zeros((B, H, n, d))
+    dk = np.zeros((B, Hkv, n, d))
+    dv = np.zeros((B, Hkv, n, d))
+    for b in range(B):
+        for h in range(H):
+            W = head_weights(q, k, cfg, b, h, G, R)
+            g = h // G
+            gq, gk, gv = weighted_backward(q[b, h].astype(np.float64), k[b, g].astype(np.float64),
+                                           v[b, g].astype(np.float64), W, np.asarray(do[b, h], np.float64))
+            dq[b, h] = gq
+            dk[b, g] += gk
+            dv[b, g] += gv
+    return dq, dk, dv

@@ -1,0 +1,170 @@
+"""Pins of the oracle backward (CPU only).
+
+* the weight matrix W, fed to a plain weighted softmax, reproduces the
+  step-by-step forward of ``oracle.hyperattn`` (non-causal and causal);
+* central finite differences of that step-by-step forward (ranks and
+  samples held fixed) match the analytic gradients;
+* W = 1 (block >= n, or min_seq_len >= n causal) reduces to exact attention,
+  whose gradients torch autograd computes in fp64;
+* grouped heads: dK, dV of a KV head are the sums over its query heads;
+* planted mistakes in the backward formula are caught by the finite
+  differences.
+"""
+
+import numpy as np
+import pytest
+import torch
+
+from oracle import backward as ob
+from oracle import hyperattn as oh
+from oracle.gauss import projections
+
+pytestmark = pytest.mark.filterwarnings("ignore::RuntimeWarning")
+
+
+def _inputs(n, d, seed, scale=0.5):
+    g = np.random.default_rng(seed)
+    q = g.standard_normal((n, d)) * scale
+    k = g.standard_normal((n, d)) * scale
+    v = g.standard_normal((n, d))
+    return q, k, v
+
+
+def _ranks(q, k, r, seed):
+    R = projections(seed, q.shape[1], r)
+    return oh.ranks(q.astype(np.float32), R), oh.ranks(k.astype(np.float32), R)
+
+
+def _fwd(q, k, v, rq, rk, cfg):
+    """Step-by-step forward of one head with ranks held fixed."""
+    if cfg.causal:
+        return oh.causal_problem(q, k, v, rq, rk, cfg.seed, 0, 0, cfg)
+    return oh.noncausal_problem(q, k, v, rq, rk, cfg.seed, 0, 0, 1, cfg.block, cfg.samples)
+
+
+CASES = [
+    oh.HAConfig(block=16, samples=12, proj_bits=4, seed=3),
+    oh.HAConfig(block=8, samples=40, proj_bits=5, seed=4),                  # many duplicate samples
+    oh.HAConfig(block=16, samples=10, proj_bits=4, causal=True, min_seq_len=16, seed=5),
+    oh.HAConfig(block=4, samples=6, proj_bits=3, causal=True, min_seq_len=8, seed=6),
+]
+
+
+def _weights(rq, rk, cfg):
+    if cfg.causal:
+        return ob.causal_weights(rq, rk, cfg.seed, 0, 0, cfg)
+    return ob.noncausal_weights(rq, rk, cfg.seed, 0, 0, 1, cfg.block, cfg.samples)
+
+
+@pytest.mark.parametrize("cfg", CASES)
+def test_weights_reproduce_the_forward(cfg):
+    q, k, v = _inputs(64, 8, cfg.seed)
+    rq, rk = _ranks(q, k, cfg.proj_bits, cfg.seed)
+    o, lse = _fwd(q, k, v, rq, rk, cfg)
+    W = _weights(rq, rk, cfg)
+    o2, lse2 = ob.weighted_attention(q, k, v, W)
+    assert np.max(np.abs(o - o2)) < 1e-12
+    assert np.max(np.abs(lse - lse2)) < 1e-12
+
+
+@pytest.mark.parametrize("cfg", CASES)
+def test_gradients_match_finite_differences(cfg):
+    n, d = 64, 8
+    q, k, v = _inputs(n, d, cfg.seed + 10)
+    rq, rk = _ranks(q, k, cfg.proj_bits, cfg.seed)
+    do = np.random.default_rng(cfg.seed + 20).standard_normal((n, d))
+    W = _weights(rq, rk, cfg)
+    dq, dk, dv = ob.weighted_backward(q, k, v, W, do)
+
+    def loss(q_, k_, v_):
+        return float(np.sum(do * _fwd(q_, k_, v_, rq, rk, cfg)[0]))
+
+    g = np.random.default_rng(cfg.seed + 30)
+    h = 1e-5
+    for name, grad in (("q", dq), ("k", dk), ("v", dv)):
+        for _ in range(6):
+            i, j = int(g.integers(n)), int(g.integers(d))
+            args = {"q": q.copy(), "k": k.copy(), "v": v.copy()}
+            args[name][i, j] += h
+            lp = loss(args["q"], args["k"], args["v"])
+            args[name][i, j] -= 2 * h
+            lm = loss(args["q"], args["k"], args["v"])
+            fd = (lp - lm) / (2 * h)
+            assert abs(fd - grad[i, j]) <= 1e-6 * max(1.0, abs(fd)), (name, i, j, fd, grad[i, j])
+
+
+@pytest.mark.parametrize("causal", [False, True])
+def test_exact_case_matches_autograd(causal):
+    n, d = 48, 8
+    q, k, v = _inputs(n, d, 7)
+    do = np.random.default_rng(8).standard_normal((n, d))
+    cfg = oh.HAConfig(block=n, samples=5, proj_bits=4, causal=causal, min_seq_len=n, seed=1)
+    rq, rk = _ranks(q, k, cfg.proj_bits, cfg.seed)
+    W = _weights(rq, rk, cfg)
+    assert np.all(W == (np.tril(np.ones((n, n))) if causal else 1.0))
+    dq, dk, dv = ob.weighted_backward(q, k, v, W, do)
+    tq, tk, tv = (torch.tensor(x, dtype=torch.float64, requires_grad=True) for x in (q, k, v))
+    S = tq @ tk.T
+    if causal:
+        S = S.masked_fill(torch.triu(torch.ones(n, n, dtype=torch.bool), 1), float("-inf"))
+    out = torch.softmax(S, dim=-1) @ tv
+    out.backward(torch.tensor(do))
+    for got, ref in ((dq, tq.grad), (dk, tk.grad), (dv, tv.grad)):
+        assert np.max(np.abs(got - ref.numpy())) < 1e-12
+
+
+def test_grouped_heads_sum_over_the_group():
+    B, H, Hkv, n, d = 1, 4, 2, 32, 8
+    g = np.random.default_rng(9)
+    q = (g.standard_normal((B, H, n, d)) * 0.5).astype(np.float32)
+    k = (g.standard_normal((B, Hkv, n, d)) * 0.5).astype(np.float32)
+    v = g.standard_normal((B, Hkv, n, d)).astype(np.float32)
+    do = g.standard_normal((B, H, n, d))
+    cfg = oh.HAConfig(block=8, samples=6, proj_bits=4, seed=2)
+    dq, dk, dv = ob.backward(q, k, v, do, cfg)
+    R = projections(cfg.seed, d, cfg.proj_bits)
+    for kv in range(Hkv):
+        sk = np.zeros((n, d))
+        sv = np.zeros((n, d))
+        for h in (2 * kv, 2 * kv + 1):
+            rq, rk = oh.ranks(q[0, h], R), oh.ranks(k[0, kv], R)
+            W = ob.noncausal_weights(rq, rk, cfg.seed, 0, h, 1, cfg.block, cfg.samples)
+            gq, gk, gv = ob.weighted_backward(q[0, h].astype(np.float64), k[0, kv].astype(np.float64),
+                                              v[0, kv].astype(np.float64), W, do[0, h])
+            assert np.array_equal(dq[0, h], gq)
+            sk += gk
+            sv += gv
+        assert np.max(np.abs(dk[0, kv] - sk)) < 1e-12
+        assert np.max(np.abs(dv[0, kv] - sv)) < 1e-12
+
+
+_correct_backward = ob.weighted_backward
+
+
+def _drop_d(q, k, v, W, do):           # forgets the row term D
+    O, lse = ob.weighted_attention(q, k, v, W)
+    P = np.where(W > 0, W * np.exp(q @ k.T - lse[:, None]), 0.0)
+    dS = P * (do @ v.T)
+    return dS @ k, dS.T @ q, P.T @ do
+
+
+def _unweighted_p(q, k, v, W, do):     # drops the sample weight from P
+    O, lse = ob.weighted_attention(q, k, v, W)
+    P = np.where(W > 0, np.exp(q @ k.T - lse[:, None]), 0.0)
+    dS = P * (do @ v.T - np.sum(do * O, axis=1)[:, None])
+    return dS @ k, dS.T @ q, P.T @ do
+
+
+def _transposed_dk(q, k, v, W, do):    # dK from dS instead of dS^T
+    dq, dk, dv = _correct_backward(q, k, v, W, do)
+    O, lse = ob.weighted_attention(q, k, v, W)
+    P = np.where(W > 0, W * np.exp(q @ k.T - lse[:, None]), 0.0)
+    dS = P * (do @ v.T - np.sum(do * O, axis=1)[:, None])
+    return dq, dS @ q, dv
+
+
+@pytest.mark.parametrize("mutant", [_drop_d, _unweighted_p, _transposed_dk])
+def test_planted_backward_mistakes_are_caught(monkeypatch, mutant):
+    monkeypatch.setattr(ob, "weighted_backward", mutant)
+    with pytest.raises(AssertionError):
+        test_gradients_match_finite_differences(CASES[0])
