@@ -1,4 +1,4 @@
-"""MI355X (gfx950) HyperAttention forward: Python binding of libhyperattn.so.
+"""MI355X (gfx950) HyperAttention forward and backward: Python binding of libhyperattn.so.
 
 Argument marshalling only: every step of the method runs in the HIP
 kernels behind the C ABI declared in ``include/hyperattn.h``.  PyTorch
@@ -17,7 +17,8 @@ LIB_PATH = os.path.join(_HERE, "libhyperattn.so")
 HA_BF16, HA_F32 = 0, 1
 HA_FLAG_MATERIALIZE, HA_FLAG_UNFUSED = 1, 2
 HA_OK, HA_EINVAL, HA_EUNSUPPORTED, HA_EWORKSPACE, HA_ESHAPE, HA_EHIP = 0, -1, -2, -3, -4, -5
-KERNEL_CLASSES = ["proj", "hash", "sort", "samples", "gather", "attend", "merge", "leaf", "quadrant"]
+KERNEL_CLASSES = ["proj", "hash", "sort", "samples", "gather", "attend", "merge", "leaf", "quadrant",
+                  "bwd_dq", "bwd_dkv"]
 
 _c_int, _c_i64, _c_u64, _c_size, _vp = ctypes.c_int, ctypes.c_int64, ctypes.c_uint64, ctypes.c_size_t, ctypes.c_void_p
 
@@ -27,6 +28,8 @@ _SIGNATURES = {
     "hyperattn_workspace_bytes": (_c_size, [_c_int] * 12),
     "hyperattn_forward": (_c_int, [_vp, _vp, _vp, _c_int] + [_c_int] * 10 + [_c_u64, _vp, _vp, _vp, _c_size, _vp]),
     "hyperattn_forward_ex": (_c_int, [_vp, _vp, _vp, _c_int] + [_c_int] * 10 + [_c_u64, _c_int, _vp, _vp, _vp, _c_size, _vp]),
+    "hyperattn_backward_workspace_bytes": (_c_size, [_c_int] * 11),
+    "hyperattn_backward": (_c_int, [_vp] * 6 + [_c_int] * 11 + [_c_u64, _vp, _vp, _vp, _vp, _c_size, _vp]),
     "hyperattn_projections_host": (_c_int, [_c_u64, _c_int, _c_int, _vp]),
     "hyperattn_projections": (_c_int, [_c_u64, _c_int, _c_int, _vp, _vp]),
     "hyperattn_hash": (_c_int, [_vp, _c_int, _c_i64, _c_int, _c_int, _vp, _vp, _vp]),
@@ -145,6 +148,42 @@ def forward(q, k, v, *, block, samples, proj_bits, causal=False, min_seq_len=0, 
           proj_bits, int(bool(causal)), min_seq_len, ctypes.c_uint64(seed), flags, _ptr(out),
           _ptr(lse), _ptr(workspace), workspace.numel(), _stream(dev))
     return out, lse
+
+
+def backward(q, k, v, out, lse, dout, *, block, samples, proj_bits, causal=False, min_seq_len=0,
+             seed=0, dq=None, dk=None, dv=None, workspace=None):
+    """Gradients of sum(dout * out) for (out, lse) = forward(q, k, v, ...)
+    with the same arguments.  bf16 inputs; returns float32 (dq like q,
+    dk and dv like k)."""
+    _need(q, "q", torch.bfloat16)
+    dev = q.device
+    for t, name in ((k, "k"), (v, "v"), (out, "out"), (dout, "dout")):
+        _need(t, name, torch.bfloat16, dev)
+    _need(lse, "lse", torch.float32, dev)
+    if q.dim() != 4 or k.dim() != 4 or k.shape != v.shape or out.shape != q.shape or dout.shape != q.shape:
+        raise ValueError("q, out, dout must be [B, H, n, d] and k, v [B, Hkv, n, d]")
+    B, H, n, d = q.shape
+    Hkv = k.shape[1]
+    if lse.shape != (B, H, n):
+        raise ValueError("lse must be [B, H, n]")
+    if dq is None:
+        dq = torch.empty(q.shape, dtype=torch.float32, device=dev)
+    if dk is None:
+        dk = torch.empty(k.shape, dtype=torch.float32, device=dev)
+    if dv is None:
+        dv = torch.empty(k.shape, dtype=torch.float32, device=dev)
+    for t, name, shp in ((dq, "dq", q.shape), (dk, "dk", k.shape), (dv, "dv", k.shape)):
+        _need(t, name, torch.float32, dev)
+        if t.shape != shp:
+            raise ValueError(f"{name} must have shape {tuple(shp)}")
+    wsb = lib().hyperattn_backward_workspace_bytes(B, n, d, H, Hkv, block, samples, proj_bits,
+                                                   int(bool(causal)), min_seq_len, HA_BF16)
+    if workspace is None or workspace.numel() < wsb:
+        workspace = torch.empty(max(wsb, 256), dtype=torch.uint8, device=dev)
+    _call("hyperattn_backward", _ptr(q), _ptr(k), _ptr(v), _ptr(out), _ptr(lse), _ptr(dout), HA_BF16,
+          B, n, d, H, Hkv, block, samples, proj_bits, int(bool(causal)), min_seq_len, ctypes.c_uint64(seed),
+          _ptr(dq), _ptr(dk), _ptr(dv), _ptr(workspace), workspace.numel(), _stream(dev))
+    return dq, dk, dv
 
 
 # ---- stage entry points ------------------------------------------------------

@@ -393,6 +393,96 @@ static int forward_impl(const void* q, const void* k, const void* v, Shape sh, u
   return HA_OK;
 }
 
+// ---- backward (non-causal) ------------------------------------------------------
+// Same projections, hashes, sorts and samples as the forward (recomputed
+// from the seed), then D = rowsum(dO * O), dQ, the block part of dK / dV
+// (stored) and the sample part of dK / dV (added).
+
+static size_t backward_plan(const Shape& sh, void* ws, size_t cap, Plan* pl, float** drow) {
+  Shape f = sh;
+  f.flags = 0;
+  *pl = make_plan(f, ws, cap);
+  Carve cv(ws, cap);
+  cv.used = pl->total;
+  const int64_t BH = static_cast<int64_t>(sh.batch) * sh.heads;
+  *drow = cv.take<float>(BH * sh.n);
+  return align_up(cv.used, 256) + 256;
+}
+
+static int backward_impl(const void* q, const void* k, const void* v, const void* out, const float* lse,
+                         const void* dout, Shape sh, uint64_t seed, float* dq, float* dk, float* dv, void* ws,
+                         size_t ws_bytes, hipStream_t s) {
+  HA_TRY(validate(sh));
+  if (sh.causal) {
+    set_error("backward: causal problems are not built yet");
+    return HA_EUNSUPPORTED;
+  }
+  if (sh.dtype != HA_BF16) {
+    set_error("backward: bf16 inputs only");
+    return HA_EUNSUPPORTED;
+  }
+  if (sh.flags) {
+    set_error("backward takes no flags");
+    return HA_EINVAL;
+  }
+  if (sh.n == 0 || sh.batch == 0 || sh.heads == 0) return HA_OK;
+  if (!q || !k || !v || !out || !lse || !dout || !dq || !dk || !dv) {
+    set_error("null pointer argument");
+    return HA_EINVAL;
+  }
+  Plan pl;
+  float* drow = nullptr;
+  const size_t need = backward_plan(sh, nullptr, 0, &pl, &drow);
+  if (!ws || ws_bytes < need) {
+    set_error("workspace of %zu bytes < %zu required", ws_bytes, need);
+    return HA_EWORKSPACE;
+  }
+  if (reinterpret_cast<uintptr_t>(ws) % 256) {
+    set_error("workspace must be 256-byte aligned");
+    return HA_EINVAL;
+  }
+  backward_plan(sh, ws, ws_bytes, &pl, &drow);
+  const int64_t BH = static_cast<int64_t>(sh.batch) * sh.heads;
+  const int64_t BK = static_cast<int64_t>(sh.batch) * sh.kv_heads;
+  if (static_cast<int64_t>(sh.n) * sh.d * 2 >= (int64_t(1) << 32)) {
+    set_error("backward: one head of q/k/v spans 4 GiB or more");
+    return HA_EUNSUPPORTED;
+  }
+  HA_TRY(launch_projections(seed, sh.d, sh.r, pl.R, s));
+  HA_TRY(launch_hash(q, sh.dtype, BH * sh.n, sh.d, sh.r, pl.R, pl.rank_q, s));
+  HA_TRY(launch_hash(k, sh.dtype, BK * sh.n, sh.d, sh.r, pl.R, pl.rank_k, s));
+  HA_TRY(launch_sort(pl.rank_q, BH, sh.n, sh.n, 0, sh.n, 1, sh.r, pl.perm_q, pl.sort_ws, pl.sort_ws_bytes, s));
+  HA_TRY(launch_sort(pl.rank_k, BK, sh.n, sh.n, 0, sh.n, 1, sh.r, pl.perm_k, pl.sort_ws, pl.sort_ws_bytes, s));
+  HA_TRY(launch_sample_indices(seed, sh.batch, sh.heads, 1, 1, sh.n, sh.samples, pl.sidx, s));
+  BwdParams bp;
+  bp.q = q;
+  bp.k = k;
+  bp.v = v;
+  bp.out = out;
+  bp.dout = dout;
+  bp.lse = lse;
+  bp.drow = drow;
+  bp.d = sh.d;
+  bp.n = sh.n;
+  bp.H = sh.heads;
+  bp.Hkv = sh.kv_heads;
+  bp.BH = static_cast<int>(BH);
+  bp.seg = sh.n;
+  bp.perm_q = pl.perm_q;
+  bp.perm_k = pl.perm_k;
+  bp.sidx = pl.sidx;
+  bp.m = sh.samples;
+  bp.log2w = sh.samples > 0 ? static_cast<float>(std::log2(static_cast<double>(sh.n) / sh.samples)) : 0.f;
+  bp.b_eff = sh.block < sh.n ? sh.block : sh.n;
+  bp.dq = dq;
+  bp.dk = dk;
+  bp.dv = dv;
+  HA_TRY(launch_bwd_rowdot(bp, s));
+  HA_TRY(launch_bwd_dq(bp, s));
+  HA_TRY(launch_bwd_dkv(bp, false, s));
+  return launch_bwd_dkv(bp, true, s);
+}
+
 }  // namespace ha
 
 using namespace ha;
@@ -428,6 +518,27 @@ int hyperattn_forward(const void* q, const void* k, const void* v, int dtype, in
   return hyperattn_forward_ex(q, k, v, dtype, batch, n, d, heads, kv_heads, block, samples,
                               proj_bits, causal, min_seq_len, seed, 0, out, lse, workspace,
                               workspace_bytes, stream);
+}
+
+size_t hyperattn_backward_workspace_bytes(int batch, int n, int d, int heads, int kv_heads, int block,
+                                          int samples, int proj_bits, int causal, int min_seq_len,
+                                          int dtype) {
+  Shape sh{batch, n, d, heads, kv_heads, block, samples, proj_bits, causal, min_seq_len, dtype, 0};
+  if (validate(sh) != HA_OK) return 0;
+  Plan pl;
+  float* drow = nullptr;
+  return backward_plan(sh, nullptr, 0, &pl, &drow);
+}
+
+int hyperattn_backward(const void* q, const void* k, const void* v, const void* out, const float* lse,
+                       const void* dout, int dtype, int batch, int n, int d, int heads, int kv_heads,
+                       int block, int samples, int proj_bits, int causal, int min_seq_len, uint64_t seed,
+                       float* dq, float* dk, float* dv, void* workspace, size_t workspace_bytes,
+                       void* stream) {
+  g_last_error.clear();
+  Shape sh{batch, n, d, heads, kv_heads, block, samples, proj_bits, causal, min_seq_len, dtype, 0};
+  return backward_impl(q, k, v, out, lse, dout, sh, seed, dq, dk, dv, workspace, workspace_bytes,
+                       static_cast<hipStream_t>(stream));
 }
 
 int hyperattn_projections_host(uint64_t seed, int d, int proj_bits, float* host_out) {

@@ -41,13 +41,12 @@
 #include <cstring>
 #include <type_traits>
 
+#include "ha_device.h"
 #include "ha_kernels.h"
 
 namespace ha {
 
 constexpr int kKT = 64;                // keys per LDS tile
-constexpr float kLog2e = 1.4426950408889634f;
-constexpr float kLn2 = 0.6931471805599453f;
 constexpr float kRescale = 8.f;        // log2 slack before rescaling
 
 constexpr int align16(int x) { return (x + 15) / 16 * 16; }
@@ -77,34 +76,6 @@ struct Geo {
 // LDS bytes after the two K/V buffers (sorted problems): brow[bcap],
 // srow[m], spos[m], rrow[m] and one count per 64 samples.
 __host__ __device__ constexpr int list_bytes(int bcap, int m) { return 4 * (bcap + 3 * m + (m + 63) / 64); }
-
-__device__ __forceinline__ int xcd_remap(int bid, int nblocks) {
-  // Dispatch places workgroup i on XCD i % 8; give each XCD a contiguous
-  // range of logical tiles so tiles that share keys share an L2.
-  const int full = nblocks / 8 * 8;
-  if (bid >= full) return bid;
-  const int per = nblocks / 8;
-  return (bid % 8) * per + bid / 8;
-}
-
-__device__ __forceinline__ float fast_exp2(float x) { return __builtin_amdgcn_exp2f(x); }
-
-// 16-byte load from a workgroup-uniform base plus a per-lane byte offset
-// below 2^32 (one head's rows; the host checks n * d * element < 2^32), so
-// the base stays in scalar registers and the lane carries 32 bits.
-__device__ __forceinline__ uint4v ld16(const void* base, uint32_t off) {
-  return *reinterpret_cast<const uint4v*>(static_cast<const char*>(base) + off);
-}
-
-typedef short short4v __attribute__((ext_vector_type(4)));
-typedef __attribute__((address_space(3))) short4v lds_short4v;
-
-// 4 bf16 of a transposing LDS read (gfx950 ds_read_b64_tr_b16): inside each
-// group of 16 lanes, lane i receives element (i & 3) of the 8-byte rows
-// addressed by lanes 4v + (i >> 2), v = 0..3.
-__device__ __forceinline__ short4v lds_read_tr16(const void* p) {
-  return __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_short4v*)(const_cast<void*>(p)));
-}
 
 // Minimum waves per SIMD the register allocation must allow: 4 (<= 128
 // VGPRs) for the bf16 d = 64 shapes of 8 waves x 32 queries, where it fits

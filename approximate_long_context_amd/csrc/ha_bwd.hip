@@ -1,0 +1,573 @@
+// Backward of the HyperAttention forward on gfx950 (non-causal problems).
+//
+// ("HyperAttention: Long-context Attention in Near-Linear Time",
+// research-map summary: section Approach for the forward; section Key
+// results times the method forward and backward.)
+//
+// For fixed ranks and samples the forward is a softmax over key rows with
+// fixed multiplicities W (1 inside the query's block of the sorted matrix,
+// seg / m per kept sample), so with P = W o exp(S - lse) rebuilt from the
+// forward's lse, D = rowsum(dO o O) and dS = P o (dO V^T - D):
+//     dQ = dS K,   dK = dS^T Q,   dV = P^T dO.
+// The kernels keep the forward's conventions (bf16 operands, fp32
+// accumulation, v_mfma_f32_32x32x16_bf16 with each lane owning one column
+// of a 32-wide result, 64-row tiles double-buffered through LDS):
+//   * bwd_rowdot_kernel: D for every row;
+//   * bwd_dq_kernel: query-owned like the forward -- a workgroup of 8 waves
+//     owns 256 consecutive sorted queries, block and sample key tiles
+//     stream through LDS; per 32-key half S^T = K Q^T and dP^T = V dO^T,
+//     dS is packed to bf16 and dQ^T += K^T dS^T reads K transposed;
+//   * bwd_dkv_kernel: key-owned -- a workgroup owns 256 sorted keys (block
+//     part, every query head of the group) or 256 sample slots of one query
+//     head and a chunk of its queries (sample part); per 32-query half
+//     S = Q K^T and dP = dO V^T with a lane owning a key column, then
+//     dV^T += dO^T P and dK^T += Q^T dS read Q and dO transposed.  Block
+//     keys are stored (each key's block is owned by one workgroup); sample
+//     keys then add their chunk's share with fp32 atomics.
+#include <cmath>
+
+#include "ha_device.h"
+#include "ha_kernels.h"
+
+namespace ha {
+
+constexpr int kBT = 64;      // rows per LDS tile
+constexpr int kBW = 8;       // waves per workgroup
+constexpr int kBNT = 64 * kBW;
+constexpr int kBTQ = 32 * kBW;   // rows owned by a workgroup
+
+template <int D>
+struct BGeo {
+  static constexpr int STR = D + 8;               // LDS row stride (bf16 elements)
+  static constexpr int TB = kBT * STR * 2;        // bytes of one 64-row tile
+  static constexpr int CPR = D / 8;               // 16-byte chunks per row
+  static constexpr int CPT = kBT * CPR / kBNT;    // chunks per thread per tile
+  static constexpr int NQF = D / 16;              // k-chunks of one MFMA operand row
+  static constexpr int NDT = D / 32;              // 32-column result tiles over d
+  static_assert((kBT * CPR) % kBNT == 0, "tile split");
+};
+
+// ---- D = rowsum(dO o O) -------------------------------------------------------------
+
+template <int D>
+__global__ __launch_bounds__(256) void bwd_rowdot_kernel(const bf16* __restrict__ o, const bf16* __restrict__ dout,
+                                                         int64_t rows, float* __restrict__ drow) {
+  constexpr int LPR = D / 8;                      // lanes per row, 8 elements each
+  constexpr int RPW = 64 / LPR;
+  const int lane = threadIdx.x & 63;
+  const int64_t wave = (static_cast<int64_t>(blockIdx.x) * blockDim.x + threadIdx.x) >> 6;
+  const int64_t nwaves = (static_cast<int64_t>(gridDim.x) * blockDim.x) >> 6;
+  for (int64_t r0 = wave * RPW; r0 < rows; r0 += nwaves * RPW) {
+    const int64_t row = r0 + lane / LPR;
+    float acc = 0.f;
+    if (row < rows) {
+      const int64_t off = row * D + 8 * (lane % LPR);
+      const uint4v a = *reinterpret_cast<const uint4v*>(o + off);
+      const uint4v g = *reinterpret_cast<const uint4v*>(dout + off);
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        acc += __uint_as_float(a[i] << 16) * __uint_as_float(g[i] << 16);
+        acc += __uint_as_float(a[i] & 0xFFFF0000u) * __uint_as_float(g[i] & 0xFFFF0000u);
+      }
+    }
+#pragma unroll
+    for (int off = LPR / 2; off >= 1; off >>= 1) acc += __shfl_xor(acc, off);
+    if (row < rows && lane % LPR == 0) drow[row] = acc;
+  }
+}
+
+int launch_bwd_rowdot(const BwdParams& p, hipStream_t s) {
+  const int64_t rows = static_cast<int64_t>(p.BH) * p.n;
+  if (rows == 0) return HA_OK;
+  const int rpw = 64 / (p.d / 8);
+  int64_t blocks = (rows + 4 * rpw - 1) / (4 * rpw);
+  if (blocks > 16384) blocks = 16384;
+  const bf16* o = static_cast<const bf16*>(p.out);
+  const bf16* g = static_cast<const bf16*>(p.dout);
+  if (p.d == 64) hipLaunchKernelGGL(bwd_rowdot_kernel<64>, dim3(blocks), dim3(256), 0, s, o, g, rows, p.drow);
+  else hipLaunchKernelGGL(bwd_rowdot_kernel<128>, dim3(blocks), dim3(256), 0, s, o, g, rows, p.drow);
+  return after_launch("backward rowdot", s);
+}
+
+// ---- dQ (query-owned) -----------------------------------------------------------------
+
+// LDS after the two K/V tile buffers: brow[bcap], srow[m], spos[m], rrow[m],
+// one count per 64 samples.
+static int dq_list_bytes(int bcap, int m) { return 4 * (bcap + 3 * m + (m + 63) / 64); }
+
+template <int D>
+__global__ __launch_bounds__(kBNT, 2) void bwd_dq_kernel(BwdParams p) {
+  typedef BGeo<D> G;
+  constexpr int NQF = G::NQF, NDT = G::NDT;
+  extern __shared__ __attribute__((aligned(16))) char smem[];
+  const int tid = threadIdx.x;
+  const int lane = tid & 63;
+  const int wave = tid >> 6;
+  const int h2 = lane >> 5;
+  const int col = lane & 31;
+
+  const int QT = (p.seg + kBTQ - 1) / kBTQ;
+  const int lid = xcd_remap(blockIdx.x, gridDim.x);
+  const int qt = lid % QT;
+  const int bh = lid / QT;
+  const int b = bh / p.H;
+  const int bkv = b * p.Hkv + (bh % p.H) / (p.H / p.Hkv);
+  const int q0 = qt * kBTQ;
+  const int qend = min(q0 + kBTQ, p.seg);
+  const int b_eff = p.b_eff;
+
+  const bf16* qb = static_cast<const bf16*>(p.q) + static_cast<int64_t>(bh) * p.n * D;
+  const bf16* gb = static_cast<const bf16*>(p.dout) + static_cast<int64_t>(bh) * p.n * D;
+  const bf16* kbase = static_cast<const bf16*>(p.k) + static_cast<int64_t>(bkv) * p.n * D;
+  const bf16* vbase = static_cast<const bf16*>(p.v) + static_cast<int64_t>(bkv) * p.n * D;
+  const int32_t* pq = p.perm_q + static_cast<int64_t>(bh) * p.seg;
+  const int32_t* pk = p.perm_k + static_cast<int64_t>(bkv) * p.seg;
+
+  const int ka0 = (q0 / b_eff) * b_eff;
+  const int ka1 = min(((qend - 1) / b_eff + 1) * b_eff, p.seg);
+  const bool multi_block = (q0 / b_eff) != ((qend - 1) / b_eff);
+  const bool samp = p.m > 0;
+  const bool samp_multi = samp && multi_block;
+  const int nbl = ka1 - ka0;
+
+  // ---- key row lists (as the forward): block rows, compacted sample rows
+  int* brow = reinterpret_cast<int*>(smem + 4 * G::TB);
+  int* srow = brow + p.bcap;
+  int* spos = srow + p.m;
+  int* rrow = spos + p.m;
+  int* ccount = rrow + p.m;
+  const bool blist = p.bcap > 0;
+  int nsamp = 0;
+  if (blist)
+    for (int j = tid; j < nbl; j += kBNT) brow[j] = pk[ka0 + j];
+  if (samp) {
+    const int32_t* si = p.sidx + static_cast<int64_t>(bh) * p.m;
+    const int tq = q0 / b_eff;
+    int* raw = samp_multi ? srow : rrow;
+    for (int c = 64 * wave; c < p.m; c += kBNT) {
+      const int i = c + lane;
+      const int sp = i < p.m ? si[i] : 0;
+      if (i < p.m) {
+        spos[i] = sp;
+        raw[i] = pk[sp];
+      }
+      const uint64_t keep = __ballot(i < p.m && (samp_multi || (sp / b_eff) != tq));
+      if (lane == 0) ccount[c / 64] = __popcll(keep);
+    }
+    __syncthreads();
+    for (int k = 0; k < (p.m + 63) / 64; ++k) nsamp += ccount[k];
+    if (!samp_multi) {
+      for (int c = 64 * wave; c < p.m; c += kBNT) {
+        int base = 0;
+        for (int k = 0; k < c / 64; ++k) base += ccount[k];
+        const int i = c + lane;
+        const bool keep = i < p.m && (spos[i] / b_eff) != tq;
+        const uint64_t bal = __ballot(keep);
+        const uint64_t lower = lane == 0 ? 0ull : (~0ull >> (64 - lane));
+        if (keep) srow[base + __popcll(bal & lower)] = rrow[i];
+      }
+    }
+  }
+  __syncthreads();
+
+  // ---- this lane's query: operands, lse and D
+  const int ql = q0 + wave * 32 + col;
+  const int qls = ql < qend ? ql : q0;
+  const int orow = pq[qls];
+  const int64_t ridx = static_cast<int64_t>(bh) * p.n + orow;
+  const float lse2 = p.lse[ridx] * kLog2e;
+  const float dl = p.drow[ridx];
+  bf16x8 qf[NQF], gf[NQF];
+#pragma unroll
+  for (int c = 0; c < NQF; ++c) {
+    const uint32_t off = static_cast<uint32_t>(orow * D + 16 * c + 8 * h2) * 2;
+    qf[c] = __builtin_bit_cast(bf16x8, ld16(qb, off));
+    gf[c] = __builtin_bit_cast(bf16x8, ld16(gb, off));
+  }
+  floatx16 acc[NDT];
+#pragma unroll
+  for (int t = 0; t < NDT; ++t)
+#pragma unroll
+    for (int r = 0; r < 16; ++r) acc[t][r] = 0.f;
+
+  const int nA = nbl > 0 ? (nbl + kBT - 1) / kBT : 0;
+  const int nB = (nsamp + kBT - 1) / kBT;
+  const int ntiles = nA + nB;
+
+  // ---- tile staging
+  const int c_in_row = tid % G::CPR;
+  const int j_first = tid / G::CPR;
+  constexpr int JSTEP = kBNT / G::CPR;
+  uint4v kreg[G::CPT], vreg[G::CPT];
+  auto load_tile = [&](int it) {
+    const bool isB = it >= nA;
+    const int kb = isB ? (it - nA) * kBT : ka0 + it * kBT;
+    const int kcnt = isB ? min(kBT, nsamp - kb) : min(kBT, ka1 - kb);
+#pragma unroll
+    for (int c = 0; c < G::CPT; ++c) {
+      const int j = j_first + c * JSTEP;
+      uint4v kw = {0u, 0u, 0u, 0u}, vw = {0u, 0u, 0u, 0u};
+      if (j < kcnt) {
+        const int row = isB ? srow[kb + j] : (blist ? brow[kb - ka0 + j] : pk[kb + j]);
+        const uint32_t off = static_cast<uint32_t>(row * D + 8 * c_in_row) * 2;
+        kw = ld16(kbase, off);
+        vw = ld16(vbase, off);
+      }
+      kreg[c] = kw;
+      vreg[c] = vw;
+    }
+  };
+  auto store_tile = [&](int buf) {
+    bf16* ks = reinterpret_cast<bf16*>(smem + (2 * buf) * G::TB);
+    bf16* vs = reinterpret_cast<bf16*>(smem + (2 * buf + 1) * G::TB);
+#pragma unroll
+    for (int c = 0; c < G::CPT; ++c) {
+      const int j = j_first + c * JSTEP;
+      *reinterpret_cast<uint4v*>(&ks[j * G::STR + 8 * c_in_row]) = kreg[c];
+      *reinterpret_cast<uint4v*>(&vs[j * G::STR + 8 * c_in_row]) = vreg[c];
+    }
+  };
+
+  const int row_blk = ql / b_eff;
+  if (ntiles > 0) load_tile(0);
+  for (int it = 0; it < ntiles; ++it) {
+    const int buf = it & 1;
+    store_tile(buf);
+    __syncthreads();
+    if (it + 1 < ntiles) load_tile(it + 1);
+    const bool isB = it >= nA;
+    const int kb = isB ? (it - nA) * kBT : ka0 + it * kBT;
+    const int kcnt = isB ? min(kBT, nsamp - kb) : min(kBT, ka1 - kb);
+    const bf16* ks = reinterpret_cast<const bf16*>(smem + (2 * buf) * G::TB);
+    const bf16* vs = reinterpret_cast<const bf16*>(smem + (2 * buf + 1) * G::TB);
+    const float off = (isB ? p.log2w : 0.f) - lse2;
+    const bool need_mask = kcnt < kBT || (isB ? samp_multi : multi_block);
+#pragma unroll
+    for (int kt = 0; kt < 2; ++kt) {
+      floatx16 s, dp;
+#pragma unroll
+      for (int r = 0; r < 16; ++r) s[r] = dp[r] = 0.f;
+#pragma unroll
+      for (int c = 0; c < NQF; ++c) {
+        const int e = (32 * kt + col) * G::STR + 16 * c + 8 * h2;
+        s = __builtin_amdgcn_mfma_f32_32x32x16_bf16(*reinterpret_cast<const bf16x8*>(&ks[e]), qf[c], s, 0, 0, 0);
+        dp = __builtin_amdgcn_mfma_f32_32x32x16_bf16(*reinterpret_cast<const bf16x8*>(&vs[e]), gf[c], dp, 0, 0, 0);
+      }
+      bf16x8 da, db;
+#pragma unroll
+      for (int r = 0; r < 16; ++r) {
+        bool ok = true;
+        if (need_mask) {
+          const int j = 32 * kt + 8 * (r >> 2) + 4 * h2 + (r & 3);
+          ok = j < kcnt;
+          if (isB) {
+            if (samp_multi) ok = ok && (spos[kb + min(j, kcnt - 1)] / b_eff) != row_blk;
+          } else if (multi_block) {
+            ok = ok && ((kb + j) / b_eff) == row_blk;
+          }
+        }
+        const float pr = ok ? fast_exp2(fmaf(s[r], kLog2e, off)) : 0.f;
+        const bf16 dsv = static_cast<bf16>(pr * (dp[r] - dl));
+        if (r < 8) da[r] = dsv;
+        else db[r - 8] = dsv;
+      }
+#pragma unroll
+      for (int t = 0; t < NDT; ++t) {
+        acc[t] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(lds_tr_operand(ks, G::STR, 2 * kt, t, lane), da, acc[t], 0, 0, 0);
+        acc[t] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(lds_tr_operand(ks, G::STR, 2 * kt + 1, t, lane), db, acc[t], 0, 0, 0);
+      }
+    }
+  }
+
+  // ---- dQ rows (fp32): register r of tile t holds column 32 t + 8 (r / 4) + 4 h2 + r % 4
+  if (ql < qend) {
+    float* dst = p.dq + ridx * D;
+#pragma unroll
+    for (int t = 0; t < NDT; ++t)
+#pragma unroll
+      for (int g = 0; g < 4; ++g) {
+        floatx4 v4;
+#pragma unroll
+        for (int i = 0; i < 4; ++i) v4[i] = acc[t][4 * g + i];
+        *reinterpret_cast<floatx4*>(dst + 32 * t + 8 * g + 4 * h2) = v4;
+      }
+  }
+}
+
+// ---- dK, dV (key-owned) ---------------------------------------------------------------
+
+// LDS per buffer: Q tile, dO tile (64 rows each), lse2[64], D[64].
+template <int D>
+constexpr int dkv_buf_bytes() { return 2 * BGeo<D>::TB + 2 * kBT * 4; }
+
+template <int D, bool SAMPLE>
+__global__ __launch_bounds__(kBNT, 2) void bwd_dkv_kernel(BwdParams p) {
+  typedef BGeo<D> G;
+  constexpr int NQF = G::NQF, NDT = G::NDT;
+  constexpr int BUF = dkv_buf_bytes<D>();
+  extern __shared__ __attribute__((aligned(16))) char smem[];
+  const int tid = threadIdx.x;
+  const int lane = tid & 63;
+  const int wave = tid >> 6;
+  const int h2 = lane >> 5;
+  const int col = lane & 31;
+  const int b_eff = p.b_eff;
+  const int G_ = p.H / p.Hkv;
+
+  // ---- work item
+  const int lid = xcd_remap(blockIdx.x, gridDim.x);
+  int bkv, bh0, nheads, k0, kend, qa0, qa1;
+  if constexpr (!SAMPLE) {
+    const int KT = (p.seg + kBTQ - 1) / kBTQ;
+    bkv = lid / KT;
+    k0 = (lid % KT) * kBTQ;
+    kend = min(k0 + kBTQ, p.seg);
+    const int b = bkv / p.Hkv;
+    bh0 = b * p.H + (bkv % p.Hkv) * G_;
+    nheads = G_;
+    qa0 = (k0 / b_eff) * b_eff;
+    qa1 = min(((kend - 1) / b_eff + 1) * b_eff, p.seg);
+  } else {
+    const int NC = (p.seg + p.qchunk - 1) / p.qchunk;
+    const int SG = (p.m + kBTQ - 1) / kBTQ;
+    const int chunk = lid % NC;
+    const int rest = lid / NC;
+    k0 = (rest % SG) * kBTQ;
+    kend = min(k0 + kBTQ, p.m);
+    bh0 = rest / SG;
+    bkv = (bh0 / p.H) * p.Hkv + (bh0 % p.H) / G_;
+    nheads = 1;
+    qa0 = chunk * p.qchunk;
+    qa1 = min(qa0 + p.qchunk, p.seg);
+  }
+  const bf16* kbase = static_cast<const bf16*>(p.k) + static_cast<int64_t>(bkv) * p.n * D;
+  const bf16* vbase = static_cast<const bf16*>(p.v) + static_cast<int64_t>(bkv) * p.n * D;
+  const int32_t* pk = p.perm_k + static_cast<int64_t>(bkv) * p.seg;
+
+  // ---- this lane's key: operands and block
+  const int kj = k0 + wave * 32 + col;           // key position (block) or sample slot (sample)
+  const bool kvalid = kj < kend;
+  const int kjs = kvalid ? kj : k0;
+  int kpos;                                      // sorted key position
+  if constexpr (SAMPLE) kpos = p.sidx[static_cast<int64_t>(bh0) * p.m + kjs];
+  else kpos = kjs;
+  const int krow = pk[kpos];
+  const int kblk = kpos / b_eff;
+  bf16x8 kf[NQF], vf[NQF];
+#pragma unroll
+  for (int c = 0; c < NQF; ++c) {
+    const uint32_t off = static_cast<uint32_t>(krow * D + 16 * c + 8 * h2) * 2;
+    kf[c] = __builtin_bit_cast(bf16x8, ld16(kbase, off));
+    vf[c] = __builtin_bit_cast(bf16x8, ld16(vbase, off));
+  }
+  floatx16 dk[NDT], dv[NDT];
+#pragma unroll
+  for (int t = 0; t < NDT; ++t)
+#pragma unroll
+    for (int r = 0; r < 16; ++r) dk[t][r] = dv[t][r] = 0.f;
+
+  const int qtiles = qa1 > qa0 ? (qa1 - qa0 + kBT - 1) / kBT : 0;
+  const int ntiles = qtiles * nheads;
+  const float wbias = SAMPLE ? p.log2w : 0.f;
+
+  // ---- tile staging: query rows of Q and dO, their lse (log2) and D
+  const int c_in_row = tid % G::CPR;
+  const int j_first = tid / G::CPR;
+  constexpr int JSTEP = kBNT / G::CPR;
+  uint4v qreg[G::CPT], greg[G::CPT];
+  float lreg = 0.f, dreg = 0.f;
+  auto load_tile = [&](int it) {
+    const int hh = it / qtiles;
+    const int tq0 = qa0 + (it % qtiles) * kBT;
+    const int qcnt = min(kBT, qa1 - tq0);
+    const int bh = bh0 + hh;
+    const bf16* qb = static_cast<const bf16*>(p.q) + static_cast<int64_t>(bh) * p.n * D;
+    const bf16* gb = static_cast<const bf16*>(p.dout) + static_cast<int64_t>(bh) * p.n * D;
+    const int32_t* pq = p.perm_q + static_cast<int64_t>(bh) * p.seg;
+#pragma unroll
+    for (int c = 0; c < G::CPT; ++c) {
+      const int j = j_first + c * JSTEP;
+      uint4v qw = {0u, 0u, 0u, 0u}, gw = {0u, 0u, 0u, 0u};
+      if (j < qcnt) {
+        const uint32_t off = static_cast<uint32_t>(pq[tq0 + j] * D + 8 * c_in_row) * 2;
+        qw = ld16(qb, off);
+        gw = ld16(gb, off);
+      }
+      qreg[c] = qw;
+      greg[c] = gw;
+    }
+    if (tid < kBT) {
+      lreg = -INFINITY;
+      dreg = 0.f;
+      if (tid < qcnt) {
+        const int64_t r = static_cast<int64_t>(bh) * p.n + pq[tq0 + tid];
+        lreg = p.lse[r] * kLog2e;
+        dreg = p.drow[r];
+      }
+    }
+  };
+  auto store_tile = [&](int buf) {
+    char* base = smem + buf * BUF;
+    bf16* qs = reinterpret_cast<bf16*>(base);
+    bf16* gs = reinterpret_cast<bf16*>(base + G::TB);
+    float* ls = reinterpret_cast<float*>(base + 2 * G::TB);
+#pragma unroll
+    for (int c = 0; c < G::CPT; ++c) {
+      const int j = j_first + c * JSTEP;
+      *reinterpret_cast<uint4v*>(&qs[j * G::STR + 8 * c_in_row]) = qreg[c];
+      *reinterpret_cast<uint4v*>(&gs[j * G::STR + 8 * c_in_row]) = greg[c];
+    }
+    if (tid < kBT) {
+      ls[tid] = lreg;
+      ls[kBT + tid] = dreg;
+    }
+  };
+
+  if (ntiles > 0) load_tile(0);
+  for (int it = 0; it < ntiles; ++it) {
+    const int buf = it & 1;
+    store_tile(buf);
+    __syncthreads();
+    if (it + 1 < ntiles) load_tile(it + 1);
+    const int tq0 = qa0 + (it % qtiles) * kBT;
+    const int qcnt = min(kBT, qa1 - tq0);
+    const char* base = smem + buf * BUF;
+    const bf16* qs = reinterpret_cast<const bf16*>(base);
+    const bf16* gs = reinterpret_cast<const bf16*>(base + G::TB);
+    const float* ls = reinterpret_cast<const float*>(base + 2 * G::TB);
+#pragma unroll
+    for (int qt = 0; qt < 2; ++qt) {
+      floatx16 s, dp;
+#pragma unroll
+      for (int r = 0; r < 16; ++r) s[r] = dp[r] = 0.f;
+#pragma unroll
+      for (int c = 0; c < NQF; ++c) {
+        const int e = (32 * qt + col) * G::STR + 16 * c + 8 * h2;
+        s = __builtin_amdgcn_mfma_f32_32x32x16_bf16(*reinterpret_cast<const bf16x8*>(&qs[e]), kf[c], s, 0, 0, 0);
+        dp = __builtin_amdgcn_mfma_f32_32x32x16_bf16(*reinterpret_cast<const bf16x8*>(&gs[e]), vf[c], dp, 0, 0, 0);
+      }
+      bf16x8 pa, pb, da, db;
+#pragma unroll
+      for (int g = 0; g < 4; ++g) {
+        const int j0 = 32 * qt + 8 * g + 4 * h2;      // 4 consecutive queries of the tile
+        const floatx4 l4 = *reinterpret_cast<const floatx4*>(ls + j0);
+        const floatx4 d4 = *reinterpret_cast<const floatx4*>(ls + kBT + j0);
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          const int r = 4 * g + i;
+          const int j = j0 + i;
+          const int qblk = (tq0 + j) / b_eff;
+          bool ok = kvalid && j < qcnt;
+          if constexpr (SAMPLE) ok = ok && qblk != kblk;
+          else ok = ok && qblk == kblk;
+          const float pr = ok ? fast_exp2(fmaf(s[r], kLog2e, wbias - l4[i])) : 0.f;
+          const bf16 pv = static_cast<bf16>(pr);
+          const bf16 dsv = static_cast<bf16>(pr * (dp[r] - d4[i]));
+          if (r < 8) {
+            pa[r] = pv;
+            da[r] = dsv;
+          } else {
+            pb[r - 8] = pv;
+            db[r - 8] = dsv;
+          }
+        }
+      }
+#pragma unroll
+      for (int t = 0; t < NDT; ++t) {
+        dv[t] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(lds_tr_operand(gs, G::STR, 2 * qt, t, lane), pa, dv[t], 0, 0, 0);
+        dv[t] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(lds_tr_operand(gs, G::STR, 2 * qt + 1, t, lane), pb, dv[t], 0, 0, 0);
+        dk[t] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(lds_tr_operand(qs, G::STR, 2 * qt, t, lane), da, dk[t], 0, 0, 0);
+        dk[t] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(lds_tr_operand(qs, G::STR, 2 * qt + 1, t, lane), db, dk[t], 0, 0, 0);
+      }
+    }
+  }
+
+  // ---- dK, dV rows (fp32): register r of tile t holds column 32 t + 8 (r / 4) + 4 h2 + r % 4
+  if (kvalid) {
+    const int64_t rbase = (static_cast<int64_t>(bkv) * p.n + krow) * D;
+#pragma unroll
+    for (int t = 0; t < NDT; ++t)
+#pragma unroll
+      for (int g = 0; g < 4; ++g) {
+        const int c0 = 32 * t + 8 * g + 4 * h2;
+        if constexpr (SAMPLE) {
+#pragma unroll
+          for (int i = 0; i < 4; ++i) {
+            unsafeAtomicAdd(p.dk + rbase + c0 + i, dk[t][4 * g + i]);
+            unsafeAtomicAdd(p.dv + rbase + c0 + i, dv[t][4 * g + i]);
+          }
+        } else {
+          floatx4 a, c;
+#pragma unroll
+          for (int i = 0; i < 4; ++i) {
+            a[i] = dk[t][4 * g + i];
+            c[i] = dv[t][4 * g + i];
+          }
+          *reinterpret_cast<floatx4*>(p.dk + rbase + c0) = a;
+          *reinterpret_cast<floatx4*>(p.dv + rbase + c0) = c;
+        }
+      }
+  }
+}
+
+// ---- launches ---------------------------------------------------------------------------
+
+template <int D>
+static int launch_dq_d(const BwdParams& p, hipStream_t s) {
+  BwdParams q = p;
+  q.bcap = 0;
+  const int64_t span = static_cast<int64_t>((kBTQ - 1) / p.b_eff + 2) * p.b_eff;
+  const int64_t cap = span < p.seg ? span : p.seg;
+  if (cap <= kBlockListCap) q.bcap = static_cast<int>(cap);
+  const size_t lds = 4 * BGeo<D>::TB + dq_list_bytes(q.bcap, p.m);
+  const int64_t blocks = static_cast<int64_t>(p.BH) * ((p.seg + kBTQ - 1) / kBTQ);
+  auto fn = bwd_dq_kernel<D>;
+  static bool attr = false;
+  if (!attr) {
+    HA_CHECK_HIP(hipFuncSetAttribute(reinterpret_cast<const void*>(fn), hipFuncAttributeMaxDynamicSharedMemorySize,
+                                     160 * 1024));
+    attr = true;
+  }
+  hipLaunchKernelGGL(fn, dim3(static_cast<unsigned>(blocks)), dim3(kBNT), lds, s, q);
+  return HA_OK;
+}
+
+int launch_bwd_dq(const BwdParams& p, hipStream_t s) {
+  if (p.seg == 0 || p.BH == 0) return HA_OK;
+  if (p.m > kMaxSamples) {
+    set_error("backward: samples %d > %d", p.m, kMaxSamples);
+    return HA_EUNSUPPORTED;
+  }
+  timing_begin(HA_K_BWD_DQ, s);
+  const int st = p.d == 64 ? launch_dq_d<64>(p, s) : launch_dq_d<128>(p, s);
+  timing_end(HA_K_BWD_DQ, s);
+  if (st != HA_OK) return st;
+  return after_launch("backward dq", s);
+}
+
+template <int D, bool SAMPLE>
+static int launch_dkv_d(const BwdParams& p, hipStream_t s) {
+  int64_t blocks;
+  if constexpr (SAMPLE) {
+    blocks = static_cast<int64_t>(p.BH) * ((p.m + kBTQ - 1) / kBTQ) * ((p.seg + p.qchunk - 1) / p.qchunk);
+  } else {
+    blocks = static_cast<int64_t>(p.BH / (p.H / p.Hkv)) * ((p.seg + kBTQ - 1) / kBTQ);
+  }
+  if (blocks == 0) return HA_OK;
+  const size_t lds = 2 * dkv_buf_bytes<D>();
+  hipLaunchKernelGGL((bwd_dkv_kernel<D, SAMPLE>), dim3(static_cast<unsigned>(blocks)), dim3(kBNT), lds, s, p);
+  return HA_OK;
+}
+
+int launch_bwd_dkv(const BwdParams& p, bool samples, hipStream_t s) {
+  if (p.seg == 0 || p.BH == 0 || (samples && p.m == 0)) return HA_OK;
+  timing_begin(HA_K_BWD_DKV, s);
+  int st;
+  if (p.d == 64) st = samples ? launch_dkv_d<64, true>(p, s) : launch_dkv_d<64, false>(p, s);
+  else st = samples ? launch_dkv_d<128, true>(p, s) : launch_dkv_d<128, false>(p, s);
+  timing_end(HA_K_BWD_DKV, s);
+  if (st != HA_OK) return st;
+  return after_launch(samples ? "backward dk/dv samples" : "backward dk/dv block", s);
+}
+
+}  // namespace ha

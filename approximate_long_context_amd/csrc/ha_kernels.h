@@ -82,4 +82,35 @@ struct AttnParams {
 
 int launch_attention(const AttnParams& p, int timing_kind, hipStream_t s);
 
+// ---- backward (ha_bwd.hip) ------------------------------------------------
+struct BwdParams {
+  const void* q = nullptr;           // [BH][n][d] bf16
+  const void* k = nullptr;           // [BHkv][n][d]
+  const void* v = nullptr;
+  const void* out = nullptr;         // forward output [BH][n][d]
+  const void* dout = nullptr;        // upstream gradient [BH][n][d]
+  const float* lse = nullptr;        // forward lse [BH][n] (natural log)
+  float* drow = nullptr;             // D = rowsum(dout * out) [BH][n]
+  int d = 64;
+  int n = 0;
+  int H = 1, Hkv = 1;
+  int BH = 0;
+  int seg = 0;                       // queries = keys of the (single) problem
+  const int32_t* perm_q = nullptr;   // [BH][seg]
+  const int32_t* perm_k = nullptr;   // [BHkv][seg]
+  const int32_t* sidx = nullptr;     // [BH][m]
+  int m = 0;
+  float log2w = 0.f;                 // log2(seg / m)
+  int b_eff = 1;
+  int bcap = 0;                      // LDS block key list capacity (launcher)
+  int qchunk = 2048;                 // queries per sample-key workgroup
+  float* dq = nullptr;               // [BH][n][d] fp32
+  float* dk = nullptr;               // [BHkv][n][d] fp32
+  float* dv = nullptr;
+};
+
+int launch_bwd_rowdot(const BwdParams& p, hipStream_t s);
+int launch_bwd_dq(const BwdParams& p, hipStream_t s);
+int launch_bwd_dkv(const BwdParams& p, bool samples, hipStream_t s);
+
 }  // namespace ha

@@ -136,6 +136,48 @@ int hyperattn_forward_ex(const void* q, const void* k, const void* v, int dtype,
                          void* workspace, size_t workspace_bytes, void* stream);
 
 /* ------------------------------------------------------------------------
+ * Backward ("HyperAttention: Long-context Attention in Near-Linear Time",
+ * research-map summary, section Key results: the method is timed forward
+ * and backward; the pages print no backward formulas).  For the ranks and
+ * samples the forward draws (recomputed here from the same seed) the
+ * forward is a softmax with fixed key multiplicities W -- 1 inside the
+ * query's block of the sorted matrix, n / samples per kept sample -- so
+ * with P = W * exp(Q K^T - lse), D = rowsum(dout * out) and
+ * dS = P * (dout V^T - D) the gradients are dQ = dS K, dK = dS^T Q,
+ * dV = P^T dout (dK, dV of a KV head summed over its query heads).
+ * ------------------------------------------------------------------------ */
+
+/* Bytes of device workspace hyperattn_backward needs (0 for invalid
+ * shapes).  Arguments as hyperattn_workspace_bytes. */
+size_t hyperattn_backward_workspace_bytes(int batch, int n, int d, int heads, int kv_heads,
+                                          int block, int samples, int proj_bits, int causal,
+                                          int min_seq_len, int dtype);
+
+/*
+ * Gradients of sum(dout * out) for out = hyperattn_forward(q, k, v, ...)
+ * with the same shape and method arguments and seed.
+ *   q, k, v    device, as for hyperattn_forward (bf16 only)
+ *   out, lse   device, the forward's outputs (out [B, H, n, d] bf16, lse
+ *              [B, H, n] fp32 natural log)
+ *   dout       device [B, H, n, d] bf16, upstream gradient of out
+ *   dq         device [B, H, n, d] fp32, written (every element)
+ *   dk, dv     device [B, Hkv, n, d] fp32, written (every element)
+ *   workspace  device, >= hyperattn_backward_workspace_bytes(...) bytes,
+ *              256-byte aligned, owned by the caller, clobbered
+ *   stream     hipStream_t or NULL; asynchronous on it
+ * The sample part of dK and dV is accumulated with fp32 atomic adds, so
+ * their last bits may vary from run to run; dQ is deterministic.
+ * Errors: as hyperattn_forward; HA_EUNSUPPORTED for causal problems (not
+ * built yet) and for fp32 inputs.
+ */
+int hyperattn_backward(const void* q, const void* k, const void* v, const void* out,
+                       const float* lse, const void* dout, int dtype,
+                       int batch, int n, int d, int heads, int kv_heads,
+                       int block, int samples, int proj_bits, int causal, int min_seq_len,
+                       uint64_t seed, float* dq, float* dk, float* dv,
+                       void* workspace, size_t workspace_bytes, void* stream);
+
+/* ------------------------------------------------------------------------
  * Stages of the forward, exported for parity checks and timing.  The
  * forward calls the same kernels.
  * ------------------------------------------------------------------------ */
@@ -257,13 +299,14 @@ int hyperattn_causal_leaves(const void* q, const void* k, const void* v, int dty
                             int leaf_len, float* o_out, float* lse_out, void* stream);
 
 /* ------------------------------------------------------------------------
- * Timing hooks (used by the benchmark): when enabled, the forward records
+ * Timing hooks (used by the benchmark): when enabled, the library records
  * a pair of HIP events around each kernel launch on its stream and sums
  * the elapsed times per kernel class on the next hyperattn_timing_read.
  * ------------------------------------------------------------------------ */
 enum {
   HA_K_PROJ = 0, HA_K_HASH, HA_K_SORT, HA_K_SAMPLES, HA_K_GATHER,
-  HA_K_ATTEND, HA_K_MERGE, HA_K_LEAF, HA_K_QUADRANT, HA_K_COUNT
+  HA_K_ATTEND, HA_K_MERGE, HA_K_LEAF, HA_K_QUADRANT, HA_K_BWD_DQ, HA_K_BWD_DKV,
+  HA_K_COUNT
 };
 /* Enable (1) or disable (0) event timing; clears the accumulators. */
 int hyperattn_timing_enable(int enable);

@@ -1,0 +1,95 @@
+"""GPU parity of the backward (non-causal, bf16) against the fp64 oracle.
+
+The library's forward gives (out, lse); its backward then gives dq, dk, dv
+in fp32, compared with ``oracle.backward.backward`` on the same bf16 inputs
+and upstream gradient.  Tolerance (derived from the arithmetic): the
+kernels round P to bf16 before the P^T dO product and dS = P (dP - D) to
+bf16 before dS K and dS^T Q (relative 2^-9 ~ 2e-3 per term, averaging
+down over the sums), and D comes from the bf16-rounded forward output; so
+the Frobenius error is about 2e-3 relative (measured 1.7e-3) and the
+largest element error a few 1e-3 of the largest reference magnitude
+(measured up to 3.4e-3).  Bounds: 5e-3 and 8e-3.
+"""
+
+import numpy as np
+import pytest
+import torch
+
+import approximate_long_context_amd as ha
+from oracle import HAConfig
+from oracle import backward as ob
+
+from _util import np32
+
+pytestmark = pytest.mark.gpu
+DEV = "cuda"
+
+REL_F = 5e-3
+REL_MAX = 8e-3
+
+
+def _inputs(B, H, Hkv, n, d, seed):
+    g = torch.Generator(device="cpu").manual_seed(seed)
+    s = d ** -0.25
+    q = (torch.randn(B, H, n, d, generator=g) * s).to(torch.bfloat16)
+    k = (torch.randn(B, Hkv, n, d, generator=g) * s).to(torch.bfloat16)
+    v = torch.randn(B, Hkv, n, d, generator=g).to(torch.bfloat16)
+    do = torch.randn(B, H, n, d, generator=g).to(torch.bfloat16)
+    return q, k, v, do
+
+
+def _compare(got, ref, what):
+    got = got.astype(np.float64)
+    assert got.shape == ref.shape, (what, got.shape, ref.shape)
+    assert np.all(np.isfinite(got)), f"{what}: non-finite"
+    scale = float(np.max(np.abs(ref))) or 1.0
+    max_err = float(np.max(np.abs(got - ref)))
+    rel = float(np.linalg.norm(got - ref) / (np.linalg.norm(ref) or 1.0))
+    assert max_err <= REL_MAX * scale, f"{what}: max-abs {max_err:.3e} > {REL_MAX} x {scale:.3e}"
+    assert rel <= REL_F, f"{what}: rel-Frobenius {rel:.3e} > {REL_F}"
+
+
+CASES = [
+    # B, H, Hkv, n, d, block, samples, r, seed
+    (1, 2, 1, 1024, 64, 256, 128, 7, 3),      # grouped heads, 8 waves x 32 per block
+    (1, 2, 2, 1000, 128, 40, 50, 6, 4),       # blocks smaller than a tile, ragged
+    (2, 2, 2, 512, 64, 64, 200, 5, 5),        # many duplicate samples
+    (1, 1, 1, 768, 64, 768, 30, 7, 6),        # one block = the whole segment: samples all excluded
+    (1, 2, 1, 1024, 64, 128, 0, 7, 7),        # no samples
+    (1, 4, 2, 2048, 128, 512, 256, 8, 8),     # d = 128, block wider than a workgroup
+]
+
+
+@pytest.mark.parametrize("B,H,Hkv,n,d,block,m,r,seed", CASES)
+def test_backward_matches_oracle(B, H, Hkv, n, d, block, m, r, seed):
+    q, k, v, do = _inputs(B, H, Hkv, n, d, 100 + seed)
+    args = dict(block=block, samples=m, proj_bits=r, seed=seed)
+    qd, kd, vd, dod = q.to(DEV), k.to(DEV), v.to(DEV), do.to(DEV)
+    out, lse = ha.forward(qd, kd, vd, **args)
+    dq, dk, dv = ha.backward(qd, kd, vd, out, lse, dod, **args)
+    torch.cuda.synchronize()
+    cfg = HAConfig(block=block, samples=m, proj_bits=r, seed=seed)
+    rq, rk, rv = ob.backward(np32(q), np32(k), np32(v), np32(do), cfg)
+    _compare(dq.cpu().numpy(), rq, "dq")
+    _compare(dk.cpu().numpy(), rk, "dk")
+    _compare(dv.cpu().numpy(), rv, "dv")
+
+
+def test_backward_dq_deterministic():
+    q, k, v, do = _inputs(1, 2, 2, 1024, 64, 11)
+    args = dict(block=256, samples=64, proj_bits=7, seed=1)
+    qd, kd, vd, dod = q.to(DEV), k.to(DEV), v.to(DEV), do.to(DEV)
+    out, lse = ha.forward(qd, kd, vd, **args)
+    a = ha.backward(qd, kd, vd, out, lse, dod, **args)
+    b = ha.backward(qd, kd, vd, out, lse, dod, **args)
+    assert torch.equal(a[0], b[0])
+
+
+def test_backward_rejects_what_is_not_built():
+    q, k, v, do = _inputs(1, 1, 1, 256, 64, 12)
+    qd, kd, vd, dod = q.to(DEV), k.to(DEV), v.to(DEV), do.to(DEV)
+    out, lse = ha.forward(qd, kd, vd, block=64, samples=16, proj_bits=5, causal=True, min_seq_len=64)
+    with pytest.raises(ha.HyperAttnError) as e:
+        ha.backward(qd, kd, vd, out, lse, dod, block=64, samples=16, proj_bits=5, causal=True,
+                    min_seq_len=64)
+    assert e.value.code == ha.HA_EUNSUPPORTED
