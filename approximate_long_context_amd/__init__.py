@@ -150,6 +150,12 @@ def forward(q, k, v, *, block, samples, proj_bits, causal=False, min_seq_len=0, 
     return out, lse
 
 
+def backward_workspace_bytes(batch, n, d, heads, kv_heads, block, samples, proj_bits, causal=False,
+                             min_seq_len=0):
+    return lib().hyperattn_backward_workspace_bytes(batch, n, d, heads, kv_heads, block, samples, proj_bits,
+                                                    int(bool(causal)), min_seq_len, HA_BF16)
+
+
 def backward(q, k, v, out, lse, dout, *, block, samples, proj_bits, causal=False, min_seq_len=0,
              seed=0, dq=None, dk=None, dv=None, workspace=None):
     """Gradients of sum(dout * out) for (out, lse) = forward(q, k, v, ...)

@@ -398,7 +398,7 @@ static int forward_impl(const void* q, const void* k, const void* v, Shape sh, u
 // from the seed), then D = rowsum(dO * O), dQ, the block part of dK / dV
 // (stored) and the sample part of dK / dV (added).
 
-static size_t backward_plan(const Shape& sh, void* ws, size_t cap, Plan* pl, float** drow) {
+static size_t backward_plan(const Shape& sh, void* ws, size_t cap, Plan* pl, float** drow, float** part) {
   Shape f = sh;
   f.flags = 0;
   *pl = make_plan(f, ws, cap);
@@ -406,6 +406,8 @@ static size_t backward_plan(const Shape& sh, void* ws, size_t cap, Plan* pl, flo
   cv.used = pl->total;
   const int64_t BH = static_cast<int64_t>(sh.batch) * sh.heads;
   *drow = cv.take<float>(BH * sh.n);
+  const int64_t nchunk = sh.n > 0 ? (sh.n + bwd_query_chunk(sh.n) - 1) / bwd_query_chunk(sh.n) : 0;
+  *part = cv.take<float>(nchunk * BH * sh.samples * 2 * sh.d);
   return align_up(cv.used, 256) + 256;
 }
 
@@ -432,7 +434,8 @@ static int backward_impl(const void* q, const void* k, const void* v, const void
   }
   Plan pl;
   float* drow = nullptr;
-  const size_t need = backward_plan(sh, nullptr, 0, &pl, &drow);
+  float* part = nullptr;
+  const size_t need = backward_plan(sh, nullptr, 0, &pl, &drow, &part);
   if (!ws || ws_bytes < need) {
     set_error("workspace of %zu bytes < %zu required", ws_bytes, need);
     return HA_EWORKSPACE;
@@ -441,7 +444,7 @@ static int backward_impl(const void* q, const void* k, const void* v, const void
     set_error("workspace must be 256-byte aligned");
     return HA_EINVAL;
   }
-  backward_plan(sh, ws, ws_bytes, &pl, &drow);
+  backward_plan(sh, ws, ws_bytes, &pl, &drow, &part);
   const int64_t BH = static_cast<int64_t>(sh.batch) * sh.heads;
   const int64_t BK = static_cast<int64_t>(sh.batch) * sh.kv_heads;
   if (static_cast<int64_t>(sh.n) * sh.d * 2 >= (int64_t(1) << 32)) {
@@ -474,6 +477,8 @@ static int backward_impl(const void* q, const void* k, const void* v, const void
   bp.m = sh.samples;
   bp.log2w = sh.samples > 0 ? static_cast<float>(std::log2(static_cast<double>(sh.n) / sh.samples)) : 0.f;
   bp.b_eff = sh.block < sh.n ? sh.block : sh.n;
+  bp.qchunk = bwd_query_chunk(sh.n);
+  bp.part = part;
   bp.dq = dq;
   bp.dk = dk;
   bp.dv = dv;
@@ -527,7 +532,8 @@ size_t hyperattn_backward_workspace_bytes(int batch, int n, int d, int heads, in
   if (validate(sh) != HA_OK) return 0;
   Plan pl;
   float* drow = nullptr;
-  return backward_plan(sh, nullptr, 0, &pl, &drow);
+  float* part = nullptr;
+  return backward_plan(sh, nullptr, 0, &pl, &drow, &part);
 }
 
 int hyperattn_backward(const void* q, const void* k, const void* v, const void* out, const float* lse,

@@ -23,7 +23,8 @@
 //     S = Q K^T and dP = dO V^T with a lane owning a key column, then
 //     dV^T += dO^T P and dK^T += Q^T dS read Q and dO transposed.  Block
 //     keys are stored (each key's block is owned by one workgroup); sample
-//     keys then add their chunk's share with fp32 atomics.
+//     slots store their chunk's partial rows, and bwd_dkv_reduce_kernel
+//     sums them over the chunks and adds them to the key rows.
 #include <cmath>
 
 #include "ha_device.h"
@@ -316,7 +317,7 @@ __global__ __launch_bounds__(kBNT, 2) void bwd_dkv_kernel(BwdParams p) {
 
   // ---- work item
   const int lid = xcd_remap(blockIdx.x, gridDim.x);
-  int bkv, bh0, nheads, k0, kend, qa0, qa1;
+  int bkv, bh0, nheads, k0, kend, qa0, qa1, chunk = 0;
   if constexpr (!SAMPLE) {
     const int KT = (p.seg + kBTQ - 1) / kBTQ;
     bkv = lid / KT;
@@ -330,7 +331,7 @@ __global__ __launch_bounds__(kBNT, 2) void bwd_dkv_kernel(BwdParams p) {
   } else {
     const int NC = (p.seg + p.qchunk - 1) / p.qchunk;
     const int SG = (p.m + kBTQ - 1) / kBTQ;
-    const int chunk = lid % NC;
+    chunk = lid % NC;
     const int rest = lid / NC;
     k0 = (rest % SG) * kBTQ;
     kend = min(k0 + kBTQ, p.m);
@@ -435,6 +436,14 @@ __global__ __launch_bounds__(kBNT, 2) void bwd_dkv_kernel(BwdParams p) {
     const bf16* qs = reinterpret_cast<const bf16*>(base);
     const bf16* gs = reinterpret_cast<const bf16*>(base + G::TB);
     const float* ls = reinterpret_cast<const float*>(base + 2 * G::TB);
+    // query j of the tile lies in this lane's key block iff (unsigned)(j - lo) < b_eff
+    const int lo = kblk * b_eff - tq0;
+    // masks are needed unless the tile is full and, for every lane of the
+    // wave, wholly inside (block part) or wholly outside (sample part) the
+    // key's block
+    const bool inside = lo <= 0 && lo + b_eff >= kBT;
+    const bool outside = lo >= kBT || lo + b_eff <= 0;
+    const bool need_mask = qcnt < kBT || __ballot(!kvalid || (SAMPLE ? !outside : !inside)) != 0;
 #pragma unroll
     for (int qt = 0; qt < 2; ++qt) {
       floatx16 s, dp;
@@ -456,10 +465,11 @@ __global__ __launch_bounds__(kBNT, 2) void bwd_dkv_kernel(BwdParams p) {
         for (int i = 0; i < 4; ++i) {
           const int r = 4 * g + i;
           const int j = j0 + i;
-          const int qblk = (tq0 + j) / b_eff;
-          bool ok = kvalid && j < qcnt;
-          if constexpr (SAMPLE) ok = ok && qblk != kblk;
-          else ok = ok && qblk == kblk;
+          bool ok = true;
+          if (need_mask) {
+            const bool in_blk = static_cast<unsigned>(j - lo) < static_cast<unsigned>(b_eff);
+            ok = kvalid && j < qcnt && (SAMPLE ? !in_blk : in_blk);
+          }
           const float pr = ok ? fast_exp2(fmaf(s[r], kLog2e, wbias - l4[i])) : 0.f;
           const bf16 pv = static_cast<bf16>(pr);
           const bf16 dsv = static_cast<bf16>(pr * (dp[r] - d4[i]));
@@ -482,32 +492,66 @@ __global__ __launch_bounds__(kBNT, 2) void bwd_dkv_kernel(BwdParams p) {
     }
   }
 
-  // ---- dK, dV rows (fp32): register r of tile t holds column 32 t + 8 (r / 4) + 4 h2 + r % 4
+  // ---- dK, dV rows (fp32): register r of tile t holds column 32 t + 8 (r / 4) + 4 h2 + r % 4.
+  // Block keys: the final rows.  Sample slots: this chunk's partial row
+  // [dK | dV] of the slot, summed over the chunks by bwd_dkv_reduce_kernel.
   if (kvalid) {
-    const int64_t rbase = (static_cast<int64_t>(bkv) * p.n + krow) * D;
+    float* dkr;
+    float* dvr;
+    if constexpr (SAMPLE) {
+      dkr = p.part + ((static_cast<int64_t>(chunk) * p.BH + bh0) * p.m + kj) * (2 * D);
+      dvr = dkr + D;
+    } else {
+      dkr = p.dk + (static_cast<int64_t>(bkv) * p.n + krow) * D;
+      dvr = p.dv + (static_cast<int64_t>(bkv) * p.n + krow) * D;
+    }
 #pragma unroll
     for (int t = 0; t < NDT; ++t)
 #pragma unroll
       for (int g = 0; g < 4; ++g) {
         const int c0 = 32 * t + 8 * g + 4 * h2;
-        if constexpr (SAMPLE) {
+        floatx4 a, c;
 #pragma unroll
-          for (int i = 0; i < 4; ++i) {
-            unsafeAtomicAdd(p.dk + rbase + c0 + i, dk[t][4 * g + i]);
-            unsafeAtomicAdd(p.dv + rbase + c0 + i, dv[t][4 * g + i]);
-          }
-        } else {
-          floatx4 a, c;
-#pragma unroll
-          for (int i = 0; i < 4; ++i) {
-            a[i] = dk[t][4 * g + i];
-            c[i] = dv[t][4 * g + i];
-          }
-          *reinterpret_cast<floatx4*>(p.dk + rbase + c0) = a;
-          *reinterpret_cast<floatx4*>(p.dv + rbase + c0) = c;
+        for (int i = 0; i < 4; ++i) {
+          a[i] = dk[t][4 * g + i];
+          c[i] = dv[t][4 * g + i];
         }
+        *reinterpret_cast<floatx4*>(dkr + c0) = a;
+        *reinterpret_cast<floatx4*>(dvr + c0) = c;
       }
   }
+}
+
+// Sum of a sample slot's partial [dK | dV] rows over the query chunks,
+// added to the rows of the slot's key (several slots -- duplicate samples,
+// the query heads of a group -- can share a key row, hence the atomics).
+// One thread per 4 columns of a slot row.
+template <int D>
+__global__ __launch_bounds__(256) void bwd_dkv_reduce_kernel(BwdParams p, int nchunk) {
+  constexpr int TPR = 2 * D / 4;                    // threads per slot row
+  const int64_t t = static_cast<int64_t>(blockIdx.x) * 256 + threadIdx.x;
+  const int64_t row = t / TPR;                      // bh * m + slot
+  if (row >= static_cast<int64_t>(p.BH) * p.m) return;
+  const int c = static_cast<int>(t % TPR) * 4;
+  const int64_t cstride = static_cast<int64_t>(p.BH) * p.m * (2 * D);
+  const float* src = p.part + row * (2 * D) + c;
+  floatx4 acc = {0.f, 0.f, 0.f, 0.f};
+  int ch = 0;
+  for (; ch + 4 <= nchunk; ch += 4) {
+    floatx4 x[4];
+#pragma unroll
+    for (int u = 0; u < 4; ++u) x[u] = *reinterpret_cast<const floatx4*>(src + (ch + u) * cstride);
+#pragma unroll
+    for (int u = 0; u < 4; ++u) acc += x[u];
+  }
+  for (; ch < nchunk; ++ch) acc += *reinterpret_cast<const floatx4*>(src + ch * cstride);
+  const int bh = static_cast<int>(row / p.m);
+  const int bkv = (bh / p.H) * p.Hkv + (bh % p.H) / (p.H / p.Hkv);
+  const int kpos = p.sidx[row];
+  const int krow = p.perm_k[static_cast<int64_t>(bkv) * p.seg + kpos];
+  float* dst = (c < D ? p.dk : p.dv) + (static_cast<int64_t>(bkv) * p.n + krow) * D + (c < D ? c : c - D);
+#pragma unroll
+  for (int i = 0; i < 4; ++i) unsafeAtomicAdd(dst + i, acc[i]);
 }
 
 // ---- launches ---------------------------------------------------------------------------
@@ -548,19 +592,29 @@ int launch_bwd_dq(const BwdParams& p, hipStream_t s) {
 template <int D, bool SAMPLE>
 static int launch_dkv_d(const BwdParams& p, hipStream_t s) {
   int64_t blocks;
+  const int nchunk = (p.seg + p.qchunk - 1) / p.qchunk;
   if constexpr (SAMPLE) {
-    blocks = static_cast<int64_t>(p.BH) * ((p.m + kBTQ - 1) / kBTQ) * ((p.seg + p.qchunk - 1) / p.qchunk);
+    blocks = static_cast<int64_t>(p.BH) * ((p.m + kBTQ - 1) / kBTQ) * nchunk;
   } else {
     blocks = static_cast<int64_t>(p.BH / (p.H / p.Hkv)) * ((p.seg + kBTQ - 1) / kBTQ);
   }
   if (blocks == 0) return HA_OK;
   const size_t lds = 2 * dkv_buf_bytes<D>();
   hipLaunchKernelGGL((bwd_dkv_kernel<D, SAMPLE>), dim3(static_cast<unsigned>(blocks)), dim3(kBNT), lds, s, p);
+  if constexpr (SAMPLE) {
+    const int64_t threads = static_cast<int64_t>(p.BH) * p.m * (2 * D / 4);
+    hipLaunchKernelGGL((bwd_dkv_reduce_kernel<D>), dim3(static_cast<unsigned>((threads + 255) / 256)), dim3(256), 0,
+                       s, p, nchunk);
+  }
   return HA_OK;
 }
 
 int launch_bwd_dkv(const BwdParams& p, bool samples, hipStream_t s) {
   if (p.seg == 0 || p.BH == 0 || (samples && p.m == 0)) return HA_OK;
+  if (samples && (!p.part || p.qchunk < kBT || p.qchunk % kBT)) {
+    set_error("backward dk/dv: bad sample partial buffer or query chunk");
+    return HA_EINVAL;
+  }
   timing_begin(HA_K_BWD_DKV, s);
   int st;
   if (p.d == 64) st = samples ? launch_dkv_d<64, true>(p, s) : launch_dkv_d<64, false>(p, s);

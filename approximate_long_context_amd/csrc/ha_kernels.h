@@ -103,11 +103,19 @@ struct BwdParams {
   float log2w = 0.f;                 // log2(seg / m)
   int b_eff = 1;
   int bcap = 0;                      // LDS block key list capacity (launcher)
-  int qchunk = 2048;                 // queries per sample-key workgroup
+  int qchunk = 2048;                 // queries per sample-key workgroup (bwd_query_chunk)
+  float* part = nullptr;             // sample-key partials [ceil(seg / qchunk)][BH][m][2 d] fp32
   float* dq = nullptr;               // [BH][n][d] fp32
   float* dk = nullptr;               // [BHkv][n][d] fp32
   float* dv = nullptr;
 };
+
+// Queries per sample-key workgroup of the dK/dV pass: at least 2048, and
+// at most 64 chunks per problem (bounds the partial buffer).
+inline int bwd_query_chunk(int seg) {
+  const int per64 = ((seg + 63) / 64 + 63) / 64 * 64;
+  return per64 > 2048 ? per64 : 2048;
+}
 
 int launch_bwd_rowdot(const BwdParams& p, hipStream_t s);
 int launch_bwd_dq(const BwdParams& p, hipStream_t s);

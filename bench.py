@@ -273,6 +273,8 @@ def main():
     if not args.no_extras:
         result["approx_rel_error"] = approx_error(ha, torch, w_nc, w_c, q, k, v, out)
         result["configs"] = other_configs(ha, torch, dev, stream)
+        del ws
+        result["backward"] = backward_bench(ha, torch, w_nc, q, k, v, out, lse, stream)
     if not args.no_cpu_baseline:
         result["cpu_baseline"] = cpu_baseline(w_nc, w_c, q, k, v)
     else:
@@ -294,6 +296,46 @@ def approx_error(ha, torch, w_nc, w_c, q, k, v, out):
         b = ex.float()
         res[name] = float(torch.linalg.vector_norm(a - b) / torch.linalg.vector_norm(b))
         del a, b
+    return res
+
+
+def backward_bench(ha, torch, w, q, k, v, out, lse, stream, reps=5):
+    """ms and effective TFLOP/s of the non-causal backward (dQ, dK, dV) of
+    the headline configuration (not part of `value`).  Algorithmic FLOPs:
+    10 d per (row, key) pair -- S, dP, dV, dQ, dK -- i.e. 2.5 times the
+    forward's; the kernels recompute S and dP once more (14 d)."""
+    ha.forward(q, k, v, out=out, lse=lse, **w.method_args())
+    g = torch.Generator(device=q.device).manual_seed(77)
+    dout = torch.randn(q.shape, generator=g, device=q.device).to(torch.bfloat16)
+    dq = torch.empty(q.shape, dtype=torch.float32, device=q.device)
+    dk = torch.empty(k.shape, dtype=torch.float32, device=q.device)
+    dv = torch.empty(k.shape, dtype=torch.float32, device=q.device)
+    ws = torch.empty(ha.backward_workspace_bytes(w.batch, w.n, w.d, w.heads, w.kv_heads, w.block, w.samples,
+                                                 w.proj_bits), dtype=torch.uint8, device=q.device)
+    args = w.method_args()
+    args.pop("flags", None)
+
+    def run():
+        ha.backward(q, k, v, out, lse, dout, dq=dq, dk=dk, dv=dv, workspace=ws, **args)
+
+    for _ in range(2):
+        run()
+    torch.cuda.synchronize()
+    ha.timing_enable(True)
+    e0 = torch.cuda.Event(enable_timing=True)
+    e1 = torch.cuda.Event(enable_timing=True)
+    e0.record(stream)
+    for _ in range(reps):
+        run()
+    e1.record(stream)
+    torch.cuda.synchronize()
+    per_kernel = ha.timing_read()
+    ha.timing_enable(False)
+    ms = e0.elapsed_time(e1) / reps
+    f_fwd, _ = alg_flops(w, False)
+    res = {"ms": ms, "tflops": 2.5 * f_fwd / (ms * 1e-3) / 1e12, "causal": False,
+           "kernels": {name: t / reps for name, (t, cnt) in per_kernel.items() if cnt}}
+    del dout, dq, dk, dv, ws
     return res
 
 
