@@ -398,14 +398,14 @@ static int forward_impl(const void* q, const void* k, const void* v, Shape sh, u
 // from the seed), then D = rowsum(dO * O), dQ, the block part of dK / dV
 // (stored) and the sample part of dK / dV (added).
 
-static size_t backward_plan(const Shape& sh, void* ws, size_t cap, Plan* pl, float** drow, float** part) {
+static size_t backward_plan(const Shape& sh, void* ws, size_t cap, Plan* pl, float** qstat, float** part) {
   Shape f = sh;
   f.flags = 0;
   *pl = make_plan(f, ws, cap);
   Carve cv(ws, cap);
   cv.used = pl->total;
   const int64_t BH = static_cast<int64_t>(sh.batch) * sh.heads;
-  *drow = cv.take<float>(BH * sh.n);
+  *qstat = cv.take<float>(2 * BH * sh.n);
   const int64_t nchunk = sh.n > 0 ? (sh.n + bwd_query_chunk(sh.n) - 1) / bwd_query_chunk(sh.n) : 0;
   *part = cv.take<float>(nchunk * BH * sh.samples * 2 * sh.d);
   return align_up(cv.used, 256) + 256;
@@ -433,9 +433,9 @@ static int backward_impl(const void* q, const void* k, const void* v, const void
     return HA_EINVAL;
   }
   Plan pl;
-  float* drow = nullptr;
+  float* qstat = nullptr;
   float* part = nullptr;
-  const size_t need = backward_plan(sh, nullptr, 0, &pl, &drow, &part);
+  const size_t need = backward_plan(sh, nullptr, 0, &pl, &qstat, &part);
   if (!ws || ws_bytes < need) {
     set_error("workspace of %zu bytes < %zu required", ws_bytes, need);
     return HA_EWORKSPACE;
@@ -444,7 +444,7 @@ static int backward_impl(const void* q, const void* k, const void* v, const void
     set_error("workspace must be 256-byte aligned");
     return HA_EINVAL;
   }
-  backward_plan(sh, ws, ws_bytes, &pl, &drow, &part);
+  backward_plan(sh, ws, ws_bytes, &pl, &qstat, &part);
   const int64_t BH = static_cast<int64_t>(sh.batch) * sh.heads;
   const int64_t BK = static_cast<int64_t>(sh.batch) * sh.kv_heads;
   if (static_cast<int64_t>(sh.n) * sh.d * 2 >= (int64_t(1) << 32)) {
@@ -464,7 +464,7 @@ static int backward_impl(const void* q, const void* k, const void* v, const void
   bp.out = out;
   bp.dout = dout;
   bp.lse = lse;
-  bp.drow = drow;
+  bp.qstat = qstat;
   bp.d = sh.d;
   bp.n = sh.n;
   bp.H = sh.heads;
@@ -482,7 +482,7 @@ static int backward_impl(const void* q, const void* k, const void* v, const void
   bp.dq = dq;
   bp.dk = dk;
   bp.dv = dv;
-  HA_TRY(launch_bwd_rowdot(bp, s));
+  HA_TRY(launch_bwd_qstat(bp, s));
   HA_TRY(launch_bwd_dq(bp, s));
   HA_TRY(launch_bwd_dkv(bp, false, s));
   return launch_bwd_dkv(bp, true, s);
@@ -531,9 +531,9 @@ size_t hyperattn_backward_workspace_bytes(int batch, int n, int d, int heads, in
   Shape sh{batch, n, d, heads, kv_heads, block, samples, proj_bits, causal, min_seq_len, dtype, 0};
   if (validate(sh) != HA_OK) return 0;
   Plan pl;
-  float* drow = nullptr;
+  float* qstat = nullptr;
   float* part = nullptr;
-  return backward_plan(sh, nullptr, 0, &pl, &drow, &part);
+  return backward_plan(sh, nullptr, 0, &pl, &qstat, &part);
 }
 
 int hyperattn_backward(const void* q, const void* k, const void* v, const void* out, const float* lse,

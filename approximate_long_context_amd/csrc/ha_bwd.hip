@@ -12,11 +12,16 @@
 // The kernels keep the forward's conventions (bf16 operands, fp32
 // accumulation, v_mfma_f32_32x32x16_bf16 with each lane owning one column
 // of a 32-wide result, 64-row tiles double-buffered through LDS):
-//   * bwd_rowdot_kernel: D for every row;
+//   * bwd_qstat_kernel: per query, in sorted order, lse in log2 units and
+//     D, so later passes read both contiguously;
 //   * bwd_dq_kernel: query-owned like the forward -- a workgroup of 8 waves
 //     owns 256 consecutive sorted queries, block and sample key tiles
 //     stream through LDS; per 32-key half S^T = K Q^T and dP^T = V dO^T,
 //     dS is packed to bf16 and dQ^T += K^T dS^T reads K transposed;
+// Both attention passes build P without branches (a masked logit becomes
+// -inf, whose exp2 is 0) in a masked and an unmasked instance of the tile
+// body, chosen per tile and wave; tile loads are unconditional (clamped
+// rows get P = dS = 0).
 //   * bwd_dkv_kernel: key-owned -- a workgroup owns 256 sorted keys (block
 //     part, every query head of the group) or 256 sample slots of one query
 //     head and a chunk of its queries (sample part); per 32-query half
@@ -31,6 +36,11 @@
 #include "ha_kernels.h"
 
 namespace ha {
+
+template <bool B>
+struct Flag {
+  static constexpr bool value = B;
+};
 
 constexpr int kBT = 64;      // rows per LDS tile
 constexpr int kBW = 8;       // waves per workgroup
@@ -48,51 +58,58 @@ struct BGeo {
   static_assert((kBT * CPR) % kBNT == 0, "tile split");
 };
 
-// ---- D = rowsum(dO o O) -------------------------------------------------------------
+// ---- per-query statistics: (lse log2 e, D = rowsum(dO o O)) in sorted order ---------
 
 template <int D>
-__global__ __launch_bounds__(256) void bwd_rowdot_kernel(const bf16* __restrict__ o, const bf16* __restrict__ dout,
-                                                         int64_t rows, float* __restrict__ drow) {
+__global__ __launch_bounds__(256) void bwd_qstat_kernel(BwdParams p) {
   constexpr int LPR = D / 8;                      // lanes per row, 8 elements each
   constexpr int RPW = 64 / LPR;
+  const bf16* o = static_cast<const bf16*>(p.out);
+  const bf16* dout = static_cast<const bf16*>(p.dout);
+  const int64_t rows = static_cast<int64_t>(p.BH) * p.seg;
   const int lane = threadIdx.x & 63;
   const int64_t wave = (static_cast<int64_t>(blockIdx.x) * blockDim.x + threadIdx.x) >> 6;
   const int64_t nwaves = (static_cast<int64_t>(gridDim.x) * blockDim.x) >> 6;
   for (int64_t r0 = wave * RPW; r0 < rows; r0 += nwaves * RPW) {
-    const int64_t row = r0 + lane / LPR;
+    const int64_t t = r0 + lane / LPR;              // sorted position over all problems
+    const int64_t ts = t < rows ? t : rows - 1;
+    const int64_t bh = ts / p.seg;
+    const int64_t row = bh * p.n + p.perm_q[ts];
+    const int64_t off = row * D + 8 * (lane % LPR);
+    const uint4v a = *reinterpret_cast<const uint4v*>(o + off);
+    const uint4v g = *reinterpret_cast<const uint4v*>(dout + off);
+    const float l = p.lse[row];
     float acc = 0.f;
-    if (row < rows) {
-      const int64_t off = row * D + 8 * (lane % LPR);
-      const uint4v a = *reinterpret_cast<const uint4v*>(o + off);
-      const uint4v g = *reinterpret_cast<const uint4v*>(dout + off);
 #pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        acc += __uint_as_float(a[i] << 16) * __uint_as_float(g[i] << 16);
-        acc += __uint_as_float(a[i] & 0xFFFF0000u) * __uint_as_float(g[i] & 0xFFFF0000u);
-      }
+    for (int i = 0; i < 4; ++i) {
+      acc += __uint_as_float(a[i] << 16) * __uint_as_float(g[i] << 16);
+      acc += __uint_as_float(a[i] & 0xFFFF0000u) * __uint_as_float(g[i] & 0xFFFF0000u);
     }
 #pragma unroll
-    for (int off = LPR / 2; off >= 1; off >>= 1) acc += __shfl_xor(acc, off);
-    if (row < rows && lane % LPR == 0) drow[row] = acc;
+    for (int sh = LPR / 2; sh >= 1; sh >>= 1) acc += __shfl_xor(acc, sh);
+    if (t < rows && lane % LPR == 0) {
+      floatx2 st;
+      st[0] = l * kLog2e;
+      st[1] = acc;
+      *reinterpret_cast<floatx2*>(p.qstat + 2 * t) = st;
+    }
   }
 }
 
-int launch_bwd_rowdot(const BwdParams& p, hipStream_t s) {
-  const int64_t rows = static_cast<int64_t>(p.BH) * p.n;
+int launch_bwd_qstat(const BwdParams& p, hipStream_t s) {
+  const int64_t rows = static_cast<int64_t>(p.BH) * p.seg;
   if (rows == 0) return HA_OK;
   const int rpw = 64 / (p.d / 8);
   int64_t blocks = (rows + 4 * rpw - 1) / (4 * rpw);
   if (blocks > 16384) blocks = 16384;
-  const bf16* o = static_cast<const bf16*>(p.out);
-  const bf16* g = static_cast<const bf16*>(p.dout);
-  if (p.d == 64) hipLaunchKernelGGL(bwd_rowdot_kernel<64>, dim3(blocks), dim3(256), 0, s, o, g, rows, p.drow);
-  else hipLaunchKernelGGL(bwd_rowdot_kernel<128>, dim3(blocks), dim3(256), 0, s, o, g, rows, p.drow);
-  return after_launch("backward rowdot", s);
+  if (p.d == 64) hipLaunchKernelGGL(bwd_qstat_kernel<64>, dim3(blocks), dim3(256), 0, s, p);
+  else hipLaunchKernelGGL(bwd_qstat_kernel<128>, dim3(blocks), dim3(256), 0, s, p);
+  return after_launch("backward query statistics", s);
 }
 
 // ---- dQ (query-owned) -----------------------------------------------------------------
 
-// LDS after the two K/V tile buffers: brow[bcap], srow[m], spos[m], rrow[m],
+// LDS after the two K/V tile buffers: brow[bcap], srow[m], sblk[m], rrow[m],
 // one count per 64 samples.
 static int dq_list_bytes(int bcap, int m) { return 4 * (bcap + 3 * m + (m + 63) / 64); }
 
@@ -134,8 +151,8 @@ __global__ __launch_bounds__(kBNT, 2) void bwd_dq_kernel(BwdParams p) {
   // ---- key row lists (as the forward): block rows, compacted sample rows
   int* brow = reinterpret_cast<int*>(smem + 4 * G::TB);
   int* srow = brow + p.bcap;
-  int* spos = srow + p.m;
-  int* rrow = spos + p.m;
+  int* sblk = srow + p.m;                         // block of each sample's sorted position
+  int* rrow = sblk + p.m;
   int* ccount = rrow + p.m;
   const bool blist = p.bcap > 0;
   int nsamp = 0;
@@ -149,7 +166,7 @@ __global__ __launch_bounds__(kBNT, 2) void bwd_dq_kernel(BwdParams p) {
       const int i = c + lane;
       const int sp = i < p.m ? si[i] : 0;
       if (i < p.m) {
-        spos[i] = sp;
+        sblk[i] = sp / b_eff;
         raw[i] = pk[sp];
       }
       const uint64_t keep = __ballot(i < p.m && (samp_multi || (sp / b_eff) != tq));
@@ -162,7 +179,7 @@ __global__ __launch_bounds__(kBNT, 2) void bwd_dq_kernel(BwdParams p) {
         int base = 0;
         for (int k = 0; k < c / 64; ++k) base += ccount[k];
         const int i = c + lane;
-        const bool keep = i < p.m && (spos[i] / b_eff) != tq;
+        const bool keep = i < p.m && sblk[i] != tq;
         const uint64_t bal = __ballot(keep);
         const uint64_t lower = lane == 0 ? 0ull : (~0ull >> (64 - lane));
         if (keep) srow[base + __popcll(bal & lower)] = rrow[i];
@@ -176,8 +193,9 @@ __global__ __launch_bounds__(kBNT, 2) void bwd_dq_kernel(BwdParams p) {
   const int qls = ql < qend ? ql : q0;
   const int orow = pq[qls];
   const int64_t ridx = static_cast<int64_t>(bh) * p.n + orow;
-  const float lse2 = p.lse[ridx] * kLog2e;
-  const float dl = p.drow[ridx];
+  const floatx2 qst = *reinterpret_cast<const floatx2*>(p.qstat + 2 * (static_cast<int64_t>(bh) * p.seg + qls));
+  const float lse2 = qst[0];
+  const float dl = qst[1];
   bf16x8 qf[NQF], gf[NQF];
 #pragma unroll
   for (int c = 0; c < NQF; ++c) {
@@ -206,16 +224,11 @@ __global__ __launch_bounds__(kBNT, 2) void bwd_dq_kernel(BwdParams p) {
     const int kcnt = isB ? min(kBT, nsamp - kb) : min(kBT, ka1 - kb);
 #pragma unroll
     for (int c = 0; c < G::CPT; ++c) {
-      const int j = j_first + c * JSTEP;
-      uint4v kw = {0u, 0u, 0u, 0u}, vw = {0u, 0u, 0u, 0u};
-      if (j < kcnt) {
-        const int row = isB ? srow[kb + j] : (blist ? brow[kb - ka0 + j] : pk[kb + j]);
-        const uint32_t off = static_cast<uint32_t>(row * D + 8 * c_in_row) * 2;
-        kw = ld16(kbase, off);
-        vw = ld16(vbase, off);
-      }
-      kreg[c] = kw;
-      vreg[c] = vw;
+      const int j = min(j_first + c * JSTEP, kcnt - 1);
+      const int row = isB ? srow[kb + j] : (blist ? brow[kb - ka0 + j] : pk[kb + j]);
+      const uint32_t off = static_cast<uint32_t>(row * D + 8 * c_in_row) * 2;
+      kreg[c] = ld16(kbase, off);
+      vreg[c] = ld16(vbase, off);
     }
   };
   auto store_tile = [&](int buf) {
@@ -242,42 +255,63 @@ __global__ __launch_bounds__(kBNT, 2) void bwd_dq_kernel(BwdParams p) {
     const bf16* ks = reinterpret_cast<const bf16*>(smem + (2 * buf) * G::TB);
     const bf16* vs = reinterpret_cast<const bf16*>(smem + (2 * buf + 1) * G::TB);
     const float off = (isB ? p.log2w : 0.f) - lse2;
-    const bool need_mask = kcnt < kBT || (isB ? samp_multi : multi_block);
+    // key j of a block tile lies in the query's block iff (unsigned)(j - lo) < b_eff
+    const int lo = row_blk * b_eff - kb;
+    const bool blk_test = !isB && multi_block;
+    const bool smp_test = isB && samp_multi;
+    auto tile = [&](auto mflag) {
+      constexpr bool M = decltype(mflag)::value;
 #pragma unroll
-    for (int kt = 0; kt < 2; ++kt) {
-      floatx16 s, dp;
+      for (int kt = 0; kt < 2; ++kt) {
+        bf16x8 ka[NQF], va[NQF];
 #pragma unroll
-      for (int r = 0; r < 16; ++r) s[r] = dp[r] = 0.f;
-#pragma unroll
-      for (int c = 0; c < NQF; ++c) {
-        const int e = (32 * kt + col) * G::STR + 16 * c + 8 * h2;
-        s = __builtin_amdgcn_mfma_f32_32x32x16_bf16(*reinterpret_cast<const bf16x8*>(&ks[e]), qf[c], s, 0, 0, 0);
-        dp = __builtin_amdgcn_mfma_f32_32x32x16_bf16(*reinterpret_cast<const bf16x8*>(&vs[e]), gf[c], dp, 0, 0, 0);
-      }
-      bf16x8 da, db;
-#pragma unroll
-      for (int r = 0; r < 16; ++r) {
-        bool ok = true;
-        if (need_mask) {
-          const int j = 32 * kt + 8 * (r >> 2) + 4 * h2 + (r & 3);
-          ok = j < kcnt;
-          if (isB) {
-            if (samp_multi) ok = ok && (spos[kb + min(j, kcnt - 1)] / b_eff) != row_blk;
-          } else if (multi_block) {
-            ok = ok && ((kb + j) / b_eff) == row_blk;
-          }
+        for (int c = 0; c < NQF; ++c) {
+          const int e = (32 * kt + col) * G::STR + 16 * c + 8 * h2;
+          ka[c] = *reinterpret_cast<const bf16x8*>(&ks[e]);
+          va[c] = *reinterpret_cast<const bf16x8*>(&vs[e]);
         }
-        const float pr = ok ? fast_exp2(fmaf(s[r], kLog2e, off)) : 0.f;
-        const bf16 dsv = static_cast<bf16>(pr * (dp[r] - dl));
-        if (r < 8) da[r] = dsv;
-        else db[r - 8] = dsv;
-      }
+        floatx16 s, dp;
 #pragma unroll
-      for (int t = 0; t < NDT; ++t) {
-        acc[t] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(lds_tr_operand(ks, G::STR, 2 * kt, t, lane), da, acc[t], 0, 0, 0);
-        acc[t] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(lds_tr_operand(ks, G::STR, 2 * kt + 1, t, lane), db, acc[t], 0, 0, 0);
+        for (int r = 0; r < 16; ++r) s[r] = dp[r] = 0.f;
+#pragma unroll
+        for (int c = 0; c < NQF; ++c) {
+          s = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ka[c], qf[c], s, 0, 0, 0);
+          dp = __builtin_amdgcn_mfma_f32_32x32x16_bf16(va[c], gf[c], dp, 0, 0, 0);
+        }
+        __builtin_amdgcn_sched_barrier(0);
+        bf16x8 kto[NDT][2];
+#pragma unroll
+        for (int t = 0; t < NDT; ++t) {
+          kto[t][0] = lds_tr_operand(ks, G::STR, 2 * kt, t, lane);
+          kto[t][1] = lds_tr_operand(ks, G::STR, 2 * kt + 1, t, lane);
+        }
+        bf16x8 da, db;
+#pragma unroll
+        for (int r = 0; r < 16; ++r) {
+          float x = fmaf(s[r], kLog2e, off);
+          if constexpr (M) {
+            const int j = 32 * kt + 8 * (r >> 2) + 4 * h2 + (r & 3);
+            bool ok = j < kcnt;
+            if (blk_test) ok &= static_cast<unsigned>(j - lo) < static_cast<unsigned>(b_eff);
+            if (smp_test) ok &= sblk[kb + min(j, kcnt - 1)] != row_blk;
+            x = ok ? x : -INFINITY;
+          }
+          const float pr = fast_exp2(x);
+          const bf16 dsv = static_cast<bf16>(pr * (dp[r] - dl));
+          if (r < 8) da[r] = dsv;
+          else db[r - 8] = dsv;
+        }
+        __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+        for (int t = 0; t < NDT; ++t) {
+          acc[t] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kto[t][0], da, acc[t], 0, 0, 0);
+          acc[t] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kto[t][1], db, acc[t], 0, 0, 0);
+        }
+        __builtin_amdgcn_sched_barrier(0);
       }
-    }
+    };
+    if (kcnt < kBT || blk_test || smp_test) tile(Flag<true>());
+    else tile(Flag<false>());
   }
 
   // ---- dQ rows (fp32): register r of tile t holds column 32 t + 8 (r / 4) + 4 h2 + r % 4
@@ -297,11 +331,16 @@ __global__ __launch_bounds__(kBNT, 2) void bwd_dq_kernel(BwdParams p) {
 
 // ---- dK, dV (key-owned) ---------------------------------------------------------------
 
-// LDS per buffer: Q tile, dO tile (64 rows each), lse2[64], D[64].
+// LDS per buffer: Q tile, dO tile (64 rows each), lse log2 e [64], D[64].
 template <int D>
 constexpr int dkv_buf_bytes() { return 2 * BGeo<D>::TB + 2 * kBT * 4; }
 
-template <int D, bool SAMPLE>
+// EMASK: per-element block masks, needed when the block size is not a
+// multiple of the 64-row tile.  Otherwise every query tile lies wholly inside
+// or wholly outside a key's block, and the mask is a per-lane, per-tile bias
+// (0 or -inf) folded into the exponent; ragged query rows carry lse = +inf.
+// Lanes past the last key need no mask: their column is never stored.
+template <int D, bool SAMPLE, bool EMASK>
 __global__ __launch_bounds__(kBNT, 2) void bwd_dkv_kernel(BwdParams p) {
   typedef BGeo<D> G;
   constexpr int NQF = G::NQF, NDT = G::NDT;
@@ -371,40 +410,42 @@ __global__ __launch_bounds__(kBNT, 2) void bwd_dkv_kernel(BwdParams p) {
   const int ntiles = qtiles * nheads;
   const float wbias = SAMPLE ? p.log2w : 0.f;
 
-  // ---- tile staging: query rows of Q and dO, their lse (log2) and D
+  // ---- tile staging: query rows of Q and dO and their statistics.  The
+  // permutation entries of a tile are fetched one tile ahead of its rows,
+  // so no row load waits on a load issued in the same iteration.
   const int c_in_row = tid % G::CPR;
   const int j_first = tid / G::CPR;
   constexpr int JSTEP = kBNT / G::CPR;
   uint4v qreg[G::CPT], greg[G::CPT];
-  float lreg = 0.f, dreg = 0.f;
-  auto load_tile = [&](int it) {
-    const int hh = it / qtiles;
-    const int tq0 = qa0 + (it % qtiles) * kBT;
-    const int qcnt = min(kBT, qa1 - tq0);
-    const int bh = bh0 + hh;
-    const bf16* qb = static_cast<const bf16*>(p.q) + static_cast<int64_t>(bh) * p.n * D;
-    const bf16* gb = static_cast<const bf16*>(p.dout) + static_cast<int64_t>(bh) * p.n * D;
+  int prow[G::CPT];
+  floatx2 sreg = {0.f, 0.f};
+  auto tile_rows = [&](int it, int& tq0, int& qcnt, int& bh) {
+    tq0 = qa0 + (it % qtiles) * kBT;
+    qcnt = min(kBT, qa1 - tq0);
+    bh = bh0 + it / qtiles;
+  };
+  auto fetch_perm = [&](int it) {
+    int tq0, qcnt, bh;
+    tile_rows(it, tq0, qcnt, bh);
     const int32_t* pq = p.perm_q + static_cast<int64_t>(bh) * p.seg;
 #pragma unroll
+    for (int c = 0; c < G::CPT; ++c) prow[c] = pq[tq0 + min(j_first + c * JSTEP, qcnt - 1)];
+  };
+  auto load_tile = [&](int it) {
+    int tq0, qcnt, bh;
+    tile_rows(it, tq0, qcnt, bh);
+    const bf16* qb = static_cast<const bf16*>(p.q) + static_cast<int64_t>(bh) * p.n * D;
+    const bf16* gb = static_cast<const bf16*>(p.dout) + static_cast<int64_t>(bh) * p.n * D;
+#pragma unroll
     for (int c = 0; c < G::CPT; ++c) {
-      const int j = j_first + c * JSTEP;
-      uint4v qw = {0u, 0u, 0u, 0u}, gw = {0u, 0u, 0u, 0u};
-      if (j < qcnt) {
-        const uint32_t off = static_cast<uint32_t>(pq[tq0 + j] * D + 8 * c_in_row) * 2;
-        qw = ld16(qb, off);
-        gw = ld16(gb, off);
-      }
-      qreg[c] = qw;
-      greg[c] = gw;
+      const uint32_t off = static_cast<uint32_t>(prow[c] * D + 8 * c_in_row) * 2;
+      qreg[c] = ld16(qb, off);
+      greg[c] = ld16(gb, off);
     }
     if (tid < kBT) {
-      lreg = -INFINITY;
-      dreg = 0.f;
-      if (tid < qcnt) {
-        const int64_t r = static_cast<int64_t>(bh) * p.n + pq[tq0 + tid];
-        lreg = p.lse[r] * kLog2e;
-        dreg = p.drow[r];
-      }
+      sreg = *reinterpret_cast<const floatx2*>(p.qstat + 2 * (static_cast<int64_t>(bh) * p.seg + tq0 +
+                                                               min(tid, qcnt - 1)));
+      if (tid >= qcnt) sreg[0] = INFINITY;      // ragged row: P = 0
     }
   };
   auto store_tile = [&](int buf) {
@@ -419,75 +460,99 @@ __global__ __launch_bounds__(kBNT, 2) void bwd_dkv_kernel(BwdParams p) {
       *reinterpret_cast<uint4v*>(&gs[j * G::STR + 8 * c_in_row]) = greg[c];
     }
     if (tid < kBT) {
-      ls[tid] = lreg;
-      ls[kBT + tid] = dreg;
+      ls[tid] = sreg[0];
+      ls[kBT + tid] = sreg[1];
     }
   };
 
-  if (ntiles > 0) load_tile(0);
+  if (ntiles > 0) {
+    fetch_perm(0);
+    load_tile(0);
+    if (ntiles > 1) fetch_perm(1);
+  }
   for (int it = 0; it < ntiles; ++it) {
     const int buf = it & 1;
     store_tile(buf);
     __syncthreads();
-    if (it + 1 < ntiles) load_tile(it + 1);
-    const int tq0 = qa0 + (it % qtiles) * kBT;
-    const int qcnt = min(kBT, qa1 - tq0);
+    if (it + 1 < ntiles) {
+      load_tile(it + 1);
+      if (it + 2 < ntiles) fetch_perm(it + 2);
+    }
+    int tq0, qcnt, bh_unused;
+    tile_rows(it, tq0, qcnt, bh_unused);
     const char* base = smem + buf * BUF;
     const bf16* qs = reinterpret_cast<const bf16*>(base);
     const bf16* gs = reinterpret_cast<const bf16*>(base + G::TB);
     const float* ls = reinterpret_cast<const float*>(base + 2 * G::TB);
     // query j of the tile lies in this lane's key block iff (unsigned)(j - lo) < b_eff
     const int lo = kblk * b_eff - tq0;
-    // masks are needed unless the tile is full and, for every lane of the
-    // wave, wholly inside (block part) or wholly outside (sample part) the
-    // key's block
-    const bool inside = lo <= 0 && lo + b_eff >= kBT;
-    const bool outside = lo >= kBT || lo + b_eff <= 0;
-    const bool need_mask = qcnt < kBT || __ballot(!kvalid || (SAMPLE ? !outside : !inside)) != 0;
+    float bias = wbias;
+    if constexpr (!EMASK) {
+      const bool tin = static_cast<unsigned>(-lo) < static_cast<unsigned>(b_eff);
+      if (SAMPLE ? tin : !tin) bias = -INFINITY;
+    }
+    {
 #pragma unroll
-    for (int qt = 0; qt < 2; ++qt) {
-      floatx16 s, dp;
+      for (int qt = 0; qt < 2; ++qt) {
+        bf16x8 qa[NQF], ga[NQF];
 #pragma unroll
-      for (int r = 0; r < 16; ++r) s[r] = dp[r] = 0.f;
+        for (int c = 0; c < NQF; ++c) {
+          const int e = (32 * qt + col) * G::STR + 16 * c + 8 * h2;
+          qa[c] = *reinterpret_cast<const bf16x8*>(&qs[e]);
+          ga[c] = *reinterpret_cast<const bf16x8*>(&gs[e]);
+        }
+        floatx16 s, dp;
 #pragma unroll
-      for (int c = 0; c < NQF; ++c) {
-        const int e = (32 * qt + col) * G::STR + 16 * c + 8 * h2;
-        s = __builtin_amdgcn_mfma_f32_32x32x16_bf16(*reinterpret_cast<const bf16x8*>(&qs[e]), kf[c], s, 0, 0, 0);
-        dp = __builtin_amdgcn_mfma_f32_32x32x16_bf16(*reinterpret_cast<const bf16x8*>(&gs[e]), vf[c], dp, 0, 0, 0);
-      }
-      bf16x8 pa, pb, da, db;
+        for (int r = 0; r < 16; ++r) s[r] = dp[r] = 0.f;
 #pragma unroll
-      for (int g = 0; g < 4; ++g) {
-        const int j0 = 32 * qt + 8 * g + 4 * h2;      // 4 consecutive queries of the tile
-        const floatx4 l4 = *reinterpret_cast<const floatx4*>(ls + j0);
-        const floatx4 d4 = *reinterpret_cast<const floatx4*>(ls + kBT + j0);
+        for (int c = 0; c < NQF; ++c) {
+          s = __builtin_amdgcn_mfma_f32_32x32x16_bf16(qa[c], kf[c], s, 0, 0, 0);
+          dp = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ga[c], vf[c], dp, 0, 0, 0);
+        }
+        __builtin_amdgcn_sched_barrier(0);
+        bf16x8 gto[NDT][2], qto[NDT][2];
 #pragma unroll
-        for (int i = 0; i < 4; ++i) {
-          const int r = 4 * g + i;
-          const int j = j0 + i;
-          bool ok = true;
-          if (need_mask) {
-            const bool in_blk = static_cast<unsigned>(j - lo) < static_cast<unsigned>(b_eff);
-            ok = kvalid && j < qcnt && (SAMPLE ? !in_blk : in_blk);
-          }
-          const float pr = ok ? fast_exp2(fmaf(s[r], kLog2e, wbias - l4[i])) : 0.f;
-          const bf16 pv = static_cast<bf16>(pr);
-          const bf16 dsv = static_cast<bf16>(pr * (dp[r] - d4[i]));
-          if (r < 8) {
-            pa[r] = pv;
-            da[r] = dsv;
-          } else {
-            pb[r - 8] = pv;
-            db[r - 8] = dsv;
+        for (int t = 0; t < NDT; ++t) {
+          gto[t][0] = lds_tr_operand(gs, G::STR, 2 * qt, t, lane);
+          gto[t][1] = lds_tr_operand(gs, G::STR, 2 * qt + 1, t, lane);
+          qto[t][0] = lds_tr_operand(qs, G::STR, 2 * qt, t, lane);
+          qto[t][1] = lds_tr_operand(qs, G::STR, 2 * qt + 1, t, lane);
+        }
+        bf16x8 pa, pb, da, db;
+#pragma unroll
+        for (int g = 0; g < 4; ++g) {
+          const int j0 = 32 * qt + 8 * g + 4 * h2;      // 4 consecutive queries of the tile
+          const floatx4 l4 = *reinterpret_cast<const floatx4*>(ls + j0);
+          const floatx4 d4 = *reinterpret_cast<const floatx4*>(ls + kBT + j0);
+#pragma unroll
+          for (int i = 0; i < 4; ++i) {
+            const int r = 4 * g + i;
+            float x = fmaf(s[r], kLog2e, bias - l4[i]);
+            if constexpr (EMASK) {
+              const bool in_blk = static_cast<unsigned>(j0 + i - lo) < static_cast<unsigned>(b_eff);
+              x = (SAMPLE ? !in_blk : in_blk) ? x : -INFINITY;
+            }
+            const float pr = fast_exp2(x);
+            const bf16 pv = static_cast<bf16>(pr);
+            const bf16 dsv = static_cast<bf16>(pr * (dp[r] - d4[i]));
+            if (r < 8) {
+              pa[r] = pv;
+              da[r] = dsv;
+            } else {
+              pb[r - 8] = pv;
+              db[r - 8] = dsv;
+            }
           }
         }
-      }
+        __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
-      for (int t = 0; t < NDT; ++t) {
-        dv[t] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(lds_tr_operand(gs, G::STR, 2 * qt, t, lane), pa, dv[t], 0, 0, 0);
-        dv[t] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(lds_tr_operand(gs, G::STR, 2 * qt + 1, t, lane), pb, dv[t], 0, 0, 0);
-        dk[t] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(lds_tr_operand(qs, G::STR, 2 * qt, t, lane), da, dk[t], 0, 0, 0);
-        dk[t] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(lds_tr_operand(qs, G::STR, 2 * qt + 1, t, lane), db, dk[t], 0, 0, 0);
+        for (int t = 0; t < NDT; ++t) {
+          dv[t] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(gto[t][0], pa, dv[t], 0, 0, 0);
+          dv[t] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(gto[t][1], pb, dv[t], 0, 0, 0);
+          dk[t] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(qto[t][0], da, dk[t], 0, 0, 0);
+          dk[t] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(qto[t][1], db, dk[t], 0, 0, 0);
+        }
+        __builtin_amdgcn_sched_barrier(0);
       }
     }
   }
@@ -589,8 +654,8 @@ int launch_bwd_dq(const BwdParams& p, hipStream_t s) {
   return after_launch("backward dq", s);
 }
 
-template <int D, bool SAMPLE>
-static int launch_dkv_d(const BwdParams& p, hipStream_t s) {
+template <int D, bool SAMPLE, bool EMASK>
+static int launch_dkv_d2(const BwdParams& p, hipStream_t s) {
   int64_t blocks;
   const int nchunk = (p.seg + p.qchunk - 1) / p.qchunk;
   if constexpr (SAMPLE) {
@@ -600,13 +665,19 @@ static int launch_dkv_d(const BwdParams& p, hipStream_t s) {
   }
   if (blocks == 0) return HA_OK;
   const size_t lds = 2 * dkv_buf_bytes<D>();
-  hipLaunchKernelGGL((bwd_dkv_kernel<D, SAMPLE>), dim3(static_cast<unsigned>(blocks)), dim3(kBNT), lds, s, p);
+  hipLaunchKernelGGL((bwd_dkv_kernel<D, SAMPLE, EMASK>), dim3(static_cast<unsigned>(blocks)), dim3(kBNT), lds, s, p);
   if constexpr (SAMPLE) {
     const int64_t threads = static_cast<int64_t>(p.BH) * p.m * (2 * D / 4);
     hipLaunchKernelGGL((bwd_dkv_reduce_kernel<D>), dim3(static_cast<unsigned>((threads + 255) / 256)), dim3(256), 0,
                        s, p, nchunk);
   }
   return HA_OK;
+}
+
+template <int D, bool SAMPLE>
+static int launch_dkv_d(const BwdParams& p, hipStream_t s) {
+  if (p.b_eff % kBT) return launch_dkv_d2<D, SAMPLE, true>(p, s);
+  return launch_dkv_d2<D, SAMPLE, false>(p, s);
 }
 
 int launch_bwd_dkv(const BwdParams& p, bool samples, hipStream_t s) {

@@ -90,7 +90,7 @@ struct BwdParams {
   const void* out = nullptr;         // forward output [BH][n][d]
   const void* dout = nullptr;        // upstream gradient [BH][n][d]
   const float* lse = nullptr;        // forward lse [BH][n] (natural log)
-  float* drow = nullptr;             // D = rowsum(dout * out) [BH][n]
+  float* qstat = nullptr;            // per sorted query: (lse log2 e, rowsum(dout * out)) [BH][seg][2]
   int d = 64;
   int n = 0;
   int H = 1, Hkv = 1;
@@ -117,7 +117,7 @@ inline int bwd_query_chunk(int seg) {
   return per64 > 2048 ? per64 : 2048;
 }
 
-int launch_bwd_rowdot(const BwdParams& p, hipStream_t s);
+int launch_bwd_qstat(const BwdParams& p, hipStream_t s);
 int launch_bwd_dq(const BwdParams& p, hipStream_t s);
 int launch_bwd_dkv(const BwdParams& p, bool samples, hipStream_t s);
 

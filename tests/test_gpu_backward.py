@@ -57,6 +57,7 @@ CASES = [
     (1, 1, 1, 768, 64, 768, 30, 7, 6),        # one block = the whole segment: samples all excluded
     (1, 2, 1, 1024, 64, 128, 0, 7, 7),        # no samples
     (1, 4, 2, 2048, 128, 512, 256, 8, 8),     # d = 128, block wider than a workgroup
+    (1, 2, 1, 960, 64, 96, 70, 6, 9),         # block not a multiple of the 64-row tile
 ]
 
 
