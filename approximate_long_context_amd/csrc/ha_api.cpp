@@ -393,32 +393,79 @@ static int forward_impl(const void* q, const void* k, const void* v, Shape sh, u
   return HA_OK;
 }
 
-// ---- backward (non-causal) ------------------------------------------------------
+// ---- backward -------------------------------------------------------------------
 // Same projections, hashes, sorts and samples as the forward (recomputed
-// from the seed), then D = rowsum(dO * O), dQ, the block part of dK / dV
-// (stored) and the sample part of dK / dV (added).
+// from the seed), then the per-row statistics (lse, D = rowsum(dO * O)) and,
+// for every problem the forward solved, dQ, the block part of dK / dV and
+// the sample part of dK / dV.  Non-causal: one problem per head (dQ and the
+// block part stored, the sample part added).  Causal: the exact leaves first
+// (dQ stored; dK / dV of each key's own 256-query square stored, the later
+// queries added), then every level's quadrant problems, all added.
 
-static size_t backward_plan(const Shape& sh, void* ws, size_t cap, Plan* pl, float** qstat, float** part) {
-  Shape f = sh;
-  f.flags = 0;
-  *pl = make_plan(f, ws, cap);
+struct BwdPlan {
+  float* R;
+  uint16_t* rank_q;
+  uint16_t* rank_k;
+  int32_t* perm_q;
+  int32_t* perm_k;
+  int32_t* sidx;
+  void* sort_ws;
+  size_t sort_ws_bytes;
+  float* qstat;
+  float* part;
+  size_t total;
+};
+
+static int64_t bwd_part_floats(int64_t BH, int seg, int pieces, int m, int d) {
+  const int qc = bwd_query_chunk(seg);
+  return static_cast<int64_t>((seg + qc - 1) / qc) * BH * pieces * m * 2 * d;
+}
+
+static BwdPlan backward_plan(const Shape& sh, void* ws, size_t cap) {
+  BwdPlan pl{};
   Carve cv(ws, cap);
-  cv.used = pl->total;
   const int64_t BH = static_cast<int64_t>(sh.batch) * sh.heads;
-  *qstat = cv.take<float>(2 * BH * sh.n);
-  const int64_t nchunk = sh.n > 0 ? (sh.n + bwd_query_chunk(sh.n) - 1) / bwd_query_chunk(sh.n) : 0;
-  *part = cv.take<float>(nchunk * BH * sh.samples * 2 * sh.d);
-  return align_up(cv.used, 256) + 256;
+  const int64_t BK = static_cast<int64_t>(sh.batch) * sh.kv_heads;
+  const int m1 = sh.samples > 0 ? sh.samples : 1;
+  pl.R = cv.take<float>(static_cast<size_t>(sh.r) * sh.d);
+  pl.rank_q = cv.take<uint16_t>(BH * sh.n);
+  pl.rank_k = cv.take<uint16_t>(BK * sh.n);
+  pl.qstat = cv.take<float>(2 * BH * sh.n);
+  if (!sh.causal) {
+    pl.perm_q = cv.take<int32_t>(BH * sh.n);
+    pl.perm_k = cv.take<int32_t>(BK * sh.n);
+    pl.sidx = cv.take<int32_t>(BH * m1);
+    size_t a = sort_ws_bytes(BH, sh.n, 1, sh.r), b = sort_ws_bytes(BK, sh.n, 1, sh.r);
+    pl.sort_ws_bytes = a > b ? a : b;
+    pl.sort_ws = cv.take<char>(pl.sort_ws_bytes);
+    pl.part = cv.take<float>(bwd_part_floats(BH, sh.n, 1, sh.samples, sh.d));
+  } else if (sh.levels > 0) {
+    pl.perm_q = cv.take<int32_t>(BH * (sh.n / 2));
+    pl.perm_k = cv.take<int32_t>(BK * (sh.n / 2));
+    pl.sidx = cv.take<int32_t>(BH * (int64_t(1) << (sh.levels - 1)) * m1);
+    size_t mx = 0;
+    int64_t part = 0;
+    for (int l = 1; l <= sh.levels; ++l) {
+      const int seg = sh.n >> l;
+      const int pieces = 1 << (l - 1);
+      size_t a = sort_ws_bytes(BH, seg, pieces, sh.r), b = sort_ws_bytes(BK, seg, pieces, sh.r);
+      if (a > mx) mx = a;
+      if (b > mx) mx = b;
+      const int64_t f = bwd_part_floats(BH, seg, pieces, sh.samples, sh.d);
+      if (f > part) part = f;
+    }
+    pl.sort_ws_bytes = mx;
+    pl.sort_ws = cv.take<char>(mx);
+    pl.part = cv.take<float>(part);
+  }
+  pl.total = align_up(cv.used, 256) + 256;
+  return pl;
 }
 
 static int backward_impl(const void* q, const void* k, const void* v, const void* out, const float* lse,
                          const void* dout, Shape sh, uint64_t seed, float* dq, float* dk, float* dv, void* ws,
                          size_t ws_bytes, hipStream_t s) {
   HA_TRY(validate(sh));
-  if (sh.causal) {
-    set_error("backward: causal problems are not built yet");
-    return HA_EUNSUPPORTED;
-  }
   if (sh.dtype != HA_BF16) {
     set_error("backward: bf16 inputs only");
     return HA_EUNSUPPORTED;
@@ -432,10 +479,7 @@ static int backward_impl(const void* q, const void* k, const void* v, const void
     set_error("null pointer argument");
     return HA_EINVAL;
   }
-  Plan pl;
-  float* qstat = nullptr;
-  float* part = nullptr;
-  const size_t need = backward_plan(sh, nullptr, 0, &pl, &qstat, &part);
+  const size_t need = backward_plan(sh, nullptr, 0).total;
   if (!ws || ws_bytes < need) {
     set_error("workspace of %zu bytes < %zu required", ws_bytes, need);
     return HA_EWORKSPACE;
@@ -444,19 +488,17 @@ static int backward_impl(const void* q, const void* k, const void* v, const void
     set_error("workspace must be 256-byte aligned");
     return HA_EINVAL;
   }
-  backward_plan(sh, ws, ws_bytes, &pl, &qstat, &part);
-  const int64_t BH = static_cast<int64_t>(sh.batch) * sh.heads;
-  const int64_t BK = static_cast<int64_t>(sh.batch) * sh.kv_heads;
   if (static_cast<int64_t>(sh.n) * sh.d * 2 >= (int64_t(1) << 32)) {
     set_error("backward: one head of q/k/v spans 4 GiB or more");
     return HA_EUNSUPPORTED;
   }
+  const BwdPlan pl = backward_plan(sh, ws, ws_bytes);
+  const int64_t BH = static_cast<int64_t>(sh.batch) * sh.heads;
+  const int64_t BK = static_cast<int64_t>(sh.batch) * sh.kv_heads;
   HA_TRY(launch_projections(seed, sh.d, sh.r, pl.R, s));
   HA_TRY(launch_hash(q, sh.dtype, BH * sh.n, sh.d, sh.r, pl.R, pl.rank_q, s));
   HA_TRY(launch_hash(k, sh.dtype, BK * sh.n, sh.d, sh.r, pl.R, pl.rank_k, s));
-  HA_TRY(launch_sort(pl.rank_q, BH, sh.n, sh.n, 0, sh.n, 1, sh.r, pl.perm_q, pl.sort_ws, pl.sort_ws_bytes, s));
-  HA_TRY(launch_sort(pl.rank_k, BK, sh.n, sh.n, 0, sh.n, 1, sh.r, pl.perm_k, pl.sort_ws, pl.sort_ws_bytes, s));
-  HA_TRY(launch_sample_indices(seed, sh.batch, sh.heads, 1, 1, sh.n, sh.samples, pl.sidx, s));
+
   BwdParams bp;
   bp.q = q;
   bp.k = k;
@@ -464,28 +506,72 @@ static int backward_impl(const void* q, const void* k, const void* v, const void
   bp.out = out;
   bp.dout = dout;
   bp.lse = lse;
-  bp.qstat = qstat;
+  bp.qstat = pl.qstat;
   bp.d = sh.d;
   bp.n = sh.n;
   bp.H = sh.heads;
   bp.Hkv = sh.kv_heads;
   bp.BH = static_cast<int>(BH);
-  bp.seg = sh.n;
-  bp.perm_q = pl.perm_q;
-  bp.perm_k = pl.perm_k;
-  bp.sidx = pl.sidx;
-  bp.m = sh.samples;
-  bp.log2w = sh.samples > 0 ? static_cast<float>(std::log2(static_cast<double>(sh.n) / sh.samples)) : 0.f;
-  bp.b_eff = sh.block < sh.n ? sh.block : sh.n;
-  bp.qchunk = bwd_query_chunk(sh.n);
-  bp.part = part;
+  bp.part = pl.part;
   bp.dq = dq;
   bp.dk = dk;
   bp.dv = dv;
   HA_TRY(launch_bwd_qstat(bp, s));
-  HA_TRY(launch_bwd_dq(bp, s));
-  HA_TRY(launch_bwd_dkv(bp, false, s));
-  return launch_bwd_dkv(bp, true, s);
+
+  // one sorted problem per piece: queries [p stride + q_first, + seg), keys [p stride + k_first, + seg)
+  auto sorted_problems = [&](int seg, int pieces, int q_first, int k_first, int stride, int accumulate) -> int {
+    BwdParams qp = bp;
+    qp.pieces = pieces;
+    qp.seg = seg;
+    qp.stride = stride;
+    qp.q_first = q_first;
+    qp.k_first = k_first;
+    qp.perm_q = pl.perm_q;
+    qp.perm_k = pl.perm_k;
+    qp.sidx = pl.sidx;
+    qp.m = sh.samples;
+    qp.log2w = sh.samples > 0 ? static_cast<float>(std::log2(static_cast<double>(seg) / sh.samples)) : 0.f;
+    qp.b_eff = sh.block < seg ? sh.block : seg;
+    qp.qchunk = bwd_query_chunk(seg);
+    qp.accumulate = accumulate;
+    HA_TRY(launch_bwd_dq(qp, s));
+    HA_TRY(launch_bwd_dkv(qp, false, s));
+    return launch_bwd_dkv(qp, true, s);
+  };
+
+  if (!sh.causal) {
+    HA_TRY(launch_sort(pl.rank_q, BH, sh.n, sh.n, 0, sh.n, 1, sh.r, pl.perm_q, pl.sort_ws, pl.sort_ws_bytes, s));
+    HA_TRY(launch_sort(pl.rank_k, BK, sh.n, sh.n, 0, sh.n, 1, sh.r, pl.perm_k, pl.sort_ws, pl.sort_ws_bytes, s));
+    HA_TRY(launch_sample_indices(seed, sh.batch, sh.heads, 1, 1, sh.n, sh.samples, pl.sidx, s));
+    return sorted_problems(sh.n, 1, 0, 0, sh.n, 0);
+  }
+
+  // exact causal leaves, rows in their own order
+  BwdParams lp = bp;
+  lp.pieces = sh.n / sh.leaf;
+  lp.seg = sh.leaf;
+  lp.stride = sh.leaf;
+  lp.b_eff = sh.leaf;
+  lp.causal = 1;
+  HA_TRY(launch_bwd_dq(lp, s));
+  lp.diag = 2;
+  HA_TRY(launch_bwd_dkv(lp, false, s));
+  lp.diag = 1;
+  lp.accumulate = 1;
+  HA_TRY(launch_bwd_dkv(lp, false, s));
+
+  // quadrant problems of every level: queries [mid, hi), keys [lo, mid) of each node
+  for (int l = sh.levels; l >= 1; --l) {
+    const int seg = sh.n >> l;
+    const int pieces = 1 << (l - 1);
+    HA_TRY(launch_sort(pl.rank_q, BH, sh.n, seg, seg, 2 * seg, pieces, sh.r, pl.perm_q, pl.sort_ws,
+                       pl.sort_ws_bytes, s));
+    HA_TRY(launch_sort(pl.rank_k, BK, sh.n, seg, 0, 2 * seg, pieces, sh.r, pl.perm_k, pl.sort_ws,
+                       pl.sort_ws_bytes, s));
+    HA_TRY(launch_sample_indices(seed, sh.batch, sh.heads, pieces, pieces, seg, sh.samples, pl.sidx, s));
+    HA_TRY(sorted_problems(seg, pieces, seg, 0, 2 * seg, 1));
+  }
+  return HA_OK;
 }
 
 }  // namespace ha
@@ -530,10 +616,7 @@ size_t hyperattn_backward_workspace_bytes(int batch, int n, int d, int heads, in
                                           int dtype) {
   Shape sh{batch, n, d, heads, kv_heads, block, samples, proj_bits, causal, min_seq_len, dtype, 0};
   if (validate(sh) != HA_OK) return 0;
-  Plan pl;
-  float* qstat = nullptr;
-  float* part = nullptr;
-  return backward_plan(sh, nullptr, 0, &pl, &qstat, &part);
+  return backward_plan(sh, nullptr, 0).total;
 }
 
 int hyperattn_backward(const void* q, const void* k, const void* v, const void* out, const float* lse,

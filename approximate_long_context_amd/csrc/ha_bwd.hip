@@ -50,7 +50,7 @@ constexpr int kBTQ = 32 * kBW;   // rows owned by a workgroup
 template <int D>
 struct BGeo {
   static constexpr int STR = D + 8;               // LDS row stride (bf16 elements)
-  static constexpr int TB = kBT * STR * 2;        // bytes of one 64-row tile
+  static constexpr int TB = kBT * STR * 2;        // bytes of one tile
   static constexpr int CPR = D / 8;               // 16-byte chunks per row
   static constexpr int CPT = kBT * CPR / kBNT;    // chunks per thread per tile
   static constexpr int NQF = D / 16;              // k-chunks of one MFMA operand row
@@ -58,7 +58,7 @@ struct BGeo {
   static_assert((kBT * CPR) % kBNT == 0, "tile split");
 };
 
-// ---- per-query statistics: (lse log2 e, D = rowsum(dO o O)) in sorted order ---------
+// ---- per-row statistics: (lse log2 e, D = rowsum(dO o O)) in row order ------------------
 
 template <int D>
 __global__ __launch_bounds__(256) void bwd_qstat_kernel(BwdParams p) {
@@ -66,15 +66,13 @@ __global__ __launch_bounds__(256) void bwd_qstat_kernel(BwdParams p) {
   constexpr int RPW = 64 / LPR;
   const bf16* o = static_cast<const bf16*>(p.out);
   const bf16* dout = static_cast<const bf16*>(p.dout);
-  const int64_t rows = static_cast<int64_t>(p.BH) * p.seg;
+  const int64_t rows = static_cast<int64_t>(p.BH) * p.n;
   const int lane = threadIdx.x & 63;
   const int64_t wave = (static_cast<int64_t>(blockIdx.x) * blockDim.x + threadIdx.x) >> 6;
   const int64_t nwaves = (static_cast<int64_t>(gridDim.x) * blockDim.x) >> 6;
   for (int64_t r0 = wave * RPW; r0 < rows; r0 += nwaves * RPW) {
-    const int64_t t = r0 + lane / LPR;              // sorted position over all problems
-    const int64_t ts = t < rows ? t : rows - 1;
-    const int64_t bh = ts / p.seg;
-    const int64_t row = bh * p.n + p.perm_q[ts];
+    const int64_t t = r0 + lane / LPR;
+    const int64_t row = t < rows ? t : rows - 1;
     const int64_t off = row * D + 8 * (lane % LPR);
     const uint4v a = *reinterpret_cast<const uint4v*>(o + off);
     const uint4v g = *reinterpret_cast<const uint4v*>(dout + off);
@@ -97,14 +95,14 @@ __global__ __launch_bounds__(256) void bwd_qstat_kernel(BwdParams p) {
 }
 
 int launch_bwd_qstat(const BwdParams& p, hipStream_t s) {
-  const int64_t rows = static_cast<int64_t>(p.BH) * p.seg;
+  const int64_t rows = static_cast<int64_t>(p.BH) * p.n;
   if (rows == 0) return HA_OK;
   const int rpw = 64 / (p.d / 8);
   int64_t blocks = (rows + 4 * rpw - 1) / (4 * rpw);
   if (blocks > 16384) blocks = 16384;
   if (p.d == 64) hipLaunchKernelGGL(bwd_qstat_kernel<64>, dim3(blocks), dim3(256), 0, s, p);
   else hipLaunchKernelGGL(bwd_qstat_kernel<128>, dim3(blocks), dim3(256), 0, s, p);
-  return after_launch("backward query statistics", s);
+  return after_launch("backward row statistics", s);
 }
 
 // ---- dQ (query-owned) -----------------------------------------------------------------
@@ -127,7 +125,9 @@ __global__ __launch_bounds__(kBNT, 2) void bwd_dq_kernel(BwdParams p) {
   const int QT = (p.seg + kBTQ - 1) / kBTQ;
   const int lid = xcd_remap(blockIdx.x, gridDim.x);
   const int qt = lid % QT;
-  const int bh = lid / QT;
+  const int prob = lid / QT;                      // bh * pieces + piece
+  const int bh = prob / p.pieces;
+  const int piece = prob - bh * p.pieces;
   const int b = bh / p.H;
   const int bkv = b * p.Hkv + (bh % p.H) / (p.H / p.Hkv);
   const int q0 = qt * kBTQ;
@@ -138,11 +138,15 @@ __global__ __launch_bounds__(kBNT, 2) void bwd_dq_kernel(BwdParams p) {
   const bf16* gb = static_cast<const bf16*>(p.dout) + static_cast<int64_t>(bh) * p.n * D;
   const bf16* kbase = static_cast<const bf16*>(p.k) + static_cast<int64_t>(bkv) * p.n * D;
   const bf16* vbase = static_cast<const bf16*>(p.v) + static_cast<int64_t>(bkv) * p.n * D;
-  const int32_t* pq = p.perm_q + static_cast<int64_t>(bh) * p.seg;
-  const int32_t* pk = p.perm_k + static_cast<int64_t>(bkv) * p.seg;
+  const int32_t* pq = p.perm_q ? p.perm_q + static_cast<int64_t>(prob) * p.seg : nullptr;
+  const int32_t* pk = p.perm_k ? p.perm_k + (static_cast<int64_t>(bkv) * p.pieces + piece) * p.seg : nullptr;
+  const int qrow0 = piece * p.stride + p.q_first;
+  const int krow0 = piece * p.stride + p.k_first;
+  auto krow_of = [&](int t) { return pk ? pk[t] : krow0 + t; };
 
   const int ka0 = (q0 / b_eff) * b_eff;
-  const int ka1 = min(((qend - 1) / b_eff + 1) * b_eff, p.seg);
+  int ka1 = min(((qend - 1) / b_eff + 1) * b_eff, p.seg);
+  if (p.causal) ka1 = min(ka1, qend);             // keys after the last query carry no weight
   const bool multi_block = (q0 / b_eff) != ((qend - 1) / b_eff);
   const bool samp = p.m > 0;
   const bool samp_multi = samp && multi_block;
@@ -157,9 +161,9 @@ __global__ __launch_bounds__(kBNT, 2) void bwd_dq_kernel(BwdParams p) {
   const bool blist = p.bcap > 0;
   int nsamp = 0;
   if (blist)
-    for (int j = tid; j < nbl; j += kBNT) brow[j] = pk[ka0 + j];
+    for (int j = tid; j < nbl; j += kBNT) brow[j] = krow_of(ka0 + j);
   if (samp) {
-    const int32_t* si = p.sidx + static_cast<int64_t>(bh) * p.m;
+    const int32_t* si = p.sidx + static_cast<int64_t>(prob) * p.m;
     const int tq = q0 / b_eff;
     int* raw = samp_multi ? srow : rrow;
     for (int c = 64 * wave; c < p.m; c += kBNT) {
@@ -167,7 +171,7 @@ __global__ __launch_bounds__(kBNT, 2) void bwd_dq_kernel(BwdParams p) {
       const int sp = i < p.m ? si[i] : 0;
       if (i < p.m) {
         sblk[i] = sp / b_eff;
-        raw[i] = pk[sp];
+        raw[i] = krow_of(sp);
       }
       const uint64_t keep = __ballot(i < p.m && (samp_multi || (sp / b_eff) != tq));
       if (lane == 0) ccount[c / 64] = __popcll(keep);
@@ -191,9 +195,9 @@ __global__ __launch_bounds__(kBNT, 2) void bwd_dq_kernel(BwdParams p) {
   // ---- this lane's query: operands, lse and D
   const int ql = q0 + wave * 32 + col;
   const int qls = ql < qend ? ql : q0;
-  const int orow = pq[qls];
+  const int orow = pq ? pq[qls] : qrow0 + qls;
   const int64_t ridx = static_cast<int64_t>(bh) * p.n + orow;
-  const floatx2 qst = *reinterpret_cast<const floatx2*>(p.qstat + 2 * (static_cast<int64_t>(bh) * p.seg + qls));
+  const floatx2 qst = *reinterpret_cast<const floatx2*>(p.qstat + 2 * ridx);
   const float lse2 = qst[0];
   const float dl = qst[1];
   bf16x8 qf[NQF], gf[NQF];
@@ -225,7 +229,7 @@ __global__ __launch_bounds__(kBNT, 2) void bwd_dq_kernel(BwdParams p) {
 #pragma unroll
     for (int c = 0; c < G::CPT; ++c) {
       const int j = min(j_first + c * JSTEP, kcnt - 1);
-      const int row = isB ? srow[kb + j] : (blist ? brow[kb - ka0 + j] : pk[kb + j]);
+      const int row = isB ? srow[kb + j] : (blist ? brow[kb - ka0 + j] : krow_of(kb + j));
       const uint32_t off = static_cast<uint32_t>(row * D + 8 * c_in_row) * 2;
       kreg[c] = ld16(kbase, off);
       vreg[c] = ld16(vbase, off);
@@ -259,10 +263,11 @@ __global__ __launch_bounds__(kBNT, 2) void bwd_dq_kernel(BwdParams p) {
     const int lo = row_blk * b_eff - kb;
     const bool blk_test = !isB && multi_block;
     const bool smp_test = isB && samp_multi;
+    const bool cau_test = p.causal && kb + kBT - 1 > q0;   // some key of the tile after some query
     auto tile = [&](auto mflag) {
       constexpr bool M = decltype(mflag)::value;
 #pragma unroll
-      for (int kt = 0; kt < 2; ++kt) {
+      for (int kt = 0; kt < kBT / 32; ++kt) {
         bf16x8 ka[NQF], va[NQF];
 #pragma unroll
         for (int c = 0; c < NQF; ++c) {
@@ -294,6 +299,7 @@ __global__ __launch_bounds__(kBNT, 2) void bwd_dq_kernel(BwdParams p) {
             bool ok = j < kcnt;
             if (blk_test) ok &= static_cast<unsigned>(j - lo) < static_cast<unsigned>(b_eff);
             if (smp_test) ok &= sblk[kb + min(j, kcnt - 1)] != row_blk;
+            if (cau_test) ok &= kb + j <= ql;
             x = ok ? x : -INFINITY;
           }
           const float pr = fast_exp2(x);
@@ -310,13 +316,20 @@ __global__ __launch_bounds__(kBNT, 2) void bwd_dq_kernel(BwdParams p) {
         __builtin_amdgcn_sched_barrier(0);
       }
     };
-    if (kcnt < kBT || blk_test || smp_test) tile(Flag<true>());
+    if (kcnt < kBT || blk_test || smp_test || cau_test) tile(Flag<true>());
     else tile(Flag<false>());
   }
 
   // ---- dQ rows (fp32): register r of tile t holds column 32 t + 8 (r / 4) + 4 h2 + r % 4
   if (ql < qend) {
     float* dst = p.dq + ridx * D;
+    floatx4 old[NDT][4];
+    if (p.accumulate) {
+#pragma unroll
+      for (int t = 0; t < NDT; ++t)
+#pragma unroll
+        for (int g = 0; g < 4; ++g) old[t][g] = *reinterpret_cast<const floatx4*>(dst + 32 * t + 8 * g + 4 * h2);
+    }
 #pragma unroll
     for (int t = 0; t < NDT; ++t)
 #pragma unroll
@@ -324,6 +337,7 @@ __global__ __launch_bounds__(kBNT, 2) void bwd_dq_kernel(BwdParams p) {
         floatx4 v4;
 #pragma unroll
         for (int i = 0; i < 4; ++i) v4[i] = acc[t][4 * g + i];
+        if (p.accumulate) v4 += old[t][g];
         *reinterpret_cast<floatx4*>(dst + 32 * t + 8 * g + 4 * h2) = v4;
       }
   }
@@ -335,12 +349,14 @@ __global__ __launch_bounds__(kBNT, 2) void bwd_dq_kernel(BwdParams p) {
 template <int D>
 constexpr int dkv_buf_bytes() { return 2 * BGeo<D>::TB + 2 * kBT * 4; }
 
-// EMASK: per-element block masks, needed when the block size is not a
-// multiple of the 64-row tile.  Otherwise every query tile lies wholly inside
-// or wholly outside a key's block, and the mask is a per-lane, per-tile bias
-// (0 or -inf) folded into the exponent; ragged query rows carry lse = +inf.
-// Lanes past the last key need no mask: their column is never stored.
-template <int D, bool SAMPLE, bool EMASK>
+// MASK 0: every query tile lies wholly inside or wholly outside a key's
+// block (block sizes that are multiples of the 64-row tile), so the block
+// mask is a per-lane, per-tile bias (0 or -inf) folded into the exponent.
+// MASK 1: per-element block masks (other block sizes).  MASK 2: per-element
+// causal mask (exact causal problems, the keys' own query square).  Ragged
+// query rows always carry lse = +inf; lanes past the last key need no mask,
+// their column is never stored.
+template <int D, bool SAMPLE, int MASK>
 __global__ __launch_bounds__(kBNT, 2) void bwd_dkv_kernel(BwdParams p) {
   typedef BGeo<D> G;
   constexpr int NQF = G::NQF, NDT = G::NDT;
@@ -354,19 +370,28 @@ __global__ __launch_bounds__(kBNT, 2) void bwd_dkv_kernel(BwdParams p) {
   const int b_eff = p.b_eff;
   const int G_ = p.H / p.Hkv;
 
-  // ---- work item
+  // ---- work item: key problem (KV head, piece), its keys [k0, kend), the
+  // query problems qprob0 + hh * pieces (hh < nheads) and their queries [qa0, qa1)
   const int lid = xcd_remap(blockIdx.x, gridDim.x);
-  int bkv, bh0, nheads, k0, kend, qa0, qa1, chunk = 0;
+  int bkv, piece, qprob0, nheads, k0, kend, qa0, qa1, chunk = 0, sprob = 0;
   if constexpr (!SAMPLE) {
     const int KT = (p.seg + kBTQ - 1) / kBTQ;
-    bkv = lid / KT;
+    const int kprob = lid / KT;
+    bkv = kprob / p.pieces;
+    piece = kprob - bkv * p.pieces;
     k0 = (lid % KT) * kBTQ;
     kend = min(k0 + kBTQ, p.seg);
     const int b = bkv / p.Hkv;
-    bh0 = b * p.H + (bkv % p.Hkv) * G_;
+    qprob0 = (b * p.H + (bkv % p.Hkv) * G_) * p.pieces + piece;
     nheads = G_;
     qa0 = (k0 / b_eff) * b_eff;
     qa1 = min(((kend - 1) / b_eff + 1) * b_eff, p.seg);
+    if (p.diag == 2) {
+      qa0 = k0;
+      qa1 = min(qa1, k0 + kBTQ);
+    } else if (p.diag == 1) {
+      qa0 = k0 + kBTQ;
+    }
   } else {
     const int NC = (p.seg + p.qchunk - 1) / p.qchunk;
     const int SG = (p.m + kBTQ - 1) / kBTQ;
@@ -374,24 +399,28 @@ __global__ __launch_bounds__(kBNT, 2) void bwd_dkv_kernel(BwdParams p) {
     const int rest = lid / NC;
     k0 = (rest % SG) * kBTQ;
     kend = min(k0 + kBTQ, p.m);
-    bh0 = rest / SG;
-    bkv = (bh0 / p.H) * p.Hkv + (bh0 % p.H) / G_;
+    sprob = rest / SG;                            // bh * pieces + piece
+    const int bh = sprob / p.pieces;
+    piece = sprob - bh * p.pieces;
+    bkv = (bh / p.H) * p.Hkv + (bh % p.H) / G_;
+    qprob0 = sprob;
     nheads = 1;
     qa0 = chunk * p.qchunk;
     qa1 = min(qa0 + p.qchunk, p.seg);
   }
   const bf16* kbase = static_cast<const bf16*>(p.k) + static_cast<int64_t>(bkv) * p.n * D;
   const bf16* vbase = static_cast<const bf16*>(p.v) + static_cast<int64_t>(bkv) * p.n * D;
-  const int32_t* pk = p.perm_k + static_cast<int64_t>(bkv) * p.seg;
+  const int32_t* pk = p.perm_k ? p.perm_k + (static_cast<int64_t>(bkv) * p.pieces + piece) * p.seg : nullptr;
+  const int qrow0 = piece * p.stride + p.q_first;
 
   // ---- this lane's key: operands and block
   const int kj = k0 + wave * 32 + col;           // key position (block) or sample slot (sample)
   const bool kvalid = kj < kend;
   const int kjs = kvalid ? kj : k0;
   int kpos;                                      // sorted key position
-  if constexpr (SAMPLE) kpos = p.sidx[static_cast<int64_t>(bh0) * p.m + kjs];
+  if constexpr (SAMPLE) kpos = p.sidx[static_cast<int64_t>(sprob) * p.m + kjs];
   else kpos = kjs;
-  const int krow = pk[kpos];
+  const int krow = pk ? pk[kpos] : piece * p.stride + p.k_first + kpos;
   const int kblk = kpos / b_eff;
   bf16x8 kf[NQF], vf[NQF];
 #pragma unroll
@@ -418,22 +447,28 @@ __global__ __launch_bounds__(kBNT, 2) void bwd_dkv_kernel(BwdParams p) {
   constexpr int JSTEP = kBNT / G::CPR;
   uint4v qreg[G::CPT], greg[G::CPT];
   int prow[G::CPT];
-  floatx2 sreg = {0.f, 0.f};
-  auto tile_rows = [&](int it, int& tq0, int& qcnt, int& bh) {
+  floatx2 sreg[G::CPT];
+  auto tile_rows = [&](int it, int& tq0, int& qcnt, int& qprob) {
     tq0 = qa0 + (it % qtiles) * kBT;
     qcnt = min(kBT, qa1 - tq0);
-    bh = bh0 + it / qtiles;
+    qprob = qprob0 + (it / qtiles) * p.pieces;
   };
   auto fetch_perm = [&](int it) {
-    int tq0, qcnt, bh;
-    tile_rows(it, tq0, qcnt, bh);
-    const int32_t* pq = p.perm_q + static_cast<int64_t>(bh) * p.seg;
+    int tq0, qcnt, qprob;
+    tile_rows(it, tq0, qcnt, qprob);
+    const int32_t* pq = p.perm_q ? p.perm_q + static_cast<int64_t>(qprob) * p.seg : nullptr;
 #pragma unroll
-    for (int c = 0; c < G::CPT; ++c) prow[c] = pq[tq0 + min(j_first + c * JSTEP, qcnt - 1)];
+    for (int c = 0; c < G::CPT; ++c) {
+      const int t = tq0 + min(j_first + c * JSTEP, qcnt - 1);
+      prow[c] = pq ? pq[t] : qrow0 + t;
+    }
   };
+  // rows of Q and dO; the row's statistics are loaded by the thread that
+  // stages the row's first 16 bytes (rows past the tile carry lse = +inf: P = 0)
   auto load_tile = [&](int it) {
-    int tq0, qcnt, bh;
-    tile_rows(it, tq0, qcnt, bh);
+    int tq0, qcnt, qprob;
+    tile_rows(it, tq0, qcnt, qprob);
+    const int bh = qprob / p.pieces;
     const bf16* qb = static_cast<const bf16*>(p.q) + static_cast<int64_t>(bh) * p.n * D;
     const bf16* gb = static_cast<const bf16*>(p.dout) + static_cast<int64_t>(bh) * p.n * D;
 #pragma unroll
@@ -441,11 +476,10 @@ __global__ __launch_bounds__(kBNT, 2) void bwd_dkv_kernel(BwdParams p) {
       const uint32_t off = static_cast<uint32_t>(prow[c] * D + 8 * c_in_row) * 2;
       qreg[c] = ld16(qb, off);
       greg[c] = ld16(gb, off);
-    }
-    if (tid < kBT) {
-      sreg = *reinterpret_cast<const floatx2*>(p.qstat + 2 * (static_cast<int64_t>(bh) * p.seg + tq0 +
-                                                               min(tid, qcnt - 1)));
-      if (tid >= qcnt) sreg[0] = INFINITY;      // ragged row: P = 0
+      if (c_in_row == 0) {
+        sreg[c] = *reinterpret_cast<const floatx2*>(p.qstat + 2 * (static_cast<int64_t>(bh) * p.n + prow[c]));
+        if (j_first + c * JSTEP >= qcnt) sreg[c][0] = INFINITY;
+      }
     }
   };
   auto store_tile = [&](int buf) {
@@ -458,10 +492,10 @@ __global__ __launch_bounds__(kBNT, 2) void bwd_dkv_kernel(BwdParams p) {
       const int j = j_first + c * JSTEP;
       *reinterpret_cast<uint4v*>(&qs[j * G::STR + 8 * c_in_row]) = qreg[c];
       *reinterpret_cast<uint4v*>(&gs[j * G::STR + 8 * c_in_row]) = greg[c];
-    }
-    if (tid < kBT) {
-      ls[tid] = sreg[0];
-      ls[kBT + tid] = sreg[1];
+      if (c_in_row == 0) {
+        ls[j] = sreg[c][0];
+        ls[kBT + j] = sreg[c][1];
+      }
     }
   };
 
@@ -478,8 +512,8 @@ __global__ __launch_bounds__(kBNT, 2) void bwd_dkv_kernel(BwdParams p) {
       load_tile(it + 1);
       if (it + 2 < ntiles) fetch_perm(it + 2);
     }
-    int tq0, qcnt, bh_unused;
-    tile_rows(it, tq0, qcnt, bh_unused);
+    int tq0, qcnt, qprob_unused;
+    tile_rows(it, tq0, qcnt, qprob_unused);
     const char* base = smem + buf * BUF;
     const bf16* qs = reinterpret_cast<const bf16*>(base);
     const bf16* gs = reinterpret_cast<const bf16*>(base + G::TB);
@@ -487,13 +521,13 @@ __global__ __launch_bounds__(kBNT, 2) void bwd_dkv_kernel(BwdParams p) {
     // query j of the tile lies in this lane's key block iff (unsigned)(j - lo) < b_eff
     const int lo = kblk * b_eff - tq0;
     float bias = wbias;
-    if constexpr (!EMASK) {
+    if constexpr (MASK == 0) {
       const bool tin = static_cast<unsigned>(-lo) < static_cast<unsigned>(b_eff);
       if (SAMPLE ? tin : !tin) bias = -INFINITY;
     }
     {
 #pragma unroll
-      for (int qt = 0; qt < 2; ++qt) {
+      for (int qt = 0; qt < kBT / 32; ++qt) {
         bf16x8 qa[NQF], ga[NQF];
 #pragma unroll
         for (int c = 0; c < NQF; ++c) {
@@ -528,9 +562,11 @@ __global__ __launch_bounds__(kBNT, 2) void bwd_dkv_kernel(BwdParams p) {
           for (int i = 0; i < 4; ++i) {
             const int r = 4 * g + i;
             float x = fmaf(s[r], kLog2e, bias - l4[i]);
-            if constexpr (EMASK) {
+            if constexpr (MASK == 1) {
               const bool in_blk = static_cast<unsigned>(j0 + i - lo) < static_cast<unsigned>(b_eff);
               x = (SAMPLE ? !in_blk : in_blk) ? x : -INFINITY;
+            } else if constexpr (MASK == 2) {
+              x = j0 + i >= kpos - tq0 ? x : -INFINITY;   // query position >= key position
             }
             const float pr = fast_exp2(x);
             const bf16 pv = static_cast<bf16>(pr);
@@ -563,12 +599,24 @@ __global__ __launch_bounds__(kBNT, 2) void bwd_dkv_kernel(BwdParams p) {
   if (kvalid) {
     float* dkr;
     float* dvr;
+    bool add = false;
     if constexpr (SAMPLE) {
-      dkr = p.part + ((static_cast<int64_t>(chunk) * p.BH + bh0) * p.m + kj) * (2 * D);
+      dkr = p.part + ((static_cast<int64_t>(chunk) * p.BH * p.pieces + sprob) * p.m + kj) * (2 * D);
       dvr = dkr + D;
     } else {
       dkr = p.dk + (static_cast<int64_t>(bkv) * p.n + krow) * D;
       dvr = p.dv + (static_cast<int64_t>(bkv) * p.n + krow) * D;
+      add = p.accumulate;
+    }
+    floatx4 ok_[NDT][4], ov_[NDT][4];
+    if (add) {
+#pragma unroll
+      for (int t = 0; t < NDT; ++t)
+#pragma unroll
+        for (int g = 0; g < 4; ++g) {
+          ok_[t][g] = *reinterpret_cast<const floatx4*>(dkr + 32 * t + 8 * g + 4 * h2);
+          ov_[t][g] = *reinterpret_cast<const floatx4*>(dvr + 32 * t + 8 * g + 4 * h2);
+        }
     }
 #pragma unroll
     for (int t = 0; t < NDT; ++t)
@@ -580,6 +628,10 @@ __global__ __launch_bounds__(kBNT, 2) void bwd_dkv_kernel(BwdParams p) {
         for (int i = 0; i < 4; ++i) {
           a[i] = dk[t][4 * g + i];
           c[i] = dv[t][4 * g + i];
+        }
+        if (add) {
+          a += ok_[t][g];
+          c += ov_[t][g];
         }
         *reinterpret_cast<floatx4*>(dkr + c0) = a;
         *reinterpret_cast<floatx4*>(dvr + c0) = c;
@@ -595,10 +647,10 @@ template <int D>
 __global__ __launch_bounds__(256) void bwd_dkv_reduce_kernel(BwdParams p, int nchunk) {
   constexpr int TPR = 2 * D / 4;                    // threads per slot row
   const int64_t t = static_cast<int64_t>(blockIdx.x) * 256 + threadIdx.x;
-  const int64_t row = t / TPR;                      // bh * m + slot
-  if (row >= static_cast<int64_t>(p.BH) * p.m) return;
+  const int64_t row = t / TPR;                      // (bh * pieces + piece) * m + slot
+  if (row >= static_cast<int64_t>(p.BH) * p.pieces * p.m) return;
   const int c = static_cast<int>(t % TPR) * 4;
-  const int64_t cstride = static_cast<int64_t>(p.BH) * p.m * (2 * D);
+  const int64_t cstride = static_cast<int64_t>(p.BH) * p.pieces * p.m * (2 * D);
   const float* src = p.part + row * (2 * D) + c;
   floatx4 acc = {0.f, 0.f, 0.f, 0.f};
   int ch = 0;
@@ -610,10 +662,12 @@ __global__ __launch_bounds__(256) void bwd_dkv_reduce_kernel(BwdParams p, int nc
     for (int u = 0; u < 4; ++u) acc += x[u];
   }
   for (; ch < nchunk; ++ch) acc += *reinterpret_cast<const floatx4*>(src + ch * cstride);
-  const int bh = static_cast<int>(row / p.m);
+  const int prob = static_cast<int>(row / p.m);
+  const int bh = prob / p.pieces;
+  const int piece = prob - bh * p.pieces;
   const int bkv = (bh / p.H) * p.Hkv + (bh % p.H) / (p.H / p.Hkv);
   const int kpos = p.sidx[row];
-  const int krow = p.perm_k[static_cast<int64_t>(bkv) * p.seg + kpos];
+  const int krow = p.perm_k[(static_cast<int64_t>(bkv) * p.pieces + piece) * p.seg + kpos];
   float* dst = (c < D ? p.dk : p.dv) + (static_cast<int64_t>(bkv) * p.n + krow) * D + (c < D ? c : c - D);
 #pragma unroll
   for (int i = 0; i < 4; ++i) unsafeAtomicAdd(dst + i, acc[i]);
@@ -629,7 +683,7 @@ static int launch_dq_d(const BwdParams& p, hipStream_t s) {
   const int64_t cap = span < p.seg ? span : p.seg;
   if (cap <= kBlockListCap) q.bcap = static_cast<int>(cap);
   const size_t lds = 4 * BGeo<D>::TB + dq_list_bytes(q.bcap, p.m);
-  const int64_t blocks = static_cast<int64_t>(p.BH) * ((p.seg + kBTQ - 1) / kBTQ);
+  const int64_t blocks = static_cast<int64_t>(p.BH) * p.pieces * ((p.seg + kBTQ - 1) / kBTQ);
   auto fn = bwd_dq_kernel<D>;
   static bool attr = false;
   if (!attr) {
@@ -654,20 +708,20 @@ int launch_bwd_dq(const BwdParams& p, hipStream_t s) {
   return after_launch("backward dq", s);
 }
 
-template <int D, bool SAMPLE, bool EMASK>
+template <int D, bool SAMPLE, int MASK>
 static int launch_dkv_d2(const BwdParams& p, hipStream_t s) {
   int64_t blocks;
   const int nchunk = (p.seg + p.qchunk - 1) / p.qchunk;
   if constexpr (SAMPLE) {
-    blocks = static_cast<int64_t>(p.BH) * ((p.m + kBTQ - 1) / kBTQ) * nchunk;
+    blocks = static_cast<int64_t>(p.BH) * p.pieces * ((p.m + kBTQ - 1) / kBTQ) * nchunk;
   } else {
-    blocks = static_cast<int64_t>(p.BH / (p.H / p.Hkv)) * ((p.seg + kBTQ - 1) / kBTQ);
+    blocks = static_cast<int64_t>(p.BH / (p.H / p.Hkv)) * p.pieces * ((p.seg + kBTQ - 1) / kBTQ);
   }
   if (blocks == 0) return HA_OK;
   const size_t lds = 2 * dkv_buf_bytes<D>();
-  hipLaunchKernelGGL((bwd_dkv_kernel<D, SAMPLE, EMASK>), dim3(static_cast<unsigned>(blocks)), dim3(kBNT), lds, s, p);
+  hipLaunchKernelGGL((bwd_dkv_kernel<D, SAMPLE, MASK>), dim3(static_cast<unsigned>(blocks)), dim3(kBNT), lds, s, p);
   if constexpr (SAMPLE) {
-    const int64_t threads = static_cast<int64_t>(p.BH) * p.m * (2 * D / 4);
+    const int64_t threads = static_cast<int64_t>(p.BH) * p.pieces * p.m * (2 * D / 4);
     hipLaunchKernelGGL((bwd_dkv_reduce_kernel<D>), dim3(static_cast<unsigned>((threads + 255) / 256)), dim3(256), 0,
                        s, p, nchunk);
   }
@@ -676,14 +730,19 @@ static int launch_dkv_d2(const BwdParams& p, hipStream_t s) {
 
 template <int D, bool SAMPLE>
 static int launch_dkv_d(const BwdParams& p, hipStream_t s) {
-  if (p.b_eff % kBT) return launch_dkv_d2<D, SAMPLE, true>(p, s);
-  return launch_dkv_d2<D, SAMPLE, false>(p, s);
+  if (!SAMPLE && p.causal && p.diag == 2) return launch_dkv_d2<D, false, 2>(p, s);
+  if (p.b_eff % kBT) return launch_dkv_d2<D, SAMPLE, 1>(p, s);
+  return launch_dkv_d2<D, SAMPLE, 0>(p, s);
 }
 
 int launch_bwd_dkv(const BwdParams& p, bool samples, hipStream_t s) {
   if (p.seg == 0 || p.BH == 0 || (samples && p.m == 0)) return HA_OK;
-  if (samples && (!p.part || p.qchunk < kBT || p.qchunk % kBT)) {
-    set_error("backward dk/dv: bad sample partial buffer or query chunk");
+  if (samples && (!p.part || !p.perm_k || p.qchunk < kBT || p.qchunk % kBT)) {
+    set_error("backward dk/dv: bad sample partial buffer, permutation or query chunk");
+    return HA_EINVAL;
+  }
+  if (p.causal && (samples || (p.diag != 1 && p.diag != 2))) {
+    set_error("backward dk/dv: causal problems take no samples and need a diagonal part");
     return HA_EINVAL;
   }
   timing_begin(HA_K_BWD_DKV, s);

@@ -90,21 +90,31 @@ struct BwdParams {
   const void* out = nullptr;         // forward output [BH][n][d]
   const void* dout = nullptr;        // upstream gradient [BH][n][d]
   const float* lse = nullptr;        // forward lse [BH][n] (natural log)
-  float* qstat = nullptr;            // per sorted query: (lse log2 e, rowsum(dout * out)) [BH][seg][2]
+  float* qstat = nullptr;            // per row: (lse log2 e, rowsum(dout * out)) [BH][n][2]
   int d = 64;
   int n = 0;
   int H = 1, Hkv = 1;
   int BH = 0;
-  int seg = 0;                       // queries = keys of the (single) problem
-  const int32_t* perm_q = nullptr;   // [BH][seg]
-  const int32_t* perm_k = nullptr;   // [BHkv][seg]
-  const int32_t* sidx = nullptr;     // [BH][m]
+  // Problems: piece p of every head has queries at rows p * stride + q_first + t
+  // and keys at rows p * stride + k_first + t (t < seg), in sorted order
+  // through perm_q / perm_k ([heads][pieces][seg], rows within the head) or in
+  // row order when a permutation is null.
+  int pieces = 1;
+  int seg = 0;
+  int stride = 0;
+  int q_first = 0, k_first = 0;
+  const int32_t* perm_q = nullptr;
+  const int32_t* perm_k = nullptr;
+  const int32_t* sidx = nullptr;     // [BH][pieces][m] sorted key positions
   int m = 0;
   float log2w = 0.f;                 // log2(seg / m)
   int b_eff = 1;
+  int causal = 0;                    // exact causal problem: key position <= query position
+  int diag = 0;                      // causal dK/dV: 2 = the keys' own 256-query square, 1 = the queries after it
+  int accumulate = 0;                // add to dq / dk / dv instead of storing
   int bcap = 0;                      // LDS block key list capacity (launcher)
   int qchunk = 2048;                 // queries per sample-key workgroup (bwd_query_chunk)
-  float* part = nullptr;             // sample-key partials [ceil(seg / qchunk)][BH][m][2 d] fp32
+  float* part = nullptr;             // sample-key partials [ceil(seg / qchunk)][BH][pieces][m][2 d] fp32
   float* dq = nullptr;               // [BH][n][d] fp32
   float* dk = nullptr;               // [BHkv][n][d] fp32
   float* dv = nullptr;

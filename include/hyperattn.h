@@ -141,7 +141,9 @@ int hyperattn_forward_ex(const void* q, const void* k, const void* v, int dtype,
  * and backward; the pages print no backward formulas).  For the ranks and
  * samples the forward draws (recomputed here from the same seed) the
  * forward is a softmax with fixed key multiplicities W -- 1 inside the
- * query's block of the sorted matrix, n / samples per kept sample -- so
+ * query's block of the sorted matrix, seg / samples per kept sample, and for
+ * causal calls the exact leaves' lower triangles plus every level's quadrant
+ * weights (the log-sum-exp merge of the parts is the joint softmax) -- so
  * with P = W * exp(Q K^T - lse), D = rowsum(dout * out) and
  * dS = P * (dout V^T - D) the gradients are dQ = dS K, dK = dS^T Q,
  * dV = P^T dout (dK, dV of a KV head summed over its query heads).
@@ -167,8 +169,9 @@ size_t hyperattn_backward_workspace_bytes(int batch, int n, int d, int heads, in
  *   stream     hipStream_t or NULL; asynchronous on it
  * The sample part of dK and dV is accumulated with fp32 atomic adds, so
  * their last bits may vary from run to run; dQ is deterministic.
- * Errors: as hyperattn_forward; HA_EUNSUPPORTED for causal problems (not
- * built yet) and for fp32 inputs.
+ * Causal calls run the exact leaves first (dq, dk, dv stored), then every
+ * level's quadrant problems (added).
+ * Errors: as hyperattn_forward; HA_EUNSUPPORTED for fp32 inputs.
  */
 int hyperattn_backward(const void* q, const void* k, const void* v, const void* out,
                        const float* lse, const void* dout, int dtype,

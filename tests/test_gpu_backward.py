@@ -1,4 +1,4 @@
-"""GPU parity of the backward (non-causal, bf16) against the fp64 oracle.
+"""GPU parity of the backward (bf16, non-causal and causal) against the fp64 oracle.
 
 The library's forward gives (out, lse); its backward then gives dq, dk, dv
 in fp32, compared with ``oracle.backward.backward`` on the same bf16 inputs
@@ -61,19 +61,37 @@ CASES = [
 ]
 
 
-@pytest.mark.parametrize("B,H,Hkv,n,d,block,m,r,seed", CASES)
-def test_backward_matches_oracle(B, H, Hkv, n, d, block, m, r, seed):
+CAUSAL_CASES = [
+    # B, H, Hkv, n, d, block, samples, r, min_seq_len, seed
+    (1, 2, 1, 1024, 64, 64, 32, 6, 256, 21),      # two levels, 256-row leaves, grouped heads
+    (1, 2, 2, 1000, 128, 25, 20, 6, 128, 22),     # 125-row leaves, blocks not a multiple of 64
+    (1, 4, 2, 2048, 64, 128, 64, 7, 512, 23),     # grouped heads, leaves of two workgroups
+    (1, 2, 1, 512, 64, 64, 16, 5, 512, 24),       # leaf only (no quadrant level)
+    (2, 2, 2, 2048, 128, 256, 128, 7, 256, 25),   # d = 128, three levels, batch 2
+]
+
+
+def _run(B, H, Hkv, n, d, seed, **args):
     q, k, v, do = _inputs(B, H, Hkv, n, d, 100 + seed)
-    args = dict(block=block, samples=m, proj_bits=r, seed=seed)
     qd, kd, vd, dod = q.to(DEV), k.to(DEV), v.to(DEV), do.to(DEV)
-    out, lse = ha.forward(qd, kd, vd, **args)
-    dq, dk, dv = ha.backward(qd, kd, vd, out, lse, dod, **args)
+    out, lse = ha.forward(qd, kd, vd, seed=seed, **args)
+    dq, dk, dv = ha.backward(qd, kd, vd, out, lse, dod, seed=seed, **args)
     torch.cuda.synchronize()
-    cfg = HAConfig(block=block, samples=m, proj_bits=r, seed=seed)
+    cfg = HAConfig(seed=seed, **args)
     rq, rk, rv = ob.backward(np32(q), np32(k), np32(v), np32(do), cfg)
     _compare(dq.cpu().numpy(), rq, "dq")
     _compare(dk.cpu().numpy(), rk, "dk")
     _compare(dv.cpu().numpy(), rv, "dv")
+
+
+@pytest.mark.parametrize("B,H,Hkv,n,d,block,m,r,seed", CASES)
+def test_backward_matches_oracle(B, H, Hkv, n, d, block, m, r, seed):
+    _run(B, H, Hkv, n, d, seed, block=block, samples=m, proj_bits=r)
+
+
+@pytest.mark.parametrize("B,H,Hkv,n,d,block,m,r,s,seed", CAUSAL_CASES)
+def test_causal_backward_matches_oracle(B, H, Hkv, n, d, block, m, r, s, seed):
+    _run(B, H, Hkv, n, d, seed, block=block, samples=m, proj_bits=r, causal=True, min_seq_len=s)
 
 
 def test_backward_dq_deterministic():
@@ -86,11 +104,15 @@ def test_backward_dq_deterministic():
     assert torch.equal(a[0], b[0])
 
 
-def test_backward_rejects_what_is_not_built():
-    q, k, v, do = _inputs(1, 1, 1, 256, 64, 12)
-    qd, kd, vd, dod = q.to(DEV), k.to(DEV), v.to(DEV), do.to(DEV)
-    out, lse = ha.forward(qd, kd, vd, block=64, samples=16, proj_bits=5, causal=True, min_seq_len=64)
+def test_backward_rejects_fp32():
+    """The C entry point answers fp32 inputs with HA_EUNSUPPORTED before any launch."""
+    import ctypes
+    q, k, v, do = (t.float().to(DEV) for t in _inputs(1, 1, 1, 256, 64, 12))
+    out, lse = ha.forward(q, k, v, block=64, samples=16, proj_bits=5)
+    dq, dk, dv = (torch.empty_like(t) for t in (q, k, v))
+    ws = torch.empty(1 << 20, dtype=torch.uint8, device=DEV)
     with pytest.raises(ha.HyperAttnError) as e:
-        ha.backward(qd, kd, vd, out, lse, dod, block=64, samples=16, proj_bits=5, causal=True,
-                    min_seq_len=64)
+        ha._call("hyperattn_backward", ha._ptr(q), ha._ptr(k), ha._ptr(v), ha._ptr(out), ha._ptr(lse),
+                 ha._ptr(do), ha.HA_F32, 1, 256, 64, 1, 1, 64, 16, 5, 0, 0, ctypes.c_uint64(0),
+                 ha._ptr(dq), ha._ptr(dk), ha._ptr(dv), ha._ptr(ws), ws.numel(), ha._stream(q.device))
     assert e.value.code == ha.HA_EUNSUPPORTED
