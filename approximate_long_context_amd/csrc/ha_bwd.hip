@@ -111,7 +111,9 @@ int launch_bwd_qstat(const BwdParams& p, hipStream_t s) {
 // one count per 64 samples.
 static int dq_list_bytes(int bcap, int m) { return 4 * (bcap + 3 * m + (m + 63) / 64); }
 
-template <int D>
+// IDENT: the problem's rows are in row order (exact causal leaves); the
+// permutations are not read.
+template <int D, bool IDENT>
 __global__ __launch_bounds__(kBNT, 2) void bwd_dq_kernel(BwdParams p) {
   typedef BGeo<D> G;
   constexpr int NQF = G::NQF, NDT = G::NDT;
@@ -138,11 +140,11 @@ __global__ __launch_bounds__(kBNT, 2) void bwd_dq_kernel(BwdParams p) {
   const bf16* gb = static_cast<const bf16*>(p.dout) + static_cast<int64_t>(bh) * p.n * D;
   const bf16* kbase = static_cast<const bf16*>(p.k) + static_cast<int64_t>(bkv) * p.n * D;
   const bf16* vbase = static_cast<const bf16*>(p.v) + static_cast<int64_t>(bkv) * p.n * D;
-  const int32_t* pq = p.perm_q ? p.perm_q + static_cast<int64_t>(prob) * p.seg : nullptr;
-  const int32_t* pk = p.perm_k ? p.perm_k + (static_cast<int64_t>(bkv) * p.pieces + piece) * p.seg : nullptr;
+  const int32_t* pq = IDENT ? nullptr : p.perm_q + static_cast<int64_t>(prob) * p.seg;
+  const int32_t* pk = IDENT ? nullptr : p.perm_k + (static_cast<int64_t>(bkv) * p.pieces + piece) * p.seg;
   const int qrow0 = piece * p.stride + p.q_first;
   const int krow0 = piece * p.stride + p.k_first;
-  auto krow_of = [&](int t) { return pk ? pk[t] : krow0 + t; };
+  auto krow_of = [&](int t) { return IDENT ? krow0 + t : pk[t]; };
 
   const int ka0 = (q0 / b_eff) * b_eff;
   int ka1 = min(((qend - 1) / b_eff + 1) * b_eff, p.seg);
@@ -158,7 +160,7 @@ __global__ __launch_bounds__(kBNT, 2) void bwd_dq_kernel(BwdParams p) {
   int* sblk = srow + p.m;                         // block of each sample's sorted position
   int* rrow = sblk + p.m;
   int* ccount = rrow + p.m;
-  const bool blist = p.bcap > 0;
+  const bool blist = !IDENT && p.bcap > 0;
   int nsamp = 0;
   if (blist)
     for (int j = tid; j < nbl; j += kBNT) brow[j] = krow_of(ka0 + j);
@@ -195,7 +197,7 @@ __global__ __launch_bounds__(kBNT, 2) void bwd_dq_kernel(BwdParams p) {
   // ---- this lane's query: operands, lse and D
   const int ql = q0 + wave * 32 + col;
   const int qls = ql < qend ? ql : q0;
-  const int orow = pq ? pq[qls] : qrow0 + qls;
+  const int orow = IDENT ? qrow0 + qls : pq[qls];
   const int64_t ridx = static_cast<int64_t>(bh) * p.n + orow;
   const floatx2 qst = *reinterpret_cast<const floatx2*>(p.qstat + 2 * ridx);
   const float lse2 = qst[0];
@@ -356,7 +358,7 @@ constexpr int dkv_buf_bytes() { return 2 * BGeo<D>::TB + 2 * kBT * 4; }
 // causal mask (exact causal problems, the keys' own query square).  Ragged
 // query rows always carry lse = +inf; lanes past the last key need no mask,
 // their column is never stored.
-template <int D, bool SAMPLE, int MASK>
+template <int D, bool SAMPLE, int MASK, bool IDENT>
 __global__ __launch_bounds__(kBNT, 2) void bwd_dkv_kernel(BwdParams p) {
   typedef BGeo<D> G;
   constexpr int NQF = G::NQF, NDT = G::NDT;
@@ -410,7 +412,7 @@ __global__ __launch_bounds__(kBNT, 2) void bwd_dkv_kernel(BwdParams p) {
   }
   const bf16* kbase = static_cast<const bf16*>(p.k) + static_cast<int64_t>(bkv) * p.n * D;
   const bf16* vbase = static_cast<const bf16*>(p.v) + static_cast<int64_t>(bkv) * p.n * D;
-  const int32_t* pk = p.perm_k ? p.perm_k + (static_cast<int64_t>(bkv) * p.pieces + piece) * p.seg : nullptr;
+  const int32_t* pk = IDENT ? nullptr : p.perm_k + (static_cast<int64_t>(bkv) * p.pieces + piece) * p.seg;
   const int qrow0 = piece * p.stride + p.q_first;
 
   // ---- this lane's key: operands and block
@@ -420,7 +422,7 @@ __global__ __launch_bounds__(kBNT, 2) void bwd_dkv_kernel(BwdParams p) {
   int kpos;                                      // sorted key position
   if constexpr (SAMPLE) kpos = p.sidx[static_cast<int64_t>(sprob) * p.m + kjs];
   else kpos = kjs;
-  const int krow = pk ? pk[kpos] : piece * p.stride + p.k_first + kpos;
+  const int krow = IDENT ? piece * p.stride + p.k_first + kpos : pk[kpos];
   const int kblk = kpos / b_eff;
   bf16x8 kf[NQF], vf[NQF];
 #pragma unroll
@@ -448,6 +450,7 @@ __global__ __launch_bounds__(kBNT, 2) void bwd_dkv_kernel(BwdParams p) {
   uint4v qreg[G::CPT], greg[G::CPT];
   int prow[G::CPT];
   floatx2 sreg[G::CPT];
+  bool sval[G::CPT];
   auto tile_rows = [&](int it, int& tq0, int& qcnt, int& qprob) {
     tq0 = qa0 + (it % qtiles) * kBT;
     qcnt = min(kBT, qa1 - tq0);
@@ -456,15 +459,15 @@ __global__ __launch_bounds__(kBNT, 2) void bwd_dkv_kernel(BwdParams p) {
   auto fetch_perm = [&](int it) {
     int tq0, qcnt, qprob;
     tile_rows(it, tq0, qcnt, qprob);
-    const int32_t* pq = p.perm_q ? p.perm_q + static_cast<int64_t>(qprob) * p.seg : nullptr;
 #pragma unroll
     for (int c = 0; c < G::CPT; ++c) {
       const int t = tq0 + min(j_first + c * JSTEP, qcnt - 1);
-      prow[c] = pq ? pq[t] : qrow0 + t;
+      prow[c] = IDENT ? qrow0 + t : p.perm_q[static_cast<int64_t>(qprob) * p.seg + t];
     }
   };
-  // rows of Q and dO; the row's statistics are loaded by the thread that
-  // stages the row's first 16 bytes (rows past the tile carry lse = +inf: P = 0)
+  // rows of Q and dO and the rows' statistics (every thread loads its row's;
+  // rows past the tile carry lse = +inf: P = 0).  No load is conditional, so
+  // none forces a wait where control flow joins.
   auto load_tile = [&](int it) {
     int tq0, qcnt, qprob;
     tile_rows(it, tq0, qcnt, qprob);
@@ -476,10 +479,8 @@ __global__ __launch_bounds__(kBNT, 2) void bwd_dkv_kernel(BwdParams p) {
       const uint32_t off = static_cast<uint32_t>(prow[c] * D + 8 * c_in_row) * 2;
       qreg[c] = ld16(qb, off);
       greg[c] = ld16(gb, off);
-      if (c_in_row == 0) {
-        sreg[c] = *reinterpret_cast<const floatx2*>(p.qstat + 2 * (static_cast<int64_t>(bh) * p.n + prow[c]));
-        if (j_first + c * JSTEP >= qcnt) sreg[c][0] = INFINITY;
-      }
+      sreg[c] = *reinterpret_cast<const floatx2*>(p.qstat + 2 * (static_cast<int64_t>(bh) * p.n + prow[c]));
+      sval[c] = j_first + c * JSTEP < qcnt;     // applied at the store, not here: no wait on the load
     }
   };
   auto store_tile = [&](int buf) {
@@ -493,7 +494,7 @@ __global__ __launch_bounds__(kBNT, 2) void bwd_dkv_kernel(BwdParams p) {
       *reinterpret_cast<uint4v*>(&qs[j * G::STR + 8 * c_in_row]) = qreg[c];
       *reinterpret_cast<uint4v*>(&gs[j * G::STR + 8 * c_in_row]) = greg[c];
       if (c_in_row == 0) {
-        ls[j] = sreg[c][0];
+        ls[j] = sval[c] ? sreg[c][0] : INFINITY;
         ls[kBT + j] = sreg[c][1];
       }
     }
@@ -675,7 +676,7 @@ __global__ __launch_bounds__(256) void bwd_dkv_reduce_kernel(BwdParams p, int nc
 
 // ---- launches ---------------------------------------------------------------------------
 
-template <int D>
+template <int D, bool IDENT>
 static int launch_dq_d(const BwdParams& p, hipStream_t s) {
   BwdParams q = p;
   q.bcap = 0;
@@ -684,7 +685,7 @@ static int launch_dq_d(const BwdParams& p, hipStream_t s) {
   if (cap <= kBlockListCap) q.bcap = static_cast<int>(cap);
   const size_t lds = 4 * BGeo<D>::TB + dq_list_bytes(q.bcap, p.m);
   const int64_t blocks = static_cast<int64_t>(p.BH) * p.pieces * ((p.seg + kBTQ - 1) / kBTQ);
-  auto fn = bwd_dq_kernel<D>;
+  auto fn = bwd_dq_kernel<D, IDENT>;
   static bool attr = false;
   if (!attr) {
     HA_CHECK_HIP(hipFuncSetAttribute(reinterpret_cast<const void*>(fn), hipFuncAttributeMaxDynamicSharedMemorySize,
@@ -702,13 +703,19 @@ int launch_bwd_dq(const BwdParams& p, hipStream_t s) {
     return HA_EUNSUPPORTED;
   }
   timing_begin(HA_K_BWD_DQ, s);
-  const int st = p.d == 64 ? launch_dq_d<64>(p, s) : launch_dq_d<128>(p, s);
+  if (!p.perm_q != !p.perm_k || (!p.perm_q && p.m > 0)) {
+    set_error("backward dq: both permutations or neither; samples need them");
+    return HA_EINVAL;
+  }
+  int st;
+  if (p.perm_q) st = p.d == 64 ? launch_dq_d<64, false>(p, s) : launch_dq_d<128, false>(p, s);
+  else st = p.d == 64 ? launch_dq_d<64, true>(p, s) : launch_dq_d<128, true>(p, s);
   timing_end(HA_K_BWD_DQ, s);
   if (st != HA_OK) return st;
   return after_launch("backward dq", s);
 }
 
-template <int D, bool SAMPLE, int MASK>
+template <int D, bool SAMPLE, int MASK, bool IDENT>
 static int launch_dkv_d2(const BwdParams& p, hipStream_t s) {
   int64_t blocks;
   const int nchunk = (p.seg + p.qchunk - 1) / p.qchunk;
@@ -719,7 +726,8 @@ static int launch_dkv_d2(const BwdParams& p, hipStream_t s) {
   }
   if (blocks == 0) return HA_OK;
   const size_t lds = 2 * dkv_buf_bytes<D>();
-  hipLaunchKernelGGL((bwd_dkv_kernel<D, SAMPLE, MASK>), dim3(static_cast<unsigned>(blocks)), dim3(kBNT), lds, s, p);
+  hipLaunchKernelGGL((bwd_dkv_kernel<D, SAMPLE, MASK, IDENT>), dim3(static_cast<unsigned>(blocks)), dim3(kBNT), lds,
+                     s, p);
   if constexpr (SAMPLE) {
     const int64_t threads = static_cast<int64_t>(p.BH) * p.pieces * p.m * (2 * D / 4);
     hipLaunchKernelGGL((bwd_dkv_reduce_kernel<D>), dim3(static_cast<unsigned>((threads + 255) / 256)), dim3(256), 0,
@@ -730,9 +738,18 @@ static int launch_dkv_d2(const BwdParams& p, hipStream_t s) {
 
 template <int D, bool SAMPLE>
 static int launch_dkv_d(const BwdParams& p, hipStream_t s) {
-  if (!SAMPLE && p.causal && p.diag == 2) return launch_dkv_d2<D, false, 2>(p, s);
-  if (p.b_eff % kBT) return launch_dkv_d2<D, SAMPLE, 1>(p, s);
-  return launch_dkv_d2<D, SAMPLE, 0>(p, s);
+  if constexpr (SAMPLE) {
+    if (p.b_eff % kBT) return launch_dkv_d2<D, true, 1, false>(p, s);
+    return launch_dkv_d2<D, true, 0, false>(p, s);
+  } else {
+    if (!p.perm_q) {                               // exact causal leaves
+      if (p.diag == 2) return launch_dkv_d2<D, false, 2, true>(p, s);
+      if (p.b_eff % kBT) return launch_dkv_d2<D, false, 1, true>(p, s);
+      return launch_dkv_d2<D, false, 0, true>(p, s);
+    }
+    if (p.b_eff % kBT) return launch_dkv_d2<D, false, 1, false>(p, s);
+    return launch_dkv_d2<D, false, 0, false>(p, s);
+  }
 }
 
 int launch_bwd_dkv(const BwdParams& p, bool samples, hipStream_t s) {
@@ -743,6 +760,10 @@ int launch_bwd_dkv(const BwdParams& p, bool samples, hipStream_t s) {
   }
   if (p.causal && (samples || (p.diag != 1 && p.diag != 2))) {
     set_error("backward dk/dv: causal problems take no samples and need a diagonal part");
+    return HA_EINVAL;
+  }
+  if (!p.perm_q != !p.perm_k || (!p.perm_q && !p.causal) || (p.perm_q && p.causal)) {
+    set_error("backward dk/dv: row-order problems are exactly the causal leaves");
     return HA_EINVAL;
   }
   timing_begin(HA_K_BWD_DKV, s);

@@ -274,7 +274,8 @@ def main():
         result["approx_rel_error"] = approx_error(ha, torch, w_nc, w_c, q, k, v, out)
         result["configs"] = other_configs(ha, torch, dev, stream)
         del ws
-        result["backward"] = backward_bench(ha, torch, w_nc, q, k, v, out, lse, stream)
+        result["backward"] = {name: backward_bench(ha, torch, w, q, k, v, out, lse, stream)
+                              for name, w in (("noncausal", w_nc), ("causal", w_c))}
     if not args.no_cpu_baseline:
         result["cpu_baseline"] = cpu_baseline(w_nc, w_c, q, k, v)
     else:
@@ -299,8 +300,8 @@ def approx_error(ha, torch, w_nc, w_c, q, k, v, out):
     return res
 
 
-def backward_bench(ha, torch, w, q, k, v, out, lse, stream, reps=5):
-    """ms and effective TFLOP/s of the non-causal backward (dQ, dK, dV) of
+def backward_bench(ha, torch, w, q, k, v, out, lse, stream, reps=3):
+    """ms and effective TFLOP/s of the backward (dQ, dK, dV) of one pass of
     the headline configuration (not part of `value`).  Algorithmic FLOPs:
     10 d per (row, key) pair -- S, dP, dV, dQ, dK -- i.e. 2.5 times the
     forward's; the kernels recompute S and dP once more (14 d)."""
@@ -311,7 +312,8 @@ def backward_bench(ha, torch, w, q, k, v, out, lse, stream, reps=5):
     dk = torch.empty(k.shape, dtype=torch.float32, device=q.device)
     dv = torch.empty(k.shape, dtype=torch.float32, device=q.device)
     ws = torch.empty(ha.backward_workspace_bytes(w.batch, w.n, w.d, w.heads, w.kv_heads, w.block, w.samples,
-                                                 w.proj_bits), dtype=torch.uint8, device=q.device)
+                                                 w.proj_bits, w.causal, w.min_seq_len),
+                     dtype=torch.uint8, device=q.device)
     args = w.method_args()
     args.pop("flags", None)
 
@@ -332,8 +334,8 @@ def backward_bench(ha, torch, w, q, k, v, out, lse, stream, reps=5):
     per_kernel = ha.timing_read()
     ha.timing_enable(False)
     ms = e0.elapsed_time(e1) / reps
-    f_fwd, _ = alg_flops(w, False)
-    res = {"ms": ms, "tflops": 2.5 * f_fwd / (ms * 1e-3) / 1e12, "causal": False,
+    f_fwd, _ = alg_flops(w, w.causal)
+    res = {"ms": ms, "tflops": 2.5 * f_fwd / (ms * 1e-3) / 1e12, "causal": w.causal,
            "kernels": {name: t / reps for name, (t, cnt) in per_kernel.items() if cnt}}
     del dout, dq, dk, dv, ws
     return res
