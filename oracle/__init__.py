@@ -1,4 +1,5 @@
-"""CPU oracle for the HyperAttention forward pass and its backward.
+"""CPU oracle for the HyperAttention forward pass, its backward and the
+row-norm-sampling variant of the product (``oracle.rownorm``).
 
 TEST INFRASTRUCTURE ONLY.  Nothing on the product path may import, call or
 link anything in this package: only ``tests/``, ``__graft_entry__.smoke()``
@@ -59,4 +60,5 @@ __all__ = [
     "lse_merge", "noncausal_problem", "causal_problem", "forward", "forward_rows",
     "exact_attention", "causal_levels",
 ]
-from . import backward  # noqa: E402  (weighted-softmax backward, fp64)
+from . import backward
+from . import rownorm  # noqa: E402  (weighted-softmax backward, fp64)
