@@ -60,5 +60,5 @@ __all__ = [
     "lse_merge", "noncausal_problem", "causal_problem", "forward", "forward_rows",
     "exact_attention", "causal_levels",
 ]
-from . import backward
-from . import rownorm  # noqa: E402  (weighted-softmax backward, fp64)
+from . import backward  # noqa: E402  (weighted-softmax backward, fp64)
+from . import rownorm  # noqa: E402  (row-norm-sampling variant of the product)
