@@ -15,7 +15,7 @@ _HERE = os.path.dirname(os.path.abspath(__file__))
 LIB_PATH = os.path.join(_HERE, "libhyperattn.so")
 
 HA_BF16, HA_F32 = 0, 1
-HA_FLAG_MATERIALIZE, HA_FLAG_UNFUSED = 1, 2
+HA_FLAG_MATERIALIZE, HA_FLAG_UNFUSED, HA_FLAG_ROWNORM = 1, 2, 4
 HA_OK, HA_EINVAL, HA_EUNSUPPORTED, HA_EWORKSPACE, HA_ESHAPE, HA_EHIP = 0, -1, -2, -3, -4, -5
 KERNEL_CLASSES = ["proj", "hash", "sort", "samples", "gather", "attend", "merge", "leaf", "quadrant",
                   "bwd_dq", "bwd_dkv"]
@@ -40,6 +40,8 @@ _SIGNATURES = {
     "hyperattn_attend": (_c_int, [_vp, _vp, _vp, _c_int] + [_c_int] * 7 + [_vp, _vp, _vp, _c_int, _vp, _vp, _vp]),
     "hyperattn_merge_unsort": (_c_int, [_vp, _vp, _vp, _vp, _vp, _c_i64, _c_int, _c_int, _c_int, _vp, _vp, _vp]),
     "hyperattn_causal_leaves": (_c_int, [_vp, _vp, _vp, _c_int] + [_c_int] * 6 + [_vp, _vp, _vp]),
+    "hyperattn_row_sqnorms": (_c_int, [_vp, _c_int, _c_i64, _c_int, _vp, _vp]),
+    "hyperattn_rownorm_samples": (_c_int, [_vp, _vp] + [_c_int] * 5 + [_c_u64, _vp, _vp, _vp]),
     "hyperattn_timing_enable": (_c_int, [_c_int]),
     "hyperattn_timing_read": (_c_int, [_vp, _vp]),
 }
@@ -238,6 +240,31 @@ def sample_indices(seed, batch, heads, ns, samples, node_first=1, node_count=1, 
     _call("hyperattn_sample_indices", ctypes.c_uint64(seed), batch, heads, node_first, node_count, ns,
           samples, _ptr(out), _stream(out.device))
     return out
+
+
+def row_sqnorms(x):
+    """fp32 squared norms of the rows of x ([..., d]) in the row-norm
+    variant's fixed order."""
+    _need(x, "x")
+    d = x.shape[-1]
+    rows = x.numel() // d if d else 0
+    w = torch.empty(x.shape[:-1], dtype=torch.float32, device=x.device)
+    _call("hyperattn_row_sqnorms", _ptr(x), _dtype_code(x.dtype), rows, d, _ptr(w), _stream(x.device))
+    return w
+
+
+def rownorm_samples(w, perm_k, heads, samples, seed):
+    """Draws of the row-norm variant: w fp32 [B, Hkv, n] squared value-row
+    norms, perm_k int32 [B, Hkv, n] the keys' sort permutation.  Returns
+    (cum int64 [B, Hkv, n], sidx int32 [B, heads, samples])."""
+    _need(w, "w", torch.float32)
+    _need(perm_k, "perm_k", torch.int32, w.device)
+    B, Hkv, n = w.shape
+    cum = torch.empty((B, Hkv, n), dtype=torch.int64, device=w.device)
+    sidx = torch.empty((B, heads, samples), dtype=torch.int32, device=w.device)
+    _call("hyperattn_rownorm_samples", _ptr(w), _ptr(perm_k), B, heads, Hkv, n, samples, ctypes.c_uint64(seed),
+          _ptr(cum), _ptr(sidx), _stream(w.device))
+    return cum, sidx
 
 
 def gather_rows(src, perm):

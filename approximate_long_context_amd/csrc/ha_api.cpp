@@ -154,13 +154,17 @@ static int validate(Shape& sh) {
     set_error("head dim %d not built (64 or 128)", sh.d);
     return HA_EUNSUPPORTED;
   }
-  if (sh.flags & ~(HA_FLAG_MATERIALIZE | HA_FLAG_UNFUSED)) {
+  if (sh.flags & ~(HA_FLAG_MATERIALIZE | HA_FLAG_UNFUSED | HA_FLAG_ROWNORM)) {
     set_error("unknown flags 0x%x", sh.flags);
     return HA_EINVAL;
   }
   if (sh.causal && sh.flags) {
     set_error("flags apply to the non-causal forward only");
     return HA_EUNSUPPORTED;
+  }
+  if ((sh.flags & HA_FLAG_ROWNORM) && sh.flags != HA_FLAG_ROWNORM) {
+    set_error("the row-norm variant takes no other flag");
+    return HA_EINVAL;
   }
   if (sh.samples > kMaxSamples) {
     set_error("samples %d > %d", sh.samples, kMaxSamples);
@@ -208,8 +212,11 @@ struct Plan {
   void* qs;
   void* ks;
   void* vs;
-  float* part_o[2];
-  float* part_lse[2];
+  float* part_o[3];
+  float* part_lse[3];
+  float* rn_w;                 // row-norm variant: squared norms of V rows
+  int64_t* rn_cum;             // integer CDF per KV head
+  int32_t* rn_sidx;            // draws per query head
   size_t total;
 };
 
@@ -229,16 +236,22 @@ static Plan make_plan(const Shape& sh, void* ws, size_t cap) {
     size_t a = sort_ws_bytes(BH, sh.n, 1, sh.r), b = sort_ws_bytes(BK, sh.n, 1, sh.r);
     pl.sort_ws_bytes = a > b ? a : b;
     pl.sort_ws = cv.take<char>(pl.sort_ws_bytes);
-    if (sh.flags & HA_FLAG_MATERIALIZE) {
+    const bool rn = sh.flags & HA_FLAG_ROWNORM;
+    if ((sh.flags & HA_FLAG_MATERIALIZE) || rn) {
       pl.qs = cv.take<char>(BH * sh.n * sh.d * esz);
       pl.ks = cv.take<char>(BK * sh.n * sh.d * esz);
       pl.vs = cv.take<char>(BK * sh.n * sh.d * esz);
     }
-    if (sh.flags & HA_FLAG_UNFUSED) {
-      for (int i = 0; i < 2; ++i) {
+    if ((sh.flags & HA_FLAG_UNFUSED) || rn) {
+      for (int i = 0; i < (rn ? 3 : 2); ++i) {
         pl.part_o[i] = cv.take<float>(BH * sh.n * sh.d);
         pl.part_lse[i] = cv.take<float>(BH * sh.n);
       }
+    }
+    if (rn) {
+      pl.rn_w = cv.take<float>(BK * sh.n);
+      pl.rn_cum = cv.take<int64_t>(BK * sh.n);
+      pl.rn_sidx = cv.take<int32_t>(BH * (sh.samples > 0 ? sh.samples : 1));
     }
   } else {
     if (sh.levels > 0) {
@@ -318,6 +331,43 @@ static int forward_impl(const void* q, const void* k, const void* v, Shape sh, u
     ap.sidx = pl.sidx;
     ap.m = sh.samples;
     ap.log2w = sh.samples > 0 ? static_cast<float>(std::log2(static_cast<double>(sh.n) / sh.samples)) : 0.f;
+    if (sh.flags & HA_FLAG_ROWNORM) {
+      // block part, uniform-sample part (its normaliser), row-norm part (its
+      // numerator, weights folded into a sorted copy of V), merged
+      ap.out_mode = kOutPartial;
+      ap.use_block = 1;
+      ap.use_samples = 0;
+      ap.part_o = pl.part_o[0];
+      ap.part_lse = pl.part_lse[0];
+      HA_TRY(launch_attention(ap, HA_K_ATTEND, s));
+      ap.use_block = 0;
+      ap.use_samples = sh.samples > 0;
+      ap.part_o = pl.part_o[1];
+      ap.part_lse = pl.part_lse[1];
+      if (sh.samples > 0) HA_TRY(launch_attention(ap, HA_K_ATTEND, s));
+      if (sh.samples > 0) {
+        HA_TRY(launch_rownorm_sqnorm(v, sh.dtype, BK * sh.n, sh.d, pl.rn_w, s));
+        HA_TRY(launch_rownorm_cdf(pl.rn_w, pl.perm_k, BK, sh.n, pl.rn_cum, s));
+        HA_TRY(launch_rownorm_samples(pl.rn_cum, sh.n, seed, sh.batch, sh.heads, sh.kv_heads, sh.samples,
+                                      pl.rn_sidx, s));
+        HA_TRY(launch_gather(q, sh.dtype, BH, sh.n, sh.d, pl.perm_q, sh.n, pl.qs, s));
+        HA_TRY(launch_gather(k, sh.dtype, BK, sh.n, sh.d, pl.perm_k, sh.n, pl.ks, s));
+        HA_TRY(launch_rownorm_scale_gather(v, sh.dtype, pl.perm_k, pl.rn_cum, BK, sh.n, sh.d, sh.samples, pl.vs,
+                                           s));
+      }
+      ap.qs = pl.qs;
+      ap.ks = pl.ks;
+      ap.vs = pl.vs;
+      ap.sidx = pl.rn_sidx;
+      ap.log2w = 0.f;
+      ap.part_o = pl.part_o[2];
+      ap.part_lse = pl.part_lse[2];
+      if (sh.samples > 0) HA_TRY(launch_attention(ap, HA_K_ATTEND, s));
+      const bool smp = sh.samples > 0;          // no samples: both sampled parts are empty
+      return launch_rownorm_merge(pl.part_o[0], pl.part_lse[0], smp ? pl.part_lse[1] : nullptr,
+                                  smp ? pl.part_o[2] : nullptr, smp ? pl.part_lse[2] : nullptr, pl.perm_q, BH,
+                                  sh.n, sh.d, sh.dtype, out, lse, s);
+    }
     if (sh.flags & HA_FLAG_MATERIALIZE) {
       HA_TRY(launch_gather(q, sh.dtype, BH, sh.n, sh.d, pl.perm_q, sh.n, pl.qs, s));
       HA_TRY(launch_gather(k, sh.dtype, BK, sh.n, sh.d, pl.perm_k, sh.n, pl.ks, s));
@@ -628,6 +678,32 @@ int hyperattn_backward(const void* q, const void* k, const void* v, const void* 
   Shape sh{batch, n, d, heads, kv_heads, block, samples, proj_bits, causal, min_seq_len, dtype, 0};
   return backward_impl(q, k, v, out, lse, dout, sh, seed, dq, dk, dv, workspace, workspace_bytes,
                        static_cast<hipStream_t>(stream));
+}
+
+int hyperattn_row_sqnorms(const void* x, int dtype, int64_t rows, int d, float* w, void* stream) {
+  g_last_error.clear();
+  if (rows < 0 || (rows > 0 && (!x || !w))) {
+    set_error("row_sqnorms: bad arguments");
+    return HA_EINVAL;
+  }
+  if ((dtype != HA_BF16 && dtype != HA_F32) || (d != 64 && d != 128)) {
+    set_error("row_sqnorms: dtype %d / d %d not built", dtype, d);
+    return HA_EUNSUPPORTED;
+  }
+  return launch_rownorm_sqnorm(x, dtype, rows, d, w, static_cast<hipStream_t>(stream));
+}
+
+int hyperattn_rownorm_samples(const float* w, const int32_t* perm_k, int batch, int heads, int kv_heads, int n,
+                              int samples, uint64_t seed, int64_t* cum, int32_t* sidx, void* stream) {
+  g_last_error.clear();
+  if (batch < 0 || heads < 1 || kv_heads < 1 || heads % kv_heads || n < 0 || samples < 0 ||
+      (n > 0 && batch > 0 && (!w || !perm_k || !cum || (samples > 0 && !sidx)))) {
+    set_error("rownorm_samples: bad arguments");
+    return HA_EINVAL;
+  }
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  HA_TRY(launch_rownorm_cdf(w, perm_k, static_cast<int64_t>(batch) * kv_heads, n, cum, s));
+  return launch_rownorm_samples(cum, n, seed, batch, heads, kv_heads, samples, sidx, s);
 }
 
 int hyperattn_projections_host(uint64_t seed, int d, int proj_bits, float* host_out) {

@@ -127,6 +127,18 @@ inline int bwd_query_chunk(int seg) {
   return per64 > 2048 ? per64 : 2048;
 }
 
+// Row-norm variant (ha_rownorm.hip).
+int launch_rownorm_sqnorm(const void* v, int dtype, int64_t rows, int d, float* w, hipStream_t s);
+int launch_rownorm_cdf(const float* w, const int32_t* perm_k, int64_t problems, int n, int64_t* cum,
+                       hipStream_t s);
+int launch_rownorm_samples(const int64_t* cum, int n, uint64_t seed, int batch, int heads, int kv_heads, int m,
+                           int32_t* out, hipStream_t s);
+int launch_rownorm_scale_gather(const void* v, int dtype, const int32_t* perm_k, const int64_t* cum,
+                                int64_t problems, int n, int d, int m, void* out, hipStream_t s);
+int launch_rownorm_merge(const float* ob, const float* lb, const float* lu, const float* orr, const float* lr,
+                         const int32_t* perm, int64_t heads, int n, int d, int dtype, void* out, float* lse,
+                         hipStream_t s);
+
 int launch_bwd_qstat(const BwdParams& p, hipStream_t s);
 int launch_bwd_dq(const BwdParams& p, hipStream_t s);
 int launch_bwd_dkv(const BwdParams& p, bool samples, hipStream_t s);

@@ -1,0 +1,279 @@
+// Row-norm-sampling variant of the product with V (non-causal problems).
+//
+// ("HyperAttention: Long-context Attention in Near-Linear Time",
+// research-map summary, section Approach: the product with V is
+// approximated by row-norm sampling; "Builds on": approximate matrix
+// multiplication via row norm sampling.)
+//
+// The normaliser keeps its exact block row sums plus uniform samples; the
+// numerator's residual (keys outside the row's block) is estimated from m
+// key positions drawn with probability proportional to the squared norm of
+// the value row, each kept draw weighted 1 / (m p).  Probabilities are exact
+// integers so that draws are reproducible bit for bit:
+//   w_t = ||v_t||^2 in fp32 (squares rounded, groups of 8 consecutive
+//         squares summed by halving, group sums by halving);
+//   n_t = floor(w_t 2^(40 - e)) with max w = f 2^e, f in [0.5, 1);
+//   c_t = n_0 + ... + n_t over the sorted key positions, T = c_last;
+//   draw i: word x of Philox counter (i / 4, node, head, 2 batch + 2),
+//   r = floor(x T / 2^32), position = smallest t with c_t > r;
+//   weight T / (m n_t), folded into a sorted copy of V (the draw's row).
+// Kernels: squared norms, the per-problem integer CDF (one workgroup per
+// KV problem), the draws (binary search), the weighted sorted V copy, and
+// the three-part merge + unsort
+//   out = (N_blk + N_rn) / (D_blk + D_unif),  lse = ln(D_blk + D_unif).
+#include <cmath>
+
+#include "ha_device.h"
+#include "ha_kernels.h"
+#include "ha_rng.h"
+
+namespace ha {
+
+constexpr int kRnQBits = 40;
+
+// ---- squared row norms: 8 lanes per row (64 columns) or 16 (128); squares
+// and sums rounded separately (no multiply-add contraction) -----------------
+
+#pragma clang fp contract(off)
+template <typename T, int D>
+__global__ __launch_bounds__(256) void rownorm_sqnorm_kernel(const T* __restrict__ v, int64_t rows,
+                                                             float* __restrict__ w) {
+  constexpr int LPR = D / 8;                       // lanes per row, one group of 8 each
+  constexpr int RPW = 64 / LPR;
+  const int lane = threadIdx.x & 63;
+  const int64_t wave = (static_cast<int64_t>(blockIdx.x) * blockDim.x + threadIdx.x) >> 6;
+  const int64_t nwaves = (static_cast<int64_t>(gridDim.x) * blockDim.x) >> 6;
+  for (int64_t r0 = wave * RPW; r0 < rows; r0 += nwaves * RPW) {
+    const int64_t row = r0 + lane / LPR;
+    const int64_t rs = row < rows ? row : rows - 1;
+    const T* src = v + rs * D + 8 * (lane % LPR);
+    float sq[8];
+#pragma unroll
+    for (int i = 0; i < 8; ++i) {
+      const float x = static_cast<float>(src[i]);
+      sq[i] = x * x;
+    }
+    // halving within the group: pairs 4 apart, 2 apart, 1 apart
+#pragma unroll
+    for (int i = 0; i < 4; ++i) sq[i] = sq[i] + sq[i + 4];
+    sq[0] = sq[0] + sq[2];
+    sq[1] = sq[1] + sq[3];
+    float g = sq[0] + sq[1];
+    // halving over the groups (xor partners: lane i < h pairs with i + h)
+#pragma unroll
+    for (int h = LPR / 2; h >= 1; h >>= 1) g = g + __shfl_xor(g, h);
+    if (row < rows && lane % LPR == 0) w[row] = g;
+  }
+}
+
+// ---- integer CDF of one KV problem per workgroup -----------------------------
+
+constexpr int kRnCdfThreads = 1024;
+
+__global__ __launch_bounds__(kRnCdfThreads) void rownorm_cdf_kernel(const float* __restrict__ w,
+                                                                     const int32_t* __restrict__ perm_k, int n,
+                                                                     int64_t* __restrict__ cum) {
+  __shared__ float smax[kRnCdfThreads / 64];
+  __shared__ int64_t ssum[kRnCdfThreads];
+  const int tid = threadIdx.x;
+  const int64_t prob = blockIdx.x;
+  const float* wp = w + prob * n;
+  const int32_t* pk = perm_k + prob * n;
+  int64_t* cp = cum + prob * n;
+
+  float mx = 0.f;
+  for (int t = tid; t < n; t += kRnCdfThreads) mx = fmaxf(mx, wp[t]);
+#pragma unroll
+  for (int h = 32; h >= 1; h >>= 1) mx = fmaxf(mx, __shfl_xor(mx, h));
+  if ((tid & 63) == 0) smax[tid >> 6] = mx;
+  __syncthreads();
+  mx = 0.f;
+#pragma unroll
+  for (int i = 0; i < kRnCdfThreads / 64; ++i) mx = fmaxf(mx, smax[i]);
+  int e = 0;
+  if (mx > 0.f) frexp(static_cast<double>(mx), &e);
+  const int shift = kRnQBits - e;
+  auto weight = [&](int t) -> int64_t {
+    return mx > 0.f ? static_cast<int64_t>(floor(ldexp(static_cast<double>(wp[pk[t]]), shift))) : 0;
+  };
+
+  // each thread: a contiguous run of sorted positions
+  const int per = (n + kRnCdfThreads - 1) / kRnCdfThreads;
+  const int t0 = tid * per;
+  const int t1 = min(t0 + per, n);
+  int64_t local = 0;
+  for (int t = t0; t < t1; ++t) local += weight(t);
+  ssum[tid] = local;
+  __syncthreads();
+  // inclusive scan over the thread totals (Hillis-Steele in LDS)
+  for (int off = 1; off < kRnCdfThreads; off <<= 1) {
+    const int64_t add = tid >= off ? ssum[tid - off] : 0;
+    __syncthreads();
+    ssum[tid] += add;
+    __syncthreads();
+  }
+  int64_t run = ssum[tid] - local;
+  for (int t = t0; t < t1; ++t) {
+    run += weight(t);
+    cp[t] = run;
+  }
+}
+
+// ---- draws ---------------------------------------------------------------------
+
+__global__ void rownorm_sample_kernel(const int64_t* __restrict__ cum, int n, uint64_t seed, int heads,
+                                      int kv_heads, int m, int64_t total_ctr, int32_t* __restrict__ out) {
+  const int nctr = (m + 3) / 4;
+  const int G = heads / kv_heads;
+  for (int64_t t = static_cast<int64_t>(blockIdx.x) * blockDim.x + threadIdx.x; t < total_ctr;
+       t += static_cast<int64_t>(gridDim.x) * blockDim.x) {
+    const int64_t bh = t / nctr;
+    const int j = static_cast<int>(t % nctr);
+    const int h = static_cast<int>(bh % heads);
+    const int b = static_cast<int>(bh / heads);
+    const int64_t* cp = cum + (static_cast<int64_t>(b) * kv_heads + h / G) * n;
+    const uint64_t T = static_cast<uint64_t>(cp[n - 1]);
+    U32x4 c = {static_cast<uint32_t>(j), 1u, static_cast<uint32_t>(h), static_cast<uint32_t>(2 * b + 2)};
+    U32x4 r = philox4x32_10(c, seed);
+#pragma unroll
+    for (int wi = 0; wi < 4; ++wi) {
+      const int i = 4 * j + wi;
+      if (i >= m) break;
+      const uint64_t x = philox_word(r, wi);
+      // floor(x T / 2^32) exactly: T = Th 2^32 + Tl
+      const uint64_t rr = x * (T >> 32) + ((x * (T & 0xFFFFFFFFull)) >> 32);
+      int lo = 0, hi = n - 1;                       // smallest t with c_t > rr
+      while (lo < hi) {
+        const int mid = (lo + hi) >> 1;
+        if (static_cast<uint64_t>(cp[mid]) > rr) hi = mid;
+        else lo = mid + 1;
+      }
+      out[bh * m + i] = T > 0 ? lo : 0;
+    }
+  }
+}
+
+// ---- V copy in sorted key order, row t scaled by T / (m n_t) -------------------
+
+template <typename T>
+__global__ void rownorm_scale_gather_kernel(const T* __restrict__ v, const int32_t* __restrict__ perm_k,
+                                            const int64_t* __restrict__ cum, int n, int d, int m, int64_t rows,
+                                            T* __restrict__ out) {
+  const int64_t total = rows * d;
+  for (int64_t e = static_cast<int64_t>(blockIdx.x) * blockDim.x + threadIdx.x; e < total;
+       e += static_cast<int64_t>(gridDim.x) * blockDim.x) {
+    const int64_t rt = e / d;                       // kv problem * n + sorted position
+    const int c = static_cast<int>(e % d);
+    const int64_t prob = rt / n;
+    const int t = static_cast<int>(rt % n);
+    const int64_t* cp = cum + prob * n;
+    const int64_t nt = cp[t] - (t > 0 ? cp[t - 1] : 0);
+    const double scale = nt > 0 ? static_cast<double>(cp[n - 1]) / (static_cast<double>(m) * nt) : 0.0;
+    const float x = static_cast<float>(v[(prob * n + perm_k[rt]) * d + c]);
+    out[e] = static_cast<T>(x * static_cast<float>(scale));
+  }
+}
+
+// ---- three-part merge + unsort ---------------------------------------------------
+
+template <typename T>
+__global__ void rownorm_merge_kernel(const float* __restrict__ ob, const float* __restrict__ lb,
+                                     const float* __restrict__ lu, const float* __restrict__ orr,
+                                     const float* __restrict__ lr, const int32_t* __restrict__ perm, int n, int d,
+                                     int64_t total, T* __restrict__ out, float* __restrict__ lse) {
+  const int cpr = d / 4;
+  for (int64_t t = static_cast<int64_t>(blockIdx.x) * blockDim.x + threadIdx.x; t < total;
+       t += static_cast<int64_t>(gridDim.x) * blockDim.x) {
+    const int64_t rp = t / cpr;                     // head * n + sorted position
+    const int c = static_cast<int>(t % cpr);
+    const int64_t hd = rp / n;
+    // absent parts (null: no samples) count as empty, lse = -inf
+    const float a = lb[rp], u = lu ? lu[rp] : -INFINITY, r = lr ? lr[rp] : -INFINITY;
+    const float mm = fmaxf(a, u);                   // the normaliser's reference
+    float L = -INFINITY, wb = 0.f, wr = 0.f;
+    if (mm != -INFINITY) {
+      L = mm + logf(expf(a - mm) + expf(u - mm));
+      wb = expf(a - L);
+      wr = r == -INFINITY ? 0.f : expf(r - L);
+    }
+    const floatx4 x = reinterpret_cast<const floatx4*>(ob)[t];
+    floatx4 y = {0.f, 0.f, 0.f, 0.f};
+    if (wr != 0.f) y = reinterpret_cast<const floatx4*>(orr)[t];
+    const int64_t orow = hd * n + perm[rp];
+    T* dst = out + orow * d + 4 * c;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) dst[i] = static_cast<T>(x[i] * wb + y[i] * wr);
+    if (c == 0 && lse) lse[orow] = L;
+  }
+}
+
+// ---- launches ------------------------------------------------------------------------
+
+static unsigned grid_for(int64_t work, int per_block) {
+  int64_t blocks = (work + per_block - 1) / per_block;
+  if (blocks > 65536) blocks = 65536;
+  return static_cast<unsigned>(blocks < 1 ? 1 : blocks);
+}
+
+int launch_rownorm_sqnorm(const void* v, int dtype, int64_t rows, int d, float* w, hipStream_t s) {
+  if (rows == 0) return HA_OK;
+  const int rpw = 64 / (d / 8);
+  const unsigned g = grid_for(rows, 4 * rpw);
+  if (dtype == HA_BF16) {
+    if (d == 64) hipLaunchKernelGGL((rownorm_sqnorm_kernel<bf16, 64>), dim3(g), dim3(256), 0, s, static_cast<const bf16*>(v), rows, w);
+    else hipLaunchKernelGGL((rownorm_sqnorm_kernel<bf16, 128>), dim3(g), dim3(256), 0, s, static_cast<const bf16*>(v), rows, w);
+  } else {
+    if (d == 64) hipLaunchKernelGGL((rownorm_sqnorm_kernel<float, 64>), dim3(g), dim3(256), 0, s, static_cast<const float*>(v), rows, w);
+    else hipLaunchKernelGGL((rownorm_sqnorm_kernel<float, 128>), dim3(g), dim3(256), 0, s, static_cast<const float*>(v), rows, w);
+  }
+  return after_launch("row-norm squared norms", s);
+}
+
+int launch_rownorm_cdf(const float* w, const int32_t* perm_k, int64_t problems, int n, int64_t* cum,
+                       hipStream_t s) {
+  if (problems == 0 || n == 0) return HA_OK;
+  hipLaunchKernelGGL(rownorm_cdf_kernel, dim3(static_cast<unsigned>(problems)), dim3(kRnCdfThreads), 0, s, w,
+                     perm_k, n, cum);
+  return after_launch("row-norm cdf", s);
+}
+
+int launch_rownorm_samples(const int64_t* cum, int n, uint64_t seed, int batch, int heads, int kv_heads, int m,
+                           int32_t* out, hipStream_t s) {
+  const int64_t total = static_cast<int64_t>(batch) * heads * ((m + 3) / 4);
+  if (total == 0 || n == 0) return HA_OK;
+  hipLaunchKernelGGL(rownorm_sample_kernel, dim3(grid_for(total, 256)), dim3(256), 0, s, cum, n, seed, heads,
+                     kv_heads, m, total, out);
+  return after_launch("row-norm samples", s);
+}
+
+int launch_rownorm_scale_gather(const void* v, int dtype, const int32_t* perm_k, const int64_t* cum,
+                                int64_t problems, int n, int d, int m, void* out, hipStream_t s) {
+  const int64_t rows = problems * n;
+  if (rows == 0) return HA_OK;
+  const unsigned g = grid_for(rows * d, 256);
+  if (dtype == HA_BF16)
+    hipLaunchKernelGGL(rownorm_scale_gather_kernel<bf16>, dim3(g), dim3(256), 0, s, static_cast<const bf16*>(v),
+                       perm_k, cum, n, d, m, rows, static_cast<bf16*>(out));
+  else
+    hipLaunchKernelGGL(rownorm_scale_gather_kernel<float>, dim3(g), dim3(256), 0, s, static_cast<const float*>(v),
+                       perm_k, cum, n, d, m, rows, static_cast<float*>(out));
+  return after_launch("row-norm weighted V", s);
+}
+
+int launch_rownorm_merge(const float* ob, const float* lb, const float* lu, const float* orr, const float* lr,
+                         const int32_t* perm, int64_t heads, int n, int d, int dtype, void* out, float* lse,
+                         hipStream_t s) {
+  const int64_t total = heads * n * (d / 4);
+  if (total == 0) return HA_OK;
+  timing_begin(HA_K_MERGE, s);
+  if (dtype == HA_BF16)
+    hipLaunchKernelGGL(rownorm_merge_kernel<bf16>, dim3(grid_for(total, 256)), dim3(256), 0, s, ob, lb, lu, orr, lr,
+                       perm, n, d, total, static_cast<bf16*>(out), lse);
+  else
+    hipLaunchKernelGGL(rownorm_merge_kernel<float>, dim3(grid_for(total, 256)), dim3(256), 0, s, ob, lb, lu, orr,
+                       lr, perm, n, d, total, static_cast<float*>(out), lse);
+  timing_end(HA_K_MERGE, s);
+  return after_launch("row-norm merge+unsort", s);
+}
+
+}  // namespace ha

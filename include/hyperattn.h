@@ -64,7 +64,20 @@ enum {
   /* Run the block part, the sampled part and the merge as three kernels
    * (hyperattn_attend twice, then hyperattn_merge_unsort) instead of one
    * fused kernel (non-causal only; same results up to fp32 rounding). */
-  HA_FLAG_UNFUSED = 2
+  HA_FLAG_UNFUSED = 2,
+  /* Row-norm-sampling variant of the product ("HyperAttention: Long-context
+   * Attention in Near-Linear Time", research-map summary, section Approach:
+   * the product with V by row-norm sampling; "Builds on": approximate matrix
+   * multiplication via row norm sampling).  The normaliser is unchanged
+   * (block row sums + uniform samples, weight seg / samples); the residual
+   * product (keys outside the row's block) is estimated from `samples`
+   * key positions drawn with probability p_t proportional to the squared
+   * norm of the value row, each kept draw weighted 1 / (samples p_t):
+   *   out = (N_block + N_rownorm) / (D_block + D_uniform),
+   *   lse = ln(D_block + D_uniform).
+   * The draws are defined exactly (hyperattn_rownorm_samples).  Non-causal
+   * only; not combined with the other flags. */
+  HA_FLAG_ROWNORM = 4
 };
 
 /* Thread-local text of the last error returned on this thread ("" if none). */
@@ -134,6 +147,32 @@ int hyperattn_forward_ex(const void* q, const void* k, const void* v, int dtype,
                          int block, int samples, int proj_bits, int causal, int min_seq_len,
                          uint64_t seed, int flags, void* out, float* lse,
                          void* workspace, size_t workspace_bytes, void* stream);
+
+/* Squared row norms for the row-norm variant: w[i] = ||x_i||^2 in fp32,
+ * each square rounded, groups of 8 consecutive squares summed by halving
+ * (pairs 4, 2, 1 apart), the group sums by halving; no multiply-add
+ * contraction.  x device [rows, d] (bf16 or fp32, d 64 or 128), w device
+ * [rows] fp32, written.  Errors: HA_EINVAL (bad arguments),
+ * HA_EUNSUPPORTED (d or dtype). */
+int hyperattn_row_sqnorms(const void* x, int dtype, int64_t rows, int d, float* w, void* stream);
+
+/* Draws of the row-norm variant for non-causal problems.
+ *   w        device [batch * kv_heads][n] fp32, squared norms of the value
+ *            rows (hyperattn_row_sqnorms), row order
+ *   perm_k   device [batch * kv_heads][n] i32, the keys' sort permutation
+ *            (row within the head for each sorted position)
+ *   cum      device [batch * kv_heads][n] int64, written: with max w =
+ *            f 2^e (f in [0.5, 1)) and n_t = floor(w[perm_k[t]] 2^(40 - e)),
+ *            cum[t] = n_0 + ... + n_t (exact integers)
+ *   sidx     device [batch * heads][samples] i32, written: draw i of query
+ *            head h of batch entry b takes word i % 4 of Philox4x32-10 under
+ *            the seed with counter (i / 4, 1, h, 2 b + 2), r = floor(word T
+ *            / 2^32) with T = cum[n - 1] of the head's KV head, and is the
+ *            smallest sorted position t with cum[t] > r (0 when T = 0)
+ * Errors: HA_EINVAL (bad arguments). */
+int hyperattn_rownorm_samples(const float* w, const int32_t* perm_k, int batch, int heads, int kv_heads,
+                              int n, int samples, uint64_t seed, int64_t* cum, int32_t* sidx,
+                              void* stream);
 
 /* ------------------------------------------------------------------------
  * Backward ("HyperAttention: Long-context Attention in Near-Linear Time",

@@ -1,0 +1,108 @@
+"""GPU parity of the row-norm-sampling variant (HA_FLAG_ROWNORM) against
+``oracle.rownorm``.
+
+* squared value-row norms: bit-exact (bf16 and fp32, d 64 and 128);
+* integer CDF and draws: bit-exact (the draws decide integers, both sides
+  use the same exact integer arithmetic);
+* forward outputs: the block and uniform parts as in the fused forward,
+  the row-norm part from a sorted copy of V whose rows carry the draw
+  weight T / (m n_t), rounded to the input dtype (bf16: 2^-9 relative per
+  term) -- so the per-element bound is the forward's, scaled by the
+  largest reference magnitude (draws of small-norm rows carry large
+  weights and can lift outputs above 1): max-abs <= 2e-2 max(1, max|ref|)
+  and relative Frobenius <= 1e-2 for bf16 (1e-4 for fp32); lse as the
+  forward's (the normaliser is the uniform method's).
+"""
+
+import numpy as np
+import pytest
+import torch
+
+import approximate_long_context_amd as ha
+from oracle import HAConfig
+from oracle import rownorm as rn
+from oracle import hyperattn as oh
+
+from _util import np32, compare_lse, TOL
+
+pytestmark = pytest.mark.gpu
+DEV = "cuda"
+
+
+def _inputs(B, H, Hkv, n, d, seed, dtype=torch.bfloat16):
+    g = torch.Generator(device="cpu").manual_seed(seed)
+    s = d ** -0.25
+    q = (torch.randn(B, H, n, d, generator=g) * s).to(dtype)
+    k = (torch.randn(B, Hkv, n, d, generator=g) * s).to(dtype)
+    scale = torch.exp(0.7 * torch.randn(B, Hkv, n, 1, generator=g))      # varied row norms
+    v = (torch.randn(B, Hkv, n, d, generator=g) * scale).to(dtype)
+    return q, k, v
+
+
+@pytest.mark.parametrize("dtype", [torch.bfloat16, torch.float32])
+@pytest.mark.parametrize("d", [64, 128])
+def test_row_sqnorms_bit_exact(dtype, d):
+    _, _, v = _inputs(1, 1, 2, 700, d, 1, dtype)
+    w = ha.row_sqnorms(v.to(DEV)).cpu().numpy()
+    ref = rn.row_norms_sq(np32(v).reshape(-1, d)).reshape(w.shape)
+    assert np.array_equal(w.view(np.uint32), ref.view(np.uint32))
+
+
+@pytest.mark.parametrize("B,H,Hkv,n,d,m,seed", [(1, 2, 1, 1000, 64, 300, 2), (2, 4, 2, 4096, 128, 64, 3)])
+def test_rownorm_draws_bit_exact(B, H, Hkv, n, d, m, seed):
+    _, k, v = _inputs(B, H, Hkv, n, d, seed)
+    R = oh.projections(seed, d, 6)
+    perm = np.stack([np.stack([oh.sort_perm(oh.ranks(np32(k)[b, g], R)) for g in range(Hkv)])
+                     for b in range(B)]).astype(np.int32)
+    w = ha.row_sqnorms(v.to(DEV))
+    cum, sidx = ha.rownorm_samples(w, torch.from_numpy(perm).to(DEV), H, m, seed)
+    cum, sidx = cum.cpu().numpy(), sidx.cpu().numpy()
+    G = H // Hkv
+    for b in range(B):
+        for g in range(Hkv):
+            n_sorted = rn.quantized_weights(rn.row_norms_sq(np32(v)[b, g]))[perm[b, g]]
+            assert np.array_equal(cum[b, g], np.cumsum(n_sorted))
+        for h in range(H):
+            n_sorted = rn.quantized_weights(rn.row_norms_sq(np32(v)[b, h // G]))[perm[b, h // G]]
+            pos, _ = rn.rownorm_positions(seed, b, h, 1, n_sorted, m)
+            assert np.array_equal(sidx[b, h], pos), (b, h)
+
+
+CASES = [
+    # B, H, Hkv, n, d, block, samples, r, seed, dtype
+    (1, 2, 1, 1024, 64, 64, 128, 7, 4, torch.bfloat16),       # grouped heads
+    (1, 2, 2, 1000, 128, 40, 50, 6, 5, torch.bfloat16),       # block not a multiple of 64, ragged tail
+    (2, 1, 1, 512, 64, 512, 40, 5, 6, torch.bfloat16),        # one block: every draw excluded -> exact
+    (1, 2, 2, 768, 64, 128, 0, 6, 7, torch.bfloat16),         # no samples: block part only
+    (1, 1, 1, 1024, 64, 64, 64, 7, 8, torch.float32),         # fp32
+]
+
+
+@pytest.mark.parametrize("B,H,Hkv,n,d,block,m,r,seed,dtype", CASES)
+def test_rownorm_forward_matches_oracle(B, H, Hkv, n, d, block, m, r, seed, dtype):
+    q, k, v = _inputs(B, H, Hkv, n, d, 10 + seed, dtype)
+    args = dict(block=block, samples=m, proj_bits=r, seed=seed)
+    out, lse = ha.forward(q.to(DEV), k.to(DEV), v.to(DEV), flags=ha.HA_FLAG_ROWNORM, **args)
+    torch.cuda.synchronize()
+    ro, rl = rn.forward(np32(q), np32(k), np32(v), HAConfig(**args))
+    got = np32(out).astype(np.float64)
+    tol = TOL[dtype]
+    scale = max(1.0, float(np.max(np.abs(ro))))
+    err = float(np.max(np.abs(got - ro)))
+    rel = float(np.linalg.norm(got - ro) / np.linalg.norm(ro))
+    assert np.all(np.isfinite(got))
+    assert err <= tol["max_abs"] * scale, f"max-abs {err:.3e} > {tol['max_abs']} x {scale:.2f}"
+    assert rel <= tol["rel_fro"], f"rel-Frobenius {rel:.3e}"
+    compare_lse(lse.cpu().numpy(), rl, dtype, "lse")
+    if m == 0 or block >= n:
+        _, l0 = ha.forward(q.to(DEV), k.to(DEV), v.to(DEV), **args)
+        assert torch.allclose(lse, l0, atol=TOL[dtype]["lse"], rtol=0)
+
+
+def test_rownorm_rejects_causal_and_other_flags():
+    q, k, v = (t.to(DEV) for t in _inputs(1, 1, 1, 256, 64, 30))
+    with pytest.raises(ha.HyperAttnError):
+        ha.forward(q, k, v, block=64, samples=16, proj_bits=5, causal=True, min_seq_len=64,
+                   flags=ha.HA_FLAG_ROWNORM)
+    with pytest.raises(ha.HyperAttnError):
+        ha.forward(q, k, v, block=64, samples=16, proj_bits=5, flags=ha.HA_FLAG_ROWNORM | ha.HA_FLAG_UNFUSED)
