@@ -273,6 +273,7 @@ def main():
     if not args.no_extras:
         result["approx_rel_error"] = approx_error(ha, torch, w_nc, w_c, q, k, v, out)
         result["configs"] = other_configs(ha, torch, dev, stream)
+        result["rownorm"] = rownorm_bench(ha, torch, w_nc, q, k, v, out, stream)
         del ws
         result["backward"] = {name: backward_bench(ha, torch, w, q, k, v, out, lse, stream)
                               for name, w in (("noncausal", w_nc), ("causal", w_c))}
@@ -298,6 +299,39 @@ def approx_error(ha, torch, w_nc, w_c, q, k, v, out):
         res[name] = float(torch.linalg.vector_norm(a - b) / torch.linalg.vector_norm(b))
         del a, b
     return res
+
+
+def rownorm_bench(ha, torch, w, q, k, v, out, stream, reps=3):
+    """The row-norm-sampling variant of the product (HA_FLAG_ROWNORM) on the
+    non-causal headline pass: ms, effective TFLOP/s counted like the
+    forward's (4 d (b + m) per row) and its error against exact attention
+    next to the uniform method's (not part of `value`)."""
+    args = w.method_args()
+    ws = torch.empty(ha.workspace_bytes(w.batch, w.n, w.d, w.heads, w.kv_heads, w.block, w.samples, w.proj_bits,
+                                        w.causal, w.min_seq_len, w.dtype, flags=ha.HA_FLAG_ROWNORM),
+                     dtype=torch.uint8, device=q.device)
+
+    def run():
+        ha.forward(q, k, v, out=out, workspace=ws, flags=ha.HA_FLAG_ROWNORM, **args)
+
+    run()
+    torch.cuda.synchronize()
+    e0 = torch.cuda.Event(enable_timing=True)
+    e1 = torch.cuda.Event(enable_timing=True)
+    e0.record(stream)
+    for _ in range(reps):
+        run()
+    e1.record(stream)
+    torch.cuda.synchronize()
+    ms = e0.elapsed_time(e1) / reps
+    f, _ = alg_flops(w, False)
+    ex = torch.empty_like(out)
+    ha.forward(q, k, v, out=ex, **w.with_(block=w.n).method_args())
+    run()
+    a, b = out.float(), ex.float()
+    err = float(torch.linalg.vector_norm(a - b) / torch.linalg.vector_norm(b))
+    del a, b, ex, ws
+    return {"ms": ms, "tflops": f / (ms * 1e-3) / 1e12, "approx_rel_error": err}
 
 
 def backward_bench(ha, torch, w, q, k, v, out, lse, stream, reps=3):
