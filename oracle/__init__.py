@@ -1,5 +1,6 @@
 """CPU oracle for the HyperAttention forward pass, its backward and the
-row-norm-sampling variant of the product (``oracle.rownorm``).
+row-norm-sampling variant of the product (``oracle.rownorm``) and the
+method's fine-grained parameters as diagnostics (``oracle.diagnostics``).
 
 TEST INFRASTRUCTURE ONLY.  Nothing on the product path may import, call or
 link anything in this package: only ``tests/``, ``__graft_entry__.smoke()``
@@ -62,3 +63,4 @@ __all__ = [
 ]
 from . import backward  # noqa: E402  (weighted-softmax backward, fp64)
 from . import rownorm  # noqa: E402  (row-norm-sampling variant of the product)
+from . import diagnostics  # noqa: E402  (alpha and the residual row-sum ratio)
