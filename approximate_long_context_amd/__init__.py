@@ -42,6 +42,8 @@ _SIGNATURES = {
     "hyperattn_causal_leaves": (_c_int, [_vp, _vp, _vp, _c_int] + [_c_int] * 6 + [_vp, _vp, _vp]),
     "hyperattn_row_sqnorms": (_c_int, [_vp, _c_int, _c_i64, _c_int, _vp, _vp]),
     "hyperattn_rownorm_samples": (_c_int, [_vp, _vp] + [_c_int] * 5 + [_c_u64, _vp, _vp, _vp]),
+    "hyperattn_column_sqmass": (_c_int, [_vp, _vp, _vp] + [_c_int] * 8 + [_vp, _vp, _vp]),
+    "hyperattn_residual_ratio": (_c_int, [_vp, _vp, _vp, _c_i64, _c_int, _vp, _vp]),
     "hyperattn_timing_enable": (_c_int, [_c_int]),
     "hyperattn_timing_read": (_c_int, [_vp, _vp]),
 }
@@ -265,6 +267,35 @@ def rownorm_samples(w, perm_k, heads, samples, seed):
     _call("hyperattn_rownorm_samples", _ptr(w), _ptr(perm_k), B, heads, Hkv, n, samples, ctypes.c_uint64(seed),
           _ptr(cum), _ptr(sidx), _stream(w.device))
     return cum, sidx
+
+
+def column_sqmass(q, k, lse, *, causal=False, skip=0):
+    """(colmass [B, H, n], alpha [B, H]) of the exact softmax matrix given
+    its exact lse (natural log, [B, H, n]); bf16 q [B, H, n, d], k
+    [B, Hkv, n, d]."""
+    _need(q, "q", torch.bfloat16)
+    _need(k, "k", torch.bfloat16, q.device)
+    _need(lse, "lse", torch.float32, q.device)
+    B, H, n, d = q.shape
+    colmass = torch.empty((B, H, n), dtype=torch.float32, device=q.device)
+    alpha = torch.empty((B, H), dtype=torch.float32, device=q.device)
+    _call("hyperattn_column_sqmass", _ptr(q), _ptr(k), _ptr(lse), HA_BF16, B, n, d, H, k.shape[1],
+          int(bool(causal)), skip, _ptr(colmass), _ptr(alpha), _stream(q.device))
+    return colmass, alpha
+
+
+def residual_ratio(lse_exact, lse_block, perm_q):
+    """kappa per problem from the exact lse (row order), the block part's
+    lse (sorted positions) and the queries' permutation, all [..., n]."""
+    _need(lse_exact, "lse_exact", torch.float32)
+    _need(lse_block, "lse_block", torch.float32, lse_exact.device)
+    _need(perm_q, "perm_q", torch.int32, lse_exact.device)
+    n = lse_exact.shape[-1]
+    problems = lse_exact.numel() // n if n else 0
+    kappa = torch.empty(lse_exact.shape[:-1], dtype=torch.float32, device=lse_exact.device)
+    _call("hyperattn_residual_ratio", _ptr(lse_exact), _ptr(lse_block), _ptr(perm_q), problems, n, _ptr(kappa),
+          _stream(lse_exact.device))
+    return kappa
 
 
 def gather_rows(src, perm):

@@ -19,7 +19,7 @@ INCLUDE = os.path.join(ROOT, "include")
 BUILD = os.path.join(HERE, "_build")
 LIB = os.path.join(HERE, "libhyperattn.so")
 
-SOURCES = ["ha_api.cpp", "ha_hash.hip", "ha_sort.hip", "ha_attn.hip", "ha_aux.hip", "ha_bwd.hip", "ha_rownorm.hip"]
+SOURCES = ["ha_api.cpp", "ha_hash.hip", "ha_sort.hip", "ha_attn.hip", "ha_aux.hip", "ha_bwd.hip", "ha_rownorm.hip", "ha_diag.hip"]
 ARCH = os.environ.get("HYPERATTN_ARCH", "gfx950")
 
 FLAGS = [

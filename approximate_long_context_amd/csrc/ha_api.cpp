@@ -706,6 +706,37 @@ int hyperattn_rownorm_samples(const float* w, const int32_t* perm_k, int batch, 
   return launch_rownorm_samples(cum, n, seed, batch, heads, kv_heads, samples, sidx, s);
 }
 
+int hyperattn_column_sqmass(const void* q, const void* k, const float* lse, int dtype, int batch, int n, int d,
+                            int heads, int kv_heads, int causal, int skip, float* colmass, float* alpha,
+                            void* stream) {
+  g_last_error.clear();
+  if (batch < 0 || n < 0 || heads < 1 || kv_heads < 1 || heads % kv_heads || skip < 0 ||
+      (batch > 0 && n > 0 && (!q || !k || !lse || !colmass))) {
+    set_error("column_sqmass: bad arguments");
+    return HA_EINVAL;
+  }
+  if (dtype != HA_BF16 || (d != 64 && d != 128)) {
+    set_error("column_sqmass: bf16 with d 64 or 128 only");
+    return HA_EUNSUPPORTED;
+  }
+  if (static_cast<int64_t>(n) * d * 2 >= (int64_t(1) << 32)) {
+    set_error("column_sqmass: one head spans 4 GiB or more");
+    return HA_EUNSUPPORTED;
+  }
+  return launch_colmass(q, k, lse, batch, n, d, heads, kv_heads, causal, skip, colmass, alpha,
+                        static_cast<hipStream_t>(stream));
+}
+
+int hyperattn_residual_ratio(const float* lse_exact, const float* lse_block, const int32_t* perm_q,
+                             int64_t problems, int n, float* kappa, void* stream) {
+  g_last_error.clear();
+  if (problems < 0 || n < 0 || (problems > 0 && n > 0 && (!lse_exact || !lse_block || !perm_q || !kappa))) {
+    set_error("residual_ratio: bad arguments");
+    return HA_EINVAL;
+  }
+  return launch_kappa(lse_exact, lse_block, perm_q, problems, n, kappa, static_cast<hipStream_t>(stream));
+}
+
 int hyperattn_projections_host(uint64_t seed, int d, int proj_bits, float* host_out) {
   g_last_error.clear();
   if (!host_out || d < 1 || proj_bits < 1 || proj_bits > 16) {

@@ -139,6 +139,12 @@ int launch_rownorm_merge(const float* ob, const float* lb, const float* lu, cons
                          const int32_t* perm, int64_t heads, int n, int d, int dtype, void* out, float* lse,
                          hipStream_t s);
 
+// Diagnostics (ha_diag.hip).
+int launch_colmass(const void* q, const void* k, const float* lse, int batch, int n, int d, int heads,
+                   int kv_heads, int causal, int skip, float* colmass, float* alpha, hipStream_t s);
+int launch_kappa(const float* lse_exact, const float* lse_block, const int32_t* perm_q, int64_t problems, int n,
+                 float* kappa, hipStream_t s);
+
 int launch_bwd_qstat(const BwdParams& p, hipStream_t s);
 int launch_bwd_dq(const BwdParams& p, hipStream_t s);
 int launch_bwd_dkv(const BwdParams& p, bool samples, hipStream_t s);

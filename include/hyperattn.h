@@ -175,6 +175,42 @@ int hyperattn_rownorm_samples(const float* w, const int32_t* perm_k, int batch, 
                               void* stream);
 
 /* ------------------------------------------------------------------------
+ * Diagnostics: the method's fine-grained parameters ("HyperAttention:
+ * Long-context Attention in Near-Linear Time", research-map summary,
+ * sections Approach and Limitations -- alpha, the largest squared column
+ * norm of the softmax matrix D^-1 A, and the ratio of row norms of A after
+ * the large entries are removed; section Surprising findings -- alpha taken
+ * without the first 32 columns for chatglm2).
+ * ------------------------------------------------------------------------ */
+
+/* Squared column mass of the exact softmax matrix and alpha.
+ *   q, k       device bf16, [batch, heads, n, d] and [batch, kv_heads, n, d]
+ *   lse        device [batch, heads, n] fp32, the exact attention's natural
+ *              log row sums (hyperattn_forward with block >= n, or causal
+ *              with min_seq_len >= n)
+ *   colmass    device [batch, heads, n] fp32, written: c_j = sum_i
+ *              exp(2 (q_i . k_j - lse_i)) (causal: over i >= j)
+ *   alpha      device [batch, heads] fp32 or NULL, written: max over
+ *              columns j >= skip of c_j (-inf if skip >= n)
+ * Errors: HA_EINVAL (bad arguments), HA_EUNSUPPORTED (not bf16, d not 64
+ * or 128). */
+int hyperattn_column_sqmass(const void* q, const void* k, const float* lse, int dtype, int batch, int n, int d,
+                            int heads, int kv_heads, int causal, int skip, float* colmass, float* alpha,
+                            void* stream);
+
+/* Ratio of the largest to the smallest residual row sum, r_i = sum of A_ij
+ * over the keys outside row i's sortLSH block = exp(lse_exact_i) (1 -
+ * exp(lse_block_i - lse_exact_i)), per problem (fp64 inside).
+ *   lse_exact  device [problems, n] fp32, exact lse, row order
+ *   lse_block  device [problems, n] fp32, the block part's lse at sorted
+ *              positions (hyperattn_attend with parts = 1)
+ *   perm_q     device [problems, n] i32, the queries' sort permutation
+ *   kappa      device [problems] fp32, written (+inf if some r_i is 0)
+ * Errors: HA_EINVAL. */
+int hyperattn_residual_ratio(const float* lse_exact, const float* lse_block, const int32_t* perm_q,
+                             int64_t problems, int n, float* kappa, void* stream);
+
+/* ------------------------------------------------------------------------
  * Backward ("HyperAttention: Long-context Attention in Near-Linear Time",
  * research-map summary, section Key results: the method is timed forward
  * and backward; the pages print no backward formulas).  For the ranks and

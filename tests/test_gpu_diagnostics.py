@@ -1,0 +1,109 @@
+"""GPU parity of the diagnostics against ``oracle.diagnostics``.
+
+* column squared mass with the oracle's exact lse as input: every term
+  exp(2 (s - lse)) has fp32 scores of exact bf16 products (relative error a
+  few 1e-7 of |s|) and an fp32 lse, so each column sum is within 1e-4
+  relative of the fp64 oracle;
+* alpha end to end (the library's exact-mode lse, whose bf16-rounded
+  weights move lse by up to ~2e-3, i.e. c_j by ~0.4 %): within 1e-2
+  relative; skipping the 32 planted heavy columns of chatglm2-like keys
+  lowers alpha;
+* kappa end to end (the library's exact lse, the block part's lse from
+  the stage entry points): within 2e-2 relative.
+"""
+
+import numpy as np
+import pytest
+import torch
+
+import approximate_long_context_amd as ha
+from oracle import diagnostics as dg
+from oracle import hyperattn as oh
+
+from _util import np32
+
+pytestmark = pytest.mark.gpu
+DEV = "cuda"
+
+
+def _inputs(B, H, Hkv, n, d, seed, sinks=0):
+    g = torch.Generator(device="cpu").manual_seed(seed)
+    s = d ** -0.25
+    q = (torch.randn(B, H, n, d, generator=g) * s).to(torch.bfloat16)
+    k = torch.randn(B, Hkv, n, d, generator=g) * s
+    k[:, :, :sinks] *= 4.0
+    v = torch.randn(B, Hkv, n, d, generator=g).to(torch.bfloat16)
+    return q, k.to(torch.bfloat16), v
+
+
+CASES = [
+    # B, H, Hkv, n, d, causal, seed
+    (1, 2, 1, 1000, 64, False, 1),
+    (1, 2, 2, 1000, 64, True, 2),
+    (2, 2, 1, 1536, 128, False, 3),
+    (1, 4, 2, 777, 128, True, 4),
+]
+
+
+@pytest.mark.parametrize("B,H,Hkv,n,d,causal,seed", CASES)
+def test_column_sqmass_matches_oracle(B, H, Hkv, n, d, causal, seed):
+    q, k, _ = _inputs(B, H, Hkv, n, d, seed)
+    G = H // Hkv
+    lse = np.zeros((B, H, n))
+    ref = np.zeros((B, H, n))
+    for b in range(B):
+        for h in range(H):
+            qh, kh = np32(q)[b, h].astype(np.float64), np32(k)[b, h // G].astype(np.float64)
+            S = qh @ kh.T
+            if causal:
+                S = np.where(np.tril(np.ones((n, n), dtype=bool)), S, -np.inf)
+            mx = S.max(axis=1)
+            lse[b, h] = mx + np.log(np.exp(S - mx[:, None]).sum(axis=1))
+            ref[b, h] = dg.column_sqmass(qh, kh, causal)
+    cm, alpha = ha.column_sqmass(q.to(DEV), k.to(DEV), torch.from_numpy(lse.astype(np.float32)).to(DEV),
+                                 causal=causal, skip=3)
+    cm = cm.cpu().numpy()
+    assert np.max(np.abs(cm - ref) / ref) < 1e-4
+    assert np.allclose(alpha.cpu().numpy(), ref[..., 3:].max(axis=-1), rtol=1e-4, atol=0)
+
+
+def _exact_lse(q, k, v, causal):
+    n = q.shape[2]
+    args = dict(block=n, samples=0, proj_bits=4, causal=causal, min_seq_len=n if causal else 0)
+    return ha.forward(q, k, v, **args)[1]
+
+
+@pytest.mark.parametrize("causal", [False, True])
+def test_alpha_end_to_end_and_skipped_sinks(causal):
+    B, H, Hkv, n, d = 1, 2, 1, 2048, 128
+    q, k, v = _inputs(B, H, Hkv, n, d, 5, sinks=32)
+    qd, kd, vd = q.to(DEV), k.to(DEV), v.to(DEV)
+    lse = _exact_lse(qd, kd, vd, causal)
+    _, a0 = ha.column_sqmass(qd, kd, lse, causal=causal, skip=0)
+    _, a32 = ha.column_sqmass(qd, kd, lse, causal=causal, skip=32)
+    for h in range(H):
+        qh, kh = np32(q)[0, h].astype(np.float64), np32(k)[0, 0].astype(np.float64)
+        r0, r32 = dg.alpha(qh, kh, causal), dg.alpha(qh, kh, causal, skip=32)
+        assert abs(float(a0[0, h]) - r0) <= 1e-2 * r0
+        assert abs(float(a32[0, h]) - r32) <= 1e-2 * r32
+        if not causal:
+            assert r32 < r0
+
+
+@pytest.mark.parametrize("block", [64, 256])
+def test_kappa_end_to_end(block):
+    B, H, Hkv, n, d, r, seed = 1, 2, 2, 2048, 64, 7, 6
+    q, k, v = _inputs(B, H, Hkv, n, d, seed)
+    qd, kd, vd = q.to(DEV), k.to(DEV), v.to(DEV)
+    le = _exact_lse(qd, kd, vd, False)
+    R = ha.projections(seed, d, r, DEV)
+    perm_q = ha.sort_ranks(ha.hash_rows(qd.view(-1, n, d), R), r).view(H, n)
+    perm_k = ha.sort_ranks(ha.hash_rows(kd.view(-1, n, d), R), r).view(Hkv, n)
+    idx = ha.sample_indices(seed, 1, H, n, 16, device=DEV)      # unused by the block part
+    _, lb = ha.attend(qd, kd, vd, perm_q, perm_k, idx, block=block, samples=16, parts=1)
+    kappa = ha.residual_ratio(le.view(H, n), lb.reshape(H, n).contiguous(), perm_q.contiguous()).cpu().numpy()
+    Rn = oh.projections(seed, d, r)
+    for h in range(H):
+        qh, kh = np32(q)[0, h], np32(k)[0, h]
+        ref = dg.kappa(qh.astype(np.float64), kh.astype(np.float64), oh.ranks(qh, Rn), oh.ranks(kh, Rn), block)
+        assert abs(kappa[h] - ref) <= 2e-2 * ref, (h, kappa[h], ref)
