@@ -274,6 +274,7 @@ def main():
         result["approx_rel_error"] = approx_error(ha, torch, w_nc, w_c, q, k, v, out)
         result["configs"] = other_configs(ha, torch, dev, stream)
         result["rownorm"] = rownorm_bench(ha, torch, w_nc, q, k, v, out, stream)
+        result["diagnostics"] = diagnostics_bench(ha, torch, dev, stream)
         del ws
         result["backward"] = {name: backward_bench(ha, torch, w, q, k, v, out, lse, stream)
                               for name, w in (("noncausal", w_nc), ("causal", w_c))}
@@ -298,6 +299,45 @@ def approx_error(ha, torch, w_nc, w_c, q, k, v, out):
         b = ex.float()
         res[name] = float(torch.linalg.vector_norm(a - b) / torch.linalg.vector_norm(b))
         del a, b
+    return res
+
+
+def diagnostics_bench(ha, torch, dev, stream):
+    """alpha (largest squared column norm of the exact softmax matrix; with
+    and without the first 32 columns) on the 32k GQA causal configuration
+    with planted attention sinks, and kappa (largest / smallest residual
+    row sum outside the sortLSH blocks) on the 32k non-causal one; maxima
+    over heads, and the column pass's time (not part of `value`)."""
+    from approximate_long_context_amd.workloads import WORKLOADS, make_inputs
+    res = {}
+    w = WORKLOADS["glm32k"]
+    q, k, v = make_inputs(w, dev)
+    n = w.n
+    lse = ha.forward(q, k, v, block=n, samples=0, proj_bits=w.proj_bits, causal=True, min_seq_len=n)[1]
+    ha.column_sqmass(q, k, lse, causal=True)
+    e0 = torch.cuda.Event(enable_timing=True)
+    e1 = torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    e0.record(stream)
+    _, a0 = ha.column_sqmass(q, k, lse, causal=True, skip=0)
+    e1.record(stream)
+    _, a32 = ha.column_sqmass(q, k, lse, causal=True, skip=32)
+    torch.cuda.synchronize()
+    res["glm32k_causal"] = {"alpha": float(a0.max()), "alpha_skip32": float(a32.max()),
+                            "column_pass_ms": e0.elapsed_time(e1), "n": n}
+    del q, k, v, lse
+    w = WORKLOADS["c32k"]
+    q, k, v = make_inputs(w, dev)
+    B, H, n, d = q.shape
+    le = ha.forward(q, k, v, block=n, samples=0, proj_bits=w.proj_bits)[1]
+    R = ha.projections(w.seed, d, w.proj_bits, dev)
+    perm_q = ha.sort_ranks(ha.hash_rows(q.view(-1, n, d), R), w.proj_bits).view(B * H, n)
+    perm_k = ha.sort_ranks(ha.hash_rows(k.view(-1, n, d), R), w.proj_bits).view(B * w.kv_heads, n)
+    idx = ha.sample_indices(w.seed, B, H, n, 16, device=dev)
+    _, lb = ha.attend(q, k, v, perm_q, perm_k, idx, block=w.block, samples=16, parts=1)
+    kappa = ha.residual_ratio(le.view(B * H, n), lb.reshape(B * H, n).contiguous(), perm_q.contiguous())
+    res["c32k"] = {"kappa": float(kappa.max()), "block": w.block, "n": n}
+    del q, k, v
     return res
 
 
