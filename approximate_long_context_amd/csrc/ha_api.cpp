@@ -171,14 +171,7 @@ static int validate(Shape& sh) {
     return HA_EUNSUPPORTED;
   }
   if (sh.n == 0) return HA_OK;
-  if (!sh.causal) {
-    const int b = sh.block < sh.n ? sh.block : sh.n;
-    if (sh.n % b) {
-      set_error("n = %d is not a multiple of block %d", sh.n, b);
-      return HA_ESHAPE;
-    }
-    return HA_OK;
-  }
+  if (!sh.causal) return HA_OK;
   int ns = sh.n, L = 0;
   while (ns > sh.s) {
     if (ns % 2) {
@@ -187,11 +180,6 @@ static int validate(Shape& sh) {
     }
     ns /= 2;
     ++L;
-    const int b = sh.block < ns ? sh.block : ns;
-    if (ns % b) {
-      set_error("causal quadrant length %d is not a multiple of block %d", ns, b);
-      return HA_ESHAPE;
-    }
   }
   sh.levels = L;
   sh.leaf = ns;

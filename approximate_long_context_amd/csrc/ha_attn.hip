@@ -139,7 +139,7 @@ __global__ __launch_bounds__(64 * NW, (min_waves<T, D, KIND, NW, QPW>())) void a
       ka1 = qend;
     } else {
       ka0 = (q0 / p.b_eff) * p.b_eff;
-      ka1 = ((qend - 1) / p.b_eff + 1) * p.b_eff;
+      ka1 = min(((qend - 1) / p.b_eff + 1) * p.b_eff, p.seg);   // the last block may be short
     }
   }
   const bool samp = !LEAF && p.use_samples && p.m > 0;

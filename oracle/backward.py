@@ -44,8 +44,6 @@ def noncausal_weights(rank_q, rank_k, seed, batch_idx, head, node, block, sample
     if ns == 0:
         return np.zeros((0, 0))
     b_eff = min(block, ns)
-    if ns % b_eff:
-        raise ValueError(f"segment length {ns} is not a multiple of block {b_eff}")
     pq = sort_perm(rank_q)
     pk = sort_perm(rank_k)
     spos_q = np.empty(ns, dtype=np.int64)

@@ -172,25 +172,25 @@ def _softmax_stats(S, V):
 
 def block_part(Qs, Ks, Vs, b_eff, positions=None):
     """Exact attention of sorted query p over the sorted keys of its own
-    diagonal block t = p // b_eff, i.e. keys [t b_eff, (t+1) b_eff).
-    Returns (lse_blk, o_blk) for ``positions`` (all if None):
-    exp(lse_blk) = sum_{j in blk} e^{S_pj},  o_blk = that softmax times V."""
+    diagonal block t = p // b_eff, i.e. keys [t b_eff, min((t+1) b_eff, ns))
+    (reading R9: consecutive runs of b_eff sorted positions, the last run
+    holding what remains).  Returns (lse_blk, o_blk) for ``positions`` (all
+    if None): exp(lse_blk) = sum_{j in blk} e^{S_pj},  o_blk = that softmax
+    times V."""
     ns, d = Qs.shape
     if positions is None:
-        nb = ns // b_eff
-        S = np.matmul(Qs.reshape(nb, b_eff, d), Ks.reshape(nb, b_eff, d).transpose(0, 2, 1))
-        lse, o = _softmax_stats(S, Vs.reshape(nb, b_eff, d))
-        return lse.reshape(ns), o.reshape(ns, d)
+        positions = np.arange(ns)
     positions = np.asarray(positions, dtype=np.int64)
     lse = np.empty(len(positions))
     o = np.empty((len(positions), d))
-    for c in range(0, len(positions), 256):
-        p = positions[c:c + 256]
-        keys = (p // b_eff)[:, None] * b_eff + np.arange(b_eff)[None, :]
-        S = np.einsum("rd,rkd->rk", Qs[p], Ks[keys])
-        l, oo = _softmax_stats(S[:, None, :], Vs[keys])
-        lse[c:c + 256] = l[:, 0]
-        o[c:c + 256] = oo[:, 0, :]
+    blk = positions // b_eff
+    for t in np.unique(blk):
+        rows = np.nonzero(blk == t)[0]
+        lo, hi = t * b_eff, min((t + 1) * b_eff, ns)
+        S = Qs[positions[rows]] @ Ks[lo:hi].T
+        l, oo = _softmax_stats(S, Vs[lo:hi])
+        lse[rows] = l
+        o[rows] = oo
     return lse, o
 
 
@@ -248,8 +248,8 @@ def noncausal_problem(q, k, v, rank_q, rank_k, seed, batch_idx, head, node,
     if ns == 0:
         return np.zeros((0, d)), np.zeros(0)
     b_eff = min(block, ns)
-    if b_eff < 1 or ns % b_eff:
-        raise ValueError(f"segment length {ns} is not a multiple of block {b_eff}")
+    if b_eff < 1:
+        raise ValueError("block must be >= 1")
     pq = sort_perm(rank_q)
     pk = sort_perm(rank_k)
     Qs, Ks, Vs = q[pq], k[pk], v[pk]

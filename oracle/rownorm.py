@@ -132,8 +132,8 @@ def noncausal_problem_rownorm(q, k, v, rank_q, rank_k, v32, seed, batch_idx, hea
     in original row order (``rows``: local indices, all if None)."""
     ns, d = q.shape
     b_eff = min(block, ns)
-    if b_eff < 1 or ns % b_eff:
-        raise ValueError(f"segment length {ns} is not a multiple of block {b_eff}")
+    if b_eff < 1:
+        raise ValueError("block must be >= 1")
     pq = sort_perm(rank_q)
     pk = sort_perm(rank_k)
     Qs, Ks, Vs = q[pq], k[pk], v[pk]

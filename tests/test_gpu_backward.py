@@ -58,6 +58,8 @@ CASES = [
     (1, 2, 1, 1024, 64, 128, 0, 7, 7),        # no samples
     (1, 4, 2, 2048, 128, 512, 256, 8, 8),     # d = 128, block wider than a workgroup
     (1, 2, 1, 960, 64, 96, 70, 6, 9),         # block not a multiple of the 64-row tile
+    (1, 2, 1, 1000, 64, 256, 64, 7, 10),      # ragged last block (1000 = 3 x 256 + 232)
+    (1, 2, 2, 1100, 128, 64, 40, 6, 11),      # ragged last block, d = 128
 ]
 
 
@@ -68,6 +70,7 @@ CAUSAL_CASES = [
     (1, 4, 2, 2048, 64, 128, 64, 7, 512, 23),     # grouped heads, leaves of two workgroups
     (1, 2, 1, 512, 64, 64, 16, 5, 512, 24),       # leaf only (no quadrant level)
     (2, 2, 2, 2048, 128, 256, 128, 7, 256, 25),   # d = 128, three levels, batch 2
+    (1, 2, 1, 2048, 64, 96, 32, 6, 256, 26),      # quadrants of 1024, 512, 256 rows: ragged last blocks
 ]
 
 

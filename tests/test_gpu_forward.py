@@ -50,6 +50,10 @@ SMALL = [
     Workload("c_fp32", 1, 1, 1, 512, 64, torch.float32, 32, 16, 6, True, 64, "iid", 8, 21),
     Workload("c_leafonly", 1, 2, 1, 1000, 64, torch.bfloat16, 64, 16, 7, True, 1000, "iid", 9, 22),
     Workload("c_clusters", 1, 2, 2, 2048, 128, torch.bfloat16, 128, 128, 8, True, 512, "clusters", 10, 23),
+    # ragged last block: n (or a quadrant) not a multiple of the block
+    Workload("nc_lastblock", 1, 2, 1, 1000, 64, torch.bfloat16, 64, 48, 7, False, 0, "iid", 11, 24),
+    Workload("nc_lastblock_d128", 1, 2, 2, 1500, 128, torch.bfloat16, 256, 64, 7, False, 0, "planted", 12, 25),
+    Workload("c_lastblock", 1, 2, 1, 2048, 64, torch.bfloat16, 96, 32, 6, True, 256, "iid", 13, 26),
 ]
 
 
@@ -63,7 +67,7 @@ def test_forward_small_matches_oracle(w):
 
 @pytest.mark.parametrize("flags", [ha.HA_FLAG_MATERIALIZE, ha.HA_FLAG_UNFUSED,
                                    ha.HA_FLAG_MATERIALIZE | ha.HA_FLAG_UNFUSED])
-@pytest.mark.parametrize("name", ["nc_bf16_d64", "nc_ragged"])
+@pytest.mark.parametrize("name", ["nc_bf16_d64", "nc_ragged", "nc_lastblock"])
 def test_forward_variants_match_fused(flags, name):
     w = next(x for x in SMALL if x.name == name)
     q, k, v, out0, lse0 = _run(w)

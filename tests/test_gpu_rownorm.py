@@ -75,6 +75,7 @@ CASES = [
     (2, 1, 1, 512, 64, 512, 40, 5, 6, torch.bfloat16),        # one block: every draw excluded -> exact
     (1, 2, 2, 768, 64, 128, 0, 6, 7, torch.bfloat16),         # no samples: block part only
     (1, 1, 1, 1024, 64, 64, 64, 7, 8, torch.float32),         # fp32
+    (1, 2, 1, 1000, 64, 128, 96, 7, 9, torch.bfloat16),       # ragged last block
 ]
 
 

@@ -47,6 +47,8 @@ CASES = [
     oh.HAConfig(block=8, samples=40, proj_bits=5, seed=4),                  # many duplicate samples
     oh.HAConfig(block=16, samples=10, proj_bits=4, causal=True, min_seq_len=16, seed=5),
     oh.HAConfig(block=4, samples=6, proj_bits=3, causal=True, min_seq_len=8, seed=6),
+    oh.HAConfig(block=12, samples=10, proj_bits=4, seed=7),                 # ragged last block
+    oh.HAConfig(block=12, samples=8, proj_bits=4, causal=True, min_seq_len=16, seed=8),  # ragged quadrants
 ]
 
 
