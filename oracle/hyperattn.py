@@ -170,14 +170,23 @@ def _softmax_stats(S, V):
     return lse, o
 
 
-def block_part(Qs, Ks, Vs, b_eff, positions=None):
+def key_block(b_eff, n_q, n_k):
+    """Key block size b_k of a problem with n_q queries, n_k keys and query
+    blocks of b_eff (reading R18): ceil(b_eff n_k / n_q), so that query
+    block t pairs with key block t and b_k = b_eff when n_k = n_q."""
+    return -(-b_eff * n_k // n_q)
+
+
+def block_part(Qs, Ks, Vs, b_eff, positions=None, b_k=None):
     """Exact attention of sorted query p over the sorted keys of its own
-    diagonal block t = p // b_eff, i.e. keys [t b_eff, min((t+1) b_eff, ns))
+    diagonal block t = p // b_eff, i.e. keys [t b_k, min((t+1) b_k, n_k))
     (reading R9: consecutive runs of b_eff sorted positions, the last run
-    holding what remains).  Returns (lse_blk, o_blk) for ``positions`` (all
-    if None): exp(lse_blk) = sum_{j in blk} e^{S_pj},  o_blk = that softmax
-    times V."""
+    holding what remains; b_k = b_eff for square problems, R18 otherwise).
+    Returns (lse_blk, o_blk) for ``positions`` (all if None):
+    exp(lse_blk) = sum_{j in blk} e^{S_pj},  o_blk = that softmax times V."""
     ns, d = Qs.shape
+    n_k = Ks.shape[0]
+    b_k = b_eff if b_k is None else b_k
     if positions is None:
         positions = np.arange(ns)
     positions = np.asarray(positions, dtype=np.int64)
@@ -186,7 +195,11 @@ def block_part(Qs, Ks, Vs, b_eff, positions=None):
     blk = positions // b_eff
     for t in np.unique(blk):
         rows = np.nonzero(blk == t)[0]
-        lo, hi = t * b_eff, min((t + 1) * b_eff, ns)
+        lo, hi = min(t * b_k, n_k), min((t + 1) * b_k, n_k)
+        if hi <= lo:                        # a rectangular problem's query block past the keys
+            lse[rows] = -np.inf
+            o[rows] = 0.0
+            continue
         S = Qs[positions[rows]] @ Ks[lo:hi].T
         l, oo = _softmax_stats(S, Vs[lo:hi])
         lse[rows] = l
@@ -194,13 +207,15 @@ def block_part(Qs, Ks, Vs, b_eff, positions=None):
     return lse, o
 
 
-def sample_part(Qs, Ks, Vs, idx, b_eff, positions=None):
+def sample_part(Qs, Ks, Vs, idx, b_eff, positions=None, b_k=None):
     """Sampled estimate of the mass outside the row's block:
-    D_smp = (ns/m) sum_{i: idx_i // b_eff != p // b_eff} e^{S_{p, idx_i}}
-    and the matching weighted sum of value rows; duplicates count each time.
-    Returns (lse_smp, o_smp) with exp(lse_smp) = D_smp; an empty sum gives
-    lse = -inf, o = 0."""
+    D_smp = (n_k/m) sum_{i: idx_i // b_k != p // b_eff} e^{S_{p, idx_i}}
+    and the matching weighted sum of value rows; duplicates count each time
+    (b_k = b_eff for square problems).  Returns (lse_smp, o_smp) with
+    exp(lse_smp) = D_smp; an empty sum gives lse = -inf, o = 0."""
     ns, d = Qs.shape
+    n_k = Ks.shape[0]
+    b_k = b_eff if b_k is None else b_k
     if positions is None:
         positions = np.arange(ns)
     positions = np.asarray(positions, dtype=np.int64)
@@ -210,7 +225,7 @@ def sample_part(Qs, Ks, Vs, idx, b_eff, positions=None):
     idx = np.asarray(idx, dtype=np.int64)
     Ksm = Ks[idx]
     Vsm = Vs[idx]
-    col_blk = idx // b_eff
+    col_blk = idx // b_k
     lse = np.empty(len(positions))
     o = np.empty((len(positions), d))
     for c in range(0, len(positions), 4096):
@@ -219,7 +234,7 @@ def sample_part(Qs, Ks, Vs, idx, b_eff, positions=None):
         keep = (p // b_eff)[:, None] != col_blk[None, :]
         S = np.where(keep, S, -np.inf)
         l, oo = _softmax_stats(S, Vsm)
-        lse[c:c + 4096] = l + np.log(ns / m)
+        lse[c:c + 4096] = l + np.log(n_k / m)
         o[c:c + 4096] = oo
     return lse, o
 
@@ -236,36 +251,40 @@ def lse_merge(l1, o1, l2, o2):
 
 def noncausal_problem(q, k, v, rank_q, rank_k, seed, batch_idx, head, node,
                       block, samples, rows=None, parts=None):
-    """One non-causal (sub)problem of ns queries and ns keys.
+    """One non-causal (sub)problem of ns queries and n_k keys (n_k = ns
+    unless the problem is rectangular, reading R18).
 
-    q, k, v: fp64 [ns, d] rows in original order; rank_q, rank_k: bucket
-    ranks of those rows.  Returns (o, lse) for ``rows`` (local indices,
-    all if None) in original row order.  If ``parts`` is a dict it receives
-    the intermediates (perms, samples, per-part lse/o in sorted order)."""
+    q: fp64 [ns, d], k, v: fp64 [n_k, d] rows in original order; rank_q,
+    rank_k: bucket ranks of those rows.  Returns (o, lse) for ``rows``
+    (local indices, all if None) in original row order.  If ``parts`` is a
+    dict it receives the intermediates (perms, samples, per-part lse/o in
+    sorted order)."""
     ns, d = q.shape
-    if k.shape[0] != ns:
-        raise ValueError("square problems only")
+    n_k = k.shape[0]
     if ns == 0:
         return np.zeros((0, d)), np.zeros(0)
+    if n_k == 0:
+        raise ValueError("a problem with queries needs keys")
     b_eff = min(block, ns)
     if b_eff < 1:
         raise ValueError("block must be >= 1")
+    b_k = key_block(b_eff, ns, n_k)
     pq = sort_perm(rank_q)
     pk = sort_perm(rank_k)
     Qs, Ks, Vs = q[pq], k[pk], v[pk]
-    idx = sample_positions(seed, batch_idx, head, node, ns, samples)
+    idx = sample_positions(seed, batch_idx, head, node, n_k, samples)
     if rows is None:
         positions = None
     else:
         inv = np.empty(ns, dtype=np.int64)
         inv[pq] = np.arange(ns)
         positions = inv[np.asarray(rows, dtype=np.int64)]
-    lb, ob = block_part(Qs, Ks, Vs, b_eff, positions)
-    ls, osm = sample_part(Qs, Ks, Vs, idx, b_eff, positions)
+    lb, ob = block_part(Qs, Ks, Vs, b_eff, positions, b_k)
+    ls, osm = sample_part(Qs, Ks, Vs, idx, b_eff, positions, b_k)
     lse, o = lse_merge(lb, ob, ls, osm)
     if parts is not None:
         parts.update(perm_q=pq, perm_k=pk, idx=idx, lse_blk=lb, o_blk=ob,
-                     lse_smp=ls, o_smp=osm, b_eff=b_eff)
+                     lse_smp=ls, o_smp=osm, b_eff=b_eff, b_k=b_k)
     if rows is None:
         out = np.empty_like(o)
         out[pq] = o                                # unsort
@@ -407,6 +426,35 @@ def forward(q, k, v, cfg):
     B, H = q.shape[:2]
     out, lse = forward_rows(q, k, v, cfg)
     return out.reshape(B, H, q.shape[2], q.shape[3]), lse.reshape(B, H, q.shape[2])
+
+
+def forward_rect(q, k, v, cfg):
+    """Non-causal forward of a rectangular problem (reading R18): q
+    [B, H, n_q, d], k, v [B, Hkv, n_k, d] float32 arrays holding the input
+    values exactly.  Returns (out [B, H, n_q, d], lse [B, H, n_q]) in fp64."""
+    if cfg.causal:
+        raise ValueError("rectangular problems are non-causal")
+    B, H, n_q, d = q.shape
+    if k.shape[0] != B or k.shape[3] != d or v.shape != k.shape:
+        raise ValueError("shape mismatch")
+    Hkv, n_k = k.shape[1], k.shape[2]
+    if Hkv < 1 or H % Hkv:
+        raise ValueError("heads must be a multiple of kv_heads")
+    if cfg.block < 1 or cfg.samples < 0 or not 1 <= cfg.proj_bits <= 16:
+        raise ValueError("bad method arguments")
+    G = H // Hkv
+    R = projections(cfg.seed, d, cfg.proj_bits)
+    out = np.zeros((B, H, n_q, d))
+    lse = np.zeros((B, H, n_q))
+    for b in range(B):
+        for h in range(H):
+            g = h // G
+            o, l = noncausal_problem(q[b, h].astype(np.float64), k[b, g].astype(np.float64),
+                                     v[b, g].astype(np.float64), ranks(q[b, h], R), ranks(k[b, g], R),
+                                     cfg.seed, b, h, 1, cfg.block, cfg.samples)
+            out[b, h] = o
+            lse[b, h] = l
+    return out, lse
 
 
 def exact_attention(q, k, v, causal=False):

@@ -248,12 +248,12 @@ def _bruteforce_error():
     return np.max(np.abs(out - o_ref))
 
 
-def _wrong_sample_part(Qs, Ks, Vs, idx, b_eff, positions=None):      # no in-block exclusion
-    return _orig_sample_part(Qs, Ks, Vs, idx, 1 << 40, positions)
+def _wrong_sample_part(Qs, Ks, Vs, idx, b_eff, positions=None, b_k=None):  # (almost) no in-block exclusion
+    return _orig_sample_part(Qs, Ks, Vs, idx, 1, positions, 1 << 40)
 
 
-def _wrong_weight_sample_part(Qs, Ks, Vs, idx, b_eff, positions=None):  # weight 1 instead of ns/m
-    l, o = _orig_sample_part(Qs, Ks, Vs, idx, b_eff, positions)
+def _wrong_weight_sample_part(Qs, Ks, Vs, idx, b_eff, positions=None, b_k=None):  # weight 1 instead of ns/m
+    l, o = _orig_sample_part(Qs, Ks, Vs, idx, b_eff, positions, b_k)
     return l - np.log(Qs.shape[0] / len(idx)), o
 
 
@@ -277,7 +277,7 @@ def test_planted_mistakes_are_caught(monkeypatch, mutant):
     elif mutant == "transposed_kv":
         orig = hyperattn.block_part
         monkeypatch.setattr(hyperattn, "block_part",
-                            lambda Qs, Ks, Vs, b, positions=None: orig(Qs, Vs, Ks, b, positions))
+                            lambda Qs, Ks, Vs, b, positions=None, b_k=None: orig(Qs, Vs, Ks, b, positions, b_k))
     assert _bruteforce_error() > 1e-6
 
 
