@@ -44,6 +44,8 @@ _SIGNATURES = {
     "hyperattn_rownorm_samples": (_c_int, [_vp, _vp] + [_c_int] * 5 + [_c_u64, _vp, _vp, _vp]),
     "hyperattn_column_sqmass": (_c_int, [_vp, _vp, _vp] + [_c_int] * 8 + [_vp, _vp, _vp]),
     "hyperattn_residual_ratio": (_c_int, [_vp, _vp, _vp, _c_i64, _c_int, _vp, _vp]),
+    "hyperattn_rect_workspace_bytes": (_c_size, [_c_int] * 10),
+    "hyperattn_forward_rect": (_c_int, [_vp, _vp, _vp] + [_c_int] * 10 + [_c_u64, _vp, _vp, _vp, _c_size, _vp]),
     "hyperattn_timing_enable": (_c_int, [_c_int]),
     "hyperattn_timing_read": (_c_int, [_vp, _vp]),
 }
@@ -151,6 +153,30 @@ def forward(q, k, v, *, block, samples, proj_bits, causal=False, min_seq_len=0, 
     _call("hyperattn_forward_ex", _ptr(q), _ptr(k), _ptr(v), dt, B, n, d, H, Hkv, block, samples,
           proj_bits, int(bool(causal)), min_seq_len, ctypes.c_uint64(seed), flags, _ptr(out),
           _ptr(lse), _ptr(workspace), workspace.numel(), _stream(dev))
+    return out, lse
+
+
+def forward_rect(q, k, v, *, block, samples, proj_bits, seed=0, out=None, lse=None, workspace=None):
+    """Non-causal forward of a rectangular problem: q [B, H, n_q, d], k, v
+    [B, Hkv, n_k, d] (bf16 or fp32).  Returns (out like q, lse [B, H, n_q])."""
+    _need(q, "q")
+    dev = q.device
+    _need(k, "k", q.dtype, dev)
+    _need(v, "v", q.dtype, dev)
+    if q.dim() != 4 or k.dim() != 4 or k.shape != v.shape or k.shape[0] != q.shape[0] or k.shape[3] != q.shape[3]:
+        raise ValueError("q must be [B, H, n_q, d] and k, v [B, Hkv, n_k, d]")
+    B, H, nq, d = q.shape
+    Hkv, nk = k.shape[1], k.shape[2]
+    dt = _dtype_code(q.dtype)
+    if out is None:
+        out = torch.empty_like(q)
+    if lse is None:
+        lse = torch.empty((B, H, nq), dtype=torch.float32, device=dev)
+    wsb = lib().hyperattn_rect_workspace_bytes(B, nq, nk, d, H, Hkv, block, samples, proj_bits, dt)
+    if workspace is None or workspace.numel() < wsb:
+        workspace = torch.empty(max(wsb, 256), dtype=torch.uint8, device=dev)
+    _call("hyperattn_forward_rect", _ptr(q), _ptr(k), _ptr(v), dt, B, nq, nk, d, H, Hkv, block, samples, proj_bits,
+          ctypes.c_uint64(seed), _ptr(out), _ptr(lse), _ptr(workspace), workspace.numel(), _stream(dev))
     return out, lse
 
 

@@ -431,6 +431,112 @@ static int forward_impl(const void* q, const void* k, const void* v, Shape sh, u
   return HA_OK;
 }
 
+// ---- rectangular non-causal problems ----------------------------------------------
+// n_q queries and n_k keys per head: query blocks of b_eff = min(block, n_q)
+// sorted positions, key blocks of b_k = ceil(b_eff n_k / n_q), query block t
+// paired with key block t; samples uniform over the n_k keys, weight n_k / m.
+
+struct RectPlan {
+  float* R;
+  uint16_t* rank_q;
+  uint16_t* rank_k;
+  int32_t* perm_q;
+  int32_t* perm_k;
+  int32_t* sidx;
+  void* sort_ws;
+  size_t sort_ws_bytes;
+  size_t total;
+};
+
+static RectPlan rect_plan(const Shape& sh, int n_k, void* ws, size_t cap) {
+  RectPlan pl{};
+  Carve cv(ws, cap);
+  const int64_t BH = static_cast<int64_t>(sh.batch) * sh.heads;
+  const int64_t BK = static_cast<int64_t>(sh.batch) * sh.kv_heads;
+  pl.R = cv.take<float>(static_cast<size_t>(sh.r) * sh.d);
+  pl.rank_q = cv.take<uint16_t>(BH * sh.n);
+  pl.rank_k = cv.take<uint16_t>(BK * n_k);
+  pl.perm_q = cv.take<int32_t>(BH * sh.n);
+  pl.perm_k = cv.take<int32_t>(BK * n_k);
+  pl.sidx = cv.take<int32_t>(BH * (sh.samples > 0 ? sh.samples : 1));
+  const size_t a = sort_ws_bytes(BH, sh.n, 1, sh.r), b = sort_ws_bytes(BK, n_k, 1, sh.r);
+  pl.sort_ws_bytes = a > b ? a : b;
+  pl.sort_ws = cv.take<char>(pl.sort_ws_bytes);
+  pl.total = align_up(cv.used, 256) + 256;
+  return pl;
+}
+
+static int rect_validate(Shape& sh, int n_k) {
+  HA_TRY(validate(sh));
+  if (n_k < 0 || (sh.n > 0 && n_k == 0)) {
+    set_error("rectangular problem: n_k = %d (queries need keys)", n_k);
+    return HA_EINVAL;
+  }
+  if (static_cast<int64_t>(n_k) * sh.d * 4 >= (int64_t(1) << 32) ||
+      static_cast<int64_t>(sh.n) * sh.d * 4 >= (int64_t(1) << 32)) {
+    set_error("rectangular problem: one head spans 4 GiB or more");
+    return HA_EUNSUPPORTED;
+  }
+  return HA_OK;
+}
+
+static int forward_rect_impl(const void* q, const void* k, const void* v, Shape sh, int n_k, uint64_t seed,
+                             void* out, float* lse, void* ws, size_t ws_bytes, hipStream_t s) {
+  HA_TRY(rect_validate(sh, n_k));
+  if (sh.n == 0 || sh.batch == 0 || sh.heads == 0) return HA_OK;
+  if (!q || !k || !v || !out) {
+    set_error("null q, k, v or out");
+    return HA_EINVAL;
+  }
+  const size_t need = rect_plan(sh, n_k, nullptr, 0).total;
+  if (!ws || ws_bytes < need) {
+    set_error("workspace of %zu bytes < %zu required", ws_bytes, need);
+    return HA_EWORKSPACE;
+  }
+  if (reinterpret_cast<uintptr_t>(ws) % 256) {
+    set_error("workspace must be 256-byte aligned");
+    return HA_EINVAL;
+  }
+  const RectPlan pl = rect_plan(sh, n_k, ws, ws_bytes);
+  const int64_t BH = static_cast<int64_t>(sh.batch) * sh.heads;
+  const int64_t BK = static_cast<int64_t>(sh.batch) * sh.kv_heads;
+  HA_TRY(launch_projections(seed, sh.d, sh.r, pl.R, s));
+  HA_TRY(launch_hash(q, sh.dtype, BH * sh.n, sh.d, sh.r, pl.R, pl.rank_q, s));
+  HA_TRY(launch_hash(k, sh.dtype, BK * n_k, sh.d, sh.r, pl.R, pl.rank_k, s));
+  HA_TRY(launch_sort(pl.rank_q, BH, sh.n, sh.n, 0, sh.n, 1, sh.r, pl.perm_q, pl.sort_ws, pl.sort_ws_bytes, s));
+  HA_TRY(launch_sort(pl.rank_k, BK, n_k, n_k, 0, n_k, 1, sh.r, pl.perm_k, pl.sort_ws, pl.sort_ws_bytes, s));
+  HA_TRY(launch_sample_indices(seed, sh.batch, sh.heads, 1, 1, n_k, sh.samples, pl.sidx, s));
+  AttnParams ap;
+  ap.q = q;
+  ap.k = k;
+  ap.v = v;
+  ap.dtype = sh.dtype;
+  ap.d = sh.d;
+  ap.n = sh.n;
+  ap.n_k = n_k;
+  ap.H = sh.heads;
+  ap.Hkv = sh.kv_heads;
+  ap.BH = static_cast<int>(BH);
+  ap.kind = kKindSorted;
+  ap.pieces = 1;
+  ap.seg = sh.n;
+  ap.seg_k = n_k;
+  ap.stride = sh.n;
+  ap.perm_q = pl.perm_q;
+  ap.perm_k = pl.perm_k;
+  ap.b_eff = sh.block < sh.n ? sh.block : sh.n;
+  ap.b_k = static_cast<int>((static_cast<int64_t>(ap.b_eff) * n_k + sh.n - 1) / sh.n);
+  ap.sidx = pl.sidx;
+  ap.m = sh.samples;
+  ap.log2w = sh.samples > 0 ? static_cast<float>(std::log2(static_cast<double>(n_k) / sh.samples)) : 0.f;
+  ap.out_mode = kOutFinal;
+  ap.out = out;
+  ap.lse = lse;
+  ap.use_block = 1;
+  ap.use_samples = sh.samples > 0;
+  return launch_attention(ap, HA_K_ATTEND, s);
+}
+
 // ---- backward -------------------------------------------------------------------
 // Same projections, hashes, sorts and samples as the forward (recomputed
 // from the seed), then the per-row statistics (lse, D = rowsum(dO * O)) and,
@@ -647,6 +753,22 @@ int hyperattn_forward(const void* q, const void* k, const void* v, int dtype, in
   return hyperattn_forward_ex(q, k, v, dtype, batch, n, d, heads, kv_heads, block, samples,
                               proj_bits, causal, min_seq_len, seed, 0, out, lse, workspace,
                               workspace_bytes, stream);
+}
+
+size_t hyperattn_rect_workspace_bytes(int batch, int n_q, int n_k, int d, int heads, int kv_heads, int block,
+                                      int samples, int proj_bits, int dtype) {
+  Shape sh{batch, n_q, d, heads, kv_heads, block, samples, proj_bits, 0, 0, dtype, 0};
+  if (rect_validate(sh, n_k) != HA_OK) return 0;
+  return rect_plan(sh, n_k, nullptr, 0).total;
+}
+
+int hyperattn_forward_rect(const void* q, const void* k, const void* v, int dtype, int batch, int n_q, int n_k,
+                           int d, int heads, int kv_heads, int block, int samples, int proj_bits, uint64_t seed,
+                           void* out, float* lse, void* workspace, size_t workspace_bytes, void* stream) {
+  g_last_error.clear();
+  Shape sh{batch, n_q, d, heads, kv_heads, block, samples, proj_bits, 0, 0, dtype, 0};
+  return forward_rect_impl(q, k, v, sh, n_k, seed, out, lse, workspace, workspace_bytes,
+                           static_cast<hipStream_t>(stream));
 }
 
 size_t hyperattn_backward_workspace_bytes(int batch, int n, int d, int heads, int kv_heads, int block,

@@ -121,13 +121,13 @@ __global__ __launch_bounds__(64 * NW, (min_waves<T, D, KIND, NW, QPW>())) void a
   const int64_t kpiece = static_cast<int64_t>(bkv) * p.pieces + piece;   // [BHkv][pieces]
 
   const T* qbase = static_cast<const T*>(p.q) + static_cast<int64_t>(bh) * p.n * D;
-  const T* kbase = static_cast<const T*>(p.k) + static_cast<int64_t>(bkv) * p.n * D;
-  const T* vbase = static_cast<const T*>(p.v) + static_cast<int64_t>(bkv) * p.n * D;
+  const T* kbase = static_cast<const T*>(p.k) + static_cast<int64_t>(bkv) * p.n_k * D;
+  const T* vbase = static_cast<const T*>(p.v) + static_cast<int64_t>(bkv) * p.n_k * D;
   const bool mat = !LEAF && p.qs != nullptr;   // materialised sorted copies
-  const T* ksb = mat ? static_cast<const T*>(p.ks) + kpiece * p.seg * D : nullptr;
-  const T* vsb = mat ? static_cast<const T*>(p.vs) + kpiece * p.seg * D : nullptr;
+  const T* ksb = mat ? static_cast<const T*>(p.ks) + kpiece * p.seg_k * D : nullptr;
+  const T* vsb = mat ? static_cast<const T*>(p.vs) + kpiece * p.seg_k * D : nullptr;
   const int32_t* pq = (!LEAF && p.perm_q) ? p.perm_q + qpiece * p.seg : nullptr;
-  const int32_t* pk = (!LEAF && p.perm_k) ? p.perm_k + kpiece * p.seg : nullptr;
+  const int32_t* pk = (!LEAF && p.perm_k) ? p.perm_k + kpiece * p.seg_k : nullptr;
   const int qrow0 = p.q_first + piece * p.stride;
   const int krow0 = p.k_first + piece * p.stride;
 
@@ -138,8 +138,10 @@ __global__ __launch_bounds__(64 * NW, (min_waves<T, D, KIND, NW, QPW>())) void a
     if (LEAF) {
       ka1 = qend;
     } else {
-      ka0 = (q0 / p.b_eff) * p.b_eff;
-      ka1 = min(((qend - 1) / p.b_eff + 1) * p.b_eff, p.seg);   // the last block may be short
+      // query block t pairs with key block t (key blocks of b_k; the last
+      // block may be short, and a rectangular problem's may be empty)
+      ka1 = min(((qend - 1) / p.b_eff + 1) * p.b_k, p.seg_k);
+      ka0 = min((q0 / p.b_eff) * p.b_k, ka1);
     }
   }
   const bool samp = !LEAF && p.use_samples && p.m > 0;
@@ -253,7 +255,7 @@ __global__ __launch_bounds__(64 * NW, (min_waves<T, D, KIND, NW, QPW>())) void a
           spos[i] = spi;
           raw[i] = first ? sr : key_row(spi);
         }
-        const uint64_t keep = __ballot(i < p.m && (samp_multi || (spi / p.b_eff) != tq));
+        const uint64_t keep = __ballot(i < p.m && (samp_multi || (spi / p.b_k) != tq));
         if (lane == 0) ccount[c / 64] = __popcll(keep);
       }
       __syncthreads();
@@ -264,7 +266,7 @@ __global__ __launch_bounds__(64 * NW, (min_waves<T, D, KIND, NW, QPW>())) void a
           int base = 0;
           for (int k = 0; k < c / 64; ++k) base += ccount[k];
           const int i = c + lane;
-          const bool keep = i < p.m && (spos[i] / p.b_eff) != tq;
+          const bool keep = i < p.m && (spos[i] / p.b_k) != tq;
           const uint64_t bal = __ballot(keep);
           const uint64_t lower = lane == 0 ? 0ull : (~0ull >> (64 - lane));
           if (keep) srow[base + __popcll(bal & lower)] = rrow[i];
@@ -392,11 +394,11 @@ __global__ __launch_bounds__(64 * NW, (min_waves<T, D, KIND, NW, QPW>())) void a
           const int j = 32 * kt + 8 * (r >> 2) + 4 * h2 + (r & 3);
           bool ok = j < kcnt;
           if (isB) {
-            if (samp_multi) ok = ok && (spos[kb + min(j, kcnt - 1)] / p.b_eff) != row_blk;
+            if (samp_multi) ok = ok && (spos[kb + min(j, kcnt - 1)] / p.b_k) != row_blk;
           } else if (LEAF) {
             ok = ok && (kb + j <= ql[0]);
           } else if (multi_block) {
-            ok = ok && ((kb + j) / p.b_eff) == row_blk;
+            ok = ok && ((kb + j) / p.b_k) == row_blk;
           }
           if (!ok) sv[r] = -INFINITY;
         }
@@ -548,11 +550,11 @@ __global__ __launch_bounds__(64 * NW, (min_waves<T, D, KIND, NW, QPW>())) void a
               const int j = 32 * kt + 8 * (r >> 2) + 4 * h2 + (r & 3);
               bool ok = j < kcnt;
               if (isB) {
-                if (samp_multi) ok = ok && (spos[kb + min(j, kcnt - 1)] / p.b_eff) != row_blk;
+                if (samp_multi) ok = ok && (spos[kb + min(j, kcnt - 1)] / p.b_k) != row_blk;
               } else if (LEAF) {
                 ok = ok && (kb + j <= ql[u]);
               } else if (multi_block) {
-                ok = ok && ((kb + j) / p.b_eff) == row_blk;
+                ok = ok && ((kb + j) / p.b_k) == row_blk;
               }
               if (!ok) s[kt][u][r] = -INFINITY;
             }
@@ -843,8 +845,8 @@ static int launch_attn_t(const AttnParams& p, hipStream_t s) {
   if (KIND == kKindSorted) {
     if (p.use_block) {
       // a workgroup's queries span at most (TQ - 1) / b_eff + 2 blocks
-      const int64_t span = static_cast<int64_t>((G::TQ - 1) / p.b_eff + 2) * p.b_eff;
-      const int64_t cap = span < p.seg ? span : p.seg;
+      const int64_t span = static_cast<int64_t>((G::TQ - 1) / p.b_eff + 2) * p.b_k;
+      const int64_t cap = span < p.seg_k ? span : p.seg_k;
       if (cap <= kBlockListCap) q.bcap = static_cast<int>(cap);
     }
     lds += list_bytes(q.bcap, p.m);
@@ -912,13 +914,21 @@ static int launch_attn_d(const AttnParams& p, hipStream_t s) {
   return HA_EINVAL;
 }
 
-int launch_attention(const AttnParams& p, int timing_kind, hipStream_t s) {
+int launch_attention(const AttnParams& p_in, int timing_kind, hipStream_t s) {
+  AttnParams p = p_in;                       // key geometry defaults to the query side's
+  if (p.n_k == 0) p.n_k = p.n;
+  if (p.seg_k == 0) p.seg_k = p.seg;
+  if (p.b_k == 0) p.b_k = p.b_eff;
   if (p.seg == 0 || p.BH == 0 || p.pieces == 0) return HA_OK;
+  if (p.seg_k == 0 || p.b_k < 1 || (p.kind == kKindLeaf && (p.seg_k != p.seg || p.b_k != p.b_eff))) {
+    set_error("attention: bad key geometry (seg_k %d, b_k %d)", p.seg_k, p.b_k);
+    return HA_EINVAL;
+  }
   if (p.m > kMaxSamples) {
     set_error("attention: samples %d > %d", p.m, kMaxSamples);
     return HA_EUNSUPPORTED;
   }
-  const int64_t head_bytes = static_cast<int64_t>(p.n) * p.d * (p.dtype == HA_BF16 ? 2 : 4);
+  const int64_t head_bytes = static_cast<int64_t>(p.n > p.n_k ? p.n : p.n_k) * p.d * (p.dtype == HA_BF16 ? 2 : 4);
   if (head_bytes >= (int64_t(1) << 32)) {
     set_error("attention: one head of q/k/v spans %lld bytes (limit 4 GiB)", static_cast<long long>(head_bytes));
     return HA_EUNSUPPORTED;

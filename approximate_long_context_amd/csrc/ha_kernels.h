@@ -47,7 +47,8 @@ struct AttnParams {
   const void* v = nullptr;
   int dtype = HA_BF16;
   int d = 64;
-  int n = 0;             // rows per head in q, k, v
+  int n = 0;             // rows per head in q (and in k, v unless n_k is set)
+  int n_k = 0;           // rows per head in k, v (launch_attention: 0 -> n)
   int H = 1, Hkv = 1;    // query / kv heads per batch entry
   int BH = 0;            // batch * H
   // problems: `pieces` per head, each of `seg` queries and `seg` keys.
@@ -55,6 +56,7 @@ struct AttnParams {
   // k_first + i*stride + [0, seg) (through the permutations when given).
   int pieces = 1;
   int seg = 0;
+  int seg_k = 0;         // keys per problem (0 -> seg; rectangular problems)
   int q_first = 0, k_first = 0, stride = 0;
   const int32_t* perm_q = nullptr;   // [BH][pieces][seg]  sorted pos -> row
   const int32_t* perm_k = nullptr;   // [BHkv][pieces][seg]
@@ -64,7 +66,8 @@ struct AttnParams {
   const void* ks = nullptr;
   const void* vs = nullptr;
   int kind = kKindSorted;
-  int b_eff = 1;
+  int b_eff = 1;         // query block size
+  int b_k = 0;           // key block size (0 -> b_eff; rectangular problems)
   int bcap = 0;          // LDS block key list capacity (set by the launcher)
   int use_block = 1;
   int use_samples = 1;

@@ -148,6 +148,30 @@ int hyperattn_forward_ex(const void* q, const void* k, const void* v, int dtype,
                          uint64_t seed, int flags, void* out, float* lse,
                          void* workspace, size_t workspace_bytes, void* stream);
 
+/* ------------------------------------------------------------------------
+ * Rectangular non-causal problems: n_q queries and n_k keys per head (the
+ * pages are silent on rectangular shapes; the reading keeps the square
+ * case's structure).  Query blocks are runs of b = min(block, n_q) sorted
+ * query positions, key blocks runs of b_k = ceil(b n_k / n_q) sorted key
+ * positions (b_k = b when n_k = n_q); query block t pairs with key block t
+ * (a short or empty last key block is allowed); `samples` key positions
+ * are drawn uniformly over the n_k keys (hyperattn_sample_indices with
+ * ns = n_k) with weight n_k / samples and excluded from the rows of their
+ * block.
+ * ------------------------------------------------------------------------ */
+
+/* Workspace bytes for hyperattn_forward_rect (0 for invalid arguments). */
+size_t hyperattn_rect_workspace_bytes(int batch, int n_q, int n_k, int d, int heads, int kv_heads, int block,
+                                      int samples, int proj_bits, int dtype);
+
+/* As hyperattn_forward (non-causal) with q [batch, heads, n_q, d], k, v
+ * [batch, kv_heads, n_k, d], out [batch, heads, n_q, d], lse [batch,
+ * heads, n_q].  Errors: as hyperattn_forward; HA_EINVAL when n_q > 0 and
+ * n_k = 0. */
+int hyperattn_forward_rect(const void* q, const void* k, const void* v, int dtype, int batch, int n_q, int n_k,
+                           int d, int heads, int kv_heads, int block, int samples, int proj_bits, uint64_t seed,
+                           void* out, float* lse, void* workspace, size_t workspace_bytes, void* stream);
+
 /* Squared row norms for the row-norm variant: w[i] = ||x_i||^2 in fp32,
  * each square rounded, groups of 8 consecutive squares summed by halving
  * (pairs 4, 2, 1 apart), the group sums by halving; no multiply-add
