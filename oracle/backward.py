@@ -30,34 +30,34 @@ gradients against finite differences of it and, for W = 1, against autograd.
 import numpy as np
 
 from .gauss import projections
-from .hyperattn import (_check, causal_levels, ranks, sample_positions, sort_perm)
+from .hyperattn import (_check, causal_levels, key_block, ranks, sample_positions, sort_perm)
 
 
 def noncausal_weights(rank_q, rank_k, seed, batch_idx, head, node, block, samples):
-    """W [ns, ns] (rows: queries, columns: keys, both in original local
+    """W [n_q, n_k] (rows: queries, columns: keys, both in original local
     order) of one non-causal problem: 1 inside the row's diagonal block of
-    the sorted matrix, plus ns/m per sample at the key's sorted position
-    when that position lies outside the row's block."""
-    ns = len(rank_q)
-    if len(rank_k) != ns:
-        raise ValueError("square problems only")
-    if ns == 0:
-        return np.zeros((0, 0))
+    the sorted matrix (query blocks of b, key blocks of b_k, reading R18),
+    plus n_k/m per sample at the key's sorted position when that position
+    lies outside the row's block."""
+    ns, n_k = len(rank_q), len(rank_k)
+    if ns == 0 or n_k == 0:
+        return np.zeros((ns, n_k))
     b_eff = min(block, ns)
+    b_k = key_block(b_eff, ns, n_k)
     pq = sort_perm(rank_q)
     pk = sort_perm(rank_k)
     spos_q = np.empty(ns, dtype=np.int64)
     spos_q[pq] = np.arange(ns)                      # sorted position of each query row
-    spos_k = np.empty(ns, dtype=np.int64)
-    spos_k[pk] = np.arange(ns)
+    spos_k = np.empty(n_k, dtype=np.int64)
+    spos_k[pk] = np.arange(n_k)
     blk_q = spos_q // b_eff
-    blk_k = spos_k // b_eff
+    blk_k = spos_k // b_k
     same = blk_q[:, None] == blk_k[None, :]
     W = same.astype(np.float64)
     if samples > 0:
-        idx = sample_positions(seed, batch_idx, head, node, ns, samples)
-        count = np.bincount(idx, minlength=ns)[spos_k]   # samples on each key row
-        W += np.where(same, 0.0, (ns / samples) * count[None, :])
+        idx = sample_positions(seed, batch_idx, head, node, n_k, samples)
+        count = np.bincount(idx, minlength=n_k)[spos_k]   # samples on each key row
+        W += np.where(same, 0.0, (n_k / samples) * count[None, :])
     return W
 
 

@@ -308,12 +308,11 @@ def _exact_causal_rows(q, k, v, rows):
 
 
 def causal_levels(n, min_seq_len):
-    """Number of recursion levels: halvings until a span is <= min_seq_len."""
+    """Depth of the recursion: splits until every span is <= min_seq_len
+    (the longest span at each depth has ceil(ns / 2) rows)."""
     L, ns = 0, n
     while ns > min_seq_len:
-        if ns % 2:
-            raise ValueError(f"causal split of odd length {ns}")
-        ns //= 2
+        ns = ns - ns // 2
         L += 1
     return L
 
@@ -321,11 +320,13 @@ def causal_levels(n, min_seq_len):
 def causal_problem(q, k, v, rank_q, rank_k, seed, batch_idx, head, cfg, rows=None):
     """Causal HyperAttention of one head.  causal(lo, hi, node): a span of
     length <= min_seq_len is exact causal attention; otherwise, with
-    mid = (lo + hi) / 2, causal(lo, mid, 2 node) and causal(mid, hi,
+    mid = lo + (hi - lo) // 2 (reading R19: an odd span gives its right
+    half the extra row), causal(lo, mid, 2 node) and causal(mid, hi,
     2 node + 1) recurse, and rows [mid, hi) are merged (deepest level
     first) with the non-causal problem of queries [mid, hi) over keys
-    [lo, mid), with this node's samples.  Ranks come from the one hash of
-    the whole sequence (one projection matrix for all nodes)."""
+    [lo, mid) (rectangular when the span is odd, reading R18), with this
+    node's samples.  Ranks come from the one hash of the whole sequence
+    (one projection matrix for all nodes)."""
     n, d = q.shape
     s = cfg.min_seq_len
     all_rows = np.arange(n) if rows is None else np.sort(np.asarray(rows, dtype=np.int64))
@@ -343,8 +344,6 @@ def causal_problem(q, k, v, rank_q, rank_k, seed, batch_idx, head, cfg, rows=Non
                 o_out[pos_of[int(r)]] = o[j]
                 l_out[pos_of[int(r)]] = l[j]
             return
-        if ns % 2:
-            raise ValueError(f"causal split of odd length {ns}")
         mid = lo + ns // 2
         rec(lo, mid, 2 * node, want[want < mid])
         upper = want[want >= mid]

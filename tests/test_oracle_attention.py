@@ -57,7 +57,8 @@ def test_full_block_is_exact_attention(n, block, m):
     assert np.max(np.abs(lse - ex_lse)) < 1e-12
 
 
-@pytest.mark.parametrize("n,s,block", [(64, 64, 8), (64, 100, 8), (128, 16, 64), (96, 12, 48)])
+@pytest.mark.parametrize("n,s,block", [(64, 64, 8), (64, 100, 8), (128, 16, 64), (96, 12, 48),
+                                       (45, 6, 64), (101, 10, 51)])    # odd splits (R19)
 def test_causal_special_cases_are_exact_causal(n, s, block):
     rng = np.random.default_rng(n + s + block)
     q, k, v = _rand_qkv(rng, 1, 2, 1, n, 8, scale=0.8)
@@ -218,8 +219,8 @@ def test_argument_errors():
     with pytest.raises(ValueError):
         oracle.forward(q, k, v, HAConfig(block=4, samples=1, proj_bits=17))
     q, k, v = _rand_qkv(rng, 1, 2, 1, 48, 8)
-    with pytest.raises(ValueError):       # 48 -> 24 -> 12 -> 6 -> 3 (odd, > 2)
-        oracle.forward(q, k, v, HAConfig(block=3, samples=1, proj_bits=3, causal=True, min_seq_len=2))
+    # 48 -> 24 -> 12 -> 6 -> 3 -> (1, 2): odd splits are valid (R19)
+    oracle.forward(q, k, v, HAConfig(block=3, samples=1, proj_bits=3, causal=True, min_seq_len=2))
 
 
 def test_empty_sequence():

@@ -58,9 +58,10 @@ def _weights(rq, rk, cfg):
     return ob.noncausal_weights(rq, rk, cfg.seed, 0, 0, 1, cfg.block, cfg.samples)
 
 
+@pytest.mark.parametrize("n", [64, 45])                                   # 45: odd causal splits
 @pytest.mark.parametrize("cfg", CASES)
-def test_weights_reproduce_the_forward(cfg):
-    q, k, v = _inputs(64, 8, cfg.seed)
+def test_weights_reproduce_the_forward(cfg, n):
+    q, k, v = _inputs(n, 8, cfg.seed)
     rq, rk = _ranks(q, k, cfg.proj_bits, cfg.seed)
     o, lse = _fwd(q, k, v, rq, rk, cfg)
     W = _weights(rq, rk, cfg)
