@@ -18,6 +18,7 @@
 // host synchronisation inside.
 #include <hip/hip_runtime.h>
 
+#include <algorithm>
 #include <cmath>
 #include <cstdarg>
 #include <cstdio>
@@ -119,8 +120,9 @@ void timing_end(int kind, hipStream_t s) {
 
 struct Shape {
   int batch, n, d, heads, kv_heads, block, samples, r, causal, s, dtype, flags;
-  int levels = 0;    // causal levels
-  int leaf = 0;      // causal leaf length
+  int levels = 0;    // causal levels (every split even)
+  int leaf = 0;      // causal leaf length (every split even)
+  bool odd = false;  // causal: some span splits unevenly (node-by-node driver)
 };
 
 static int validate(Shape& sh) {
@@ -172,17 +174,17 @@ static int validate(Shape& sh) {
   }
   if (sh.n == 0) return HA_OK;
   if (!sh.causal) return HA_OK;
+  // even splits all the way down: one launch per level; otherwise (an odd
+  // span, split with the extra row on the right) one launch per node
   int ns = sh.n, L = 0;
+  sh.odd = false;
   while (ns > sh.s) {
-    if (ns % 2) {
-      set_error("causal split of odd length %d", ns);
-      return HA_ESHAPE;
-    }
-    ns /= 2;
+    if (ns % 2) sh.odd = true;
+    ns = ns - ns / 2;
     ++L;
   }
-  sh.levels = L;
-  sh.leaf = ns;
+  sh.levels = sh.odd ? 0 : L;
+  sh.leaf = sh.odd ? 0 : ns;
   return HA_OK;
 }
 
@@ -241,6 +243,16 @@ static Plan make_plan(const Shape& sh, void* ws, size_t cap) {
       pl.rn_cum = cv.take<int64_t>(BK * sh.n);
       pl.rn_sidx = cv.take<int32_t>(BH * (sh.samples > 0 ? sh.samples : 1));
     }
+  } else if (sh.odd) {
+    const int half = sh.n - sh.n / 2;         // the longest quadrant side
+    pl.acc_o = cv.take<float>(BH * sh.n * sh.d);
+    pl.acc_lse = cv.take<float>(BH * sh.n);
+    pl.perm_q = cv.take<int32_t>(BH * half);
+    pl.perm_k = cv.take<int32_t>(BK * half);
+    pl.sidx = cv.take<int32_t>(BH * (sh.samples > 0 ? sh.samples : 1));
+    const size_t a = sort_ws_bytes(BH, half, 1, sh.r), b = sort_ws_bytes(BK, half, 1, sh.r);
+    pl.sort_ws_bytes = a > b ? a : b;
+    pl.sort_ws = cv.take<char>(pl.sort_ws_bytes);
   } else {
     if (sh.levels > 0) {
       pl.acc_o = cv.take<float>(BH * sh.n * sh.d);
@@ -263,6 +275,84 @@ static Plan make_plan(const Shape& sh, void* ws, size_t cap) {
   }
   pl.total = align_up(cv.used, 256) + 256;
   return pl;
+}
+
+// Causal recursion node by node (some span has odd length): the exact
+// leaves first, then every node's quadrant (queries [mid, hi), keys
+// [lo, mid), rectangular when the span is odd) deepest first, merged into the
+// accumulator.  Rows become final in the first leaf and in the quadrants of
+// the nodes on the leftmost path (no shallower node holds them in its right
+// half), which write the output directly.
+static int forward_causal_nodes(const AttnParams& ap, const Shape& sh, const Plan& pl, uint64_t seed,
+                                hipStream_t s) {
+  struct Node {
+    int lo, mid, hi, id, depth;
+    bool leftmost;
+  };
+  std::vector<Node> leaves, quads;
+  std::vector<Node> todo{{0, 0, sh.n, 1, 0, true}};
+  while (!todo.empty()) {
+    Node nd = todo.back();
+    todo.pop_back();
+    const int ns = nd.hi - nd.lo;
+    if (ns <= sh.s) {
+      leaves.push_back(nd);
+      continue;
+    }
+    nd.mid = nd.lo + ns / 2;
+    quads.push_back(nd);
+    todo.push_back({nd.lo, 0, nd.mid, 2 * nd.id, nd.depth + 1, nd.leftmost});
+    todo.push_back({nd.mid, 0, nd.hi, 2 * nd.id + 1, nd.depth + 1, false});
+  }
+  std::stable_sort(quads.begin(), quads.end(), [](const Node& a, const Node& b) { return a.depth > b.depth; });
+  const int64_t BH = static_cast<int64_t>(sh.batch) * sh.heads;
+  const int64_t BK = static_cast<int64_t>(sh.batch) * sh.kv_heads;
+  for (const Node& nd : leaves) {
+    AttnParams lp = ap;
+    lp.kind = kKindLeaf;
+    lp.pieces = 1;
+    lp.seg = nd.hi - nd.lo;
+    lp.stride = 0;
+    lp.q_first = nd.lo;
+    lp.k_first = nd.lo;
+    lp.b_eff = lp.seg;
+    lp.use_block = 1;
+    lp.use_samples = 0;
+    lp.out_mode = kOutLeaf;
+    lp.final_piece = nd.leftmost ? 0 : -1;
+    lp.acc_o = pl.acc_o;
+    lp.acc_lse = pl.acc_lse;
+    HA_TRY(launch_attention(lp, HA_K_LEAF, s));
+  }
+  for (const Node& nd : quads) {
+    const int nq = nd.hi - nd.mid, nk = nd.mid - nd.lo;
+    HA_TRY(launch_sort(pl.rank_q, BH, sh.n, nq, nd.mid, nq, 1, sh.r, pl.perm_q, pl.sort_ws, pl.sort_ws_bytes, s));
+    HA_TRY(launch_sort(pl.rank_k, BK, sh.n, nk, nd.lo, nk, 1, sh.r, pl.perm_k, pl.sort_ws, pl.sort_ws_bytes, s));
+    HA_TRY(launch_sample_indices(seed, sh.batch, sh.heads, nd.id, 1, nk, sh.samples, pl.sidx, s));
+    AttnParams qp = ap;
+    qp.kind = kKindSorted;
+    qp.pieces = 1;
+    qp.seg = nq;
+    qp.seg_k = nk;
+    qp.q_first = nd.mid;
+    qp.k_first = nd.lo;
+    qp.stride = 0;
+    qp.perm_q = pl.perm_q;
+    qp.perm_k = pl.perm_k;
+    qp.b_eff = sh.block < nq ? sh.block : nq;
+    qp.b_k = static_cast<int>((static_cast<int64_t>(qp.b_eff) * nk + nq - 1) / nq);
+    qp.use_block = 1;
+    qp.use_samples = sh.samples > 0;
+    qp.sidx = pl.sidx;
+    qp.m = sh.samples;
+    qp.log2w = sh.samples > 0 ? static_cast<float>(std::log2(static_cast<double>(nk) / sh.samples)) : 0.f;
+    qp.out_mode = kOutMerge;
+    qp.final_piece = nd.leftmost ? 0 : -1;
+    qp.acc_o = pl.acc_o;
+    qp.acc_lse = pl.acc_lse;
+    HA_TRY(launch_attention(qp, HA_K_QUADRANT, s));
+  }
+  return HA_OK;
 }
 
 static int forward_impl(const void* q, const void* k, const void* v, Shape sh, uint64_t seed,
@@ -386,6 +476,7 @@ static int forward_impl(const void* q, const void* k, const void* v, Shape sh, u
   }
 
   // ---- causal ----
+  if (sh.odd) return forward_causal_nodes(ap, sh, pl, seed, s);
   AttnParams lp = ap;
   lp.kind = kKindLeaf;
   lp.pieces = sh.n / sh.leaf;
@@ -614,6 +705,10 @@ static int backward_impl(const void* q, const void* k, const void* v, const void
     set_error("backward: bf16 inputs only");
     return HA_EUNSUPPORTED;
   }
+  if (sh.causal && sh.odd) {
+    set_error("backward: causal recursions with odd splits are not built");
+    return HA_EUNSUPPORTED;
+  }
   if (sh.flags) {
     set_error("backward takes no flags");
     return HA_EINVAL;
@@ -775,7 +870,7 @@ size_t hyperattn_backward_workspace_bytes(int batch, int n, int d, int heads, in
                                           int samples, int proj_bits, int causal, int min_seq_len,
                                           int dtype) {
   Shape sh{batch, n, d, heads, kv_heads, block, samples, proj_bits, causal, min_seq_len, dtype, 0};
-  if (validate(sh) != HA_OK) return 0;
+  if (validate(sh) != HA_OK || (sh.causal && sh.odd)) return 0;
   return backward_plan(sh, nullptr, 0).total;
 }
 

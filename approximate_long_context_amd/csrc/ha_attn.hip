@@ -709,8 +709,8 @@ __global__ __launch_bounds__(64 * NW, (min_waves<T, D, KIND, NW, QPW>())) void a
   // normalised O^T (32 queries x 32 dims, fp32) is staged in the K/V
   // buffers, then lane L merges and stores dims 4 (L & 7) .. +3 of staged
   // query (L >> 3) + 8 k.
-  const bool to_final = OUT == kOutFinal || ((OUT == kOutLeaf || OUT == kOutMerge) && piece == 0);
-  const bool to_acc = ((OUT == kOutLeaf || OUT == kOutMerge) && piece != 0) || OUT == kOutAcc;
+  const bool to_final = OUT == kOutFinal || ((OUT == kOutLeaf || OUT == kOutMerge) && piece == p.final_piece);
+  const bool to_acc = ((OUT == kOutLeaf || OUT == kOutMerge) && piece != p.final_piece) || OUT == kOutAcc;
   constexpr int SST = 36;                         // staged row stride (floats)
   constexpr int STG = 32 * SST + 64;              // floats per wave: slice, lse, rows
   static_assert(NW * STG * 4 <= 2 * G::BUF, "epilogue staging fits the K/V buffers");

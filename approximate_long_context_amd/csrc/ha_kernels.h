@@ -75,6 +75,7 @@ struct AttnParams {
   int m = 0;
   float log2w = 0.f;                 // log2(seg / m)
   int out_mode = kOutFinal;
+  int final_piece = 0;               // kOutLeaf / kOutMerge: the piece whose rows are final (-1: none)
   void* out = nullptr;               // [BH][n][d] dtype
   float* lse = nullptr;              // [BH][n] (may be null for kOutFinal)
   float* acc_o = nullptr;            // [BH][n][d]

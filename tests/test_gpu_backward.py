@@ -119,3 +119,12 @@ def test_backward_rejects_fp32():
                  ha._ptr(do), ha.HA_F32, 1, 256, 64, 1, 1, 64, 16, 5, 0, 0, ctypes.c_uint64(0),
                  ha._ptr(dq), ha._ptr(dk), ha._ptr(dv), ha._ptr(ws), ws.numel(), ha._stream(q.device))
     assert e.value.code == ha.HA_EUNSUPPORTED
+
+
+def test_backward_rejects_odd_causal_splits():
+    q, k, v, do = (t.to(DEV) for t in _inputs(1, 1, 1, 1000, 64, 13))
+    args = dict(block=64, samples=16, proj_bits=5, causal=True, min_seq_len=100)
+    out, lse = ha.forward(q, k, v, **args)
+    with pytest.raises(ha.HyperAttnError) as e:
+        ha.backward(q, k, v, out, lse, do, **args)
+    assert e.value.code == ha.HA_EUNSUPPORTED

@@ -54,6 +54,9 @@ SMALL = [
     Workload("nc_lastblock", 1, 2, 1, 1000, 64, torch.bfloat16, 64, 48, 7, False, 0, "iid", 11, 24),
     Workload("nc_lastblock_d128", 1, 2, 2, 1500, 128, torch.bfloat16, 256, 64, 7, False, 0, "planted", 12, 25),
     Workload("c_lastblock", 1, 2, 1, 2048, 64, torch.bfloat16, 96, 32, 6, True, 256, "iid", 13, 26),
+    # odd causal splits: node-by-node recursion with rectangular quadrants
+    Workload("c_odd", 1, 2, 1, 1000, 64, torch.bfloat16, 64, 32, 6, True, 100, "iid", 14, 27),
+    Workload("c_odd_d128", 1, 2, 2, 777, 128, torch.bfloat16, 128, 48, 7, True, 64, "sink", 15, 28),
 ]
 
 
