@@ -255,15 +255,12 @@ static Plan make_plan(const Shape& sh, void* ws, size_t cap) {
     pl.sort_ws = cv.take<char>(pl.sort_ws_bytes);
   } else {
     if (sh.levels > 0) {
-      // every level keeps its own permutations and samples (all are prepared
-      // up front, beside the leaves): level l at offsets (l - 1) BH n/2 and
-      // (2^(l-1) - 1) BH m
       pl.acc_o = cv.take<float>(BH * sh.n * sh.d);
       pl.acc_lse = cv.take<float>(BH * sh.n);
-      pl.perm_q = cv.take<int32_t>(BH * (sh.n / 2) * sh.levels);
-      pl.perm_k = cv.take<int32_t>(BK * (sh.n / 2) * sh.levels);
-      const int64_t allp = (int64_t(1) << sh.levels) - 1;
-      pl.sidx = cv.take<int32_t>(BH * allp * (sh.samples > 0 ? sh.samples : 1));
+      pl.perm_q = cv.take<int32_t>(BH * (sh.n / 2));
+      pl.perm_k = cv.take<int32_t>(BK * (sh.n / 2));
+      const int64_t maxp = int64_t(1) << (sh.levels - 1);
+      pl.sidx = cv.take<int32_t>(BH * maxp * (sh.samples > 0 ? sh.samples : 1));
       size_t mx = 0;
       for (int l = 1; l <= sh.levels; ++l) {
         const int seg = sh.n >> l;
@@ -278,20 +275,6 @@ static Plan make_plan(const Shape& sh, void* ws, size_t cap) {
   }
   pl.total = align_up(cv.used, 256) + 256;
   return pl;
-}
-
-// A second stream per device (non-blocking, default priority) for work
-// that can run beside the causal leaves; created on first use.
-static hipStream_t side_stream() {
-  static std::mutex mu;
-  static hipStream_t streams[64] = {};
-  int dev = 0;
-  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return nullptr;
-  std::lock_guard<std::mutex> lock(mu);
-  if (!streams[dev] && hipStreamCreateWithFlags(&streams[dev], hipStreamNonBlocking) != hipSuccess) {
-    streams[dev] = nullptr;
-  }
-  return streams[dev];
 }
 
 // Causal recursion node by node (some span has odd length): the exact
@@ -393,11 +376,9 @@ static int forward_impl(const void* q, const void* k, const void* v, Shape sh, u
   const int64_t BH = static_cast<int64_t>(sh.batch) * sh.heads;
   const int64_t BK = static_cast<int64_t>(sh.batch) * sh.kv_heads;
 
-  auto hash_qk = [&](hipStream_t st) -> int {
-    HA_TRY(launch_projections(seed, sh.d, sh.r, pl.R, st));
-    HA_TRY(launch_hash(q, sh.dtype, BH * sh.n, sh.d, sh.r, pl.R, pl.rank_q, st));
-    return launch_hash(k, sh.dtype, BK * sh.n, sh.d, sh.r, pl.R, pl.rank_k, st);
-  };
+  HA_TRY(launch_projections(seed, sh.d, sh.r, pl.R, s));
+  HA_TRY(launch_hash(q, sh.dtype, BH * sh.n, sh.d, sh.r, pl.R, pl.rank_q, s));
+  HA_TRY(launch_hash(k, sh.dtype, BK * sh.n, sh.d, sh.r, pl.R, pl.rank_k, s));
 
   AttnParams ap;
   ap.q = q;
@@ -413,7 +394,6 @@ static int forward_impl(const void* q, const void* k, const void* v, Shape sh, u
   ap.lse = lse;
 
   if (!sh.causal) {
-    HA_TRY(hash_qk(s));
     HA_TRY(launch_sort(pl.rank_q, BH, sh.n, sh.n, 0, sh.n, 1, sh.r, pl.perm_q, pl.sort_ws,
                        pl.sort_ws_bytes, s));
     HA_TRY(launch_sort(pl.rank_k, BK, sh.n, sh.n, 0, sh.n, 1, sh.r, pl.perm_k, pl.sort_ws,
@@ -496,56 +476,7 @@ static int forward_impl(const void* q, const void* k, const void* v, Shape sh, u
   }
 
   // ---- causal ----
-  if (sh.odd) {
-    HA_TRY(hash_qk(s));
-    return forward_causal_nodes(ap, sh, pl, seed, s);
-  }
-  // The leaves need no hashing: the hashes, every level's sorts and every
-  // level's samples are prepared on a second stream while the leaves run,
-  // and the levels wait for them (events order the two streams).
-  hipStream_t side = sh.levels > 0 ? side_stream() : nullptr;
-  hipEvent_t ev_in = nullptr, ev_prep = nullptr;
-  auto release = [&]() {
-    if (ev_in) (void)hipEventDestroy(ev_in);
-    if (ev_prep) (void)hipEventDestroy(ev_prep);
-  };
-  auto level_perm_q = [&](int l) { return pl.perm_q + (l - 1) * BH * (sh.n / 2); };
-  auto level_perm_k = [&](int l) { return pl.perm_k + (l - 1) * BK * (sh.n / 2); };
-  auto level_sidx = [&](int l) {
-    return pl.sidx + ((int64_t(1) << (l - 1)) - 1) * BH * (sh.samples > 0 ? sh.samples : 1);
-  };
-  auto prepare_levels = [&](hipStream_t st) -> int {
-    HA_TRY(hash_qk(st));
-    for (int l = sh.levels; l >= 1; --l) {
-      const int seg = sh.n >> l;
-      const int pieces = 1 << (l - 1);
-      HA_TRY(launch_sort(pl.rank_q, BH, sh.n, seg, seg, 2 * seg, pieces, sh.r, level_perm_q(l), pl.sort_ws,
-                         pl.sort_ws_bytes, st));
-      HA_TRY(launch_sort(pl.rank_k, BK, sh.n, seg, 0, 2 * seg, pieces, sh.r, level_perm_k(l), pl.sort_ws,
-                         pl.sort_ws_bytes, st));
-      HA_TRY(launch_sample_indices(seed, sh.batch, sh.heads, pieces, pieces, seg, sh.samples, level_sidx(l), st));
-    }
-    return HA_OK;
-  };
-  if (sh.levels > 0) {
-    if (side && hipEventCreateWithFlags(&ev_in, hipEventDisableTiming) == hipSuccess &&
-        hipEventCreateWithFlags(&ev_prep, hipEventDisableTiming) == hipSuccess &&
-        hipEventRecord(ev_in, s) == hipSuccess && hipStreamWaitEvent(side, ev_in, 0) == hipSuccess) {
-      const int st = prepare_levels(side);
-      const hipError_t e = hipEventRecord(ev_prep, side);
-      if (st != HA_OK || e != hipSuccess) {
-        // join what the second stream already holds before reporting
-        if (e == hipSuccess) (void)hipStreamWaitEvent(s, ev_prep, 0);
-        else (void)hipStreamSynchronize(side);
-        release();
-        return st != HA_OK ? st : hip_status(e, "record the level preparation");
-      }
-    } else {
-      release();
-      ev_in = ev_prep = nullptr;
-      HA_TRY(prepare_levels(s));                 // no second stream: in order on the caller's
-    }
-  }
+  if (sh.odd) return forward_causal_nodes(ap, sh, pl, seed, s);
   AttnParams lp = ap;
   lp.kind = kKindLeaf;
   lp.pieces = sh.n / sh.leaf;
@@ -557,23 +488,17 @@ static int forward_impl(const void* q, const void* k, const void* v, Shape sh, u
   lp.out_mode = kOutLeaf;
   lp.acc_o = pl.acc_o;
   lp.acc_lse = pl.acc_lse;
-  {
-    const int st = launch_attention(lp, HA_K_LEAF, s);
-    if (st != HA_OK) {
-      if (ev_prep) (void)hipStreamWaitEvent(s, ev_prep, 0);   // leave no work of this call unjoined
-      release();
-      return st;
-    }
-  }
-  if (ev_prep) {
-    const hipError_t e = hipStreamWaitEvent(s, ev_prep, 0);
-    release();
-    if (e != hipSuccess) return hip_status(e, "wait for the level preparation");
-  }
+  HA_TRY(launch_attention(lp, HA_K_LEAF, s));
 
   for (int l = sh.levels; l >= 1; --l) {
     const int seg = sh.n >> l;
     const int pieces = 1 << (l - 1);
+    HA_TRY(launch_sort(pl.rank_q, BH, sh.n, seg, seg, 2 * seg, pieces, sh.r, pl.perm_q,
+                       pl.sort_ws, pl.sort_ws_bytes, s));
+    HA_TRY(launch_sort(pl.rank_k, BK, sh.n, seg, 0, 2 * seg, pieces, sh.r, pl.perm_k,
+                       pl.sort_ws, pl.sort_ws_bytes, s));
+    HA_TRY(launch_sample_indices(seed, sh.batch, sh.heads, pieces, pieces, seg, sh.samples,
+                                 pl.sidx, s));
     AttnParams qp = ap;
     qp.kind = kKindSorted;
     qp.pieces = pieces;
@@ -581,12 +506,12 @@ static int forward_impl(const void* q, const void* k, const void* v, Shape sh, u
     qp.q_first = seg;
     qp.k_first = 0;
     qp.stride = 2 * seg;
-    qp.perm_q = level_perm_q(l);
-    qp.perm_k = level_perm_k(l);
+    qp.perm_q = pl.perm_q;
+    qp.perm_k = pl.perm_k;
     qp.b_eff = sh.block < seg ? sh.block : seg;
     qp.use_block = 1;
     qp.use_samples = sh.samples > 0;
-    qp.sidx = level_sidx(l);
+    qp.sidx = pl.sidx;
     qp.m = sh.samples;
     qp.log2w = sh.samples > 0 ? static_cast<float>(std::log2(static_cast<double>(seg) / sh.samples)) : 0.f;
     qp.out_mode = kOutMerge;
