@@ -41,7 +41,8 @@ _SIGNATURES = {
     "hyperattn_merge_unsort": (_c_int, [_vp, _vp, _vp, _vp, _vp, _c_i64, _c_int, _c_int, _c_int, _vp, _vp, _vp]),
     "hyperattn_causal_leaves": (_c_int, [_vp, _vp, _vp, _c_int] + [_c_int] * 6 + [_vp, _vp, _vp]),
     "hyperattn_row_sqnorms": (_c_int, [_vp, _c_int, _c_i64, _c_int, _vp, _vp]),
-    "hyperattn_rownorm_samples": (_c_int, [_vp, _vp] + [_c_int] * 5 + [_c_u64, _vp, _vp, _vp]),
+    "hyperattn_rownorm_samples_workspace_bytes": (_c_size, [_c_int] * 3),
+    "hyperattn_rownorm_samples": (_c_int, [_vp, _vp] + [_c_int] * 5 + [_c_u64, _vp, _vp, _vp, _c_size, _vp]),
     "hyperattn_column_sqmass": (_c_int, [_vp, _vp, _vp] + [_c_int] * 8 + [_vp, _vp, _vp]),
     "hyperattn_residual_ratio": (_c_int, [_vp, _vp, _vp, _c_i64, _c_int, _vp, _vp]),
     "hyperattn_rect_workspace_bytes": (_c_size, [_c_int] * 10),
@@ -290,8 +291,10 @@ def rownorm_samples(w, perm_k, heads, samples, seed):
     B, Hkv, n = w.shape
     cum = torch.empty((B, Hkv, n), dtype=torch.int64, device=w.device)
     sidx = torch.empty((B, heads, samples), dtype=torch.int32, device=w.device)
+    wsb = lib().hyperattn_rownorm_samples_workspace_bytes(B, Hkv, n)
+    ws = torch.empty(max(wsb, 1), dtype=torch.uint8, device=w.device)
     _call("hyperattn_rownorm_samples", _ptr(w), _ptr(perm_k), B, heads, Hkv, n, samples, ctypes.c_uint64(seed),
-          _ptr(cum), _ptr(sidx), _stream(w.device))
+          _ptr(cum), _ptr(sidx), _ptr(ws), wsb, _stream(w.device))
     return cum, sidx
 
 

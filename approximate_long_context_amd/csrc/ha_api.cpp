@@ -207,6 +207,7 @@ struct Plan {
   float* rn_w;                 // row-norm variant: squared norms of V rows
   int64_t* rn_cum;             // integer CDF per KV head
   int32_t* rn_sidx;            // draws per query head
+  void* rn_ws;                 // CDF scratch: per-problem shift and chunk totals
   size_t total;
 };
 
@@ -242,6 +243,7 @@ static Plan make_plan(const Shape& sh, void* ws, size_t cap) {
       pl.rn_w = cv.take<float>(BK * sh.n);
       pl.rn_cum = cv.take<int64_t>(BK * sh.n);
       pl.rn_sidx = cv.take<int32_t>(BH * (sh.samples > 0 ? sh.samples : 1));
+      pl.rn_ws = cv.take<char>(rownorm_cdf_ws_bytes(BK, sh.n));
     }
   } else if (sh.odd) {
     const int half = sh.n - sh.n / 2;         // the longest quadrant side
@@ -425,7 +427,7 @@ static int forward_impl(const void* q, const void* k, const void* v, Shape sh, u
       if (sh.samples > 0) HA_TRY(launch_attention(ap, HA_K_ATTEND, s));
       if (sh.samples > 0) {
         HA_TRY(launch_rownorm_sqnorm(v, sh.dtype, BK * sh.n, sh.d, pl.rn_w, s));
-        HA_TRY(launch_rownorm_cdf(pl.rn_w, pl.perm_k, BK, sh.n, pl.rn_cum, s));
+        HA_TRY(launch_rownorm_cdf(pl.rn_w, pl.perm_k, BK, sh.n, pl.rn_cum, pl.rn_ws, s));
         HA_TRY(launch_rownorm_samples(pl.rn_cum, sh.n, seed, sh.batch, sh.heads, sh.kv_heads, sh.samples,
                                       pl.rn_sidx, s));
         HA_TRY(launch_gather(q, sh.dtype, BH, sh.n, sh.d, pl.perm_q, sh.n, pl.qs, s));
@@ -898,16 +900,28 @@ int hyperattn_row_sqnorms(const void* x, int dtype, int64_t rows, int d, float* 
   return launch_rownorm_sqnorm(x, dtype, rows, d, w, static_cast<hipStream_t>(stream));
 }
 
+size_t hyperattn_rownorm_samples_workspace_bytes(int batch, int kv_heads, int n) {
+  if (batch < 0 || kv_heads < 1 || n < 0) return 0;
+  return rownorm_cdf_ws_bytes(static_cast<int64_t>(batch) * kv_heads, n);
+}
+
 int hyperattn_rownorm_samples(const float* w, const int32_t* perm_k, int batch, int heads, int kv_heads, int n,
-                              int samples, uint64_t seed, int64_t* cum, int32_t* sidx, void* stream) {
+                              int samples, uint64_t seed, int64_t* cum, int32_t* sidx, void* workspace,
+                              size_t workspace_bytes, void* stream) {
   g_last_error.clear();
   if (batch < 0 || heads < 1 || kv_heads < 1 || heads % kv_heads || n < 0 || samples < 0 ||
       (n > 0 && batch > 0 && (!w || !perm_k || !cum || (samples > 0 && !sidx)))) {
     set_error("rownorm_samples: bad arguments");
     return HA_EINVAL;
   }
+  const int64_t problems = static_cast<int64_t>(batch) * kv_heads;
+  if (n > 0 && batch > 0 && (!workspace || workspace_bytes < rownorm_cdf_ws_bytes(problems, n))) {
+    set_error("rownorm_samples: workspace of %zu bytes, %zu needed", workspace_bytes,
+              rownorm_cdf_ws_bytes(problems, n));
+    return HA_EWORKSPACE;
+  }
   hipStream_t s = static_cast<hipStream_t>(stream);
-  HA_TRY(launch_rownorm_cdf(w, perm_k, static_cast<int64_t>(batch) * kv_heads, n, cum, s));
+  HA_TRY(launch_rownorm_cdf(w, perm_k, problems, n, cum, workspace, s));
   return launch_rownorm_samples(cum, n, seed, batch, heads, kv_heads, samples, sidx, s);
 }
 

@@ -133,7 +133,8 @@ inline int bwd_query_chunk(int seg) {
 
 // Row-norm variant (ha_rownorm.hip).
 int launch_rownorm_sqnorm(const void* v, int dtype, int64_t rows, int d, float* w, hipStream_t s);
-int launch_rownorm_cdf(const float* w, const int32_t* perm_k, int64_t problems, int n, int64_t* cum,
+size_t rownorm_cdf_ws_bytes(int64_t problems, int n);
+int launch_rownorm_cdf(const float* w, const int32_t* perm_k, int64_t problems, int n, int64_t* cum, void* ws,
                        hipStream_t s);
 int launch_rownorm_samples(const int64_t* cum, int n, uint64_t seed, int batch, int heads, int kv_heads, int m,
                            int32_t* out, hipStream_t s);

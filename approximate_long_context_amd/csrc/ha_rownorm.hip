@@ -17,8 +17,8 @@
 //   draw i: word x of Philox counter (i / 4, node, head, 2 batch + 2),
 //   r = floor(x T / 2^32), position = smallest t with c_t > r;
 //   weight T / (m n_t), folded into a sorted copy of V (the draw's row).
-// Kernels: squared norms, the per-problem integer CDF (one workgroup per
-// KV problem), the draws (binary search), the weighted sorted V copy, and
+// Kernels: squared norms, the per-problem integer CDF (max, chunk scans,
+// chunk offsets), the draws (binary search), the weighted sorted V copy, and
 // the three-part merge + unsort
 //   out = (N_blk + N_rn) / (D_blk + D_unif),  lse = ln(D_blk + D_unif).
 #include <cmath>
@@ -66,57 +66,86 @@ __global__ __launch_bounds__(256) void rownorm_sqnorm_kernel(const T* __restrict
   }
 }
 
-// ---- integer CDF of one KV problem per workgroup -----------------------------
+// ---- integer CDF: per-problem max, chunk scans, chunk offsets -----------------
+// (1) rownorm_max_kernel: one workgroup per KV problem, the largest w;
+// (2) rownorm_chunk_kernel: one workgroup per 2048 sorted positions, the
+//     quantised weights n_t (gathered through the permutation) and their
+//     inclusive scan within the chunk, plus the chunk's total;
+// (3) rownorm_offset_kernel: each chunk adds the totals of the chunks before
+//     it (exact int64 sums, so the order of additions does not matter).
 
-constexpr int kRnCdfThreads = 1024;
+constexpr int kRnThreads = 256;
+constexpr int kRnChunk = 2048;                      // 8 positions per thread
 
-__global__ __launch_bounds__(kRnCdfThreads) void rownorm_cdf_kernel(const float* __restrict__ w,
-                                                                     const int32_t* __restrict__ perm_k, int n,
-                                                                     int64_t* __restrict__ cum) {
-  __shared__ float smax[kRnCdfThreads / 64];
-  __shared__ int64_t ssum[kRnCdfThreads];
-  const int tid = threadIdx.x;
-  const int64_t prob = blockIdx.x;
+__global__ __launch_bounds__(kRnThreads) void rownorm_max_kernel(const float* __restrict__ w, int n,
+                                                                  int* __restrict__ shift) {
+  __shared__ float red[kRnThreads / 64];
+  const float* wp = w + static_cast<int64_t>(blockIdx.x) * n;
+  float mx = 0.f;
+  for (int t = threadIdx.x; t < n; t += kRnThreads) mx = fmaxf(mx, wp[t]);
+#pragma unroll
+  for (int h = 32; h >= 1; h >>= 1) mx = fmaxf(mx, __shfl_xor(mx, h));
+  if ((threadIdx.x & 63) == 0) red[threadIdx.x >> 6] = mx;
+  __syncthreads();
+  if (threadIdx.x == 0) {
+    mx = fmaxf(fmaxf(red[0], red[1]), fmaxf(red[2], red[3]));
+    int e = 0;
+    if (mx > 0.f) frexp(static_cast<double>(mx), &e);
+    shift[blockIdx.x] = mx > 0.f ? kRnQBits - e : -100000;   // no positive weight: every n_t = 0
+  }
+}
+
+__global__ __launch_bounds__(kRnThreads) void rownorm_chunk_kernel(const float* __restrict__ w,
+                                                                    const int32_t* __restrict__ perm_k, int n,
+                                                                    int nchunk, const int* __restrict__ shift,
+                                                                    int64_t* __restrict__ cum,
+                                                                    int64_t* __restrict__ chunk_sum) {
+  __shared__ int64_t ssum[kRnThreads];
+  const int64_t prob = blockIdx.x / nchunk;
+  const int chunk = blockIdx.x % nchunk;
+  const int sh = shift[prob];
   const float* wp = w + prob * n;
   const int32_t* pk = perm_k + prob * n;
   int64_t* cp = cum + prob * n;
-
-  float mx = 0.f;
-  for (int t = tid; t < n; t += kRnCdfThreads) mx = fmaxf(mx, wp[t]);
-#pragma unroll
-  for (int h = 32; h >= 1; h >>= 1) mx = fmaxf(mx, __shfl_xor(mx, h));
-  if ((tid & 63) == 0) smax[tid >> 6] = mx;
-  __syncthreads();
-  mx = 0.f;
-#pragma unroll
-  for (int i = 0; i < kRnCdfThreads / 64; ++i) mx = fmaxf(mx, smax[i]);
-  int e = 0;
-  if (mx > 0.f) frexp(static_cast<double>(mx), &e);
-  const int shift = kRnQBits - e;
-  auto weight = [&](int t) -> int64_t {
-    return mx > 0.f ? static_cast<int64_t>(floor(ldexp(static_cast<double>(wp[pk[t]]), shift))) : 0;
-  };
-
-  // each thread: a contiguous run of sorted positions
-  const int per = (n + kRnCdfThreads - 1) / kRnCdfThreads;
-  const int t0 = tid * per;
-  const int t1 = min(t0 + per, n);
+  constexpr int PER = kRnChunk / kRnThreads;
+  const int t0 = chunk * kRnChunk + threadIdx.x * PER;
+  int64_t v[PER];
   int64_t local = 0;
-  for (int t = t0; t < t1; ++t) local += weight(t);
-  ssum[tid] = local;
+#pragma unroll
+  for (int i = 0; i < PER; ++i) {
+    const int t = t0 + i;
+    const int ts = t < n ? t : n - 1;
+    const double x = ldexp(static_cast<double>(wp[pk[ts]]), sh);
+    v[i] = (t < n && sh > -100000) ? static_cast<int64_t>(floor(x)) : 0;
+    local += v[i];
+  }
+  ssum[threadIdx.x] = local;
   __syncthreads();
-  // inclusive scan over the thread totals (Hillis-Steele in LDS)
-  for (int off = 1; off < kRnCdfThreads; off <<= 1) {
-    const int64_t add = tid >= off ? ssum[tid - off] : 0;
+  for (int off = 1; off < kRnThreads; off <<= 1) {
+    const int64_t add = threadIdx.x >= off ? ssum[threadIdx.x - off] : 0;
     __syncthreads();
-    ssum[tid] += add;
+    ssum[threadIdx.x] += add;
     __syncthreads();
   }
-  int64_t run = ssum[tid] - local;
-  for (int t = t0; t < t1; ++t) {
-    run += weight(t);
-    cp[t] = run;
+  int64_t run = ssum[threadIdx.x] - local;
+#pragma unroll
+  for (int i = 0; i < PER; ++i) {
+    run += v[i];
+    if (t0 + i < n) cp[t0 + i] = run;
   }
+  if (threadIdx.x == kRnThreads - 1) chunk_sum[blockIdx.x] = ssum[kRnThreads - 1];
+}
+
+__global__ __launch_bounds__(kRnThreads) void rownorm_offset_kernel(int n, int nchunk,
+                                                                     const int64_t* __restrict__ chunk_sum,
+                                                                     int64_t* __restrict__ cum) {
+  const int64_t prob = blockIdx.x / nchunk;
+  const int chunk = blockIdx.x % nchunk;
+  if (chunk == 0) return;
+  int64_t off = 0;
+  for (int c = 0; c < chunk; ++c) off += chunk_sum[prob * nchunk + c];
+  int64_t* cp = cum + prob * n;
+  for (int t = chunk * kRnChunk + threadIdx.x; t < min((chunk + 1) * kRnChunk, n); t += kRnThreads) cp[t] += off;
 }
 
 // ---- draws ---------------------------------------------------------------------
@@ -229,11 +258,23 @@ int launch_rownorm_sqnorm(const void* v, int dtype, int64_t rows, int d, float* 
   return after_launch("row-norm squared norms", s);
 }
 
-int launch_rownorm_cdf(const float* w, const int32_t* perm_k, int64_t problems, int n, int64_t* cum,
+size_t rownorm_cdf_ws_bytes(int64_t problems, int n) {
+  const int64_t nchunk = (n + kRnChunk - 1) / kRnChunk;
+  return static_cast<size_t>(problems) * (sizeof(int) + nchunk * sizeof(int64_t)) + 64;
+}
+
+int launch_rownorm_cdf(const float* w, const int32_t* perm_k, int64_t problems, int n, int64_t* cum, void* ws,
                        hipStream_t s) {
   if (problems == 0 || n == 0) return HA_OK;
-  hipLaunchKernelGGL(rownorm_cdf_kernel, dim3(static_cast<unsigned>(problems)), dim3(kRnCdfThreads), 0, s, w,
-                     perm_k, n, cum);
+  const int nchunk = (n + kRnChunk - 1) / kRnChunk;
+  int64_t* chunk_sum = static_cast<int64_t*>(ws);
+  int* shift = reinterpret_cast<int*>(chunk_sum + problems * nchunk);
+  const unsigned grid = static_cast<unsigned>(problems * nchunk);
+  hipLaunchKernelGGL(rownorm_max_kernel, dim3(static_cast<unsigned>(problems)), dim3(kRnThreads), 0, s, w, n,
+                     shift);
+  hipLaunchKernelGGL(rownorm_chunk_kernel, dim3(grid), dim3(kRnThreads), 0, s, w, perm_k, n, nchunk, shift, cum,
+                     chunk_sum);
+  hipLaunchKernelGGL(rownorm_offset_kernel, dim3(grid), dim3(kRnThreads), 0, s, n, nchunk, chunk_sum, cum);
   return after_launch("row-norm cdf", s);
 }
 

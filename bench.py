@@ -275,6 +275,7 @@ def main():
         result["configs"] = other_configs(ha, torch, dev, stream)
         result["rownorm"] = rownorm_bench(ha, torch, w_nc, q, k, v, out, stream)
         result["diagnostics"] = diagnostics_bench(ha, torch, dev, stream)
+        result["rect"] = rect_bench(ha, torch, dev, stream)
         del ws
         result["backward"] = {name: backward_bench(ha, torch, w, q, k, v, out, lse, stream)
                               for name, w in (("noncausal", w_nc), ("causal", w_c))}
@@ -300,6 +301,37 @@ def approx_error(ha, torch, w_nc, w_c, q, k, v, out):
         res[name] = float(torch.linalg.vector_norm(a - b) / torch.linalg.vector_norm(b))
         del a, b
     return res
+
+
+def rect_bench(ha, torch, dev, stream, reps=5):
+    """A rectangular non-causal problem shaped like a prefill chunk: 32768
+    queries over 131072 keys, 32 heads, d = 64, bf16, block 256 (key
+    blocks of 1024), 256 samples (not part of `value`).  FLOPs
+    4 d (b_k + m) per query row."""
+    B, H, nq, nk, d, block, m, r = 1, 32, 32768, 131072, 64, 256, 256, 7
+    g = torch.Generator(device=dev).manual_seed(5)
+    q = (torch.randn(B, H, nq, d, generator=g, device=dev) * d ** -0.25).to(torch.bfloat16)
+    k = (torch.randn(B, H, nk, d, generator=g, device=dev) * d ** -0.25).to(torch.bfloat16)
+    v = torch.randn(B, H, nk, d, generator=g, device=dev).to(torch.bfloat16)
+    out = torch.empty_like(q)
+    ws = torch.empty(ha.lib().hyperattn_rect_workspace_bytes(B, nq, nk, d, H, H, block, m, r, ha.HA_BF16),
+                     dtype=torch.uint8, device=dev)
+    args = dict(block=block, samples=m, proj_bits=r)
+    ha.forward_rect(q, k, v, out=out, workspace=ws, **args)
+    e0 = torch.cuda.Event(enable_timing=True)
+    e1 = torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    e0.record(stream)
+    for _ in range(reps):
+        ha.forward_rect(q, k, v, out=out, workspace=ws, **args)
+    e1.record(stream)
+    torch.cuda.synchronize()
+    ms = e0.elapsed_time(e1) / reps
+    b_k = -(-block * nk // nq)
+    flops = 4.0 * d * B * H * nq * (b_k + m)
+    del q, k, v, out, ws
+    return {"n_q": nq, "n_k": nk, "heads": H, "head_dim": d, "block": block, "key_block": b_k, "samples": m,
+            "ms": ms, "tflops": flops / (ms * 1e-3) / 1e12}
 
 
 def diagnostics_bench(ha, torch, dev, stream):

@@ -193,10 +193,15 @@ int hyperattn_row_sqnorms(const void* x, int dtype, int64_t rows, int d, float* 
  *            the seed with counter (i / 4, 1, h, 2 b + 2), r = floor(word T
  *            / 2^32) with T = cum[n - 1] of the head's KV head, and is the
  *            smallest sorted position t with cum[t] > r (0 when T = 0)
- * Errors: HA_EINVAL (bad arguments). */
+ *   workspace device scratch of at least
+ *            hyperattn_rownorm_samples_workspace_bytes(batch, kv_heads, n)
+ *            bytes, owned by the caller, contents undefined afterwards
+ * Errors: HA_EINVAL (bad arguments), HA_EWORKSPACE (workspace missing or
+ * too small). */
+size_t hyperattn_rownorm_samples_workspace_bytes(int batch, int kv_heads, int n);
 int hyperattn_rownorm_samples(const float* w, const int32_t* perm_k, int batch, int heads, int kv_heads,
                               int n, int samples, uint64_t seed, int64_t* cum, int32_t* sidx,
-                              void* stream);
+                              void* workspace, size_t workspace_bytes, void* stream);
 
 /* ------------------------------------------------------------------------
  * Diagnostics: the method's fine-grained parameters ("HyperAttention:
