@@ -224,8 +224,7 @@ static Plan make_plan(const Shape& sh, void* ws, size_t cap) {
     pl.perm_q = cv.take<int32_t>(BH * sh.n);
     pl.perm_k = cv.take<int32_t>(BK * sh.n);
     pl.sidx = cv.take<int32_t>(BH * (sh.samples > 0 ? sh.samples : 1));
-    size_t a = sort_ws_bytes(BH, sh.n, 1, sh.r), b = sort_ws_bytes(BK, sh.n, 1, sh.r);
-    pl.sort_ws_bytes = a > b ? a : b;
+    pl.sort_ws_bytes = sort_ws_bytes(BH, sh.n, 1, sh.r) + sort_ws_bytes(BK, sh.n, 1, sh.r);
     pl.sort_ws = cv.take<char>(pl.sort_ws_bytes);
     const bool rn = sh.flags & HA_FLAG_ROWNORM;
     if ((sh.flags & HA_FLAG_MATERIALIZE) || rn) {
@@ -252,8 +251,7 @@ static Plan make_plan(const Shape& sh, void* ws, size_t cap) {
     pl.perm_q = cv.take<int32_t>(BH * half);
     pl.perm_k = cv.take<int32_t>(BK * half);
     pl.sidx = cv.take<int32_t>(BH * (sh.samples > 0 ? sh.samples : 1));
-    const size_t a = sort_ws_bytes(BH, half, 1, sh.r), b = sort_ws_bytes(BK, half, 1, sh.r);
-    pl.sort_ws_bytes = a > b ? a : b;
+    pl.sort_ws_bytes = sort_ws_bytes(BH, half, 1, sh.r) + sort_ws_bytes(BK, half, 1, sh.r);
     pl.sort_ws = cv.take<char>(pl.sort_ws_bytes);
   } else {
     if (sh.levels > 0) {
@@ -267,8 +265,7 @@ static Plan make_plan(const Shape& sh, void* ws, size_t cap) {
       for (int l = 1; l <= sh.levels; ++l) {
         const int seg = sh.n >> l;
         const int pieces = 1 << (l - 1);
-        size_t a = sort_ws_bytes(BH, seg, pieces, sh.r), b = sort_ws_bytes(BK, seg, pieces, sh.r);
-        if (a > mx) mx = a;
+        const size_t b = sort_ws_bytes(BH, seg, pieces, sh.r) + sort_ws_bytes(BK, seg, pieces, sh.r);
         if (b > mx) mx = b;
       }
       pl.sort_ws_bytes = mx;
@@ -328,8 +325,9 @@ static int forward_causal_nodes(const AttnParams& ap, const Shape& sh, const Pla
   }
   for (const Node& nd : quads) {
     const int nq = nd.hi - nd.mid, nk = nd.mid - nd.lo;
-    HA_TRY(launch_sort(pl.rank_q, BH, sh.n, nq, nd.mid, nq, 1, sh.r, pl.perm_q, pl.sort_ws, pl.sort_ws_bytes, s));
-    HA_TRY(launch_sort(pl.rank_k, BK, sh.n, nk, nd.lo, nk, 1, sh.r, pl.perm_k, pl.sort_ws, pl.sort_ws_bytes, s));
+    const SortJobDesc jobs[2] = {{pl.rank_q, BH, sh.n, nq, nd.mid, nq, 1, pl.perm_q},
+                                 {pl.rank_k, BK, sh.n, nk, nd.lo, nk, 1, pl.perm_k}};
+    HA_TRY(launch_sort_batch(jobs, 2, sh.r, pl.sort_ws, pl.sort_ws_bytes, s));
     HA_TRY(launch_sample_indices(seed, sh.batch, sh.heads, nd.id, 1, nk, sh.samples, pl.sidx, s));
     AttnParams qp = ap;
     qp.kind = kKindSorted;
@@ -355,6 +353,18 @@ static int forward_causal_nodes(const AttnParams& ap, const Shape& sh, const Pla
     HA_TRY(launch_attention(qp, HA_K_QUADRANT, s));
   }
   return HA_OK;
+}
+
+// The segments of causal level l (queries [mid, hi) and keys [lo, mid) of
+// every node at that depth) in one batched sort.
+static int sort_causal_level(const uint16_t* rank_q, const uint16_t* rank_k, int64_t BH, int64_t BK, int n,
+                             int l, int r, int32_t* perm_q, int32_t* perm_k, void* ws, size_t ws_bytes,
+                             hipStream_t s) {
+  const int seg = n >> l;
+  const int pieces = 1 << (l - 1);
+  const SortJobDesc jobs[2] = {{rank_q, BH, n, seg, seg, 2 * seg, pieces, perm_q},
+                               {rank_k, BK, n, seg, 0, 2 * seg, pieces, perm_k}};
+  return launch_sort_batch(jobs, 2, r, ws, ws_bytes, s);
 }
 
 static int forward_impl(const void* q, const void* k, const void* v, Shape sh, uint64_t seed,
@@ -396,10 +406,9 @@ static int forward_impl(const void* q, const void* k, const void* v, Shape sh, u
   ap.lse = lse;
 
   if (!sh.causal) {
-    HA_TRY(launch_sort(pl.rank_q, BH, sh.n, sh.n, 0, sh.n, 1, sh.r, pl.perm_q, pl.sort_ws,
-                       pl.sort_ws_bytes, s));
-    HA_TRY(launch_sort(pl.rank_k, BK, sh.n, sh.n, 0, sh.n, 1, sh.r, pl.perm_k, pl.sort_ws,
-                       pl.sort_ws_bytes, s));
+    const SortJobDesc jobs[2] = {{pl.rank_q, BH, sh.n, sh.n, 0, sh.n, 1, pl.perm_q},
+                                 {pl.rank_k, BK, sh.n, sh.n, 0, sh.n, 1, pl.perm_k}};
+    HA_TRY(launch_sort_batch(jobs, 2, sh.r, pl.sort_ws, pl.sort_ws_bytes, s));
     HA_TRY(launch_sample_indices(seed, sh.batch, sh.heads, 1, 1, sh.n, sh.samples, pl.sidx, s));
     ap.kind = kKindSorted;
     ap.pieces = 1;
@@ -495,10 +504,8 @@ static int forward_impl(const void* q, const void* k, const void* v, Shape sh, u
   for (int l = sh.levels; l >= 1; --l) {
     const int seg = sh.n >> l;
     const int pieces = 1 << (l - 1);
-    HA_TRY(launch_sort(pl.rank_q, BH, sh.n, seg, seg, 2 * seg, pieces, sh.r, pl.perm_q,
-                       pl.sort_ws, pl.sort_ws_bytes, s));
-    HA_TRY(launch_sort(pl.rank_k, BK, sh.n, seg, 0, 2 * seg, pieces, sh.r, pl.perm_k,
-                       pl.sort_ws, pl.sort_ws_bytes, s));
+    HA_TRY(sort_causal_level(pl.rank_q, pl.rank_k, BH, BK, sh.n, l, sh.r, pl.perm_q, pl.perm_k, pl.sort_ws,
+                             pl.sort_ws_bytes, s));
     HA_TRY(launch_sample_indices(seed, sh.batch, sh.heads, pieces, pieces, seg, sh.samples,
                                  pl.sidx, s));
     AttnParams qp = ap;
@@ -523,6 +530,7 @@ static int forward_impl(const void* q, const void* k, const void* v, Shape sh, u
   }
   return HA_OK;
 }
+
 
 // ---- rectangular non-causal problems ----------------------------------------------
 // n_q queries and n_k keys per head: query blocks of b_eff = min(block, n_q)
@@ -552,8 +560,7 @@ static RectPlan rect_plan(const Shape& sh, int n_k, void* ws, size_t cap) {
   pl.perm_q = cv.take<int32_t>(BH * sh.n);
   pl.perm_k = cv.take<int32_t>(BK * n_k);
   pl.sidx = cv.take<int32_t>(BH * (sh.samples > 0 ? sh.samples : 1));
-  const size_t a = sort_ws_bytes(BH, sh.n, 1, sh.r), b = sort_ws_bytes(BK, n_k, 1, sh.r);
-  pl.sort_ws_bytes = a > b ? a : b;
+  pl.sort_ws_bytes = sort_ws_bytes(BH, sh.n, 1, sh.r) + sort_ws_bytes(BK, n_k, 1, sh.r);
   pl.sort_ws = cv.take<char>(pl.sort_ws_bytes);
   pl.total = align_up(cv.used, 256) + 256;
   return pl;
@@ -596,8 +603,9 @@ static int forward_rect_impl(const void* q, const void* k, const void* v, Shape 
   HA_TRY(launch_projections(seed, sh.d, sh.r, pl.R, s));
   HA_TRY(launch_hash(q, sh.dtype, BH * sh.n, sh.d, sh.r, pl.R, pl.rank_q, s));
   HA_TRY(launch_hash(k, sh.dtype, BK * n_k, sh.d, sh.r, pl.R, pl.rank_k, s));
-  HA_TRY(launch_sort(pl.rank_q, BH, sh.n, sh.n, 0, sh.n, 1, sh.r, pl.perm_q, pl.sort_ws, pl.sort_ws_bytes, s));
-  HA_TRY(launch_sort(pl.rank_k, BK, n_k, n_k, 0, n_k, 1, sh.r, pl.perm_k, pl.sort_ws, pl.sort_ws_bytes, s));
+  const SortJobDesc jobs[2] = {{pl.rank_q, BH, sh.n, sh.n, 0, sh.n, 1, pl.perm_q},
+                               {pl.rank_k, BK, n_k, n_k, 0, n_k, 1, pl.perm_k}};
+  HA_TRY(launch_sort_batch(jobs, 2, sh.r, pl.sort_ws, pl.sort_ws_bytes, s));
   HA_TRY(launch_sample_indices(seed, sh.batch, sh.heads, 1, 1, n_k, sh.samples, pl.sidx, s));
   AttnParams ap;
   ap.q = q;
@@ -672,8 +680,7 @@ static BwdPlan backward_plan(const Shape& sh, void* ws, size_t cap) {
     pl.perm_q = cv.take<int32_t>(BH * sh.n);
     pl.perm_k = cv.take<int32_t>(BK * sh.n);
     pl.sidx = cv.take<int32_t>(BH * m1);
-    size_t a = sort_ws_bytes(BH, sh.n, 1, sh.r), b = sort_ws_bytes(BK, sh.n, 1, sh.r);
-    pl.sort_ws_bytes = a > b ? a : b;
+    pl.sort_ws_bytes = sort_ws_bytes(BH, sh.n, 1, sh.r) + sort_ws_bytes(BK, sh.n, 1, sh.r);
     pl.sort_ws = cv.take<char>(pl.sort_ws_bytes);
     pl.part = cv.take<float>(bwd_part_floats(BH, sh.n, 1, sh.samples, sh.d));
   } else if (sh.levels > 0) {
@@ -685,8 +692,7 @@ static BwdPlan backward_plan(const Shape& sh, void* ws, size_t cap) {
     for (int l = 1; l <= sh.levels; ++l) {
       const int seg = sh.n >> l;
       const int pieces = 1 << (l - 1);
-      size_t a = sort_ws_bytes(BH, seg, pieces, sh.r), b = sort_ws_bytes(BK, seg, pieces, sh.r);
-      if (a > mx) mx = a;
+      const size_t b = sort_ws_bytes(BH, seg, pieces, sh.r) + sort_ws_bytes(BK, seg, pieces, sh.r);
       if (b > mx) mx = b;
       const int64_t f = bwd_part_floats(BH, seg, pieces, sh.samples, sh.d);
       if (f > part) part = f;
@@ -760,15 +766,16 @@ static int backward_impl(const void* q, const void* k, const void* v, const void
   HA_TRY(launch_bwd_qstat(bp, s));
 
   // one sorted problem per piece: queries [p stride + q_first, + seg), keys [p stride + k_first, + seg)
-  auto sorted_problems = [&](int seg, int pieces, int q_first, int k_first, int stride, int accumulate) -> int {
+  auto sorted_problems = [&](int seg, int pieces, int q_first, int k_first, int stride, int accumulate,
+                             const int32_t* perm_q, const int32_t* perm_k) -> int {
     BwdParams qp = bp;
     qp.pieces = pieces;
     qp.seg = seg;
     qp.stride = stride;
     qp.q_first = q_first;
     qp.k_first = k_first;
-    qp.perm_q = pl.perm_q;
-    qp.perm_k = pl.perm_k;
+    qp.perm_q = perm_q;
+    qp.perm_k = perm_k;
     qp.sidx = pl.sidx;
     qp.m = sh.samples;
     qp.log2w = sh.samples > 0 ? static_cast<float>(std::log2(static_cast<double>(seg) / sh.samples)) : 0.f;
@@ -781,10 +788,11 @@ static int backward_impl(const void* q, const void* k, const void* v, const void
   };
 
   if (!sh.causal) {
-    HA_TRY(launch_sort(pl.rank_q, BH, sh.n, sh.n, 0, sh.n, 1, sh.r, pl.perm_q, pl.sort_ws, pl.sort_ws_bytes, s));
-    HA_TRY(launch_sort(pl.rank_k, BK, sh.n, sh.n, 0, sh.n, 1, sh.r, pl.perm_k, pl.sort_ws, pl.sort_ws_bytes, s));
+    const SortJobDesc jobs[2] = {{pl.rank_q, BH, sh.n, sh.n, 0, sh.n, 1, pl.perm_q},
+                                 {pl.rank_k, BK, sh.n, sh.n, 0, sh.n, 1, pl.perm_k}};
+    HA_TRY(launch_sort_batch(jobs, 2, sh.r, pl.sort_ws, pl.sort_ws_bytes, s));
     HA_TRY(launch_sample_indices(seed, sh.batch, sh.heads, 1, 1, sh.n, sh.samples, pl.sidx, s));
-    return sorted_problems(sh.n, 1, 0, 0, sh.n, 0);
+    return sorted_problems(sh.n, 1, 0, 0, sh.n, 0, pl.perm_q, pl.perm_k);
   }
 
   // exact causal leaves, rows in their own order
@@ -805,12 +813,10 @@ static int backward_impl(const void* q, const void* k, const void* v, const void
   for (int l = sh.levels; l >= 1; --l) {
     const int seg = sh.n >> l;
     const int pieces = 1 << (l - 1);
-    HA_TRY(launch_sort(pl.rank_q, BH, sh.n, seg, seg, 2 * seg, pieces, sh.r, pl.perm_q, pl.sort_ws,
-                       pl.sort_ws_bytes, s));
-    HA_TRY(launch_sort(pl.rank_k, BK, sh.n, seg, 0, 2 * seg, pieces, sh.r, pl.perm_k, pl.sort_ws,
-                       pl.sort_ws_bytes, s));
+    HA_TRY(sort_causal_level(pl.rank_q, pl.rank_k, BH, BK, sh.n, l, sh.r, pl.perm_q, pl.perm_k, pl.sort_ws,
+                             pl.sort_ws_bytes, s));
     HA_TRY(launch_sample_indices(seed, sh.batch, sh.heads, pieces, pieces, seg, sh.samples, pl.sidx, s));
-    HA_TRY(sorted_problems(seg, pieces, seg, 0, 2 * seg, 1));
+    HA_TRY(sorted_problems(seg, pieces, seg, 0, 2 * seg, 1, pl.perm_q, pl.perm_k));
   }
   return HA_OK;
 }

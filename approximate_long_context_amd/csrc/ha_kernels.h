@@ -16,6 +16,17 @@ int launch_hash(const void* x, int dtype, int64_t rows, int d, int r, const floa
 
 // ---- segmented stable counting sort (ha_sort.hip) ------------------------
 size_t sort_ws_bytes(int64_t heads, int len, int pieces, int r);
+// One job of a batched sort: segment p (< pieces) of head h holds rows
+// first + p * stride + [0, len) of rank[h * n ...]; perm [heads][pieces][len].
+struct SortJobDesc {
+  const uint16_t* rank;
+  int64_t heads;
+  int n, len, first, stride, pieces;
+  int32_t* perm;
+};
+constexpr int kSortMaxJobs = 16;
+size_t sort_batch_ws_bytes(const SortJobDesc* jobs, int njobs, int r);
+int launch_sort_batch(const SortJobDesc* jobs, int njobs, int r, void* ws, size_t ws_bytes, hipStream_t s);
 int launch_sort(const uint16_t* rank, int64_t heads, int n, int len, int first, int stride,
                 int pieces, int r, int32_t* perm, void* ws, size_t ws_bytes, hipStream_t s);
 

@@ -6,13 +6,17 @@
 // sorts one 8-bit digit (least significant first), so r <= 8 takes one
 // pass and r <= 16 two.
 //
-// A pass over a segment cut into tiles of kTile elements:
-//   1. hist:    each tile counts its digits in LDS -> counts[seg][digit][tile]
+// One launch sorts a batch of jobs (for example Q and K of a problem, or
+// every level of the causal recursion); each job is a set of equal-length
+// segments of one rank array.  A pass over the batch cuts every segment
+// into tiles of kTile elements:
+//   1. hist:    each tile counts its digits in LDS -> counts[seg][tile][digit]
 //   2. scatter: each tile sums the counts of the segment into its first
 //               output slot per digit, then each wave ranks its elements
 //               among equal digits of the lower lanes (ballot per digit
 //               bit), chunk by chunk in order, and writes the row index.
-// A segment of one tile takes a single fused kernel.
+// The workgroups of all jobs form one flat grid; a workgroup finds its job
+// by scanning the (few) job start offsets.
 //
 // HBM traffic per pass: 2 bytes of rank read twice (hist + scatter) or
 // 4 bytes of input permutation + 2 of rank per element, 4 bytes written.
@@ -30,40 +34,57 @@ struct SortPass {
   int n;
   int len, first, stride, pieces;
   const int32_t* perm_in;   // [segs][len] or null (identity over the segment)
-  int shift, bits;
   int32_t* perm_out;        // [segs][len]
   int tiles;
-  int32_t* counts;          // [segs][256][tiles]
+  int32_t* counts;          // [segs][tiles][256]
+  uint32_t block0;          // first workgroup of this job in the flat grid
 };
 
+struct SortBatch {
+  SortPass job[kSortMaxJobs];
+  int njobs;
+  int shift, bits;
+};
+
+// The job, segment and tile of workgroup `b` of the flat grid.
+__device__ __forceinline__ const SortPass& find_job(const SortBatch& B, uint32_t b, int64_t* seg, int* tile) {
+  int j = 0;
+  for (int i = 1; i < B.njobs; ++i) j = b >= B.job[i].block0 ? i : j;
+  const SortPass& p = B.job[j];
+  const uint32_t local = b - p.block0;
+  *seg = local / static_cast<uint32_t>(p.tiles);
+  *tile = static_cast<int>(local % static_cast<uint32_t>(p.tiles));
+  return p;
+}
+
 // Row (within the head) of element e of segment `seg`, and its digit.
-__device__ __forceinline__ void sort_elem(const SortPass& p, int64_t seg, int e, int32_t* row,
-                                          uint32_t* digit) {
+__device__ __forceinline__ void sort_elem(const SortPass& p, int shift, int bits, int64_t seg, int e,
+                                          int32_t* row, uint32_t* digit) {
   const int64_t hd = seg / p.pieces;
   const int piece = static_cast<int>(seg % p.pieces);
   int32_t r = p.perm_in ? p.perm_in[seg * p.len + e] : p.first + piece * p.stride + e;
   *row = r;
-  *digit = (static_cast<uint32_t>(p.rank[hd * p.n + r]) >> p.shift) & ((1u << p.bits) - 1u);
+  *digit = (static_cast<uint32_t>(p.rank[hd * p.n + r]) >> shift) & ((1u << bits) - 1u);
 }
 
-__global__ __launch_bounds__(kSortThreads) void sort_hist_kernel(SortPass p) {
+__global__ __launch_bounds__(kSortThreads) void sort_hist_kernel(SortBatch B) {
   __shared__ int hist[256];
-  const int tile = blockIdx.x;
-  const int64_t seg = blockIdx.y;
-  const int nb = 1 << p.bits;
-  for (int b = threadIdx.x; b < nb; b += kSortThreads) hist[b] = 0;
+  int64_t seg;
+  int tile;
+  const SortPass& p = find_job(B, blockIdx.x, &seg, &tile);
+  for (int b = threadIdx.x; b < 256; b += kSortThreads) hist[b] = 0;
   __syncthreads();
   const int e0 = tile * kTile;
   const int e1 = min(p.len, e0 + kTile);
   for (int e = e0 + threadIdx.x; e < e1; e += kSortThreads) {
     int32_t row;
     uint32_t dg;
-    sort_elem(p, seg, e, &row, &dg);
+    sort_elem(p, B.shift, B.bits, seg, e, &row, &dg);
     atomicAdd(&hist[dg], 1);
   }
   __syncthreads();
-  for (int b = threadIdx.x; b < nb; b += kSortThreads)
-    p.counts[(seg * 256 + b) * p.tiles + tile] = hist[b];
+  for (int b = threadIdx.x; b < 256; b += kSortThreads)
+    p.counts[(seg * p.tiles + tile) * 256 + b] = hist[b];
 }
 
 // Rank the wave's 64 elements among equal digits: the mask of lanes with the
@@ -90,9 +111,9 @@ __device__ __forceinline__ uint64_t wave_peers(bool valid, uint32_t dg, int bits
 // (LDS operations of one wave complete in issue order, so the chunks stay
 // ordered while their ranking overlaps).
 constexpr int kChunks = kWaveSpan / 64;
-__device__ __forceinline__ void scatter_tile(const SortPass& p, int64_t seg, int e0, int e1,
-                                             const int* base, int (*wh)[256]) {
-  const int nb = 1 << p.bits;
+__device__ __forceinline__ void scatter_tile(const SortPass& p, int shift, int bits, int64_t seg, int e0,
+                                             int e1, const int* base, int (*wh)[256]) {
+  const int nb = 1 << bits;
   const int w = threadIdx.x >> 6;
   const int lane = threadIdx.x & 63;
   const int ws = e0 + w * kWaveSpan;
@@ -103,7 +124,7 @@ __device__ __forceinline__ void scatter_tile(const SortPass& p, int64_t seg, int
     const int e = ws + 64 * c + lane;
     row[c] = 0;
     dg[c] = 0;
-    if (e < e1) sort_elem(p, seg, e, &row[c], &dg[c]);
+    if (e < e1) sort_elem(p, shift, bits, seg, e, &row[c], &dg[c]);
   }
   for (int i = threadIdx.x; i < kSortWaves * 256; i += kSortThreads) (&wh[0][0])[i] = 0;
   __syncthreads();
@@ -125,7 +146,7 @@ __device__ __forceinline__ void scatter_tile(const SortPass& p, int64_t seg, int
     if (ws + 64 * c >= e1) break;                 // wave-uniform
     const bool valid = ws + 64 * c + lane < e1;
     int below, cnt;
-    const uint64_t peers = wave_peers(valid, dg[c], p.bits, lane, &below, &cnt);
+    const uint64_t peers = wave_peers(valid, dg[c], bits, lane, &below, &cnt);
     int slot = 0;
     if (valid && below == 0) slot = atomicAdd(&wh[w][dg[c]], cnt);
     const int leader = valid ? static_cast<int>(__builtin_ctzll(peers)) : lane;
@@ -136,25 +157,33 @@ __device__ __forceinline__ void scatter_tile(const SortPass& p, int64_t seg, int
 
 // Tile t of a segment: its first slot per digit is the number of elements
 // with a smaller digit in the segment plus those with the same digit in the
-// tiles before it (read from the per-tile counts of the histogram pass).
-__global__ __launch_bounds__(kSortThreads) void sort_scatter_kernel(SortPass p) {
+// tiles before it (read from the per-tile counts of the histogram pass;
+// thread b reads digit b of every tile, so each tile's row is one
+// coalesced 1 KiB read).
+__global__ __launch_bounds__(kSortThreads) void sort_scatter_kernel(SortBatch B) {
   __shared__ int wh[kSortWaves][256];
   __shared__ int base[256];
   __shared__ int tot[256];
-  const int tile = blockIdx.x;
-  const int64_t seg = blockIdx.y;
-  const int nb = 1 << p.bits;
+  int64_t seg;
+  int tile;
+  const SortPass& p = find_job(B, blockIdx.x, &seg, &tile);
   const int e0 = tile * kTile;
   const int e1 = min(p.len, e0 + kTile);
-  for (int b = threadIdx.x; b < 256; b += kSortThreads) {
+  {
+    const int b = threadIdx.x;                    // kSortThreads == 256 digits
+    const int32_t* c = p.counts + seg * p.tiles * 256 + b;
     int before = 0, all = 0;
-    if (b < nb) {
-      const int32_t* c = p.counts + (seg * 256 + b) * p.tiles;
-      for (int t = 0; t < p.tiles; ++t) {
-        const int x = c[t];
-        before += t < tile ? x : 0;
-        all += x;
-      }
+    int t = 0;
+    for (; t + 4 <= p.tiles; t += 4) {
+      const int x0 = c[(t + 0) * 256], x1 = c[(t + 1) * 256], x2 = c[(t + 2) * 256], x3 = c[(t + 3) * 256];
+      before += (t + 0 < tile ? x0 : 0) + (t + 1 < tile ? x1 : 0) + (t + 2 < tile ? x2 : 0) +
+                (t + 3 < tile ? x3 : 0);
+      all += x0 + x1 + x2 + x3;
+    }
+    for (; t < p.tiles; ++t) {
+      const int x = c[t * 256];
+      before += t < tile ? x : 0;
+      all += x;
     }
     base[b] = before;
     tot[b] = all;
@@ -180,115 +209,88 @@ __global__ __launch_bounds__(kSortThreads) void sort_scatter_kernel(SortPass p) 
     }
   }
   __syncthreads();
-  scatter_tile(p, seg, e0, e1, base, wh);
+  scatter_tile(p, B.shift, B.bits, seg, e0, e1, base, wh);
 }
 
-// Whole segment in one tile: histogram, scan and scatter in one block.
-__global__ __launch_bounds__(kSortThreads) void sort_single_tile_kernel(SortPass p) {
-  __shared__ int wh[kSortWaves][256];
-  __shared__ int base[256];
-  const int64_t seg = blockIdx.x;
-  const int nb = 1 << p.bits;
-  for (int b = threadIdx.x; b < 256; b += kSortThreads) base[b] = 0;
-  __syncthreads();
-  for (int e = threadIdx.x; e < p.len; e += kSortThreads) {
-    int32_t row;
-    uint32_t dg;
-    sort_elem(p, seg, e, &row, &dg);
-    atomicAdd(&base[dg], 1);
-  }
-  __syncthreads();
-  if (threadIdx.x < 64) {                         // exclusive scan of the 256 digit totals
-    const int lane = threadIdx.x;
-    int v[4];
-    int sum = 0;
-    for (int i = 0; i < 4; ++i) {
-      v[i] = base[lane * 4 + i];
-      sum += v[i];
-    }
-    int incl = sum;
-    for (int off = 1; off < 64; off <<= 1) {
-      const int y = __shfl_up(incl, off);
-      if (lane >= off) incl += y;
-    }
-    int run = incl - sum;
-    for (int i = 0; i < 4; ++i) {
-      base[lane * 4 + i] = run;
-      run += v[i];
-    }
-  }
-  __syncthreads();
-  (void)nb;
-  scatter_tile(p, seg, 0, p.len, base, wh);
-}
-
-size_t sort_ws_bytes(int64_t heads, int len, int pieces, int r) {
-  const int64_t segs = heads * pieces;
+static size_t job_ws_bytes(int64_t segs, int len, int r) {
   const int64_t tiles = (static_cast<int64_t>(len) + kTile - 1) / kTile;
   size_t bytes = align_up(static_cast<size_t>(segs) * 256 * (tiles < 1 ? 1 : tiles) * 4, 256);
   if (r > 8) bytes += align_up(static_cast<size_t>(segs) * len * 4, 256);
   return bytes;
 }
 
-static int run_pass(SortPass p, int64_t segs, hipStream_t s) {
-  if (p.tiles == 1) {
-    hipLaunchKernelGGL(sort_single_tile_kernel, dim3(static_cast<unsigned>(segs)),
-                       dim3(kSortThreads), 0, s, p);
-    return after_launch("sort (single tile)", s);
+size_t sort_ws_bytes(int64_t heads, int len, int pieces, int r) { return job_ws_bytes(heads * pieces, len, r); }
+
+size_t sort_batch_ws_bytes(const SortJobDesc* jobs, int njobs, int r) {
+  size_t bytes = 0;
+  for (int j = 0; j < njobs; ++j) bytes += job_ws_bytes(jobs[j].heads * jobs[j].pieces, jobs[j].len, r);
+  return bytes;
+}
+
+int launch_sort_batch(const SortJobDesc* jobs, int njobs, int r, void* ws, size_t ws_bytes, hipStream_t s) {
+  if (njobs < 0 || njobs > kSortMaxJobs) {
+    set_error("sort: %d jobs in one batch (at most %d)", njobs, kSortMaxJobs);
+    return HA_EINVAL;
   }
-  dim3 g(p.tiles, static_cast<unsigned>(segs));
-  hipLaunchKernelGGL(sort_hist_kernel, g, dim3(kSortThreads), 0, s, p);
-  HA_TRY(after_launch("sort hist", s));
-  hipLaunchKernelGGL(sort_scatter_kernel, g, dim3(kSortThreads), 0, s, p);
-  return after_launch("sort scatter", s);
+  if (ws_bytes < sort_batch_ws_bytes(jobs, njobs, r)) {
+    set_error("sort: workspace %zu < %zu bytes", ws_bytes, sort_batch_ws_bytes(jobs, njobs, r));
+    return HA_EWORKSPACE;
+  }
+  Carve cv(ws, ws_bytes);
+  SortBatch B{};
+  int32_t* tmp[kSortMaxJobs] = {};
+  int32_t* out[kSortMaxJobs] = {};
+  uint64_t blocks = 0;
+  for (int j = 0; j < njobs; ++j) {
+    const SortJobDesc& d = jobs[j];
+    const int64_t segs = d.heads * d.pieces;
+    if (segs == 0 || d.len == 0) continue;
+    const int tiles = (d.len + kTile - 1) / kTile;
+    SortPass& p = B.job[B.njobs++];
+    p.rank = d.rank;
+    p.n = d.n;
+    p.len = d.len;
+    p.first = d.first;
+    p.stride = d.stride;
+    p.pieces = d.pieces;
+    p.tiles = tiles;
+    p.counts = cv.take<int32_t>(static_cast<size_t>(segs) * 256 * tiles);
+    p.perm_in = nullptr;
+    out[B.njobs - 1] = d.perm;
+    tmp[B.njobs - 1] = r > 8 ? cv.take<int32_t>(static_cast<size_t>(segs) * d.len) : nullptr;
+    p.block0 = static_cast<uint32_t>(blocks);
+    blocks += static_cast<uint64_t>(segs) * tiles;
+  }
+  if (B.njobs == 0) return HA_OK;
+  if (blocks >= (uint64_t(1) << 31)) {
+    set_error("sort: %llu tiles in one batch", static_cast<unsigned long long>(blocks));
+    return HA_EUNSUPPORTED;
+  }
+  const dim3 grid(static_cast<unsigned>(blocks));
+  timing_begin(HA_K_SORT, s);
+  int st = HA_OK;
+  for (int pass = 0; pass < (r > 8 ? 2 : 1) && st == HA_OK; ++pass) {
+    const bool two = r > 8;
+    B.shift = pass == 0 ? 0 : 8;
+    B.bits = two ? (pass == 0 ? 8 : r - 8) : r;
+    for (int j = 0; j < B.njobs; ++j) {
+      B.job[j].perm_in = pass == 0 ? nullptr : tmp[j];
+      B.job[j].perm_out = (two && pass == 0) ? tmp[j] : out[j];
+    }
+    hipLaunchKernelGGL(sort_hist_kernel, grid, dim3(kSortThreads), 0, s, B);
+    st = after_launch("sort hist", s);
+    if (st != HA_OK) break;
+    hipLaunchKernelGGL(sort_scatter_kernel, grid, dim3(kSortThreads), 0, s, B);
+    st = after_launch("sort scatter", s);
+  }
+  timing_end(HA_K_SORT, s);
+  return st;
 }
 
 int launch_sort(const uint16_t* rank, int64_t heads, int n, int len, int first, int stride,
                 int pieces, int r, int32_t* perm, void* ws, size_t ws_bytes, hipStream_t s) {
-  const int64_t segs = heads * pieces;
-  if (segs == 0 || len == 0) return HA_OK;
-  if (ws_bytes < sort_ws_bytes(heads, len, pieces, r)) {
-    set_error("sort: workspace %zu < %zu bytes", ws_bytes, sort_ws_bytes(heads, len, pieces, r));
-    return HA_EWORKSPACE;
-  }
-  const int tiles = (len + kTile - 1) / kTile;
-  Carve cv(ws, ws_bytes);
-  int32_t* counts = cv.take<int32_t>(static_cast<size_t>(segs) * 256 * tiles);
-  int32_t* tmp = r > 8 ? cv.take<int32_t>(static_cast<size_t>(segs) * len) : nullptr;
-
-  SortPass p;
-  p.rank = rank;
-  p.n = n;
-  p.len = len;
-  p.first = first;
-  p.stride = stride;
-  p.pieces = pieces;
-  p.tiles = tiles;
-  p.counts = counts;
-  timing_begin(HA_K_SORT, s);
-  int st;
-  if (r <= 8) {
-    p.perm_in = nullptr;
-    p.shift = 0;
-    p.bits = r;
-    p.perm_out = perm;
-    st = run_pass(p, segs, s);
-  } else {
-    p.perm_in = nullptr;
-    p.shift = 0;
-    p.bits = 8;
-    p.perm_out = tmp;
-    st = run_pass(p, segs, s);
-    if (st == HA_OK) {
-      p.perm_in = tmp;
-      p.shift = 8;
-      p.bits = r - 8;
-      p.perm_out = perm;
-      st = run_pass(p, segs, s);
-    }
-  }
-  timing_end(HA_K_SORT, s);
-  return st;
+  SortJobDesc d{rank, heads, n, len, first, stride, pieces, perm};
+  return launch_sort_batch(&d, 1, r, ws, ws_bytes, s);
 }
 
 }  // namespace ha
