@@ -245,7 +245,7 @@ __global__ __launch_bounds__(64 * NW, (min_waves<T, D, KIND, NW, QPW>())) void a
       for (int j = tid + G::NT; j < nbl; j += G::NT) brow[j] = key_row(ka0 + j);
     }
     if (samp) {
-      const int tq = q0 / p.b_eff;
+      const int tblo = (q0 / p.b_eff) * p.b_k;   // the workgroup's key block (when it has one)
       int* raw = samp_multi ? srow : rrow;
       for (int c = 64 * wave; c < p.m; c += G::NT) {
         const int i = c + lane;
@@ -255,7 +255,8 @@ __global__ __launch_bounds__(64 * NW, (min_waves<T, D, KIND, NW, QPW>())) void a
           spos[i] = spi;
           raw[i] = first ? sr : key_row(spi);
         }
-        const uint64_t keep = __ballot(i < p.m && (samp_multi || (spi / p.b_k) != tq));
+        const uint64_t keep =
+            __ballot((i < p.m) & (samp_multi | (static_cast<unsigned>(spi - tblo) >= static_cast<unsigned>(p.b_k))));
         if (lane == 0) ccount[c / 64] = __popcll(keep);
       }
       __syncthreads();
@@ -266,7 +267,7 @@ __global__ __launch_bounds__(64 * NW, (min_waves<T, D, KIND, NW, QPW>())) void a
           int base = 0;
           for (int k = 0; k < c / 64; ++k) base += ccount[k];
           const int i = c + lane;
-          const bool keep = i < p.m && (spos[i] / p.b_k) != tq;
+          const bool keep = (i < p.m) && (static_cast<unsigned>(spos[i] - tblo) >= static_cast<unsigned>(p.b_k));
           const uint64_t bal = __ballot(keep);
           const uint64_t lower = lane == 0 ? 0ull : (~0ull >> (64 - lane));
           if (keep) srow[base + __popcll(bal & lower)] = rrow[i];
@@ -376,7 +377,7 @@ __global__ __launch_bounds__(64 * NW, (min_waves<T, D, KIND, NW, QPW>())) void a
       const float bias = isB ? p.log2w : 0.f;
       const bool diag = LEAF && (kb + kKT - 1 > wq0);
       const bool need_mask = kcnt < kKT || (isB ? samp_multi : (multi_block || diag));
-      const int row_blk = ql[0] / p.b_eff;
+      const int blo = LEAF ? 0 : (ql[0] / p.b_eff) * p.b_k;   // the query's key block [blo, blo + b_k)
 
       auto k_read = [&](int kt, int c) {
         return *reinterpret_cast<const bf16x8*>(&ks[(32 * kt + col) * G::KSTR + 16 * c + 8 * h2]);
@@ -394,11 +395,11 @@ __global__ __launch_bounds__(64 * NW, (min_waves<T, D, KIND, NW, QPW>())) void a
           const int j = 32 * kt + 8 * (r >> 2) + 4 * h2 + (r & 3);
           bool ok = j < kcnt;
           if (isB) {
-            if (samp_multi) ok = ok && (spos[kb + min(j, kcnt - 1)] / p.b_k) != row_blk;
+            if (samp_multi) ok = ok && (static_cast<unsigned>(spos[kb + min(j, kcnt - 1)] - blo) >= static_cast<unsigned>(p.b_k));
           } else if (LEAF) {
             ok = ok && (kb + j <= ql[0]);
           } else if (multi_block) {
-            ok = ok && ((kb + j) / p.b_k) == row_blk;
+            ok = ok && (static_cast<unsigned>(kb + j - blo) < static_cast<unsigned>(p.b_k));
           }
           if (!ok) sv[r] = -INFINITY;
         }
@@ -726,10 +727,13 @@ __global__ __launch_bounds__(64 * NW, (min_waves<T, D, KIND, NW, QPW>())) void a
   const int c = lane & 7;                         // this lane's 4-column chunk of a slice
 #pragma unroll
   for (int u = 0; u < NQT; ++u) {
+    // ltot >= 1 when any key counted (the weights are relative to a running
+    // reference that some counted key reached), so the hardware reciprocal
+    // and base-2 logarithm (1 ulp) serve
     const float ltot = lsum[u] + __shfl_xor(lsum[u], 32);
     const bool any = ltot > 0.f;
-    const float inv = any ? 1.f / ltot : 0.f;
-    const float lse2 = any ? (mrun[u] + log2f(ltot)) * kLn2 : -INFINITY;
+    const float inv = any ? __builtin_amdgcn_rcpf(ltot) : 0.f;
+    const float lse2 = any ? (mrun[u] + __builtin_amdgcn_logf(ltot)) * kLn2 : -INFINITY;
     // rows of the staged queries (clamped into range; `valid` marks the real ones)
     const uint64_t valid = __ballot(ql[u] < qend);
     if (h2 == 0) {
@@ -766,17 +770,20 @@ __global__ __launch_bounds__(64 * NW, (min_waves<T, D, KIND, NW, QPW>())) void a
 #pragma unroll
         for (int t = 0; t < NDT; ++t) oldv[t][k] = *reinterpret_cast<const floatx4*>(p.acc_o + ridx * D + 32 * t + 4 * c);
       }
+      // lse = m + ln(e^(l1 - m) + e^(l2 - m)), m = max(l1, l2): the sum lies
+      // in [1, 2], so hardware exp2 / log2 / reciprocal (1 ulp) serve
 #pragma unroll
       for (int k = 0; k < 4; ++k) {
         const float mm = fmaxf(l1[k], lqk[k]);
-        if (mm == -INFINITY) {
-          lse_out[k] = -INFINITY;
-          w_new[k] = 0.f;
-        } else {
-          lse_out[k] = mm + logf(expf(l1[k] - mm) + expf(lqk[k] - mm));
-          w_old[k] = expf(l1[k] - lse_out[k]);
-          w_new[k] = expf(lqk[k] - lse_out[k]);
-        }
+        const bool none = mm == -INFINITY;
+        const float ms = none ? 0.f : mm;
+        const float ea = fast_exp2((l1[k] - ms) * kLog2e);
+        const float eb = fast_exp2((lqk[k] - ms) * kLog2e);
+        const float sum = ea + eb;
+        const float r = __builtin_amdgcn_rcpf(sum);
+        w_old[k] = none ? 0.f : ea * r;
+        w_new[k] = none ? 0.f : eb * r;
+        lse_out[k] = none ? -INFINITY : ms + __builtin_amdgcn_logf(sum) * kLn2;
       }
     }
 #pragma unroll
