@@ -98,7 +98,7 @@ __global__ __launch_bounds__(64 * NW, (min_waves<T, D, KIND, NW, QPW>())) void a
 
   const int tid = threadIdx.x;
   const int lane = tid & 63;
-  const int wave = tid >> 6;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);   // uniform: keeps wave-level bounds scalar
   const int h2 = lane >> 5;             // half-wave
   const int col = lane & 31;            // query column of this lane in a 32-query tile
 
@@ -290,6 +290,9 @@ __global__ __launch_bounds__(64 * NW, (min_waves<T, D, KIND, NW, QPW>())) void a
     mrun[u] = -INFINITY;
     lsum[u] = 0.f;
   }
+  // kept in step with mrun[0] by the one-tile bf16 body: -mrun[0], or 0
+  // while the lane has no reference
+  float nref = 0.f;
 
   const int nB = (nsamp + kKT - 1) / kKT;
   const int ntiles = nA + nB;
@@ -300,10 +303,17 @@ __global__ __launch_bounds__(64 * NW, (min_waves<T, D, KIND, NW, QPW>())) void a
     const bool isB = it >= nA;
     const int kb = isB ? (it - nA) * kKT : ka0 + it * kKT;
     const int kcnt = isB ? min(kKT, nsamp - kb) : min(kKT, ka1 - kb);
-    if (LEAF && kcnt == kKT) {
+    if constexpr (LEAF) {
+      // rows past the leaf's last key repeat that key (finite values, masked)
 #pragma unroll
       for (int c = 0; c < G::CPT; ++c) {
-        const uint32_t off = leaf_off + static_cast<uint32_t>((kb + c * JSTEP) * D) * sizeof(T);
+        uint32_t off;
+        if (kcnt == kKT) {
+          off = leaf_off + static_cast<uint32_t>((kb + c * JSTEP) * D) * sizeof(T);
+        } else {
+          const int j = min(j_first + c * JSTEP, kcnt - 1);
+          off = static_cast<uint32_t>((krow0 + kb + j) * D + G::EPC * c_in_row) * sizeof(T);
+        }
         kreg[c] = ld16(kbase, off);
         vreg[c] = ld16(vbase, off);
       }
@@ -404,7 +414,7 @@ __global__ __launch_bounds__(64 * NW, (min_waves<T, D, KIND, NW, QPW>())) void a
           if (!ok) sv[r] = -INFINITY;
         }
       };
-      auto offset = [&]() { return bias - (mrun[0] == -INFINITY ? 0.f : mrun[0]); };
+      auto offset = [&]() { return bias + nref; };
       // weights of S elements i, i+1 into the B operands of the half's two
       // 16-key chunks (elements 0..7 -> pa, 8..15 -> pb), summed into l
       auto p_pair = [&](const floatx16& sv, int i, float off, bf16x8& pa, bf16x8& pb, float& l) {
@@ -436,6 +446,7 @@ __global__ __launch_bounds__(64 * NW, (min_waves<T, D, KIND, NW, QPW>())) void a
             for (int r = 0; r < 16; ++r) o[0][t][r] *= alpha;
           lsum[0] *= alpha;
           mrun[0] = mnew;
+          nref = mnew == -INFINITY ? 0.f : -mnew;
         }
       };
       // rare path: some lane's weights of the half outgrew the reference
