@@ -474,6 +474,7 @@ __global__ __launch_bounds__(64 * NW, (min_waves<T, D, KIND, NW, QPW>())) void a
       // scheduling fences keep the compiler from regrouping it.
       bf16x8 pa, pb;
       float l0 = 0.f;
+      if (it == 0) raise_half(s0);        // first tile: take the reference before any weight
       {
         const float off = offset();
         constexpr int kPer = 16 / NQF;
