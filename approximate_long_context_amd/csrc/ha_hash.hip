@@ -6,11 +6,17 @@
 // the rank = position of that code in the reflected-binary Gray sequence,
 // so that consecutive buckets differ in one hash bit.
 //
-// The fp32 dot products follow one fixed order so that ranks are exact
-// and reproducible: the d products are cut into groups of 8 consecutive
-// elements, each group is summed by halving (pairs 4, 2, 1 apart), and the
-// d/8 group sums are combined by halving as well (pairs d/16, ..., 1
-// apart).  No multiply-add contraction.
+// Bit p is the sign of the exact real dot product <x, R_p> (an exact zero,
+// or a non-finite value in x or R_p, gives 0), so ranks do not depend on an
+// evaluation order.  A lane computes t = sum_k x_k R_pk in fp32 with fused
+// multiply-adds (four interleaved chains); its distance from the exact sum
+// is at most gamma_{d+4} sum_k |x_k R_pk| + d 2^-150 (each step rounds once;
+// the second term covers subnormal partial sums), and the sum of magnitudes
+// is at most max_k |x_k| * sum_k |R_pk|.  When t is finite and |t| exceeds
+// that bound (with margin) its sign is the exact sign.  Otherwise (a fraction of a percent of
+// random rows) an fp64 pass with exact products decides unless |t| is below
+// 2 d 2^-53 sum |x_k R_pk|, and what remains (exact cancellation) goes to an
+// exact integer accumulator.
 //
 // HBM traffic: each input row is read once (d * elem bytes) and 2 bytes
 // of rank are written.
@@ -46,67 +52,162 @@ __device__ __forceinline__ uint32_t gray_inverse(uint32_t x) {
   return x;
 }
 
-// Halving sum of v[0 .. N): pairs N/2 apart, then N/4 apart, ... (the fixed
-// order of the group sums).
-template <int N>
-__device__ __forceinline__ float halving_sum(const float* v) {
-#pragma clang fp contract(off)
-  if constexpr (N == 1) {
-    return v[0];
-  } else {
-    float h[N / 2];
-#pragma unroll
-    for (int i = 0; i < N / 2; ++i) h[i] = v[i] + v[i + N / 2];
-    return halving_sum<N / 2>(h);
+// The exact sign bit of <x, R_p> for a row that the fp32 bound left open:
+// fp64 with exact products first, then, for sums that cancel below the
+// fp64 bound, exact integer arithmetic.  `row` is the row (d elements of
+// T, in LDS or global memory), `rp` projection p.  Rare: its digit array
+// lives in private memory and its loops stay rolled, so it costs the
+// common path no registers.
+template <typename T, int D>
+__device__ __forceinline__ uint32_t exact_sign_bit(const T* row, const float* rp) {
+  auto elem = [&](int k) -> float {
+    if constexpr (sizeof(T) == 2) {
+      return __uint_as_float(static_cast<uint32_t>(__builtin_bit_cast(uint16_t, row[k])) << 16);
+    } else {
+      return row[k];
+    }
+  };
+  double t = 0.0, s = 0.0;
+#pragma unroll 1
+  for (int k = 0; k < D; ++k) {
+    const double pr = static_cast<double>(elem(k)) * static_cast<double>(rp[k]);   // exact
+    t += pr;
+    s += fabs(pr);
   }
+  if (!(s <= 1e300)) return 0u;                  // a non-finite operand (products stay below 2^257)
+  if (fabs(t) > 2.0 * D * 0x1p-53 * s) return t > 0.0 ? 1u : 0u;
+  if (s == 0.0) return 0u;
+  // exact: sum of m 2^e with m = mx mr < 2^48 and e >= -298, as signed
+  // 32-bit digits (digit i weighs 2^(32 i - 298)) accumulated in int64
+  constexpr int kLimbs = 19;
+  int64_t limb[kLimbs];
+#pragma unroll 1
+  for (int i = 0; i < kLimbs; ++i) limb[i] = 0;
+#pragma unroll 1
+  for (int k = 0; k < D; ++k) {
+    const uint32_t xb = __float_as_uint(elem(k)), rb = __float_as_uint(rp[k]);
+    uint32_t ex = (xb >> 23) & 255u, er = (rb >> 23) & 255u;
+    uint64_t mx = xb & 0x7FFFFFu, mr = rb & 0x7FFFFFu;
+    if (ex) mx |= 0x800000u; else ex = 1;       // value = m 2^(e - 150)
+    if (er) mr |= 0x800000u; else er = 1;
+    const uint64_t m = mx * mr;
+    if (m == 0) continue;
+    const int sh = static_cast<int>(ex + er) - 300 + 298;
+    const int q = sh >> 5, r = sh & 31;
+    const uint64_t lo = (m & 0xFFFFFFFFull) << r, hi = (m >> 32) << r;
+    int64_t d0 = static_cast<int64_t>(lo & 0xFFFFFFFFull);
+    int64_t d1 = static_cast<int64_t>((lo >> 32) + (hi & 0xFFFFFFFFull));
+    int64_t d2 = static_cast<int64_t>(hi >> 32);
+    if ((xb ^ rb) >> 31) {
+      d0 = -d0;
+      d1 = -d1;
+      d2 = -d2;
+    }
+    limb[q] += d0;
+    limb[q + 1] += d1;
+    limb[q + 2] += d2;
+  }
+  int64_t carry = 0;
+  bool nonzero = false;
+#pragma unroll 1
+  for (int i = 0; i < kLimbs; ++i) {
+    const int64_t v = limb[i] + carry;
+    const int64_t low = v & 0xFFFFFFFFll;         // in [0, 2^32)
+    carry = (v - low) >> 32;                       // exact: v - low is a multiple of 2^32
+    nonzero |= low != 0;
+  }
+  return (carry > 0 || (carry == 0 && nonzero)) ? 1u : 0u;
 }
 
-// One row per lane.  A workgroup of 4 waves takes 256 consecutive rows per
-// step: the rows are read with coalesced 16-byte loads into LDS (padded
-// rows, conflict-free), then each lane walks its own row group by group.
-// The projection values are uniform across lanes and come from scalar
-// loads.  Per row: d r products and the adds of the two halving levels.
+// A workgroup takes 64 consecutive rows per step, one row per lane, with
+// one wave per 128 bytes of row (NW = d * elem / 128 waves: 1 for bf16 at
+// d = 64).  The rows are read with coalesced 16-byte loads into LDS (padded
+// rows, conflict-free); the next step's chunks are loaded into registers
+// while this step computes.  Wave w converts its 128-byte column slice of
+// its lane's row to fp32 and, one projection at a time (the projection
+// values are uniform and come from scalar loads), takes the partial dot
+// product with fused multiply-adds; wave 0 adds the partials of the other
+// waves (through LDS), tests the bound and sets the bit.
+constexpr int kHashRows = 64;
+
 template <typename T, int D, int R>
-__global__ __launch_bounds__(256) void hash_kernel(const T* __restrict__ x, int64_t rows,
+__global__ __launch_bounds__(D * sizeof(T) / 2) void hash_kernel(const T* __restrict__ x, int64_t rows,
                                                    const float* __restrict__ Rm,
                                                    uint16_t* __restrict__ rank) {
-#pragma clang fp contract(off)
-  constexpr int G = D / 8;                          // groups of 8 elements
   constexpr int ROWB = D * static_cast<int>(sizeof(T));
+  constexpr int NW = ROWB / 128;                    // waves per workgroup
+  constexpr int NT = 64 * NW;
+  constexpr int DW = D / NW;                        // elements per wave
   constexpr int CH = ROWB / 16;                     // 16-byte chunks per row
+  constexpr int CPT = kHashRows * CH / NT;          // chunks per thread and step (8)
   constexpr int STR = ROWB + 16;                    // LDS row stride (bytes)
-  constexpr int TR = 256;                           // rows per workgroup step
+  constexpr int TR = kHashRows;
+  static_assert(NW >= 1 && DW % 8 == 0 && CPT * NT == TR * CH, "hash split");
+  // |t - <x, R_p>| <= gamma_{D+4} max|x| sum|R_p| + D 2^-150 (see above);
+  // the factor 1.0001 covers the rounding of the bound itself, and the
+  // absolute term D 2^-148 also covers a bound that falls in the subnormals
+  constexpr float kGam = 1.0001f * (D + 4) * 0x1p-24f / (1.f - (D + 4) * 0x1p-24f);
+  constexpr float kAbs = D * 0x1p-148f;
   __shared__ __attribute__((aligned(16))) char stage[TR * STR];
+  __shared__ float part[NW > 1 ? NW : 1][R + 1][64];   // per wave: partial sums and max|x| (NW > 1)
+  __shared__ float rn1[R];
   const int tid = threadIdx.x;
+  const int lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const char* xb = reinterpret_cast<const char*>(x);
 
-  for (int64_t r0 = static_cast<int64_t>(blockIdx.x) * TR; r0 < rows; r0 += static_cast<int64_t>(gridDim.x) * TR) {
-    const int nr = rows - r0 < TR ? static_cast<int>(rows - r0) : TR;
-    // coalesced staging: chunk q of the step = row q / CH, chunk q % CH
+  // sum_k |R_pk| per projection (lanes split k, a butterfly sums; wave 0
+  // publishes it, read back after the first step's barrier)
+  if (wave == 0) {
 #pragma unroll
-    for (int c = 0; c < CH; ++c) {
-      const int q = c * TR + tid;
-      const int rr = q / CH, cc = q % CH;
-      uint4v w = {0u, 0u, 0u, 0u};
-      if (rr < nr) w = *reinterpret_cast<const uint4v*>(xb + (r0 + rr) * ROWB + 16 * cc);
-      *reinterpret_cast<uint4v*>(stage + rr * STR + 16 * cc) = w;
+    for (int p = 0; p < R; ++p) {
+      float a = 0.f;
+#pragma unroll
+      for (int k = lane; k < D; k += 64) a += fabsf(Rm[p * D + k]);
+#pragma unroll
+      for (int h = 32; h >= 1; h >>= 1) a += __shfl_xor(a, h);
+      if (lane == 0) rn1[p] = a;
+    }
+  }
+
+  // coalesced staging: chunk q of a step = row q / CH, chunk q % CH
+  const int64_t rstep = static_cast<int64_t>(gridDim.x) * TR;
+  uint4v pre[CPT];
+  // rows past the end repeat the last row (their ranks are not written)
+  auto load_step = [&](int64_t r0) {
+#pragma unroll
+    for (int c = 0; c < CPT; ++c) {
+      const int q = c * NT + tid;
+      const int64_t rr = min(r0 + q / CH, rows - 1);
+      pre[c] = *reinterpret_cast<const uint4v*>(xb + rr * ROWB + 16 * (q % CH));
+    }
+  };
+  if (static_cast<int64_t>(blockIdx.x) * TR < rows) load_step(static_cast<int64_t>(blockIdx.x) * TR);
+  for (int64_t r0 = static_cast<int64_t>(blockIdx.x) * TR; r0 < rows; r0 += rstep) {
+    const int nr = rows - r0 < TR ? static_cast<int>(rows - r0) : TR;
+#pragma unroll
+    for (int c = 0; c < CPT; ++c) {
+      const int q = c * NT + tid;
+      *reinterpret_cast<uint4v*>(stage + (q / CH) * STR + 16 * (q % CH)) = pre[c];
     }
     __syncthreads();
+    if (r0 + rstep < rows) load_step(r0 + rstep);
 
-    const char* row = stage + tid * STR;
-    float xv[D];                                     // this lane's row in fp32
+    const char* row = stage + lane * STR;
+    const char* slice = row + wave * 128;
+    float xv[DW];                                    // this wave's slice of the lane's row, fp32
 #pragma unroll
-    for (int g = 0; g < G; ++g) {
+    for (int g = 0; g < DW / 8; ++g) {
       if constexpr (sizeof(T) == 2) {
-        const uint4v w = *reinterpret_cast<const uint4v*>(row + 16 * g);
+        const uint4v w = *reinterpret_cast<const uint4v*>(slice + 16 * g);
 #pragma unroll
         for (int i = 0; i < 4; ++i) {
           xv[8 * g + 2 * i] = __uint_as_float(w[i] << 16);
           xv[8 * g + 2 * i + 1] = __uint_as_float(w[i] & 0xFFFF0000u);
         }
       } else {
-        const floatx4 a = *reinterpret_cast<const floatx4*>(row + 32 * g);
-        const floatx4 b = *reinterpret_cast<const floatx4*>(row + 32 * g + 16);
+        const floatx4 a = *reinterpret_cast<const floatx4*>(slice + 32 * g);
+        const floatx4 b = *reinterpret_cast<const floatx4*>(slice + 32 * g + 16);
 #pragma unroll
         for (int i = 0; i < 4; ++i) {
           xv[8 * g + i] = a[i];
@@ -114,22 +215,56 @@ __global__ __launch_bounds__(256) void hash_kernel(const T* __restrict__ x, int6
         }
       }
     }
-    // one projection at a time (its d values sit in scalar registers)
-    uint32_t code = 0;
-#pragma unroll 1
-    for (int p = 0; p < R; ++p) {
-      const float* rp = Rm + p * D;
-      float gsum[G];
+    float xinf = 0.f;                                // max |x_k| (a NaN is skipped; t is then NaN)
 #pragma unroll
-      for (int g = 0; g < G; ++g) {
-        float pr[8];
+    for (int k = 0; k < DW; ++k) xinf = fmaxf(xinf, fabsf(xv[k]));
+
+    // the partial dot product of projection p over this wave's slice
+    auto partial = [&](int p) {
+      const float* rp = Rm + p * D + wave * DW;
+      float a0 = 0.f, a1 = 0.f, a2 = 0.f, a3 = 0.f;
 #pragma unroll
-        for (int i = 0; i < 8; ++i) pr[i] = xv[8 * g + i] * rp[8 * g + i];
-        gsum[g] = halving_sum<8>(pr);
+      for (int k = 0; k < DW; k += 4) {
+        a0 = fmaf(xv[k], rp[k], a0);
+        a1 = fmaf(xv[k + 1], rp[k + 1], a1);
+        a2 = fmaf(xv[k + 2], rp[k + 2], a2);
+        a3 = fmaf(xv[k + 3], rp[k + 3], a3);
       }
-      code |= (halving_sum<G>(gsum) > 0.f ? 1u : 0u) << p;
+      return (a0 + a1) + (a2 + a3);
+    };
+    // bit p from the full sum t (wave 0)
+    auto decide = [&](int p, float t) -> uint32_t {
+      const float bound = fmaf(xinf * rn1[p], kGam, kAbs);
+      // settled: beyond the bound and finite (a partial sum that overflowed
+      // leaves t infinite or NaN)
+      const float at = fabsf(t);
+      if (at > bound && at <= 0x1.fffffep127f) return t > 0.f ? 1u : 0u;
+      return exact_sign_bit<T, D>(reinterpret_cast<const T*>(row), Rm + p * D);
+    };
+    uint32_t code = 0;
+    if constexpr (NW == 1) {
+#pragma unroll 1
+      for (int p = 0; p < R; ++p) code |= decide(p, partial(p)) << p;
+    } else {
+#pragma unroll 1
+      for (int p = 0; p < R; ++p) part[wave][p][lane] = partial(p);
+      part[wave][R][lane] = xinf;
+      __syncthreads();
+      if (wave == 0) {
+#pragma unroll
+        for (int w = 1; w < NW; ++w) xinf = fmaxf(xinf, part[w][R][lane]);
+#pragma unroll 1
+        for (int p = 0; p < R; ++p) {
+          float t = part[0][p][lane];
+#pragma unroll
+          for (int w = 1; w < NW; ++w) t += part[w][p][lane];
+          code |= decide(p, t) << p;
+        }
+      }
     }
-    if (tid < nr) rank[r0 + tid] = static_cast<uint16_t>(gray_inverse(code));
+    if (wave == 0) {
+      if (lane < nr) rank[r0 + lane] = static_cast<uint16_t>(gray_inverse(code));
+    }
     __syncthreads();
   }
 }
@@ -137,10 +272,12 @@ __global__ __launch_bounds__(256) void hash_kernel(const T* __restrict__ x, int6
 template <typename T, int D>
 static int launch_hash_d(const T* x, int64_t rows, int r, const float* R, uint16_t* rank,
                          hipStream_t s) {
-  int64_t blocks = (rows + 255) / 256;
-  if (blocks > 8192) blocks = 8192;
+  constexpr int NT = 64 * (D * static_cast<int>(sizeof(T)) / 128);
+  int64_t blocks = (rows + kHashRows - 1) / kHashRows;
+  const int64_t cap = 256 * 2048 / NT;               // 32 waves per CU, then a grid-stride loop
+  if (blocks > cap) blocks = cap;
   if (blocks < 1) blocks = 1;
-  dim3 g(static_cast<unsigned>(blocks)), b(256);
+  dim3 g(static_cast<unsigned>(blocks)), b(NT);
   switch (r) {
 #define HA_HASH_CASE(RR) \
     case RR: hipLaunchKernelGGL((hash_kernel<T, D, RR>), g, b, 0, s, x, rows, R, rank); break;

@@ -470,10 +470,17 @@ def other_configs(ha, torch, dev, stream, reps=5):
         e1.record(stream)
         torch.cuda.synchronize()
         ms = e0.elapsed_time(e1) / reps
+        # per-kernel-class ms per forward, from a separate timed set of calls
+        ha.timing_enable(True)
+        for _ in range(reps):
+            ha.forward(q, k, v, out=out, workspace=ws, **w.method_args())
+        torch.cuda.synchronize()
+        kern = {kn: round(kms / reps, 4) for kn, (kms, cnt) in ha.timing_read().items() if cnt}
+        ha.timing_enable(False)
         f, _ = alg_flops(w, w.causal)
         res[name] = {"ms": ms, "tflops": f / (ms * 1e-3) / 1e12, "causal": w.causal, "n": w.n,
                      "heads": w.heads, "kv_heads": w.kv_heads, "head_dim": w.d,
-                     "block": w.block, "samples": w.samples}
+                     "block": w.block, "samples": w.samples, "kernels_ms": kern}
         del q, k, v, out, ws
     return res
 

@@ -304,10 +304,9 @@ int hyperattn_projections(uint64_t seed, int d, int proj_bits, float* dev_out, v
 
 /*
  * Bucket rank of each row of x ([S] Approach, Hamming-sorted LSH):
- * bit p of the code is 1 iff <x_row, R_p> > 0, the dot product taken in
- * fp32 with every product rounded, the d products cut into groups of 8
- * consecutive elements, each group summed by halving (pairs 4, 2, 1
- * apart) and the group sums by halving; rank = position of the code in
+ * bit p of the code is 1 iff the exact real dot product <x_row, R_p> is
+ * positive (no rounding: an exact zero gives 0, and a row or projection
+ * holding a NaN or an infinity gives 0); rank = position of the code in
  * the reflected-binary Gray sequence.
  *   x         device, [rows, d] of dtype (d in {64, 128})
  *   proj_dev  device, float32 [proj_bits, d] (from hyperattn_projections)

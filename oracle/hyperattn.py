@@ -25,6 +25,8 @@ the function that uses it):
   * the product with V re-uses the uniform column samples of the
     normaliser; [S] "Approach" names row-norm sampling for the product,
     which is a different estimator and not built here;
+  * a hash bit is the sign of the exact real dot product with the
+    projection (no rounding);
   * A = exp(Q K^T) with no softmax scale (callers pre-scale Q and K);
   * no clipping or threshold constants (none are printed);
   * samples are iid uniform *with replacement* over the sorted key
@@ -36,6 +38,7 @@ the function that uses it):
   * the non-causal call is one problem (node 1) and ignores min_seq_len.
 """
 
+import math
 from dataclasses import dataclass
 
 import numpy as np
@@ -59,55 +62,40 @@ class HAConfig:
 # "Builds on": Hamming sorted LSH)
 # ----------------------------------------------------------------------------
 
-def _padded_dim(d):
-    """Smallest 8 * 2^k >= d."""
-    g = 1
-    while 8 * g < d:
-        g *= 2
-    return 8 * g
-
-
-def _halving_sum_last(v):
-    """Sum over the last axis by repeated halving: v <- v[:h] + v[h:]."""
-    while v.shape[-1] > 1:
-        h = v.shape[-1] // 2
-        v = v[..., :h] + v[..., h:]
-    return v[..., 0]
-
-
-def projection_sums(x32, R):
-    """t[i, p] = <x_i, R_p> in fp32 with a fixed summation order.
-
-    Reading: the pages give no arithmetic for the hash.  Here every product
-    x_k * R[p][k] is rounded to fp32, the row is cut into consecutive groups
-    of 8 products, each group is summed by halving (pairs 4 apart, then 2,
-    then 1), and the group sums are summed by halving.  d is padded with
-    zeros to 8 * 2^k.  No fused multiply-add anywhere."""
-    x32 = np.asarray(x32, dtype=np.float32)
-    R = np.asarray(R, dtype=np.float32)
-    rows, d = x32.shape
-    r = R.shape[0]
-    dp = _padded_dim(d)
-    xp = np.zeros((rows, dp), dtype=np.float32)
-    xp[:, :d] = x32
-    rp = np.zeros((r, dp), dtype=np.float32)
-    rp[:, :d] = R
-    t = np.empty((rows, r), dtype=np.float32)
-    for p in range(r):
-        prod = xp * rp[p]                                  # fp32 products
-        groups = _halving_sum_last(prod.reshape(rows, dp // 8, 8))
-        t[:, p] = _halving_sum_last(groups)
-    return t
-
-
 def hash_codes(x32, R):
-    """Sign-bit code: bit p is 1 iff <x, R_p> > 0 (so +0, -0 and NaN give 0);
-    projection 0 is the least significant bit."""
-    t = projection_sums(x32, R)
-    bits = (t > 0).astype(np.uint32)
-    code = np.zeros(t.shape[0], dtype=np.uint32)
-    for p in range(t.shape[1]):
-        code |= bits[:, p] << np.uint32(p)
+    """Sign-bit code: bit p is 1 iff the exact real dot product <x, R_p> is
+    positive (so an exact zero gives 0); projection 0 is the least
+    significant bit.  A row or projection holding a non-finite value gives
+    bit 0.
+
+    Reading R3: the pages define the hash by the sign of the projection and
+    give no arithmetic, so the sign is that of the exact sum.  Computed here
+    as follows.  x (bf16 or fp32 values) and R (fp32) widen to fp64 exactly,
+    and each product x_k R_pk is exact in fp64 (two 24-bit significands).
+    Their fp64 sum t, in any order, is within (d - 1) u / (1 - (d - 1) u)
+    of S = sum_k |x_k R_pk| (u = 2^-53, no underflow or overflow over this
+    range), so |t| > 2 d u S fixes the sign.  The remaining cases take
+    math.fsum, whose correctly rounded result has the sign of the exact
+    sum."""
+    x = np.asarray(x32, dtype=np.float64)
+    Rd = np.asarray(R, dtype=np.float64)
+    rows, d = x.shape
+    code = np.zeros(rows, dtype=np.uint32)
+    finite_x = np.all(np.isfinite(x), axis=1)
+    for p in range(Rd.shape[0]):
+        if not np.all(np.isfinite(Rd[p])):
+            continue                                   # bit p is 0 for every row
+        with np.errstate(invalid="ignore", over="ignore"):
+            prod = x * Rd[p]                           # exact products
+            t = prod.sum(axis=1)
+            S = np.abs(prod).sum(axis=1)
+        sure = np.abs(t) > 2.0 * d * 2.0 ** -53 * S
+        bit = np.zeros(rows, dtype=bool)
+        bit[sure] = t[sure] > 0
+        for i in np.nonzero(~sure & finite_x)[0]:
+            bit[i] = math.fsum(prod[i]) > 0
+        bit &= finite_x
+        code |= bit.astype(np.uint32) << np.uint32(p)
     return code
 
 

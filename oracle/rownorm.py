@@ -19,7 +19,7 @@ approximate-matrix-multiplication reading that the rest supports):
 
 Exact probabilities, so that the draws are reproducible bit for bit:
 w_t = ||v_t||^2 in fp32 (each square rounded, groups of 8 consecutive
-squares summed by halving, group sums by halving -- the hash's order);
+squares summed by halving, group sums by halving);
 with max_t w_t = f 2^e (f in [0.5, 1)), n_t = floor(w_t 2^(40 - e)), an
 integer below 2^40 (keys whose weight is below 2^-40 of the largest get
 n_t = 0 and are never drawn); c_t = n_0 + ... + n_t in exact integers,
@@ -35,12 +35,27 @@ from fractions import Fraction
 
 import numpy as np
 
-from .hyperattn import (_halving_sum_last, _padded_dim, block_part, sample_part, sample_positions,
-                        sort_perm, _check, ranks)
+from .hyperattn import block_part, sample_part, sample_positions, sort_perm, _check, ranks
 from .gauss import projections
 from .philox import philox_words
 
 QBITS = 40
+
+
+def _padded_dim(d):
+    """Smallest 8 * 2^k >= d."""
+    g = 1
+    while 8 * g < d:
+        g *= 2
+    return 8 * g
+
+
+def _halving_sum_last(v):
+    """Sum over the last axis by repeated halving: v <- v[:h] + v[h:]."""
+    while v.shape[-1] > 1:
+        h = v.shape[-1] // 2
+        v = v[..., :h] + v[..., h:]
+    return v[..., 0]
 
 
 def row_norms_sq(v32):

@@ -45,6 +45,66 @@ def test_hash_bit_exact(dtype, d, r):
     assert np.array_equal(got, ref), int((got != ref).sum())
 
 
+def _adversarial_rows(d, dtype, seed):
+    """Rows whose dot products with R (see _adversarial_R) cancel exactly,
+    lose low-order terms in fp32 and fp64, sit near the subnormal range or
+    hold non-finite values; plus random rows."""
+    rng = np.random.default_rng(seed)
+    rows = []
+    for a in (1.0, 2.0**-20, 2.0**20, 3.0):
+        x = np.zeros(d, np.float64)
+        x[0], x[1] = a, -a                                # R_0 = R_1: exact zero for every projection
+        rows.append(x)
+        y = x.copy()
+        y[5] = 2.0**-30                                   # tiny term decides the sign
+        rows.append(y)
+    x = np.zeros(d, np.float64)
+    x[2], x[3], x[4] = 1.0, 2.0**100, -(2.0**100)         # R_2 + 2^100 R_3 - 2^100 R_3: sign of R_2,
+    rows.append(x)                                        # lost by fp32 and fp64 sums in any order
+    rows.append(-x)
+    x = np.zeros(d, np.float64)
+    x[3:9] = 2.0**-126 if dtype == torch.float32 else 2.0**-120   # tiny magnitudes
+    rows.append(x)
+    x = np.ones(d, np.float64)
+    x[7] = np.inf
+    rows.append(x)
+    x = np.ones(d, np.float64)
+    x[9] = np.nan
+    rows.append(x)
+    rows.append(np.zeros(d, np.float64))
+    for _ in range(200):
+        rows.append(rng.standard_normal(d))
+    return torch.tensor(np.stack(rows), dtype=torch.float64).to(dtype)
+
+
+def _adversarial_R(d, r, seed):
+    rng = np.random.default_rng(seed)
+    R = rng.standard_normal((r, d)).astype(np.float32)
+    R[:, 1] = R[:, 0]
+    R[:, 4] = R[:, 3]
+    R[:, 2] = np.abs(R[:, 2]) * np.where(np.arange(r) % 2 == 0, 1, -1)   # sign of R_2 alternates
+    return R
+
+
+@pytest.mark.parametrize("dtype", [torch.bfloat16, torch.float32])
+@pytest.mark.parametrize("d", [64, 128])
+def test_hash_exact_sign_adversarial(dtype, d):
+    r = 8
+    x = _adversarial_rows(d, dtype, 5 + d)
+    R = _adversarial_R(d, r, 9 + d)
+    Rn = R.copy()
+    Rn[3, 4] = np.inf                                     # a non-finite projection: bit 3 is 0 everywhere
+    for Rm in (R, Rn):
+        got = ha.hash_rows(x.to(DEV), torch.from_numpy(Rm).to(DEV)).cpu().numpy().astype(np.uint32)
+        ref = oracle.ranks(np32(x), Rm)
+        assert np.array_equal(got, ref), np.nonzero(got != ref)[0][:10]
+    codes = oracle.hash_codes(np32(x), R)
+    assert all(codes[i] == 0 for i in range(0, 8, 2))    # exact zeros
+    assert codes[8] == sum(1 << p for p in range(r) if p % 2 == 0)   # sign of R_2
+    assert codes[9] == sum(1 << p for p in range(r) if p % 2 == 1)
+    assert codes[11] == 0 and codes[12] == 0 and codes[13] == 0       # inf, NaN, zero rows
+
+
 @pytest.mark.parametrize("heads,n,length,first,stride,pieces,r", [
     (3, 5000, 5000, 0, 5000, 1, 7),       # two tiles, ragged
     (2, 20000, 20000, 0, 20000, 1, 8),    # five tiles

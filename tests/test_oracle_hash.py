@@ -1,11 +1,12 @@
 """Pins of the oracle's sortLSH step: sign-bit hash, Gray-code rank, stable sort.
 
 * Gray rank: exhaustive closed-form checks for every r <= 16.
-* Hash bits: on integer-valued inputs every fp32 product and partial sum
-  is exact, so the bits must equal the signs of exact integer dot products
-  (pins the bit order, the sign convention and which projection is which).
-* Summation order: a hand-derived fp32 case whose sign depends on the
-  order (derivation in the test).
+* Hash bits: on integer-valued inputs the bits must equal the signs of
+  exact integer dot products (pins the bit order, the sign convention and
+  which projection is which).
+* Exact sign: cancelling sums whose fp32 and fp64 evaluations lose the
+  sign (hand-derived, in the test), and random fp32 rows against exact
+  rational arithmetic (Python fractions).
 * Sort: Python's ``sorted`` on (rank, index) pairs.
 """
 
@@ -44,35 +45,60 @@ def test_hash_bits_equal_exact_integer_signs(d, r):
     assert code[0] == 0
 
 
-def test_hash_summation_order_hand_derived():
-    # R = all ones, d = 64, one projection.  Nonzero inputs:
-    #   x[9] = 1, x[20] = 2^24, x[38] = -2^24, x[39] = -1   (exact sum 0).
-    # Defined order: groups of 8 consecutive elements, each summed by
-    # halving (pairs 4 apart, 2 apart, 1 apart), then the 8 group sums by
-    # halving.
-    #   group 1 = 1;  group 2 = 2^24;
-    #   group 4: pairs 4 apart give (-2^24, -1) in slots (2, 3), then slots
-    #   (0, 1) = (-2^24, -1), then -2^24 - 1 = -16777217 rounds to -2^24
-    #   (tie to even);
-    #   group sums [0, 1, 2^24, 0, -2^24, 0, 0, 0]: pairs 4 apart
-    #   [-2^24, 1, 2^24, 0], pairs 2 apart [0, 1], total +1 > 0 -> bit 1.
-    # (Plain halving over 64 gives 0, a running sum -1: both bit 0.)
-    x = np.zeros((2, 64), dtype=np.float32)
-    x[0, 9], x[0, 20], x[0, 38], x[0, 39] = 1.0, 2.0**24, -(2.0**24), -1.0
-    x[1] = -x[0]                                  # mirror: total -1 -> bit 0
+def test_hash_exact_sign_hand_derived():
+    # R = all ones, d = 64, one projection; the sign must be that of the
+    # exact sum, whatever order a floating-point evaluation would take.
+    #   row 0: 2^60 + 1 - 2^60 = 1 > 0 -> bit 1 (fp32 and fp64 running sums
+    #          both absorb the 1 and give 0);
+    #   row 1: the mirror, -1 -> bit 0;
+    #   row 2: 1 + 2^24 - 2^24 - 1 = 0 exactly -> bit 0 (fp32 running sum
+    #          gives -1, a halving order can give +1);
+    #   row 3: 2^-100 + 2^50 - 2^50 = 2^-100 > 0 -> bit 1.
+    x = np.zeros((4, 64), dtype=np.float32)
+    x[0, 3], x[0, 17], x[0, 40] = 2.0**60, 1.0, -(2.0**60)
+    x[1] = -x[0]
+    x[2, 9], x[2, 20], x[2, 38], x[2, 39] = 1.0, 2.0**24, -(2.0**24), -1.0
+    x[3, 0], x[3, 1], x[3, 63] = 2.0**-100, 2.0**50, -(2.0**50)
     R = np.ones((1, 64), dtype=np.float32)
-    t = hyperattn.projection_sums(x, R)
-    assert t[0, 0] == 1.0 and t[1, 0] == -1.0
-    assert hyperattn.hash_codes(x, R).tolist() == [1, 0]
+    assert hyperattn.hash_codes(x, R).tolist() == [1, 0, 0, 1]
 
 
-def test_hash_zero_and_negative_zero_give_bit_zero():
+def test_hash_bits_equal_exact_rational_signs():
+    from fractions import Fraction
+    rng = np.random.default_rng(11)
+    d, r = 16, 5
+    R = rng.standard_normal((r, d)).astype(np.float32)
+    x = rng.standard_normal((300, d)).astype(np.float32)
+    # rows built to cancel: pairs x_i R_i = -x_j R_j exactly, plus rows
+    # scaled far apart so that fp64 sums lose low-order terms
+    x[:40] = 0.0
+    for i in range(40):
+        a, b = rng.choice(d, size=2, replace=False)
+        x[i, a] = np.float32(2.0 ** int(rng.integers(-20, 20)))
+        x[i, b] = -x[i, a]
+    x[40:80] *= np.float32(2.0 ** 40)
+    x[40:80, 0] = np.float32(2.0 ** -60)
+    code = hyperattn.hash_codes(x, R)
+    for i in range(len(x)):
+        for p in range(r):
+            exact = sum(Fraction(float(a)) * Fraction(float(b)) for a, b in zip(x[i], R[p]))
+            assert (int(code[i]) >> p) & 1 == (1 if exact > 0 else 0), (i, p)
+
+
+def test_hash_zero_and_non_finite_give_bit_zero():
     R = np.ones((2, 64), dtype=np.float32)
     R[1] = -1.0
-    x = np.zeros((3, 64), dtype=np.float32)
+    x = np.ones((5, 64), dtype=np.float32)
+    x[0] = 0.0
+    x[1] = 0.0
     x[1, 0] = -0.0
     x[2, 5] = np.nan
-    assert hyperattn.hash_codes(x, R).tolist() == [0, 0, 0]
+    x[3, 7] = np.inf                              # +inf: still bit 0 for both projections
+    x[4, 7] = -np.inf
+    assert hyperattn.hash_codes(x, R).tolist() == [0, 0, 0, 0, 0]
+    R2 = np.ones((2, 64), dtype=np.float32)
+    R2[1, 3] = np.nan                             # a non-finite projection gives bit 0 for every row
+    assert hyperattn.hash_codes(np.ones((2, 64), dtype=np.float32), R2).tolist() == [1, 1]
 
 
 def test_hash_agrees_with_fp64_signs_away_from_zero():
