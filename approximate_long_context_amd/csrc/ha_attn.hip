@@ -387,6 +387,12 @@ __global__ __launch_bounds__(64 * NW, (min_waves<T, D, KIND, NW, QPW>())) void a
       const float bias = isB ? p.log2w : 0.f;
       const bool diag = LEAF && (kb + kKT - 1 > wq0);
       const bool need_mask = kcnt < kKT || (isB ? samp_multi : (multi_block || diag));
+      // a leaf half needs its mask only when it is short or reaches past the
+      // wave's first query
+      auto need_half = [&](int kt) {
+        if constexpr (LEAF) return kcnt < 32 * (kt + 1) || kb + 32 * kt + 31 > wq0;
+        return need_mask;
+      };
       const int blo = LEAF ? 0 : (ql[0] / p.b_eff) * p.b_k;   // the query's key block [blo, blo + b_k)
 
       auto k_read = [&](int kt, int c) {
@@ -400,18 +406,26 @@ __global__ __launch_bounds__(64 * NW, (min_waves<T, D, KIND, NW, QPW>())) void a
         return __builtin_bit_cast(bf16x8, va8);
       };
       auto mask_half = [&](int kt, floatx16& sv) {
+        if constexpr (LEAF) {
+          // keys j < jhi of the tile count: the tile's fill and the causal limit
+          const int jhi = min(kcnt, ql[0] - kb + 1);
 #pragma unroll
-        for (int r = 0; r < 16; ++r) {
-          const int j = 32 * kt + 8 * (r >> 2) + 4 * h2 + (r & 3);
-          bool ok = j < kcnt;
-          if (isB) {
-            if (samp_multi) ok = ok && (static_cast<unsigned>(spos[kb + min(j, kcnt - 1)] - blo) >= static_cast<unsigned>(p.b_k));
-          } else if (LEAF) {
-            ok = ok && (kb + j <= ql[0]);
-          } else if (multi_block) {
-            ok = ok && (static_cast<unsigned>(kb + j - blo) < static_cast<unsigned>(p.b_k));
+          for (int r = 0; r < 16; ++r) {
+            const int j = 32 * kt + 8 * (r >> 2) + 4 * h2 + (r & 3);
+            if (!(j < jhi)) sv[r] = -INFINITY;
           }
-          if (!ok) sv[r] = -INFINITY;
+        } else {
+#pragma unroll
+          for (int r = 0; r < 16; ++r) {
+            const int j = 32 * kt + 8 * (r >> 2) + 4 * h2 + (r & 3);
+            bool ok = j < kcnt;
+            if (isB) {
+              if (samp_multi) ok = ok && (static_cast<unsigned>(spos[kb + min(j, kcnt - 1)] - blo) >= static_cast<unsigned>(p.b_k));
+            } else if (multi_block) {
+              ok = ok && (static_cast<unsigned>(kb + j - blo) < static_cast<unsigned>(p.b_k));
+            }
+            if (!ok) sv[r] = -INFINITY;
+          }
         }
       };
       auto offset = [&]() { return bias + nref; };
@@ -467,7 +481,7 @@ __global__ __launch_bounds__(64 * NW, (min_waves<T, D, KIND, NW, QPW>())) void a
       for (int r = 0; r < 16; ++r) s0[r] = s1[r] = 0.f;
 #pragma unroll
       for (int c = 0; c < NQF; ++c) s0 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(k_read(0, c), qf[0][c], s0, 0, 0, 0);
-      if (need_mask) mask_half(0, s0);
+      if (need_half(0)) mask_half(0, s0);
 
       // phase 2: S^T of keys [32, 64), each MFMA followed by a share of the
       // weights of keys [0, 32).  Written out in issue order; the
@@ -492,7 +506,7 @@ __global__ __launch_bounds__(64 * NW, (min_waves<T, D, KIND, NW, QPW>())) void a
         }
       }
       settle(s0, pa, pb, l0);
-      if (need_mask) mask_half(1, s1);
+      if (need_half(1)) mask_half(1, s1);
 
       // phase 3: P V of keys [0, 32), each MFMA followed by a share of the
       // weights of keys [32, 64)
