@@ -282,19 +282,21 @@ static Plan make_plan(const Shape& sh, void* ws, size_t cap) {
 // accumulator.  Rows become final in the first leaf and in the quadrants of
 // the nodes on the leftmost path (no shallower node holds them in its right
 // half), which write the output directly.
-static int forward_causal_nodes(const AttnParams& ap, const Shape& sh, const Plan& pl, uint64_t seed,
-                                hipStream_t s) {
-  struct Node {
-    int lo, mid, hi, id, depth;
-    bool leftmost;
-  };
-  std::vector<Node> leaves, quads;
-  std::vector<Node> todo{{0, 0, sh.n, 1, 0, true}};
+struct CausalNode {
+  int lo, mid, hi, id, depth;
+  bool leftmost;                  // no shallower node holds its rows in its right half
+};
+
+// The recursion tree of a causal problem of n rows: spans of at most s rows
+// are leaves; a longer span [lo, hi) splits at mid = lo + floor((hi - lo) / 2)
+// (node ids: root 1, children 2 id and 2 id + 1).  Quadrants deepest first.
+static void causal_nodes(int n, int s, std::vector<CausalNode>& leaves, std::vector<CausalNode>& quads) {
+  std::vector<CausalNode> todo{{0, 0, n, 1, 0, true}};
   while (!todo.empty()) {
-    Node nd = todo.back();
+    CausalNode nd = todo.back();
     todo.pop_back();
     const int ns = nd.hi - nd.lo;
-    if (ns <= sh.s) {
+    if (ns <= s) {
       leaves.push_back(nd);
       continue;
     }
@@ -303,7 +305,15 @@ static int forward_causal_nodes(const AttnParams& ap, const Shape& sh, const Pla
     todo.push_back({nd.lo, 0, nd.mid, 2 * nd.id, nd.depth + 1, nd.leftmost});
     todo.push_back({nd.mid, 0, nd.hi, 2 * nd.id + 1, nd.depth + 1, false});
   }
-  std::stable_sort(quads.begin(), quads.end(), [](const Node& a, const Node& b) { return a.depth > b.depth; });
+  std::stable_sort(quads.begin(), quads.end(),
+                   [](const CausalNode& a, const CausalNode& b) { return a.depth > b.depth; });
+}
+
+static int forward_causal_nodes(const AttnParams& ap, const Shape& sh, const Plan& pl, uint64_t seed,
+                                hipStream_t s) {
+  typedef CausalNode Node;
+  std::vector<Node> leaves, quads;
+  causal_nodes(sh.n, sh.s, leaves, quads);
   const int64_t BH = static_cast<int64_t>(sh.batch) * sh.heads;
   const int64_t BK = static_cast<int64_t>(sh.batch) * sh.kv_heads;
   for (const Node& nd : leaves) {
@@ -700,6 +710,14 @@ static BwdPlan backward_plan(const Shape& sh, void* ws, size_t cap) {
     pl.sort_ws_bytes = mx;
     pl.sort_ws = cv.take<char>(mx);
     pl.part = cv.take<float>(part);
+  } else if (sh.odd) {
+    const int half = sh.n - sh.n / 2;           // the longest quadrant side
+    pl.perm_q = cv.take<int32_t>(BH * half);
+    pl.perm_k = cv.take<int32_t>(BK * half);
+    pl.sidx = cv.take<int32_t>(BH * m1);
+    pl.sort_ws_bytes = sort_ws_bytes(BH, half, 1, sh.r) + sort_ws_bytes(BK, half, 1, sh.r);
+    pl.sort_ws = cv.take<char>(pl.sort_ws_bytes);
+    pl.part = cv.take<float>(bwd_part_floats(BH, half, 1, sh.samples, sh.d));
   }
   pl.total = align_up(cv.used, 256) + 256;
   return pl;
@@ -711,10 +729,6 @@ static int backward_impl(const void* q, const void* k, const void* v, const void
   HA_TRY(validate(sh));
   if (sh.dtype != HA_BF16) {
     set_error("backward: bf16 inputs only");
-    return HA_EUNSUPPORTED;
-  }
-  if (sh.causal && sh.odd) {
-    set_error("backward: causal recursions with odd splits are not built");
     return HA_EUNSUPPORTED;
   }
   if (sh.flags) {
@@ -765,12 +779,15 @@ static int backward_impl(const void* q, const void* k, const void* v, const void
   bp.dv = dv;
   HA_TRY(launch_bwd_qstat(bp, s));
 
-  // one sorted problem per piece: queries [p stride + q_first, + seg), keys [p stride + k_first, + seg)
+  // one sorted problem per piece: queries [p stride + q_first, + seg), keys
+  // [p stride + k_first, + seg_k); query blocks of b_eff = min(block, seg) pair
+  // with key blocks of ceil(b_eff seg_k / seg), samples weigh seg_k / m
   auto sorted_problems = [&](int seg, int pieces, int q_first, int k_first, int stride, int accumulate,
-                             const int32_t* perm_q, const int32_t* perm_k) -> int {
+                             const int32_t* perm_q, const int32_t* perm_k, int seg_k) -> int {
     BwdParams qp = bp;
     qp.pieces = pieces;
     qp.seg = seg;
+    qp.seg_k = seg_k;
     qp.stride = stride;
     qp.q_first = q_first;
     qp.k_first = k_first;
@@ -778,8 +795,9 @@ static int backward_impl(const void* q, const void* k, const void* v, const void
     qp.perm_k = perm_k;
     qp.sidx = pl.sidx;
     qp.m = sh.samples;
-    qp.log2w = sh.samples > 0 ? static_cast<float>(std::log2(static_cast<double>(seg) / sh.samples)) : 0.f;
+    qp.log2w = sh.samples > 0 ? static_cast<float>(std::log2(static_cast<double>(seg_k) / sh.samples)) : 0.f;
     qp.b_eff = sh.block < seg ? sh.block : seg;
+    qp.b_k = static_cast<int>((static_cast<int64_t>(qp.b_eff) * seg_k + seg - 1) / seg);
     qp.qchunk = bwd_query_chunk(seg);
     qp.accumulate = accumulate;
     HA_TRY(launch_bwd_dq(qp, s));
@@ -792,7 +810,39 @@ static int backward_impl(const void* q, const void* k, const void* v, const void
                                  {pl.rank_k, BK, sh.n, sh.n, 0, sh.n, 1, pl.perm_k}};
     HA_TRY(launch_sort_batch(jobs, 2, sh.r, pl.sort_ws, pl.sort_ws_bytes, s));
     HA_TRY(launch_sample_indices(seed, sh.batch, sh.heads, 1, 1, sh.n, sh.samples, pl.sidx, s));
-    return sorted_problems(sh.n, 1, 0, 0, sh.n, 0, pl.perm_q, pl.perm_k);
+    return sorted_problems(sh.n, 1, 0, 0, sh.n, 0, pl.perm_q, pl.perm_k, sh.n);
+  }
+
+  if (sh.odd) {
+    // node by node: the exact leaves (each row in one leaf, so they store),
+    // then every quadrant (rectangular when its span is odd), accumulated
+    std::vector<CausalNode> leaves, quads;
+    causal_nodes(sh.n, sh.s, leaves, quads);
+    for (const CausalNode& nd : leaves) {
+      BwdParams lp = bp;
+      lp.pieces = 1;
+      lp.seg = nd.hi - nd.lo;
+      lp.stride = 0;
+      lp.q_first = nd.lo;
+      lp.k_first = nd.lo;
+      lp.b_eff = lp.seg;
+      lp.causal = 1;
+      HA_TRY(launch_bwd_dq(lp, s));
+      lp.diag = 2;
+      HA_TRY(launch_bwd_dkv(lp, false, s));
+      lp.diag = 1;
+      lp.accumulate = 1;
+      HA_TRY(launch_bwd_dkv(lp, false, s));
+    }
+    for (const CausalNode& nd : quads) {
+      const int nq = nd.hi - nd.mid, nk = nd.mid - nd.lo;
+      const SortJobDesc jobs[2] = {{pl.rank_q, BH, sh.n, nq, nd.mid, nq, 1, pl.perm_q},
+                                   {pl.rank_k, BK, sh.n, nk, nd.lo, nk, 1, pl.perm_k}};
+      HA_TRY(launch_sort_batch(jobs, 2, sh.r, pl.sort_ws, pl.sort_ws_bytes, s));
+      HA_TRY(launch_sample_indices(seed, sh.batch, sh.heads, nd.id, 1, nk, sh.samples, pl.sidx, s));
+      HA_TRY(sorted_problems(nq, 1, nd.mid, nd.lo, 0, 1, pl.perm_q, pl.perm_k, nk));
+    }
+    return HA_OK;
   }
 
   // exact causal leaves, rows in their own order
@@ -816,7 +866,7 @@ static int backward_impl(const void* q, const void* k, const void* v, const void
     HA_TRY(sort_causal_level(pl.rank_q, pl.rank_k, BH, BK, sh.n, l, sh.r, pl.perm_q, pl.perm_k, pl.sort_ws,
                              pl.sort_ws_bytes, s));
     HA_TRY(launch_sample_indices(seed, sh.batch, sh.heads, pieces, pieces, seg, sh.samples, pl.sidx, s));
-    HA_TRY(sorted_problems(seg, pieces, seg, 0, 2 * seg, 1, pl.perm_q, pl.perm_k));
+    HA_TRY(sorted_problems(seg, pieces, seg, 0, 2 * seg, 1, pl.perm_q, pl.perm_k, seg));
   }
   return HA_OK;
 }
@@ -878,7 +928,7 @@ size_t hyperattn_backward_workspace_bytes(int batch, int n, int d, int heads, in
                                           int samples, int proj_bits, int causal, int min_seq_len,
                                           int dtype) {
   Shape sh{batch, n, d, heads, kv_heads, block, samples, proj_bits, causal, min_seq_len, dtype, 0};
-  if (validate(sh) != HA_OK || (sh.causal && sh.odd)) return 0;
+  if (validate(sh) != HA_OK) return 0;
   return backward_plan(sh, nullptr, 0).total;
 }
 

@@ -141,13 +141,15 @@ __global__ __launch_bounds__(kBNT, 2) void bwd_dq_kernel(BwdParams p) {
   const bf16* kbase = static_cast<const bf16*>(p.k) + static_cast<int64_t>(bkv) * p.n * D;
   const bf16* vbase = static_cast<const bf16*>(p.v) + static_cast<int64_t>(bkv) * p.n * D;
   const int32_t* pq = IDENT ? nullptr : p.perm_q + static_cast<int64_t>(prob) * p.seg;
-  const int32_t* pk = IDENT ? nullptr : p.perm_k + (static_cast<int64_t>(bkv) * p.pieces + piece) * p.seg;
+  const int32_t* pk = IDENT ? nullptr : p.perm_k + (static_cast<int64_t>(bkv) * p.pieces + piece) * p.seg_k;
   const int qrow0 = piece * p.stride + p.q_first;
   const int krow0 = piece * p.stride + p.k_first;
+  const int b_k = p.b_k;
   auto krow_of = [&](int t) { return IDENT ? krow0 + t : pk[t]; };
 
-  const int ka0 = (q0 / b_eff) * b_eff;
-  int ka1 = min(((qend - 1) / b_eff + 1) * b_eff, p.seg);
+  // query block t pairs with key block t
+  int ka1 = min(((qend - 1) / b_eff + 1) * b_k, p.seg_k);
+  const int ka0 = min((q0 / b_eff) * b_k, ka1);
   if (p.causal) ka1 = min(ka1, qend);             // keys after the last query carry no weight
   const bool multi_block = (q0 / b_eff) != ((qend - 1) / b_eff);
   const bool samp = p.m > 0;
@@ -172,10 +174,10 @@ __global__ __launch_bounds__(kBNT, 2) void bwd_dq_kernel(BwdParams p) {
       const int i = c + lane;
       const int sp = i < p.m ? si[i] : 0;
       if (i < p.m) {
-        sblk[i] = sp / b_eff;
+        sblk[i] = sp / b_k;
         raw[i] = krow_of(sp);
       }
-      const uint64_t keep = __ballot(i < p.m && (samp_multi || (sp / b_eff) != tq));
+      const uint64_t keep = __ballot(i < p.m && (samp_multi || (sp / b_k) != tq));
       if (lane == 0) ccount[c / 64] = __popcll(keep);
     }
     __syncthreads();
@@ -261,8 +263,8 @@ __global__ __launch_bounds__(kBNT, 2) void bwd_dq_kernel(BwdParams p) {
     const bf16* ks = reinterpret_cast<const bf16*>(smem + (2 * buf) * G::TB);
     const bf16* vs = reinterpret_cast<const bf16*>(smem + (2 * buf + 1) * G::TB);
     const float off = (isB ? p.log2w : 0.f) - lse2;
-    // key j of a block tile lies in the query's block iff (unsigned)(j - lo) < b_eff
-    const int lo = row_blk * b_eff - kb;
+    // key j of a block tile lies in the query's key block iff (unsigned)(j - lo) < b_k
+    const int lo = row_blk * b_k - kb;
     const bool blk_test = !isB && multi_block;
     const bool smp_test = isB && samp_multi;
     const bool cau_test = p.causal && kb + kBT - 1 > q0;   // some key of the tile after some query
@@ -299,7 +301,7 @@ __global__ __launch_bounds__(kBNT, 2) void bwd_dq_kernel(BwdParams p) {
           if constexpr (M) {
             const int j = 32 * kt + 8 * (r >> 2) + 4 * h2 + (r & 3);
             bool ok = j < kcnt;
-            if (blk_test) ok &= static_cast<unsigned>(j - lo) < static_cast<unsigned>(b_eff);
+            if (blk_test) ok &= static_cast<unsigned>(j - lo) < static_cast<unsigned>(b_k);
             if (smp_test) ok &= sblk[kb + min(j, kcnt - 1)] != row_blk;
             if (cau_test) ok &= kb + j <= ql;
             x = ok ? x : -INFINITY;
@@ -377,17 +379,18 @@ __global__ __launch_bounds__(kBNT, 2) void bwd_dkv_kernel(BwdParams p) {
   const int lid = xcd_remap(blockIdx.x, gridDim.x);
   int bkv, piece, qprob0, nheads, k0, kend, qa0, qa1, chunk = 0, sprob = 0;
   if constexpr (!SAMPLE) {
-    const int KT = (p.seg + kBTQ - 1) / kBTQ;
+    const int KT = (p.seg_k + kBTQ - 1) / kBTQ;
     const int kprob = lid / KT;
     bkv = kprob / p.pieces;
     piece = kprob - bkv * p.pieces;
     k0 = (lid % KT) * kBTQ;
-    kend = min(k0 + kBTQ, p.seg);
+    kend = min(k0 + kBTQ, p.seg_k);
     const int b = bkv / p.Hkv;
     qprob0 = (b * p.H + (bkv % p.Hkv) * G_) * p.pieces + piece;
     nheads = G_;
-    qa0 = (k0 / b_eff) * b_eff;
-    qa1 = min(((kend - 1) / b_eff + 1) * b_eff, p.seg);
+    // key block t pairs with query block t
+    qa1 = min(((kend - 1) / p.b_k + 1) * b_eff, p.seg);
+    qa0 = min((k0 / p.b_k) * b_eff, qa1);
     if (p.diag == 2) {
       qa0 = k0;
       qa1 = min(qa1, k0 + kBTQ);
@@ -412,7 +415,7 @@ __global__ __launch_bounds__(kBNT, 2) void bwd_dkv_kernel(BwdParams p) {
   }
   const bf16* kbase = static_cast<const bf16*>(p.k) + static_cast<int64_t>(bkv) * p.n * D;
   const bf16* vbase = static_cast<const bf16*>(p.v) + static_cast<int64_t>(bkv) * p.n * D;
-  const int32_t* pk = IDENT ? nullptr : p.perm_k + (static_cast<int64_t>(bkv) * p.pieces + piece) * p.seg;
+  const int32_t* pk = IDENT ? nullptr : p.perm_k + (static_cast<int64_t>(bkv) * p.pieces + piece) * p.seg_k;
   const int qrow0 = piece * p.stride + p.q_first;
 
   // ---- this lane's key: operands and block
@@ -423,7 +426,7 @@ __global__ __launch_bounds__(kBNT, 2) void bwd_dkv_kernel(BwdParams p) {
   if constexpr (SAMPLE) kpos = p.sidx[static_cast<int64_t>(sprob) * p.m + kjs];
   else kpos = kjs;
   const int krow = IDENT ? piece * p.stride + p.k_first + kpos : pk[kpos];
-  const int kblk = kpos / b_eff;
+  const int kblk = kpos / p.b_k;                 // pairs with query block kblk
   bf16x8 kf[NQF], vf[NQF];
 #pragma unroll
   for (int c = 0; c < NQF; ++c) {
@@ -668,7 +671,7 @@ __global__ __launch_bounds__(256) void bwd_dkv_reduce_kernel(BwdParams p, int nc
   const int piece = prob - bh * p.pieces;
   const int bkv = (bh / p.H) * p.Hkv + (bh % p.H) / (p.H / p.Hkv);
   const int kpos = p.sidx[row];
-  const int krow = p.perm_k[(static_cast<int64_t>(bkv) * p.pieces + piece) * p.seg + kpos];
+  const int krow = p.perm_k[(static_cast<int64_t>(bkv) * p.pieces + piece) * p.seg_k + kpos];
   float* dst = (c < D ? p.dk : p.dv) + (static_cast<int64_t>(bkv) * p.n + krow) * D + (c < D ? c : c - D);
 #pragma unroll
   for (int i = 0; i < 4; ++i) unsafeAtomicAdd(dst + i, acc[i]);
@@ -676,12 +679,20 @@ __global__ __launch_bounds__(256) void bwd_dkv_reduce_kernel(BwdParams p, int nc
 
 // ---- launches ---------------------------------------------------------------------------
 
+// seg_k = 0 and b_k = 0 mean a square problem (seg_k = seg, b_k = b_eff).
+static BwdParams bwd_normalized(const BwdParams& p) {
+  BwdParams q = p;
+  if (q.seg_k == 0) q.seg_k = q.seg;
+  if (q.b_k == 0) q.b_k = q.b_eff;
+  return q;
+}
+
 template <int D, bool IDENT>
 static int launch_dq_d(const BwdParams& p, hipStream_t s) {
   BwdParams q = p;
   q.bcap = 0;
-  const int64_t span = static_cast<int64_t>((kBTQ - 1) / p.b_eff + 2) * p.b_eff;
-  const int64_t cap = span < p.seg ? span : p.seg;
+  const int64_t span = static_cast<int64_t>((kBTQ - 1) / p.b_eff + 2) * p.b_k;
+  const int64_t cap = span < p.seg_k ? span : p.seg_k;
   if (cap <= kBlockListCap) q.bcap = static_cast<int>(cap);
   const size_t lds = 4 * BGeo<D>::TB + dq_list_bytes(q.bcap, p.m);
   const int64_t blocks = static_cast<int64_t>(p.BH) * p.pieces * ((p.seg + kBTQ - 1) / kBTQ);
@@ -696,8 +707,13 @@ static int launch_dq_d(const BwdParams& p, hipStream_t s) {
   return HA_OK;
 }
 
-int launch_bwd_dq(const BwdParams& p, hipStream_t s) {
+int launch_bwd_dq(const BwdParams& p0, hipStream_t s) {
+  const BwdParams p = bwd_normalized(p0);
   if (p.seg == 0 || p.BH == 0) return HA_OK;
+  if (p.seg_k < 1 || p.b_k < 1 || (p.causal && (p.seg_k != p.seg || p.b_k != p.b_eff))) {
+    set_error("backward dq: a problem needs keys; causal problems are square");
+    return HA_EINVAL;
+  }
   if (p.m > kMaxSamples) {
     set_error("backward: samples %d > %d", p.m, kMaxSamples);
     return HA_EUNSUPPORTED;
@@ -722,7 +738,7 @@ static int launch_dkv_d2(const BwdParams& p, hipStream_t s) {
   if constexpr (SAMPLE) {
     blocks = static_cast<int64_t>(p.BH) * p.pieces * ((p.m + kBTQ - 1) / kBTQ) * nchunk;
   } else {
-    blocks = static_cast<int64_t>(p.BH / (p.H / p.Hkv)) * p.pieces * ((p.seg + kBTQ - 1) / kBTQ);
+    blocks = static_cast<int64_t>(p.BH / (p.H / p.Hkv)) * p.pieces * ((p.seg_k + kBTQ - 1) / kBTQ);
   }
   if (blocks == 0) return HA_OK;
   const size_t lds = 2 * dkv_buf_bytes<D>();
@@ -752,8 +768,13 @@ static int launch_dkv_d(const BwdParams& p, hipStream_t s) {
   }
 }
 
-int launch_bwd_dkv(const BwdParams& p, bool samples, hipStream_t s) {
+int launch_bwd_dkv(const BwdParams& p0, bool samples, hipStream_t s) {
+  const BwdParams p = bwd_normalized(p0);
   if (p.seg == 0 || p.BH == 0 || (samples && p.m == 0)) return HA_OK;
+  if (p.seg_k < 1 || p.b_k < 1 || (p.causal && (p.seg_k != p.seg || p.b_k != p.b_eff))) {
+    set_error("backward dk/dv: a problem needs keys; causal problems are square");
+    return HA_EINVAL;
+  }
   if (samples && (!p.part || !p.perm_k || p.qchunk < kBT || p.qchunk % kBT)) {
     set_error("backward dk/dv: bad sample partial buffer, permutation or query chunk");
     return HA_EINVAL;

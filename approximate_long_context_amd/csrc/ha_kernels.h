@@ -116,14 +116,16 @@ struct BwdParams {
   // row order when a permutation is null.
   int pieces = 1;
   int seg = 0;
+  int seg_k = 0;                     // keys per problem (0: seg); rectangular when they differ
   int stride = 0;
   int q_first = 0, k_first = 0;
-  const int32_t* perm_q = nullptr;
-  const int32_t* perm_k = nullptr;
-  const int32_t* sidx = nullptr;     // [BH][pieces][m] sorted key positions
+  const int32_t* perm_q = nullptr;   // [BH][pieces][seg]
+  const int32_t* perm_k = nullptr;   // [BHkv][pieces][seg_k]
+  const int32_t* sidx = nullptr;     // [BH][pieces][m] sorted key positions (< seg_k)
   int m = 0;
-  float log2w = 0.f;                 // log2(seg / m)
-  int b_eff = 1;
+  float log2w = 0.f;                 // log2(seg_k / m)
+  int b_eff = 1;                     // query block
+  int b_k = 0;                       // key block (0: b_eff); query block t pairs with key block t
   int causal = 0;                    // exact causal problem: key position <= query position
   int diag = 0;                      // causal dK/dV: 2 = the keys' own 256-query square, 1 = the queries after it
   int accumulate = 0;                // add to dq / dk / dv instead of storing

@@ -274,7 +274,8 @@ size_t hyperattn_backward_workspace_bytes(int batch, int n, int d, int heads, in
  * The sample part of dK and dV is accumulated with fp32 atomic adds, so
  * their last bits may vary from run to run; dQ is deterministic.
  * Causal calls run the exact leaves first (dq, dk, dv stored), then every
- * level's quadrant problems (added).
+ * level's quadrant problems (added); when some span splits unevenly, node
+ * by node with rectangular quadrants (n_q = n_k + 1), as the forward.
  * Errors: as hyperattn_forward; HA_EUNSUPPORTED for fp32 inputs.
  */
 int hyperattn_backward(const void* q, const void* k, const void* v, const void* out,

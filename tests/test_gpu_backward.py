@@ -121,10 +121,15 @@ def test_backward_rejects_fp32():
     assert e.value.code == ha.HA_EUNSUPPORTED
 
 
-def test_backward_rejects_odd_causal_splits():
-    q, k, v, do = (t.to(DEV) for t in _inputs(1, 1, 1, 1000, 64, 13))
-    args = dict(block=64, samples=16, proj_bits=5, causal=True, min_seq_len=100)
-    out, lse = ha.forward(q, k, v, **args)
-    with pytest.raises(ha.HyperAttnError) as e:
-        ha.backward(q, k, v, out, lse, do, **args)
-    assert e.value.code == ha.HA_EUNSUPPORTED
+ODD_CASES = [
+    # B, H, Hkv, n, d, block, samples, r, min_seq_len, seed: some span splits unevenly,
+    # so quadrants are rectangular (n_q = n_k + 1) and leaves have varied lengths
+    (1, 2, 1, 1000, 64, 64, 16, 5, 100, 31),      # 1000 -> 500 -> 250 -> 125 -> 62 | 63
+    (1, 2, 2, 777, 128, 40, 24, 6, 150, 32),      # odd at the top, d = 128
+    (1, 1, 1, 301, 64, 32, 8, 5, 64, 33),         # small ragged leaves
+]
+
+
+@pytest.mark.parametrize("B,H,Hkv,n,d,block,m,r,s,seed", ODD_CASES)
+def test_causal_backward_odd_splits_match_oracle(B, H, Hkv, n, d, block, m, r, s, seed):
+    _run(B, H, Hkv, n, d, seed, block=block, samples=m, proj_bits=r, causal=True, min_seq_len=s)
