@@ -30,6 +30,8 @@ _SIGNATURES = {
     "hyperattn_forward_ex": (_c_int, [_vp, _vp, _vp, _c_int] + [_c_int] * 10 + [_c_u64, _c_int, _vp, _vp, _vp, _c_size, _vp]),
     "hyperattn_backward_workspace_bytes": (_c_size, [_c_int] * 11),
     "hyperattn_backward": (_c_int, [_vp] * 6 + [_c_int] * 11 + [_c_u64, _vp, _vp, _vp, _vp, _c_size, _vp]),
+    "hyperattn_backward_rect_workspace_bytes": (_c_size, [_c_int] * 10),
+    "hyperattn_backward_rect": (_c_int, [_vp] * 6 + [_c_int] * 10 + [_c_u64, _vp, _vp, _vp, _vp, _c_size, _vp]),
     "hyperattn_projections_host": (_c_int, [_c_u64, _c_int, _c_int, _vp]),
     "hyperattn_projections": (_c_int, [_c_u64, _c_int, _c_int, _vp, _vp]),
     "hyperattn_hash": (_c_int, [_vp, _c_int, _c_i64, _c_int, _c_int, _vp, _vp, _vp]),
@@ -219,6 +221,39 @@ def backward(q, k, v, out, lse, dout, *, block, samples, proj_bits, causal=False
         workspace = torch.empty(max(wsb, 256), dtype=torch.uint8, device=dev)
     _call("hyperattn_backward", _ptr(q), _ptr(k), _ptr(v), _ptr(out), _ptr(lse), _ptr(dout), HA_BF16,
           B, n, d, H, Hkv, block, samples, proj_bits, int(bool(causal)), min_seq_len, ctypes.c_uint64(seed),
+          _ptr(dq), _ptr(dk), _ptr(dv), _ptr(workspace), workspace.numel(), _stream(dev))
+    return dq, dk, dv
+
+
+def backward_rect(q, k, v, out, lse, dout, *, block, samples, proj_bits, seed=0, dq=None, dk=None, dv=None,
+                  workspace=None):
+    """Gradients of sum(dout * out) for (out, lse) = forward_rect(q, k, v, ...)
+    with the same arguments: q, out, dout [B, H, n_q, d], k, v [B, Hkv, n_k, d]
+    (bf16), lse [B, H, n_q]; returns float32 (dq like q, dk and dv like k)."""
+    _need(q, "q", torch.bfloat16)
+    dev = q.device
+    for t, name in ((k, "k"), (v, "v"), (out, "out"), (dout, "dout")):
+        _need(t, name, torch.bfloat16, dev)
+    _need(lse, "lse", torch.float32, dev)
+    if (q.dim() != 4 or k.dim() != 4 or k.shape != v.shape or out.shape != q.shape or dout.shape != q.shape
+            or k.shape[0] != q.shape[0] or k.shape[3] != q.shape[3]):
+        raise ValueError("q, out, dout must be [B, H, n_q, d] and k, v [B, Hkv, n_k, d]")
+    B, H, nq, d = q.shape
+    Hkv, nk = k.shape[1], k.shape[2]
+    if lse.shape != (B, H, nq):
+        raise ValueError("lse must be [B, H, n_q]")
+    dq = torch.empty(q.shape, dtype=torch.float32, device=dev) if dq is None else dq
+    dk = torch.empty(k.shape, dtype=torch.float32, device=dev) if dk is None else dk
+    dv = torch.empty(k.shape, dtype=torch.float32, device=dev) if dv is None else dv
+    for t, name, shp in ((dq, "dq", q.shape), (dk, "dk", k.shape), (dv, "dv", k.shape)):
+        _need(t, name, torch.float32, dev)
+        if t.shape != shp:
+            raise ValueError(f"{name} must have shape {tuple(shp)}")
+    wsb = lib().hyperattn_backward_rect_workspace_bytes(B, nq, nk, d, H, Hkv, block, samples, proj_bits, HA_BF16)
+    if workspace is None or workspace.numel() < wsb:
+        workspace = torch.empty(max(wsb, 256), dtype=torch.uint8, device=dev)
+    _call("hyperattn_backward_rect", _ptr(q), _ptr(k), _ptr(v), _ptr(out), _ptr(lse), _ptr(dout), HA_BF16,
+          B, nq, nk, d, H, Hkv, block, samples, proj_bits, ctypes.c_uint64(seed),
           _ptr(dq), _ptr(dk), _ptr(dv), _ptr(workspace), workspace.numel(), _stream(dev))
     return dq, dk, dv
 

@@ -871,6 +871,101 @@ static int backward_impl(const void* q, const void* k, const void* v, const void
   return HA_OK;
 }
 
+// ---- backward of a rectangular non-causal problem -----------------------------------
+// n_q queries, n_k keys per head; the forward's geometry (query blocks of
+// b_eff = min(block, n_q), key blocks of ceil(b_eff n_k / n_q), samples over
+// the n_k keys with weight n_k / m).
+
+static BwdPlan backward_rect_plan(const Shape& sh, int n_k, void* ws, size_t cap) {
+  BwdPlan pl{};
+  Carve cv(ws, cap);
+  const int64_t BH = static_cast<int64_t>(sh.batch) * sh.heads;
+  const int64_t BK = static_cast<int64_t>(sh.batch) * sh.kv_heads;
+  const int m1 = sh.samples > 0 ? sh.samples : 1;
+  pl.R = cv.take<float>(static_cast<size_t>(sh.r) * sh.d);
+  pl.rank_q = cv.take<uint16_t>(BH * sh.n);
+  pl.rank_k = cv.take<uint16_t>(BK * n_k);
+  pl.qstat = cv.take<float>(2 * BH * sh.n);
+  pl.perm_q = cv.take<int32_t>(BH * sh.n);
+  pl.perm_k = cv.take<int32_t>(BK * n_k);
+  pl.sidx = cv.take<int32_t>(BH * m1);
+  pl.sort_ws_bytes = sort_ws_bytes(BH, sh.n, 1, sh.r) + sort_ws_bytes(BK, n_k, 1, sh.r);
+  pl.sort_ws = cv.take<char>(pl.sort_ws_bytes);
+  pl.part = cv.take<float>(bwd_part_floats(BH, sh.n, 1, sh.samples, sh.d));
+  pl.total = align_up(cv.used, 256) + 256;
+  return pl;
+}
+
+static int backward_rect_impl(const void* q, const void* k, const void* v, const void* out, const float* lse,
+                              const void* dout, Shape sh, int n_k, uint64_t seed, float* dq, float* dk, float* dv,
+                              void* ws, size_t ws_bytes, hipStream_t s) {
+  HA_TRY(rect_validate(sh, n_k));
+  if (sh.dtype != HA_BF16) {
+    set_error("backward: bf16 inputs only");
+    return HA_EUNSUPPORTED;
+  }
+  if (sh.n == 0 || sh.batch == 0 || sh.heads == 0) return HA_OK;
+  if (!q || !k || !v || !out || !lse || !dout || !dq || !dk || !dv) {
+    set_error("null pointer argument");
+    return HA_EINVAL;
+  }
+  const size_t need = backward_rect_plan(sh, n_k, nullptr, 0).total;
+  if (!ws || ws_bytes < need) {
+    set_error("workspace of %zu bytes < %zu required", ws_bytes, need);
+    return HA_EWORKSPACE;
+  }
+  if (reinterpret_cast<uintptr_t>(ws) % 256) {
+    set_error("workspace must be 256-byte aligned");
+    return HA_EINVAL;
+  }
+  const BwdPlan pl = backward_rect_plan(sh, n_k, ws, ws_bytes);
+  const int64_t BH = static_cast<int64_t>(sh.batch) * sh.heads;
+  const int64_t BK = static_cast<int64_t>(sh.batch) * sh.kv_heads;
+  HA_TRY(launch_projections(seed, sh.d, sh.r, pl.R, s));
+  HA_TRY(launch_hash(q, sh.dtype, BH * sh.n, sh.d, sh.r, pl.R, pl.rank_q, s));
+  HA_TRY(launch_hash(k, sh.dtype, BK * n_k, sh.d, sh.r, pl.R, pl.rank_k, s));
+  const SortJobDesc jobs[2] = {{pl.rank_q, BH, sh.n, sh.n, 0, sh.n, 1, pl.perm_q},
+                               {pl.rank_k, BK, n_k, n_k, 0, n_k, 1, pl.perm_k}};
+  HA_TRY(launch_sort_batch(jobs, 2, sh.r, pl.sort_ws, pl.sort_ws_bytes, s));
+  HA_TRY(launch_sample_indices(seed, sh.batch, sh.heads, 1, 1, n_k, sh.samples, pl.sidx, s));
+
+  BwdParams bp;
+  bp.q = q;
+  bp.k = k;
+  bp.v = v;
+  bp.out = out;
+  bp.dout = dout;
+  bp.lse = lse;
+  bp.qstat = pl.qstat;
+  bp.d = sh.d;
+  bp.n = sh.n;
+  bp.n_k = n_k;
+  bp.H = sh.heads;
+  bp.Hkv = sh.kv_heads;
+  bp.BH = static_cast<int>(BH);
+  bp.part = pl.part;
+  bp.dq = dq;
+  bp.dk = dk;
+  bp.dv = dv;
+  HA_TRY(launch_bwd_qstat(bp, s));
+  bp.pieces = 1;
+  bp.seg = sh.n;
+  bp.seg_k = n_k;
+  bp.stride = 0;
+  bp.perm_q = pl.perm_q;
+  bp.perm_k = pl.perm_k;
+  bp.sidx = pl.sidx;
+  bp.m = sh.samples;
+  bp.log2w = sh.samples > 0 ? static_cast<float>(std::log2(static_cast<double>(n_k) / sh.samples)) : 0.f;
+  bp.b_eff = sh.block < sh.n ? sh.block : sh.n;
+  bp.b_k = static_cast<int>((static_cast<int64_t>(bp.b_eff) * n_k + sh.n - 1) / sh.n);
+  bp.qchunk = bwd_query_chunk(sh.n);
+  bp.accumulate = 0;
+  HA_TRY(launch_bwd_dq(bp, s));
+  HA_TRY(launch_bwd_dkv(bp, false, s));
+  return launch_bwd_dkv(bp, true, s);
+}
+
 }  // namespace ha
 
 using namespace ha;
@@ -941,6 +1036,23 @@ int hyperattn_backward(const void* q, const void* k, const void* v, const void* 
   Shape sh{batch, n, d, heads, kv_heads, block, samples, proj_bits, causal, min_seq_len, dtype, 0};
   return backward_impl(q, k, v, out, lse, dout, sh, seed, dq, dk, dv, workspace, workspace_bytes,
                        static_cast<hipStream_t>(stream));
+}
+
+size_t hyperattn_backward_rect_workspace_bytes(int batch, int n_q, int n_k, int d, int heads, int kv_heads,
+                                               int block, int samples, int proj_bits, int dtype) {
+  Shape sh{batch, n_q, d, heads, kv_heads, block, samples, proj_bits, 0, 0, dtype, 0};
+  if (rect_validate(sh, n_k) != HA_OK) return 0;
+  return backward_rect_plan(sh, n_k, nullptr, 0).total;
+}
+
+int hyperattn_backward_rect(const void* q, const void* k, const void* v, const void* out, const float* lse,
+                            const void* dout, int dtype, int batch, int n_q, int n_k, int d, int heads,
+                            int kv_heads, int block, int samples, int proj_bits, uint64_t seed, float* dq,
+                            float* dk, float* dv, void* workspace, size_t workspace_bytes, void* stream) {
+  g_last_error.clear();
+  Shape sh{batch, n_q, d, heads, kv_heads, block, samples, proj_bits, 0, 0, dtype, 0};
+  return backward_rect_impl(q, k, v, out, lse, dout, sh, n_k, seed, dq, dk, dv, workspace, workspace_bytes,
+                            static_cast<hipStream_t>(stream));
 }
 
 int hyperattn_row_sqnorms(const void* x, int dtype, int64_t rows, int d, float* w, void* stream) {

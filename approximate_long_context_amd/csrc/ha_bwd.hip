@@ -138,8 +138,8 @@ __global__ __launch_bounds__(kBNT, 2) void bwd_dq_kernel(BwdParams p) {
 
   const bf16* qb = static_cast<const bf16*>(p.q) + static_cast<int64_t>(bh) * p.n * D;
   const bf16* gb = static_cast<const bf16*>(p.dout) + static_cast<int64_t>(bh) * p.n * D;
-  const bf16* kbase = static_cast<const bf16*>(p.k) + static_cast<int64_t>(bkv) * p.n * D;
-  const bf16* vbase = static_cast<const bf16*>(p.v) + static_cast<int64_t>(bkv) * p.n * D;
+  const bf16* kbase = static_cast<const bf16*>(p.k) + static_cast<int64_t>(bkv) * p.n_k * D;
+  const bf16* vbase = static_cast<const bf16*>(p.v) + static_cast<int64_t>(bkv) * p.n_k * D;
   const int32_t* pq = IDENT ? nullptr : p.perm_q + static_cast<int64_t>(prob) * p.seg;
   const int32_t* pk = IDENT ? nullptr : p.perm_k + (static_cast<int64_t>(bkv) * p.pieces + piece) * p.seg_k;
   const int qrow0 = piece * p.stride + p.q_first;
@@ -413,8 +413,8 @@ __global__ __launch_bounds__(kBNT, 2) void bwd_dkv_kernel(BwdParams p) {
     qa0 = chunk * p.qchunk;
     qa1 = min(qa0 + p.qchunk, p.seg);
   }
-  const bf16* kbase = static_cast<const bf16*>(p.k) + static_cast<int64_t>(bkv) * p.n * D;
-  const bf16* vbase = static_cast<const bf16*>(p.v) + static_cast<int64_t>(bkv) * p.n * D;
+  const bf16* kbase = static_cast<const bf16*>(p.k) + static_cast<int64_t>(bkv) * p.n_k * D;
+  const bf16* vbase = static_cast<const bf16*>(p.v) + static_cast<int64_t>(bkv) * p.n_k * D;
   const int32_t* pk = IDENT ? nullptr : p.perm_k + (static_cast<int64_t>(bkv) * p.pieces + piece) * p.seg_k;
   const int qrow0 = piece * p.stride + p.q_first;
 
@@ -608,8 +608,8 @@ __global__ __launch_bounds__(kBNT, 2) void bwd_dkv_kernel(BwdParams p) {
       dkr = p.part + ((static_cast<int64_t>(chunk) * p.BH * p.pieces + sprob) * p.m + kj) * (2 * D);
       dvr = dkr + D;
     } else {
-      dkr = p.dk + (static_cast<int64_t>(bkv) * p.n + krow) * D;
-      dvr = p.dv + (static_cast<int64_t>(bkv) * p.n + krow) * D;
+      dkr = p.dk + (static_cast<int64_t>(bkv) * p.n_k + krow) * D;
+      dvr = p.dv + (static_cast<int64_t>(bkv) * p.n_k + krow) * D;
       add = p.accumulate;
     }
     floatx4 ok_[NDT][4], ov_[NDT][4];
@@ -672,16 +672,18 @@ __global__ __launch_bounds__(256) void bwd_dkv_reduce_kernel(BwdParams p, int nc
   const int bkv = (bh / p.H) * p.Hkv + (bh % p.H) / (p.H / p.Hkv);
   const int kpos = p.sidx[row];
   const int krow = p.perm_k[(static_cast<int64_t>(bkv) * p.pieces + piece) * p.seg_k + kpos];
-  float* dst = (c < D ? p.dk : p.dv) + (static_cast<int64_t>(bkv) * p.n + krow) * D + (c < D ? c : c - D);
+  float* dst = (c < D ? p.dk : p.dv) + (static_cast<int64_t>(bkv) * p.n_k + krow) * D + (c < D ? c : c - D);
 #pragma unroll
   for (int i = 0; i < 4; ++i) unsafeAtomicAdd(dst + i, acc[i]);
 }
 
 // ---- launches ---------------------------------------------------------------------------
 
-// seg_k = 0 and b_k = 0 mean a square problem (seg_k = seg, b_k = b_eff).
+// n_k = 0, seg_k = 0 and b_k = 0 mean a square problem (n_k = n, seg_k = seg,
+// b_k = b_eff).
 static BwdParams bwd_normalized(const BwdParams& p) {
   BwdParams q = p;
+  if (q.n_k == 0) q.n_k = q.n;
   if (q.seg_k == 0) q.seg_k = q.seg;
   if (q.b_k == 0) q.b_k = q.b_eff;
   return q;

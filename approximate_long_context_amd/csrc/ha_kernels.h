@@ -107,7 +107,8 @@ struct BwdParams {
   const float* lse = nullptr;        // forward lse [BH][n] (natural log)
   float* qstat = nullptr;            // per row: (lse log2 e, rowsum(dout * out)) [BH][n][2]
   int d = 64;
-  int n = 0;
+  int n = 0;                         // rows per query head (q, out, dout, dq, lse)
+  int n_k = 0;                       // rows per KV head (k, v, dk, dv); 0: n
   int H = 1, Hkv = 1;
   int BH = 0;
   // Problems: piece p of every head has queries at rows p * stride + q_first + t

@@ -285,6 +285,21 @@ int hyperattn_backward(const void* q, const void* k, const void* v, const void* 
                        uint64_t seed, float* dq, float* dk, float* dv,
                        void* workspace, size_t workspace_bytes, void* stream);
 
+/* Backward of the rectangular forward (hyperattn_forward_rect): q, out,
+ * dout [batch, heads, n_q, d], k, v [batch, kv_heads, n_k, d] (bf16),
+ * lse [batch, heads, n_q]; dq [batch, heads, n_q, d], dk, dv [batch,
+ * kv_heads, n_k, d] fp32, written (every element).  The same weighted
+ * softmax backward over the rectangular problem's weights (query blocks of
+ * b_eff = min(block, n_q) paired with key blocks of ceil(b_eff n_k / n_q),
+ * samples over the n_k keys with weight n_k / samples).
+ * Errors: as hyperattn_forward_rect; HA_EUNSUPPORTED for fp32 inputs. */
+size_t hyperattn_backward_rect_workspace_bytes(int batch, int n_q, int n_k, int d, int heads, int kv_heads,
+                                               int block, int samples, int proj_bits, int dtype);
+int hyperattn_backward_rect(const void* q, const void* k, const void* v, const void* out, const float* lse,
+                            const void* dout, int dtype, int batch, int n_q, int n_k, int d, int heads,
+                            int kv_heads, int block, int samples, int proj_bits, uint64_t seed, float* dq,
+                            float* dk, float* dv, void* workspace, size_t workspace_bytes, void* stream);
+
 /* ------------------------------------------------------------------------
  * Stages of the forward, exported for parity checks and timing.  The
  * forward calls the same kernels.

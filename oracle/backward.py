@@ -147,3 +147,31 @@ def backward(q, k, v, do, cfg):
             dk[b, g] += gk
             dv[b, g] += gv
     return dq, dk, dv
+
+
+def backward_rect(q, k, v, do, cfg):
+    """Backward of ``oracle.hyperattn.forward_rect`` (reading R18): q, do
+    [B, H, n_q, d], k, v [B, Hkv, n_k, d] float32 arrays holding the input
+    values exactly.  Returns (dq [B, H, n_q, d], dk, dv [B, Hkv, n_k, d]) in
+    fp64; W is the rectangular problem's weights (noncausal_weights with
+    n_q queries and n_k keys)."""
+    if cfg.causal:
+        raise ValueError("rectangular problems are non-causal")
+    B, H, n_q, d = q.shape
+    Hkv, n_k = k.shape[1], k.shape[2]
+    G = H // Hkv
+    R = projections(cfg.seed, d, cfg.proj_bits)
+    dq = np.zeros((B, H, n_q, d))
+    dk = np.zeros((B, Hkv, n_k, d))
+    dv = np.zeros((B, Hkv, n_k, d))
+    for b in range(B):
+        for h in range(H):
+            g = h // G
+            W = noncausal_weights(ranks(q[b, h], R), ranks(k[b, g], R), cfg.seed, b, h, 1, cfg.block,
+                                  cfg.samples)
+            gq, gk, gv = weighted_backward(q[b, h].astype(np.float64), k[b, g].astype(np.float64),
+                                           v[b, g].astype(np.float64), W, np.asarray(do[b, h], np.float64))
+            dq[b, h] = gq
+            dk[b, g] += gk
+            dv[b, g] += gv
+    return dq, dk, dv

@@ -133,3 +133,30 @@ ODD_CASES = [
 @pytest.mark.parametrize("B,H,Hkv,n,d,block,m,r,s,seed", ODD_CASES)
 def test_causal_backward_odd_splits_match_oracle(B, H, Hkv, n, d, block, m, r, s, seed):
     _run(B, H, Hkv, n, d, seed, block=block, samples=m, proj_bits=r, causal=True, min_seq_len=s)
+
+
+RECT_CASES = [
+    # B, H, Hkv, n_q, n_k, d, block, samples, r, seed
+    (1, 2, 1, 1024, 1500, 64, 128, 64, 7, 41),     # more keys than queries, grouped heads
+    (1, 2, 2, 1200, 700, 128, 64, 40, 6, 42),      # more queries than keys, d = 128
+    (1, 1, 1, 777, 1000, 64, 96, 30, 5, 43),       # ragged blocks
+]
+
+
+@pytest.mark.parametrize("B,H,Hkv,nq,nk,d,block,m,r,seed", RECT_CASES)
+def test_rect_backward_matches_oracle(B, H, Hkv, nq, nk, d, block, m, r, seed):
+    g = torch.Generator(device="cpu").manual_seed(200 + seed)
+    sc = d ** -0.25
+    q = (torch.randn(B, H, nq, d, generator=g) * sc).to(torch.bfloat16)
+    k = (torch.randn(B, Hkv, nk, d, generator=g) * sc).to(torch.bfloat16)
+    v = torch.randn(B, Hkv, nk, d, generator=g).to(torch.bfloat16)
+    do = torch.randn(B, H, nq, d, generator=g).to(torch.bfloat16)
+    args = dict(block=block, samples=m, proj_bits=r, seed=seed)
+    qd, kd, vd, dod = q.to(DEV), k.to(DEV), v.to(DEV), do.to(DEV)
+    out, lse = ha.forward_rect(qd, kd, vd, **args)
+    dq, dk, dv = ha.backward_rect(qd, kd, vd, out, lse, dod, **args)
+    torch.cuda.synchronize()
+    rq, rk, rv = ob.backward_rect(np32(q), np32(k), np32(v), np32(do), HAConfig(**args))
+    _compare(dq.cpu().numpy(), rq, "dq")
+    _compare(dk.cpu().numpy(), rk, "dk")
+    _compare(dv.cpu().numpy(), rv, "dv")

@@ -8,7 +8,9 @@
   whose gradients torch autograd computes in fp64;
 * grouped heads: dK, dV of a KV head are the sums over its query heads;
 * planted mistakes in the backward formula are caught by the finite
-  differences.
+  differences;
+* rectangular problems (n_q != n_k): the weights reproduce
+  ``forward_rect`` and ``backward_rect`` matches finite differences.
 """
 
 import numpy as np
@@ -171,3 +173,37 @@ def test_planted_backward_mistakes_are_caught(monkeypatch, mutant):
     monkeypatch.setattr(ob, "weighted_backward", mutant)
     with pytest.raises(AssertionError):
         test_gradients_match_finite_differences(CASES[0])
+
+
+@pytest.mark.parametrize("nq,nk,block,m", [(12, 20, 4, 5), (21, 9, 5, 4)])
+def test_rect_backward(nq, nk, block, m):
+    from oracle import HAConfig
+    rng = np.random.default_rng(nq * nk)
+    q = (rng.standard_normal((1, 2, nq, 6)) * 0.7).astype(np.float32)
+    k = (rng.standard_normal((1, 1, nk, 6)) * 0.7).astype(np.float32)
+    v = rng.standard_normal((1, 1, nk, 6)).astype(np.float32)
+    do = rng.standard_normal((1, 2, nq, 6))
+    cfg = HAConfig(block=block, samples=m, proj_bits=3, seed=2)
+    dq, dk, dv = ob.backward_rect(q, k, v, do, cfg)
+    R = projections(2, 6, 3)
+    Ws = [ob.noncausal_weights(oh.ranks(q[0, h], R), oh.ranks(k[0, 0], R), 2, 0, h, 1, block, m) for h in range(2)]
+    q64, k64, v64 = (a.astype(np.float64) for a in (q, k, v))
+    # the weights reproduce the rectangular forward
+    o, l = oh.forward_rect(q, k, v, cfg)
+    for h in range(2):
+        O, L = ob.weighted_attention(q64[0, h], k64[0, 0], v64[0, 0], Ws[h])
+        assert np.max(np.abs(O - o[0, h])) < 1e-12 and np.max(np.abs(L - l[0, h])) < 1e-12
+
+    def f(qq, kk, vv):
+        return sum(np.sum(do[0, h] * ob.weighted_attention(qq[0, h], kk[0, 0], vv[0, 0], Ws[h])[0])
+                   for h in range(2))
+
+    eps = 1e-6
+    for arr, grad, idx in ((q64, dq, (0, 1, nq // 2, 2)), (k64, dk, (0, 0, nk // 2, 1)), (v64, dv, (0, 0, 1, 4))):
+        plus, minus = arr.copy(), arr.copy()
+        plus[idx] += eps
+        minus[idx] -= eps
+        args_p = [plus if a is arr else a for a in (q64, k64, v64)]
+        args_m = [minus if a is arr else a for a in (q64, k64, v64)]
+        fd = (f(*args_p) - f(*args_m)) / (2 * eps)
+        assert abs(fd - grad[idx]) < 1e-6 * max(1.0, abs(fd))
