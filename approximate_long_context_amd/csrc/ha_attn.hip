@@ -885,12 +885,10 @@ static int launch_attn_t(const AttnParams& p, hipStream_t s) {
     lds += list_bytes(q.bcap, p.m);
   }
   auto fn = attn_kernel<T, D, KIND, OUT, NW, QPW>;
-  static bool attr_set = false;   // once per instantiation
-  if (!attr_set) {
-    HA_CHECK_HIP(hipFuncSetAttribute(reinterpret_cast<const void*>(fn),
-                                     hipFuncAttributeMaxDynamicSharedMemorySize, 160 * 1024));
-    attr_set = true;
-  }
+  // once per instantiation (thread-safe static initialisation)
+  static const hipError_t attr_err = hipFuncSetAttribute(reinterpret_cast<const void*>(fn),
+                                                         hipFuncAttributeMaxDynamicSharedMemorySize, 160 * 1024);
+  HA_CHECK_HIP(attr_err);
   hipLaunchKernelGGL(fn, dim3(static_cast<unsigned>(blocks)), dim3(G::NT), lds, s, q);
   return HA_OK;
 }
@@ -899,19 +897,18 @@ static int launch_attn_t(const AttnParams& p, hipStream_t s) {
 // HYPERATTN_SHAPE_SORTED ("4x32", "8x32", "4x64", "2x64") override the
 // default for tuning.
 static int shape_override(int kind) {
-  static int cached[2] = {-1, -1};
-  if (cached[kind] < 0) {
-    const char* s = std::getenv(kind == kKindLeaf ? "HYPERATTN_SHAPE_LEAF" : "HYPERATTN_SHAPE_SORTED");
-    int v = 0;
-    if (s) {
-      if (!std::strcmp(s, "4x32")) v = 1;
-      else if (!std::strcmp(s, "8x32")) v = 2;
-      else if (!std::strcmp(s, "4x64")) v = 3;
-      else if (!std::strcmp(s, "2x64")) v = 4;
-    }
-    cached[kind] = v;
-  }
-  return cached[kind];
+  auto parse = [](const char* name) {
+    const char* s = std::getenv(name);
+    if (!s) return 0;
+    if (!std::strcmp(s, "4x32")) return 1;
+    if (!std::strcmp(s, "8x32")) return 2;
+    if (!std::strcmp(s, "4x64")) return 3;
+    if (!std::strcmp(s, "2x64")) return 4;
+    return 0;
+  };
+  // read once (thread-safe static initialisation)
+  static const int leaf = parse("HYPERATTN_SHAPE_LEAF"), sorted = parse("HYPERATTN_SHAPE_SORTED");
+  return kind == kKindLeaf ? leaf : sorted;
 }
 
 template <typename T, int D, int KIND, int OUT>

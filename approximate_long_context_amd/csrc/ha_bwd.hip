@@ -699,12 +699,10 @@ static int launch_dq_d(const BwdParams& p, hipStream_t s) {
   const size_t lds = 4 * BGeo<D>::TB + dq_list_bytes(q.bcap, p.m);
   const int64_t blocks = static_cast<int64_t>(p.BH) * p.pieces * ((p.seg + kBTQ - 1) / kBTQ);
   auto fn = bwd_dq_kernel<D, IDENT>;
-  static bool attr = false;
-  if (!attr) {
-    HA_CHECK_HIP(hipFuncSetAttribute(reinterpret_cast<const void*>(fn), hipFuncAttributeMaxDynamicSharedMemorySize,
-                                     160 * 1024));
-    attr = true;
-  }
+  // once per instantiation (thread-safe static initialisation)
+  static const hipError_t attr_err = hipFuncSetAttribute(reinterpret_cast<const void*>(fn),
+                                                         hipFuncAttributeMaxDynamicSharedMemorySize, 160 * 1024);
+  HA_CHECK_HIP(attr_err);
   hipLaunchKernelGGL(fn, dim3(static_cast<unsigned>(blocks)), dim3(kBNT), lds, s, q);
   return HA_OK;
 }
