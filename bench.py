@@ -271,6 +271,13 @@ def main():
         "ms_causal": pass_ms["causal"],
         "tflops_noncausal": f_nc / (pass_ms["noncausal"] * 1e-3) / 1e12,
         "tflops_causal": f_c / (pass_ms["causal"] * 1e-3) / 1e12,
+        # context only: the dense attention work the method avoids (4 B H n^2 d,
+        # causal 2 B H n (n + 1) d) per pass time, and the hash arithmetic
+        # (2 d r per row of Q and K, not part of `value`)
+        "dense_equiv_tflops": {
+            "noncausal": 4.0 * w_nc.batch * w_nc.heads * w_nc.n ** 2 * w_nc.d / (pass_ms["noncausal"] * 1e-3) / 1e12,
+            "causal": 2.0 * w_c.batch * w_c.heads * w_c.n * (w_c.n + 1) * w_c.d / (pass_ms["causal"] * 1e-3) / 1e12},
+        "hash_gflop_per_pass": 2.0 * w_nc.d * w_nc.proj_bits * w_nc.batch * (w_nc.heads + w_nc.kv_heads) * w_nc.n / 1e9,
         "wall_s_timed": wall,
         "roofline": roof,
         "kernels": breakdown,
