@@ -208,6 +208,9 @@ struct Plan {
   int64_t* rn_cum;             // integer CDF per KV head
   int32_t* rn_sidx;            // draws per query head
   void* rn_ws;                 // CDF scratch: per-problem shift and chunk totals
+  void* rn_kc;                 // drawn K rows per query head [BH][m][d]
+  void* rn_vc;                 // drawn V rows, weighted [BH][m][d]
+  float* rn_lse;               // lse when the caller passes none [BH][n]
   size_t total;
 };
 
@@ -227,13 +230,13 @@ static Plan make_plan(const Shape& sh, void* ws, size_t cap) {
     pl.sort_ws_bytes = sort_ws_bytes(BH, sh.n, 1, sh.r) + sort_ws_bytes(BK, sh.n, 1, sh.r);
     pl.sort_ws = cv.take<char>(pl.sort_ws_bytes);
     const bool rn = sh.flags & HA_FLAG_ROWNORM;
-    if ((sh.flags & HA_FLAG_MATERIALIZE) || rn) {
+    if ((sh.flags & HA_FLAG_MATERIALIZE) && !rn) {
       pl.qs = cv.take<char>(BH * sh.n * sh.d * esz);
       pl.ks = cv.take<char>(BK * sh.n * sh.d * esz);
       pl.vs = cv.take<char>(BK * sh.n * sh.d * esz);
     }
-    if ((sh.flags & HA_FLAG_UNFUSED) || rn) {
-      for (int i = 0; i < (rn ? 3 : 2); ++i) {
+    if ((sh.flags & HA_FLAG_UNFUSED) && !rn) {
+      for (int i = 0; i < 2; ++i) {
         pl.part_o[i] = cv.take<float>(BH * sh.n * sh.d);
         pl.part_lse[i] = cv.take<float>(BH * sh.n);
       }
@@ -243,6 +246,9 @@ static Plan make_plan(const Shape& sh, void* ws, size_t cap) {
       pl.rn_cum = cv.take<int64_t>(BK * sh.n);
       pl.rn_sidx = cv.take<int32_t>(BH * (sh.samples > 0 ? sh.samples : 1));
       pl.rn_ws = cv.take<char>(rownorm_cdf_ws_bytes(BK, sh.n));
+      pl.rn_kc = cv.take<char>(BH * sh.samples * sh.d * esz);
+      pl.rn_vc = cv.take<char>(BH * sh.samples * sh.d * esz);
+      pl.rn_lse = cv.take<float>(BH * sh.n);
     }
   } else if (sh.odd) {
     const int half = sh.n - sh.n / 2;         // the longest quadrant side
@@ -431,41 +437,26 @@ static int forward_impl(const void* q, const void* k, const void* v, Shape sh, u
     ap.m = sh.samples;
     ap.log2w = sh.samples > 0 ? static_cast<float>(std::log2(static_cast<double>(sh.n) / sh.samples)) : 0.f;
     if (sh.flags & HA_FLAG_ROWNORM) {
-      // block part, uniform-sample part (its normaliser), row-norm part (its
-      // numerator, weights folded into a sorted copy of V), merged
-      ap.out_mode = kOutPartial;
-      ap.use_block = 1;
-      ap.use_samples = 0;
-      ap.part_o = pl.part_o[0];
-      ap.part_lse = pl.part_lse[0];
+      // pass 1: the plain estimator (block + uniform samples) stores
+      // lse = ln(D_blk + D_unif); pass 2: block keys + row-norm draws (K and
+      // weighted V rows copied per head) rescaled to that normaliser
+      float* lse1 = lse ? lse : pl.rn_lse;
+      ap.out_mode = kOutFinal;
+      ap.lse = lse1;
       HA_TRY(launch_attention(ap, HA_K_ATTEND, s));
-      ap.use_block = 0;
-      ap.use_samples = sh.samples > 0;
-      ap.part_o = pl.part_o[1];
-      ap.part_lse = pl.part_lse[1];
-      if (sh.samples > 0) HA_TRY(launch_attention(ap, HA_K_ATTEND, s));
-      if (sh.samples > 0) {
-        HA_TRY(launch_rownorm_sqnorm(v, sh.dtype, BK * sh.n, sh.d, pl.rn_w, s));
-        HA_TRY(launch_rownorm_cdf(pl.rn_w, pl.perm_k, BK, sh.n, pl.rn_cum, pl.rn_ws, s));
-        HA_TRY(launch_rownorm_samples(pl.rn_cum, sh.n, seed, sh.batch, sh.heads, sh.kv_heads, sh.samples,
-                                      pl.rn_sidx, s));
-        HA_TRY(launch_gather(q, sh.dtype, BH, sh.n, sh.d, pl.perm_q, sh.n, pl.qs, s));
-        HA_TRY(launch_gather(k, sh.dtype, BK, sh.n, sh.d, pl.perm_k, sh.n, pl.ks, s));
-        HA_TRY(launch_rownorm_scale_gather(v, sh.dtype, pl.perm_k, pl.rn_cum, BK, sh.n, sh.d, sh.samples, pl.vs,
-                                           s));
-      }
-      ap.qs = pl.qs;
-      ap.ks = pl.ks;
-      ap.vs = pl.vs;
+      if (sh.samples == 0) return HA_OK;        // no draws: the numerator is the block part alone
+      HA_TRY(launch_rownorm_sqnorm(v, sh.dtype, BK * sh.n, sh.d, pl.rn_w, s));
+      HA_TRY(launch_rownorm_cdf(pl.rn_w, pl.perm_k, BK, sh.n, pl.rn_cum, pl.rn_ws, s));
+      HA_TRY(launch_rownorm_samples(pl.rn_cum, sh.n, seed, sh.batch, sh.heads, sh.kv_heads, sh.samples,
+                                    pl.rn_sidx, s));
+      HA_TRY(launch_rownorm_sample_gather(k, v, sh.dtype, pl.perm_k, pl.rn_cum, pl.rn_sidx, sh.batch, sh.heads,
+                                          sh.kv_heads, sh.n, sh.d, sh.samples, pl.rn_kc, pl.rn_vc, s));
+      ap.out_mode = kOutRescale;
       ap.sidx = pl.rn_sidx;
+      ap.smp_k = pl.rn_kc;
+      ap.smp_v = pl.rn_vc;
       ap.log2w = 0.f;
-      ap.part_o = pl.part_o[2];
-      ap.part_lse = pl.part_lse[2];
-      if (sh.samples > 0) HA_TRY(launch_attention(ap, HA_K_ATTEND, s));
-      const bool smp = sh.samples > 0;          // no samples: both sampled parts are empty
-      return launch_rownorm_merge(pl.part_o[0], pl.part_lse[0], smp ? pl.part_lse[1] : nullptr,
-                                  smp ? pl.part_o[2] : nullptr, smp ? pl.part_lse[2] : nullptr, pl.perm_q, BH,
-                                  sh.n, sh.d, sh.dtype, out, lse, s);
+      return launch_attention(ap, HA_K_ATTEND, s);
     }
     if (sh.flags & HA_FLAG_MATERIALIZE) {
       HA_TRY(launch_gather(q, sh.dtype, BH, sh.n, sh.d, pl.perm_q, sh.n, pl.qs, s));

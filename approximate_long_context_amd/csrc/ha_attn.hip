@@ -126,6 +126,10 @@ __global__ __launch_bounds__(64 * NW, (min_waves<T, D, KIND, NW, QPW>())) void a
   const bool mat = !LEAF && p.qs != nullptr;   // materialised sorted copies
   const T* ksb = mat ? static_cast<const T*>(p.ks) + kpiece * p.seg_k * D : nullptr;
   const T* vsb = mat ? static_cast<const T*>(p.vs) + kpiece * p.seg_k * D : nullptr;
+  // kOutRescale: sample rows come from the compact per-head copies, row = sample index
+  constexpr bool RS = OUT == kOutRescale;
+  const T* kcb = RS ? static_cast<const T*>(p.smp_k) + qpiece * p.m * D : nullptr;
+  const T* vcb = RS ? static_cast<const T*>(p.smp_v) + qpiece * p.m * D : nullptr;
   const int32_t* pq = (!LEAF && p.perm_q) ? p.perm_q + qpiece * p.seg : nullptr;
   const int32_t* pk = (!LEAF && p.perm_k) ? p.perm_k + kpiece * p.seg_k : nullptr;
   const int qrow0 = p.q_first + piece * p.stride;
@@ -220,7 +224,7 @@ __global__ __launch_bounds__(64 * NW, (min_waves<T, D, KIND, NW, QPW>())) void a
     sp = si[min(tid, p.m - 1)];
     load_q();
     load_t0();                                  // rows past kc0 repeat a valid row; masked
-    sr = pk[sp];
+    sr = RS ? tid : pk[sp];
   } else {
 #pragma unroll
     for (int u = 0; u < NQT; ++u) {
@@ -235,7 +239,7 @@ __global__ __launch_bounds__(64 * NW, (min_waves<T, D, KIND, NW, QPW>())) void a
     if (samp && tid < p.m) sp = si[tid];
     load_q();
     if (early0) load_t0();
-    if (samp && tid < p.m) sr = key_row(sp);
+    if (samp && tid < p.m) sr = RS ? tid : key_row(sp);
   }
 
   int nsamp = 0;
@@ -253,7 +257,7 @@ __global__ __launch_bounds__(64 * NW, (min_waves<T, D, KIND, NW, QPW>())) void a
         const int spi = first ? sp : (i < p.m ? si[i] : 0);
         if (i < p.m) {
           spos[i] = spi;
-          raw[i] = first ? sr : key_row(spi);
+          raw[i] = first ? sr : (RS ? i : key_row(spi));
         }
         const uint64_t keep =
             __ballot((i < p.m) & (samp_multi | (static_cast<unsigned>(spi - tblo) >= static_cast<unsigned>(p.b_k))));
@@ -326,8 +330,8 @@ __global__ __launch_bounds__(64 * NW, (min_waves<T, D, KIND, NW, QPW>())) void a
       if (j < kcnt) {
         const int row = isB ? srow[kb + j] : (blist ? brow[kb - ka0 + j] : key_row(kb + j));
         const uint32_t off = static_cast<uint32_t>(row * D + G::EPC * c_in_row) * sizeof(T);
-        kw = ld16(mat ? ksb : kbase, off);
-        vw = ld16(mat ? vsb : vbase, off);
+        kw = ld16((RS && isB) ? kcb : (mat ? ksb : kbase), off);
+        vw = ld16((RS && isB) ? vcb : (mat ? vsb : vbase), off);
       }
       kreg[c] = kw;
       vreg[c] = vw;
@@ -736,7 +740,7 @@ __global__ __launch_bounds__(64 * NW, (min_waves<T, D, KIND, NW, QPW>())) void a
   // normalised O^T (32 queries x 32 dims, fp32) is staged in the K/V
   // buffers, then lane L merges and stores dims 4 (L & 7) .. +3 of staged
   // query (L >> 3) + 8 k.
-  const bool to_final = OUT == kOutFinal || ((OUT == kOutLeaf || OUT == kOutMerge) && piece == p.final_piece);
+  const bool to_final = OUT == kOutFinal || RS || ((OUT == kOutLeaf || OUT == kOutMerge) && piece == p.final_piece);
   const bool to_acc = ((OUT == kOutLeaf || OUT == kOutMerge) && piece != p.final_piece) || OUT == kOutAcc;
   constexpr int SST = 36;                         // staged row stride (floats)
   constexpr int STG = 32 * SST + 64;              // floats per wave: slice, lse, rows
@@ -786,6 +790,15 @@ __global__ __launch_bounds__(64 * NW, (min_waves<T, D, KIND, NW, QPW>())) void a
       w_old[k] = 0.f;
       w_new[k] = 1.f;
       lse_out[k] = lqk[k];
+    }
+    if constexpr (RS) {
+      // rescale to the normaliser stored at the row: exp(own lse - stored lse)
+#pragma unroll
+      for (int k = 0; k < 4; ++k) {
+        const float lref = p.lse[static_cast<int64_t>(bh) * p.n + rowk[k]];
+        const bool none = lqk[k] == -INFINITY || lref == -INFINITY;
+        w_new[k] = none ? 0.f : fast_exp2((lqk[k] - lref) * kLog2e);
+      }
     }
     if constexpr (OUT == kOutMerge) {
       float l1[4];
@@ -840,6 +853,10 @@ __global__ __launch_bounds__(64 * NW, (min_waves<T, D, KIND, NW, QPW>())) void a
 #pragma unroll
             for (int i = 0; i < 4; ++i) val[i] = oldv[t][k][i] * w_old[k] + val[i] * w_new[k];
           }
+          if constexpr (RS) {
+#pragma unroll
+            for (int i = 0; i < 4; ++i) val[i] *= w_new[k];
+          }
           if (to_acc) {
             *reinterpret_cast<floatx4*>(p.acc_o + ridx * D + dc) = val;
             if (head) p.acc_lse[ridx] = lse_out[k];
@@ -852,7 +869,7 @@ __global__ __launch_bounds__(64 * NW, (min_waves<T, D, KIND, NW, QPW>())) void a
             } else {
               *reinterpret_cast<floatx4*>(static_cast<float*>(p.out) + ridx * D + dc) = val;
             }
-            if (head && p.lse) p.lse[ridx] = lse_out[k];
+            if (!RS && head && p.lse) p.lse[ridx] = lse_out[k];
           }
         }
       }
@@ -939,6 +956,7 @@ static int launch_attn_d(const AttnParams& p, hipStream_t s) {
     if (p.out_mode == kOutFinal) return launch_attn_shape<T, D, kKindSorted, kOutFinal>(p, s);
     if (p.out_mode == kOutPartial) return launch_attn_shape<T, D, kKindSorted, kOutPartial>(p, s);
     if (p.out_mode == kOutMerge) return launch_attn_shape<T, D, kKindSorted, kOutMerge>(p, s);
+    if (p.out_mode == kOutRescale) return launch_attn_shape<T, D, kKindSorted, kOutRescale>(p, s);
   }
   set_error("attention: unsupported kind %d / output mode %d", p.kind, p.out_mode);
   return HA_EINVAL;

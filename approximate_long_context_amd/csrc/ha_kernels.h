@@ -46,7 +46,8 @@ enum AttnOut {
   kOutPartial = 1,    // fp32 part_o/part_lse at the sorted position
   kOutLeaf = 2,       // piece 0 -> out/lse, other pieces -> acc (no read)
   kOutMerge = 3,      // merge with acc at the row; piece 0 -> out/lse, else -> acc
-  kOutAcc = 4         // every piece -> acc at the row (no read)
+  kOutAcc = 4,        // every piece -> acc at the row (no read)
+  kOutRescale = 5     // out at the original row, scaled by exp(own lse - lse read there); lse kept
 };
 
 constexpr int kMaxSamples = 4096;   // sample list staged in LDS
@@ -84,6 +85,10 @@ struct AttnParams {
   int use_samples = 1;
   const int32_t* sidx = nullptr;     // [BH][pieces][m] sorted key positions
   int m = 0;
+  // kOutRescale: the sampled keys' K and V rows ([BH][m][d] dtype, sample
+  // order), read in place of the rows sidx names
+  const void* smp_k = nullptr;
+  const void* smp_v = nullptr;
   float log2w = 0.f;                 // log2(seg / m)
   int out_mode = kOutFinal;
   int final_piece = 0;               // kOutLeaf / kOutMerge: the piece whose rows are final (-1: none)
@@ -152,11 +157,9 @@ int launch_rownorm_cdf(const float* w, const int32_t* perm_k, int64_t problems, 
                        hipStream_t s);
 int launch_rownorm_samples(const int64_t* cum, int n, uint64_t seed, int batch, int heads, int kv_heads, int m,
                            int32_t* out, hipStream_t s);
-int launch_rownorm_scale_gather(const void* v, int dtype, const int32_t* perm_k, const int64_t* cum,
-                                int64_t problems, int n, int d, int m, void* out, hipStream_t s);
-int launch_rownorm_merge(const float* ob, const float* lb, const float* lu, const float* orr, const float* lr,
-                         const int32_t* perm, int64_t heads, int n, int d, int dtype, void* out, float* lse,
-                         hipStream_t s);
+int launch_rownorm_sample_gather(const void* k, const void* v, int dtype, const int32_t* perm_k,
+                                 const int64_t* cum, const int32_t* sidx, int batch, int heads, int kv_heads, int n,
+                                 int d, int m, void* kc, void* vc, hipStream_t s);
 
 // Diagnostics (ha_diag.hip).
 int launch_colmass(const void* q, const void* k, const float* lse, int batch, int n, int d, int heads,

@@ -16,11 +16,16 @@
 //   c_t = n_0 + ... + n_t over the sorted key positions, T = c_last;
 //   draw i: word x of Philox counter (i / 4, node, head, 2 batch + 2),
 //   r = floor(x T / 2^32), position = smallest t with c_t > r;
-//   weight T / (m n_t), folded into a sorted copy of V (the draw's row).
-// Kernels: squared norms, the per-problem integer CDF (max, chunk scans,
-// chunk offsets), the draws (binary search), the weighted sorted V copy, and
-// the three-part merge + unsort
-//   out = (N_blk + N_rn) / (D_blk + D_unif),  lse = ln(D_blk + D_unif).
+//   weight T / (m n_t), folded into a per-head copy of the drawn V rows.
+// Kernels here: squared norms, the per-problem integer CDF (max, chunk
+// scans, chunk offsets), the draws (binary search) and the copy of the drawn
+// K / weighted V rows.  The result
+//   out = (N_blk + N_rn) / (D_blk + D_unif),  lse = ln(D_blk + D_unif)
+// takes two attention passes: the plain estimator writes lse (its output is
+// overwritten); the second pass attends to the block keys plus the drawn
+// rows (unit weight in its own normaliser D2 = D_blk + sum of their
+// exponentials) and scales its output by D2 / (D_blk + D_unif) =
+// exp(own lse - stored lse), which turns (N_blk + N_rn) / D2 into the result.
 #include <cmath>
 
 #include "ha_device.h"
@@ -182,57 +187,30 @@ __global__ void rownorm_sample_kernel(const int64_t* __restrict__ cum, int n, ui
   }
 }
 
-// ---- V copy in sorted key order, row t scaled by T / (m n_t) -------------------
+// ---- the sampled rows: K as is, V scaled by T / (m n_t) ----------------------------
+// One copy per query head in sample order ([BH][m][d]), read by the second
+// attention pass in place of the rows the sample positions name.
 
 template <typename T>
-__global__ void rownorm_scale_gather_kernel(const T* __restrict__ v, const int32_t* __restrict__ perm_k,
-                                            const int64_t* __restrict__ cum, int n, int d, int m, int64_t rows,
-                                            T* __restrict__ out) {
-  const int64_t total = rows * d;
+__global__ void rownorm_sample_gather_kernel(const T* __restrict__ k, const T* __restrict__ v,
+                                             const int32_t* __restrict__ perm_k, const int64_t* __restrict__ cum,
+                                             const int32_t* __restrict__ sidx, int n, int d, int m, int heads,
+                                             int kv_heads, int64_t total, T* __restrict__ kc, T* __restrict__ vc) {
+  const int G = heads / kv_heads;
   for (int64_t e = static_cast<int64_t>(blockIdx.x) * blockDim.x + threadIdx.x; e < total;
        e += static_cast<int64_t>(gridDim.x) * blockDim.x) {
-    const int64_t rt = e / d;                       // kv problem * n + sorted position
+    const int64_t sj = e / d;                       // query head * m + sample
     const int c = static_cast<int>(e % d);
-    const int64_t prob = rt / n;
-    const int t = static_cast<int>(rt % n);
+    const int64_t bh = sj / m;
+    const int h = static_cast<int>(bh % heads);
+    const int64_t prob = (bh / heads) * kv_heads + h / G;
+    const int t = sidx[sj];                         // sorted key position
     const int64_t* cp = cum + prob * n;
     const int64_t nt = cp[t] - (t > 0 ? cp[t - 1] : 0);
     const double scale = nt > 0 ? static_cast<double>(cp[n - 1]) / (static_cast<double>(m) * nt) : 0.0;
-    const float x = static_cast<float>(v[(prob * n + perm_k[rt]) * d + c]);
-    out[e] = static_cast<T>(x * static_cast<float>(scale));
-  }
-}
-
-// ---- three-part merge + unsort ---------------------------------------------------
-
-template <typename T>
-__global__ void rownorm_merge_kernel(const float* __restrict__ ob, const float* __restrict__ lb,
-                                     const float* __restrict__ lu, const float* __restrict__ orr,
-                                     const float* __restrict__ lr, const int32_t* __restrict__ perm, int n, int d,
-                                     int64_t total, T* __restrict__ out, float* __restrict__ lse) {
-  const int cpr = d / 4;
-  for (int64_t t = static_cast<int64_t>(blockIdx.x) * blockDim.x + threadIdx.x; t < total;
-       t += static_cast<int64_t>(gridDim.x) * blockDim.x) {
-    const int64_t rp = t / cpr;                     // head * n + sorted position
-    const int c = static_cast<int>(t % cpr);
-    const int64_t hd = rp / n;
-    // absent parts (null: no samples) count as empty, lse = -inf
-    const float a = lb[rp], u = lu ? lu[rp] : -INFINITY, r = lr ? lr[rp] : -INFINITY;
-    const float mm = fmaxf(a, u);                   // the normaliser's reference
-    float L = -INFINITY, wb = 0.f, wr = 0.f;
-    if (mm != -INFINITY) {
-      L = mm + logf(expf(a - mm) + expf(u - mm));
-      wb = expf(a - L);
-      wr = r == -INFINITY ? 0.f : expf(r - L);
-    }
-    const floatx4 x = reinterpret_cast<const floatx4*>(ob)[t];
-    floatx4 y = {0.f, 0.f, 0.f, 0.f};
-    if (wr != 0.f) y = reinterpret_cast<const floatx4*>(orr)[t];
-    const int64_t orow = hd * n + perm[rp];
-    T* dst = out + orow * d + 4 * c;
-#pragma unroll
-    for (int i = 0; i < 4; ++i) dst[i] = static_cast<T>(x[i] * wb + y[i] * wr);
-    if (c == 0 && lse) lse[orow] = L;
+    const int64_t src = (prob * n + perm_k[prob * n + t]) * d + c;
+    kc[e] = k[src];
+    vc[e] = static_cast<T>(static_cast<float>(v[src]) * static_cast<float>(scale));
   }
 }
 
@@ -287,34 +265,21 @@ int launch_rownorm_samples(const int64_t* cum, int n, uint64_t seed, int batch, 
   return after_launch("row-norm samples", s);
 }
 
-int launch_rownorm_scale_gather(const void* v, int dtype, const int32_t* perm_k, const int64_t* cum,
-                                int64_t problems, int n, int d, int m, void* out, hipStream_t s) {
-  const int64_t rows = problems * n;
-  if (rows == 0) return HA_OK;
-  const unsigned g = grid_for(rows * d, 256);
+int launch_rownorm_sample_gather(const void* k, const void* v, int dtype, const int32_t* perm_k,
+                                 const int64_t* cum, const int32_t* sidx, int batch, int heads, int kv_heads, int n,
+                                 int d, int m, void* kc, void* vc, hipStream_t s) {
+  const int64_t total = static_cast<int64_t>(batch) * heads * m * d;
+  if (total == 0 || n == 0) return HA_OK;
+  const unsigned g = grid_for(total, 256);
   if (dtype == HA_BF16)
-    hipLaunchKernelGGL(rownorm_scale_gather_kernel<bf16>, dim3(g), dim3(256), 0, s, static_cast<const bf16*>(v),
-                       perm_k, cum, n, d, m, rows, static_cast<bf16*>(out));
+    hipLaunchKernelGGL(rownorm_sample_gather_kernel<bf16>, dim3(g), dim3(256), 0, s, static_cast<const bf16*>(k),
+                       static_cast<const bf16*>(v), perm_k, cum, sidx, n, d, m, heads, kv_heads, total,
+                       static_cast<bf16*>(kc), static_cast<bf16*>(vc));
   else
-    hipLaunchKernelGGL(rownorm_scale_gather_kernel<float>, dim3(g), dim3(256), 0, s, static_cast<const float*>(v),
-                       perm_k, cum, n, d, m, rows, static_cast<float*>(out));
-  return after_launch("row-norm weighted V", s);
-}
-
-int launch_rownorm_merge(const float* ob, const float* lb, const float* lu, const float* orr, const float* lr,
-                         const int32_t* perm, int64_t heads, int n, int d, int dtype, void* out, float* lse,
-                         hipStream_t s) {
-  const int64_t total = heads * n * (d / 4);
-  if (total == 0) return HA_OK;
-  timing_begin(HA_K_MERGE, s);
-  if (dtype == HA_BF16)
-    hipLaunchKernelGGL(rownorm_merge_kernel<bf16>, dim3(grid_for(total, 256)), dim3(256), 0, s, ob, lb, lu, orr, lr,
-                       perm, n, d, total, static_cast<bf16*>(out), lse);
-  else
-    hipLaunchKernelGGL(rownorm_merge_kernel<float>, dim3(grid_for(total, 256)), dim3(256), 0, s, ob, lb, lu, orr,
-                       lr, perm, n, d, total, static_cast<float*>(out), lse);
-  timing_end(HA_K_MERGE, s);
-  return after_launch("row-norm merge+unsort", s);
+    hipLaunchKernelGGL(rownorm_sample_gather_kernel<float>, dim3(g), dim3(256), 0, s, static_cast<const float*>(k),
+                       static_cast<const float*>(v), perm_k, cum, sidx, n, d, m, heads, kv_heads, total,
+                       static_cast<float*>(kc), static_cast<float*>(vc));
+  return after_launch("row-norm sampled rows", s);
 }
 
 }  // namespace ha

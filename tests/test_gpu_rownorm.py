@@ -76,6 +76,8 @@ CASES = [
     (1, 2, 2, 768, 64, 128, 0, 6, 7, torch.bfloat16),         # no samples: block part only
     (1, 1, 1, 1024, 64, 64, 64, 7, 8, torch.float32),         # fp32
     (1, 2, 1, 1000, 64, 128, 96, 7, 9, torch.bfloat16),       # ragged last block
+    (1, 2, 2, 4096, 64, 256, 256, 7, 10, torch.bfloat16),     # many workgroups, one block each
+    (1, 1, 1, 3000, 128, 24, 300, 6, 11, torch.bfloat16),     # small blocks: several per workgroup
 ]
 
 
@@ -107,3 +109,20 @@ def test_rownorm_rejects_causal_and_other_flags():
                    flags=ha.HA_FLAG_ROWNORM)
     with pytest.raises(ha.HyperAttnError):
         ha.forward(q, k, v, block=64, samples=16, proj_bits=5, flags=ha.HA_FLAG_ROWNORM | ha.HA_FLAG_UNFUSED)
+
+
+def test_rownorm_without_lse_output():
+    """A null lse pointer: the variant keeps its normaliser in the workspace
+    and the output equals the one computed with an lse buffer."""
+    import ctypes
+    q, k, v = (t.to(DEV) for t in _inputs(1, 2, 1, 1024, 64, 31, torch.bfloat16))
+    args = dict(block=128, samples=64, proj_bits=6, seed=3)
+    ref, _ = ha.forward(q, k, v, flags=ha.HA_FLAG_ROWNORM, **args)
+    out = torch.empty_like(q)
+    wsb = ha.lib().hyperattn_workspace_bytes(1, 1024, 64, 2, 1, 128, 64, 6, 0, 0, ha.HA_BF16, ha.HA_FLAG_ROWNORM)
+    ws = torch.empty(wsb, dtype=torch.uint8, device=DEV)
+    ha._call("hyperattn_forward_ex", ha._ptr(q), ha._ptr(k), ha._ptr(v), ha.HA_BF16, 1, 1024, 64, 2, 1, 128, 64, 6,
+             0, 0, ctypes.c_uint64(3), ha.HA_FLAG_ROWNORM, ha._ptr(out), None, ha._ptr(ws), ws.numel(),
+             ha._stream(q.device))
+    torch.cuda.synchronize()
+    assert torch.equal(out, ref)
