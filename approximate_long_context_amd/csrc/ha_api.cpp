@@ -207,7 +207,7 @@ struct Plan {
   float* rn_w;                 // row-norm variant: squared norms of V rows
   int64_t* rn_cum;             // integer CDF per KV head
   int32_t* rn_sidx;            // draws per query head
-  void* rn_ws;                 // CDF scratch: per-problem shift and chunk totals
+  void* rn_ws;                 // CDF scratch: chunk maxima and chunk totals
   void* rn_kc;                 // drawn K rows per query head [BH][m][d]
   void* rn_vc;                 // drawn V rows, weighted [BH][m][d]
   float* rn_lse;               // lse when the caller passes none [BH][n]

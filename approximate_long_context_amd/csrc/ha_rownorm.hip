@@ -72,8 +72,10 @@ __global__ __launch_bounds__(256) void rownorm_sqnorm_kernel(const T* __restrict
 }
 
 // ---- integer CDF: per-problem max, chunk scans, chunk offsets -----------------
-// (1) rownorm_max_kernel: one workgroup per KV problem, the largest w;
-// (2) rownorm_chunk_kernel: one workgroup per 2048 sorted positions, the
+// (1) rownorm_max_kernel: one workgroup per 2048 rows of a KV problem, the
+//     largest w among them (row order: the maximum does not depend on it);
+// (2) rownorm_chunk_kernel: one workgroup per 2048 sorted positions: the
+//     problem's largest w from the chunk maxima (exact, any order), then the
 //     quantised weights n_t (gathered through the permutation) and their
 //     inclusive scan within the chunk, plus the chunk's total;
 // (3) rownorm_offset_kernel: each chunk adds the totals of the chunks before
@@ -82,33 +84,44 @@ __global__ __launch_bounds__(256) void rownorm_sqnorm_kernel(const T* __restrict
 constexpr int kRnThreads = 256;
 constexpr int kRnChunk = 2048;                      // 8 positions per thread
 
-__global__ __launch_bounds__(kRnThreads) void rownorm_max_kernel(const float* __restrict__ w, int n,
-                                                                  int* __restrict__ shift) {
+__global__ __launch_bounds__(kRnThreads) void rownorm_max_kernel(const float* __restrict__ w, int n, int nchunk,
+                                                                  float* __restrict__ cmax) {
   __shared__ float red[kRnThreads / 64];
-  const float* wp = w + static_cast<int64_t>(blockIdx.x) * n;
+  const int64_t prob = blockIdx.x / nchunk;
+  const int chunk = blockIdx.x % nchunk;
+  const float* wp = w + prob * n;
   float mx = 0.f;
-  for (int t = threadIdx.x; t < n; t += kRnThreads) mx = fmaxf(mx, wp[t]);
+  for (int t = chunk * kRnChunk + threadIdx.x; t < min((chunk + 1) * kRnChunk, n); t += kRnThreads)
+    mx = fmaxf(mx, wp[t]);
 #pragma unroll
   for (int h = 32; h >= 1; h >>= 1) mx = fmaxf(mx, __shfl_xor(mx, h));
   if ((threadIdx.x & 63) == 0) red[threadIdx.x >> 6] = mx;
   __syncthreads();
-  if (threadIdx.x == 0) {
-    mx = fmaxf(fmaxf(red[0], red[1]), fmaxf(red[2], red[3]));
-    int e = 0;
-    if (mx > 0.f) frexp(static_cast<double>(mx), &e);
-    shift[blockIdx.x] = mx > 0.f ? kRnQBits - e : -100000;   // no positive weight: every n_t = 0
-  }
+  if (threadIdx.x == 0) cmax[blockIdx.x] = fmaxf(fmaxf(red[0], red[1]), fmaxf(red[2], red[3]));
 }
 
 __global__ __launch_bounds__(kRnThreads) void rownorm_chunk_kernel(const float* __restrict__ w,
                                                                     const int32_t* __restrict__ perm_k, int n,
-                                                                    int nchunk, const int* __restrict__ shift,
+                                                                    int nchunk, const float* __restrict__ cmax,
                                                                     int64_t* __restrict__ cum,
                                                                     int64_t* __restrict__ chunk_sum) {
   __shared__ int64_t ssum[kRnThreads];
+  __shared__ int sh_s;
   const int64_t prob = blockIdx.x / nchunk;
   const int chunk = blockIdx.x % nchunk;
-  const int sh = shift[prob];
+  if (threadIdx.x < 64) {                           // the problem's largest weight, its shift 40 - e
+    float mx = 0.f;
+    for (int c = threadIdx.x; c < nchunk; c += 64) mx = fmaxf(mx, cmax[prob * nchunk + c]);
+#pragma unroll
+    for (int h = 32; h >= 1; h >>= 1) mx = fmaxf(mx, __shfl_xor(mx, h));
+    if (threadIdx.x == 0) {
+      int e = 0;
+      if (mx > 0.f) frexp(static_cast<double>(mx), &e);
+      sh_s = mx > 0.f ? kRnQBits - e : -100000;     // no positive weight: every n_t = 0
+    }
+  }
+  __syncthreads();
+  const int sh = sh_s;
   const float* wp = w + prob * n;
   const int32_t* pk = perm_k + prob * n;
   int64_t* cp = cum + prob * n;
@@ -238,7 +251,7 @@ int launch_rownorm_sqnorm(const void* v, int dtype, int64_t rows, int d, float* 
 
 size_t rownorm_cdf_ws_bytes(int64_t problems, int n) {
   const int64_t nchunk = (n + kRnChunk - 1) / kRnChunk;
-  return static_cast<size_t>(problems) * (sizeof(int) + nchunk * sizeof(int64_t)) + 64;
+  return static_cast<size_t>(problems) * nchunk * (sizeof(int64_t) + sizeof(float)) + 64;
 }
 
 int launch_rownorm_cdf(const float* w, const int32_t* perm_k, int64_t problems, int n, int64_t* cum, void* ws,
@@ -246,11 +259,10 @@ int launch_rownorm_cdf(const float* w, const int32_t* perm_k, int64_t problems, 
   if (problems == 0 || n == 0) return HA_OK;
   const int nchunk = (n + kRnChunk - 1) / kRnChunk;
   int64_t* chunk_sum = static_cast<int64_t*>(ws);
-  int* shift = reinterpret_cast<int*>(chunk_sum + problems * nchunk);
+  float* cmax = reinterpret_cast<float*>(chunk_sum + problems * nchunk);
   const unsigned grid = static_cast<unsigned>(problems * nchunk);
-  hipLaunchKernelGGL(rownorm_max_kernel, dim3(static_cast<unsigned>(problems)), dim3(kRnThreads), 0, s, w, n,
-                     shift);
-  hipLaunchKernelGGL(rownorm_chunk_kernel, dim3(grid), dim3(kRnThreads), 0, s, w, perm_k, n, nchunk, shift, cum,
+  hipLaunchKernelGGL(rownorm_max_kernel, dim3(grid), dim3(kRnThreads), 0, s, w, n, nchunk, cmax);
+  hipLaunchKernelGGL(rownorm_chunk_kernel, dim3(grid), dim3(kRnThreads), 0, s, w, perm_k, n, nchunk, cmax, cum,
                      chunk_sum);
   hipLaunchKernelGGL(rownorm_offset_kernel, dim3(grid), dim3(kRnThreads), 0, s, n, nchunk, chunk_sum, cum);
   return after_launch("row-norm cdf", s);
