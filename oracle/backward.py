@@ -175,3 +175,55 @@ def backward_rect(q, k, v, do, cfg):
             dk[b, g] += gk
             dv[b, g] += gv
     return dq, dk, dv
+
+
+def noncausal_backward_blocks(q, k, v, do, rank_q, rank_k, seed, batch_idx, head, node, block, samples):
+    """(dq, dk, dv) of one square non-causal problem, query block by query
+    block: the same W as ``noncausal_weights`` (block keys at weight 1,
+    kept samples at n/m per draw), but only the non-zero columns of each
+    block's rows are formed, so a 131072-row head takes seconds instead of
+    an n x n matrix.  q, do [n, d], k, v [n, d] fp64; the weighted-softmax
+    backward of the module docstring is applied to each block's rows."""
+    n, d = q.shape
+    dq = np.zeros((n, d))
+    dk = np.zeros((n, d))
+    dv = np.zeros((n, d))
+    if n == 0:
+        return dq, dk, dv
+    b_eff = min(block, n)
+    b_k = key_block(b_eff, n, n)
+    pq = sort_perm(rank_q)
+    pk = sort_perm(rank_k)
+    if samples > 0:
+        idx = sample_positions(seed, batch_idx, head, node, n, samples)
+        pos, count = np.unique(idx, return_counts=True)  # sampled sorted key positions, draws at each
+    else:
+        pos = count = np.zeros(0, dtype=np.int64)
+    for t in range((n + b_eff - 1) // b_eff):
+        qrows = pq[t * b_eff:min((t + 1) * b_eff, n)]
+        bpos = np.arange(min(t * b_k, n), min((t + 1) * b_k, n))
+        kept = (pos // b_k) != t
+        kpos = np.concatenate([bpos, pos[kept]])
+        wts = np.concatenate([np.ones(len(bpos)), (n / samples) * count[kept] if samples > 0 else np.zeros(0)])
+        krows = pk[kpos]
+        Wt = np.broadcast_to(wts, (len(qrows), len(krows)))
+        gq, gk, gv = weighted_backward(q[qrows], k[krows], v[krows], Wt, do[qrows])
+        dq[qrows] = gq
+        np.add.at(dk, krows, gk)
+        np.add.at(dv, krows, gv)
+    return dq, dk, dv
+
+
+def backward_head_blocks(q, k, v, do, cfg, b, h):
+    """Non-causal (dq of query head h, dk and dv of its KV head restricted to
+    that query head's contribution) by ``noncausal_backward_blocks``; arrays
+    as for ``backward``."""
+    if cfg.causal:
+        raise ValueError("block-wise backward: non-causal problems only")
+    B, H, Hkv, n, d = _check(q, k, v, cfg)
+    g = h // (H // Hkv)
+    R = projections(cfg.seed, d, cfg.proj_bits)
+    return noncausal_backward_blocks(q[b, h].astype(np.float64), k[b, g].astype(np.float64),
+                                     v[b, g].astype(np.float64), np.asarray(do[b, h], np.float64),
+                                     ranks(q[b, h], R), ranks(k[b, g], R), cfg.seed, b, h, 1, cfg.block,
+                                     cfg.samples)

@@ -16,6 +16,7 @@ import pytest
 import torch
 
 import approximate_long_context_amd as ha
+from approximate_long_context_amd.workloads import WORKLOADS, make_inputs
 from oracle import HAConfig
 from oracle import backward as ob
 
@@ -160,3 +161,30 @@ def test_rect_backward_matches_oracle(B, H, Hkv, nq, nk, d, block, m, r, seed):
     _compare(dq.cpu().numpy(), rq, "dq")
     _compare(dk.cpu().numpy(), rk, "dk")
     _compare(dv.cpu().numpy(), rv, "dv")
+
+
+@pytest.mark.slow
+def test_backward_full_workload_noncausal():
+    """The non-causal long131k pass (32 heads, n = 131072, d = 64, block 256,
+    256 samples), the backward the benchmark times: dq, dk and dv of the
+    first and last heads, every row, against the block-wise oracle (one KV
+    head per query head here, so a KV head's dk, dv come from its one query
+    head)."""
+    w = WORKLOADS["long131k"]
+    assert not w.causal and w.kv_heads == w.heads
+    print("[backward long131k] generating inputs", flush=True)
+    q, k, v = make_inputs(w, DEV)
+    g = torch.Generator(device="cpu").manual_seed(77)
+    do = torch.randn(q.shape, generator=g).to(torch.bfloat16).to(DEV)
+    args = w.method_args()
+    out, lse = ha.forward(q, k, v, **args)
+    dq, dk, dv = ha.backward(q, k, v, out, lse, do, **args)
+    torch.cuda.synchronize()
+    cfg = HAConfig(block=w.block, samples=w.samples, proj_bits=w.proj_bits, seed=w.seed)
+    qc, kc, vc, dc = np32(q), np32(k), np32(v), np32(do)
+    for h in (0, w.heads - 1):
+        print(f"[backward long131k] oracle head {h}", flush=True)
+        rq, rk, rv = ob.backward_head_blocks(qc, kc, vc, dc, cfg, 0, h)
+        _compare(dq[0, h].cpu().numpy(), rq, f"dq head {h}")
+        _compare(dk[0, h].cpu().numpy(), rk, f"dk head {h}")
+        _compare(dv[0, h].cpu().numpy(), rv, f"dv head {h}")

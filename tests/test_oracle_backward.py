@@ -207,3 +207,29 @@ def test_rect_backward(nq, nk, block, m):
         args_m = [minus if a is arr else a for a in (q64, k64, v64)]
         fd = (f(*args_p) - f(*args_m)) / (2 * eps)
         assert abs(fd - grad[idx]) < 1e-6 * max(1.0, abs(fd))
+
+
+@pytest.mark.parametrize("n,block,m,seed", [
+    (300, 64, 40, 1),      # ragged last block (300 = 4 x 64 + 44)
+    (257, 50, 100, 2),     # many duplicate draws, ragged
+    (256, 64, 0, 3),       # no samples: block part only
+    (200, 256, 30, 4),     # one block holds every row: every draw excluded
+    (512, 32, 16, 5),      # many small blocks
+])
+def test_block_backward_equals_dense(n, block, m, seed):
+    """The block-wise backward (used at full sizes, where an n x n W does not
+    fit) gives the dense-W backward's gradients for the same ranks and
+    draws."""
+    g = np.random.default_rng(seed)
+    d = 16
+    q = g.standard_normal((n, d)) * 0.5
+    k = g.standard_normal((n, d)) * 0.5
+    v = g.standard_normal((n, d))
+    do = g.standard_normal((n, d))
+    R = projections(seed, d, 5)
+    rq, rk = oh.ranks(q.astype(np.float32), R), oh.ranks(k.astype(np.float32), R)
+    W = ob.noncausal_weights(rq, rk, seed, 0, 3, 1, block, m)
+    want = ob.weighted_backward(q, k, v, W, do)
+    got = ob.noncausal_backward_blocks(q, k, v, do, rq, rk, seed, 0, 3, 1, block, m)
+    for a, b, what in zip(got, want, ("dq", "dk", "dv")):
+        assert np.allclose(a, b, rtol=1e-10, atol=1e-12), what
