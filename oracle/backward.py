@@ -227,3 +227,57 @@ def backward_head_blocks(q, k, v, do, cfg, b, h):
                                      v[b, g].astype(np.float64), np.asarray(do[b, h], np.float64),
                                      ranks(q[b, h], R), ranks(k[b, g], R), cfg.seed, b, h, 1, cfg.block,
                                      cfg.samples)
+
+
+def causal_dq_rows(q, k, v, do, rank_q, rank_k, seed, batch_idx, head, cfg, rows):
+    """dq of the listed rows of one causal problem, each from its own row of
+    ``causal_weights`` (the leaf's keys up to the row at weight 1, plus, at
+    every split whose upper half holds the row, the quadrant's block keys
+    and kept draws), so full sizes need no n x n matrix.  q, k, v, do
+    [n, d] fp64; returns [len(rows), d]."""
+    n = len(rank_q)
+    causal_levels(n, cfg.min_seq_len)
+    perms = {}
+
+    def quadrant_row(lo, mid, hi, node, iq):
+        # row iq (local to [mid, hi)) of noncausal_weights(rank_q[mid:hi], rank_k[lo:mid], ...)
+        if (lo, hi) not in perms:
+            pq = sort_perm(rank_q[mid:hi])
+            spos = np.empty(hi - mid, dtype=np.int64)
+            spos[pq] = np.arange(hi - mid)
+            perms[(lo, hi)] = (spos, sort_perm(rank_k[lo:mid]))
+        spos, pk = perms[(lo, hi)]
+        ns, nk = hi - mid, mid - lo
+        b_eff = min(cfg.block, ns)
+        b_k = key_block(b_eff, ns, nk)
+        t = spos[iq] // b_eff
+        bpos = np.arange(min(t * b_k, nk), min((t + 1) * b_k, nk))
+        cols, wts = [pk[bpos]], [np.ones(len(bpos))]
+        if cfg.samples > 0:
+            pos, count = np.unique(sample_positions(seed, batch_idx, head, node, nk, cfg.samples),
+                                   return_counts=True)
+            kept = (pos // b_k) != t
+            cols.append(pk[pos[kept]])
+            wts.append((nk / cfg.samples) * count[kept])
+        return lo + np.concatenate(cols), np.concatenate(wts)
+
+    out = np.zeros((len(rows), q.shape[1]))
+    for r, i in enumerate(rows):
+        cols, wts = [], []
+        lo, hi, node = 0, n, 1
+        while hi - lo > cfg.min_seq_len:
+            mid = lo + (hi - lo) // 2
+            if i >= mid:
+                c, w = quadrant_row(lo, mid, hi, node, i - mid)
+                cols.append(c)
+                wts.append(w)
+                lo, node = mid, 2 * node + 1
+            else:
+                hi, node = mid, 2 * node
+        cols.append(np.arange(lo, i + 1))
+        wts.append(np.ones(i + 1 - lo))
+        kc = np.concatenate(cols)
+        Wr = np.concatenate(wts)[None, :]
+        gq, _, _ = weighted_backward(q[i:i + 1], k[kc], v[kc], Wr, do[i:i + 1])
+        out[r] = gq[0]
+    return out

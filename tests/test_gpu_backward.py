@@ -19,6 +19,8 @@ import approximate_long_context_amd as ha
 from approximate_long_context_amd.workloads import WORKLOADS, make_inputs
 from oracle import HAConfig
 from oracle import backward as ob
+from oracle import hyperattn as oh
+from oracle.gauss import projections
 
 from _util import np32
 
@@ -188,3 +190,33 @@ def test_backward_full_workload_noncausal():
         _compare(dq[0, h].cpu().numpy(), rq, f"dq head {h}")
         _compare(dk[0, h].cpu().numpy(), rk, f"dk head {h}")
         _compare(dv[0, h].cpu().numpy(), rv, f"dv head {h}")
+
+
+@pytest.mark.slow
+def test_backward_full_workload_causal_dq_rows():
+    """The causal long131k pass (leaves of 4096 rows, five levels), the
+    causal backward the benchmark times: dq of 50 rows of the first and last
+    heads (leaf boundaries and both halves included) against the oracle's
+    row-wise form, each row over its own leaf keys and quadrant keys."""
+    w = WORKLOADS["long131k_causal"]
+    assert w.causal and w.kv_heads == w.heads
+    print("[causal backward long131k] generating inputs", flush=True)
+    q, k, v = make_inputs(w, DEV)
+    g = torch.Generator(device="cpu").manual_seed(78)
+    do = torch.randn(q.shape, generator=g).to(torch.bfloat16).to(DEV)
+    args = w.method_args()
+    out, lse = ha.forward(q, k, v, **args)
+    dq, _, _ = ha.backward(q, k, v, out, lse, do, **args)
+    torch.cuda.synchronize()
+    cfg = HAConfig(block=w.block, samples=w.samples, proj_bits=w.proj_bits, causal=True,
+                   min_seq_len=w.min_seq_len, seed=w.seed)
+    R = projections(w.seed, w.d, w.proj_bits)
+    rows = np.array(sorted(set(np.random.default_rng(1).choice(w.n, 45, replace=False).tolist())
+                           | {0, w.min_seq_len - 1, w.min_seq_len, w.n // 2, w.n - 1}))
+    for h in (0, w.heads - 1):
+        print(f"[causal backward long131k] oracle rows of head {h}", flush=True)
+        qh, kh, vh = np32(q[0, h]), np32(k[0, h]), np32(v[0, h])
+        ref = ob.causal_dq_rows(qh.astype(np.float64), kh.astype(np.float64), vh.astype(np.float64),
+                                np32(do[0, h]).astype(np.float64), oh.ranks(qh, R), oh.ranks(kh, R), w.seed, 0, h,
+                                cfg, rows)
+        _compare(dq[0, h].cpu().numpy()[rows], ref, f"dq head {h}")

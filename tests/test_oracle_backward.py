@@ -233,3 +233,28 @@ def test_block_backward_equals_dense(n, block, m, seed):
     got = ob.noncausal_backward_blocks(q, k, v, do, rq, rk, seed, 0, 3, 1, block, m)
     for a, b, what in zip(got, want, ("dq", "dk", "dv")):
         assert np.allclose(a, b, rtol=1e-10, atol=1e-12), what
+
+
+@pytest.mark.parametrize("n,block,m,s,seed", [
+    (512, 32, 16, 64, 6),     # three levels, even splits
+    (301, 24, 10, 40, 7),     # odd splits at several levels, ragged blocks
+    (256, 64, 0, 32, 8),      # no samples
+    (200, 16, 40, 200, 9),    # one leaf: exact causal attention
+])
+def test_causal_dq_rows_equal_dense(n, block, m, s, seed):
+    """Row-wise causal dq (used at full sizes) equals the dense-W backward's
+    dq on every row, for the same ranks and draws."""
+    g = np.random.default_rng(seed)
+    d = 16
+    q = g.standard_normal((n, d)) * 0.5
+    k = g.standard_normal((n, d)) * 0.5
+    v = g.standard_normal((n, d))
+    do = g.standard_normal((n, d))
+    R = projections(seed, d, 5)
+    rq, rk = oh.ranks(q.astype(np.float32), R), oh.ranks(k.astype(np.float32), R)
+    cfg = oh.HAConfig(block=block, samples=m, proj_bits=5, causal=True, min_seq_len=s, seed=seed)
+    W = ob.causal_weights(rq, rk, seed, 0, 2, cfg)
+    want = ob.weighted_backward(q, k, v, W, do)[0]
+    rows = np.arange(n)
+    got = ob.causal_dq_rows(q, k, v, do, rq, rk, seed, 0, 2, cfg, rows)
+    assert np.allclose(got, want, rtol=1e-10, atol=1e-12)
