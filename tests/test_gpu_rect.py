@@ -60,3 +60,29 @@ def test_rect_argument_errors():
     q, k, v = (t.to(DEV) for t in _inputs(1, 1, 1, 64, 0, 64, 8, torch.bfloat16))
     with pytest.raises(ha.HyperAttnError):
         ha.forward_rect(q, k, v, block=16, samples=4, proj_bits=4)
+
+
+@pytest.mark.slow
+def test_rect_full_size_sampled_rows():
+    """The rectangular problem the benchmark times (32768 queries over
+    131072 keys, 32 heads, d = 64, bf16, block 256 -> key blocks of 1024,
+    256 samples, r = 7; inputs drawn the same way): 43 sampled query rows of
+    three heads against the oracle, one row at a time."""
+    B, H, nq, nk, d, block, m, r = 1, 32, 32768, 131072, 64, 256, 256, 7
+    g = torch.Generator(device=DEV).manual_seed(5)
+    q = (torch.randn(B, H, nq, d, generator=g, device=DEV) * d ** -0.25).to(torch.bfloat16)
+    k = (torch.randn(B, H, nk, d, generator=g, device=DEV) * d ** -0.25).to(torch.bfloat16)
+    v = torch.randn(B, H, nk, d, generator=g, device=DEV).to(torch.bfloat16)
+    seed = 0
+    out, lse = ha.forward_rect(q, k, v, block=block, samples=m, proj_bits=r, seed=seed)
+    torch.cuda.synchronize()
+    rows = np.array(sorted(set(np.random.default_rng(7).choice(nq, 40, replace=False).tolist())
+                           | {0, nq // 2, nq - 1}))
+    R = oh.projections(seed, d, r)
+    for h in (0, H // 2, H - 1):
+        print(f"[rect 32k x 131k] oracle rows of head {h}", flush=True)
+        qh, kh, vh = np32(q[0, h]), np32(k[0, h]), np32(v[0, h])
+        ro, rl = oh.noncausal_problem(qh.astype(np.float64), kh.astype(np.float64), vh.astype(np.float64),
+                                      oh.ranks(qh, R), oh.ranks(kh, R), seed, 0, h, 1, block, m, rows=rows)
+        compare(np32(out[0, h])[rows], ro, torch.bfloat16, f"head {h}")
+        compare_lse(np32(lse[0, h])[rows], rl, torch.bfloat16, f"head {h} lse")
