@@ -68,3 +68,23 @@ def kappa(q, k, rank_q, rank_k, block):
     r = residual_row_sums(q, k, rank_q, rank_k, block)
     mn = float(np.min(r))
     return float(np.max(r)) / mn if mn > 0 else float("inf")
+
+
+def column_sqmass_cols(q, k, cols, causal=False, chunk=2048):
+    """c_j = sum_i P_ij^2 for the listed columns j only, the row
+    normalisers taken chunk by chunk of rows, so that an n of tens of
+    thousands needs no n x n matrix (q, k: [n, d])."""
+    q = np.asarray(q, np.float64)
+    k = np.asarray(k, np.float64)
+    cols = np.asarray(cols, dtype=np.int64)
+    n = q.shape[0]
+    out = np.zeros(len(cols))
+    for r0 in range(0, n, chunk):
+        r1 = min(n, r0 + chunk)
+        S = q[r0:r1] @ k.T
+        if causal:
+            S = np.where(np.arange(r0, r1)[:, None] >= np.arange(n)[None, :], S, -np.inf)
+        mx = np.max(S, axis=1, keepdims=True)
+        lse = mx + np.log(np.sum(np.exp(S - mx), axis=1, keepdims=True))
+        out += np.sum(np.exp(2.0 * (S[:, cols] - lse)), axis=0)
+    return out

@@ -107,3 +107,31 @@ def test_kappa_end_to_end(block):
         qh, kh = np32(q)[0, h], np32(k)[0, h]
         ref = dg.kappa(qh.astype(np.float64), kh.astype(np.float64), oh.ranks(qh, Rn), oh.ranks(kh, Rn), block)
         assert abs(kappa[h] - ref) <= 2e-2 * ref, (h, kappa[h], ref)
+
+
+@pytest.mark.slow
+def test_alpha_full_size_glm32k():
+    """The causal 32k GQA configuration with planted sink keys that the
+    benchmark reports alpha on (32 heads over 2 KV heads, n = 32768,
+    d = 128): column masses of 40 columns (the 32 sink columns among them)
+    of two heads against the oracle's chunked form, end to end through the
+    library's exact-mode lse; alpha is the largest column mass the kernel
+    returned."""
+    from approximate_long_context_amd.workloads import WORKLOADS, make_inputs
+    w = WORKLOADS["glm32k"]
+    q, k, v = make_inputs(w, DEV)
+    n = w.n
+    lse = ha.forward(q, k, v, block=n, samples=0, proj_bits=w.proj_bits, causal=True, min_seq_len=n)[1]
+    cm, a0 = ha.column_sqmass(q, k, lse, causal=True, skip=0)
+    torch.cuda.synchronize()
+    cm = cm.cpu().numpy()
+    a0 = a0.cpu().numpy()
+    cols = np.array(sorted(set(range(0, 34)) | {n // 2, n - 2, n - 1}
+                           | set(np.random.default_rng(3).choice(n, 3, replace=False).tolist())))
+    G = w.heads // w.kv_heads
+    for h in (0, w.heads - 1):
+        print(f"[alpha glm32k] oracle columns of head {h}", flush=True)
+        assert a0[0, h] == cm[0, h].max()
+        ref = dg.column_sqmass_cols(np32(q[0, h]), np32(k[0, h // G]), cols, causal=True)
+        got = cm[0, h, cols].astype(np.float64)
+        assert np.all(np.abs(got - ref) <= 1e-2 * ref), (h, np.max(np.abs(got - ref) / ref))

@@ -96,3 +96,17 @@ def test_planted_alpha_mistakes_are_caught(monkeypatch, mutant):
     with pytest.raises(AssertionError):
         test_alpha_uniform_closed_form()
         test_alpha_causal_closed_form()
+
+
+@pytest.mark.parametrize("causal", [False, True])
+def test_column_sqmass_cols_equals_dense(causal):
+    """The chunked column masses (used at full sizes) equal the dense ones
+    on the listed columns, with chunks that do not divide n."""
+    g = np.random.default_rng(11)
+    n, d = 301, 16
+    q = g.standard_normal((n, d))
+    k = g.standard_normal((n, d))
+    cols = np.array([0, 1, 5, 150, 299, 300])
+    want = dg.column_sqmass(q, k, causal)[cols]
+    got = dg.column_sqmass_cols(q, k, cols, causal, chunk=64)
+    assert np.allclose(got, want, rtol=1e-12, atol=0)
