@@ -79,6 +79,8 @@ CASES = [
     (1, 2, 1, 1000, 64, 128, 96, 7, 9, torch.bfloat16),       # ragged last block
     (1, 2, 2, 4096, 64, 256, 256, 7, 10, torch.bfloat16),     # many workgroups, one block each
     (1, 1, 1, 3000, 128, 24, 300, 6, 11, torch.bfloat16),     # small blocks: several per workgroup
+    (2, 4, 2, 1500, 128, 96, 200, 7, 12, torch.float32),      # fp32, d = 128, batch 2, grouped heads
+    (1, 2, 1, 65, 64, 16, 8, 4, 13, torch.bfloat16),          # tiny n: one partial tile, ragged blocks
 ]
 
 
