@@ -114,3 +114,15 @@ def test_binding_fails_loudly_without_library(monkeypatch):
     monkeypatch.setattr(ha, "LIB_PATH", "/nonexistent/libhyperattn.so")
     with pytest.raises(RuntimeError):
         ha.lib()
+
+
+def test_rownorm_workspace_holds_no_partials():
+    """The row-norm variant adds per-key weights and CDF (12 bytes a key),
+    a workspace lse (4 bytes a query row) and the compact drawn rows; no
+    fp32 [heads][n][d] partial and no full sorted copy."""
+    B, n, d, H, Hkv, b, m, r = 1, 131072, 64, 32, 32, 256, 256, 7
+    plain = ha.workspace_bytes(B, n, d, H, Hkv, b, m, r)
+    rn = ha.workspace_bytes(B, n, d, H, Hkv, b, m, r, flags=ha.HA_FLAG_ROWNORM)
+    extra = Hkv * n * 12 + H * n * 4 + 2 * H * m * d * 2 + H * m * 4 + (1 << 20)
+    assert plain < rn <= plain + extra
+    assert rn < plain + H * n * d * 2          # less than one bf16 copy of the queries
