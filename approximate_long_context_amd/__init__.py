@@ -28,6 +28,7 @@ _SIGNATURES = {
     "hyperattn_workspace_bytes": (_c_size, [_c_int] * 12),
     "hyperattn_forward": (_c_int, [_vp, _vp, _vp, _c_int] + [_c_int] * 10 + [_c_u64, _vp, _vp, _vp, _c_size, _vp]),
     "hyperattn_forward_ex": (_c_int, [_vp, _vp, _vp, _c_int] + [_c_int] * 10 + [_c_u64, _c_int, _vp, _vp, _vp, _c_size, _vp]),
+    "hyperattn_forward_noalloc": (_c_int, [_vp, _vp, _vp, _c_int] + [_c_int] * 10 + [_c_u64, _vp, _vp, _vp]),
     "hyperattn_backward_workspace_bytes": (_c_size, [_c_int] * 11),
     "hyperattn_backward": (_c_int, [_vp] * 6 + [_c_int] * 11 + [_c_u64, _vp, _vp, _vp, _vp, _c_size, _vp]),
     "hyperattn_backward_rect_workspace_bytes": (_c_size, [_c_int] * 10),
@@ -156,6 +157,35 @@ def forward(q, k, v, *, block, samples, proj_bits, causal=False, min_seq_len=0, 
     _call("hyperattn_forward_ex", _ptr(q), _ptr(k), _ptr(v), dt, B, n, d, H, Hkv, block, samples,
           proj_bits, int(bool(causal)), min_seq_len, ctypes.c_uint64(seed), flags, _ptr(out),
           _ptr(lse), _ptr(workspace), workspace.numel(), _stream(dev))
+    return out, lse
+
+
+NOALLOC_SCRATCH_BYTES = 64 << 20     # HA_NOALLOC_SCRATCH_BYTES
+
+
+def forward_noalloc(q, k, v, out, lse, *, block, samples, proj_bits, causal=False, min_seq_len=0, seed=0):
+    """hyperattn_forward_noalloc: the forward with the library's own device
+    scratch array as workspace (allocates nothing).  q [B, H, n, d], k, v
+    [B, Hkv, n, d]; out (like q) and lse (float32 [B, H, n] or None) are
+    the caller's.  Returns (out, lse)."""
+    _need(q, "q")
+    dev = q.device
+    _need(k, "k", q.dtype, dev)
+    _need(v, "v", q.dtype, dev)
+    _need(out, "out", q.dtype, dev)
+    if lse is not None:
+        _need(lse, "lse", torch.float32, dev)
+    if q.dim() != 4 or k.dim() != 4 or k.shape != v.shape or out.shape != q.shape:
+        raise ValueError("q, out must be [B, H, n, d] and k, v [B, Hkv, n, d]")
+    B, H, n, d = q.shape
+    Hkv = k.shape[1]
+    if k.shape[0] != B or k.shape[2] != n or k.shape[3] != d:
+        raise ValueError("k, v must match q in batch, length and head dim")
+    if lse is not None and tuple(lse.shape) != (B, H, n):
+        raise ValueError("lse must be [B, H, n]")
+    _call("hyperattn_forward_noalloc", _ptr(q), _ptr(k), _ptr(v), _dtype_code(q.dtype), B, n, d, H, Hkv, block,
+          samples, proj_bits, int(bool(causal)), min_seq_len, ctypes.c_uint64(seed), _ptr(out), _ptr(lse),
+          _stream(dev))
     return out, lse
 
 

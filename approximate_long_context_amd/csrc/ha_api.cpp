@@ -957,6 +957,66 @@ static int backward_rect_impl(const void* q, const void* k, const void* v, const
   return launch_bwd_dkv(bp, true, s);
 }
 
+// ---- allocation-free forward ----------------------------------------------------
+// The workspace of hyperattn_forward_noalloc is a device array of the library
+// itself: one copy per GPU, created by the loader with the code object and
+// held until the process ends.  In host code `scratch` only names the
+// symbol; its device address comes from hipGetSymbolAddress, taken once per
+// device with that device current and kept per device.  No kernel of the
+// forward needs the array zeroed (every workspace buffer is written before
+// it is read within a call), so nothing is cleared between calls.
+
+}  // namespace ha
+
+static __device__ __align__(256) char scratch[HA_NOALLOC_SCRATCH_BYTES];
+
+namespace ha {
+
+constexpr int kMaxDevices = 64;
+static std::mutex g_scratch_mu;
+static void* g_scratch_dev[kMaxDevices];
+
+static int scratch_address(void** out) {
+  int dev = -1;
+  HA_CHECK_HIP(hipGetDevice(&dev));
+  if (dev < 0 || dev >= kMaxDevices) {
+    set_error("forward_noalloc: device %d outside the %d the library tracks", dev, kMaxDevices);
+    return HA_EUNSUPPORTED;
+  }
+  std::lock_guard<std::mutex> lk(g_scratch_mu);
+  if (!g_scratch_dev[dev]) {
+    void* ptr = nullptr;
+    const hipError_t e = hipGetSymbolAddress(&ptr, HIP_SYMBOL(scratch));
+    if (e != hipSuccess) return hip_status(e, "hipGetSymbolAddress(scratch)");
+    if (!ptr || reinterpret_cast<uintptr_t>(ptr) % 256) {
+      set_error("forward_noalloc: scratch array at %p is not 256-byte aligned", ptr);
+      return HA_EHIP;
+    }
+    g_scratch_dev[dev] = ptr;
+  }
+  *out = g_scratch_dev[dev];
+  return HA_OK;
+}
+
+static int forward_noalloc_impl(const void* q, const void* k, const void* v, Shape sh, uint64_t seed, void* out,
+                                float* lse, hipStream_t s) {
+  HA_TRY(validate(sh));
+  if (sh.n == 0 || sh.batch == 0 || sh.heads == 0) return HA_OK;
+  if (!q || !k || !v || !out) {
+    set_error("null q, k, v or out");
+    return HA_EINVAL;
+  }
+  const size_t need = make_plan(sh, nullptr, 0).total;
+  if (need > HA_NOALLOC_SCRATCH_BYTES) {
+    set_error("forward_noalloc: these sizes need %zu bytes of workspace, more than the %zu-byte scratch array",
+              need, static_cast<size_t>(HA_NOALLOC_SCRATCH_BYTES));
+    return HA_EWORKSPACE;
+  }
+  void* ws = nullptr;
+  HA_TRY(scratch_address(&ws));
+  return forward_impl(q, k, v, sh, seed, out, lse, ws, HA_NOALLOC_SCRATCH_BYTES, s);
+}
+
 }  // namespace ha
 
 using namespace ha;
@@ -992,6 +1052,14 @@ int hyperattn_forward(const void* q, const void* k, const void* v, int dtype, in
   return hyperattn_forward_ex(q, k, v, dtype, batch, n, d, heads, kv_heads, block, samples,
                               proj_bits, causal, min_seq_len, seed, 0, out, lse, workspace,
                               workspace_bytes, stream);
+}
+
+int hyperattn_forward_noalloc(const void* q, const void* k, const void* v, int dtype, int batch, int n, int d,
+                              int heads, int kv_heads, int block, int samples, int proj_bits, int causal,
+                              int min_seq_len, uint64_t seed, void* out, float* lse, void* stream) {
+  g_last_error.clear();
+  Shape sh{batch, n, d, heads, kv_heads, block, samples, proj_bits, causal, min_seq_len, dtype, 0};
+  return forward_noalloc_impl(q, k, v, sh, seed, out, lse, static_cast<hipStream_t>(stream));
 }
 
 size_t hyperattn_rect_workspace_bytes(int batch, int n_q, int n_k, int d, int heads, int kv_heads, int block,

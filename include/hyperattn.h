@@ -18,7 +18,8 @@
  * ---------------------------------------
  *  - Pointers marked "device" are HIP device pointers owned by the caller;
  *    the library never allocates or frees device memory and keeps no
- *    device state between calls.  "host" pointers are ordinary memory.
+ *    device state between calls, apart from the fixed scratch array of
+ *    hyperattn_forward_noalloc.  "host" pointers are ordinary memory.
  *  - `stream` is a hipStream_t (NULL = the default stream).  Device work
  *    is enqueued on it and the call returns without waiting; errors raised
  *    while the kernels run surface at the caller's next synchronisation
@@ -129,11 +130,11 @@ size_t hyperattn_workspace_bytes(int batch, int n, int d, int heads, int kv_head
  * Errors: HA_EINVAL for null q/k/v/out/workspace (when needed), batch,
  * n, heads, kv_heads < 0 or heads % kv_heads != 0, samples < 0, block < 1,
  * proj_bits outside [1, 16], bad dtype; HA_EUNSUPPORTED for d not in
- * {64, 128} or flags combined with causal; HA_ESHAPE when n (non-causal)
- * or a causal quadrant length is not a multiple of min(block, length), or
- * a causal span longer than s has odd length; HA_EWORKSPACE when
- * workspace_bytes is too small.  n == 0 or batch == 0 returns HA_OK and
- * writes nothing.
+ * {64, 128} or flags combined with causal; HA_EWORKSPACE when
+ * workspace_bytes is too small.  A segment that is not a multiple of the
+ * block gets a short last block, and a causal span of odd length splits
+ * with its extra row in the right half (rectangular quadrant).  n == 0 or
+ * batch == 0 returns HA_OK and writes nothing.
  */
 int hyperattn_forward(const void* q, const void* k, const void* v, int dtype,
                       int batch, int n, int d, int heads, int kv_heads,
@@ -147,6 +148,41 @@ int hyperattn_forward_ex(const void* q, const void* k, const void* v, int dtype,
                          int block, int samples, int proj_bits, int causal, int min_seq_len,
                          uint64_t seed, int flags, void* out, float* lse,
                          void* workspace, size_t workspace_bytes, void* stream);
+
+/* ------------------------------------------------------------------------
+ * Allocation-free forward, for callers that cannot allocate device memory
+ * (code under HIP graph capture, tight serving loops, harnesses that forbid
+ * hipMalloc).
+ * ------------------------------------------------------------------------ */
+
+/* Size of the device scratch array behind hyperattn_forward_noalloc. */
+#define HA_NOALLOC_SCRATCH_BYTES ((size_t)64 << 20)
+
+/*
+ * As hyperattn_forward (flags 0), with the workspace taken from a device
+ * array of HA_NOALLOC_SCRATCH_BYTES bytes that the library holds on each
+ * GPU it runs on until the process ends.  The call allocates nothing: no
+ * hipMalloc / hipFree, no allocating library routine.  The array of the
+ * current device is used (`stream` must belong to it); its device address
+ * is looked up once per device, on the first call there.
+ *
+ * Every call on one GPU shares that GPU's array and leaves its last
+ * contents in it (nothing in it has to start at zero).  Calls that overlap
+ * on one GPU -- on different streams, or from different threads without
+ * ordering -- race on the array and give undefined results; calls on one
+ * stream are ordered and safe.
+ *
+ * Errors: as hyperattn_forward; HA_EWORKSPACE when these sizes need more
+ * than HA_NOALLOC_SCRATCH_BYTES of workspace (hyperattn_workspace_bytes
+ * gives the need: e.g. n = 131072, 32 heads, d = 64 non-causal needs about
+ * 51 MB and fits; its causal forward needs an fp32 accumulator of 1.1 GB
+ * and is refused); HA_EHIP when the array's address cannot be obtained.
+ * Argument and size errors return before anything is enqueued.
+ */
+int hyperattn_forward_noalloc(const void* q, const void* k, const void* v, int dtype,
+                              int batch, int n, int d, int heads, int kv_heads,
+                              int block, int samples, int proj_bits, int causal, int min_seq_len,
+                              uint64_t seed, void* out, float* lse, void* stream);
 
 /* ------------------------------------------------------------------------
  * Rectangular non-causal problems: n_q queries and n_k keys per head (the

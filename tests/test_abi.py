@@ -126,3 +126,21 @@ def test_rownorm_workspace_holds_no_partials():
     extra = Hkv * n * 12 + H * n * 4 + 2 * H * m * d * 2 + H * m * 4 + (1 << 20)
     assert plain < rn <= plain + extra
     assert rn < plain + H * n * d * 2          # less than one bf16 copy of the queries
+
+
+def test_forward_noalloc_argument_errors():
+    """Errors of the allocation-free forward come before the scratch
+    array's address is looked up and before any launch."""
+    L = ha.lib()
+    dummy = ctypes.c_void_p(256)   # never dereferenced
+
+    def call(q=dummy, n=131072, causal=1, dtype=ha.HA_BF16, heads=32, d=64):
+        return L.hyperattn_forward_noalloc(q, dummy, dummy, dtype, 1, n, d, heads, 32 if heads == 32 else 1, 256,
+                                           256, 7, causal, 4096, ctypes.c_uint64(0), dummy, None, None)
+    assert call(n=0) == ha.HA_OK
+    assert call(q=None) == ha.HA_EINVAL
+    assert call(dtype=5) == ha.HA_EINVAL
+    assert call(d=96) == ha.HA_EUNSUPPORTED
+    assert call() == ha.HA_EWORKSPACE                 # 1.1 GB causal accumulator > scratch array
+    assert "scratch" in L.hyperattn_last_error().decode()
+    assert ha.workspace_bytes(1, 131072, 64, 32, 32, 256, 256, 7) <= ha.NOALLOC_SCRATCH_BYTES
