@@ -29,6 +29,8 @@ _SIGNATURES = {
     "hyperattn_forward": (_c_int, [_vp, _vp, _vp, _c_int] + [_c_int] * 10 + [_c_u64, _vp, _vp, _vp, _c_size, _vp]),
     "hyperattn_forward_ex": (_c_int, [_vp, _vp, _vp, _c_int] + [_c_int] * 10 + [_c_u64, _c_int, _vp, _vp, _vp, _c_size, _vp]),
     "hyperattn_forward_noalloc": (_c_int, [_vp, _vp, _vp, _c_int] + [_c_int] * 10 + [_c_u64, _vp, _vp, _vp]),
+    "hyperattn_debug_levels": (_c_int, [_c_int] * 3),
+    "hyperattn_forward_debug": (_c_int, [_vp, _vp, _vp, _c_int] + [_c_int] * 10 + [_c_u64, _vp, _vp, _vp, _c_size, _vp, _vp]),
     "hyperattn_backward_workspace_bytes": (_c_size, [_c_int] * 11),
     "hyperattn_backward": (_c_int, [_vp] * 6 + [_c_int] * 11 + [_c_u64, _vp, _vp, _vp, _vp, _c_size, _vp]),
     "hyperattn_backward_rect_workspace_bytes": (_c_size, [_c_int] * 10),
@@ -158,6 +160,68 @@ def forward(q, k, v, *, block, samples, proj_bits, causal=False, min_seq_len=0, 
           proj_bits, int(bool(causal)), min_seq_len, ctypes.c_uint64(seed), flags, _ptr(out),
           _ptr(lse), _ptr(workspace), workspace.numel(), _stream(dev))
     return out, lse
+
+
+class DebugDump(ctypes.Structure):
+    """ha_debug_dump: optional device pointers of hyperattn_forward_debug."""
+    _fields_ = [(name, ctypes.c_void_p) for name in
+                ("perm_q", "perm_k", "idx", "o_blk", "lse_blk", "o_smp", "lse_smp", "o_leaf", "lse_leaf")]
+
+
+def debug_levels(n, causal=False, min_seq_len=0):
+    """Levels of sorted problems of a forward (hyperattn_debug_levels)."""
+    return lib().hyperattn_debug_levels(n, int(bool(causal)), min_seq_len)
+
+
+def forward_debug(q, k, v, *, block, samples, proj_bits, causal=False, min_seq_len=0, seed=0,
+                  want=("perm_q", "perm_k", "idx", "blk", "smp", "leaf")):
+    """hyperattn_forward_debug: the forward plus its intermediates.  Returns
+    (out, lse, dump) with dump a dict of the requested buffers, shaped as
+    include/hyperattn.h states (L levels, P = 2^(L-1) node slots per level):
+    perm_q [L, B*H, n], perm_k [L, B*Hkv, n], idx [L, B*H, P, m] (int32,
+    filled with -1 where not written), o_blk / o_smp [L, B*H, n, d] and
+    lse_blk / lse_smp [L, B*H, n] (float32, NaN where not written), o_leaf
+    [B*H, n, d] and lse_leaf [B*H, n] (causal)."""
+    _need(q, "q")
+    dev = q.device
+    _need(k, "k", q.dtype, dev)
+    _need(v, "v", q.dtype, dev)
+    B, H, n, d = q.shape
+    Hkv = k.shape[1]
+    L = debug_levels(n, causal, min_seq_len)
+    if L < 0:
+        raise ValueError("bad n or min_seq_len")
+    P = 1 << max(L - 1, 0)
+    BH, BK = B * H, B * Hkv
+    i32 = dict(dtype=torch.int32, device=dev)
+    f32 = dict(dtype=torch.float32, device=dev)
+    dump, st = {}, DebugDump()
+    if "perm_q" in want:
+        dump["perm_q"] = torch.full((L, BH, n), -1, **i32)
+    if "perm_k" in want:
+        dump["perm_k"] = torch.full((L, BK, n), -1, **i32)
+    if "idx" in want:
+        dump["idx"] = torch.full((L, BH, P, samples), -1, **i32)
+    for part in ("blk", "smp"):
+        if part in want:
+            dump["o_" + part] = torch.full((L, BH, n, d), float("nan"), **f32)
+            dump["lse_" + part] = torch.full((L, BH, n), float("nan"), **f32)
+    if "leaf" in want and causal:
+        dump["o_leaf"] = torch.full((BH, n, d), float("nan"), **f32)
+        dump["lse_leaf"] = torch.full((BH, n), float("nan"), **f32)
+    for name, t in dump.items():
+        if t.numel():
+            setattr(st, name, t.data_ptr())
+    dt = _dtype_code(q.dtype)
+    out = torch.empty_like(q)
+    lse = torch.empty((B, H, n), **f32)
+    wsb = lib().hyperattn_workspace_bytes(B, n, d, H, Hkv, block, samples, proj_bits, int(bool(causal)),
+                                          min_seq_len, dt, 0)
+    ws = torch.empty(max(wsb, 256), dtype=torch.uint8, device=dev)
+    _call("hyperattn_forward_debug", _ptr(q), _ptr(k), _ptr(v), dt, B, n, d, H, Hkv, block, samples, proj_bits,
+          int(bool(causal)), min_seq_len, ctypes.c_uint64(seed), _ptr(out), _ptr(lse), _ptr(ws), ws.numel(),
+          _stream(dev), ctypes.byref(st))
+    return out, lse, dump
 
 
 NOALLOC_SCRATCH_BYTES = 64 << 20     # HA_NOALLOC_SCRATCH_BYTES

@@ -123,6 +123,7 @@ struct Shape {
   int levels = 0;    // causal levels (every split even)
   int leaf = 0;      // causal leaf length (every split even)
   bool odd = false;  // causal: some span splits unevenly (node-by-node driver)
+  int nlev = 0;      // causal: depth of the recursion (levels of quadrants)
 };
 
 static int validate(Shape& sh) {
@@ -185,6 +186,7 @@ static int validate(Shape& sh) {
   }
   sh.levels = sh.odd ? 0 : L;
   sh.leaf = sh.odd ? 0 : ns;
+  sh.nlev = L;
   return HA_OK;
 }
 
@@ -315,8 +317,68 @@ static void causal_nodes(int n, int s, std::vector<CausalNode>& leaves, std::vec
                    [](const CausalNode& a, const CausalNode& b) { return a.depth > b.depth; });
 }
 
+// ---- intermediates for hyperattn_forward_debug ----------------------------------
+// After the sort and sample kernels of the sorted problems of one launch
+// (every piece of one level, or one node): copy their permutations and
+// samples into the dump at level `lvl` (queries of piece i at row q_first +
+// i * stride of the head, keys at k_first + i * stride, samples of piece i
+// at node slot slot0 + i), then run the same attention kernel once with the
+// block keys alone and once with the samples alone, writing the parts
+// (kOutPartial) at the same rows.
+static int debug_sorted(const ha_debug_dump& dd, const AttnParams& qp, const Shape& sh, int lvl, int slot0,
+                        hipStream_t s) {
+  const int64_t BH = static_cast<int64_t>(sh.batch) * sh.heads;
+  const int64_t BK = static_cast<int64_t>(sh.batch) * sh.kv_heads;
+  const int64_t n = sh.n;
+  const int64_t P = sh.causal ? (int64_t(1) << (sh.nlev - 1)) : 1;
+  const int seg_k = qp.seg_k ? qp.seg_k : qp.seg;
+  // one copy row per (head, piece): pieces > 1 tile the head (pieces * stride == n)
+  const int64_t pitch = qp.pieces > 1 ? qp.stride : n;
+  if (qp.pieces > 1 && static_cast<int64_t>(qp.pieces) * qp.stride != n) {
+    set_error("forward_debug: pieces do not tile the head");
+    return HA_EINVAL;
+  }
+  if (dd.perm_q)
+    HA_TRY(launch_copy_rows_i32(qp.perm_q, qp.seg, dd.perm_q + lvl * BH * n + qp.q_first, pitch, qp.seg,
+                                BH * qp.pieces, s));
+  if (dd.perm_k)
+    HA_TRY(launch_copy_rows_i32(qp.perm_k, seg_k, dd.perm_k + lvl * BK * n + qp.k_first, pitch, seg_k,
+                                BK * qp.pieces, s));
+  if (dd.idx && sh.samples > 0)
+    HA_TRY(launch_copy_rows_i32(qp.sidx, static_cast<int64_t>(qp.pieces) * sh.samples,
+                                dd.idx + (lvl * BH * P + slot0) * sh.samples, P * sh.samples,
+                                qp.pieces * sh.samples, BH, s));
+  AttnParams pp = qp;
+  pp.out_mode = kOutPartial;
+  if (dd.o_blk) {
+    pp.use_block = 1;
+    pp.use_samples = 0;
+    pp.part_o = dd.o_blk + lvl * BH * n * sh.d;
+    pp.part_lse = dd.lse_blk + lvl * BH * n;
+    HA_TRY(launch_attention(pp, HA_K_ATTEND, s));
+  }
+  if (dd.o_smp) {
+    pp.use_block = 0;
+    pp.use_samples = 1;
+    pp.part_o = dd.o_smp + lvl * BH * n * sh.d;
+    pp.part_lse = dd.lse_smp + lvl * BH * n;
+    HA_TRY(launch_attention(pp, HA_K_ATTEND, s));
+  }
+  return HA_OK;
+}
+
+// The exact-leaf kernel once more, into the dump's o_leaf / lse_leaf.
+static int debug_leaf(const ha_debug_dump& dd, const AttnParams& lp, hipStream_t s) {
+  if (!dd.o_leaf) return HA_OK;
+  AttnParams dp = lp;
+  dp.out_mode = kOutAcc;
+  dp.acc_o = dd.o_leaf;
+  dp.acc_lse = dd.lse_leaf;
+  return launch_attention(dp, HA_K_LEAF, s);
+}
+
 static int forward_causal_nodes(const AttnParams& ap, const Shape& sh, const Plan& pl, uint64_t seed,
-                                hipStream_t s) {
+                                hipStream_t s, const ha_debug_dump* dbg) {
   typedef CausalNode Node;
   std::vector<Node> leaves, quads;
   causal_nodes(sh.n, sh.s, leaves, quads);
@@ -338,6 +400,7 @@ static int forward_causal_nodes(const AttnParams& ap, const Shape& sh, const Pla
     lp.acc_o = pl.acc_o;
     lp.acc_lse = pl.acc_lse;
     HA_TRY(launch_attention(lp, HA_K_LEAF, s));
+    if (dbg) HA_TRY(debug_leaf(*dbg, lp, s));
   }
   for (const Node& nd : quads) {
     const int nq = nd.hi - nd.mid, nk = nd.mid - nd.lo;
@@ -366,6 +429,7 @@ static int forward_causal_nodes(const AttnParams& ap, const Shape& sh, const Pla
     qp.final_piece = nd.leftmost ? 0 : -1;
     qp.acc_o = pl.acc_o;
     qp.acc_lse = pl.acc_lse;
+    if (dbg) HA_TRY(debug_sorted(*dbg, qp, sh, nd.depth, nd.id - (1 << nd.depth), s));
     HA_TRY(launch_attention(qp, HA_K_QUADRANT, s));
   }
   return HA_OK;
@@ -384,7 +448,8 @@ static int sort_causal_level(const uint16_t* rank_q, const uint16_t* rank_k, int
 }
 
 static int forward_impl(const void* q, const void* k, const void* v, Shape sh, uint64_t seed,
-                        void* out, float* lse, void* ws, size_t ws_bytes, hipStream_t s) {
+                        void* out, float* lse, void* ws, size_t ws_bytes, hipStream_t s,
+                        const ha_debug_dump* dbg = nullptr) {
   HA_TRY(validate(sh));
   if (sh.n == 0 || sh.batch == 0 || sh.heads == 0) return HA_OK;
   if (!q || !k || !v || !out) {
@@ -484,11 +549,12 @@ static int forward_impl(const void* q, const void* k, const void* v, Shape sh, u
     ap.out_mode = kOutFinal;
     ap.use_block = 1;
     ap.use_samples = sh.samples > 0;
+    if (dbg) HA_TRY(debug_sorted(*dbg, ap, sh, 0, 0, s));
     return launch_attention(ap, HA_K_ATTEND, s);
   }
 
   // ---- causal ----
-  if (sh.odd) return forward_causal_nodes(ap, sh, pl, seed, s);
+  if (sh.odd) return forward_causal_nodes(ap, sh, pl, seed, s, dbg);
   AttnParams lp = ap;
   lp.kind = kKindLeaf;
   lp.pieces = sh.n / sh.leaf;
@@ -501,6 +567,7 @@ static int forward_impl(const void* q, const void* k, const void* v, Shape sh, u
   lp.acc_o = pl.acc_o;
   lp.acc_lse = pl.acc_lse;
   HA_TRY(launch_attention(lp, HA_K_LEAF, s));
+  if (dbg) HA_TRY(debug_leaf(*dbg, lp, s));
 
   for (int l = sh.levels; l >= 1; --l) {
     const int seg = sh.n >> l;
@@ -527,6 +594,7 @@ static int forward_impl(const void* q, const void* k, const void* v, Shape sh, u
     qp.out_mode = kOutMerge;
     qp.acc_o = pl.acc_o;
     qp.acc_lse = pl.acc_lse;
+    if (dbg) HA_TRY(debug_sorted(*dbg, qp, sh, l - 1, 0, s));
     HA_TRY(launch_attention(qp, HA_K_QUADRANT, s));
   }
   return HA_OK;
@@ -1052,6 +1120,32 @@ int hyperattn_forward(const void* q, const void* k, const void* v, int dtype, in
   return hyperattn_forward_ex(q, k, v, dtype, batch, n, d, heads, kv_heads, block, samples,
                               proj_bits, causal, min_seq_len, seed, 0, out, lse, workspace,
                               workspace_bytes, stream);
+}
+
+int hyperattn_debug_levels(int n, int causal, int min_seq_len) {
+  if (n < 0 || (causal && min_seq_len < 1)) return -1;
+  if (!causal) return 1;
+  int L = 0;
+  for (int64_t ns = n; ns > min_seq_len; ns -= ns / 2) ++L;
+  return L;
+}
+
+int hyperattn_forward_debug(const void* q, const void* k, const void* v, int dtype, int batch, int n, int d,
+                            int heads, int kv_heads, int block, int samples, int proj_bits, int causal,
+                            int min_seq_len, uint64_t seed, void* out, float* lse, void* workspace,
+                            size_t workspace_bytes, void* stream, const ha_debug_dump* dump) {
+  g_last_error.clear();
+  if (!dump) {
+    set_error("forward_debug: null dump");
+    return HA_EINVAL;
+  }
+  if (!dump->o_blk != !dump->lse_blk || !dump->o_smp != !dump->lse_smp || !dump->o_leaf != !dump->lse_leaf) {
+    set_error("forward_debug: an o_* / lse_* pair has one pointer missing");
+    return HA_EINVAL;
+  }
+  Shape sh{batch, n, d, heads, kv_heads, block, samples, proj_bits, causal, min_seq_len, dtype, 0};
+  return forward_impl(q, k, v, sh, seed, out, lse, workspace, workspace_bytes, static_cast<hipStream_t>(stream),
+                      dump);
 }
 
 int hyperattn_forward_noalloc(const void* q, const void* k, const void* v, int dtype, int batch, int n, int d,

@@ -844,7 +844,8 @@ __global__ __launch_bounds__(64 * NW, (min_waves<T, D, KIND, NW, QPW>())) void a
         // one lane per row writes the lse, on the last slice
         const bool head = t == NDT - 1 && c == 0;
         if constexpr (OUT == kOutPartial) {
-          const int64_t pr = qpiece * p.seg + rowk[k];
+          // sorted position rowk of piece `piece` at row q_first + piece stride + rowk
+          const int64_t pr = static_cast<int64_t>(bh) * p.n + qrow0 + rowk[k];
           *reinterpret_cast<floatx4*>(p.part_o + pr * D + dc) = val;
           if (head) p.part_lse[pr] = lqk[k];
         } else {

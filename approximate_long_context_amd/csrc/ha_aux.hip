@@ -76,6 +76,29 @@ int launch_gather(const void* src, int dtype, int64_t heads, int n, int d, const
   return after_launch("gather", s);
 }
 
+// ---- strided row copy (debug dumps of permutations and sample positions) -----
+
+__global__ void copy_rows_i32_kernel(const int32_t* __restrict__ src, int64_t spitch, int32_t* __restrict__ dst,
+                                     int64_t dpitch, int width, int64_t total) {
+  for (int64_t t = static_cast<int64_t>(blockIdx.x) * blockDim.x + threadIdx.x; t < total;
+       t += static_cast<int64_t>(gridDim.x) * blockDim.x) {
+    const int64_t r = t / width;
+    const int c = static_cast<int>(t % width);
+    dst[r * dpitch + c] = src[r * spitch + c];
+  }
+}
+
+int launch_copy_rows_i32(const int32_t* src, int64_t spitch, int32_t* dst, int64_t dpitch, int width, int64_t rows,
+                         hipStream_t s) {
+  const int64_t total = rows * width;
+  if (total == 0) return HA_OK;
+  int64_t blocks = (total + 255) / 256;
+  if (blocks > 65536) blocks = 65536;
+  hipLaunchKernelGGL(copy_rows_i32_kernel, dim3(static_cast<unsigned>(blocks)), dim3(256), 0, s, src, spitch, dst,
+                     dpitch, width, total);
+  return after_launch("row copy", s);
+}
+
 // ---- log-sum-exp merge + unsort ---------------------------------------------
 
 template <typename T>

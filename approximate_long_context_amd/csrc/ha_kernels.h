@@ -35,6 +35,9 @@ int launch_sample_indices(uint64_t seed, int batch, int heads, int node_first, i
                           int ns, int m, int32_t* out, hipStream_t s);
 int launch_gather(const void* src, int dtype, int64_t heads, int n, int d, const int32_t* perm,
                   int rows_per_head, void* dst, hipStream_t s);
+// dst[r * dpitch + c] = src[r * spitch + c] for r < rows, c < width (int32)
+int launch_copy_rows_i32(const int32_t* src, int64_t spitch, int32_t* dst, int64_t dpitch, int width, int64_t rows,
+                         hipStream_t s);
 int launch_merge_unsort(const float* o1, const float* l1, const float* o2, const float* l2,
                         const int32_t* perm, int64_t heads, int n, int d, int dtype, void* out,
                         float* lse, hipStream_t s);
@@ -43,7 +46,7 @@ int launch_merge_unsort(const float* o1, const float* l1, const float* o2, const
 enum AttnKind { kKindSorted = 0, kKindLeaf = 1 };
 enum AttnOut {
   kOutFinal = 0,      // out/lse at the original row (perm_q or identity)
-  kOutPartial = 1,    // fp32 part_o/part_lse at the sorted position
+  kOutPartial = 1,    // fp32 part_o/part_lse at the sorted position (offset by the problem's first row)
   kOutLeaf = 2,       // piece 0 -> out/lse, other pieces -> acc (no read)
   kOutMerge = 3,      // merge with acc at the row; piece 0 -> out/lse, else -> acc
   kOutAcc = 4,        // every piece -> acc at the row (no read)
@@ -96,8 +99,11 @@ struct AttnParams {
   float* lse = nullptr;              // [BH][n] (may be null for kOutFinal)
   float* acc_o = nullptr;            // [BH][n][d]
   float* acc_lse = nullptr;          // [BH][n]
-  float* part_o = nullptr;           // [BH][pieces][seg][d]
-  float* part_lse = nullptr;         // [BH][pieces][seg]
+  // kOutPartial: [BH][n][d] / [BH][n]; the result of sorted position t of
+  // piece i goes to row q_first + i * stride + t of its head (so one problem
+  // per head with q_first 0 fills [BH][n] in sorted order)
+  float* part_o = nullptr;
+  float* part_lse = nullptr;
 };
 
 int launch_attention(const AttnParams& p, int timing_kind, hipStream_t s);

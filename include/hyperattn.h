@@ -150,6 +150,70 @@ int hyperattn_forward_ex(const void* q, const void* k, const void* v, int dtype,
                          void* workspace, size_t workspace_bytes, void* stream);
 
 /* ------------------------------------------------------------------------
+ * Forward with its intermediates ("HyperAttention: Long-context Attention in
+ * Near-Linear Time", research-map summary, section Approach: the sortLSH
+ * permutations, the uniform column samples, the exact block part and the
+ * sampled estimate merged per row; the one-line summary and section
+ * Limitations: the recursive causal split, whose quadrants are solved
+ * unmasked and merged with the halves' results).
+ * ------------------------------------------------------------------------ */
+
+/*
+ * Levels of sorted problems: 1 for a non-causal forward (one problem per
+ * head); for a causal forward the depth of the recursion, i.e. the smallest
+ * L >= 0 with ceil(n / 2^L) <= min_seq_len (0: the whole sequence is one
+ * exact leaf).  Level l (0-based) holds the quadrants of the spans at depth
+ * l: a span [lo, hi) longer than min_seq_len splits at mid = lo +
+ * floor((hi - lo) / 2) into node ids 2 id and 2 id + 1 (root id 1), and its
+ * quadrant is the non-causal problem of queries [mid, hi) over keys
+ * [lo, mid).  The non-causal forward's one level is the problem of queries
+ * and keys [0, n) with node id 1.  Returns -1 for n < 0, or causal with
+ * min_seq_len < 1.
+ */
+int hyperattn_debug_levels(int n, int causal, int min_seq_len);
+
+/*
+ * Optional device buffers filled by hyperattn_forward_debug; any pointer may
+ * be NULL (that buffer is not written), but o_X and lse_X of one part go
+ * together.  L = hyperattn_debug_levels(...), BH = batch * heads,
+ * BK = batch * kv_heads, P = 2^(L-1), m = samples.  Within level l the
+ * problem whose queries start at row q0 and keys at row k0 of a head writes
+ * its sorted position t at index q0 + t (queries) or k0 + t (keys) of that
+ * head's n entries; entries no problem of the level covers are not written.
+ */
+typedef struct {
+  int32_t* perm_q;   /* [L][BH][n]  sorted query position -> row (within the head) */
+  int32_t* perm_k;   /* [L][BK][n]  sorted key position -> row */
+  int32_t* idx;      /* [L][BH][P][m]  sample positions (sorted key positions of the
+                        problem) of node id, at slot id - 2^l */
+  float* o_blk;      /* [L][BH][n][d]  block part alone: softmax over the row's block keys */
+  float* lse_blk;    /* [L][BH][n]     its natural-log mass (-inf when empty) */
+  float* o_smp;      /* [L][BH][n][d]  sampled part alone: kept samples, weight ns / m */
+  float* lse_smp;    /* [L][BH][n]     its natural-log mass, ln(ns / m) included */
+  float* o_leaf;     /* [BH][n][d]     causal: exact causal attention inside each leaf, at
+                        the row (not written by non-causal calls) */
+  float* lse_leaf;   /* [BH][n] */
+} ha_debug_dump;
+
+/*
+ * As hyperattn_forward (flags 0, same workspace) and, on the same stream,
+ * the buffers of `dump`: the permutations and samples are copied from the
+ * forward's own workspace after the sort and sample kernels of each level;
+ * the parts come from the forward's attention kernel run once more per level
+ * with the block keys alone and the samples alone, written before the
+ * level's merge; the leaves from the exact-leaf kernel run once more into
+ * o_leaf.  out and lse are those of hyperattn_forward.
+ * Errors: as hyperattn_forward; HA_EINVAL for a null dump or an o_X / lse_X
+ * pair with one pointer missing.
+ */
+int hyperattn_forward_debug(const void* q, const void* k, const void* v, int dtype,
+                            int batch, int n, int d, int heads, int kv_heads,
+                            int block, int samples, int proj_bits, int causal, int min_seq_len,
+                            uint64_t seed, void* out, float* lse,
+                            void* workspace, size_t workspace_bytes, void* stream,
+                            const ha_debug_dump* dump);
+
+/* ------------------------------------------------------------------------
  * Allocation-free forward, for callers that cannot allocate device memory
  * (code under HIP graph capture, tight serving loops, harnesses that forbid
  * hipMalloc).

@@ -350,6 +350,40 @@ def causal_problem(q, k, v, rank_q, rank_k, seed, batch_idx, head, cfg, rows=Non
     return o_out, l_out
 
 
+def causal_parts(q, k, v, rank_q, rank_k, seed, batch_idx, head, cfg):
+    """The intermediates of the causal recursion of one head, problem by
+    problem (the same split as ``causal_problem``): returns (leaves, quads).
+
+    leaves: list of dicts (lo, hi, o, lse) -- exact causal attention of
+    rows [lo, hi) over keys lo..row, in row order.
+    quads: list of dicts (lo, mid, hi, node, depth) plus the ``parts`` of
+    the non-causal problem of queries [mid, hi) over keys [lo, mid): perm_q
+    and perm_k (sorted position -> row within the problem), idx (this
+    node's sample positions), lse_blk, o_blk, lse_smp, o_smp (sorted query
+    order), listed parents before children.  A row's result is the log-sum-
+    exp merge of its leaf with the quadrants holding it, deepest first."""
+    n, d = q.shape
+    s = cfg.min_seq_len
+    leaves, quads = [], []
+
+    def rec(lo, hi, node, depth):
+        ns = hi - lo
+        if ns <= s:
+            o, l = _exact_causal_rows(q[lo:hi], k[lo:hi], v[lo:hi], np.arange(ns))
+            leaves.append(dict(lo=lo, hi=hi, o=o, lse=l))
+            return
+        mid = lo + ns // 2
+        parts = {}
+        noncausal_problem(q[mid:hi], k[lo:mid], v[lo:mid], rank_q[mid:hi], rank_k[lo:mid], seed,
+                          batch_idx, head, node, cfg.block, cfg.samples, parts=parts)
+        quads.append(dict(lo=lo, mid=mid, hi=hi, node=node, depth=depth, **parts))
+        rec(lo, mid, 2 * node, depth + 1)
+        rec(mid, hi, 2 * node + 1, depth + 1)
+
+    rec(0, n, 1, 0)
+    return leaves, quads
+
+
 # ----------------------------------------------------------------------------
 # Whole forward and exact attention
 # ----------------------------------------------------------------------------

@@ -144,3 +144,30 @@ def test_forward_noalloc_argument_errors():
     assert call() == ha.HA_EWORKSPACE                 # 1.1 GB causal accumulator > scratch array
     assert "scratch" in L.hyperattn_last_error().decode()
     assert ha.workspace_bytes(1, 131072, 64, 32, 32, 256, 256, 7) <= ha.NOALLOC_SCRATCH_BYTES
+
+
+def test_forward_debug_argument_errors():
+    """A null dump or an o/lse pair with one pointer missing is refused
+    before anything is enqueued; hyperattn_debug_levels counts levels."""
+    L = ha.lib()
+    dummy = ctypes.c_void_p(256)
+    st = ha.DebugDump()
+
+    def call(dump):
+        return L.hyperattn_forward_debug(dummy, dummy, dummy, ha.HA_BF16, 1, 2048, 64, 4, 2, 96, 48, 7, 1, 256,
+                                         ctypes.c_uint64(0), dummy, dummy, dummy, 1 << 30, None, dump)
+    assert call(None) == ha.HA_EINVAL
+    st.o_blk = 256
+    assert call(ctypes.byref(st)) == ha.HA_EINVAL
+    st = ha.DebugDump()
+    st.lse_leaf = 256
+    assert call(ctypes.byref(st)) == ha.HA_EINVAL
+    st = ha.DebugDump()
+    assert L.hyperattn_forward_debug(dummy, dummy, dummy, ha.HA_BF16, 1, 2048, 96, 4, 2, 96, 48, 7, 1, 256,
+                                     ctypes.c_uint64(0), dummy, dummy, dummy, 1 << 30, None,
+                                     ctypes.byref(st)) == ha.HA_EUNSUPPORTED
+    for n, causal, s, levels in [(2048, 1, 256, 3), (1000, 1, 100, 4), (131072, 1, 4096, 5), (4096, 1, 4096, 0),
+                                 (4097, 1, 4096, 1), (777, 0, 0, 1), (0, 1, 5, 0), (10, 1, 0, -1), (-1, 0, 0, -1)]:
+        assert ha.debug_levels(n, causal, s) == levels, (n, causal, s)
+        if causal and n > 0 and s > 0:
+            assert levels == oracle.causal_levels(n, s)

@@ -289,3 +289,49 @@ def test_planted_gray_mistake_is_caught(monkeypatch):
     order = codes[np.argsort(rank)]
     diff = order[1:] ^ order[:-1]
     assert not np.all((diff & (diff - 1)) == 0)
+
+
+@pytest.mark.parametrize("n,s,block,m,H,Hkv", [(256, 32, 12, 8, 2, 1), (300, 40, 16, 5, 1, 1), (128, 200, 8, 4, 1, 1)])
+def test_causal_parts_rebuild_the_forward(n, s, block, m, H, Hkv):
+    """causal_parts lists every leaf and quadrant of the recursion with its
+    intermediates: leaves partition the rows, the quadrants of one depth
+    have disjoint query and key ranges with node ids in [2^depth,
+    2^(depth+1)), and the total mass of a row -- leaf plus the block and
+    sample parts of every quadrant holding it, as plain sums e^lse -- with
+    the matching weighted outputs gives the forward's output and lse."""
+    rng = np.random.default_rng(n + s)
+    d = 16
+    q, k, v = _rand_qkv(rng, 1, H, Hkv, n, d)
+    cfg = HAConfig(block=block, samples=m, proj_bits=5, causal=True, min_seq_len=s, seed=9)
+    out, lse = oracle.forward(q, k, v, cfg)
+    R = oracle.projections(9, d, 5)
+    for h in range(H):
+        g = h // (H // Hkv)
+        qd, kd, vd = q[0, h].astype(np.float64), k[0, g].astype(np.float64), v[0, g].astype(np.float64)
+        leaves, quads = hyperattn.causal_parts(qd, kd, vd, oracle.ranks(q[0, h], R), oracle.ranks(k[0, g], R),
+                                               9, 0, h, cfg)
+        covered = np.concatenate([np.arange(lf["lo"], lf["hi"]) for lf in leaves])
+        assert np.array_equal(np.sort(covered), np.arange(n))
+        depths = [qd_["depth"] for qd_ in quads]
+        assert (max(depths) + 1 if quads else 0) == oracle.causal_levels(n, s)
+        for dep in set(depths):
+            at = [x for x in quads if x["depth"] == dep]
+            qr = np.concatenate([np.arange(x["mid"], x["hi"]) for x in at])
+            kr = np.concatenate([np.arange(x["lo"], x["mid"]) for x in at])
+            assert len(np.unique(qr)) == len(qr) and len(np.unique(kr)) == len(kr)
+            assert all(2 ** dep <= x["node"] < 2 ** (dep + 1) for x in at)
+        D = np.zeros(n)
+        N = np.zeros((n, d))
+        for lf in leaves:
+            w = np.exp(lf["lse"])
+            D[lf["lo"]:lf["hi"]] += w
+            N[lf["lo"]:lf["hi"]] += w[:, None] * lf["o"]
+        for x in quads:
+            rows = x["mid"] + x["perm_q"]                 # sorted position -> row
+            assert np.array_equal(np.sort(x["perm_k"]), np.arange(x["mid"] - x["lo"]))
+            for lk, ok in (("lse_blk", "o_blk"), ("lse_smp", "o_smp")):
+                w = np.exp(x[lk])
+                D[rows] += w
+                N[rows] += w[:, None] * x[ok]
+        assert np.max(np.abs(N / D[:, None] - out[0, h])) < 1e-12
+        assert np.max(np.abs(np.log(D) - lse[0, h])) < 1e-12
