@@ -9,11 +9,13 @@ the GPU before timing and stay resident.
 Prints one JSON line.  ``value`` is the effective throughput of the step:
 algorithmic FLOPs (4 d B H n (b + m) per non-causal pass; for the causal
 pass the same per level over n/2 query rows plus 4 d B H (n/s) s(s+1)/2 for
-the exact leaves) divided by the measured step time.  ``roofline`` is taken
-for the kernel class with the largest share of the step, timed by HIP
-events recorded around each of its launches on the launch stream.
-``cpu_baseline`` times the CPU oracle on one of the 32 heads of the same
-workload (both passes) and scales it to the same unit.
+the exact leaves) divided by the measured step time; the timed steps run
+with no per-launch instrumentation.  ``roofline`` is taken for the kernel
+class with the largest share of the step, timed by HIP events that the
+library records around each of its launches on the launch stream, over a
+second run of the same number of steps.  ``cpu_baseline`` times the CPU
+oracle on two of the 32 heads of the same workload (both passes) and
+scales it to the same unit.
 """
 
 import argparse
@@ -135,6 +137,10 @@ def main():
     ap.add_argument("--copy-calibration", type=int, default=0, metavar="MIB",
                     help="also run 5 device-to-device copies of MIB MiB (known HBM traffic) "
                          "to calibrate hardware byte counters")
+    ap.add_argument("--gather-calibration", type=int, default=0, metavar="MIB",
+                    help="also run 5 permutation gathers (hyperattn_gather) of MIB MiB of rows through a "
+                         "random permutation: known HBM traffic with the row-wise access pattern of the "
+                         "attention kernels, to check the byte-counter calibration")
     args = ap.parse_args()
     if args.gpus != 1:
         print(f"bench.py runs on one GPU only (asked for {args.gpus}); each head is an independent "
@@ -167,15 +173,26 @@ def main():
             dst.copy_(src)
         torch.cuda.synchronize()
         del src, dst
+    if args.gather_calibration:
+        # rows of d = 64 bf16 (128 bytes), 16 heads, one random permutation per head:
+        # each gather reads and writes MIB MiB exactly once
+        rows = (args.gather_calibration << 20) // 128 // 16
+        src = torch.randn(16, rows, 64, device=dev).to(torch.bfloat16)
+        g = torch.Generator(device=dev).manual_seed(3)
+        perm = torch.stack([torch.randperm(rows, generator=g, device=dev) for _ in range(16)]).to(torch.int32)
+        for _ in range(5):
+            ha.gather_rows(src, perm)
+        torch.cuda.synchronize()
+        del src, perm
 
     for _ in range(args.warmup):
         step()
     torch.cuda.synchronize()
 
+    # timed region: exactly `steps` steps, no per-launch timing hooks
     stream = torch.cuda.current_stream(dev)
     ev0 = torch.cuda.Event(enable_timing=True)
     ev1 = torch.cuda.Event(enable_timing=True)
-    ha.timing_enable(True)
     torch.cuda.synchronize()
     ev0.record(stream)
     t0 = time.perf_counter()
@@ -184,10 +201,17 @@ def main():
     ev1.record(stream)
     torch.cuda.synchronize()
     wall = time.perf_counter() - t0
-    per_kernel = ha.timing_read()
-    ha.timing_enable(False)
     ms_total = ev0.elapsed_time(ev1)
     ms_step = ms_total / args.steps
+
+    # per-kernel durations: the same steps again, with the library recording HIP
+    # events around each launch on the launch stream
+    ha.timing_enable(True)
+    for _ in range(args.steps):
+        step()
+    torch.cuda.synchronize()
+    per_kernel = ha.timing_read()
+    ha.timing_enable(False)
 
     # separate per-pass timing (untimed for `value`, reported for context)
     pass_ms = {}
@@ -460,11 +484,12 @@ def backward_bench(ha, torch, w, q, k, v, out, lse, stream, reps=3):
 
 
 def other_configs(ha, torch, dev, stream, reps=5):
-    """ms per forward and effective TFLOP/s of the other bf16 configurations
+    """ms per forward and effective TFLOP/s of the other configurations: the
+    fp32 n = 1024 single head (against the fp32 MFMA peak) and the bf16 ones
     (not part of `value`)."""
     from approximate_long_context_amd.workloads import WORKLOADS, make_inputs
     res = {}
-    for name in ("c32k", "glm32k", "stress512k"):
+    for name in ("small", "c32k", "glm32k", "stress512k"):
         w = WORKLOADS[name]
         q, k, v = make_inputs(w, dev)
         out = torch.empty_like(q)
@@ -490,9 +515,12 @@ def other_configs(ha, torch, dev, stream, reps=5):
         kern = {kn: round(kms / reps, 4) for kn, (kms, cnt) in ha.timing_read().items() if cnt}
         ha.timing_enable(False)
         f, _ = alg_flops(w, w.causal)
+        fp32 = w.dtype == torch.float32
         res[name] = {"ms": ms, "tflops": f / (ms * 1e-3) / 1e12, "causal": w.causal, "n": w.n,
                      "heads": w.heads, "kv_heads": w.kv_heads, "head_dim": w.d,
-                     "block": w.block, "samples": w.samples, "kernels_ms": kern}
+                     "block": w.block, "samples": w.samples, "dtype": "f32" if fp32 else "bf16",
+                     "mfma_peak_tflops": MFMA_FP32_PEAK_TFLOPS if fp32 else MFMA_BF16_PEAK_TFLOPS,
+                     "kernels_ms": kern}
         del q, k, v, out, ws
     return res
 
