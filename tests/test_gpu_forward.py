@@ -158,3 +158,21 @@ def test_full_workload_sampled_rows(name):
         compare_lse(np32(lse[b, h])[rows], ref_l[i], w.dtype, f"{name} head {h}")
     assert torch.isfinite(out.float()).all()
     del G
+
+
+@pytest.mark.slow
+@pytest.mark.parametrize("name,heads", [("long131k", (0, 31)), ("long131k_causal", (0, 31)), ("stress512k", (0,))])
+def test_full_workload_every_row(name, heads):
+    """Whole heads at the benchmark's sizes and launch configuration: every
+    row of the listed heads against the oracle (out and lse)."""
+    w = WORKLOADS[name]
+    print(f"[{name}] inputs and forward", flush=True)
+    q, k, v = make_inputs(w, DEV)
+    out, lse = ha.forward(q, k, v, **w.method_args())
+    torch.cuda.synchronize()
+    qc, kc, vc = np32(q), np32(k), np32(v)
+    for h in heads:
+        print(f"[{name}] oracle, every row of head {h}", flush=True)
+        ref_o, ref_l = oracle.forward_rows(qc, kc, vc, _cfg(w), heads=[(0, h)])
+        compare(np32(out[0, h]), ref_o[0], w.dtype, f"{name} head {h}")
+        compare_lse(np32(lse[0, h]), ref_l[0], w.dtype, f"{name} head {h}")
