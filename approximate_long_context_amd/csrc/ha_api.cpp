@@ -73,6 +73,20 @@ int after_launch(const char* stage, hipStream_t stream) {
   return HA_OK;
 }
 
+// ---- injected failures (HYPERATTN_FAIL_AT) -----------------------------------
+
+static const char* const kStageNames[HA_K_COUNT] = {"proj", "hash", "sort", "samples", "gather", "attend",
+                                                    "merge", "leaf", "quadrant", "bwd_dq", "bwd_dkv"};
+
+int launch_gate(int kind) {
+  const char* s = std::getenv("HYPERATTN_FAIL_AT");   // read per launch: tests change it between calls
+  if (s && kind >= 0 && kind < HA_K_COUNT && !std::strcmp(s, kStageNames[kind])) {
+    set_error("injected failure before the %s launch (HYPERATTN_FAIL_AT)", kStageNames[kind]);
+    return HA_EHIP;
+  }
+  return HA_OK;
+}
+
 // ---- timing hooks -----------------------------------------------------------
 
 struct TimingRec {

@@ -982,6 +982,7 @@ int launch_attention(const AttnParams& p_in, int timing_kind, hipStream_t s) {
     set_error("attention: one head of q/k/v spans %lld bytes (limit 4 GiB)", static_cast<long long>(head_bytes));
     return HA_EUNSUPPORTED;
   }
+  HA_TRY(launch_gate(timing_kind));
   timing_begin(timing_kind, s);
   int st;
   if (p.dtype == HA_BF16) st = p.d == 64 ? launch_attn_d<bf16, 64>(p, s) : launch_attn_d<bf16, 128>(p, s);

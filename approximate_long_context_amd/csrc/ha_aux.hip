@@ -40,6 +40,7 @@ int launch_sample_indices(uint64_t seed, int batch, int heads, int node_first, i
   const int64_t total = static_cast<int64_t>(batch) * heads * node_count * ((m + 3) / 4);
   int64_t blocks = (total + 255) / 256;
   if (blocks > 8192) blocks = 8192;
+  HA_TRY(launch_gate(HA_K_SAMPLES));
   timing_begin(HA_K_SAMPLES, s);
   hipLaunchKernelGGL(sample_idx_kernel, dim3(static_cast<unsigned>(blocks)), dim3(256), 0, s, seed,
                      heads, node_first, node_count, static_cast<uint32_t>(ns), m, total, out);
@@ -68,6 +69,7 @@ int launch_gather(const void* src, int dtype, int64_t heads, int n, int d, const
   if (total == 0) return HA_OK;
   int64_t blocks = (total + 255) / 256;
   if (blocks > 65536) blocks = 65536;
+  HA_TRY(launch_gate(HA_K_GATHER));
   timing_begin(HA_K_GATHER, s);
   hipLaunchKernelGGL(gather_kernel, dim3(static_cast<unsigned>(blocks)), dim3(256), 0, s,
                      static_cast<const uint4v*>(src), n, cpr, perm, rows_per_head, total,
@@ -141,6 +143,7 @@ int launch_merge_unsort(const float* o1, const float* l1, const float* o2, const
   if (total == 0) return HA_OK;
   int64_t blocks = (total + 255) / 256;
   if (blocks > 65536) blocks = 65536;
+  HA_TRY(launch_gate(HA_K_MERGE));
   timing_begin(HA_K_MERGE, s);
   if (dtype == HA_BF16)
     hipLaunchKernelGGL(merge_unsort_kernel<bf16>, dim3(static_cast<unsigned>(blocks)), dim3(256), 0, s,

@@ -718,6 +718,7 @@ int launch_bwd_dq(const BwdParams& p0, hipStream_t s) {
     set_error("backward: samples %d > %d", p.m, kMaxSamples);
     return HA_EUNSUPPORTED;
   }
+  HA_TRY(launch_gate(HA_K_BWD_DQ));
   timing_begin(HA_K_BWD_DQ, s);
   if (!p.perm_q != !p.perm_k || (!p.perm_q && p.m > 0)) {
     set_error("backward dq: both permutations or neither; samples need them");
@@ -787,6 +788,7 @@ int launch_bwd_dkv(const BwdParams& p0, bool samples, hipStream_t s) {
     set_error("backward dk/dv: row-order problems are exactly the causal leaves");
     return HA_EINVAL;
   }
+  HA_TRY(launch_gate(HA_K_BWD_DKV));
   timing_begin(HA_K_BWD_DKV, s);
   int st;
   if (p.d == 64) st = samples ? launch_dkv_d<64, true>(p, s) : launch_dkv_d<64, false>(p, s);

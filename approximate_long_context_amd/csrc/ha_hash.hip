@@ -38,6 +38,7 @@ __global__ void proj_kernel(uint64_t seed, int total, float* __restrict__ R) {
 int launch_projections(uint64_t seed, int d, int r, float* R, hipStream_t s) {
   const int total = d * r;
   const int blocks = (total / 2 + 255) / 256;
+  HA_TRY(launch_gate(HA_K_PROJ));
   timing_begin(HA_K_PROJ, s);
   hipLaunchKernelGGL(proj_kernel, dim3(blocks < 1 ? 1 : blocks), dim3(256), 0, s, seed, total, R);
   timing_end(HA_K_PROJ, s);
@@ -297,6 +298,7 @@ int launch_hash(const void* x, int dtype, int64_t rows, int d, int r, const floa
                 uint16_t* rank, hipStream_t s) {
   if (rows == 0) return HA_OK;
   int st;
+  HA_TRY(launch_gate(HA_K_HASH));
   timing_begin(HA_K_HASH, s);
   if (dtype == HA_BF16) {
     st = d == 64 ? launch_hash_d<bf16, 64>(static_cast<const bf16*>(x), rows, r, R, rank, s)

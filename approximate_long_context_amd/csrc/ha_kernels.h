@@ -6,6 +6,9 @@
 namespace ha {
 
 // ---- timing hooks (ha_api.cpp) -------------------------------------------
+// HA_EHIP, with a message, when HYPERATTN_FAIL_AT names the stage of kernel
+// class `kind`; launchers call it before enqueuing anything.
+int launch_gate(int kind);
 void timing_begin(int kind, hipStream_t s);
 void timing_end(int kind, hipStream_t s);
 

@@ -267,6 +267,7 @@ int launch_sort_batch(const SortJobDesc* jobs, int njobs, int r, void* ws, size_
     return HA_EUNSUPPORTED;
   }
   const dim3 grid(static_cast<unsigned>(blocks));
+  HA_TRY(launch_gate(HA_K_SORT));
   timing_begin(HA_K_SORT, s);
   int st = HA_OK;
   for (int pass = 0; pass < (r > 8 ? 2 : 1) && st == HA_OK; ++pass) {

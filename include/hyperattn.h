@@ -24,6 +24,13 @@
  *    is enqueued on it and the call returns without waiting; errors raised
  *    while the kernels run surface at the caller's next synchronisation
  *    (set HYPERATTN_SYNC=1 to wait and check after every stage).
+ *  - Failure injection, for testing error propagation: with the environment
+ *    variable HYPERATTN_FAIL_AT set to a stage name (proj, hash, sort,
+ *    samples, gather, attend, merge, leaf, quadrant, bwd_dq, bwd_dkv), the
+ *    launcher of that stage returns HA_EHIP, with a message naming the stage,
+ *    before it enqueues anything; the call stops there.  Work of earlier
+ *    stages is already enqueued, and outputs are undefined after any
+ *    error other than an argument error.
  *  - Return value: HA_OK (0) or a negative HA_E* code.  Argument errors are
  *    detected on the host before anything is enqueued, so no output buffer
  *    is written when one is returned.  hyperattn_last_error() gives a

@@ -171,3 +171,23 @@ def test_forward_debug_argument_errors():
         assert ha.debug_levels(n, causal, s) == levels, (n, causal, s)
         if causal and n > 0 and s > 0:
             assert levels == oracle.causal_levels(n, s)
+
+
+@pytest.mark.parametrize("causal,n,s", [(0, 1024, 0), (1, 2048, 256), (1, 1000, 100)])
+def test_injected_failure_before_first_launch(monkeypatch, causal, n, s):
+    """HYPERATTN_FAIL_AT=proj stops the forward and the backward at their first
+    launcher with HA_EHIP and a message naming the stage; the host planning
+    before it runs in full (dummy device pointers are never dereferenced)."""
+    monkeypatch.setenv("HYPERATTN_FAIL_AT", "proj")
+    L = ha.lib()
+    dummy = ctypes.c_void_p(256)
+    rc = L.hyperattn_forward_ex(dummy, dummy, dummy, ha.HA_BF16, 1, n, 64, 4, 2, 96, 16, 7, causal, s,
+                                ctypes.c_uint64(0), 0, dummy, dummy, dummy, 1 << 40, None)
+    assert rc == ha.HA_EHIP
+    assert "injected failure before the proj launch" in L.hyperattn_last_error().decode()
+    rc = L.hyperattn_backward(dummy, dummy, dummy, dummy, dummy, dummy, ha.HA_BF16, 1, n, 64, 4, 2, 96, 16, 7,
+                              causal, s, ctypes.c_uint64(0), dummy, dummy, dummy, dummy, 1 << 40, None)
+    assert rc == ha.HA_EHIP
+    monkeypatch.setenv("HYPERATTN_FAIL_AT", "nothing")
+    assert L.hyperattn_forward_ex(None, None, None, ha.HA_BF16, 1, n, 64, 4, 2, 96, 16, 7, causal, s,
+                                  ctypes.c_uint64(0), 0, None, None, None, 0, None) == ha.HA_EINVAL
