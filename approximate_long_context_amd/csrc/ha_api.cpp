@@ -741,6 +741,7 @@ struct BwdPlan {
   size_t sort_ws_bytes;
   float* qstat;
   float* part;
+  uint64_t* red_keys;
   size_t total;
 };
 
@@ -766,6 +767,7 @@ static BwdPlan backward_plan(const Shape& sh, void* ws, size_t cap) {
     pl.sort_ws_bytes = sort_ws_bytes(BH, sh.n, 1, sh.r) + sort_ws_bytes(BK, sh.n, 1, sh.r);
     pl.sort_ws = cv.take<char>(pl.sort_ws_bytes);
     pl.part = cv.take<float>(bwd_part_floats(BH, sh.n, 1, sh.samples, sh.d));
+    pl.red_keys = cv.take<uint64_t>(BH * m1);
   } else if (sh.levels > 0) {
     pl.perm_q = cv.take<int32_t>(BH * (sh.n / 2));
     pl.perm_k = cv.take<int32_t>(BK * (sh.n / 2));
@@ -783,6 +785,7 @@ static BwdPlan backward_plan(const Shape& sh, void* ws, size_t cap) {
     pl.sort_ws_bytes = mx;
     pl.sort_ws = cv.take<char>(mx);
     pl.part = cv.take<float>(part);
+    pl.red_keys = cv.take<uint64_t>(BH * (int64_t(1) << (sh.levels - 1)) * m1);
   } else if (sh.odd) {
     const int half = sh.n - sh.n / 2;           // the longest quadrant side
     pl.perm_q = cv.take<int32_t>(BH * half);
@@ -791,6 +794,7 @@ static BwdPlan backward_plan(const Shape& sh, void* ws, size_t cap) {
     pl.sort_ws_bytes = sort_ws_bytes(BH, half, 1, sh.r) + sort_ws_bytes(BK, half, 1, sh.r);
     pl.sort_ws = cv.take<char>(pl.sort_ws_bytes);
     pl.part = cv.take<float>(bwd_part_floats(BH, half, 1, sh.samples, sh.d));
+    pl.red_keys = cv.take<uint64_t>(BH * m1);
   }
   pl.total = align_up(cv.used, 256) + 256;
   return pl;
@@ -807,6 +811,11 @@ static int backward_impl(const void* q, const void* k, const void* v, const void
   if (sh.flags) {
     set_error("backward takes no flags");
     return HA_EINVAL;
+  }
+  if (sh.kv_heads > 0 && static_cast<int64_t>(sh.heads / sh.kv_heads) * sh.samples > kBwdMaxGroupSamples) {
+    set_error("backward: (heads / kv_heads) * samples = %lld exceeds %d",
+              static_cast<long long>(sh.heads / sh.kv_heads) * sh.samples, kBwdMaxGroupSamples);
+    return HA_EUNSUPPORTED;
   }
   if (sh.n == 0 || sh.batch == 0 || sh.heads == 0) return HA_OK;
   if (!q || !k || !v || !out || !lse || !dout || !dq || !dk || !dv) {
@@ -847,6 +856,7 @@ static int backward_impl(const void* q, const void* k, const void* v, const void
   bp.Hkv = sh.kv_heads;
   bp.BH = static_cast<int>(BH);
   bp.part = pl.part;
+  bp.red_keys = pl.red_keys;
   bp.dq = dq;
   bp.dk = dk;
   bp.dv = dv;
@@ -965,6 +975,7 @@ static BwdPlan backward_rect_plan(const Shape& sh, int n_k, void* ws, size_t cap
   pl.sort_ws_bytes = sort_ws_bytes(BH, sh.n, 1, sh.r) + sort_ws_bytes(BK, n_k, 1, sh.r);
   pl.sort_ws = cv.take<char>(pl.sort_ws_bytes);
   pl.part = cv.take<float>(bwd_part_floats(BH, sh.n, 1, sh.samples, sh.d));
+  pl.red_keys = cv.take<uint64_t>(BH * m1);
   pl.total = align_up(cv.used, 256) + 256;
   return pl;
 }
@@ -975,6 +986,11 @@ static int backward_rect_impl(const void* q, const void* k, const void* v, const
   HA_TRY(rect_validate(sh, n_k));
   if (sh.dtype != HA_BF16) {
     set_error("backward: bf16 inputs only");
+    return HA_EUNSUPPORTED;
+  }
+  if (sh.kv_heads > 0 && static_cast<int64_t>(sh.heads / sh.kv_heads) * sh.samples > kBwdMaxGroupSamples) {
+    set_error("backward: (heads / kv_heads) * samples = %lld exceeds %d",
+              static_cast<long long>(sh.heads / sh.kv_heads) * sh.samples, kBwdMaxGroupSamples);
     return HA_EUNSUPPORTED;
   }
   if (sh.n == 0 || sh.batch == 0 || sh.heads == 0) return HA_OK;
@@ -1017,6 +1033,7 @@ static int backward_rect_impl(const void* q, const void* k, const void* v, const
   bp.Hkv = sh.kv_heads;
   bp.BH = static_cast<int>(BH);
   bp.part = pl.part;
+  bp.red_keys = pl.red_keys;
   bp.dq = dq;
   bp.dk = dk;
   bp.dv = dv;

@@ -643,38 +643,90 @@ __global__ __launch_bounds__(kBNT, 2) void bwd_dkv_kernel(BwdParams p) {
   }
 }
 
-// Sum of a sample slot's partial [dK | dV] rows over the query chunks,
-// added to the rows of the slot's key (several slots -- duplicate samples,
-// the query heads of a group -- can share a key row, hence the atomics).
-// One thread per 4 columns of a slot row.
-template <int D>
-__global__ __launch_bounds__(256) void bwd_dkv_reduce_kernel(BwdParams p, int nchunk) {
-  constexpr int TPR = 2 * D / 4;                    // threads per slot row
-  const int64_t t = static_cast<int64_t>(blockIdx.x) * 256 + threadIdx.x;
-  const int64_t row = t / TPR;                      // (bh * pieces + piece) * m + slot
-  if (row >= static_cast<int64_t>(p.BH) * p.pieces * p.m) return;
-  const int c = static_cast<int>(t % TPR) * 4;
-  const int64_t cstride = static_cast<int64_t>(p.BH) * p.pieces * p.m * (2 * D);
-  const float* src = p.part + row * (2 * D) + c;
-  floatx4 acc = {0.f, 0.f, 0.f, 0.f};
-  int ch = 0;
-  for (; ch + 4 <= nchunk; ch += 4) {
-    floatx4 x[4];
-#pragma unroll
-    for (int u = 0; u < 4; ++u) x[u] = *reinterpret_cast<const floatx4*>(src + (ch + u) * cstride);
-#pragma unroll
-    for (int u = 0; u < 4; ++u) acc += x[u];
+// Sum of the sample slots' partial [dK | dV] rows, in a fixed order.  Several
+// slots can name one key row (duplicate draws, and the query heads of a KV
+// group draw on the same keys), so per problem (KV head, piece) the G m slots
+// of its query heads are first sorted by (key position, head, draw) -- a
+// bitonic sort in LDS writing the sorted keys to the workspace -- and then one
+// wave per run of equal key positions sums the run's partial rows over the
+// query chunks, slot by slot in that order, and adds the total to the key's
+// dK and dV rows as their only writer: bitwise deterministic results.
+constexpr int kRedCap = kBwdMaxGroupSamples;   // slots per problem (G m) the sort holds in LDS
+
+__global__ __launch_bounds__(1024) void bwd_red_sort_kernel(BwdParams p) {
+  __shared__ uint64_t key[kRedCap];
+  const int G = p.H / p.Hkv;
+  const int S = G * p.m;
+  int P = 1;
+  while (P < S) P <<= 1;
+  const int prob = blockIdx.x;                      // (batch * Hkv + g) * pieces + piece
+  const int bkv = prob / p.pieces, piece = prob - bkv * p.pieces;
+  const int b = bkv / p.Hkv, g = bkv - b * p.Hkv;
+  for (int e = threadIdx.x; e < P; e += 1024) {
+    uint64_t kk = ~0ull;
+    if (e < S) {
+      const int gi = e / p.m, i = e - gi * p.m;
+      const int64_t bh = static_cast<int64_t>(b) * p.H + g * G + gi;
+      const uint32_t kpos = static_cast<uint32_t>(p.sidx[(bh * p.pieces + piece) * p.m + i]);
+      kk = (static_cast<uint64_t>(kpos) << 32) | static_cast<uint32_t>(e);
+    }
+    key[e] = kk;
   }
-  for (; ch < nchunk; ++ch) acc += *reinterpret_cast<const floatx4*>(src + ch * cstride);
-  const int prob = static_cast<int>(row / p.m);
-  const int bh = prob / p.pieces;
-  const int piece = prob - bh * p.pieces;
-  const int bkv = (bh / p.H) * p.Hkv + (bh % p.H) / (p.H / p.Hkv);
-  const int kpos = p.sidx[row];
-  const int krow = p.perm_k[(static_cast<int64_t>(bkv) * p.pieces + piece) * p.seg_k + kpos];
-  float* dst = (c < D ? p.dk : p.dv) + (static_cast<int64_t>(bkv) * p.n_k + krow) * D + (c < D ? c : c - D);
+  __syncthreads();
+  for (int k = 2; k <= P; k <<= 1)
+    for (int j = k >> 1; j > 0; j >>= 1) {
+      for (int e = threadIdx.x; e < P; e += 1024) {
+        const int x = e ^ j;
+        if (x > e) {
+          const uint64_t a = key[e], c = key[x];
+          if ((a > c) == ((e & k) == 0)) {
+            key[e] = c;
+            key[x] = a;
+          }
+        }
+      }
+      __syncthreads();
+    }
+  uint64_t* out = p.red_keys + static_cast<int64_t>(prob) * S;
+  for (int e = threadIdx.x; e < S; e += 1024) out[e] = key[e];
+}
+
+template <int D>
+__global__ __launch_bounds__(256) void bwd_red_sum_kernel(BwdParams p, int nchunk) {
+  constexpr int PL = 2 * D / 64;                    // [dK | dV] columns per lane
+  const int G = p.H / p.Hkv;
+  const int S = G * p.m;
+  const int64_t w = (static_cast<int64_t>(blockIdx.x) * 256 + threadIdx.x) >> 6;
+  const int lane = threadIdx.x & 63;
+  const int64_t nprob = static_cast<int64_t>(p.BH / G) * p.pieces;
+  if (w >= nprob * S) return;
+  const int prob = static_cast<int>(w / S);
+  const int e = static_cast<int>(w - static_cast<int64_t>(prob) * S);
+  const uint64_t* sk = p.red_keys + static_cast<int64_t>(prob) * S;
+  const uint32_t kpos = static_cast<uint32_t>(sk[e] >> 32);
+  if (e > 0 && static_cast<uint32_t>(sk[e - 1] >> 32) == kpos) return;   // not the first slot of its run
+  const int bkv = prob / p.pieces, piece = prob - bkv * p.pieces;
+  const int b = bkv / p.Hkv, g = bkv - b * p.Hkv;
+  const int64_t cstride = static_cast<int64_t>(p.BH) * p.pieces * p.m * (2 * D);
+  float acc[PL];
 #pragma unroll
-  for (int i = 0; i < 4; ++i) unsafeAtomicAdd(dst + i, acc[i]);
+  for (int i = 0; i < PL; ++i) acc[i] = 0.f;
+  for (int x = e; x < S && static_cast<uint32_t>(sk[x] >> 32) == kpos; ++x) {
+    const int loc = static_cast<int>(sk[x] & 0xFFFFFFFFull);
+    const int gi = loc / p.m, i = loc - gi * p.m;
+    const int64_t bh = static_cast<int64_t>(b) * p.H + g * G + gi;
+    const float* src = p.part + ((bh * p.pieces + piece) * p.m + i) * (2 * D) + PL * lane;
+    for (int ch = 0; ch < nchunk; ++ch) {
+      const float* r = src + ch * cstride;
+#pragma unroll
+      for (int c = 0; c < PL; ++c) acc[c] += r[c];
+    }
+  }
+  const int krow = p.perm_k[static_cast<int64_t>(prob) * p.seg_k + kpos];
+  const int col = PL * lane;                         // column of [dK | dV]
+  float* dst = (col < D ? p.dk : p.dv) + (static_cast<int64_t>(bkv) * p.n_k + krow) * D + (col < D ? col : col - D);
+#pragma unroll
+  for (int c = 0; c < PL; ++c) dst[c] += acc[c];
 }
 
 // ---- launches ---------------------------------------------------------------------------
@@ -746,9 +798,11 @@ static int launch_dkv_d2(const BwdParams& p, hipStream_t s) {
   hipLaunchKernelGGL((bwd_dkv_kernel<D, SAMPLE, MASK, IDENT>), dim3(static_cast<unsigned>(blocks)), dim3(kBNT), lds,
                      s, p);
   if constexpr (SAMPLE) {
-    const int64_t threads = static_cast<int64_t>(p.BH) * p.pieces * p.m * (2 * D / 4);
-    hipLaunchKernelGGL((bwd_dkv_reduce_kernel<D>), dim3(static_cast<unsigned>((threads + 255) / 256)), dim3(256), 0,
-                       s, p, nchunk);
+    const int64_t nprob = static_cast<int64_t>(p.BH / (p.H / p.Hkv)) * p.pieces;
+    hipLaunchKernelGGL(bwd_red_sort_kernel, dim3(static_cast<unsigned>(nprob)), dim3(1024), 0, s, p);
+    const int64_t threads = nprob * (p.H / p.Hkv) * p.m * 64;   // one wave per sorted slot
+    hipLaunchKernelGGL((bwd_red_sum_kernel<D>), dim3(static_cast<unsigned>((threads + 255) / 256)), dim3(256), 0, s,
+                       p, nchunk);
   }
   return HA_OK;
 }
@@ -776,9 +830,14 @@ int launch_bwd_dkv(const BwdParams& p0, bool samples, hipStream_t s) {
     set_error("backward dk/dv: a problem needs keys; causal problems are square");
     return HA_EINVAL;
   }
-  if (samples && (!p.part || !p.perm_k || p.qchunk < kBT || p.qchunk % kBT)) {
-    set_error("backward dk/dv: bad sample partial buffer, permutation or query chunk");
+  if (samples && (!p.part || !p.red_keys || !p.perm_k || p.qchunk < kBT || p.qchunk % kBT)) {
+    set_error("backward dk/dv: bad sample partial buffer, sort buffer, permutation or query chunk");
     return HA_EINVAL;
+  }
+  if (samples && static_cast<int64_t>(p.H / p.Hkv) * p.m > kRedCap) {
+    set_error("backward dk/dv: (heads / kv_heads) * samples = %lld exceeds %d",
+              static_cast<long long>(p.H / p.Hkv) * p.m, kRedCap);
+    return HA_EUNSUPPORTED;
   }
   if (p.causal && (samples || (p.diag != 1 && p.diag != 2))) {
     set_error("backward dk/dv: causal problems take no samples and need a diagonal part");

@@ -147,10 +147,15 @@ struct BwdParams {
   int bcap = 0;                      // LDS block key list capacity (launcher)
   int qchunk = 2048;                 // queries per sample-key workgroup (bwd_query_chunk)
   float* part = nullptr;             // sample-key partials [ceil(seg / qchunk)][BH][pieces][m][2 d] fp32
+  uint64_t* red_keys = nullptr;      // sorted (key position, slot) per (KV head, piece): [BHkv][pieces][G m]
   float* dq = nullptr;               // [BH][n][d] fp32
   float* dk = nullptr;               // [BHkv][n][d] fp32
   float* dv = nullptr;
 };
+
+// Largest (heads / kv_heads) * samples of a backward (the sample reduction
+// sorts that many slots per problem in LDS).
+constexpr int kBwdMaxGroupSamples = 8192;
 
 // Queries per sample-key workgroup of the dK/dV pass: at least 2048, and
 // at most 64 chunks per problem (bounds the partial buffer).

@@ -378,8 +378,10 @@ size_t hyperattn_backward_workspace_bytes(int batch, int n, int d, int heads, in
  *   workspace  device, >= hyperattn_backward_workspace_bytes(...) bytes,
  *              256-byte aligned, owned by the caller, clobbered
  *   stream     hipStream_t or NULL; asynchronous on it
- * The sample part of dK and dV is accumulated with fp32 atomic adds, so
- * their last bits may vary from run to run; dQ is deterministic.
+ * Results are bitwise deterministic: the sampled keys' contributions to dK
+ * and dV are summed in a fixed order (per KV head and problem, sorted by key
+ * position, query head and draw), one writer per key row.  For that sort,
+ * (heads / kv_heads) * samples must not exceed 8192 (else HA_EUNSUPPORTED).
  * Causal calls run the exact leaves first (dq, dk, dv stored), then every
  * level's quadrant problems (added); when some span splits unevenly, node
  * by node with rectangular quadrants (n_q = n_k + 1), as the forward.

@@ -191,3 +191,13 @@ def test_injected_failure_before_first_launch(monkeypatch, causal, n, s):
     monkeypatch.setenv("HYPERATTN_FAIL_AT", "nothing")
     assert L.hyperattn_forward_ex(None, None, None, ha.HA_BF16, 1, n, 64, 4, 2, 96, 16, 7, causal, s,
                                   ctypes.c_uint64(0), 0, None, None, None, 0, None) == ha.HA_EINVAL
+
+
+def test_backward_group_sample_limit():
+    """The backward sorts a KV group's sample slots in LDS: (heads / kv_heads)
+    * samples above 8192 is refused before any launch."""
+    L = ha.lib()
+    dummy = ctypes.c_void_p(256)
+    rc = L.hyperattn_backward(dummy, dummy, dummy, dummy, dummy, dummy, ha.HA_BF16, 1, 4096, 64, 32, 1, 128, 512,
+                              7, 0, 0, ctypes.c_uint64(0), dummy, dummy, dummy, dummy, 1 << 40, None)
+    assert rc == ha.HA_EUNSUPPORTED and "8192" in L.hyperattn_last_error().decode()
