@@ -278,20 +278,21 @@ def forward_rect(q, k, v, *, block, samples, proj_bits, seed=0, out=None, lse=No
 
 
 def backward_workspace_bytes(batch, n, d, heads, kv_heads, block, samples, proj_bits, causal=False,
-                             min_seq_len=0):
+                             min_seq_len=0, dtype=torch.bfloat16):
     return lib().hyperattn_backward_workspace_bytes(batch, n, d, heads, kv_heads, block, samples, proj_bits,
-                                                    int(bool(causal)), min_seq_len, HA_BF16)
+                                                    int(bool(causal)), min_seq_len, _dtype_code(dtype))
 
 
 def backward(q, k, v, out, lse, dout, *, block, samples, proj_bits, causal=False, min_seq_len=0,
              seed=0, dq=None, dk=None, dv=None, workspace=None):
     """Gradients of sum(dout * out) for (out, lse) = forward(q, k, v, ...)
-    with the same arguments.  bf16 inputs; returns float32 (dq like q,
-    dk and dv like k)."""
-    _need(q, "q", torch.bfloat16)
+    with the same arguments.  bf16 or fp32 inputs (all of one dtype);
+    returns float32 (dq like q, dk and dv like k)."""
+    _need(q, "q")
     dev = q.device
+    dt = _dtype_code(q.dtype)
     for t, name in ((k, "k"), (v, "v"), (out, "out"), (dout, "dout")):
-        _need(t, name, torch.bfloat16, dev)
+        _need(t, name, q.dtype, dev)
     _need(lse, "lse", torch.float32, dev)
     if q.dim() != 4 or k.dim() != 4 or k.shape != v.shape or out.shape != q.shape or dout.shape != q.shape:
         raise ValueError("q, out, dout must be [B, H, n, d] and k, v [B, Hkv, n, d]")
@@ -310,10 +311,10 @@ def backward(q, k, v, out, lse, dout, *, block, samples, proj_bits, causal=False
         if t.shape != shp:
             raise ValueError(f"{name} must have shape {tuple(shp)}")
     wsb = lib().hyperattn_backward_workspace_bytes(B, n, d, H, Hkv, block, samples, proj_bits,
-                                                   int(bool(causal)), min_seq_len, HA_BF16)
+                                                   int(bool(causal)), min_seq_len, dt)
     if workspace is None or workspace.numel() < wsb:
         workspace = torch.empty(max(wsb, 256), dtype=torch.uint8, device=dev)
-    _call("hyperattn_backward", _ptr(q), _ptr(k), _ptr(v), _ptr(out), _ptr(lse), _ptr(dout), HA_BF16,
+    _call("hyperattn_backward", _ptr(q), _ptr(k), _ptr(v), _ptr(out), _ptr(lse), _ptr(dout), dt,
           B, n, d, H, Hkv, block, samples, proj_bits, int(bool(causal)), min_seq_len, ctypes.c_uint64(seed),
           _ptr(dq), _ptr(dk), _ptr(dv), _ptr(workspace), workspace.numel(), _stream(dev))
     return dq, dk, dv
@@ -323,11 +324,13 @@ def backward_rect(q, k, v, out, lse, dout, *, block, samples, proj_bits, seed=0,
                   workspace=None):
     """Gradients of sum(dout * out) for (out, lse) = forward_rect(q, k, v, ...)
     with the same arguments: q, out, dout [B, H, n_q, d], k, v [B, Hkv, n_k, d]
-    (bf16), lse [B, H, n_q]; returns float32 (dq like q, dk and dv like k)."""
-    _need(q, "q", torch.bfloat16)
+    (bf16 or fp32, one dtype), lse [B, H, n_q]; returns float32 (dq like q,
+    dk and dv like k)."""
+    _need(q, "q")
     dev = q.device
+    dt = _dtype_code(q.dtype)
     for t, name in ((k, "k"), (v, "v"), (out, "out"), (dout, "dout")):
-        _need(t, name, torch.bfloat16, dev)
+        _need(t, name, q.dtype, dev)
     _need(lse, "lse", torch.float32, dev)
     if (q.dim() != 4 or k.dim() != 4 or k.shape != v.shape or out.shape != q.shape or dout.shape != q.shape
             or k.shape[0] != q.shape[0] or k.shape[3] != q.shape[3]):
@@ -343,10 +346,10 @@ def backward_rect(q, k, v, out, lse, dout, *, block, samples, proj_bits, seed=0,
         _need(t, name, torch.float32, dev)
         if t.shape != shp:
             raise ValueError(f"{name} must have shape {tuple(shp)}")
-    wsb = lib().hyperattn_backward_rect_workspace_bytes(B, nq, nk, d, H, Hkv, block, samples, proj_bits, HA_BF16)
+    wsb = lib().hyperattn_backward_rect_workspace_bytes(B, nq, nk, d, H, Hkv, block, samples, proj_bits, dt)
     if workspace is None or workspace.numel() < wsb:
         workspace = torch.empty(max(wsb, 256), dtype=torch.uint8, device=dev)
-    _call("hyperattn_backward_rect", _ptr(q), _ptr(k), _ptr(v), _ptr(out), _ptr(lse), _ptr(dout), HA_BF16,
+    _call("hyperattn_backward_rect", _ptr(q), _ptr(k), _ptr(v), _ptr(out), _ptr(lse), _ptr(dout), dt,
           B, nq, nk, d, H, Hkv, block, samples, proj_bits, ctypes.c_uint64(seed),
           _ptr(dq), _ptr(dk), _ptr(dv), _ptr(workspace), workspace.numel(), _stream(dev))
     return dq, dk, dv

@@ -804,10 +804,6 @@ static int backward_impl(const void* q, const void* k, const void* v, const void
                          const void* dout, Shape sh, uint64_t seed, float* dq, float* dk, float* dv, void* ws,
                          size_t ws_bytes, hipStream_t s) {
   HA_TRY(validate(sh));
-  if (sh.dtype != HA_BF16) {
-    set_error("backward: bf16 inputs only");
-    return HA_EUNSUPPORTED;
-  }
   if (sh.flags) {
     set_error("backward takes no flags");
     return HA_EINVAL;
@@ -831,7 +827,7 @@ static int backward_impl(const void* q, const void* k, const void* v, const void
     set_error("workspace must be 256-byte aligned");
     return HA_EINVAL;
   }
-  if (static_cast<int64_t>(sh.n) * sh.d * 2 >= (int64_t(1) << 32)) {
+  if (static_cast<int64_t>(sh.n) * sh.d * (sh.dtype == HA_BF16 ? 2 : 4) >= (int64_t(1) << 32)) {
     set_error("backward: one head of q/k/v spans 4 GiB or more");
     return HA_EUNSUPPORTED;
   }
@@ -843,6 +839,7 @@ static int backward_impl(const void* q, const void* k, const void* v, const void
   HA_TRY(launch_hash(k, sh.dtype, BK * sh.n, sh.d, sh.r, pl.R, pl.rank_k, s));
 
   BwdParams bp;
+  bp.dtype = sh.dtype;
   bp.q = q;
   bp.k = k;
   bp.v = v;
@@ -984,10 +981,6 @@ static int backward_rect_impl(const void* q, const void* k, const void* v, const
                               const void* dout, Shape sh, int n_k, uint64_t seed, float* dq, float* dk, float* dv,
                               void* ws, size_t ws_bytes, hipStream_t s) {
   HA_TRY(rect_validate(sh, n_k));
-  if (sh.dtype != HA_BF16) {
-    set_error("backward: bf16 inputs only");
-    return HA_EUNSUPPORTED;
-  }
   if (sh.kv_heads > 0 && static_cast<int64_t>(sh.heads / sh.kv_heads) * sh.samples > kBwdMaxGroupSamples) {
     set_error("backward: (heads / kv_heads) * samples = %lld exceeds %d",
               static_cast<long long>(sh.heads / sh.kv_heads) * sh.samples, kBwdMaxGroupSamples);
@@ -1019,6 +1012,7 @@ static int backward_rect_impl(const void* q, const void* k, const void* v, const
   HA_TRY(launch_sample_indices(seed, sh.batch, sh.heads, 1, 1, n_k, sh.samples, pl.sidx, s));
 
   BwdParams bp;
+  bp.dtype = sh.dtype;
   bp.q = q;
   bp.k = k;
   bp.v = v;

@@ -100,7 +100,8 @@ int launch_bwd_qstat(const BwdParams& p, hipStream_t s) {
   const int rpw = 64 / (p.d / 8);
   int64_t blocks = (rows + 4 * rpw - 1) / (4 * rpw);
   if (blocks > 16384) blocks = 16384;
-  if (p.d == 64) hipLaunchKernelGGL(bwd_qstat_kernel<64>, dim3(blocks), dim3(256), 0, s, p);
+  if (p.dtype == HA_F32) HA_TRY(launch_bwd32_qstat(p, s));
+  else if (p.d == 64) hipLaunchKernelGGL(bwd_qstat_kernel<64>, dim3(blocks), dim3(256), 0, s, p);
   else hipLaunchKernelGGL(bwd_qstat_kernel<128>, dim3(blocks), dim3(256), 0, s, p);
   return after_launch("backward row statistics", s);
 }
@@ -729,6 +730,17 @@ __global__ __launch_bounds__(256) void bwd_red_sum_kernel(BwdParams p, int nchun
   for (int c = 0; c < PL; ++c) dst[c] += acc[c];
 }
 
+// The deterministic sum of the sample partials (both dtypes).
+int launch_bwd_sample_reduce(const BwdParams& p, int nchunk, hipStream_t s) {
+  const int64_t nprob = static_cast<int64_t>(p.BH / (p.H / p.Hkv)) * p.pieces;
+  hipLaunchKernelGGL(bwd_red_sort_kernel, dim3(static_cast<unsigned>(nprob)), dim3(1024), 0, s, p);
+  const int64_t threads = nprob * (p.H / p.Hkv) * p.m * 64;   // one wave per sorted slot
+  const dim3 g(static_cast<unsigned>((threads + 255) / 256)), b(256);
+  if (p.d == 64) hipLaunchKernelGGL((bwd_red_sum_kernel<64>), g, b, 0, s, p, nchunk);
+  else hipLaunchKernelGGL((bwd_red_sum_kernel<128>), g, b, 0, s, p, nchunk);
+  return HA_OK;
+}
+
 // ---- launches ---------------------------------------------------------------------------
 
 // n_k = 0, seg_k = 0 and b_k = 0 mean a square problem (n_k = n, seg_k = seg,
@@ -777,7 +789,8 @@ int launch_bwd_dq(const BwdParams& p0, hipStream_t s) {
     return HA_EINVAL;
   }
   int st;
-  if (p.perm_q) st = p.d == 64 ? launch_dq_d<64, false>(p, s) : launch_dq_d<128, false>(p, s);
+  if (p.dtype == HA_F32) st = launch_bwd32_dq(p, s);
+  else if (p.perm_q) st = p.d == 64 ? launch_dq_d<64, false>(p, s) : launch_dq_d<128, false>(p, s);
   else st = p.d == 64 ? launch_dq_d<64, true>(p, s) : launch_dq_d<128, true>(p, s);
   timing_end(HA_K_BWD_DQ, s);
   if (st != HA_OK) return st;
@@ -797,13 +810,7 @@ static int launch_dkv_d2(const BwdParams& p, hipStream_t s) {
   const size_t lds = 2 * dkv_buf_bytes<D>();
   hipLaunchKernelGGL((bwd_dkv_kernel<D, SAMPLE, MASK, IDENT>), dim3(static_cast<unsigned>(blocks)), dim3(kBNT), lds,
                      s, p);
-  if constexpr (SAMPLE) {
-    const int64_t nprob = static_cast<int64_t>(p.BH / (p.H / p.Hkv)) * p.pieces;
-    hipLaunchKernelGGL(bwd_red_sort_kernel, dim3(static_cast<unsigned>(nprob)), dim3(1024), 0, s, p);
-    const int64_t threads = nprob * (p.H / p.Hkv) * p.m * 64;   // one wave per sorted slot
-    hipLaunchKernelGGL((bwd_red_sum_kernel<D>), dim3(static_cast<unsigned>((threads + 255) / 256)), dim3(256), 0, s,
-                       p, nchunk);
-  }
+  if constexpr (SAMPLE) return launch_bwd_sample_reduce(p, nchunk, s);
   return HA_OK;
 }
 
@@ -850,7 +857,8 @@ int launch_bwd_dkv(const BwdParams& p0, bool samples, hipStream_t s) {
   HA_TRY(launch_gate(HA_K_BWD_DKV));
   timing_begin(HA_K_BWD_DKV, s);
   int st;
-  if (p.d == 64) st = samples ? launch_dkv_d<64, true>(p, s) : launch_dkv_d<64, false>(p, s);
+  if (p.dtype == HA_F32) st = launch_bwd32_dkv(p, samples, s);
+  else if (p.d == 64) st = samples ? launch_dkv_d<64, true>(p, s) : launch_dkv_d<64, false>(p, s);
   else st = samples ? launch_dkv_d<128, true>(p, s) : launch_dkv_d<128, false>(p, s);
   timing_end(HA_K_BWD_DKV, s);
   if (st != HA_OK) return st;

@@ -113,7 +113,8 @@ int launch_attention(const AttnParams& p, int timing_kind, hipStream_t s);
 
 // ---- backward (ha_bwd.hip) ------------------------------------------------
 struct BwdParams {
-  const void* q = nullptr;           // [BH][n][d] bf16
+  int dtype = HA_BF16;               // of q, k, v, out, dout (HA_F32: the fp32 kernels)
+  const void* q = nullptr;           // [BH][n][d]
   const void* k = nullptr;           // [BHkv][n][d]
   const void* v = nullptr;
   const void* out = nullptr;         // forward output [BH][n][d]
@@ -184,5 +185,11 @@ int launch_kappa(const float* lse_exact, const float* lse_block, const int32_t* 
 int launch_bwd_qstat(const BwdParams& p, hipStream_t s);
 int launch_bwd_dq(const BwdParams& p, hipStream_t s);
 int launch_bwd_dkv(const BwdParams& p, bool samples, hipStream_t s);
+// deterministic sum of the sample partials into dk / dv (ha_bwd.hip)
+int launch_bwd_sample_reduce(const BwdParams& p, int nchunk, hipStream_t s);
+// fp32 kernels (ha_bwd32.hip), reached through the launchers above
+int launch_bwd32_qstat(const BwdParams& p, hipStream_t s);
+int launch_bwd32_dq(const BwdParams& p, hipStream_t s);
+int launch_bwd32_dkv(const BwdParams& p, bool samples, hipStream_t s);
 
 }  // namespace ha

@@ -369,10 +369,10 @@ size_t hyperattn_backward_workspace_bytes(int batch, int n, int d, int heads, in
 /*
  * Gradients of sum(dout * out) for out = hyperattn_forward(q, k, v, ...)
  * with the same shape and method arguments and seed.
- *   q, k, v    device, as for hyperattn_forward (bf16 only)
- *   out, lse   device, the forward's outputs (out [B, H, n, d] bf16, lse
- *              [B, H, n] fp32 natural log)
- *   dout       device [B, H, n, d] bf16, upstream gradient of out
+ *   q, k, v    device, as for hyperattn_forward (bf16 or fp32)
+ *   out, lse   device, the forward's outputs (out [B, H, n, d] of dtype,
+ *              lse [B, H, n] fp32 natural log)
+ *   dout       device [B, H, n, d] of dtype, upstream gradient of out
  *   dq         device [B, H, n, d] fp32, written (every element)
  *   dk, dv     device [B, Hkv, n, d] fp32, written (every element)
  *   workspace  device, >= hyperattn_backward_workspace_bytes(...) bytes,
@@ -385,7 +385,9 @@ size_t hyperattn_backward_workspace_bytes(int batch, int n, int d, int heads, in
  * Causal calls run the exact leaves first (dq, dk, dv stored), then every
  * level's quadrant problems (added); when some span splits unevenly, node
  * by node with rectangular quadrants (n_q = n_k + 1), as the forward.
- * Errors: as hyperattn_forward; HA_EUNSUPPORTED for fp32 inputs.
+ * bf16 inputs run the MFMA kernels; fp32 inputs run fp32 vector kernels
+ * (one wave per query row, key and sample slot; for small problems).
+ * Errors: as hyperattn_forward.
  */
 int hyperattn_backward(const void* q, const void* k, const void* v, const void* out,
                        const float* lse, const void* dout, int dtype,
@@ -395,13 +397,13 @@ int hyperattn_backward(const void* q, const void* k, const void* v, const void* 
                        void* workspace, size_t workspace_bytes, void* stream);
 
 /* Backward of the rectangular forward (hyperattn_forward_rect): q, out,
- * dout [batch, heads, n_q, d], k, v [batch, kv_heads, n_k, d] (bf16),
+ * dout [batch, heads, n_q, d], k, v [batch, kv_heads, n_k, d] (bf16 or fp32),
  * lse [batch, heads, n_q]; dq [batch, heads, n_q, d], dk, dv [batch,
  * kv_heads, n_k, d] fp32, written (every element).  The same weighted
  * softmax backward over the rectangular problem's weights (query blocks of
  * b_eff = min(block, n_q) paired with key blocks of ceil(b_eff n_k / n_q),
  * samples over the n_k keys with weight n_k / samples).
- * Errors: as hyperattn_forward_rect; HA_EUNSUPPORTED for fp32 inputs. */
+ * Errors: as hyperattn_forward_rect. */
 size_t hyperattn_backward_rect_workspace_bytes(int batch, int n_q, int n_k, int d, int heads, int kv_heads,
                                                int block, int samples, int proj_bits, int dtype);
 int hyperattn_backward_rect(const void* q, const void* k, const void* v, const void* out, const float* lse,

@@ -1,4 +1,4 @@
-"""GPU parity of the backward (bf16, non-causal and causal) against the fp64 oracle.
+"""GPU parity of the backward (bf16 and fp32, non-causal and causal) against the fp64 oracle.
 
 The library's forward gives (out, lse); its backward then gives dq, dk, dv
 in fp32, compared with ``oracle.backward.backward`` on the same bf16 inputs
@@ -124,18 +124,56 @@ def test_backward_deterministic(H, Hkv, n, d, block, m, causal, s):
             assert torch.equal(x.view(torch.int32), y.view(torch.int32))
 
 
-def test_backward_rejects_fp32():
-    """The C entry point answers fp32 inputs with HA_EUNSUPPORTED before any launch."""
-    import ctypes
-    q, k, v, do = (t.float().to(DEV) for t in _inputs(1, 1, 1, 256, 64, 12))
-    out, lse = ha.forward(q, k, v, block=64, samples=16, proj_bits=5)
-    dq, dk, dv = (torch.empty_like(t) for t in (q, k, v))
-    ws = torch.empty(1 << 20, dtype=torch.uint8, device=DEV)
-    with pytest.raises(ha.HyperAttnError) as e:
-        ha._call("hyperattn_backward", ha._ptr(q), ha._ptr(k), ha._ptr(v), ha._ptr(out), ha._ptr(lse),
-                 ha._ptr(do), ha.HA_F32, 1, 256, 64, 1, 1, 64, 16, 5, 0, 0, ctypes.c_uint64(0),
-                 ha._ptr(dq), ha._ptr(dk), ha._ptr(dv), ha._ptr(ws), ws.numel(), ha._stream(q.device))
-    assert e.value.code == ha.HA_EUNSUPPORTED
+FP32_CASES = [
+    # B, H, Hkv, n, d, block, samples, r, causal, min_seq_len, seed
+    (1, 1, 1, 1024, 64, 64, 64, 7, False, 0, 31),       # the fp32 single-head workload
+    (1, 4, 2, 777, 128, 96, 40, 6, False, 0, 32),       # grouped heads, ragged last block, d = 128
+    (2, 2, 2, 512, 64, 64, 200, 5, False, 0, 33),       # many duplicate samples
+    (1, 2, 1, 1024, 64, 64, 32, 6, True, 256, 34),      # two causal levels, grouped heads
+    (1, 2, 2, 1000, 128, 64, 20, 6, True, 100, 35),     # odd splits
+]
+
+
+def _inputs32(B, H, Hkv, n, d, seed):
+    g = torch.Generator(device="cpu").manual_seed(seed)
+    s = d ** -0.25
+    return (torch.randn(B, H, n, d, generator=g) * s, torch.randn(B, Hkv, n, d, generator=g) * s,
+            torch.randn(B, Hkv, n, d, generator=g), torch.randn(B, H, n, d, generator=g))
+
+
+@pytest.mark.parametrize("B,H,Hkv,n,d,block,m,r,causal,s,seed", FP32_CASES)
+def test_backward_fp32_matches_oracle(B, H, Hkv, n, d, block, m, r, causal, s, seed):
+    """fp32 inputs run the fp32 kernels; against the fp64 oracle within 1e-4
+    relative (Frobenius, and per element against the largest magnitude)."""
+    q, k, v, do = _inputs32(B, H, Hkv, n, d, seed)
+    args = dict(block=block, samples=m, proj_bits=r, causal=causal, min_seq_len=s, seed=seed)
+    qd, kd, vd, dod = q.to(DEV), k.to(DEV), v.to(DEV), do.to(DEV)
+    out, lse = ha.forward(qd, kd, vd, **args)
+    dq, dk, dv = ha.backward(qd, kd, vd, out, lse, dod, **args)
+    dq2, dk2, dv2 = ha.backward(qd, kd, vd, out, lse, dod, **args)
+    torch.cuda.synchronize()
+    for a, b in ((dq, dq2), (dk, dk2), (dv, dv2)):
+        assert torch.equal(a, b)
+    rq, rk, rv = ob.backward(q.numpy(), k.numpy(), v.numpy(), do.numpy(), HAConfig(**args))
+    for got, ref, what in ((dq, rq, "dq"), (dk, rk, "dk"), (dv, rv, "dv")):
+        got = got.cpu().numpy().astype(np.float64)
+        scale = float(np.max(np.abs(ref))) or 1.0
+        assert float(np.max(np.abs(got - ref))) <= 1e-4 * scale, what
+        assert float(np.linalg.norm(got - ref) / np.linalg.norm(ref)) <= 1e-4, what
+
+
+def test_backward_rect_fp32():
+    q, k, v, do = _inputs32(1, 2, 1, 300, 64, 36)
+    k2, v2 = _inputs32(1, 1, 1, 700, 64, 37)[1:3]
+    args = dict(block=50, samples=30, proj_bits=6, seed=3)
+    qd, kd, vd, dod = q.to(DEV), k2.to(DEV), v2.to(DEV), do.to(DEV)
+    out, lse = ha.forward_rect(qd, kd, vd, **args)
+    dq, dk, dv = ha.backward_rect(qd, kd, vd, out, lse, dod, **args)
+    torch.cuda.synchronize()
+    rq, rk, rv = ob.backward_rect(q.numpy(), k2.numpy(), v2.numpy(), do.numpy(), HAConfig(**args))
+    for got, ref, what in ((dq, rq, "dq"), (dk, rk, "dk"), (dv, rv, "dv")):
+        got = got.cpu().numpy().astype(np.float64)
+        assert float(np.linalg.norm(got - ref) / np.linalg.norm(ref)) <= 1e-4, what
 
 
 ODD_CASES = [
