@@ -305,7 +305,7 @@ def causal_levels(n, min_seq_len):
     return L
 
 
-def causal_problem(q, k, v, rank_q, rank_k, seed, batch_idx, head, cfg, rows=None):
+def causal_problem(q, k, v, rank_q, rank_k, seed, batch_idx, head, cfg, rows=None, quadrant=None):
     """Causal HyperAttention of one head.  causal(lo, hi, node): a span of
     length <= min_seq_len is exact causal attention; otherwise, with
     mid = lo + (hi - lo) // 2 (reading R19: an odd span gives its right
@@ -314,7 +314,10 @@ def causal_problem(q, k, v, rank_q, rank_k, seed, batch_idx, head, cfg, rows=Non
     first) with the non-causal problem of queries [mid, hi) over keys
     [lo, mid) (rectangular when the span is odd, reading R18), with this
     node's samples.  Ranks come from the one hash of the whole sequence
-    (one projection matrix for all nodes)."""
+    (one projection matrix for all nodes).
+
+    ``quadrant(lo, mid, hi, node, local_rows) -> (o, lse)`` solves one
+    quadrant (rows local to [mid, hi)); None: ``noncausal_problem``."""
     n, d = q.shape
     s = cfg.min_seq_len
     all_rows = np.arange(n) if rows is None else np.sort(np.asarray(rows, dtype=np.int64))
@@ -338,9 +341,12 @@ def causal_problem(q, k, v, rank_q, rank_k, seed, batch_idx, head, cfg, rows=Non
         rec(mid, hi, 2 * node + 1, upper)
         if len(upper) == 0:
             return
-        oq, lq = noncausal_problem(q[mid:hi], k[lo:mid], v[lo:mid], rank_q[mid:hi],
-                                   rank_k[lo:mid], seed, batch_idx, head, node,
-                                   cfg.block, cfg.samples, rows=upper - mid)
+        if quadrant is None:
+            oq, lq = noncausal_problem(q[mid:hi], k[lo:mid], v[lo:mid], rank_q[mid:hi],
+                                       rank_k[lo:mid], seed, batch_idx, head, node,
+                                       cfg.block, cfg.samples, rows=upper - mid)
+        else:
+            oq, lq = quadrant(lo, mid, hi, node, upper - mid)
         sel = np.array([pos_of[int(r)] for r in upper])
         l_new, o_new = lse_merge(l_out[sel], o_out[sel], lq, oq)
         l_out[sel] = l_new

@@ -16,6 +16,16 @@ approximate-matrix-multiplication reading that the rest supports):
   draw inside the row's block contributes nothing; duplicates count each
   time.
 * out_i = (N_blk + N_rn) / (D_blk + D_unif), lse_i = ln(D_blk + D_unif).
+* Causal (reading R20): the leaves stay exact; every quadrant of the
+  recursion (queries [mid, hi), keys [lo, mid), node id `node`) is such a
+  problem with that node's draws -- the largest weight, the CDF and the
+  Philox counters (i // 4, node, head, 2 batch + 2) all over the node's
+  keys -- and its (out, lse) merges with the rest of the row by the usual
+  log-sum-exp merge, so a row's result is
+  (N_leaf + sum over its quadrants of (N_blk + N_rn)) /
+  (D_leaf + sum over its quadrants of (D_blk + D_unif)).  A rectangular
+  quadrant (odd span) takes the key blocks of reading R18 for both the
+  uniform and the row-norm exclusions.
 
 Exact probabilities, so that the draws are reproducible bit for bit:
 w_t = ||v_t||^2 in fp32 (each square rounded, groups of 8 consecutive
@@ -35,7 +45,8 @@ from fractions import Fraction
 
 import numpy as np
 
-from .hyperattn import block_part, sample_part, sample_positions, sort_perm, _check, ranks
+from .hyperattn import (block_part, causal_problem, key_block, sample_part, sample_positions, sort_perm, _check,
+                        ranks)
 from .gauss import projections
 from .philox import philox_words
 
@@ -96,11 +107,14 @@ def rownorm_positions(seed, batch_idx, head, node, n_sorted, m):
     return pos, T
 
 
-def rownorm_part(Qs, Ks, Vs, idx, n_sorted, T, b_eff, positions=None):
+def rownorm_part(Qs, Ks, Vs, idx, n_sorted, T, b_eff, positions=None, b_k=None):
     """Residual numerator estimate as (lse_r, o_r):
     e^{lse_r} = sum_{kept s} A_{p, idx_s} T / (m n_{idx_s}) and
-    o_r e^{lse_r} = sum_{kept s} A_{p, idx_s} T / (m n_{idx_s}) v_{idx_s}."""
+    o_r e^{lse_r} = sum_{kept s} A_{p, idx_s} T / (m n_{idx_s}) v_{idx_s};
+    draw s is kept unless idx_s // b_k == p // b_eff (b_k = b_eff for
+    square problems)."""
     ns, d = Qs.shape
+    b_k = b_eff if b_k is None else b_k
     if positions is None:
         positions = np.arange(ns)
     positions = np.asarray(positions, dtype=np.int64)
@@ -111,7 +125,7 @@ def rownorm_part(Qs, Ks, Vs, idx, n_sorted, T, b_eff, positions=None):
     n_s = np.asarray(n_sorted, dtype=np.int64)[idx]
     logw = np.log(float(T)) - np.log(float(m)) - np.log(n_s.astype(np.float64))
     Ksm, Vsm = Ks[idx], Vs[idx]
-    col_blk = idx // b_eff
+    col_blk = idx // b_k
     lse = np.empty(len(positions))
     o = np.empty((len(positions), d))
     for c in range(0, len(positions), 4096):
@@ -142,18 +156,26 @@ def merge_variant(lb, ob, lu, lr, orr):
 
 def noncausal_problem_rownorm(q, k, v, rank_q, rank_k, v32, seed, batch_idx, head, node, block,
                               samples, rows=None, parts=None):
-    """One non-causal problem with the row-norm product (reading R15).
-    v32: the value rows as fp32 (for the exact weights).  Returns (o, lse)
-    in original row order (``rows``: local indices, all if None)."""
+    """One non-causal problem of ns queries and n_k keys with the row-norm
+    product (reading R15; n_k != ns for a rectangular causal quadrant,
+    reading R18).  v32: the value rows as fp32 (for the exact weights).
+    Returns (o, lse) in original row order (``rows``: local indices, all
+    if None)."""
     ns, d = q.shape
+    n_k = k.shape[0]
+    if ns == 0:
+        return np.zeros((0, d)), np.zeros(0)
+    if n_k == 0:
+        raise ValueError("a problem with queries needs keys")
     b_eff = min(block, ns)
     if b_eff < 1:
         raise ValueError("block must be >= 1")
+    b_k = key_block(b_eff, ns, n_k)
     pq = sort_perm(rank_q)
     pk = sort_perm(rank_k)
     Qs, Ks, Vs = q[pq], k[pk], v[pk]
     n_sorted = quantized_weights(row_norms_sq(v32))[pk]
-    idx_u = sample_positions(seed, batch_idx, head, node, ns, samples)
+    idx_u = sample_positions(seed, batch_idx, head, node, n_k, samples)
     idx_r, T = rownorm_positions(seed, batch_idx, head, node, n_sorted, samples)
     if rows is None:
         positions = None
@@ -161,9 +183,9 @@ def noncausal_problem_rownorm(q, k, v, rank_q, rank_k, v32, seed, batch_idx, hea
         inv = np.empty(ns, dtype=np.int64)
         inv[pq] = np.arange(ns)
         positions = inv[np.asarray(rows, dtype=np.int64)]
-    lb, ob = block_part(Qs, Ks, Vs, b_eff, positions)
-    lu, _ = sample_part(Qs, Ks, Vs, idx_u, b_eff, positions)
-    lr, orr = rownorm_part(Qs, Ks, Vs, idx_r, n_sorted, T, b_eff, positions)
+    lb, ob = block_part(Qs, Ks, Vs, b_eff, positions, b_k)
+    lu, _ = sample_part(Qs, Ks, Vs, idx_u, b_eff, positions, b_k)
+    lr, orr = rownorm_part(Qs, Ks, Vs, idx_r, n_sorted, T, b_eff, positions, b_k)
     lse, o = merge_variant(lb, ob, lu, lr, orr)
     if parts is not None:
         parts.update(perm_q=pq, perm_k=pk, idx_u=idx_u, idx_r=idx_r, n_sorted=n_sorted, T=T,
@@ -177,11 +199,21 @@ def noncausal_problem_rownorm(q, k, v, rank_q, rank_k, v32, seed, batch_idx, hea
     return o, lse
 
 
+def causal_problem_rownorm(q, k, v, rank_q, rank_k, v32, seed, batch_idx, head, cfg, rows=None):
+    """Causal forward of one head with the row-norm product in every
+    quadrant (reading R20): the recursion of ``causal_problem`` with each
+    node's quadrant solved by ``noncausal_problem_rownorm`` under that
+    node's id.  q, k, v fp64 [n, d]; v32 the value rows as fp32."""
+    def quadrant(lo, mid, hi, node, local_rows):
+        return noncausal_problem_rownorm(q[mid:hi], k[lo:mid], v[lo:mid], rank_q[mid:hi], rank_k[lo:mid],
+                                         v32[lo:mid], seed, batch_idx, head, node, cfg.block, cfg.samples,
+                                         rows=local_rows)
+    return causal_problem(q, k, v, rank_q, rank_k, seed, batch_idx, head, cfg, rows=rows, quadrant=quadrant)
+
+
 def forward_rows(q, k, v, cfg, heads=None, rows=None):
-    """Non-causal forward with the row-norm product for the listed (batch,
-    head) pairs and rows; arguments as ``oracle.hyperattn.forward_rows``."""
-    if cfg.causal:
-        raise ValueError("the row-norm variant is defined here for non-causal problems")
+    """Forward with the row-norm product for the listed (batch, head) pairs
+    and rows; arguments as ``oracle.hyperattn.forward_rows``."""
     B, H, Hkv, n, d = _check(q, k, v, cfg)
     G = H // Hkv
     if heads is None:
@@ -195,16 +227,19 @@ def forward_rows(q, k, v, cfg, heads=None, rows=None):
     for i, (b, h) in enumerate(heads):
         g = h // G
         rq, rk = ranks(q[b, h], R), ranks(k[b, g], R)
-        o, l = noncausal_problem_rownorm(q[b, h].astype(np.float64), k[b, g].astype(np.float64),
-                                         v[b, g].astype(np.float64), rq, rk, v[b, g], cfg.seed, b, h, 1,
-                                         cfg.block, cfg.samples, rows=rows)
+        q64, k64, v64 = q[b, h].astype(np.float64), k[b, g].astype(np.float64), v[b, g].astype(np.float64)
+        if cfg.causal:
+            o, l = causal_problem_rownorm(q64, k64, v64, rq, rk, v[b, g], cfg.seed, b, h, cfg, rows=rows)
+        else:
+            o, l = noncausal_problem_rownorm(q64, k64, v64, rq, rk, v[b, g], cfg.seed, b, h, 1,
+                                             cfg.block, cfg.samples, rows=rows)
         out[i] = o
         lse[i] = l
     return out, lse
 
 
 def forward(q, k, v, cfg):
-    """Full non-causal forward with the row-norm product:
+    """Full forward with the row-norm product:
     (out [B, H, n, d], lse [B, H, n]) in fp64."""
     B, H, n, d = q.shape
     out, lse = forward_rows(q, k, v, cfg)

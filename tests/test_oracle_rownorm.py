@@ -14,6 +14,20 @@
   equals the uniform method's exactly;
 * planted mistakes (uniform weight, norm instead of squared norm, wrong
   block in the exclusion) each trip one of these.
+
+Causal variant (every quadrant with its own node's draws):
+* the normaliser (lse) equals the uniform causal method's exactly;
+* block >= n (every quadrant is one block) and min_seq_len >= n each give
+  exact causal attention;
+* unbiasedness of the whole causal numerator: with one draw per quadrant,
+  the expectation of out e^lse -- each node's draw enumerated over every
+  key position of that node with its exact probability -- equals the
+  exact causal numerator sum_{j <= i} e^{q_i . k_j} v_j (spans of odd
+  length included, so rectangular quadrants are covered);
+* each node's weights are the squared norms of its own key rows;
+* planted mistakes (weights ignoring the norms, weights of the wrong
+  rows, the merge dropping the row-norm part, the wrong key block in the
+  exclusion) each trip one of these.
 """
 
 from fractions import Fraction
@@ -168,12 +182,12 @@ _correct_part = rn.rownorm_part
 _correct_quant = rn.quantized_weights
 
 
-def _uniform_weight_part(Qs, Ks, Vs, idx, n_sorted, T, b_eff, positions=None):
-    return oh.sample_part(Qs, Ks, Vs, idx, b_eff, positions)
+def _uniform_weight_part(Qs, Ks, Vs, idx, n_sorted, T, b_eff, positions=None, b_k=None):
+    return oh.sample_part(Qs, Ks, Vs, idx, b_eff, positions, b_k)
 
 
-def _wrong_block_part(Qs, Ks, Vs, idx, n_sorted, T, b_eff, positions=None):
-    return _correct_part(Qs, Ks, Vs, idx, n_sorted, T, 1, positions)
+def _wrong_block_part(Qs, Ks, Vs, idx, n_sorted, T, b_eff, positions=None, b_k=None):
+    return _correct_part(Qs, Ks, Vs, idx, n_sorted, T, 1, positions, 1)
 
 
 def _norm_not_squared(w32):
@@ -192,3 +206,124 @@ def test_planted_norm_mistake_is_caught(monkeypatch):
     monkeypatch.setattr(rn, "quantized_weights", _norm_not_squared)
     with pytest.raises(AssertionError):
         test_probabilities_follow_squared_norms()
+
+
+# ---- causal variant -----------------------------------------------------------------------
+
+def _causal_head(n, d, seed):
+    g = np.random.default_rng(seed)
+    q = (g.standard_normal((n, d)) * 0.5).astype(np.float32)
+    k = (g.standard_normal((n, d)) * 0.5).astype(np.float32)
+    v = g.standard_normal((n, d)).astype(np.float32)
+    return q, k, v
+
+
+def _causal_run(q, k, v, cfg):
+    R = oracle.projections(cfg.seed, q.shape[1], cfg.proj_bits)
+    rq, rk = oh.ranks(q, R), oh.ranks(k, R)
+    return rn.causal_problem_rownorm(q.astype(np.float64), k.astype(np.float64), v.astype(np.float64), rq, rk, v,
+                                     cfg.seed, 0, 0, cfg)
+
+
+@pytest.mark.parametrize("n,s,block", [(64, 8, 4), (45, 6, 3)])
+def test_causal_lse_is_the_uniform_methods(n, s, block):
+    q, k, v = _causal_head(n, 8, 20 + n)
+    cfg = oh.HAConfig(block=block, samples=5, proj_bits=4, causal=True, min_seq_len=s, seed=4)
+    _, l1 = _causal_run(q, k, v, cfg)
+    _, l2 = oh.forward(q[None, None], k[None, None], v[None, None], cfg)
+    assert np.array_equal(l1, l2[0, 0])
+
+
+@pytest.mark.parametrize("block,s", [(64, 8), (8, 64)])
+def test_causal_limits_are_exact_attention(block, s):
+    n = 64
+    q, k, v = _causal_head(n, 8, 31)
+    cfg = oh.HAConfig(block=block, samples=7, proj_bits=4, causal=True, min_seq_len=s, seed=5)
+    o, l = _causal_run(q, k, v, cfg)
+    oe, le = oh.exact_attention(q[None, None].astype(np.float64), k[None, None].astype(np.float64),
+                                v[None, None].astype(np.float64), causal=True)
+    assert np.max(np.abs(o - oe[0, 0])) < 1e-12 and np.max(np.abs(l - le[0, 0])) < 1e-12
+
+
+def test_causal_numerator_is_unbiased(monkeypatch):
+    # n = 20, min_seq_len 4: spans 20 -> 10 -> 5 -> (2, 3); the spans of 5
+    # split unevenly (3 queries over 2 keys)
+    n, d = 20, 6
+    q, k, v = _causal_head(n, d, 41)
+    cfg = oh.HAConfig(block=2, samples=1, proj_bits=3, causal=True, min_seq_len=4, seed=6)
+    real = rn.rownorm_positions
+    seen = {}                                          # node -> its sorted n_t
+
+    def record(seed, b, h, node, n_sorted, m):
+        seen[node] = np.asarray(n_sorted, dtype=np.int64).copy()
+        return real(seed, b, h, node, n_sorted, m)
+
+    monkeypatch.setattr(rn, "rownorm_positions", record)
+    _causal_run(q, k, v, cfg)
+    assert sorted(seen) == [1, 2, 3, 4, 5, 6, 7]
+    # node -> its keys [lo, mid): the node's weights are the squared norms of
+    # those value rows (as a multiset: the order is the node's sort)
+    keys = {1: (0, 10), 2: (0, 5), 3: (10, 15), 4: (0, 2), 5: (5, 7), 6: (10, 12), 7: (15, 17)}
+    for node, (lo, mid) in keys.items():
+        sq = np.sum(v[lo:mid].astype(np.float64) ** 2, axis=1)
+        got = np.sort(seen[node] / seen[node].sum())
+        assert len(got) == mid - lo and np.max(np.abs(got - np.sort(sq / sq.sum()))) < 1e-6
+    choice = {node: 0 for node in seen}
+
+    def forced(seed, b, h, node, n_sorted, m):
+        assert m == 1 and np.array_equal(n_sorted, seen[node])
+        return np.array([choice[node]], dtype=np.int64), int(np.sum(n_sorted))
+
+    monkeypatch.setattr(rn, "rownorm_positions", forced)
+
+    def numerator():
+        o, l = _causal_run(q, k, v, cfg)
+        return o * np.exp(l)[:, None]
+
+    base = numerator()
+    expect = base.copy()
+    for node, ns in seen.items():                       # the estimate is linear in each node's draw
+        T = int(ns.sum())
+        for t in range(len(ns)):
+            if ns[t] == 0:
+                continue
+            choice[node] = t
+            expect += (ns[t] / T) * (numerator() - base)
+        choice[node] = 0
+    q64, k64, v64 = (x.astype(np.float64) for x in (q, k, v))
+    A = np.exp(q64 @ k64.T) * np.tri(n)
+    exact = A @ v64
+    assert np.max(np.abs(expect - exact)) < 1e-10 * np.max(np.abs(exact))
+
+
+_correct_merge = rn.merge_variant
+_correct_problem = rn.noncausal_problem_rownorm
+
+
+def _flat_weights(w32):
+    # planted: every key equally likely (the node's norms ignored)
+    return np.full(np.shape(w32), 2 ** 39, dtype=np.int64)
+
+
+def _merge_without_rownorm(lb, ob, lu, lr, orr):
+    return _correct_merge(lb, ob, lu, lr, orr * 0.0)
+
+
+def _query_rows_weights(q, k, v, rank_q, rank_k, v32, *args, **kw):
+    # planted: the weights taken from rows other than the node's keys (the
+    # head's last rows)
+    return _correct_problem(q, k, v, rank_q, rank_k, _QUERY_V[0][-len(v32):], *args, **kw)
+
+
+_QUERY_V = [None]
+
+
+@pytest.mark.parametrize("target,mutant", [("quantized_weights", _flat_weights),
+                                           ("merge_variant", _merge_without_rownorm),
+                                           ("rownorm_part", _wrong_block_part),
+                                           ("noncausal_problem_rownorm", _query_rows_weights)])
+def test_planted_causal_mistakes_are_caught(monkeypatch, target, mutant):
+    _QUERY_V[0] = _causal_head(20, 6, 41)[2]
+    monkeypatch.setattr(rn, target, mutant)
+    with pytest.raises(AssertionError):
+        test_causal_numerator_is_unbiased(monkeypatch)
