@@ -175,8 +175,8 @@ static int validate(Shape& sh) {
     set_error("unknown flags 0x%x", sh.flags);
     return HA_EINVAL;
   }
-  if (sh.causal && sh.flags) {
-    set_error("flags apply to the non-causal forward only");
+  if (sh.causal && (sh.flags & ~HA_FLAG_ROWNORM)) {
+    set_error("flags other than HA_FLAG_ROWNORM apply to the non-causal forward only");
     return HA_EUNSUPPORTED;
   }
   if ((sh.flags & HA_FLAG_ROWNORM) && sh.flags != HA_FLAG_ROWNORM) {
@@ -220,15 +220,20 @@ struct Plan {
   void* vs;
   float* part_o[3];
   float* part_lse[3];
-  float* rn_w;                 // row-norm variant: squared norms of V rows
-  int64_t* rn_cum;             // integer CDF per KV head
-  int32_t* rn_sidx;            // draws per query head
+  float* rn_w;                 // row-norm variant: squared norms of V rows [BHkv][n]
+  int64_t* rn_cum;             // integer CDF per (KV head, piece)
+  int32_t* rn_sidx;            // draws per (query head, piece)
   void* rn_ws;                 // CDF scratch: chunk maxima and chunk totals
-  void* rn_kc;                 // drawn K rows per query head [BH][m][d]
-  void* rn_vc;                 // drawn V rows, weighted [BH][m][d]
-  float* rn_lse;               // lse when the caller passes none [BH][n]
+  void* rn_kc;                 // drawn K rows per (query head, piece) [BH][pieces][m][d]
+  void* rn_vc;                 // drawn V rows, weighted [BH][pieces][m][d]
+  float* rn_lse;               // non-causal: lse when the caller passes none; causal:
+                               // the plain estimator's lse at each quadrant row [BH][n]
   size_t total;
 };
+
+static bool causal_rownorm(const Shape& sh) {
+  return sh.causal && (sh.flags & HA_FLAG_ROWNORM) && sh.samples > 0;
+}
 
 static Plan make_plan(const Shape& sh, void* ws, size_t cap) {
   Plan pl{};
@@ -236,6 +241,16 @@ static Plan make_plan(const Shape& sh, void* ws, size_t cap) {
   const int64_t BH = static_cast<int64_t>(sh.batch) * sh.heads;
   const int64_t BK = static_cast<int64_t>(sh.batch) * sh.kv_heads;
   const size_t esz = sh.dtype == HA_BF16 ? 2 : 4;
+  // causal row-norm buffers: `pieces` problems of at most `seg` keys per head
+  auto take_rn = [&](int64_t pieces, int64_t seg, size_t cdf_ws) {
+    pl.rn_w = cv.take<float>(BK * sh.n);
+    pl.rn_cum = cv.take<int64_t>(BK * pieces * seg);
+    pl.rn_sidx = cv.take<int32_t>(BH * pieces * sh.samples);
+    pl.rn_ws = cv.take<char>(cdf_ws);
+    pl.rn_kc = cv.take<char>(BH * pieces * sh.samples * sh.d * esz);
+    pl.rn_vc = cv.take<char>(BH * pieces * sh.samples * sh.d * esz);
+    pl.rn_lse = cv.take<float>(BH * sh.n);
+  };
   pl.R = cv.take<float>(static_cast<size_t>(sh.r) * sh.d);
   pl.rank_q = cv.take<uint16_t>(BH * sh.n);
   pl.rank_k = cv.take<uint16_t>(BK * sh.n);
@@ -275,6 +290,7 @@ static Plan make_plan(const Shape& sh, void* ws, size_t cap) {
     pl.sidx = cv.take<int32_t>(BH * (sh.samples > 0 ? sh.samples : 1));
     pl.sort_ws_bytes = sort_ws_bytes(BH, half, 1, sh.r) + sort_ws_bytes(BK, half, 1, sh.r);
     pl.sort_ws = cv.take<char>(pl.sort_ws_bytes);
+    if (causal_rownorm(sh)) take_rn(1, half, rownorm_cdf_ws_bytes(BK, half));
   } else {
     if (sh.levels > 0) {
       pl.acc_o = cv.take<float>(BH * sh.n * sh.d);
@@ -292,6 +308,14 @@ static Plan make_plan(const Shape& sh, void* ws, size_t cap) {
       }
       pl.sort_ws_bytes = mx;
       pl.sort_ws = cv.take<char>(mx);
+      if (causal_rownorm(sh)) {
+        size_t cdf = 0;
+        for (int l = 1; l <= sh.levels; ++l) {
+          const size_t b = rownorm_cdf_ws_bytes(BK << (l - 1), sh.n >> l);
+          if (b > cdf) cdf = b;
+        }
+        take_rn(maxp, sh.n / 2 / maxp, cdf);
+      }
     }
   }
   pl.total = align_up(cv.used, 256) + 256;
@@ -391,6 +415,41 @@ static int debug_leaf(const ha_debug_dump& dd, const AttnParams& lp, hipStream_t
   return launch_attention(dp, HA_K_LEAF, s);
 }
 
+// Row-norm variant of one launch of sorted quadrant problems (every piece
+// of one level, or one node; queries at q_first + i * stride, keys at
+// k_first + i * stride): the plain estimator (block keys + uniform samples)
+// stores its lse, ln(D_blk + D_unif), at the query rows; the pieces' draws
+// (node ids node_first + i) and their K / weighted V rows are made; the
+// second pass attends to the block keys plus the draws, rescales to the
+// stored lse and merges into the accumulator like the plain quadrant.
+static int quadrant_rownorm(AttnParams qp, const Shape& sh, const Plan& pl, int node_first, uint64_t seed,
+                            hipStream_t s) {
+  AttnParams p1 = qp;
+  p1.out_mode = kOutFinal;
+  p1.out = nullptr;
+  p1.lse = pl.rn_lse;
+  HA_TRY(launch_attention(p1, HA_K_QUADRANT, s));
+  RnGeom g;
+  g.seg = qp.seg_k ? qp.seg_k : qp.seg;
+  g.pieces = qp.pieces;
+  g.n_head = sh.n;
+  g.k_first = qp.k_first;
+  g.stride = qp.stride;
+  const int64_t BK = static_cast<int64_t>(sh.batch) * sh.kv_heads;
+  HA_TRY(launch_rownorm_cdf(pl.rn_w, qp.perm_k, BK, g, pl.rn_cum, pl.rn_ws, s));
+  HA_TRY(launch_rownorm_samples(pl.rn_cum, g, node_first, seed, sh.batch, sh.heads, sh.kv_heads, sh.samples,
+                                pl.rn_sidx, s));
+  HA_TRY(launch_rownorm_sample_gather(qp.k, qp.v, sh.dtype, qp.perm_k, pl.rn_cum, pl.rn_sidx, g, sh.batch,
+                                      sh.heads, sh.kv_heads, sh.d, sh.samples, pl.rn_kc, pl.rn_vc, s));
+  qp.out_mode = kOutRescaleMerge;
+  qp.sidx = pl.rn_sidx;
+  qp.smp_k = pl.rn_kc;
+  qp.smp_v = pl.rn_vc;
+  qp.lse_ref = pl.rn_lse;
+  qp.log2w = 0.f;
+  return launch_attention(qp, HA_K_QUADRANT, s);
+}
+
 static int forward_causal_nodes(const AttnParams& ap, const Shape& sh, const Plan& pl, uint64_t seed,
                                 hipStream_t s, const ha_debug_dump* dbg) {
   typedef CausalNode Node;
@@ -398,6 +457,8 @@ static int forward_causal_nodes(const AttnParams& ap, const Shape& sh, const Pla
   causal_nodes(sh.n, sh.s, leaves, quads);
   const int64_t BH = static_cast<int64_t>(sh.batch) * sh.heads;
   const int64_t BK = static_cast<int64_t>(sh.batch) * sh.kv_heads;
+  if (causal_rownorm(sh) && !quads.empty())
+    HA_TRY(launch_rownorm_sqnorm(ap.v, sh.dtype, BK * sh.n, sh.d, pl.rn_w, s));
   for (const Node& nd : leaves) {
     AttnParams lp = ap;
     lp.kind = kKindLeaf;
@@ -444,7 +505,8 @@ static int forward_causal_nodes(const AttnParams& ap, const Shape& sh, const Pla
     qp.acc_o = pl.acc_o;
     qp.acc_lse = pl.acc_lse;
     if (dbg) HA_TRY(debug_sorted(*dbg, qp, sh, nd.depth, nd.id - (1 << nd.depth), s));
-    HA_TRY(launch_attention(qp, HA_K_QUADRANT, s));
+    if (causal_rownorm(sh)) HA_TRY(quadrant_rownorm(qp, sh, pl, nd.id, seed, s));
+    else HA_TRY(launch_attention(qp, HA_K_QUADRANT, s));
   }
   return HA_OK;
 }
@@ -525,12 +587,16 @@ static int forward_impl(const void* q, const void* k, const void* v, Shape sh, u
       HA_TRY(launch_attention(ap, HA_K_ATTEND, s));
       if (sh.samples == 0) return HA_OK;        // no draws: the numerator is the block part alone
       HA_TRY(launch_rownorm_sqnorm(v, sh.dtype, BK * sh.n, sh.d, pl.rn_w, s));
-      HA_TRY(launch_rownorm_cdf(pl.rn_w, pl.perm_k, BK, sh.n, pl.rn_cum, pl.rn_ws, s));
-      HA_TRY(launch_rownorm_samples(pl.rn_cum, sh.n, seed, sh.batch, sh.heads, sh.kv_heads, sh.samples,
+      RnGeom g;
+      g.seg = sh.n;
+      g.n_head = sh.n;
+      HA_TRY(launch_rownorm_cdf(pl.rn_w, pl.perm_k, BK, g, pl.rn_cum, pl.rn_ws, s));
+      HA_TRY(launch_rownorm_samples(pl.rn_cum, g, 1, seed, sh.batch, sh.heads, sh.kv_heads, sh.samples,
                                     pl.rn_sidx, s));
-      HA_TRY(launch_rownorm_sample_gather(k, v, sh.dtype, pl.perm_k, pl.rn_cum, pl.rn_sidx, sh.batch, sh.heads,
-                                          sh.kv_heads, sh.n, sh.d, sh.samples, pl.rn_kc, pl.rn_vc, s));
+      HA_TRY(launch_rownorm_sample_gather(k, v, sh.dtype, pl.perm_k, pl.rn_cum, pl.rn_sidx, g, sh.batch, sh.heads,
+                                          sh.kv_heads, sh.d, sh.samples, pl.rn_kc, pl.rn_vc, s));
       ap.out_mode = kOutRescale;
+      ap.lse_ref = lse1;
       ap.sidx = pl.rn_sidx;
       ap.smp_k = pl.rn_kc;
       ap.smp_v = pl.rn_vc;
@@ -582,6 +648,8 @@ static int forward_impl(const void* q, const void* k, const void* v, Shape sh, u
   lp.acc_lse = pl.acc_lse;
   HA_TRY(launch_attention(lp, HA_K_LEAF, s));
   if (dbg) HA_TRY(debug_leaf(*dbg, lp, s));
+  if (causal_rownorm(sh) && sh.levels > 0)
+    HA_TRY(launch_rownorm_sqnorm(v, sh.dtype, BK * sh.n, sh.d, pl.rn_w, s));
 
   for (int l = sh.levels; l >= 1; --l) {
     const int seg = sh.n >> l;
@@ -609,7 +677,8 @@ static int forward_impl(const void* q, const void* k, const void* v, Shape sh, u
     qp.acc_o = pl.acc_o;
     qp.acc_lse = pl.acc_lse;
     if (dbg) HA_TRY(debug_sorted(*dbg, qp, sh, l - 1, 0, s));
-    HA_TRY(launch_attention(qp, HA_K_QUADRANT, s));
+    if (causal_rownorm(sh)) HA_TRY(quadrant_rownorm(qp, sh, pl, pieces, seed, s));
+    else HA_TRY(launch_attention(qp, HA_K_QUADRANT, s));
   }
   return HA_OK;
 }
@@ -1267,8 +1336,11 @@ int hyperattn_rownorm_samples(const float* w, const int32_t* perm_k, int batch, 
     return HA_EWORKSPACE;
   }
   hipStream_t s = static_cast<hipStream_t>(stream);
-  HA_TRY(launch_rownorm_cdf(w, perm_k, problems, n, cum, workspace, s));
-  return launch_rownorm_samples(cum, n, seed, batch, heads, kv_heads, samples, sidx, s);
+  RnGeom g;
+  g.seg = n;
+  g.n_head = n;
+  HA_TRY(launch_rownorm_cdf(w, perm_k, problems, g, cum, workspace, s));
+  return launch_rownorm_samples(cum, g, 1, seed, batch, heads, kv_heads, samples, sidx, s);
 }
 
 int hyperattn_column_sqmass(const void* q, const void* k, const float* lse, int dtype, int batch, int n, int d,

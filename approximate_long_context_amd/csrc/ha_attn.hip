@@ -126,8 +126,9 @@ __global__ __launch_bounds__(64 * NW, (min_waves<T, D, KIND, NW, QPW>())) void a
   const bool mat = !LEAF && p.qs != nullptr;   // materialised sorted copies
   const T* ksb = mat ? static_cast<const T*>(p.ks) + kpiece * p.seg_k * D : nullptr;
   const T* vsb = mat ? static_cast<const T*>(p.vs) + kpiece * p.seg_k * D : nullptr;
-  // kOutRescale: sample rows come from the compact per-head copies, row = sample index
-  constexpr bool RS = OUT == kOutRescale;
+  // kOutRescale(Merge): sample rows come from the compact per-head copies, row = sample index
+  constexpr bool RS = OUT == kOutRescale || OUT == kOutRescaleMerge;
+  constexpr bool MERGE = OUT == kOutMerge || OUT == kOutRescaleMerge;
   const T* kcb = RS ? static_cast<const T*>(p.smp_k) + qpiece * p.m * D : nullptr;
   const T* vcb = RS ? static_cast<const T*>(p.smp_v) + qpiece * p.m * D : nullptr;
   const int32_t* pq = (!LEAF && p.perm_q) ? p.perm_q + qpiece * p.seg : nullptr;
@@ -740,8 +741,9 @@ __global__ __launch_bounds__(64 * NW, (min_waves<T, D, KIND, NW, QPW>())) void a
   // normalised O^T (32 queries x 32 dims, fp32) is staged in the K/V
   // buffers, then lane L merges and stores dims 4 (L & 7) .. +3 of staged
   // query (L >> 3) + 8 k.
-  const bool to_final = OUT == kOutFinal || RS || ((OUT == kOutLeaf || OUT == kOutMerge) && piece == p.final_piece);
-  const bool to_acc = ((OUT == kOutLeaf || OUT == kOutMerge) && piece != p.final_piece) || OUT == kOutAcc;
+  const bool to_final = OUT == kOutFinal || OUT == kOutRescale || ((OUT == kOutLeaf || MERGE) && piece == p.final_piece);
+  const bool to_acc = ((OUT == kOutLeaf || MERGE) && piece != p.final_piece) || OUT == kOutAcc;
+  const bool store_o = OUT != kOutFinal || p.out != nullptr;
   constexpr int SST = 36;                         // staged row stride (floats)
   constexpr int STG = 32 * SST + 64;              // floats per wave: slice, lse, rows
   static_assert(NW * STG * 4 <= 2 * G::BUF, "epilogue staging fits the K/V buffers");
@@ -791,16 +793,20 @@ __global__ __launch_bounds__(64 * NW, (min_waves<T, D, KIND, NW, QPW>())) void a
       w_new[k] = 1.f;
       lse_out[k] = lqk[k];
     }
+    float w_rs[4];
     if constexpr (RS) {
-      // rescale to the normaliser stored at the row: exp(own lse - stored lse)
+      // rescale to the normaliser stored at the row: exp(own lse - stored lse);
+      // the rescaled result carries the stored lse
 #pragma unroll
       for (int k = 0; k < 4; ++k) {
-        const float lref = p.lse[static_cast<int64_t>(bh) * p.n + rowk[k]];
+        const float lref = p.lse_ref[static_cast<int64_t>(bh) * p.n + rowk[k]];
         const bool none = lqk[k] == -INFINITY || lref == -INFINITY;
-        w_new[k] = none ? 0.f : fast_exp2((lqk[k] - lref) * kLog2e);
+        w_rs[k] = none ? 0.f : fast_exp2((lqk[k] - lref) * kLog2e);
+        if constexpr (OUT == kOutRescale) w_new[k] = w_rs[k];
+        else lqk[k] = lref;
       }
     }
-    if constexpr (OUT == kOutMerge) {
+    if constexpr (MERGE) {
       float l1[4];
 #pragma unroll
       for (int k = 0; k < 4; ++k) {
@@ -822,6 +828,7 @@ __global__ __launch_bounds__(64 * NW, (min_waves<T, D, KIND, NW, QPW>())) void a
         const float r = __builtin_amdgcn_rcpf(sum);
         w_old[k] = none ? 0.f : ea * r;
         w_new[k] = none ? 0.f : eb * r;
+        if constexpr (RS) w_new[k] *= w_rs[k];
         lse_out[k] = none ? -INFINITY : ms + __builtin_amdgcn_logf(sum) * kLn2;
       }
     }
@@ -850,11 +857,11 @@ __global__ __launch_bounds__(64 * NW, (min_waves<T, D, KIND, NW, QPW>())) void a
           if (head) p.part_lse[pr] = lqk[k];
         } else {
           const int64_t ridx = static_cast<int64_t>(bh) * p.n + rowk[k];
-          if constexpr (OUT == kOutMerge) {
+          if constexpr (MERGE) {
 #pragma unroll
             for (int i = 0; i < 4; ++i) val[i] = oldv[t][k][i] * w_old[k] + val[i] * w_new[k];
           }
-          if constexpr (RS) {
+          if constexpr (OUT == kOutRescale) {
 #pragma unroll
             for (int i = 0; i < 4; ++i) val[i] *= w_new[k];
           }
@@ -862,7 +869,8 @@ __global__ __launch_bounds__(64 * NW, (min_waves<T, D, KIND, NW, QPW>())) void a
             *reinterpret_cast<floatx4*>(p.acc_o + ridx * D + dc) = val;
             if (head) p.acc_lse[ridx] = lse_out[k];
           } else if (to_final) {
-            if constexpr (BF) {
+            if (!store_o) {
+            } else if constexpr (BF) {
               bf16x4 ob;
 #pragma unroll
               for (int i = 0; i < 4; ++i) ob[i] = static_cast<bf16>(val[i]);
@@ -870,7 +878,7 @@ __global__ __launch_bounds__(64 * NW, (min_waves<T, D, KIND, NW, QPW>())) void a
             } else {
               *reinterpret_cast<floatx4*>(static_cast<float*>(p.out) + ridx * D + dc) = val;
             }
-            if (!RS && head && p.lse) p.lse[ridx] = lse_out[k];
+            if (OUT != kOutRescale && head && p.lse) p.lse[ridx] = lse_out[k];
           }
         }
       }
@@ -958,6 +966,7 @@ static int launch_attn_d(const AttnParams& p, hipStream_t s) {
     if (p.out_mode == kOutPartial) return launch_attn_shape<T, D, kKindSorted, kOutPartial>(p, s);
     if (p.out_mode == kOutMerge) return launch_attn_shape<T, D, kKindSorted, kOutMerge>(p, s);
     if (p.out_mode == kOutRescale) return launch_attn_shape<T, D, kKindSorted, kOutRescale>(p, s);
+    if (p.out_mode == kOutRescaleMerge) return launch_attn_shape<T, D, kKindSorted, kOutRescaleMerge>(p, s);
   }
   set_error("attention: unsupported kind %d / output mode %d", p.kind, p.out_mode);
   return HA_EINVAL;
@@ -976,6 +985,11 @@ int launch_attention(const AttnParams& p_in, int timing_kind, hipStream_t s) {
   if (p.m > kMaxSamples) {
     set_error("attention: samples %d > %d", p.m, kMaxSamples);
     return HA_EUNSUPPORTED;
+  }
+  if ((p.out_mode == kOutRescale || p.out_mode == kOutRescaleMerge) &&
+      (!p.lse_ref || (p.m > 0 && (!p.smp_k || !p.smp_v || !p.sidx)))) {
+    set_error("attention: rescaling needs lse_ref and the sampled rows");
+    return HA_EINVAL;
   }
   const int64_t head_bytes = static_cast<int64_t>(p.n > p.n_k ? p.n : p.n_k) * p.d * (p.dtype == HA_BF16 ? 2 : 4);
   if (head_bytes >= (int64_t(1) << 32)) {

@@ -53,7 +53,8 @@ enum AttnOut {
   kOutLeaf = 2,       // piece 0 -> out/lse, other pieces -> acc (no read)
   kOutMerge = 3,      // merge with acc at the row; piece 0 -> out/lse, else -> acc
   kOutAcc = 4,        // every piece -> acc at the row (no read)
-  kOutRescale = 5     // out at the original row, scaled by exp(own lse - lse read there); lse kept
+  kOutRescale = 5,    // out at the original row, scaled by exp(own lse - lse_ref there); lse kept
+  kOutRescaleMerge = 6  // as kOutRescale, the result (lse = lse_ref) then merged like kOutMerge
 };
 
 constexpr int kMaxSamples = 4096;   // sample list staged in LDS
@@ -91,14 +92,17 @@ struct AttnParams {
   int use_samples = 1;
   const int32_t* sidx = nullptr;     // [BH][pieces][m] sorted key positions
   int m = 0;
-  // kOutRescale: the sampled keys' K and V rows ([BH][m][d] dtype, sample
-  // order), read in place of the rows sidx names
+  // kOutRescale / kOutRescaleMerge: the sampled keys' K and V rows
+  // ([BH][pieces][m][d] dtype, sample order), read in place of the rows
+  // sidx names, and the normaliser the result is rescaled to ([BH][n],
+  // natural log, at the original row)
   const void* smp_k = nullptr;
   const void* smp_v = nullptr;
+  const float* lse_ref = nullptr;
   float log2w = 0.f;                 // log2(seg / m)
   int out_mode = kOutFinal;
   int final_piece = 0;               // kOutLeaf / kOutMerge: the piece whose rows are final (-1: none)
-  void* out = nullptr;               // [BH][n][d] dtype
+  void* out = nullptr;               // [BH][n][d] dtype (kOutFinal: null stores the lse alone)
   float* lse = nullptr;              // [BH][n] (may be null for kOutFinal)
   float* acc_o = nullptr;            // [BH][n][d]
   float* acc_lse = nullptr;          // [BH][n]
@@ -165,16 +169,30 @@ inline int bwd_query_chunk(int seg) {
   return per64 > 2048 ? per64 : 2048;
 }
 
-// Row-norm variant (ha_rownorm.hip).
+// Row-norm variant (ha_rownorm.hip).  Problems are (KV head, piece): piece
+// i of a head has `seg` sorted key positions (perm_k [heads][pieces][seg],
+// rows within the head of n_head rows) over the rows k_first + i * stride +
+// [0, seg) of the head.  One whole head per problem: pieces 1, seg = n_head,
+// k_first = stride = 0.
+struct RnGeom {
+  int seg = 0;
+  int pieces = 1;
+  int n_head = 0;
+  int k_first = 0;
+  int stride = 0;
+};
 int launch_rownorm_sqnorm(const void* v, int dtype, int64_t rows, int d, float* w, hipStream_t s);
 size_t rownorm_cdf_ws_bytes(int64_t problems, int n);
-int launch_rownorm_cdf(const float* w, const int32_t* perm_k, int64_t problems, int n, int64_t* cum, void* ws,
-                       hipStream_t s);
-int launch_rownorm_samples(const int64_t* cum, int n, uint64_t seed, int batch, int heads, int kv_heads, int m,
-                           int32_t* out, hipStream_t s);
+// integer CDF per problem: cum [kv_problems][pieces][seg]
+int launch_rownorm_cdf(const float* w, const int32_t* perm_k, int64_t kv_problems, const RnGeom& g, int64_t* cum,
+                       void* ws, hipStream_t s);
+// draws [batch][heads][pieces][m]; piece i uses node id node_first + i
+int launch_rownorm_samples(const int64_t* cum, const RnGeom& g, int node_first, uint64_t seed, int batch,
+                           int heads, int kv_heads, int m, int32_t* out, hipStream_t s);
+// drawn K rows and weighted V rows [batch][heads][pieces][m][d]
 int launch_rownorm_sample_gather(const void* k, const void* v, int dtype, const int32_t* perm_k,
-                                 const int64_t* cum, const int32_t* sidx, int batch, int heads, int kv_heads, int n,
-                                 int d, int m, void* kc, void* vc, hipStream_t s);
+                                 const int64_t* cum, const int32_t* sidx, const RnGeom& g, int batch, int heads,
+                                 int kv_heads, int d, int m, void* kc, void* vc, hipStream_t s);
 
 // Diagnostics (ha_diag.hip).
 int launch_colmass(const void* q, const void* k, const float* lse, int batch, int n, int d, int heads,

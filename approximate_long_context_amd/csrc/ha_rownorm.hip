@@ -84,12 +84,14 @@ __global__ __launch_bounds__(256) void rownorm_sqnorm_kernel(const T* __restrict
 constexpr int kRnThreads = 256;
 constexpr int kRnChunk = 2048;                      // 8 positions per thread
 
-__global__ __launch_bounds__(kRnThreads) void rownorm_max_kernel(const float* __restrict__ w, int n, int nchunk,
+__global__ __launch_bounds__(kRnThreads) void rownorm_max_kernel(const float* __restrict__ w, RnGeom g, int nchunk,
                                                                   float* __restrict__ cmax) {
   __shared__ float red[kRnThreads / 64];
   const int64_t prob = blockIdx.x / nchunk;
   const int chunk = blockIdx.x % nchunk;
-  const float* wp = w + prob * n;
+  const int n = g.seg;
+  const int64_t bkv = prob / g.pieces;
+  const float* wp = w + bkv * g.n_head + g.k_first + (prob - bkv * g.pieces) * g.stride;
   float mx = 0.f;
   for (int t = chunk * kRnChunk + threadIdx.x; t < min((chunk + 1) * kRnChunk, n); t += kRnThreads)
     mx = fmaxf(mx, wp[t]);
@@ -101,7 +103,7 @@ __global__ __launch_bounds__(kRnThreads) void rownorm_max_kernel(const float* __
 }
 
 __global__ __launch_bounds__(kRnThreads) void rownorm_chunk_kernel(const float* __restrict__ w,
-                                                                    const int32_t* __restrict__ perm_k, int n,
+                                                                    const int32_t* __restrict__ perm_k, RnGeom g,
                                                                     int nchunk, const float* __restrict__ cmax,
                                                                     int64_t* __restrict__ cum,
                                                                     int64_t* __restrict__ chunk_sum) {
@@ -122,7 +124,8 @@ __global__ __launch_bounds__(kRnThreads) void rownorm_chunk_kernel(const float* 
   }
   __syncthreads();
   const int sh = sh_s;
-  const float* wp = w + prob * n;
+  const int n = g.seg;
+  const float* wp = w + (prob / g.pieces) * g.n_head;   // perm_k holds rows of the head
   const int32_t* pk = perm_k + prob * n;
   int64_t* cp = cum + prob * n;
   constexpr int PER = kRnChunk / kRnThreads;
@@ -168,19 +171,23 @@ __global__ __launch_bounds__(kRnThreads) void rownorm_offset_kernel(int n, int n
 
 // ---- draws ---------------------------------------------------------------------
 
-__global__ void rownorm_sample_kernel(const int64_t* __restrict__ cum, int n, uint64_t seed, int heads,
-                                      int kv_heads, int m, int64_t total_ctr, int32_t* __restrict__ out) {
+__global__ void rownorm_sample_kernel(const int64_t* __restrict__ cum, int n, int pieces, int node_first,
+                                      uint64_t seed, int heads, int kv_heads, int m, int64_t total_ctr,
+                                      int32_t* __restrict__ out) {
   const int nctr = (m + 3) / 4;
   const int G = heads / kv_heads;
   for (int64_t t = static_cast<int64_t>(blockIdx.x) * blockDim.x + threadIdx.x; t < total_ctr;
        t += static_cast<int64_t>(gridDim.x) * blockDim.x) {
-    const int64_t bh = t / nctr;
+    const int64_t bhp = t / nctr;                   // (query head) * pieces + piece
     const int j = static_cast<int>(t % nctr);
+    const int64_t bh = bhp / pieces;
+    const int piece = static_cast<int>(bhp - bh * pieces);
     const int h = static_cast<int>(bh % heads);
     const int b = static_cast<int>(bh / heads);
-    const int64_t* cp = cum + (static_cast<int64_t>(b) * kv_heads + h / G) * n;
+    const int64_t* cp = cum + ((static_cast<int64_t>(b) * kv_heads + h / G) * pieces + piece) * n;
     const uint64_t T = static_cast<uint64_t>(cp[n - 1]);
-    U32x4 c = {static_cast<uint32_t>(j), 1u, static_cast<uint32_t>(h), static_cast<uint32_t>(2 * b + 2)};
+    U32x4 c = {static_cast<uint32_t>(j), static_cast<uint32_t>(node_first + piece), static_cast<uint32_t>(h),
+               static_cast<uint32_t>(2 * b + 2)};
     U32x4 r = philox4x32_10(c, seed);
 #pragma unroll
     for (int wi = 0; wi < 4; ++wi) {
@@ -195,7 +202,7 @@ __global__ void rownorm_sample_kernel(const int64_t* __restrict__ cum, int n, ui
         if (static_cast<uint64_t>(cp[mid]) > rr) hi = mid;
         else lo = mid + 1;
       }
-      out[bh * m + i] = T > 0 ? lo : 0;
+      out[bhp * m + i] = T > 0 ? lo : 0;
     }
   }
 }
@@ -207,21 +214,25 @@ __global__ void rownorm_sample_kernel(const int64_t* __restrict__ cum, int n, ui
 template <typename T>
 __global__ void rownorm_sample_gather_kernel(const T* __restrict__ k, const T* __restrict__ v,
                                              const int32_t* __restrict__ perm_k, const int64_t* __restrict__ cum,
-                                             const int32_t* __restrict__ sidx, int n, int d, int m, int heads,
+                                             const int32_t* __restrict__ sidx, RnGeom g, int d, int m, int heads,
                                              int kv_heads, int64_t total, T* __restrict__ kc, T* __restrict__ vc) {
   const int G = heads / kv_heads;
+  const int n = g.seg;
   for (int64_t e = static_cast<int64_t>(blockIdx.x) * blockDim.x + threadIdx.x; e < total;
        e += static_cast<int64_t>(gridDim.x) * blockDim.x) {
-    const int64_t sj = e / d;                       // query head * m + sample
+    const int64_t sj = e / d;                       // ((query head) * pieces + piece) * m + sample
     const int c = static_cast<int>(e % d);
-    const int64_t bh = sj / m;
+    const int64_t bhp = sj / m;
+    const int64_t bh = bhp / g.pieces;
+    const int piece = static_cast<int>(bhp - bh * g.pieces);
     const int h = static_cast<int>(bh % heads);
-    const int64_t prob = (bh / heads) * kv_heads + h / G;
+    const int64_t bkv = (bh / heads) * kv_heads + h / G;
+    const int64_t prob = bkv * g.pieces + piece;
     const int t = sidx[sj];                         // sorted key position
     const int64_t* cp = cum + prob * n;
     const int64_t nt = cp[t] - (t > 0 ? cp[t - 1] : 0);
     const double scale = nt > 0 ? static_cast<double>(cp[n - 1]) / (static_cast<double>(m) * nt) : 0.0;
-    const int64_t src = (prob * n + perm_k[prob * n + t]) * d + c;
+    const int64_t src = (bkv * g.n_head + perm_k[prob * n + t]) * d + c;
     kc[e] = k[src];
     vc[e] = static_cast<T>(static_cast<float>(v[src]) * static_cast<float>(scale));
   }
@@ -254,42 +265,43 @@ size_t rownorm_cdf_ws_bytes(int64_t problems, int n) {
   return static_cast<size_t>(problems) * nchunk * (sizeof(int64_t) + sizeof(float)) + 64;
 }
 
-int launch_rownorm_cdf(const float* w, const int32_t* perm_k, int64_t problems, int n, int64_t* cum, void* ws,
-                       hipStream_t s) {
-  if (problems == 0 || n == 0) return HA_OK;
-  const int nchunk = (n + kRnChunk - 1) / kRnChunk;
+int launch_rownorm_cdf(const float* w, const int32_t* perm_k, int64_t kv_problems, const RnGeom& g, int64_t* cum,
+                       void* ws, hipStream_t s) {
+  const int64_t problems = kv_problems * g.pieces;
+  if (problems == 0 || g.seg == 0) return HA_OK;
+  const int nchunk = (g.seg + kRnChunk - 1) / kRnChunk;
   int64_t* chunk_sum = static_cast<int64_t*>(ws);
   float* cmax = reinterpret_cast<float*>(chunk_sum + problems * nchunk);
   const unsigned grid = static_cast<unsigned>(problems * nchunk);
-  hipLaunchKernelGGL(rownorm_max_kernel, dim3(grid), dim3(kRnThreads), 0, s, w, n, nchunk, cmax);
-  hipLaunchKernelGGL(rownorm_chunk_kernel, dim3(grid), dim3(kRnThreads), 0, s, w, perm_k, n, nchunk, cmax, cum,
+  hipLaunchKernelGGL(rownorm_max_kernel, dim3(grid), dim3(kRnThreads), 0, s, w, g, nchunk, cmax);
+  hipLaunchKernelGGL(rownorm_chunk_kernel, dim3(grid), dim3(kRnThreads), 0, s, w, perm_k, g, nchunk, cmax, cum,
                      chunk_sum);
-  hipLaunchKernelGGL(rownorm_offset_kernel, dim3(grid), dim3(kRnThreads), 0, s, n, nchunk, chunk_sum, cum);
+  hipLaunchKernelGGL(rownorm_offset_kernel, dim3(grid), dim3(kRnThreads), 0, s, g.seg, nchunk, chunk_sum, cum);
   return after_launch("row-norm cdf", s);
 }
 
-int launch_rownorm_samples(const int64_t* cum, int n, uint64_t seed, int batch, int heads, int kv_heads, int m,
-                           int32_t* out, hipStream_t s) {
-  const int64_t total = static_cast<int64_t>(batch) * heads * ((m + 3) / 4);
-  if (total == 0 || n == 0) return HA_OK;
-  hipLaunchKernelGGL(rownorm_sample_kernel, dim3(grid_for(total, 256)), dim3(256), 0, s, cum, n, seed, heads,
-                     kv_heads, m, total, out);
+int launch_rownorm_samples(const int64_t* cum, const RnGeom& g, int node_first, uint64_t seed, int batch,
+                           int heads, int kv_heads, int m, int32_t* out, hipStream_t s) {
+  const int64_t total = static_cast<int64_t>(batch) * heads * g.pieces * ((m + 3) / 4);
+  if (total == 0 || g.seg == 0) return HA_OK;
+  hipLaunchKernelGGL(rownorm_sample_kernel, dim3(grid_for(total, 256)), dim3(256), 0, s, cum, g.seg, g.pieces,
+                     node_first, seed, heads, kv_heads, m, total, out);
   return after_launch("row-norm samples", s);
 }
 
 int launch_rownorm_sample_gather(const void* k, const void* v, int dtype, const int32_t* perm_k,
-                                 const int64_t* cum, const int32_t* sidx, int batch, int heads, int kv_heads, int n,
-                                 int d, int m, void* kc, void* vc, hipStream_t s) {
-  const int64_t total = static_cast<int64_t>(batch) * heads * m * d;
-  if (total == 0 || n == 0) return HA_OK;
-  const unsigned g = grid_for(total, 256);
+                                 const int64_t* cum, const int32_t* sidx, const RnGeom& g, int batch, int heads,
+                                 int kv_heads, int d, int m, void* kc, void* vc, hipStream_t s) {
+  const int64_t total = static_cast<int64_t>(batch) * heads * g.pieces * m * d;
+  if (total == 0 || g.seg == 0) return HA_OK;
+  const unsigned grid = grid_for(total, 256);
   if (dtype == HA_BF16)
-    hipLaunchKernelGGL(rownorm_sample_gather_kernel<bf16>, dim3(g), dim3(256), 0, s, static_cast<const bf16*>(k),
-                       static_cast<const bf16*>(v), perm_k, cum, sidx, n, d, m, heads, kv_heads, total,
+    hipLaunchKernelGGL(rownorm_sample_gather_kernel<bf16>, dim3(grid), dim3(256), 0, s, static_cast<const bf16*>(k),
+                       static_cast<const bf16*>(v), perm_k, cum, sidx, g, d, m, heads, kv_heads, total,
                        static_cast<bf16*>(kc), static_cast<bf16*>(vc));
   else
-    hipLaunchKernelGGL(rownorm_sample_gather_kernel<float>, dim3(g), dim3(256), 0, s, static_cast<const float*>(k),
-                       static_cast<const float*>(v), perm_k, cum, sidx, n, d, m, heads, kv_heads, total,
+    hipLaunchKernelGGL(rownorm_sample_gather_kernel<float>, dim3(grid), dim3(256), 0, s, static_cast<const float*>(k),
+                       static_cast<const float*>(v), perm_k, cum, sidx, g, d, m, heads, kv_heads, total,
                        static_cast<float*>(kc), static_cast<float*>(vc));
   return after_launch("row-norm sampled rows", s);
 }

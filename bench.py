@@ -309,7 +309,8 @@ def main():
     if not args.no_extras:
         result["approx_rel_error"] = approx_error(ha, torch, w_nc, w_c, q, k, v, out)
         result["configs"] = other_configs(ha, torch, dev, stream)
-        result["rownorm"] = rownorm_bench(ha, torch, w_nc, q, k, v, out, stream)
+        result["rownorm"] = {name: rownorm_bench(ha, torch, w, q, k, v, out, stream)
+                             for name, w in (("noncausal", w_nc), ("causal", w_c))}
         result["diagnostics"] = diagnostics_bench(ha, torch, dev, stream)
         result["rect"] = rect_bench(ha, torch, dev, stream)
         del ws
@@ -410,10 +411,10 @@ def diagnostics_bench(ha, torch, dev, stream):
 
 
 def rownorm_bench(ha, torch, w, q, k, v, out, stream, reps=3):
-    """The row-norm-sampling variant of the product (HA_FLAG_ROWNORM) on the
-    non-causal headline pass: ms, effective TFLOP/s counted like the
-    forward's (4 d (b + m) per row) and its error against exact attention
-    next to the uniform method's (not part of `value`)."""
+    """The row-norm-sampling variant of the product (HA_FLAG_ROWNORM) on one
+    headline pass (non-causal, or causal with every quadrant's own draws):
+    ms, effective TFLOP/s counted like the forward's and its error against
+    exact attention (not part of `value`)."""
     args = w.method_args()
     ws = torch.empty(ha.workspace_bytes(w.batch, w.n, w.d, w.heads, w.kv_heads, w.block, w.samples, w.proj_bits,
                                         w.causal, w.min_seq_len, w.dtype, flags=ha.HA_FLAG_ROWNORM),
@@ -432,9 +433,10 @@ def rownorm_bench(ha, torch, w, q, k, v, out, stream, reps=3):
     e1.record(stream)
     torch.cuda.synchronize()
     ms = e0.elapsed_time(e1) / reps
-    f, _ = alg_flops(w, False)
+    f, _ = alg_flops(w, w.causal)
     ex = torch.empty_like(out)
-    ha.forward(q, k, v, out=ex, **w.with_(block=w.n).method_args())
+    exact = w.with_(min_seq_len=w.n) if w.causal else w.with_(block=w.n)
+    ha.forward(q, k, v, out=ex, **exact.method_args())
     run()
     a, b = out.float(), ex.float()
     err = float(torch.linalg.vector_norm(a - b) / torch.linalg.vector_norm(b))

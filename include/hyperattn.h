@@ -83,8 +83,13 @@ enum {
    * norm of the value row, each kept draw weighted 1 / (samples p_t):
    *   out = (N_block + N_rownorm) / (D_block + D_uniform),
    *   lse = ln(D_block + D_uniform).
-   * The draws are defined exactly (hyperattn_rownorm_samples).  Non-causal
-   * only; not combined with the other flags. */
+   * The draws are defined exactly (hyperattn_rownorm_samples).  Causal:
+   * the leaves stay exact and every quadrant of the recursion (node id
+   * `node`, keys [lo, mid)) is such a problem over its own keys -- its
+   * largest weight, its CDF and Philox counters (i / 4, node, head,
+   * 2 batch + 2) -- merged with the rest of the row by log-sum-exp, so a
+   * row's normaliser is the plain method's.  samples = 0 gives the plain
+   * method.  Not combined with the other flags. */
   HA_FLAG_ROWNORM = 4
 };
 

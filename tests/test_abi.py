@@ -128,6 +128,27 @@ def test_rownorm_workspace_holds_no_partials():
     assert rn < plain + H * n * d * 2          # less than one bf16 copy of the queries
 
 
+def test_causal_rownorm_workspace():
+    """Causal row-norm: per-key weights and CDF, an lse per query row and
+    the drawn rows of the widest level (16 pieces at n = 131072 with
+    min_seq_len 4096); the other flags stay non-causal only; no samples,
+    no extra buffers."""
+    B, n, d, H, Hkv, b, m, r, s = 1, 131072, 64, 32, 32, 256, 256, 7, 4096
+    plain = ha.workspace_bytes(B, n, d, H, Hkv, b, m, r, causal=True, min_seq_len=s)
+    rn = ha.workspace_bytes(B, n, d, H, Hkv, b, m, r, causal=True, min_seq_len=s, flags=ha.HA_FLAG_ROWNORM)
+    pieces = 16
+    extra = Hkv * n * 4 + Hkv * n // 2 * 8 + H * n * 4 + pieces * H * m * (4 + 2 * d * 2) + (1 << 20)
+    assert plain < rn <= plain + extra
+    for odd_n in (131071, 1000):
+        assert ha.workspace_bytes(B, odd_n, d, H, Hkv, b, m, r, causal=True, min_seq_len=100,
+                                  flags=ha.HA_FLAG_ROWNORM) > 0
+    assert ha.workspace_bytes(B, n, d, H, Hkv, b, 0, r, causal=True, min_seq_len=s,
+                              flags=ha.HA_FLAG_ROWNORM) == ha.workspace_bytes(B, n, d, H, Hkv, b, 0, r, causal=True,
+                                                                              min_seq_len=s)
+    for f in (ha.HA_FLAG_MATERIALIZE, ha.HA_FLAG_UNFUSED, ha.HA_FLAG_ROWNORM | ha.HA_FLAG_UNFUSED):
+        assert ha.workspace_bytes(B, n, d, H, Hkv, b, m, r, causal=True, min_seq_len=s, flags=f) == 0
+
+
 def test_forward_noalloc_argument_errors():
     """Errors of the allocation-free forward come before the scratch
     array's address is looked up and before any launch."""

@@ -1,5 +1,6 @@
 """GPU parity of the row-norm-sampling variant (HA_FLAG_ROWNORM) against
-``oracle.rownorm``.
+``oracle.rownorm``, non-causal and causal (every quadrant of the
+recursion with its node's draws; even splits and odd, rectangular ones).
 
 * squared value-row norms: bit-exact (bf16 and fp32, d 64 and 128);
 * integer CDF and draws: bit-exact (the draws decide integers, both sides
@@ -105,13 +106,72 @@ def test_rownorm_forward_matches_oracle(B, H, Hkv, n, d, block, m, r, seed, dtyp
         assert torch.allclose(lse, l0, atol=TOL[dtype]["lse"], rtol=0)
 
 
-def test_rownorm_rejects_causal_and_other_flags():
+def test_rownorm_rejects_other_flags():
     q, k, v = (t.to(DEV) for t in _inputs(1, 1, 1, 256, 64, 30))
     with pytest.raises(ha.HyperAttnError):
-        ha.forward(q, k, v, block=64, samples=16, proj_bits=5, causal=True, min_seq_len=64,
-                   flags=ha.HA_FLAG_ROWNORM)
-    with pytest.raises(ha.HyperAttnError):
         ha.forward(q, k, v, block=64, samples=16, proj_bits=5, flags=ha.HA_FLAG_ROWNORM | ha.HA_FLAG_UNFUSED)
+    with pytest.raises(ha.HyperAttnError):
+        ha.forward(q, k, v, block=64, samples=16, proj_bits=5, causal=True, min_seq_len=64,
+                   flags=ha.HA_FLAG_ROWNORM | ha.HA_FLAG_MATERIALIZE)
+
+
+# ---- causal: every quadrant with its own node's draws ----------------------------------
+
+CAUSAL_CASES = [
+    # B, H, Hkv, n, d, block, samples, r, min_seq_len, seed, dtype
+    (1, 2, 1, 2048, 64, 128, 64, 7, 256, 21, torch.bfloat16),     # even splits: one launch per level
+    (1, 2, 2, 1000, 128, 64, 50, 6, 100, 22, torch.bfloat16),     # odd spans: node by node, rectangular
+    (1, 1, 1, 1024, 64, 64, 64, 7, 128, 23, torch.float32),       # fp32
+    (2, 4, 2, 1536, 128, 96, 200, 7, 192, 24, torch.float32),     # fp32, d = 128, batch 2, grouped heads
+    (1, 2, 1, 4096, 64, 256, 256, 7, 512, 25, torch.bfloat16),    # several pieces per level
+    (1, 2, 1, 777, 64, 32, 40, 5, 64, 26, torch.bfloat16),        # odd spans, small blocks, ragged tails
+    (1, 1, 1, 512, 64, 512, 30, 5, 64, 27, torch.bfloat16),       # block >= every quadrant: exact
+]
+
+
+def _check_against(got, ro, lse, rl, dtype, what):
+    got = got.astype(np.float64)
+    tol = TOL[dtype]
+    scale = max(1.0, float(np.max(np.abs(ro))))
+    err = float(np.max(np.abs(got - ro)))
+    rel = float(np.linalg.norm(got - ro) / np.linalg.norm(ro))
+    assert np.all(np.isfinite(got)), what
+    assert err <= tol["max_abs"] * scale, f"{what}: max-abs {err:.3e} > {tol['max_abs']} x {scale:.2f}"
+    assert rel <= tol["rel_fro"], f"{what}: rel-Frobenius {rel:.3e}"
+    compare_lse(lse, rl, dtype, f"{what} lse")
+
+
+@pytest.mark.parametrize("B,H,Hkv,n,d,block,m,r,s,seed,dtype", CAUSAL_CASES)
+def test_rownorm_causal_matches_oracle(B, H, Hkv, n, d, block, m, r, s, seed, dtype):
+    print(f"[rownorm causal] n {n} d {d} block {block} samples {m} min_seq_len {s} {dtype}", flush=True)
+    q, k, v = _inputs(B, H, Hkv, n, d, 40 + seed, dtype)
+    args = dict(block=block, samples=m, proj_bits=r, seed=seed, causal=True, min_seq_len=s)
+    out, lse = ha.forward(q.to(DEV), k.to(DEV), v.to(DEV), flags=ha.HA_FLAG_ROWNORM, **args)
+    torch.cuda.synchronize()
+    ro, rl = rn.forward(np32(q), np32(k), np32(v), HAConfig(**args))
+    _check_against(np32(out), ro, lse.cpu().numpy(), rl, dtype, "causal row-norm")
+    # the normaliser is the plain method's
+    _, l0 = ha.forward(q.to(DEV), k.to(DEV), v.to(DEV), **args)
+    assert torch.allclose(lse, l0, atol=TOL[dtype]["lse"], rtol=0)
+
+
+def test_rownorm_causal_without_samples_is_the_plain_method():
+    q, k, v = (t.to(DEV) for t in _inputs(1, 2, 1, 1000, 64, 32))
+    args = dict(block=64, samples=0, proj_bits=6, seed=5, causal=True, min_seq_len=100)
+    o1, l1 = ha.forward(q, k, v, flags=ha.HA_FLAG_ROWNORM, **args)
+    o0, l0 = ha.forward(q, k, v, **args)
+    torch.cuda.synchronize()
+    assert torch.equal(o1, o0) and torch.equal(l1, l0)
+
+
+def test_rownorm_causal_repeatable():
+    """Two calls give identical bits (no atomics; the draws are fixed by the seed)."""
+    q, k, v = (t.to(DEV) for t in _inputs(1, 2, 1, 2048, 64, 33))
+    args = dict(block=128, samples=64, proj_bits=7, seed=8, causal=True, min_seq_len=256)
+    o1, l1 = ha.forward(q, k, v, flags=ha.HA_FLAG_ROWNORM, **args)
+    o2, l2 = ha.forward(q, k, v, flags=ha.HA_FLAG_ROWNORM, **args)
+    torch.cuda.synchronize()
+    assert torch.equal(o1, o2) and torch.equal(l1, l2)
 
 
 def test_rownorm_without_lse_output():
@@ -161,3 +221,26 @@ def test_rownorm_full_workload_sampled_rows():
         assert err <= tol["max_abs"] * scale, f"head {h}: max-abs {err:.3e} > {tol['max_abs']} x {scale:.2f}"
         assert rel <= tol["rel_fro"], f"head {h}: rel-Frobenius {rel:.3e}"
         compare_lse(np32(lse[b, h])[rows], rl[0], w.dtype, f"head {h} lse")
+
+
+@pytest.mark.slow
+def test_rownorm_causal_full_workload_sampled_rows():
+    """The causal long131k forward (32 heads, n = 131072, d = 64, block 256,
+    256 samples, min_seq_len 4096: five levels of quadrants) with the
+    variant: rows sampled from two heads against the oracle one row at a
+    time."""
+    w = WORKLOADS["long131k_causal"]
+    assert w.causal
+    print("[rownorm long131k_causal] generating inputs", flush=True)
+    q, k, v = make_inputs(w, DEV)
+    out, lse = ha.forward(q, k, v, flags=ha.HA_FLAG_ROWNORM, **w.method_args())
+    torch.cuda.synchronize()
+    g = np.random.default_rng(137)
+    rows = np.array(sorted(set(g.choice(w.n, size=40, replace=False).tolist()) | {0, 4095, 4096, w.n - 1}))
+    cfg = HAConfig(block=w.block, samples=w.samples, proj_bits=w.proj_bits, causal=True,
+                   min_seq_len=w.min_seq_len, seed=w.seed)
+    qc, kc, vc = np32(q), np32(k), np32(v)
+    for b, h in [(0, 0), (0, w.heads - 1)]:
+        print(f"[rownorm long131k_causal] oracle rows of head {h}", flush=True)
+        ro, rl = rn.forward_rows(qc, kc, vc, cfg, heads=[(b, h)], rows=rows)
+        _check_against(np32(out[b, h])[rows], ro[0], np32(lse[b, h])[rows], rl[0], w.dtype, f"head {h}")
