@@ -920,16 +920,13 @@ static int launch_attn_t(const AttnParams& p, hipStream_t s) {
 }
 
 // Workgroup shape: waves x queries per wave.  HYPERATTN_SHAPE_LEAF /
-// HYPERATTN_SHAPE_SORTED ("4x32", "8x32", "4x64", "2x64") override the
-// default for tuning.
+// HYPERATTN_SHAPE_SORTED ("4x32", "8x32") override the default for tuning.
 static int shape_override(int kind) {
   auto parse = [](const char* name) {
     const char* s = std::getenv(name);
     if (!s) return 0;
     if (!std::strcmp(s, "4x32")) return 1;
     if (!std::strcmp(s, "8x32")) return 2;
-    if (!std::strcmp(s, "4x64")) return 3;
-    if (!std::strcmp(s, "2x64")) return 4;
     return 0;
   };
   // read once (thread-safe static initialisation)
@@ -947,10 +944,6 @@ static int launch_attn_shape(const AttnParams& p, hipStream_t s) {
   if (shape == 0) {
     if (KIND == kKindLeaf) shape = (sizeof(T) == 2 && D == 64 && p.seg >= 256) ? 2 : 1;
     else shape = (p.seg >= 256 && p.b_eff >= 256) ? 2 : 1;
-  }
-  if constexpr (sizeof(T) == 2) {
-    if (shape == 3) return launch_attn_t<T, D, KIND, OUT, 4, 64>(p, s);
-    if (shape == 4) return launch_attn_t<T, D, KIND, OUT, 2, 64>(p, s);
   }
   if (shape == 2) return launch_attn_t<T, D, KIND, OUT, 8, 32>(p, s);
   return launch_attn_t<T, D, KIND, OUT, 4, 32>(p, s);

@@ -123,12 +123,16 @@ __device__ __forceinline__ uint32_t exact_sign_bit(const T* row, const float* rp
 // A workgroup takes 64 consecutive rows per step, one row per lane, with
 // one wave per 128 bytes of row (NW = d * elem / 128 waves: 1 for bf16 at
 // d = 64).  The rows are read with coalesced 16-byte loads into LDS (padded
-// rows, conflict-free); the next step's chunks are loaded into registers
-// while this step computes.  Wave w converts its 128-byte column slice of
-// its lane's row to fp32 and, one projection at a time (the projection
-// values are uniform and come from scalar loads), takes the partial dot
-// product with fused multiply-adds; wave 0 adds the partials of the other
-// waves (through LDS), tests the bound and sets the bit.
+// rows, conflict-free; a full step's chunk c of thread t is the 16 bytes at
+// step base + 16 (c NT + t), so one uniform base serves every load); the
+// next step's chunks are loaded into registers while this step computes.
+// Wave w walks its 128-byte column slice of its lane's row one 16-byte
+// chunk at a time (a rolled loop: few values live at once, so four waves
+// fit per SIMD): the chunk's values in fp32, their largest magnitude, and
+// for every projection fused multiply-adds into four chains (projection
+// values are uniform and come from scalar loads).  Wave 0 adds the partials
+// of the other waves (through LDS), tests the bounds, and only for the rare
+// rows some bound leaves open runs the exact decision, in one rolled loop.
 constexpr int kHashRows = 64;
 
 template <typename T, int D, int R>
@@ -139,11 +143,12 @@ __global__ __launch_bounds__(D * sizeof(T) / 2) void hash_kernel(const T* __rest
   constexpr int NW = ROWB / 128;                    // waves per workgroup
   constexpr int NT = 64 * NW;
   constexpr int DW = D / NW;                        // elements per wave
+  constexpr int EPC = 16 / static_cast<int>(sizeof(T));   // elements per 16-byte chunk
   constexpr int CH = ROWB / 16;                     // 16-byte chunks per row
   constexpr int CPT = kHashRows * CH / NT;          // chunks per thread and step (8)
   constexpr int STR = ROWB + 16;                    // LDS row stride (bytes)
   constexpr int TR = kHashRows;
-  static_assert(NW >= 1 && DW % 8 == 0 && CPT * NT == TR * CH, "hash split");
+  static_assert(NW >= 1 && DW % EPC == 0 && CPT * NT == TR * CH && NT % CH == 0, "hash split");
   // |t - <x, R_p>| <= gamma_{D+4} max|x| sum|R_p| + D 2^-150 (see above);
   // the factor 1.0001 covers the rounding of the bound itself, and the
   // absolute term D 2^-148 also covers a bound that falls in the subnormals
@@ -171,96 +176,102 @@ __global__ __launch_bounds__(D * sizeof(T) / 2) void hash_kernel(const T* __rest
     }
   }
 
-  // coalesced staging: chunk q of a step = row q / CH, chunk q % CH
+  // coalesced staging: chunk q = c NT + tid of a step is chunk q % CH of
+  // row q / CH (NT is a multiple of CH, so the LDS slot of chunk c is
+  // this thread's first slot + c (NT / CH) rows)
   const int64_t rstep = static_cast<int64_t>(gridDim.x) * TR;
   uint4v pre[CPT];
-  // rows past the end repeat the last row (their ranks are not written)
   auto load_step = [&](int64_t r0) {
+    if (r0 + TR <= rows) {
+      const char* base = xb + r0 * ROWB + 16 * tid;
 #pragma unroll
-    for (int c = 0; c < CPT; ++c) {
-      const int q = c * NT + tid;
-      const int64_t rr = min(r0 + q / CH, rows - 1);
-      pre[c] = *reinterpret_cast<const uint4v*>(xb + rr * ROWB + 16 * (q % CH));
+      for (int c = 0; c < CPT; ++c) pre[c] = *reinterpret_cast<const uint4v*>(base + 16 * NT * c);
+    } else {                                        // the last, partial step: rows past the end repeat the last row
+#pragma unroll
+      for (int c = 0; c < CPT; ++c) {
+        const int q = c * NT + tid;
+        const int64_t rr = min(r0 + q / CH, rows - 1);
+        pre[c] = *reinterpret_cast<const uint4v*>(xb + rr * ROWB + 16 * (q % CH));
+      }
     }
   };
+  char* wslot = stage + (tid / CH) * STR + 16 * (tid % CH);
   if (static_cast<int64_t>(blockIdx.x) * TR < rows) load_step(static_cast<int64_t>(blockIdx.x) * TR);
   for (int64_t r0 = static_cast<int64_t>(blockIdx.x) * TR; r0 < rows; r0 += rstep) {
     const int nr = rows - r0 < TR ? static_cast<int>(rows - r0) : TR;
 #pragma unroll
-    for (int c = 0; c < CPT; ++c) {
-      const int q = c * NT + tid;
-      *reinterpret_cast<uint4v*>(stage + (q / CH) * STR + 16 * (q % CH)) = pre[c];
-    }
+    for (int c = 0; c < CPT; ++c) *reinterpret_cast<uint4v*>(wslot + c * (NT / CH) * STR) = pre[c];
     __syncthreads();
     if (r0 + rstep < rows) load_step(r0 + rstep);
 
     const char* row = stage + lane * STR;
     const char* slice = row + wave * 128;
-    float xv[DW];                                    // this wave's slice of the lane's row, fp32
+    float acc[R][4];
 #pragma unroll
-    for (int g = 0; g < DW / 8; ++g) {
-      if constexpr (sizeof(T) == 2) {
-        const uint4v w = *reinterpret_cast<const uint4v*>(slice + 16 * g);
+    for (int p = 0; p < R; ++p) acc[p][0] = acc[p][1] = acc[p][2] = acc[p][3] = 0.f;
+    float xinf = 0.f;                                // max |x_k| (a NaN is skipped; t is then NaN)
+#pragma unroll 1
+    for (int g = 0; g < DW / EPC; ++g) {
+      const uint4v w = *reinterpret_cast<const uint4v*>(slice + 16 * g);
+      float xv[EPC];
 #pragma unroll
-        for (int i = 0; i < 4; ++i) {
-          xv[8 * g + 2 * i] = __uint_as_float(w[i] << 16);
-          xv[8 * g + 2 * i + 1] = __uint_as_float(w[i] & 0xFFFF0000u);
+      for (int i = 0; i < 4; ++i) {
+        if constexpr (sizeof(T) == 2) {
+          xv[2 * i] = __uint_as_float(w[i] << 16);
+          xv[2 * i + 1] = __uint_as_float(w[i] & 0xFFFF0000u);
+        } else {
+          xv[i] = __uint_as_float(w[i]);
         }
-      } else {
-        const floatx4 a = *reinterpret_cast<const floatx4*>(slice + 32 * g);
-        const floatx4 b = *reinterpret_cast<const floatx4*>(slice + 32 * g + 16);
+      }
 #pragma unroll
-        for (int i = 0; i < 4; ++i) {
-          xv[8 * g + i] = a[i];
-          xv[8 * g + 4 + i] = b[i];
-        }
+      for (int k = 0; k < EPC; ++k) xinf = fmaxf(xinf, fabsf(xv[k]));
+#pragma unroll
+      for (int p = 0; p < R; ++p) {
+        const float* rp = Rm + p * D + wave * DW + EPC * g;
+#pragma unroll
+        for (int k = 0; k < EPC; ++k) acc[p][k & 3] = fmaf(xv[k], rp[k], acc[p][k & 3]);
       }
     }
-    float xinf = 0.f;                                // max |x_k| (a NaN is skipped; t is then NaN)
+    // bits from the full sums (wave 0): settled ones directly, the open
+    // ones (rare) by the exact decision
+    auto decide_all = [&](const float* t) -> uint32_t {
+      uint32_t code = 0, open = 0;
 #pragma unroll
-    for (int k = 0; k < DW; ++k) xinf = fmaxf(xinf, fabsf(xv[k]));
-
-    // the partial dot product of projection p over this wave's slice
-    auto partial = [&](int p) {
-      const float* rp = Rm + p * D + wave * DW;
-      float a0 = 0.f, a1 = 0.f, a2 = 0.f, a3 = 0.f;
-#pragma unroll
-      for (int k = 0; k < DW; k += 4) {
-        a0 = fmaf(xv[k], rp[k], a0);
-        a1 = fmaf(xv[k + 1], rp[k + 1], a1);
-        a2 = fmaf(xv[k + 2], rp[k + 2], a2);
-        a3 = fmaf(xv[k + 3], rp[k + 3], a3);
+      for (int p = 0; p < R; ++p) {
+        const float bound = fmaf(xinf * rn1[p], kGam, kAbs);
+        // settled: beyond the bound and finite (a partial sum that overflowed
+        // leaves t infinite or NaN)
+        const float at = fabsf(t[p]);
+        if (at > bound && at <= 0x1.fffffep127f) code |= (t[p] > 0.f ? 1u : 0u) << p;
+        else open |= 1u << p;
       }
-      return (a0 + a1) + (a2 + a3);
+      if (open) {
+#pragma unroll 1
+        for (int p = 0; p < R; ++p)
+          if ((open >> p) & 1u) code |= exact_sign_bit<T, D>(reinterpret_cast<const T*>(row), Rm + p * D) << p;
+      }
+      return code;
     };
-    // bit p from the full sum t (wave 0)
-    auto decide = [&](int p, float t) -> uint32_t {
-      const float bound = fmaf(xinf * rn1[p], kGam, kAbs);
-      // settled: beyond the bound and finite (a partial sum that overflowed
-      // leaves t infinite or NaN)
-      const float at = fabsf(t);
-      if (at > bound && at <= 0x1.fffffep127f) return t > 0.f ? 1u : 0u;
-      return exact_sign_bit<T, D>(reinterpret_cast<const T*>(row), Rm + p * D);
-    };
+    float t[R];
+#pragma unroll
+    for (int p = 0; p < R; ++p) t[p] = (acc[p][0] + acc[p][1]) + (acc[p][2] + acc[p][3]);
     uint32_t code = 0;
     if constexpr (NW == 1) {
-#pragma unroll 1
-      for (int p = 0; p < R; ++p) code |= decide(p, partial(p)) << p;
+      code = decide_all(t);
     } else {
-#pragma unroll 1
-      for (int p = 0; p < R; ++p) part[wave][p][lane] = partial(p);
+#pragma unroll
+      for (int p = 0; p < R; ++p) part[wave][p][lane] = t[p];
       part[wave][R][lane] = xinf;
       __syncthreads();
       if (wave == 0) {
 #pragma unroll
         for (int w = 1; w < NW; ++w) xinf = fmaxf(xinf, part[w][R][lane]);
-#pragma unroll 1
-        for (int p = 0; p < R; ++p) {
-          float t = part[0][p][lane];
 #pragma unroll
-          for (int w = 1; w < NW; ++w) t += part[w][p][lane];
-          code |= decide(p, t) << p;
+        for (int p = 0; p < R; ++p) {
+#pragma unroll
+          for (int w = 1; w < NW; ++w) t[p] += part[w][p][lane];
         }
+        code = decide_all(t);
       }
     }
     if (wave == 0) {
@@ -275,7 +286,7 @@ static int launch_hash_d(const T* x, int64_t rows, int r, const float* R, uint16
                          hipStream_t s) {
   constexpr int NT = 64 * (D * static_cast<int>(sizeof(T)) / 128);
   int64_t blocks = (rows + kHashRows - 1) / kHashRows;
-  const int64_t cap = 256 * 2048 / NT;               // 32 waves per CU, then a grid-stride loop
+  const int64_t cap = 256 * 4096 / NT;               // 64 waves per CU, then a grid-stride loop
   if (blocks > cap) blocks = cap;
   if (blocks < 1) blocks = 1;
   dim3 g(static_cast<unsigned>(blocks)), b(NT);
