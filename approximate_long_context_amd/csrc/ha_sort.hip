@@ -20,6 +20,7 @@
 //
 // HBM traffic per pass: 2 bytes of rank read twice (hist + scatter) or
 // 4 bytes of input permutation + 2 of rank per element, 4 bytes written.
+#include "ha_device.h"
 #include "ha_kernels.h"
 
 namespace ha {
@@ -46,7 +47,10 @@ struct SortBatch {
   int shift, bits;
 };
 
-// The job, segment and tile of workgroup `b` of the flat grid.
+// The job, segment and tile of workgroup `b` of the flat grid.  Callers
+// pass the XCD-remapped id, so consecutive tiles of a segment run on one
+// XCD: the scatter's short digit runs of neighbouring tiles share cache
+// lines, which then fill in one L2 and are written back once.
 __device__ __forceinline__ const SortPass& find_job(const SortBatch& B, uint32_t b, int64_t* seg, int* tile) {
   int j = 0;
   for (int i = 1; i < B.njobs; ++i) j = b >= B.job[i].block0 ? i : j;
@@ -71,7 +75,7 @@ __global__ __launch_bounds__(kSortThreads) void sort_hist_kernel(SortBatch B) {
   __shared__ int hist[256];
   int64_t seg;
   int tile;
-  const SortPass& p = find_job(B, blockIdx.x, &seg, &tile);
+  const SortPass& p = find_job(B, static_cast<uint32_t>(xcd_remap(blockIdx.x, gridDim.x)), &seg, &tile);
   for (int b = threadIdx.x; b < 256; b += kSortThreads) hist[b] = 0;
   __syncthreads();
   const int e0 = tile * kTile;
@@ -166,7 +170,7 @@ __global__ __launch_bounds__(kSortThreads) void sort_scatter_kernel(SortBatch B)
   __shared__ int tot[256];
   int64_t seg;
   int tile;
-  const SortPass& p = find_job(B, blockIdx.x, &seg, &tile);
+  const SortPass& p = find_job(B, static_cast<uint32_t>(xcd_remap(blockIdx.x, gridDim.x)), &seg, &tile);
   const int e0 = tile * kTile;
   const int e1 = min(p.len, e0 + kTile);
   {
