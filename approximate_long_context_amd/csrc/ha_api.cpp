@@ -187,6 +187,11 @@ static int validate(Shape& sh) {
     set_error("samples %d > %d", sh.samples, kMaxSamples);
     return HA_EUNSUPPORTED;
   }
+  if (attention_lds_bound(sh.dtype, sh.d, sh.samples) > kLdsBytes) {
+    set_error("%d samples need %zu bytes of LDS at this dtype and d = %d (limit %zu)", sh.samples,
+              attention_lds_bound(sh.dtype, sh.d, sh.samples), sh.d, kLdsBytes);
+    return HA_EUNSUPPORTED;
+  }
   if (sh.n == 0) return HA_OK;
   if (!sh.causal) return HA_OK;
   // even splits all the way down: one launch per level; otherwise (an odd

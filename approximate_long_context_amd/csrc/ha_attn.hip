@@ -910,13 +910,26 @@ static int launch_attn_t(const AttnParams& p, hipStream_t s) {
     }
     lds += list_bytes(q.bcap, p.m);
   }
+  if (lds > kLdsBytes) {
+    set_error("attention: %zu bytes of LDS needed (%d samples, d = %d), limit %zu", lds, p.m, D, kLdsBytes);
+    return HA_EUNSUPPORTED;
+  }
   auto fn = attn_kernel<T, D, KIND, OUT, NW, QPW>;
   // once per instantiation (thread-safe static initialisation)
   static const hipError_t attr_err = hipFuncSetAttribute(reinterpret_cast<const void*>(fn),
-                                                         hipFuncAttributeMaxDynamicSharedMemorySize, 160 * 1024);
+                                                         hipFuncAttributeMaxDynamicSharedMemorySize, kLdsBytes);
   HA_CHECK_HIP(attr_err);
   hipLaunchKernelGGL(fn, dim3(static_cast<unsigned>(blocks)), dim3(G::NT), lds, s, q);
   return HA_OK;
+}
+
+size_t attention_lds_bound(int dtype, int d, int m) {
+  // K/V buffers do not depend on the workgroup shape; the block key list
+  // is staged only up to kBlockListCap rows
+  size_t buf;
+  if (dtype == HA_BF16) buf = d == 64 ? 2 * Geo<bf16, 64, 8, 32>::BUF : 2 * Geo<bf16, 128, 8, 32>::BUF;
+  else buf = d == 64 ? 2 * Geo<float, 64, 8, 32>::BUF : 2 * Geo<float, 128, 8, 32>::BUF;
+  return buf + static_cast<size_t>(list_bytes(kBlockListCap, m));
 }
 
 // Workgroup shape: waves x queries per wave.  HYPERATTN_SHAPE_LEAF /

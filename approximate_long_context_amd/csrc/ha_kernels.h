@@ -59,6 +59,10 @@ enum AttnOut {
 
 constexpr int kMaxSamples = 4096;   // sample list staged in LDS
 constexpr int kBlockListCap = 2048; // largest block key list staged in LDS
+constexpr size_t kLdsBytes = 160 * 1024;   // LDS of one gfx950 workgroup
+// The largest LDS a sorted-problem attention launch with m samples needs
+// for this dtype and head dim (block key list at its cap).
+size_t attention_lds_bound(int dtype, int d, int m);
 
 struct AttnParams {
   const void* q = nullptr;

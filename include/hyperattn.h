@@ -142,7 +142,9 @@ size_t hyperattn_workspace_bytes(int batch, int n, int d, int heads, int kv_head
  * Errors: HA_EINVAL for null q/k/v/out/workspace (when needed), batch,
  * n, heads, kv_heads < 0 or heads % kv_heads != 0, samples < 0, block < 1,
  * proj_bits outside [1, 16], bad dtype; HA_EUNSUPPORTED for d not in
- * {64, 128} or flags combined with causal; HA_EWORKSPACE when
+ * {64, 128}, samples above 4096 (1952 for fp32 at d = 128, where the
+ * kernel's K/V tiles leave less LDS for the sample lists), or flags other
+ * than HA_FLAG_ROWNORM combined with causal; HA_EWORKSPACE when
  * workspace_bytes is too small.  A segment that is not a multiple of the
  * block gets a short last block, and a causal span of odd length splits
  * with its extra row in the right half (rectangular quadrant).  n == 0 or

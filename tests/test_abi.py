@@ -128,6 +128,20 @@ def test_rownorm_workspace_holds_no_partials():
     assert rn < plain + H * n * d * 2          # less than one bf16 copy of the queries
 
 
+def test_sample_cap_follows_lds():
+    """Sample lists live in LDS beside the K/V tiles: fp32 at d = 128 takes
+    at most 1952 samples, the other builds 4096; larger counts are refused
+    before any pointer is touched."""
+    for dt, d, cap in ((torch.float32, 128, 1952), (torch.float32, 64, 4096), (torch.bfloat16, 128, 4096),
+                       (torch.bfloat16, 64, 4096)):
+        assert ha.workspace_bytes(1, 4096, d, 2, 2, 64, cap, 7, dtype=dt) > 0
+        assert ha.workspace_bytes(1, 4096, d, 2, 2, 64, cap + 1, 7, dtype=dt) == 0
+    L = ha.lib()
+    rc = L.hyperattn_forward(None, None, None, ha.HA_F32, 1, 4096, 128, 2, 2, 64, 1953, 7, 0, 0,
+                             ctypes.c_uint64(0), None, None, None, 0, None)
+    assert rc == ha.HA_EUNSUPPORTED and b"LDS" in L.hyperattn_last_error()
+
+
 def test_causal_rownorm_workspace():
     """Causal row-norm: per-key weights and CDF, an lse per query row and
     the drawn rows of the widest level (16 pieces at n = 131072 with

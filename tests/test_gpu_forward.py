@@ -57,6 +57,10 @@ SMALL = [
     # odd causal splits: node-by-node recursion with rectangular quadrants
     Workload("c_odd", 1, 2, 1, 1000, 64, torch.bfloat16, 64, 32, 6, True, 100, "iid", 14, 27),
     Workload("c_odd_d128", 1, 2, 2, 777, 128, torch.bfloat16, 128, 48, 7, True, 64, "sink", 15, 28),
+    # the largest sample count fp32 at d = 128 accepts (its K/V tiles leave
+    # the least LDS for the sample lists); bf16 d = 64 at the global cap
+    Workload("nc_fp32_d128_maxsamples", 1, 1, 1, 1024, 128, torch.float32, 64, 1952, 6, False, 0, "iid", 16, 29),
+    Workload("nc_maxsamples", 1, 2, 1, 1024, 64, torch.bfloat16, 128, 4096, 6, False, 0, "iid", 17, 30),
 ]
 
 
