@@ -423,15 +423,15 @@ static int debug_leaf(const ha_debug_dump& dd, const AttnParams& lp, hipStream_t
 // Row-norm variant of one launch of sorted quadrant problems (every piece
 // of one level, or one node; queries at q_first + i * stride, keys at
 // k_first + i * stride): the plain estimator (block keys + uniform samples)
-// stores its lse, ln(D_blk + D_unif), at the query rows; the pieces' draws
+// stores its lse, ln(D_blk + D_unif), at the query rows (the lse-only
+// mode: no V rows, no P V products); the pieces' draws
 // (node ids node_first + i) and their K / weighted V rows are made; the
 // second pass attends to the block keys plus the draws, rescales to the
 // stored lse and merges into the accumulator like the plain quadrant.
 static int quadrant_rownorm(AttnParams qp, const Shape& sh, const Plan& pl, int node_first, uint64_t seed,
                             hipStream_t s) {
   AttnParams p1 = qp;
-  p1.out_mode = kOutFinal;
-  p1.out = nullptr;
+  p1.out_mode = kOutLse;
   p1.lse = pl.rn_lse;
   HA_TRY(launch_attention(p1, HA_K_QUADRANT, s));
   RnGeom g;
@@ -583,14 +583,17 @@ static int forward_impl(const void* q, const void* k, const void* v, Shape sh, u
     ap.m = sh.samples;
     ap.log2w = sh.samples > 0 ? static_cast<float>(std::log2(static_cast<double>(sh.n) / sh.samples)) : 0.f;
     if (sh.flags & HA_FLAG_ROWNORM) {
-      // pass 1: the plain estimator (block + uniform samples) stores
-      // lse = ln(D_blk + D_unif); pass 2: block keys + row-norm draws (K and
+      // pass 1 (lse only: no V rows, no P V products): the plain estimator
+      // (block + uniform samples) stores lse = ln(D_blk + D_unif); pass 2: block keys + row-norm draws (K and
       // weighted V rows copied per head) rescaled to that normaliser
       float* lse1 = lse ? lse : pl.rn_lse;
-      ap.out_mode = kOutFinal;
       ap.lse = lse1;
+      if (sh.samples == 0) {                    // no draws: the numerator is the block part alone
+        ap.out_mode = kOutFinal;
+        return launch_attention(ap, HA_K_ATTEND, s);
+      }
+      ap.out_mode = kOutLse;
       HA_TRY(launch_attention(ap, HA_K_ATTEND, s));
-      if (sh.samples == 0) return HA_OK;        // no draws: the numerator is the block part alone
       HA_TRY(launch_rownorm_sqnorm(v, sh.dtype, BK * sh.n, sh.d, pl.rn_w, s));
       RnGeom g;
       g.seg = sh.n;

@@ -129,6 +129,8 @@ __global__ __launch_bounds__(64 * NW, (min_waves<T, D, KIND, NW, QPW>())) void a
   // kOutRescale(Merge): sample rows come from the compact per-head copies, row = sample index
   constexpr bool RS = OUT == kOutRescale || OUT == kOutRescaleMerge;
   constexpr bool MERGE = OUT == kOutMerge || OUT == kOutRescaleMerge;
+  // kOutLse: the normaliser alone (no V rows, no P V products)
+  constexpr bool LO = OUT == kOutLse;
   const T* kcb = RS ? static_cast<const T*>(p.smp_k) + qpiece * p.m * D : nullptr;
   const T* vcb = RS ? static_cast<const T*>(p.smp_v) + qpiece * p.m * D : nullptr;
   const int32_t* pq = (!LEAF && p.perm_q) ? p.perm_q + qpiece * p.seg : nullptr;
@@ -210,7 +212,7 @@ __global__ __launch_bounds__(64 * NW, (min_waves<T, D, KIND, NW, QPW>())) void a
     for (int c = 0; c < G::CPT; ++c) {
       const uint32_t off = static_cast<uint32_t>(t0row[c] * D + G::EPC * c_in_row) * sizeof(T);
       kreg[c] = ld16(mat ? ksb : kbase, off);
-      vreg[c] = ld16(mat ? vsb : vbase, off);
+      if constexpr (!LO) vreg[c] = ld16(mat ? vsb : vbase, off);
     }
   };
 #pragma unroll
@@ -332,7 +334,7 @@ __global__ __launch_bounds__(64 * NW, (min_waves<T, D, KIND, NW, QPW>())) void a
         const int row = isB ? srow[kb + j] : (blist ? brow[kb - ka0 + j] : key_row(kb + j));
         const uint32_t off = static_cast<uint32_t>(row * D + G::EPC * c_in_row) * sizeof(T);
         kw = ld16((RS && isB) ? kcb : (mat ? ksb : kbase), off);
-        vw = ld16((RS && isB) ? vcb : (mat ? vsb : vbase), off);
+        if constexpr (!LO) vw = ld16((RS && isB) ? vcb : (mat ? vsb : vbase), off);
       }
       kreg[c] = kw;
       vreg[c] = vw;
@@ -347,12 +349,12 @@ __global__ __launch_bounds__(64 * NW, (min_waves<T, D, KIND, NW, QPW>())) void a
       const int j = j_first + c * JSTEP;
       if constexpr (BF) {
         *reinterpret_cast<uint4v*>(&ks[j * G::KSTR + 8 * c_in_row]) = kreg[c];
-        *reinterpret_cast<uint4v*>(&vs[j * G::VSTR + 8 * c_in_row]) = vreg[c];
+        if constexpr (!LO) *reinterpret_cast<uint4v*>(&vs[j * G::VSTR + 8 * c_in_row]) = vreg[c];
       } else {
 #pragma unroll
         for (int i = 0; i < 4; ++i) {
           ks[j * G::KSTR + 4 * c_in_row + i] = __uint_as_float(kreg[c][i]);
-          vs[j * G::VSTR + 4 * c_in_row + i] = __uint_as_float(vreg[c][i]);
+          if constexpr (!LO) vs[j * G::VSTR + 4 * c_in_row + i] = __uint_as_float(vreg[c][i]);
         }
       }
     }
@@ -459,10 +461,12 @@ __global__ __launch_bounds__(64 * NW, (min_waves<T, D, KIND, NW, QPW>())) void a
         if (__any(raise)) {
           const float mnew = raise ? fmaxf(mrun[0], tmax) : mrun[0];
           const float alpha = (mnew == mrun[0]) ? 1.f : fast_exp2(mrun[0] - mnew);
+          if constexpr (!LO) {
 #pragma unroll
-          for (int t = 0; t < NDT; ++t)
+            for (int t = 0; t < NDT; ++t)
 #pragma unroll
-            for (int r = 0; r < 16; ++r) o[0][t][r] *= alpha;
+              for (int r = 0; r < 16; ++r) o[0][t][r] *= alpha;
+          }
           lsum[0] *= alpha;
           mrun[0] = mnew;
           nref = mnew == -INFINITY ? 0.f : -mnew;
@@ -521,27 +525,34 @@ __global__ __launch_bounds__(64 * NW, (min_waves<T, D, KIND, NW, QPW>())) void a
         const float off = offset();
         constexpr int kSteps = 2 * NDT;
         constexpr int kPer = 16 / kSteps;
-        bf16x8 va = v_read(0, 0);
+        if constexpr (LO) {
 #pragma unroll
-        for (int st = 0; st < kSteps; ++st) {
-          const int c16 = st / NDT, t = st % NDT;
-          bf16x8 vn = va;
-          if (st + 1 < kSteps) vn = v_read((st + 1) / NDT, (st + 1) % NDT);
-          o[0][t] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(va, c16 == 0 ? pa : pb, o[0][t], 0, 0, 0);
-          __builtin_amdgcn_sched_barrier(0);
+          for (int i = 0; i < 16; i += 2) p_pair(s1, i, off, pc, pd, l1);
+        } else {
+          bf16x8 va = v_read(0, 0);
 #pragma unroll
-          for (int i = kPer * st; i < kPer * (st + 1); i += 2) p_pair(s1, i, off, pc, pd, l1);
-          __builtin_amdgcn_sched_barrier(0);
-          va = vn;
+          for (int st = 0; st < kSteps; ++st) {
+            const int c16 = st / NDT, t = st % NDT;
+            bf16x8 vn = va;
+            if (st + 1 < kSteps) vn = v_read((st + 1) / NDT, (st + 1) % NDT);
+            o[0][t] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(va, c16 == 0 ? pa : pb, o[0][t], 0, 0, 0);
+            __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+            for (int i = kPer * st; i < kPer * (st + 1); i += 2) p_pair(s1, i, off, pc, pd, l1);
+            __builtin_amdgcn_sched_barrier(0);
+            va = vn;
+          }
         }
       }
       settle(s1, pc, pd, l1);
 
       // phase 4: P V of keys [32, 64)
+      if constexpr (!LO) {
 #pragma unroll
-      for (int st = 0; st < 2 * NDT; ++st) {
-        const int c16 = 2 + st / NDT, t = st % NDT;
-        o[0][t] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(v_read(c16, t), c16 == 2 ? pc : pd, o[0][t], 0, 0, 0);
+        for (int st = 0; st < 2 * NDT; ++st) {
+          const int c16 = 2 + st / NDT, t = st % NDT;
+          o[0][t] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(v_read(c16, t), c16 == 2 ? pc : pd, o[0][t], 0, 0, 0);
+        }
       }
     } else {
       // ---- S^T = K Q^T for 64 keys x QPW queries -------------------------------
@@ -615,10 +626,12 @@ __global__ __launch_bounds__(64 * NW, (min_waves<T, D, KIND, NW, QPW>())) void a
         if (__any(raise)) {
           const float mnew = raise ? fmaxf(mrun[u], tmax) : mrun[u];
           const float alpha = (mnew == mrun[u]) ? 1.f : fast_exp2(mrun[u] - mnew);
+          if constexpr (!LO) {
   #pragma unroll
-          for (int t = 0; t < NDT; ++t)
+            for (int t = 0; t < NDT; ++t)
   #pragma unroll
-            for (int r = 0; r < 16; ++r) o[u][t][r] *= alpha;
+              for (int r = 0; r < 16; ++r) o[u][t][r] *= alpha;
+          }
           lsum[u] *= alpha;
           mrun[u] = mnew;
         }
@@ -724,10 +737,12 @@ __global__ __launch_bounds__(64 * NW, (min_waves<T, D, KIND, NW, QPW>())) void a
             const float e = fast_exp2(fmaf(s[kt][0][jr], kLog2e, off));
             lsum[0] += e;
             const int key = 32 * kt + 8 * (jr >> 2) + 4 * h2 + (jr & 3);
+            if constexpr (!LO) {
   #pragma unroll
-            for (int t = 0; t < NDT; ++t) {
-              const float va = vs[key * G::VSTR + 32 * t + col];
-              o[0][t] = __builtin_amdgcn_mfma_f32_32x32x2f32(va, e, o[0][t], 0, 0, 0);
+              for (int t = 0; t < NDT; ++t) {
+                const float va = vs[key * G::VSTR + 32 * t + col];
+                o[0][t] = __builtin_amdgcn_mfma_f32_32x32x2f32(va, e, o[0][t], 0, 0, 0);
+              }
             }
           }
       }
@@ -741,9 +756,19 @@ __global__ __launch_bounds__(64 * NW, (min_waves<T, D, KIND, NW, QPW>())) void a
   // normalised O^T (32 queries x 32 dims, fp32) is staged in the K/V
   // buffers, then lane L merges and stores dims 4 (L & 7) .. +3 of staged
   // query (L >> 3) + 8 k.
+  if constexpr (LO) {
+    // the lse of each query at its original row (lanes 0-31 hold the queries)
+#pragma unroll
+    for (int u = 0; u < NQT; ++u) {
+      const float ltot = lsum[u] + __shfl_xor(lsum[u], 32);
+      const bool any = ltot > 0.f;
+      const float lse2 = any ? (mrun[u] + __builtin_amdgcn_logf(ltot)) * kLn2 : -INFINITY;
+      if (h2 == 0 && ql[u] < qend) p.lse[static_cast<int64_t>(bh) * p.n + orow[u]] = lse2;
+    }
+    return;
+  }
   const bool to_final = OUT == kOutFinal || OUT == kOutRescale || ((OUT == kOutLeaf || MERGE) && piece == p.final_piece);
   const bool to_acc = ((OUT == kOutLeaf || MERGE) && piece != p.final_piece) || OUT == kOutAcc;
-  const bool store_o = OUT != kOutFinal || p.out != nullptr;
   constexpr int SST = 36;                         // staged row stride (floats)
   constexpr int STG = 32 * SST + 64;              // floats per wave: slice, lse, rows
   static_assert(NW * STG * 4 <= 2 * G::BUF, "epilogue staging fits the K/V buffers");
@@ -869,8 +894,7 @@ __global__ __launch_bounds__(64 * NW, (min_waves<T, D, KIND, NW, QPW>())) void a
             *reinterpret_cast<floatx4*>(p.acc_o + ridx * D + dc) = val;
             if (head) p.acc_lse[ridx] = lse_out[k];
           } else if (to_final) {
-            if (!store_o) {
-            } else if constexpr (BF) {
+            if constexpr (BF) {
               bf16x4 ob;
 #pragma unroll
               for (int i = 0; i < 4; ++i) ob[i] = static_cast<bf16>(val[i]);
@@ -973,6 +997,7 @@ static int launch_attn_d(const AttnParams& p, hipStream_t s) {
     if (p.out_mode == kOutMerge) return launch_attn_shape<T, D, kKindSorted, kOutMerge>(p, s);
     if (p.out_mode == kOutRescale) return launch_attn_shape<T, D, kKindSorted, kOutRescale>(p, s);
     if (p.out_mode == kOutRescaleMerge) return launch_attn_shape<T, D, kKindSorted, kOutRescaleMerge>(p, s);
+    if (p.out_mode == kOutLse) return launch_attn_shape<T, D, kKindSorted, kOutLse>(p, s);
   }
   set_error("attention: unsupported kind %d / output mode %d", p.kind, p.out_mode);
   return HA_EINVAL;
@@ -991,6 +1016,10 @@ int launch_attention(const AttnParams& p_in, int timing_kind, hipStream_t s) {
   if (p.m > kMaxSamples) {
     set_error("attention: samples %d > %d", p.m, kMaxSamples);
     return HA_EUNSUPPORTED;
+  }
+  if (p.out_mode == kOutLse && (!p.lse || p.qs)) {
+    set_error("attention: the lse-only mode needs lse and reads rows through the permutations");
+    return HA_EINVAL;
   }
   if ((p.out_mode == kOutRescale || p.out_mode == kOutRescaleMerge) &&
       (!p.lse_ref || (p.m > 0 && (!p.smp_k || !p.smp_v || !p.sidx)))) {

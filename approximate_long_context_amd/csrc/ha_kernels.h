@@ -54,7 +54,8 @@ enum AttnOut {
   kOutMerge = 3,      // merge with acc at the row; piece 0 -> out/lse, else -> acc
   kOutAcc = 4,        // every piece -> acc at the row (no read)
   kOutRescale = 5,    // out at the original row, scaled by exp(own lse - lse_ref there); lse kept
-  kOutRescaleMerge = 6  // as kOutRescale, the result (lse = lse_ref) then merged like kOutMerge
+  kOutRescaleMerge = 6, // as kOutRescale, the result (lse = lse_ref) then merged like kOutMerge
+  kOutLse = 7           // lse alone at the original row (no V, no P V products)
 };
 
 constexpr int kMaxSamples = 4096;   // sample list staged in LDS
@@ -106,7 +107,7 @@ struct AttnParams {
   float log2w = 0.f;                 // log2(seg / m)
   int out_mode = kOutFinal;
   int final_piece = 0;               // kOutLeaf / kOutMerge: the piece whose rows are final (-1: none)
-  void* out = nullptr;               // [BH][n][d] dtype (kOutFinal: null stores the lse alone)
+  void* out = nullptr;               // [BH][n][d] dtype
   float* lse = nullptr;              // [BH][n] (may be null for kOutFinal)
   float* acc_o = nullptr;            // [BH][n][d]
   float* acc_lse = nullptr;          // [BH][n]

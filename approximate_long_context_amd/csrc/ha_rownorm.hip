@@ -21,9 +21,9 @@
 // scans, chunk offsets), the draws (binary search) and the copy of the drawn
 // K / weighted V rows.  The result
 //   out = (N_blk + N_rn) / (D_blk + D_unif),  lse = ln(D_blk + D_unif)
-// takes two attention passes: the plain estimator writes lse (its output is
-// overwritten); the second pass attends to the block keys plus the drawn
-// rows (unit weight in its own normaliser D2 = D_blk + sum of their
+// takes two attention passes: the first, in the lse-only mode (no V rows,
+// no P V products), stores the plain estimator's lse; the second attends
+// to the block keys plus the drawn rows (unit weight in its own normaliser D2 = D_blk + sum of their
 // exponentials) and scales its output by D2 / (D_blk + D_unif) =
 // exp(own lse - stored lse), which turns (N_blk + N_rn) / D2 into the result.
 #include <cmath>
