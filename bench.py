@@ -313,6 +313,7 @@ def main():
                              for name, w in (("noncausal", w_nc), ("causal", w_c))}
         result["diagnostics"] = diagnostics_bench(ha, torch, dev, stream)
         result["rect"] = rect_bench(ha, torch, dev, stream)
+        result["gather"] = gather_bench(ha, torch, w_nc, k, stream)
         del ws
         result["backward"] = {name: backward_bench(ha, torch, w, q, k, v, out, lse, stream)
                               for name, w in (("noncausal", w_nc), ("causal", w_c))}
@@ -442,6 +443,33 @@ def rownorm_bench(ha, torch, w, q, k, v, out, stream, reps=3):
     err = float(torch.linalg.vector_norm(a - b) / torch.linalg.vector_norm(b))
     del a, b, ex, ws
     return {"ms": ms, "tflops": f / (ms * 1e-3) / 1e12, "approx_rel_error": err}
+
+
+def gather_bench(ha, torch, w, k, stream, reps=5):
+    """The stand-alone permutation gather (hyperattn_gather, the materialised
+    mode's copy of rows into sorted order) on the headline K through its own
+    LSH sort permutation: HBM bytes = rows x (row read + row written +
+    4-byte permutation entry) per launch, against the 8 TB/s peak.  The
+    default forward fuses this gather into the attention kernels' row loads
+    (their bytes are in `kernels.attend.gbs`)."""
+    R = ha.projections(w.seed, w.d, w.proj_bits, device=k.device)
+    heads = w.batch * w.kv_heads
+    k2 = k.reshape(heads, w.n, w.d)
+    perm = ha.sort_ranks(ha.hash_rows(k2, R), w.proj_bits)[:, 0, :].contiguous()
+    ha.gather_rows(k2, perm)
+    torch.cuda.synchronize()
+    e0 = torch.cuda.Event(enable_timing=True)
+    e1 = torch.cuda.Event(enable_timing=True)
+    e0.record(stream)
+    for _ in range(reps):
+        ha.gather_rows(k2, perm)
+    e1.record(stream)
+    torch.cuda.synchronize()
+    ms = e0.elapsed_time(e1) / reps
+    nbytes = heads * w.n * (2 * w.d * k.element_size() + 4)
+    gbs = nbytes / (ms * 1e-3) / 1e9
+    return {"ms": ms, "bytes": nbytes, "gbs": gbs, "peak_gbs": HBM_PEAK_GBS, "frac": gbs / HBM_PEAK_GBS,
+            "rows": heads * w.n, "row_bytes": w.d * k.element_size()}
 
 
 def backward_bench(ha, torch, w, q, k, v, out, lse, stream, reps=3):
