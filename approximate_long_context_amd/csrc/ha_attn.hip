@@ -70,7 +70,7 @@ struct Geo {
   static constexpr int CPR = D / EPC;                             // chunks per row
   static constexpr int CPT = kKT * CPR / NT;                      // chunks per thread per tensor
   static_assert(NT % CPR == 0 && (kKT * CPR) % NT == 0, "tile split");
-  static_assert(QPW == 32 || (QPW == 64 && BF), "64 queries per wave: bf16 only");
+  static_assert(QPW == 32, "one 32-query MFMA tile per wave");
 };
 
 // LDS bytes after the two K/V buffers (sorted problems): brow[bcap],
@@ -379,8 +379,8 @@ __global__ __launch_bounds__(64 * NW, (min_waves<T, D, KIND, NW, QPW>())) void a
     const T* ks = reinterpret_cast<const T*>(smem + buf * G::BUF);
     const T* vs = reinterpret_cast<const T*>(smem + buf * G::BUF + G::KBYTES);
 
-    if constexpr (BF && NQT == 1) {
-      // ---- bf16, one 32-query tile per wave: half-tile pipeline ------------------
+    if constexpr (BF) {
+      // ---- bf16: half-tile pipeline ------------------------------------------------
       // Keys [0, 32) and [32, 64) of the tile are two halves.  The S^T MFMAs
       // of the second half do not depend on the softmax of the first, nor
       // the P V MFMAs of the first half on the softmax of the second, so
@@ -555,7 +555,7 @@ __global__ __launch_bounds__(64 * NW, (min_waves<T, D, KIND, NW, QPW>())) void a
         }
       }
     } else {
-      // ---- S^T = K Q^T for 64 keys x QPW queries -------------------------------
+      // ---- fp32: S^T = K Q^T for 64 keys x 32 queries ---------------------------
       floatx16 s[2][NQT];
   #pragma unroll
       for (int kt = 0; kt < 2; ++kt) {
@@ -565,17 +565,10 @@ __global__ __launch_bounds__(64 * NW, (min_waves<T, D, KIND, NW, QPW>())) void a
           for (int r = 0; r < 16; ++r) s[kt][u][r] = 0.f;
   #pragma unroll
         for (int c = 0; c < NQF; ++c) {
-          if constexpr (BF) {
-            const bf16x8 ka = *reinterpret_cast<const bf16x8*>(&ks[(32 * kt + col) * G::KSTR + 16 * c + 8 * h2]);
+          const float ka = ks[(32 * kt + col) * G::KSTR + 2 * c + h2];
   #pragma unroll
-            for (int u = 0; u < NQT; ++u)
-              s[kt][u] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ka, qf[u][c], s[kt][u], 0, 0, 0);
-          } else {
-            const float ka = ks[(32 * kt + col) * G::KSTR + 2 * c + h2];
-  #pragma unroll
-            for (int u = 0; u < NQT; ++u)
-              s[kt][u] = __builtin_amdgcn_mfma_f32_32x32x2f32(ka, qf[u][c], s[kt][u], 0, 0, 0);
-          }
+          for (int u = 0; u < NQT; ++u)
+            s[kt][u] = __builtin_amdgcn_mfma_f32_32x32x2f32(ka, qf[u][c], s[kt][u], 0, 0, 0);
         }
       }
 
@@ -638,96 +631,7 @@ __global__ __launch_bounds__(64 * NW, (min_waves<T, D, KIND, NW, QPW>())) void a
       };
 
       // ---- P, row sums and O^T += V^T P^T -----------------------------------------
-      if constexpr (BF && !LEAF) {
-        // sorted problems (gather-bound, occupancy-sensitive): maximum every
-        // tile, exponentials interleaved with the P V MFMAs chunk by chunk
-        const bf16x2 ones = {static_cast<bf16>(1.f), static_cast<bf16>(1.f)};
-        float off[NQT];
-  #pragma unroll
-        for (int u = 0; u < NQT; ++u) {
-          tile_max_raise(u);
-          off[u] = bias - (mrun[u] == -INFINITY ? 0.f : mrun[u]);
-        }
-  #pragma unroll
-        for (int c16 = 0; c16 < 4; ++c16) {
-          const int kt = c16 >> 1;
-          const int hi = c16 & 1;
-          bf16x8 pb[NQT];
-  #pragma unroll
-          for (int u = 0; u < NQT; ++u) {
-            float l = 0.f;
-  #pragma unroll
-            for (int i = 0; i < 8; i += 2) {
-              const float e0 = fast_exp2(fmaf(s[kt][u][8 * hi + i], kLog2e, off[u]));
-              const float e1 = fast_exp2(fmaf(s[kt][u][8 * hi + i + 1], kLog2e, off[u]));
-              const bf16x2 two = __builtin_convertvector((float __attribute__((ext_vector_type(2)))){e0, e1}, bf16x2);
-              l = __builtin_amdgcn_fdot2_f32_bf16(two, ones, l, false);
-              pb[u][i] = two[0];
-              pb[u][i + 1] = two[1];
-            }
-            lsum[u] += l;
-          }
-  #pragma unroll
-          for (int t = 0; t < NDT; ++t) {
-            const T* vp = vs + (16 * c16 + tr_key) * G::VSTR + 32 * t + tr_col;
-            const short4v lo = lds_read_tr16(vp);
-            const short4v hv = lds_read_tr16(vp + 8 * G::VSTR);
-            const short __attribute__((ext_vector_type(8))) va8 = {lo[0], lo[1], lo[2], lo[3], hv[0], hv[1], hv[2], hv[3]};
-            const bf16x8 va = __builtin_bit_cast(bf16x8, va8);
-  #pragma unroll
-            for (int u = 0; u < NQT; ++u)
-              o[u][t] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(va, pb[u], o[u][t], 0, 0, 0);
-          }
-        }
-      } else if constexpr (BF) {
-        // causal leaves (compute-bound): maximum only when needed
-        const bf16x2 ones = {static_cast<bf16>(1.f), static_cast<bf16>(1.f)};
-        bf16x8 pb[4][NQT];
-        float ls[NQT];
-        auto make_p = [&](int u) {
-          const float off = bias - (mrun[u] == -INFINITY ? 0.f : mrun[u]);
-          float l0 = 0.f, l1 = 0.f;
-  #pragma unroll
-          for (int c16 = 0; c16 < 4; ++c16) {
-            const int kt = c16 >> 1;
-            const int hi = c16 & 1;
-  #pragma unroll
-            for (int i = 0; i < 8; i += 2) {
-              const float e0 = fast_exp2(fmaf(s[kt][u][8 * hi + i], kLog2e, off));
-              const float e1 = fast_exp2(fmaf(s[kt][u][8 * hi + i + 1], kLog2e, off));
-              const bf16x2 two = __builtin_convertvector((float __attribute__((ext_vector_type(2)))){e0, e1}, bf16x2);
-              if (i & 2) l1 = __builtin_amdgcn_fdot2_f32_bf16(two, ones, l1, false);
-              else l0 = __builtin_amdgcn_fdot2_f32_bf16(two, ones, l0, false);
-              pb[c16][u][i] = two[0];
-              pb[c16][u][i + 1] = two[1];
-            }
-          }
-          ls[u] = l0 + l1;
-        };
-  #pragma unroll
-        for (int u = 0; u < NQT; ++u) {
-          if (mrun[u] == -INFINITY) tile_max_raise(u);
-          make_p(u);
-          if (__any(!(ls[u] <= 32768.f))) {        // reference too low (or no reference)
-            tile_max_raise(u);
-            make_p(u);
-          }
-          lsum[u] += ls[u];
-        }
-  #pragma unroll
-        for (int c16 = 0; c16 < 4; ++c16)
-  #pragma unroll
-          for (int t = 0; t < NDT; ++t) {
-            const T* vp = vs + (16 * c16 + tr_key) * G::VSTR + 32 * t + tr_col;
-            const short4v lo = lds_read_tr16(vp);
-            const short4v hv = lds_read_tr16(vp + 8 * G::VSTR);
-            const short __attribute__((ext_vector_type(8))) va8 = {lo[0], lo[1], lo[2], lo[3], hv[0], hv[1], hv[2], hv[3]};
-            const bf16x8 va = __builtin_bit_cast(bf16x8, va8);
-  #pragma unroll
-            for (int u = 0; u < NQT; ++u)
-              o[u][t] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(va, pb[c16][u], o[u][t], 0, 0, 0);
-          }
-      } else {
+      {
         tile_max_raise(0);
         const float off = bias - (mrun[0] == -INFINITY ? 0.f : mrun[0]);
   #pragma unroll
