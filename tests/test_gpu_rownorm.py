@@ -157,6 +157,25 @@ def test_rownorm_causal_matches_oracle(B, H, Hkv, n, d, block, m, r, s, seed, dt
     assert torch.equal(lse, l0)
 
 
+@pytest.mark.parametrize("causal", [False, True])
+def test_rownorm_degenerate_value_rows(causal):
+    """Degenerate weights: KV head 0 has all-zero value rows (T = 0: no
+    draws, the numerator is the block part alone) and KV head 1 a single
+    nonzero value row (every draw lands on it)."""
+    B, H, Hkv, n, d = 1, 4, 2, 1024, 64
+    q, k, v = _inputs(B, H, Hkv, n, d, 50)
+    v[:, 0] = 0
+    keep = v[:, 1, 333].clone()
+    v[:, 1] = 0
+    v[:, 1, 333] = keep
+    args = dict(block=64, samples=96, proj_bits=6, seed=9, causal=causal, min_seq_len=128 if causal else 0)
+    out, lse = ha.forward(q.to(DEV), k.to(DEV), v.to(DEV), flags=ha.HA_FLAG_ROWNORM, **args)
+    torch.cuda.synchronize()
+    ro, rl = rn.forward(np32(q), np32(k), np32(v), HAConfig(**args))
+    _check_against(np32(out), ro, lse.cpu().numpy(), rl, torch.bfloat16, "degenerate values")
+    assert not np.any(np32(out)[0, :2])                # heads of KV head 0: zero output
+
+
 def test_rownorm_causal_without_samples_is_the_plain_method():
     q, k, v = (t.to(DEV) for t in _inputs(1, 2, 1, 1000, 64, 32))
     args = dict(block=64, samples=0, proj_bits=6, seed=5, causal=True, min_seq_len=100)
