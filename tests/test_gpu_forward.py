@@ -114,6 +114,20 @@ def test_forward_empty_and_lse_optional():
     assert torch.equal(out, out2)
 
 
+@pytest.mark.parametrize("n", [1, 2, 3, 5, 33])
+@pytest.mark.parametrize("causal", [False, True])
+def test_forward_tiny_n(n, causal):
+    """Heads of a few rows: one partial tile, blocks of the whole head,
+    every sample inside the row's block (non-causal), odd splits down to
+    leaves of one or two rows (causal, min_seq_len 1 and 2)."""
+    for s in ((1, 2) if causal else (0,)):
+        w = Workload(f"tiny_{n}", 1, 2, 1, n, 64, torch.bfloat16, 2, 3, 5, causal, s, "iid", 0, 40 + n)
+        q, k, v, out, lse = _run(w)
+        ref_o, ref_l = oracle.forward(np32(q), np32(k), np32(v), _cfg(w))
+        compare(np32(out), ref_o, w.dtype, f"{w.name} s={s}")
+        compare_lse(np32(lse), ref_l, w.dtype, f"{w.name} s={s}")
+
+
 # ---------------------------------------------------------------------------
 # Full-size workloads: sampled rows + bit-exact ranks/permutations
 # ---------------------------------------------------------------------------
