@@ -190,6 +190,26 @@ def test_causal_backward_odd_splits_match_oracle(B, H, Hkv, n, d, block, m, r, s
     _run(B, H, Hkv, n, d, seed, block=block, samples=m, proj_bits=r, causal=True, min_seq_len=s)
 
 
+@pytest.mark.parametrize("n", [1, 3, 33])
+@pytest.mark.parametrize("causal", [False, True])
+def test_backward_tiny_n(n, causal):
+    """Heads of a few rows (one partial tile; causal splits down to leaves
+    of one or two rows), bf16 and fp32."""
+    for s in ((1, 2) if causal else (0,)):
+        args = dict(block=2, samples=3, proj_bits=5, causal=causal, min_seq_len=s)
+        _run(1, 2, 1, n, 64, 50 + n, **args)
+        q, k, v, do = _inputs32(1, 2, 1, n, 64, 60 + n)
+        qd, kd, vd, dod = q.to(DEV), k.to(DEV), v.to(DEV), do.to(DEV)
+        out, lse = ha.forward(qd, kd, vd, seed=5, **args)
+        dq, dk, dv = ha.backward(qd, kd, vd, out, lse, dod, seed=5, **args)
+        torch.cuda.synchronize()
+        rq, rk, rv = ob.backward(q.numpy(), k.numpy(), v.numpy(), do.numpy(), HAConfig(seed=5, **args))
+        for got, ref, what in ((dq, rq, "dq"), (dk, rk, "dk"), (dv, rv, "dv")):
+            got = got.cpu().numpy().astype(np.float64)
+            scale = float(np.max(np.abs(ref))) or 1.0
+            assert float(np.max(np.abs(got - ref))) <= 1e-4 * scale, (n, s, what)
+
+
 RECT_CASES = [
     # B, H, Hkv, n_q, n_k, d, block, samples, r, seed
     (1, 2, 1, 1024, 1500, 64, 128, 64, 7, 41),     # more keys than queries, grouped heads
