@@ -48,6 +48,19 @@ def test_rect_matches_oracle(B, H, Hkv, nq, nk, d, block, m, r, seed, dtype):
     compare_lse(lse.cpu().numpy(), rl, dtype, "lse")
 
 
+@pytest.mark.parametrize("nq,nk", [(1, 1), (1, 5), (5, 1), (3, 70), (70, 3)])
+def test_rect_tiny(nq, nk):
+    """A few rows on either side: key blocks of one row or empty, samples
+    over one key, one partial tile."""
+    q, k, v = _inputs(1, 2, 1, nq, nk, 64, 90 + nq + nk, torch.bfloat16)
+    args = dict(block=2, samples=3, proj_bits=5, seed=7)
+    out, lse = ha.forward_rect(q.to(DEV), k.to(DEV), v.to(DEV), **args)
+    torch.cuda.synchronize()
+    ro, rl = oh.forward_rect(np32(q), np32(k), np32(v), HAConfig(**args))
+    compare(np32(out), ro, torch.bfloat16, f"{nq}x{nk}")
+    compare_lse(lse.cpu().numpy(), rl, torch.bfloat16, f"{nq}x{nk}")
+
+
 def test_square_rect_equals_forward():
     q, k, v = (t.to(DEV) for t in _inputs(1, 2, 1, 1024, 1024, 64, 7, torch.bfloat16))
     args = dict(block=128, samples=64, proj_bits=7, seed=3)

@@ -176,6 +176,17 @@ def test_rownorm_degenerate_value_rows(causal):
     assert not np.any(np32(out)[0, :2])                # heads of KV head 0: zero output
 
 
+@pytest.mark.parametrize("n", [1, 3, 33])
+@pytest.mark.parametrize("causal", [False, True])
+def test_rownorm_tiny_n(n, causal):
+    q, k, v = _inputs(1, 2, 1, n, 64, 70 + n)
+    args = dict(block=2, samples=5, proj_bits=5, seed=4, causal=causal, min_seq_len=1 if causal else 0)
+    out, lse = ha.forward(q.to(DEV), k.to(DEV), v.to(DEV), flags=ha.HA_FLAG_ROWNORM, **args)
+    torch.cuda.synchronize()
+    ro, rl = rn.forward(np32(q), np32(k), np32(v), HAConfig(**args))
+    _check_against(np32(out), ro, lse.cpu().numpy(), rl, torch.bfloat16, f"tiny {n}")
+
+
 def test_rownorm_causal_without_samples_is_the_plain_method():
     q, k, v = (t.to(DEV) for t in _inputs(1, 2, 1, 1000, 64, 32))
     args = dict(block=64, samples=0, proj_bits=6, seed=5, causal=True, min_seq_len=100)
