@@ -1,0 +1,82 @@
+"""A seeded sweep of forward configurations against the oracle: random
+sizes (n up to 1500, ragged everywhere), block sizes from 1 to beyond n,
+sample counts from 0 to above n, grouped-head ratios, proj_bits from 1
+to 16 (two-pass sort above 8), causal spans with random min_seq_len (even
+and odd splits), d 64 / 128, bf16 and fp32, and the row-norm variant on
+a share of them (with varied value-row norms; the plain cases use unit
+normal values, as the parity bar assumes |o| of order one).  The draws are
+fixed by the seed list, so the sweep is the same on every run."""
+
+import numpy as np
+import pytest
+import torch
+
+import approximate_long_context_amd as ha
+import oracle
+from oracle import rownorm as rn
+from oracle.hyperattn import HAConfig
+
+from _util import compare, compare_lse, np32, TOL
+
+pytestmark = pytest.mark.gpu
+DEV = "cuda"
+
+
+def _case(i):
+    g = np.random.default_rng(1000 + i)
+    dtype = torch.float32 if g.random() < 0.25 else torch.bfloat16
+    d = int(g.choice([64, 128]))
+    kv = int(g.choice([1, 2]))
+    heads = kv * int(g.choice([1, 2, 3]))
+    n = int(g.integers(1, 1501))
+    block = int(g.choice([1, 3, 16, 40, 64, 100, 256, 2048]))
+    samples = int(g.choice([0, 1, 7, 64, 300, 1600]))
+    if dtype == torch.float32 and d == 128:
+        samples = min(samples, 1952)
+    r = int(g.integers(1, 17))
+    causal = bool(g.random() < 0.5)
+    s = int(g.integers(1, max(2, n))) if causal else 0
+    rownorm = bool(g.random() < 0.3)
+    return dict(dtype=dtype, d=d, kv=kv, heads=heads, n=n, block=block, samples=samples, r=r, causal=causal,
+                s=s, rownorm=rownorm, seed=int(g.integers(0, 2 ** 31)))
+
+
+CASES = [_case(i) for i in range(40)]
+
+
+def _inputs(c):
+    g = torch.Generator(device="cpu").manual_seed(c["seed"] & 0xFFFF)
+    sc = c["d"] ** -0.25
+    q = (torch.randn(1, c["heads"], c["n"], c["d"], generator=g) * sc).to(c["dtype"])
+    k = (torch.randn(1, c["kv"], c["n"], c["d"], generator=g) * sc).to(c["dtype"])
+    v = torch.randn(1, c["kv"], c["n"], c["d"], generator=g)
+    if c["rownorm"]:                              # varied value-row norms for the row-norm draws
+        v = v * torch.exp(0.5 * torch.randn(1, c["kv"], c["n"], 1, generator=g))
+    return q, k, v.to(c["dtype"])
+
+
+@pytest.mark.parametrize("i", range(len(CASES)))
+def test_sweep_matches_oracle(i):
+    c = CASES[i]
+    print(f"[sweep {i}] {c}", flush=True)
+    q, k, v = _inputs(c)
+    args = dict(block=c["block"], samples=c["samples"], proj_bits=c["r"], seed=c["seed"], causal=c["causal"],
+                min_seq_len=c["s"])
+    flags = ha.HA_FLAG_ROWNORM if c["rownorm"] else 0
+    out, lse = ha.forward(q.to(DEV), k.to(DEV), v.to(DEV), flags=flags, **args)
+    torch.cuda.synchronize()
+    cfg = HAConfig(**args)
+    if c["rownorm"]:
+        ro, rl = rn.forward(np32(q), np32(k), np32(v), cfg)
+        got = np32(out).astype(np.float64)
+        tol = TOL[c["dtype"]]
+        scale = max(1.0, float(np.max(np.abs(ro))))
+        assert np.all(np.isfinite(got))
+        assert float(np.max(np.abs(got - ro))) <= tol["max_abs"] * scale
+        den = float(np.linalg.norm(ro))
+        if den > 0:
+            assert float(np.linalg.norm(got - ro)) / den <= tol["rel_fro"]
+    else:
+        ro, rl = oracle.forward(np32(q), np32(k), np32(v), cfg)
+        compare(np32(out), ro, c["dtype"], f"sweep {i}")
+    compare_lse(np32(lse), rl, c["dtype"], f"sweep {i}")
