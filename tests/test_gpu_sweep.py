@@ -5,7 +5,9 @@ to 16 (two-pass sort above 8), causal spans with random min_seq_len (even
 and odd splits), d 64 / 128, bf16 and fp32, and the row-norm variant on
 a share of them (with varied value-row norms; the plain cases use unit
 normal values, as the parity bar assumes |o| of order one).  The draws are
-fixed by the seed list, so the sweep is the same on every run."""
+fixed by the seed list, so the sweep is the same on every run.  A second
+sweep of 20 configurations runs the backward (bf16 and fp32) against the
+oracle's gradients."""
 
 import numpy as np
 import pytest
@@ -80,3 +82,54 @@ def test_sweep_matches_oracle(i):
         ro, rl = oracle.forward(np32(q), np32(k), np32(v), cfg)
         compare(np32(out), ro, c["dtype"], f"sweep {i}")
     compare_lse(np32(lse), rl, c["dtype"], f"sweep {i}")
+
+
+# ---- backward ---------------------------------------------------------------------
+
+def _bcase(i):
+    g = np.random.default_rng(5000 + i)
+    dtype = torch.float32 if g.random() < 0.3 else torch.bfloat16
+    d = int(g.choice([64, 128]))
+    kv = int(g.choice([1, 2]))
+    heads = kv * int(g.choice([1, 2]))
+    n = int(g.integers(1, 900))
+    block = int(g.choice([1, 5, 32, 64, 100, 256, 1024]))
+    samples = int(g.choice([0, 1, 13, 64, 400]))
+    causal = bool(g.random() < 0.5)
+    s = int(g.integers(1, max(2, n))) if causal else 0
+    return dict(dtype=dtype, d=d, kv=kv, heads=heads, n=n, block=block, samples=samples,
+                r=int(g.integers(1, 17)), causal=causal, s=s, seed=int(g.integers(0, 2 ** 31)))
+
+
+BCASES = [_bcase(i) for i in range(20)]
+
+
+@pytest.mark.parametrize("i", range(len(BCASES)))
+def test_sweep_backward_matches_oracle(i):
+    from oracle import backward as ob
+    c = BCASES[i]
+    print(f"[backward sweep {i}] {c}", flush=True)
+    g = torch.Generator(device="cpu").manual_seed(c["seed"] & 0xFFFF)
+    sc = c["d"] ** -0.25
+    q = (torch.randn(1, c["heads"], c["n"], c["d"], generator=g) * sc).to(c["dtype"])
+    k = (torch.randn(1, c["kv"], c["n"], c["d"], generator=g) * sc).to(c["dtype"])
+    v = torch.randn(1, c["kv"], c["n"], c["d"], generator=g).to(c["dtype"])
+    do = torch.randn(1, c["heads"], c["n"], c["d"], generator=g).to(c["dtype"])
+    args = dict(block=c["block"], samples=c["samples"], proj_bits=c["r"], seed=c["seed"], causal=c["causal"],
+                min_seq_len=c["s"])
+    qd, kd, vd, dod = q.to(DEV), k.to(DEV), v.to(DEV), do.to(DEV)
+    out, lse = ha.forward(qd, kd, vd, **args)
+    dq, dk, dv = ha.backward(qd, kd, vd, out, lse, dod, **args)
+    torch.cuda.synchronize()
+    rq, rk, rv = ob.backward(np32(q), np32(k), np32(v), np32(do), HAConfig(**args))
+    # bf16: P and dS rounded to bf16 before their products (as the backward
+    # tests); fp32: the fp32 kernels within 1e-4
+    rel_max, rel_f = (8e-3, 5e-3) if c["dtype"] == torch.bfloat16 else (1e-4, 1e-4)
+    for got, ref, what in ((dq, rq, "dq"), (dk, rk, "dk"), (dv, rv, "dv")):
+        got = got.cpu().numpy().astype(np.float64)
+        assert np.all(np.isfinite(got)), what
+        scale = float(np.max(np.abs(ref))) or 1.0
+        assert float(np.max(np.abs(got - ref))) <= rel_max * scale, what
+        den = float(np.linalg.norm(ref))
+        if den > 0:
+            assert float(np.linalg.norm(got - ref)) / den <= rel_f, what
