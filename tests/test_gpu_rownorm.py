@@ -9,10 +9,12 @@ recursion with its node's draws; even splits and odd, rectangular ones).
   the row-norm part from a per-head copy of the drawn V rows carrying the
   draw weight T / (m n_t), rounded to the input dtype (bf16: 2^-9 relative
   per term) -- so the per-element bound is the forward's, scaled by the
-  largest reference magnitude (draws of small-norm rows carry large
-  weights and can lift outputs above 1): max-abs <= 2e-2 max(1, max|ref|)
-  and relative Frobenius <= 1e-2 for bf16 (1e-4 for fp32); lse as the
-  forward's (the normaliser is the uniform method's).
+  largest reference magnitude for bf16 (draws of small-norm rows carry
+  large weights and lift outputs above 1 -- 2 to 5 here even with unit
+  normal values -- where one bf16 rounding alone approaches 2e-2):
+  max-abs <= 2e-2 max(1, max|ref|) and relative Frobenius <= 1e-2; fp32
+  keeps the forward's unscaled bound, 1e-4 both; lse as the forward's (the
+  normaliser is the uniform method's, and is asserted bit-identical to it).
 """
 
 import numpy as np
@@ -94,7 +96,7 @@ def test_rownorm_forward_matches_oracle(B, H, Hkv, n, d, block, m, r, seed, dtyp
     ro, rl = rn.forward(np32(q), np32(k), np32(v), HAConfig(**args))
     got = np32(out).astype(np.float64)
     tol = TOL[dtype]
-    scale = max(1.0, float(np.max(np.abs(ro))))
+    scale = max(1.0, float(np.max(np.abs(ro)))) if dtype == torch.bfloat16 else 1.0
     err = float(np.max(np.abs(got - ro)))
     rel = float(np.linalg.norm(got - ro) / np.linalg.norm(ro))
     assert np.all(np.isfinite(got))
@@ -133,7 +135,7 @@ CAUSAL_CASES = [
 def _check_against(got, ro, lse, rl, dtype, what):
     got = got.astype(np.float64)
     tol = TOL[dtype]
-    scale = max(1.0, float(np.max(np.abs(ro))))
+    scale = max(1.0, float(np.max(np.abs(ro)))) if dtype == torch.bfloat16 else 1.0
     err = float(np.max(np.abs(got - ro)))
     rel = float(np.linalg.norm(got - ro) / np.linalg.norm(ro))
     assert np.all(np.isfinite(got)), what

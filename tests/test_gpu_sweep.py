@@ -72,7 +72,7 @@ def test_sweep_matches_oracle(i):
         ro, rl = rn.forward(np32(q), np32(k), np32(v), cfg)
         got = np32(out).astype(np.float64)
         tol = TOL[c["dtype"]]
-        scale = max(1.0, float(np.max(np.abs(ro))))
+        scale = max(1.0, float(np.max(np.abs(ro)))) if c["dtype"] == torch.bfloat16 else 1.0
         assert np.all(np.isfinite(got))
         assert float(np.max(np.abs(got - ro))) <= tol["max_abs"] * scale
         den = float(np.linalg.norm(ro))
