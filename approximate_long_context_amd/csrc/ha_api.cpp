@@ -246,7 +246,7 @@ static Plan make_plan(const Shape& sh, void* ws, size_t cap) {
   const int64_t BH = static_cast<int64_t>(sh.batch) * sh.heads;
   const int64_t BK = static_cast<int64_t>(sh.batch) * sh.kv_heads;
   const size_t esz = sh.dtype == HA_BF16 ? 2 : 4;
-  // causal row-norm buffers: `pieces` problems of at most `seg` keys per head
+  // row-norm buffers: `pieces` problems of at most `seg` keys per head
   auto take_rn = [&](int64_t pieces, int64_t seg, size_t cdf_ws) {
     pl.rn_w = cv.take<float>(BK * sh.n);
     pl.rn_cum = cv.take<int64_t>(BK * pieces * seg);
@@ -277,15 +277,7 @@ static Plan make_plan(const Shape& sh, void* ws, size_t cap) {
         pl.part_lse[i] = cv.take<float>(BH * sh.n);
       }
     }
-    if (rn) {
-      pl.rn_w = cv.take<float>(BK * sh.n);
-      pl.rn_cum = cv.take<int64_t>(BK * sh.n);
-      pl.rn_sidx = cv.take<int32_t>(BH * (sh.samples > 0 ? sh.samples : 1));
-      pl.rn_ws = cv.take<char>(rownorm_cdf_ws_bytes(BK, sh.n));
-      pl.rn_kc = cv.take<char>(BH * sh.samples * sh.d * esz);
-      pl.rn_vc = cv.take<char>(BH * sh.samples * sh.d * esz);
-      pl.rn_lse = cv.take<float>(BH * sh.n);
-    }
+    if (rn) take_rn(1, sh.n, rownorm_cdf_ws_bytes(BK, sh.n));
   } else if (sh.odd) {
     const int half = sh.n - sh.n / 2;         // the longest quadrant side
     pl.acc_o = cv.take<float>(BH * sh.n * sh.d);
