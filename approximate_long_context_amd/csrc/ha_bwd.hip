@@ -14,16 +14,16 @@
 // of a 32-wide result, 64-row tiles double-buffered through LDS):
 //   * bwd_qstat_kernel: per query, in sorted order, lse in log2 units and
 //     D, so later passes read both contiguously;
-//   * bwd_dq_kernel: query-owned like the forward -- a workgroup of 8 waves
-//     owns 256 consecutive sorted queries, block and sample key tiles
+//   * bwd_dq_kernel: query-owned like the forward -- a workgroup of 4 waves
+//     owns 128 consecutive sorted queries, block and sample key tiles
 //     stream through LDS; per 32-key half S^T = K Q^T and dP^T = V dO^T,
 //     dS is packed to bf16 and dQ^T += K^T dS^T reads K transposed;
 // Both attention passes build P without branches (a masked logit becomes
 // -inf, whose exp2 is 0) in a masked and an unmasked instance of the tile
 // body, chosen per tile and wave; tile loads are unconditional (clamped
 // rows get P = dS = 0).
-//   * bwd_dkv_kernel: key-owned -- a workgroup owns 256 sorted keys (block
-//     part, every query head of the group) or 256 sample slots of one query
+//   * bwd_dkv_kernel: key-owned -- a workgroup owns 128 sorted keys (block
+//     part, every query head of the group) or 128 sample slots of one query
 //     head and a chunk of its queries (sample part); per 32-query half
 //     S = Q K^T and dP = dO V^T with a lane owning a key column, then
 //     dV^T += dO^T P and dK^T += Q^T dS read Q and dO transposed.  Block
@@ -43,9 +43,17 @@ struct Flag {
 };
 
 constexpr int kBT = 64;      // rows per LDS tile
-constexpr int kBW = 8;       // waves per workgroup
+constexpr int kBW = 4;       // waves per workgroup
 constexpr int kBNT = 64 * kBW;
 constexpr int kBTQ = 32 * kBW;   // rows owned by a workgroup
+
+// Waves per SIMD the register budget is set for.  d = 64: two (at most 256
+// VGPRs; two 4-wave workgroups per CU, whose tile phases drift apart).
+// d = 128: one -- a wave then holds up to 512 registers (the accumulators
+// in AGPRs), where at two waves per SIMD the operands and accumulators
+// spilled to scratch memory (measured 3.7x slower).
+template <int D>
+constexpr int bwd_min_waves() { return D == 64 ? 2 : 1; }
 
 template <int D>
 struct BGeo {
@@ -115,7 +123,7 @@ static int dq_list_bytes(int bcap, int m) { return 4 * (bcap + 3 * m + (m + 63) 
 // IDENT: the problem's rows are in row order (exact causal leaves); the
 // permutations are not read.
 template <int D, bool IDENT>
-__global__ __launch_bounds__(kBNT, 2) void bwd_dq_kernel(BwdParams p) {
+__global__ __launch_bounds__(kBNT, bwd_min_waves<D>()) void bwd_dq_kernel(BwdParams p) {
   typedef BGeo<D> G;
   constexpr int NQF = G::NQF, NDT = G::NDT;
   extern __shared__ __attribute__((aligned(16))) char smem[];
@@ -261,6 +269,7 @@ __global__ __launch_bounds__(kBNT, 2) void bwd_dq_kernel(BwdParams p) {
     const bool isB = it >= nA;
     const int kb = isB ? (it - nA) * kBT : ka0 + it * kBT;
     const int kcnt = isB ? min(kBT, nsamp - kb) : min(kBT, ka1 - kb);
+    if (p.causal && kb > q0 + 32 * wave + 31) continue;   // every key of the tile after this wave's queries
     const bf16* ks = reinterpret_cast<const bf16*>(smem + (2 * buf) * G::TB);
     const bf16* vs = reinterpret_cast<const bf16*>(smem + (2 * buf + 1) * G::TB);
     const float off = (isB ? p.log2w : 0.f) - lse2;
@@ -362,7 +371,7 @@ constexpr int dkv_buf_bytes() { return 2 * BGeo<D>::TB + 2 * kBT * 4; }
 // query rows always carry lse = +inf; lanes past the last key need no mask,
 // their column is never stored.
 template <int D, bool SAMPLE, int MASK, bool IDENT>
-__global__ __launch_bounds__(kBNT, 2) void bwd_dkv_kernel(BwdParams p) {
+__global__ __launch_bounds__(kBNT, bwd_min_waves<D>()) void bwd_dkv_kernel(BwdParams p) {
   typedef BGeo<D> G;
   constexpr int NQF = G::NQF, NDT = G::NDT;
   constexpr int BUF = dkv_buf_bytes<D>();

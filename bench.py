@@ -317,6 +317,7 @@ def main():
         del ws
         result["backward"] = {name: backward_bench(ha, torch, w, q, k, v, out, lse, stream)
                               for name, w in (("noncausal", w_nc), ("causal", w_c))}
+        result["backward"]["glm32k"] = backward_config_bench(ha, torch, "glm32k", dev, stream)
     if not args.no_cpu_baseline:
         result["cpu_baseline"] = cpu_baseline(w_nc, w_c, q, k, v)
     else:
@@ -510,6 +511,20 @@ def backward_bench(ha, torch, w, q, k, v, out, lse, stream, reps=3):
     res = {"ms": ms, "tflops": 2.5 * f_fwd / (ms * 1e-3) / 1e12, "causal": w.causal,
            "kernels": {name: t / reps for name, (t, cnt) in per_kernel.items() if cnt}}
     del dout, dq, dk, dv, ws
+    return res
+
+
+def backward_config_bench(ha, torch, name, dev, stream):
+    """backward_bench on another named configuration (its own inputs; the
+    d = 128 grouped-head causal one shows the d = 128 kernels)."""
+    from approximate_long_context_amd.workloads import WORKLOADS, make_inputs
+    w = WORKLOADS[name]
+    q, k, v = make_inputs(w, dev)
+    out = torch.empty_like(q)
+    lse = torch.empty(q.shape[:-1], dtype=torch.float32, device=dev)
+    res = backward_bench(ha, torch, w, q, k, v, out, lse, stream)
+    res["config"] = name
+    del q, k, v, out, lse
     return res
 
 
