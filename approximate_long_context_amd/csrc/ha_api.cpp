@@ -240,51 +240,6 @@ static bool causal_rownorm(const Shape& sh) {
   return sh.causal && (sh.flags & HA_FLAG_ROWNORM) && sh.samples > 0;
 }
 
-// Permutations of causal level l (1 = the top split): queries [mid, hi)
-// and keys [lo, mid) of every node at that depth, BH (BK) * n / 2 entries
-// each, level after level.
-static int32_t* level_perm(int32_t* perm, int64_t heads, int n, int l) {
-  return perm + heads * (n / 2) * (l - 1);
-}
-
-// The segments of every causal level, sorted before the leaves run: one
-// batched sort (a histogram and a scatter launch) per kSortLevelBatch
-// levels instead of one per level, so a launch holds several levels' tiles.
-static int sort_causal_levels(const Shape& sh, const uint16_t* rank_q, const uint16_t* rank_k, int32_t* perm_q,
-                              int32_t* perm_k, void* ws, size_t ws_bytes, hipStream_t s) {
-  const int64_t BH = static_cast<int64_t>(sh.batch) * sh.heads;
-  const int64_t BK = static_cast<int64_t>(sh.batch) * sh.kv_heads;
-  for (int l0 = 1; l0 <= sh.levels; l0 += kSortLevelBatch) {
-    SortJobDesc jobs[2 * kSortLevelBatch];
-    int nj = 0;
-    for (int l = l0; l < l0 + kSortLevelBatch && l <= sh.levels; ++l) {
-      const int seg = sh.n >> l;
-      const int pieces = 1 << (l - 1);
-      jobs[nj++] = {rank_q, BH, sh.n, seg, seg, 2 * seg, pieces, level_perm(perm_q, BH, sh.n, l)};
-      jobs[nj++] = {rank_k, BK, sh.n, seg, 0, 2 * seg, pieces, level_perm(perm_k, BK, sh.n, l)};
-    }
-    HA_TRY(launch_sort_batch(jobs, nj, sh.r, ws, ws_bytes, s));
-  }
-  return HA_OK;
-}
-
-// Workspace of sort_causal_levels: its largest batch.
-static size_t sort_causal_levels_ws(const Shape& sh) {
-  const int64_t BH = static_cast<int64_t>(sh.batch) * sh.heads;
-  const int64_t BK = static_cast<int64_t>(sh.batch) * sh.kv_heads;
-  size_t mx = 0;
-  for (int l0 = 1; l0 <= sh.levels; l0 += kSortLevelBatch) {
-    size_t b = 0;
-    for (int l = l0; l < l0 + kSortLevelBatch && l <= sh.levels; ++l) {
-      const int seg = sh.n >> l;
-      const int pieces = 1 << (l - 1);
-      b += sort_ws_bytes(BH, seg, pieces, sh.r) + sort_ws_bytes(BK, seg, pieces, sh.r);
-    }
-    if (b > mx) mx = b;
-  }
-  return mx;
-}
-
 static Plan make_plan(const Shape& sh, void* ws, size_t cap) {
   Plan pl{};
   Carve cv(ws, cap);
@@ -337,13 +292,19 @@ static Plan make_plan(const Shape& sh, void* ws, size_t cap) {
     if (sh.levels > 0) {
       pl.acc_o = cv.take<float>(BH * sh.n * sh.d);
       pl.acc_lse = cv.take<float>(BH * sh.n);
-      // one permutation pair per level: every level is sorted up front
-      pl.perm_q = cv.take<int32_t>(BH * (sh.n / 2) * sh.levels);
-      pl.perm_k = cv.take<int32_t>(BK * (sh.n / 2) * sh.levels);
+      pl.perm_q = cv.take<int32_t>(BH * (sh.n / 2));
+      pl.perm_k = cv.take<int32_t>(BK * (sh.n / 2));
       const int64_t maxp = int64_t(1) << (sh.levels - 1);
       pl.sidx = cv.take<int32_t>(BH * maxp * (sh.samples > 0 ? sh.samples : 1));
-      pl.sort_ws_bytes = sort_causal_levels_ws(sh);
-      pl.sort_ws = cv.take<char>(pl.sort_ws_bytes);
+      size_t mx = 0;
+      for (int l = 1; l <= sh.levels; ++l) {
+        const int seg = sh.n >> l;
+        const int pieces = 1 << (l - 1);
+        const size_t b = sort_ws_bytes(BH, seg, pieces, sh.r) + sort_ws_bytes(BK, seg, pieces, sh.r);
+        if (b > mx) mx = b;
+      }
+      pl.sort_ws_bytes = mx;
+      pl.sort_ws = cv.take<char>(mx);
       if (causal_rownorm(sh)) {
         size_t cdf = 0;
         for (int l = 1; l <= sh.levels; ++l) {
@@ -547,6 +508,18 @@ static int forward_causal_nodes(const AttnParams& ap, const Shape& sh, const Pla
   return HA_OK;
 }
 
+// The segments of causal level l (queries [mid, hi) and keys [lo, mid) of
+// every node at that depth) in one batched sort.
+static int sort_causal_level(const uint16_t* rank_q, const uint16_t* rank_k, int64_t BH, int64_t BK, int n,
+                             int l, int r, int32_t* perm_q, int32_t* perm_k, void* ws, size_t ws_bytes,
+                             hipStream_t s) {
+  const int seg = n >> l;
+  const int pieces = 1 << (l - 1);
+  const SortJobDesc jobs[2] = {{rank_q, BH, n, seg, seg, 2 * seg, pieces, perm_q},
+                               {rank_k, BK, n, seg, 0, 2 * seg, pieces, perm_k}};
+  return launch_sort_batch(jobs, 2, r, ws, ws_bytes, s);
+}
+
 static int forward_impl(const void* q, const void* k, const void* v, Shape sh, uint64_t seed,
                         void* out, float* lse, void* ws, size_t ws_bytes, hipStream_t s,
                         const ha_debug_dump* dbg = nullptr) {
@@ -662,7 +635,6 @@ static int forward_impl(const void* q, const void* k, const void* v, Shape sh, u
 
   // ---- causal ----
   if (sh.odd) return forward_causal_nodes(ap, sh, pl, seed, s, dbg);
-  HA_TRY(sort_causal_levels(sh, pl.rank_q, pl.rank_k, pl.perm_q, pl.perm_k, pl.sort_ws, pl.sort_ws_bytes, s));
   AttnParams lp = ap;
   lp.kind = kKindLeaf;
   lp.pieces = sh.n / sh.leaf;
@@ -682,6 +654,8 @@ static int forward_impl(const void* q, const void* k, const void* v, Shape sh, u
   for (int l = sh.levels; l >= 1; --l) {
     const int seg = sh.n >> l;
     const int pieces = 1 << (l - 1);
+    HA_TRY(sort_causal_level(pl.rank_q, pl.rank_k, BH, BK, sh.n, l, sh.r, pl.perm_q, pl.perm_k, pl.sort_ws,
+                             pl.sort_ws_bytes, s));
     HA_TRY(launch_sample_indices(seed, sh.batch, sh.heads, pieces, pieces, seg, sh.samples,
                                  pl.sidx, s));
     AttnParams qp = ap;
@@ -691,8 +665,8 @@ static int forward_impl(const void* q, const void* k, const void* v, Shape sh, u
     qp.q_first = seg;
     qp.k_first = 0;
     qp.stride = 2 * seg;
-    qp.perm_q = level_perm(pl.perm_q, BH, sh.n, l);
-    qp.perm_k = level_perm(pl.perm_k, BK, sh.n, l);
+    qp.perm_q = pl.perm_q;
+    qp.perm_k = pl.perm_k;
     qp.b_eff = sh.block < seg ? sh.block : seg;
     qp.use_block = 1;
     qp.use_samples = sh.samples > 0;
@@ -864,16 +838,21 @@ static BwdPlan backward_plan(const Shape& sh, void* ws, size_t cap) {
     pl.part = cv.take<float>(bwd_part_floats(BH, sh.n, 1, sh.samples, sh.d));
     pl.red_keys = cv.take<uint64_t>(BH * m1);
   } else if (sh.levels > 0) {
-    pl.perm_q = cv.take<int32_t>(BH * (sh.n / 2) * sh.levels);   // one pair per level, sorted up front
-    pl.perm_k = cv.take<int32_t>(BK * (sh.n / 2) * sh.levels);
+    pl.perm_q = cv.take<int32_t>(BH * (sh.n / 2));
+    pl.perm_k = cv.take<int32_t>(BK * (sh.n / 2));
     pl.sidx = cv.take<int32_t>(BH * (int64_t(1) << (sh.levels - 1)) * m1);
+    size_t mx = 0;
     int64_t part = 0;
     for (int l = 1; l <= sh.levels; ++l) {
-      const int64_t f = bwd_part_floats(BH, sh.n >> l, 1 << (l - 1), sh.samples, sh.d);
+      const int seg = sh.n >> l;
+      const int pieces = 1 << (l - 1);
+      const size_t b = sort_ws_bytes(BH, seg, pieces, sh.r) + sort_ws_bytes(BK, seg, pieces, sh.r);
+      if (b > mx) mx = b;
+      const int64_t f = bwd_part_floats(BH, seg, pieces, sh.samples, sh.d);
       if (f > part) part = f;
     }
-    pl.sort_ws_bytes = sort_causal_levels_ws(sh);
-    pl.sort_ws = cv.take<char>(pl.sort_ws_bytes);
+    pl.sort_ws_bytes = mx;
+    pl.sort_ws = cv.take<char>(mx);
     pl.part = cv.take<float>(part);
     pl.red_keys = cv.take<uint64_t>(BH * (int64_t(1) << (sh.levels - 1)) * m1);
   } else if (sh.odd) {
@@ -1015,8 +994,6 @@ static int backward_impl(const void* q, const void* k, const void* v, const void
     return HA_OK;
   }
 
-  HA_TRY(sort_causal_levels(sh, pl.rank_q, pl.rank_k, pl.perm_q, pl.perm_k, pl.sort_ws, pl.sort_ws_bytes, s));
-
   // exact causal leaves, rows in their own order
   BwdParams lp = bp;
   lp.pieces = sh.n / sh.leaf;
@@ -1035,9 +1012,10 @@ static int backward_impl(const void* q, const void* k, const void* v, const void
   for (int l = sh.levels; l >= 1; --l) {
     const int seg = sh.n >> l;
     const int pieces = 1 << (l - 1);
+    HA_TRY(sort_causal_level(pl.rank_q, pl.rank_k, BH, BK, sh.n, l, sh.r, pl.perm_q, pl.perm_k, pl.sort_ws,
+                             pl.sort_ws_bytes, s));
     HA_TRY(launch_sample_indices(seed, sh.batch, sh.heads, pieces, pieces, seg, sh.samples, pl.sidx, s));
-    HA_TRY(sorted_problems(seg, pieces, seg, 0, 2 * seg, 1, level_perm(pl.perm_q, BH, sh.n, l),
-                           level_perm(pl.perm_k, BK, sh.n, l), seg));
+    HA_TRY(sorted_problems(seg, pieces, seg, 0, 2 * seg, 1, pl.perm_q, pl.perm_k, seg));
   }
   return HA_OK;
 }

@@ -28,7 +28,6 @@ struct SortJobDesc {
   int32_t* perm;
 };
 constexpr int kSortMaxJobs = 16;
-constexpr int kSortLevelBatch = kSortMaxJobs / 2;   // causal levels per batched sort (a Q and a K job each)
 size_t sort_batch_ws_bytes(const SortJobDesc* jobs, int njobs, int r);
 int launch_sort_batch(const SortJobDesc* jobs, int njobs, int r, void* ws, size_t ws_bytes, hipStream_t s);
 int launch_sort(const uint16_t* rank, int64_t heads, int n, int len, int first, int stride,
