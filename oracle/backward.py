@@ -101,15 +101,26 @@ def weighted_attention(q, k, v, W):
     return O, lse
 
 
-def weighted_backward(q, k, v, W, do):
-    """(dq, dk, dv) of sum(do * O) for O = weighted_attention(q, k, v, W)."""
+def round_bf16(x):
+    """x (fp64 array, normal range) rounded to the nearest bfloat16 value,
+    ties to even: 8 significant bits (frexp gives x = m 2^e, m in [0.5, 1))."""
+    m, e = np.frexp(np.asarray(x, dtype=np.float64))
+    return np.ldexp(np.round(np.ldexp(m, 8)), e - 8)
+
+
+def weighted_backward(q, k, v, W, do, out_round=None):
+    """(dq, dk, dv) of sum(do * O) for O = weighted_attention(q, k, v, W).
+
+    out_round: None, or a rounding applied to O before D = rowsum(do * O)
+    (reading R14b: a backward handed the forward's output in the input
+    dtype forms D from that output; ``round_bf16`` models a bf16 one)."""
     O, lse = weighted_attention(q, k, v, W)
     S = q @ k.T
     with np.errstate(invalid="ignore", over="ignore"):
         P = np.where(W > 0, W * np.exp(S - np.where(np.isfinite(lse), lse, 0.0)[:, None]), 0.0)
     dv = P.T @ do
     dP = do @ v.T
-    D = np.sum(do * O, axis=1)
+    D = np.sum(do * (O if out_round is None else out_round(O)), axis=1)
     dS = P * (dP - D[:, None])
     dq = dS @ k
     dk = dS.T @ q
@@ -229,12 +240,13 @@ def backward_head_blocks(q, k, v, do, cfg, b, h):
                                      cfg.samples)
 
 
-def causal_dq_rows(q, k, v, do, rank_q, rank_k, seed, batch_idx, head, cfg, rows):
+def causal_dq_rows(q, k, v, do, rank_q, rank_k, seed, batch_idx, head, cfg, rows, out_round=None):
     """dq of the listed rows of one causal problem, each from its own row of
     ``causal_weights`` (the leaf's keys up to the row at weight 1, plus, at
     every split whose upper half holds the row, the quadrant's block keys
     and kept draws), so full sizes need no n x n matrix.  q, k, v, do
-    [n, d] fp64; returns [len(rows), d]."""
+    [n, d] fp64; returns [len(rows), d].  out_round as for
+    ``weighted_backward``."""
     n = len(rank_q)
     causal_levels(n, cfg.min_seq_len)
     perms = {}
@@ -278,6 +290,6 @@ def causal_dq_rows(q, k, v, do, rank_q, rank_k, seed, batch_idx, head, cfg, rows
         wts.append(np.ones(i + 1 - lo))
         kc = np.concatenate(cols)
         Wr = np.concatenate(wts)[None, :]
-        gq, _, _ = weighted_backward(q[i:i + 1], k[kc], v[kc], Wr, do[i:i + 1])
+        gq, _, _ = weighted_backward(q[i:i + 1], k[kc], v[kc], Wr, do[i:i + 1], out_round)
         out[r] = gq[0]
     return out

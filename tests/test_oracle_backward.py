@@ -10,7 +10,9 @@
 * planted mistakes in the backward formula are caught by the finite
   differences;
 * rectangular problems (n_q != n_k): the weights reproduce
-  ``forward_rect`` and ``backward_rect`` matches finite differences.
+  ``forward_rect`` and ``backward_rect`` matches finite differences;
+* ``round_bf16`` (the bf16 output that D is formed from, reading R14b)
+  equals torch's float32 -> bfloat16 conversion, ties included.
 """
 
 import numpy as np
@@ -241,9 +243,11 @@ def test_block_backward_equals_dense(n, block, m, seed):
     (256, 64, 0, 32, 8),      # no samples
     (200, 16, 40, 200, 9),    # one leaf: exact causal attention
 ])
-def test_causal_dq_rows_equal_dense(n, block, m, s, seed):
+@pytest.mark.parametrize("out_round", [None, ob.round_bf16], ids=["fp64_out", "bf16_out"])
+def test_causal_dq_rows_equal_dense(n, block, m, s, seed, out_round):
     """Row-wise causal dq (used at full sizes) equals the dense-W backward's
-    dq on every row, for the same ranks and draws."""
+    dq on every row, for the same ranks and draws (D from the exact or the
+    bf16-rounded output)."""
     g = np.random.default_rng(seed)
     d = 16
     q = g.standard_normal((n, d)) * 0.5
@@ -254,7 +258,25 @@ def test_causal_dq_rows_equal_dense(n, block, m, s, seed):
     rq, rk = oh.ranks(q.astype(np.float32), R), oh.ranks(k.astype(np.float32), R)
     cfg = oh.HAConfig(block=block, samples=m, proj_bits=5, causal=True, min_seq_len=s, seed=seed)
     W = ob.causal_weights(rq, rk, seed, 0, 2, cfg)
-    want = ob.weighted_backward(q, k, v, W, do)[0]
+    want = ob.weighted_backward(q, k, v, W, do, out_round)[0]
     rows = np.arange(n)
-    got = ob.causal_dq_rows(q, k, v, do, rq, rk, seed, 0, 2, cfg, rows)
+    got = ob.causal_dq_rows(q, k, v, do, rq, rk, seed, 0, 2, cfg, rows, out_round=out_round)
     assert np.allclose(got, want, rtol=1e-10, atol=1e-12)
+    if out_round is not None:             # the rounding reaches dq
+        assert not np.allclose(got, ob.weighted_backward(q, k, v, W, do)[0], rtol=1e-6, atol=1e-9)
+
+
+def test_round_bf16_matches_torch():
+    """round_bf16 equals torch's float32 -> bfloat16 conversion (nearest,
+    ties to even) on fp32 values over a wide range, on exact ties (a bf16
+    value plus half its last place, both signs, odd and even last bits)
+    and on zero; a rounding to 7 or 9 bits, or one that breaks ties away
+    from zero, fails it."""
+    g = np.random.default_rng(3)
+    x = (g.standard_normal(20000) * np.exp(g.uniform(-20, 20, 20000))).astype(np.float32)
+    b = torch.from_numpy(x[:4000]).to(torch.bfloat16).double().numpy()
+    _, e = np.frexp(b)
+    ties = (b + np.ldexp(1.0, e - 9)).astype(np.float32)     # half of 2^(e-8), the last place of 8 bits
+    x = np.concatenate([x, ties, -ties, np.float32([0.0, 1.0, -2.5, 3.0])])
+    want = torch.from_numpy(x).to(torch.bfloat16).double().numpy()
+    assert np.array_equal(ob.round_bf16(x.astype(np.float64)), want)
