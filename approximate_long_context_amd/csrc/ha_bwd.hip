@@ -506,9 +506,9 @@ __global__ __launch_bounds__(kBNT, bwd_min_waves<D>()) void bwd_dkv_kernel(BwdPa
       const int j = j_first + c * JSTEP;
       *reinterpret_cast<uint4v*>(&qs[j * G::STR + 8 * c_in_row]) = qreg[c];
       *reinterpret_cast<uint4v*>(&gs[j * G::STR + 8 * c_in_row]) = greg[c];
-      if (c_in_row == 0) {
-        ls[j] = sval[c] ? sreg[c][0] : INFINITY;
-        ls[kBT + j] = sreg[c][1];
+      if (c_in_row == 0) {                      // accumulator starts: -lse (natural log units), -D
+        ls[j] = sval[c] ? -sreg[c][0] * kLn2 : -INFINITY;
+        ls[kBT + j] = -sreg[c][1];
       }
     }
   };
@@ -549,9 +549,20 @@ __global__ __launch_bounds__(kBNT, bwd_min_waves<D>()) void bwd_dkv_kernel(BwdPa
           qa[c] = *reinterpret_cast<const bf16x8*>(&qs[e]);
           ga[c] = *reinterpret_cast<const bf16x8*>(&gs[e]);
         }
+        // S and dP accumulate onto the rows' statistics, so they end as
+        // S - lse and dP - D (register r holds query 32 qt + 8 (r / 4) + 4 h2 + r % 4)
         floatx16 s, dp;
 #pragma unroll
-        for (int r = 0; r < 16; ++r) s[r] = dp[r] = 0.f;
+        for (int g = 0; g < 4; ++g) {
+          const int j0 = 32 * qt + 8 * g + 4 * h2;
+          const floatx4 a4 = *reinterpret_cast<const floatx4*>(ls + j0);
+          const floatx4 b4 = *reinterpret_cast<const floatx4*>(ls + kBT + j0);
+#pragma unroll
+          for (int i = 0; i < 4; ++i) {
+            s[4 * g + i] = a4[i];
+            dp[4 * g + i] = b4[i];
+          }
+        }
 #pragma unroll
         for (int c = 0; c < NQF; ++c) {
           s = __builtin_amdgcn_mfma_f32_32x32x16_bf16(qa[c], kf[c], s, 0, 0, 0);
@@ -570,12 +581,10 @@ __global__ __launch_bounds__(kBNT, bwd_min_waves<D>()) void bwd_dkv_kernel(BwdPa
 #pragma unroll
         for (int g = 0; g < 4; ++g) {
           const int j0 = 32 * qt + 8 * g + 4 * h2;      // 4 consecutive queries of the tile
-          const floatx4 l4 = *reinterpret_cast<const floatx4*>(ls + j0);
-          const floatx4 d4 = *reinterpret_cast<const floatx4*>(ls + kBT + j0);
 #pragma unroll
           for (int i = 0; i < 4; ++i) {
             const int r = 4 * g + i;
-            float x = fmaf(s[r], kLog2e, bias - l4[i]);
+            float x = fmaf(s[r], kLog2e, bias);
             if constexpr (MASK == 1) {
               const bool in_blk = static_cast<unsigned>(j0 + i - lo) < static_cast<unsigned>(b_eff);
               x = (SAMPLE ? !in_blk : in_blk) ? x : -INFINITY;
@@ -584,7 +593,7 @@ __global__ __launch_bounds__(kBNT, bwd_min_waves<D>()) void bwd_dkv_kernel(BwdPa
             }
             const float pr = fast_exp2(x);
             const bf16 pv = static_cast<bf16>(pr);
-            const bf16 dsv = static_cast<bf16>(pr * (dp[r] - d4[i]));
+            const bf16 dsv = static_cast<bf16>(pr * dp[r]);
             if (r < 8) {
               pa[r] = pv;
               da[r] = dsv;
