@@ -79,6 +79,22 @@ def alg_bytes(w, causal):
 CPU_HEADS = 2      # heads of the bounded oracle sample (about 10-20 s of CPU work)
 
 
+def rep_times(torch, stream, fn, reps):
+    """ms of each of `reps` calls of fn, from an event pair per call on `stream`,
+    and their mean, median, p10 and p90."""
+    import numpy as np
+    evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(reps)]
+    torch.cuda.synchronize()
+    for a, b in evs:
+        a.record(stream)
+        fn()
+        b.record(stream)
+    torch.cuda.synchronize()
+    ms = np.array([a.elapsed_time(b) for a, b in evs])
+    return {"mean": float(ms.mean()), "median": float(np.median(ms)), "p10": float(np.percentile(ms, 10)),
+            "p90": float(np.percentile(ms, 90)), "reps": reps}
+
+
 def cpu_baseline(w_nc, w_c, q, k, v):
     """Time the oracle on the first CPU_HEADS heads of both passes; returns
     the baseline dict."""
@@ -103,9 +119,18 @@ def cpu_baseline(w_nc, w_c, q, k, v):
         f, _ = alg_flops(w.with_(heads=nh, kv_heads=nh), w.causal)
         flops += f
     dt = time.perf_counter() - t0
+    # the whole fp32 n = 1024 configuration as well (well under a second)
+    from approximate_long_context_amd.workloads import WORKLOADS, make_inputs
+    ws = WORKLOADS["small"]
+    qs, ks, vs = (t.numpy() for t in make_inputs(ws, "cpu"))
+    t1 = time.perf_counter()
+    oracle.forward(qs, ks, vs, HAConfig(block=ws.block, samples=ws.samples, proj_bits=ws.proj_bits,
+                                        causal=ws.causal, min_seq_len=ws.min_seq_len, seed=ws.seed))
+    dt_small = time.perf_counter() - t1
     return {"value": flops / dt / 1e12, "unit": "TFLOP/s", "cores": int(threads), "kind": "oracle",
             "sample": f"heads 0..{nh - 1} of {w_nc.heads}, all {w_nc.n} rows, non-causal + causal passes, fp64 numpy; "
-                      f"{dt:.1f} s on {os.cpu_count()} host CPUs", "seconds": dt}
+                      f"{dt:.1f} s on {os.cpu_count()} host CPUs", "seconds": dt,
+            "configs_ms": {"small": dt_small * 1e3}}
 
 
 def traffic_record(kernel_class):
@@ -214,16 +239,12 @@ def main():
     ha.timing_enable(False)
 
     # separate per-pass timing (untimed for `value`, reported for context)
-    pass_ms = {}
+    pass_ms, pass_stats = {}, {}
     for name, w in (("noncausal", w_nc), ("causal", w_c)):
-        e0 = torch.cuda.Event(enable_timing=True)
-        e1 = torch.cuda.Event(enable_timing=True)
-        e0.record(stream)
-        for _ in range(args.steps):
-            ha.forward(q, k, v, out=out, lse=lse, workspace=ws, **w.method_args())
-        e1.record(stream)
-        torch.cuda.synchronize()
-        pass_ms[name] = e0.elapsed_time(e1) / args.steps
+        st = rep_times(torch, stream, lambda w=w: ha.forward(q, k, v, out=out, lse=lse, workspace=ws, **w.method_args()),
+                       max(args.steps, 3))
+        pass_ms[name] = st["mean"]
+        pass_stats[name] = st
 
     f_nc, parts_nc = alg_flops(w_nc, False)
     f_c, parts_c = alg_flops(w_c, True)
@@ -292,6 +313,7 @@ def main():
                    "batch": w_nc.batch, "heads": w_nc.heads, "seq_len": w_nc.n, "head_dim": w_nc.d,
                    "parallelism": "single GPU"},
         "ms_noncausal": pass_ms["noncausal"],
+        "pass_ms_stats": pass_stats,
         "ms_causal": pass_ms["causal"],
         "tflops_noncausal": f_nc / (pass_ms["noncausal"] * 1e-3) / 1e12,
         "tflops_causal": f_c / (pass_ms["causal"] * 1e-3) / 1e12,
@@ -528,10 +550,11 @@ def backward_config_bench(ha, torch, name, dev, stream):
     return res
 
 
-def other_configs(ha, torch, dev, stream, reps=5):
-    """ms per forward and effective TFLOP/s of the other configurations: the
-    fp32 n = 1024 single head (against the fp32 MFMA peak) and the bf16 ones
-    (not part of `value`)."""
+def other_configs(ha, torch, dev, stream, reps=20):
+    """ms per forward (median of `reps` after 3 warm-ups, with p10 / p90) and
+    effective TFLOP/s of the other configurations: the fp32 n = 1024 single
+    head (against the fp32 MFMA peak) and the bf16 ones (not part of
+    `value`)."""
     from approximate_long_context_amd.workloads import WORKLOADS, make_inputs
     res = {}
     for name in ("small", "c32k", "glm32k", "stress512k"):
@@ -541,17 +564,10 @@ def other_configs(ha, torch, dev, stream, reps=5):
         ws = torch.empty(ha.workspace_bytes(w.batch, w.n, w.d, w.heads, w.kv_heads, w.block, w.samples,
                                             w.proj_bits, w.causal, w.min_seq_len, w.dtype),
                          dtype=torch.uint8, device=dev)
-        for _ in range(2):
+        for _ in range(3):
             ha.forward(q, k, v, out=out, workspace=ws, **w.method_args())
-        e0 = torch.cuda.Event(enable_timing=True)
-        e1 = torch.cuda.Event(enable_timing=True)
-        torch.cuda.synchronize()
-        e0.record(stream)
-        for _ in range(reps):
-            ha.forward(q, k, v, out=out, workspace=ws, **w.method_args())
-        e1.record(stream)
-        torch.cuda.synchronize()
-        ms = e0.elapsed_time(e1) / reps
+        st = rep_times(torch, stream, lambda: ha.forward(q, k, v, out=out, workspace=ws, **w.method_args()), reps)
+        ms = st["median"]
         # per-kernel-class ms per forward, from a separate timed set of calls
         ha.timing_enable(True)
         for _ in range(reps):
@@ -561,7 +577,8 @@ def other_configs(ha, torch, dev, stream, reps=5):
         ha.timing_enable(False)
         f, _ = alg_flops(w, w.causal)
         fp32 = w.dtype == torch.float32
-        res[name] = {"ms": ms, "tflops": f / (ms * 1e-3) / 1e12, "causal": w.causal, "n": w.n,
+        res[name] = {"ms": ms, "ms_p10": st["p10"], "ms_p90": st["p90"], "reps": reps,
+                     "tflops": f / (ms * 1e-3) / 1e12, "causal": w.causal, "n": w.n,
                      "heads": w.heads, "kv_heads": w.kv_heads, "head_dim": w.d,
                      "block": w.block, "samples": w.samples, "dtype": "f32" if fp32 else "bf16",
                      "mfma_peak_tflops": MFMA_FP32_PEAK_TFLOPS if fp32 else MFMA_BF16_PEAK_TFLOPS,
