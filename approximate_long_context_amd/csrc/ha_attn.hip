@@ -877,13 +877,15 @@ static int shape_override(int kind) {
 
 template <typename T, int D, int KIND, int OUT>
 static int launch_attn_shape(const AttnParams& p, hipStream_t s) {
-  // Default (measured on MI355X at n = 131072, d = 64): causal leaves 8
-  // waves x 32 queries (128 VGPRs, 4 waves per SIMD); sorted problems 8
-  // waves x 32 queries when the block holds >= 256 rows (all of a block's
-  // queries share each K/V tile), else 4 waves x 32.
+  // Default (measured on MI355X): bf16 causal leaves of >= 256 rows 8
+  // waves x 32 queries (d = 64: 128 VGPRs, 4 waves per SIMD; d = 128: 2
+  // waves per SIMD, each K/V tile shared by twice the queries of a 4-wave
+  // workgroup, which pays on long leaves); sorted problems 8 waves x 32
+  // queries when the block holds >= 256 rows (all of a block's queries
+  // share each K/V tile), else 4 waves x 32.
   int shape = shape_override(KIND);
   if (shape == 0) {
-    if (KIND == kKindLeaf) shape = (sizeof(T) == 2 && D == 64 && p.seg >= 256) ? 2 : 1;
+    if (KIND == kKindLeaf) shape = (sizeof(T) == 2 && p.seg >= 256) ? 2 : 1;
     else shape = (p.seg >= 256 && p.b_eff >= 256) ? 2 : 1;
   }
   if (shape == 2) return launch_attn_t<T, D, KIND, OUT, 8, 32>(p, s);
