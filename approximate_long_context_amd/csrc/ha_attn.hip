@@ -435,7 +435,7 @@ __global__ __launch_bounds__(64 * NW, (min_waves<T, D, KIND, NW, QPW>())) void a
           }
         }
       };
-      auto offset = [&]() { return bias + nref; };
+      auto offset = [&]() { return LEAF ? nref : bias + nref; };   // leaves carry no sample weight
       // weights of S elements i, i+1 into the B operands of the half's two
       // 16-key chunks (elements 0..7 -> pa, 8..15 -> pb), summed into l
       auto p_pair = [&](const floatx16& sv, int i, float off, bf16x8& pa, bf16x8& pb, float& l) {
