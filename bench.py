@@ -95,9 +95,35 @@ def rep_times(torch, stream, fn, reps):
             "p90": float(np.percentile(ms, 90)), "reps": reps}
 
 
-def cpu_baseline(w_nc, w_c, q, k, v):
+def gpu_sample(ha, torch, w_nc, w_c, q, k, v, ws, nh):
+    """What the library computes on the first nh heads of the benchmark's
+    inputs (outside any timed region): each pass's out and lse, the bucket
+    ranks of the Q and K rows, the non-causal whole-head permutations and
+    sample positions; host numpy arrays for the comparison with the oracle."""
+    import numpy as np
+    res = {}
+    for name, w in (("noncausal", w_nc), ("causal", w_c)):
+        out, lse = ha.forward(q, k, v, workspace=ws, **w.method_args())
+        res[name] = (out[:, :nh].float().cpu().numpy(), lse[:, :nh].cpu().numpy())
+        del out, lse
+    R = ha.projections(w_nc.seed, w_nc.d, w_nc.proj_bits, q.device)
+    rq = ha.hash_rows(q[0, :nh].contiguous(), R)
+    rk = ha.hash_rows(k[0, :nh].contiguous(), R)
+    res["rank_q"], res["rank_k"] = rq.cpu().numpy().astype(np.uint32), rk.cpu().numpy().astype(np.uint32)
+    res["perm_q"] = ha.sort_ranks(rq, w_nc.proj_bits).cpu().numpy()[:, 0]
+    res["perm_k"] = ha.sort_ranks(rk, w_nc.proj_bits).cpu().numpy()[:, 0]
+    res["samples"] = ha.sample_indices(w_nc.seed, 1, nh, w_nc.n, w_nc.samples, device=q.device).cpu().numpy()[0, :, 0]
+    torch.cuda.synchronize()
+    return res
+
+
+def cpu_baseline(w_nc, w_c, q, k, v, gpu=None):
     """Time the oracle on the first CPU_HEADS heads of both passes; returns
-    the baseline dict."""
+    the baseline dict.  With `gpu` (gpu_sample's arrays for the same heads)
+    the dict also carries the library's agreement with that oracle run:
+    output and lse errors per pass, and mismatch counts of ranks,
+    permutations and sample positions (expected zero: the library computes
+    these bit-exactly)."""
     import numpy as np
     import oracle
     from oracle.hyperattn import HAConfig
@@ -111,14 +137,35 @@ def cpu_baseline(w_nc, w_c, q, k, v):
     kh = k[:, :nh].float().cpu().numpy()
     vh = v[:, :nh].float().cpu().numpy()
     flops = 0.0
+    refs = {}
     t0 = time.perf_counter()
-    for w in (w_nc, w_c):
+    for name, w in (("noncausal", w_nc), ("causal", w_c)):
         cfg = HAConfig(block=w.block, samples=w.samples, proj_bits=w.proj_bits, causal=w.causal,
                        min_seq_len=w.min_seq_len, seed=w.seed)
-        oracle.forward(qh, kh, vh, cfg)
+        refs[name] = oracle.forward(qh, kh, vh, cfg)
         f, _ = alg_flops(w.with_(heads=nh, kv_heads=nh), w.causal)
         flops += f
     dt = time.perf_counter() - t0
+    parity = None
+    if gpu is not None:
+        parity = {"heads": nh}
+        for name, (o_ref, l_ref) in refs.items():
+            o_gpu, l_gpu = gpu[name]
+            both_inf = np.isneginf(l_gpu) & np.isneginf(l_ref)
+            parity[name] = {"out_max_abs": float(np.abs(o_gpu - o_ref).max()),
+                            "out_rel_fro": float(np.linalg.norm(o_gpu - o_ref) / np.linalg.norm(o_ref)),
+                            "lse_max_abs": float(np.where(both_inf, 0.0, np.abs(l_gpu - l_ref)).max())}
+        R = oracle.projections(w_nc.seed, w_nc.d, w_nc.proj_bits)
+        mism = {"rank": 0, "perm": 0, "sample": 0}
+        for h in range(nh):
+            for x, key in ((qh, "q"), (kh, "k")):
+                rk = oracle.ranks(x[0, h], R)
+                mism["rank"] += int(np.count_nonzero(gpu["rank_" + key][h] != rk))
+                mism["perm"] += int(np.count_nonzero(gpu["perm_" + key][h] != oracle.sort_perm(rk)))
+            ref_s = oracle.sample_positions(w_nc.seed, 0, h, 1, w_nc.n, w_nc.samples)
+            mism["sample"] += int(np.count_nonzero(gpu["samples"][h] != ref_s))
+        parity["mismatches"] = mism
+        parity["compared"] = {"rank": 2 * nh * w_nc.n, "perm": 2 * nh * w_nc.n, "sample": nh * w_nc.samples}
     # the whole fp32 n = 1024 configuration as well (well under a second)
     from approximate_long_context_amd.workloads import WORKLOADS, make_inputs
     ws = WORKLOADS["small"]
@@ -130,7 +177,7 @@ def cpu_baseline(w_nc, w_c, q, k, v):
     return {"value": flops / dt / 1e12, "unit": "TFLOP/s", "cores": int(threads), "kind": "oracle",
             "sample": f"heads 0..{nh - 1} of {w_nc.heads}, all {w_nc.n} rows, non-causal + causal passes, fp64 numpy; "
                       f"{dt:.1f} s on {os.cpu_count()} host CPUs", "seconds": dt,
-            "configs_ms": {"small": dt_small * 1e3}}
+            "configs_ms": {"small": dt_small * 1e3}, "parity": parity}
 
 
 def traffic_record(kernel_class):
@@ -246,6 +293,11 @@ def main():
         pass_ms[name] = st["mean"]
         pass_stats[name] = st
 
+    # the library's results on the oracle sample's heads (compared in cpu_baseline)
+    gpu_par = None
+    if not args.no_cpu_baseline:
+        gpu_par = gpu_sample(ha, torch, w_nc, w_c, q, k, v, ws, min(CPU_HEADS, w_nc.heads, w_nc.kv_heads))
+
     f_nc, parts_nc = alg_flops(w_nc, False)
     f_c, parts_c = alg_flops(w_c, True)
     flops_step = f_nc + f_c
@@ -341,7 +393,7 @@ def main():
                               for name, w in (("noncausal", w_nc), ("causal", w_c))}
         result["backward"]["glm32k"] = backward_config_bench(ha, torch, "glm32k", dev, stream)
     if not args.no_cpu_baseline:
-        result["cpu_baseline"] = cpu_baseline(w_nc, w_c, q, k, v)
+        result["cpu_baseline"] = cpu_baseline(w_nc, w_c, q, k, v, gpu_par)
     else:
         result["cpu_baseline"] = None
     print(json.dumps(result))
