@@ -179,7 +179,8 @@ def test_full_workload_sampled_rows(name):
 
 
 @pytest.mark.slow
-@pytest.mark.parametrize("name,heads", [("long131k", (0, 31)), ("long131k_causal", (0, 31)), ("stress512k", (0,))])
+@pytest.mark.parametrize("name,heads", [("long131k", (0, 31)), ("long131k_causal", (0, 31)), ("stress512k", (0,)),
+                                        ("c32k", (0, 31)), ("glm32k", (0, 31)), ("small", (0,))])
 def test_full_workload_every_row(name, heads):
     """Whole heads at the benchmark's sizes and launch configuration: every
     row of the listed heads against the oracle (out and lse)."""
